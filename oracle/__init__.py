@@ -1,0 +1,126 @@
+"""fp64 CPU oracle for ELU+1 linear attention (test infrastructure only).
+
+The oracle is the slow, plainly written checker the GPU library is compared
+against.  Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's
+CPU-baseline leg may import it; the product path never does.  It shares no
+code with the HIP library: the arithmetic lives in ``linattn_ref.c`` (plain C,
+double precision), this module only converts arrays and calls it.
+
+Definition followed (LinearTile 1.0.0 README, "How It Works"; causal form
+from its "Features" list and Katharopoulos et al. 2020 cited under its
+"Reference" section): O = phi(Q) (phi(K)^T V), phi = ELU + 1, causal rows
+see keys s <= t, optional normaliser phi(q_t) . z_t.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "linattn_ref.c")
+_LIB_PATH = os.path.join(_HERE, "liblinattn_ref.so")
+# A test may point the wrapper at a deliberately broken build of the oracle
+# (mutation tests); normal use never sets this.
+_LIB_OVERRIDE = os.environ.get("LINATTN_REF_LIB")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (IEEE double, no contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+             "-shared", _SRC, "-o", tmp, "-lm", "-lpthread"],
+            check=True,
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = _LIB_OVERRIDE or _LIB_PATH
+        if not _LIB_OVERRIDE and not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.linattn_ref_phi.restype = ctypes.c_double
+        lib.linattn_ref_phi.argtypes = [ctypes.c_double]
+        lib.linattn_ref_fwd.restype = ctypes.c_int
+        lib.linattn_ref_fwd.argtypes = [dp, dp, dp, dp] + [ctypes.c_int] * 7 + [dp, dp, ctypes.c_int]
+        lib.linattn_ref_decode_step.restype = ctypes.c_int
+        lib.linattn_ref_decode_step.argtypes = [dp] * 6 + [ctypes.c_int] * 5
+        _lib = lib
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    """Exact fp64 copy of a numpy array or a CPU torch tensor (fp32/bf16/fp64)."""
+    if hasattr(x, "detach"):  # torch tensor: widen exactly through float64
+        import torch
+
+        x = x.detach().to("cpu", torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def phi(x: float) -> float:
+    """phi(x) = ELU(x) + 1 with alpha = 1, evaluated by the C oracle."""
+    return _load().linattn_ref_phi(float(x))
+
+
+def ref_fwd(q, k, v, causal: bool = True, normalise: bool = True,
+            want_state: bool = False, nthreads: int | None = None):
+    """Forward pass.  q [B,H,N,d], k/v [B,Hkv,N,d] -> out [B,H,N,d] (fp64).
+
+    With ``want_state`` also returns S_N [B,Hkv,d,d] and z_N [B,Hkv,d].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, d) and v.shape == (B, Hkv, N, d)
+    out = np.zeros((B, H, N, d), dtype=np.float64)
+    S = np.zeros((B, Hkv, d, d), dtype=np.float64) if want_state else None
+    z = np.zeros((B, Hkv, d), dtype=np.float64) if want_state else None
+    rc = _load().linattn_ref_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, N, d,
+                                 int(bool(causal)), int(bool(normalise)), _ptr(S), _ptr(z),
+                                 nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"linattn_ref_fwd rejected its arguments (rc={rc})")
+    return (out, S, z) if want_state else out
+
+
+def ref_decode_step(S: np.ndarray, z: np.ndarray | None, q, k, v, normalise: bool = True):
+    """One decode step; S [B,Hkv,d,d] and z [B,Hkv,d] (fp64) are updated in place.
+
+    q [B,H,d], k/v [B,Hkv,d]; returns out [B,H,d] (fp64).
+    """
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    if z is not None:
+        assert z.dtype == np.float64 and z.flags.c_contiguous
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, d = q.shape
+    Hkv = k.shape[1]
+    out = np.zeros((B, H, d), dtype=np.float64)
+    rc = _load().linattn_ref_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                         B, H, Hkv, d, int(bool(normalise)))
+    if rc != 0:
+        raise ValueError(f"linattn_ref_decode_step rejected its arguments (rc={rc})")
+    return out

@@ -1,0 +1,211 @@
+/*
+ * linattn_ref.c - fp64 CPU oracle for linear attention with the feature map
+ * phi(x) = ELU(x) + 1.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plainly written checker
+ * that the GPU library is compared against.  Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load it.  It shares no code,
+ * header, table or helper with the HIP library, and nothing in the library
+ * may call it.
+ *
+ * What it computes (source: the LinearTile 1.0.0 README on PyPI, section
+ * "How It Works", and the paper it cites there, Katharopoulos et al. 2020,
+ * "Transformers are RNNs"):
+ *   - attention output O = phi(Q) (phi(K)^T V), i.e. the key/value product is
+ *     formed first and then applied to the queries;
+ *   - phi(x) = ELU(x) + 1 with the usual alpha = 1, so phi(x) = x + 1 for
+ *     x > 0 and exp(x) otherwise (always positive);
+ *   - causal form (README "Features" list, the causal-masking item): query t
+ *     only sees keys s <= t.  Written as a running state
+ *         S_t = sum_{s<=t} phi(k_s) v_s^T   (d x d)
+ *         z_t = sum_{s<=t} phi(k_s)         (d)
+ *         o_t = phi(q_t)^T S_t / (phi(q_t) . z_t)   (normalised)
+ *         o_t = phi(q_t)^T S_t                      (normalise == 0)
+ *   - non-causal form: S and z summed over the whole sequence, then applied
+ *     to every query;
+ *   - grouped-query attention (README "Features" list, the GQA item): query
+ *     head h reads key/value head floor(h / (H / Hkv)).
+ *   - decode: one token appended to a carried (S, z); the state is updated
+ *     first and then read, so the new token sees itself (s <= t).
+ *
+ * Readings where the pages are silent: no 1/sqrt(d) scale, no epsilon in the
+ * denominator, d_k = d_v = d, layouts q/out [B][H][N][d], k/v [B][Hkv][N][d],
+ * state [B][Hkv][d][d] with S[i][j] = sum phi(k)_i v_j, z [B][Hkv][d].
+ *
+ * Everything is double precision and follows the recurrence one token at a
+ * time; no blocking, no reordering beyond the definition above.  Threads
+ * split the work over independent (batch, kv head, 16-wide value-column
+ * block) items only; each item runs the plain recurrence for its columns.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define REF_COLBLOCK 16
+
+/* phi(x) = ELU(x) + 1, alpha = 1. */
+double linattn_ref_phi(double x)
+{
+    return x > 0.0 ? x + 1.0 : exp(x);
+}
+
+typedef struct {
+    const double *q, *k, *v;
+    double *out, *state_out, *z_out;
+    int B, H, Hkv, N, d, causal, normalise;
+    int nitems, nthreads, tid;
+} fwd_job;
+
+/* One item: batch b, kv head g, value columns [j0, j0 + w). */
+static void fwd_item(const fwd_job *J, int item)
+{
+    const int d = J->d, N = J->N, G = J->H / J->Hkv;
+    const int ncb = (d + REF_COLBLOCK - 1) / REF_COLBLOCK;
+    const int b = item / (J->Hkv * ncb);
+    const int g = (item / ncb) % J->Hkv;
+    const int j0 = (item % ncb) * REF_COLBLOCK;
+    const int w = (d - j0) < REF_COLBLOCK ? (d - j0) : REF_COLBLOCK;
+
+    double *S = calloc((size_t)d * w, sizeof(double)); /* S[i][jj] */
+    double *z = calloc((size_t)d, sizeof(double));
+    double *f = malloc((size_t)d * sizeof(double));
+    double *p = malloc((size_t)d * sizeof(double));
+
+    const double *kb = J->k + ((size_t)b * J->Hkv + g) * (size_t)N * d;
+    const double *vb = J->v + ((size_t)b * J->Hkv + g) * (size_t)N * d;
+
+    if (!J->causal) {
+        /* Pass over all keys first: S = sum_t phi(k_t) v_t^T, z = sum_t phi(k_t). */
+        for (int t = 0; t < N; ++t) {
+            for (int i = 0; i < d; ++i) f[i] = linattn_ref_phi(kb[(size_t)t * d + i]);
+            for (int i = 0; i < d; ++i) {
+                for (int jj = 0; jj < w; ++jj) S[(size_t)i * w + jj] += f[i] * vb[(size_t)t * d + j0 + jj];
+                z[i] += f[i];
+            }
+        }
+    }
+
+    for (int t = 0; t < N; ++t) {
+        if (J->causal) {
+            /* Absorb token t before reading: query t sees keys s <= t. */
+            for (int i = 0; i < d; ++i) f[i] = linattn_ref_phi(kb[(size_t)t * d + i]);
+            for (int i = 0; i < d; ++i) {
+                for (int jj = 0; jj < w; ++jj) S[(size_t)i * w + jj] += f[i] * vb[(size_t)t * d + j0 + jj];
+                z[i] += f[i];
+            }
+        }
+        for (int h = g * G; h < (g + 1) * G; ++h) {
+            const double *qt = J->q + (((size_t)b * J->H + h) * N + t) * d;
+            double *ot = J->out + (((size_t)b * J->H + h) * N + t) * d;
+            for (int i = 0; i < d; ++i) p[i] = linattn_ref_phi(qt[i]);
+            double den = 0.0;
+            for (int i = 0; i < d; ++i) den += p[i] * z[i];
+            for (int jj = 0; jj < w; ++jj) {
+                double num = 0.0;
+                for (int i = 0; i < d; ++i) num += p[i] * S[(size_t)i * w + jj];
+                ot[j0 + jj] = J->normalise ? num / den : num;
+            }
+        }
+    }
+
+    if (J->state_out) {
+        double *so = J->state_out + ((size_t)b * J->Hkv + g) * (size_t)d * d;
+        for (int i = 0; i < d; ++i)
+            for (int jj = 0; jj < w; ++jj) so[(size_t)i * d + j0 + jj] = S[(size_t)i * w + jj];
+    }
+    if (J->z_out && j0 == 0) {
+        double *zo = J->z_out + ((size_t)b * J->Hkv + g) * (size_t)d;
+        for (int i = 0; i < d; ++i) zo[i] = z[i];
+    }
+    free(S);
+    free(z);
+    free(f);
+    free(p);
+}
+
+static void *fwd_worker(void *arg)
+{
+    const fwd_job *J = (const fwd_job *)arg;
+    for (int item = J->tid; item < J->nitems; item += J->nthreads) fwd_item(J, item);
+    return NULL;
+}
+
+/*
+ * Forward pass.  All arrays are contiguous fp64 host arrays in the layouts
+ * given above.  state_out / z_out may be NULL.  Returns 0, or -1 on invalid
+ * arguments (nothing is written then).
+ */
+int linattn_ref_fwd(const double *q, const double *k, const double *v, double *out,
+                    int B, int H, int Hkv, int N, int d, int causal, int normalise,
+                    double *state_out, double *z_out, int nthreads)
+{
+    if (!q || !k || !v || !out) return -1;
+    if (B < 0 || H <= 0 || Hkv <= 0 || N < 0 || d <= 0 || H % Hkv != 0) return -1;
+    if (B == 0) return 0;
+    const int ncb = (d + REF_COLBLOCK - 1) / REF_COLBLOCK;
+    const int nitems = B * Hkv * ncb;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > nitems) nthreads = nitems;
+
+    fwd_job *jobs = malloc((size_t)nthreads * sizeof(fwd_job));
+    pthread_t *th = malloc((size_t)nthreads * sizeof(pthread_t));
+    for (int t = 0; t < nthreads; ++t) {
+        fwd_job J = {q, k, v, out, state_out, z_out, B, H, Hkv, N, d, causal, normalise,
+                     nitems, nthreads, t};
+        jobs[t] = J;
+    }
+    for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, fwd_worker, &jobs[t]);
+    fwd_worker(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+    free(jobs);
+    free(th);
+    return 0;
+}
+
+/*
+ * One decode step for a batch of B sequences, each with Hkv carried states.
+ * state [B][Hkv][d][d] and z [B][Hkv][d] are updated in place (z may be NULL
+ * when normalise == 0).  q/out are [B][H][d], k/v are [B][Hkv][d].
+ * The state absorbs (k, v) first, then every query head of the group reads it.
+ */
+int linattn_ref_decode_step(double *state, double *z, const double *q, const double *k,
+                            const double *v, double *out, int B, int H, int Hkv, int d,
+                            int normalise)
+{
+    if (!state || !q || !k || !v || !out) return -1;
+    if (normalise && !z) return -1;
+    if (B < 0 || H <= 0 || Hkv <= 0 || d <= 0 || H % Hkv != 0) return -1;
+    const int G = H / Hkv;
+    double *f = malloc((size_t)d * sizeof(double));
+    double *p = malloc((size_t)d * sizeof(double));
+    for (int b = 0; b < B; ++b) {
+        for (int g = 0; g < Hkv; ++g) {
+            double *S = state + ((size_t)b * Hkv + g) * (size_t)d * d;
+            double *zz = z ? z + ((size_t)b * Hkv + g) * (size_t)d : NULL;
+            const double *kt = k + ((size_t)b * Hkv + g) * (size_t)d;
+            const double *vt = v + ((size_t)b * Hkv + g) * (size_t)d;
+            for (int i = 0; i < d; ++i) f[i] = linattn_ref_phi(kt[i]);
+            for (int i = 0; i < d; ++i) {
+                for (int j = 0; j < d; ++j) S[(size_t)i * d + j] += f[i] * vt[j];
+                if (zz) zz[i] += f[i];
+            }
+            for (int h = g * G; h < (g + 1) * G; ++h) {
+                const double *qt = q + ((size_t)b * H + h) * (size_t)d;
+                double *ot = out + ((size_t)b * H + h) * (size_t)d;
+                for (int i = 0; i < d; ++i) p[i] = linattn_ref_phi(qt[i]);
+                double den = 0.0;
+                if (normalise)
+                    for (int i = 0; i < d; ++i) den += p[i] * zz[i];
+                for (int j = 0; j < d; ++j) {
+                    double num = 0.0;
+                    for (int i = 0; i < d; ++i) num += p[i] * S[(size_t)i * d + j];
+                    ot[j] = normalise ? num / den : num;
+                }
+            }
+        }
+    }
+    free(f);
+    free(p);
+    return 0;
+}

@@ -1,0 +1,96 @@
+"""Planted-mistake check for the oracle's pins (CPU only).
+
+Each case copies ``oracle/linattn_ref.c``, plants one plausible slip (a dropped
+term, a wrong index, an exclusive mask, a different GQA head map, a
+transposed state read, ...), compiles the copy into a temporary library and
+runs the oracle pin suite against it in a child process.  The suite must fail
+for every mutant; a mutant that survives means the pins have a blind spot.
+The real oracle source is never modified.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "linattn_ref.c")
+
+CAUSAL_ABSORB = """        if (J->causal) {
+            /* Absorb token t before reading: query t sees keys s <= t. */
+            for (int i = 0; i < d; ++i) f[i] = linattn_ref_phi(kb[(size_t)t * d + i]);
+            for (int i = 0; i < d; ++i) {
+                for (int jj = 0; jj < w; ++jj) S[(size_t)i * w + jj] += f[i] * vb[(size_t)t * d + j0 + jj];
+                z[i] += f[i];
+            }
+        }
+"""
+
+
+def _exclusive_mask(src: str) -> str:
+    """Move the causal absorb after the reads: query t would see only s < t."""
+    assert CAUSAL_ABSORB in src
+    src = src.replace(CAUSAL_ABSORB, "")
+    anchor = """                ot[j0 + jj] = J->normalise ? num / den : num;
+            }
+        }
+"""
+    assert anchor in src
+    return src.replace(anchor, anchor + CAUSAL_ABSORB, 1)
+
+
+DECODE_UPDATE = """            for (int i = 0; i < d; ++i) {
+                for (int j = 0; j < d; ++j) S[(size_t)i * d + j] += f[i] * vt[j];
+                if (zz) zz[i] += f[i];
+            }
+"""
+
+
+def _decode_reads_before_update(src: str) -> str:
+    """Apply the decode update after the queries read the state (exclusive decode)."""
+    assert DECODE_UPDATE in src
+    src = src.replace(DECODE_UPDATE, "")
+    anchor = """                    ot[j] = normalise ? num / den : num;
+                }
+            }
+"""
+    assert anchor in src
+    return src.replace(anchor, anchor + DECODE_UPDATE, 1)
+
+
+MUTANTS = {
+    "phi_drops_plus_one": lambda s: s.replace("x > 0.0 ? x + 1.0 : exp(x)", "x > 0.0 ? x : exp(x)"),
+    "phi_negative_branch_is_plain_elu": lambda s: s.replace("x > 0.0 ? x + 1.0 : exp(x)",
+                                                           "x > 0.0 ? x + 1.0 : exp(x) - 1.0"),
+    "exclusive_causal_mask": _exclusive_mask,
+    "denominator_drops_query": lambda s: s.replace("for (int i = 0; i < d; ++i) den += p[i] * z[i];",
+                                                   "for (int i = 0; i < d; ++i) den += z[i];", 1),
+    "value_column_offset_lost": lambda s: s.replace("vb[(size_t)t * d + j0 + jj]", "vb[(size_t)t * d + jj]"),
+    "interleaved_head_map": lambda s: s.replace(
+        "for (int h = g * G; h < (g + 1) * G; ++h) {\n            const double *qt = J->q",
+        "for (int h = g; h < J->H; h += J->Hkv) {\n            const double *qt = J->q"),
+    "state_read_transposed": lambda s: s.replace("num += p[i] * S[(size_t)i * w + jj];",
+                                                 "num += p[i] * S[(size_t)jj * w + i];"),
+    "noncausal_drops_last_token": lambda s: s.replace(
+        "for (int t = 0; t < N; ++t) {\n            for (int i = 0; i < d; ++i) f[i] = linattn_ref_phi(kb",
+        "for (int t = 0; t < N - 1; ++t) {\n            for (int i = 0; i < d; ++i) f[i] = linattn_ref_phi(kb"),
+    "decode_skips_z_update": lambda s: s.replace("if (zz) zz[i] += f[i];", ""),
+    "decode_reads_before_update": _decode_reads_before_update,
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    src = open(SRC).read()
+    mutated = MUTANTS[name](src)
+    assert mutated != src, f"mutation {name} did not apply"
+    c_path = tmp_path / "mutant.c"
+    so_path = tmp_path / "libmutant.so"
+    c_path.write_text(mutated)
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-w", str(c_path), "-o", str(so_path),
+                    "-lm", "-lpthread"], check=True)
+    env = dict(os.environ, LINATTN_REF_LIB=str(so_path))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived the oracle pins:\n{r.stdout[-2000:]}"
