@@ -1,0 +1,146 @@
+/*
+ * linattn.h - C ABI of liblinattn.so: linear attention with the feature map
+ * phi(x) = ELU(x) + 1 on AMD Instinct MI355X (gfx950).
+ *
+ * Method (LinearTile 1.0.0 README on PyPI, section "How It Works"): the
+ * attention output is O = phi(Q) (phi(K)^T V) with phi(x) = ELU(x) + 1
+ * (alpha = 1, so phi(x) = x + 1 for x > 0 and exp(x) otherwise).  The causal
+ * form (README "Features" list, causal-masking item; Katharopoulos et al. 2020,
+ * "Transformers are RNNs", cited under the README's "Reference" section) is
+ * the running state
+ *     S_t = sum_{s<=t} phi(k_s) v_s^T,   z_t = sum_{s<=t} phi(k_s),
+ *     o_t = phi(q_t)^T S_t / (phi(q_t) . z_t)      (normalise = 1)
+ *     o_t = phi(q_t)^T S_t                         (normalise = 0)
+ * No 1/sqrt(d) scale and no epsilon are applied.  Grouped-query attention
+ * (README "Features" list, GQA item): query head h reads key/value head
+ * floor(h / (H / Hkv)).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or synchronises; it keeps no state
+ *     between calls and is reentrant.
+ *   - Work is enqueued on `stream` (a hipStream_t; 0 = the null stream) and
+ *     the call returns after enqueueing.  Buffers must stay alive until the
+ *     stream has passed that point.
+ *   - Layouts are dense row-major: q and out [B][H][N][d]; k and v
+ *     [B][Hkv][N][d]; a state S [B][Hkv][d][d] with S[i][j] = sum phi(k)_i v_j;
+ *     a normaliser z [B][Hkv][d].
+ *   - q, k, v and out share `dtype` (LINATTN_F32 or LINATTN_BF16).  Arithmetic
+ *     accumulates in fp32 and the state is always fp32.  The output is
+ *     rounded once, to nearest even, when stored.
+ *   - Supported: d in {32, 64, 128}; H % Hkv == 0; every pointer 16-byte
+ *     aligned; out must not alias q, k or v.
+ *   - Errors: arguments are checked before anything is enqueued; a negative
+ *     LINATTN_ERR_* code is returned and nothing is launched.  A failed
+ *     kernel launch returns LINATTN_ERR_HIP.  The library never prints,
+ *     aborts or throws.  NaN / Inf inputs are not checked and propagate.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LINATTN_ABI_VERSION 1
+
+enum { LINATTN_F32 = 0, LINATTN_BF16 = 1 };
+
+enum {
+    LINATTN_OK = 0,
+    LINATTN_ERR_NULL = -1,        /* a required pointer is NULL                       */
+    LINATTN_ERR_SHAPE = -2,       /* B, H, Hkv, N or d out of range, or H % Hkv != 0  */
+    LINATTN_ERR_DTYPE = -3,       /* dtype is not LINATTN_F32 / LINATTN_BF16          */
+    LINATTN_ERR_UNSUPPORTED = -4, /* d or chunk not supported by the kernels          */
+    LINATTN_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required       */
+    LINATTN_ERR_HIP = -6,         /* a HIP launch or runtime call failed              */
+    LINATTN_ERR_ALIGN = -7        /* a pointer is not 16-byte aligned                 */
+};
+
+/*
+ * linattn_fwd - forward pass over whole sequences.
+ *
+ * Computes `out` from q, k, v as stated at the top of this file: causal = 1
+ * gives the running-state (s <= t) form; causal = 0 the non-causal form
+ * O = phi(Q) (phi(K)^T V) over all N keys (README "How It Works"; the
+ * normaliser is then phi(q_t) . sum_s phi(k_s)).
+ *
+ *   q, k, v     device, dtype, layouts above; read only.
+ *   out         device, dtype, [B][H][N][d]; fully written.
+ *   B, H, Hkv   batch, query heads, key/value heads (B >= 0, H % Hkv == 0).
+ *   N           tokens per sequence (N >= 0; any N, ragged tails are masked).
+ *   d           head dimension, 32, 64 or 128.
+ *   causal      1 causal, 0 non-causal.
+ *   normalise   1 divide by phi(q_t) . z_t, 0 return the numerator only.
+ *   dtype       LINATTN_F32 or LINATTN_BF16.
+ *   state_out   nullable device fp32 [B][Hkv][d][d]: receives S_N (all N keys).
+ *   z_out       nullable device fp32 [B][Hkv][d]: receives z_N.
+ *   chunk       tokens per intra-chunk block: 0 = automatic, else 32, 64, 128
+ *               or 256.  It changes only the order of summation.
+ *   workspace   device scratch of at least linattn_fwd_workspace_bytes(...)
+ *               bytes (may be NULL when that size is 0); its contents on
+ *               entry do not matter and are clobbered.
+ *   stream      HIP stream to enqueue on.
+ * Returns LINATTN_OK or a LINATTN_ERR_* code.  B == 0 or N == 0 is a valid
+ * no-op except that state_out / z_out, if given, are zero-filled.
+ */
+int linattn_fwd(const void *q, const void *k, const void *v, void *out,
+                int B, int H, int Hkv, int N, int d, int causal, int normalise, int dtype,
+                float *state_out, float *z_out, int chunk,
+                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * linattn_fwd_workspace_bytes - scratch size linattn_fwd needs for these
+ * arguments (0 when none).  Returns (size_t)-1 for invalid arguments.
+ * The scratch holds one fp32 partial state and normaliser, d*(d+1) floats,
+ * per (batch, kv head, sequence segment).
+ */
+size_t linattn_fwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int causal, int dtype,
+                                   int chunk);
+
+/*
+ * linattn_fwd_plan - the launch plan linattn_fwd would use (host only, no
+ * GPU work): chunk size and number of sequence segments per (batch, kv head).
+ * Either output pointer may be NULL.  Returns LINATTN_OK or an error code.
+ */
+int linattn_fwd_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int chunk,
+                     int *chunk_out, int *segments_out);
+
+/*
+ * linattn_decode_step - append one token to every carried state and emit
+ * the outputs for it (README "Features" list: KV cache reuse and fast
+ * decoding; the fixed-size state replaces a growing key/value cache).
+ *
+ * For every batch b and kv head g, in place:
+ *     S[b][g] += phi(k[b][g]) v[b][g]^T,   z[b][g] += phi(k[b][g]),
+ * and then for every query head h of the group
+ *     out[b][h] = phi(q[b][h])^T S[b][g] / (phi(q[b][h]) . z[b][g])
+ * (or the numerator only when normalise == 0).  The update happens before
+ * the read, so the new token attends to itself (s <= t), and a decode step
+ * after a prefill of N tokens equals row N of a prefill of N + 1 tokens.
+ *
+ *   state   device fp32 [B][Hkv][d][d], read and written in place.
+ *   z       device fp32 [B][Hkv][d], read and written in place; may be NULL
+ *           only when normalise == 0 (then it is neither read nor written).
+ *   q, out  device, dtype, [B][H][d];  k, v  device, dtype, [B][Hkv][d].
+ *   out must not alias state, z, q, k or v.
+ * Returns LINATTN_OK or a LINATTN_ERR_* code.
+ */
+int linattn_decode_step(float *state, float *z, const void *q, const void *k, const void *v,
+                        void *out, int B, int H, int Hkv, int d, int normalise, int dtype,
+                        hipStream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *linattn_status_string(int status);
+
+/* LINATTN_ABI_VERSION of the built library. */
+int linattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -1,0 +1,874 @@
+// linattn.hip - gfx950 (MI355X) kernels and the C ABI of liblinattn.so.
+//
+// Linear attention with phi(x) = ELU(x) + 1 (LinearTile 1.0.0 README, "How It
+// Works": O = phi(Q) (phi(K)^T V), key/value product first).  Causal rows use
+// the running state S_t = sum_{s<=t} phi(k_s) v_s^T and z_t = sum_{s<=t}
+// phi(k_s) (README "Features": causal masking without a quadratic buffer;
+// Katharopoulos et al. 2020, cited in the README's "Reference" section).
+//
+// Kernel family (one workgroup = 4 wave64s = 256 threads everywhere):
+//   seg_totals    per (sequence, segment): T_p = phi(K_p)^T V_p and sum phi(K_p)
+//                 on MFMA, written as fp32 partials (causal: all segments but
+//                 the last; non-causal: all segments).
+//   seg_scan      inclusive prefix of the partials along the segments (causal),
+//                 or their sum (non-causal).
+//   causal_chunks per (sequence, segment): walks the segment in chunks of C
+//                 tokens.  Per chunk, for every query tile of 32 rows:
+//                   O^T = V^T (M . phi(K) phi(Q)^T) + S_prev^T phi(Q)^T
+//                 (intra-chunk masked term plus the carried-state term, both
+//                 on MFMA), then S += phi(K)^T V on MFMA.  The d x d fp32 state
+//                 lives in MFMA accumulators spread over the four waves; the
+//                 waves see it through an LDS copy refreshed once per chunk.
+//   noncausal_apply  O = phi(Q) S / phi(Q) . z with the summed S, z.
+//   decode_step   one token: S += phi(k) v^T, z += phi(k), then G query heads
+//                 read the updated state.  Bandwidth bound, plain fp32 VALU.
+//
+// MFMA shapes: bf16 uses v_mfma_f32_32x32x16_bf16, fp32 uses
+// v_mfma_f32_32x32x2_f32 (true fp32 products).  Every operand fragment holds,
+// per lane, 8 values of one row/column for one "K-block" of 16 reduction
+// indices; which reduction index a (half-wave, slot) pair holds is free as
+// long as both operands agree, and the kernels exploit that to feed one
+// product's accumulator layout straight into the next product.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "linattn.h"
+#include "linattn_plan.h"
+
+namespace {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+// phi(x) = ELU(x) + 1 (alpha = 1): x + 1 for x > 0, exp(x) otherwise.
+__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+// ------------------------------------------------------------------ types
+
+template <typename E> struct Vt;
+template <> struct Vt<bf16> {
+    using v8 = bf16x8;  // 8 consecutive elements: one MFMA operand fragment
+    using v4 = bf16x4;
+    using g16 = bf16x8; // one 16-byte group
+    static constexpr int U = 8;  // elements per 16 bytes
+};
+template <> struct Vt<float> {
+    using v8 = f32x8;
+    using v4 = f32x4;
+    using g16 = f32x4;
+    static constexpr int U = 4;
+};
+
+// acc += A(32 x 16) * B(16 x 32) for one K-block of 16.
+__device__ __forceinline__ void mma(f32x16 &acc, const bf16x8 &a, const bf16x8 &b)
+{
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16 &acc, const f32x8 &a, const f32x8 &b)
+{
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 cat(const bf16x4 &a, const bf16x4 &b)
+{
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ f32x8 cat(const f32x4 &a, const f32x4 &b)
+{
+    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+template <typename E> __device__ __forceinline__ typename Vt<E>::v8 cvt8(const float *x);
+template <> __device__ __forceinline__ bf16x8 cvt8<bf16>(const float *x)
+{
+    f32x8 f{x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+    return __builtin_convertvector(f, bf16x8);
+}
+template <> __device__ __forceinline__ f32x8 cvt8<float>(const float *x)
+{
+    return f32x8{x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+}
+template <typename E> __device__ __forceinline__ typename Vt<E>::v4 cvt4(f32x4 x);
+template <> __device__ __forceinline__ bf16x4 cvt4<bf16>(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
+template <> __device__ __forceinline__ f32x4 cvt4<float>(f32x4 x) { return x; }
+
+// ---------------------------------------------------------- LDS tiles
+//
+// Tiles are stored row-major with 16-byte groups permuted inside each row:
+// element (r, c) lives at r * COLS + (c ^ (sig(r) * U)).  The XOR moves whole
+// 16-byte groups, so 4- and 8-element runs that start on a 4-aligned column
+// stay contiguous (fp32: an 8-run spans two groups and is read as two).
+
+template <typename E, int COLS>
+struct LdsTile {
+    E *p;
+    static constexpr int U = Vt<E>::U;
+    __device__ __forceinline__ int at(int r, int c, int sig) const { return r * COLS + (c ^ (sig * U)); }
+    __device__ __forceinline__ typename Vt<E>::v8 read8(int r, int c, int sig) const
+    {
+        if constexpr (U == 8) {
+            return *reinterpret_cast<const bf16x8 *>(p + at(r, c, sig));
+        } else {
+            return cat(*reinterpret_cast<const f32x4 *>(p + at(r, c, sig)),
+                       *reinterpret_cast<const f32x4 *>(p + at(r, c + 4, sig)));
+        }
+    }
+    __device__ __forceinline__ typename Vt<E>::v4 read4(int r, int c, int sig) const
+    {
+        return *reinterpret_cast<const typename Vt<E>::v4 *>(p + at(r, c, sig));
+    }
+    __device__ __forceinline__ void write4(int r, int c, int sig, typename Vt<E>::v4 x) const
+    {
+        *reinterpret_cast<typename Vt<E>::v4 *>(p + at(r, c, sig)) = x;
+    }
+    __device__ __forceinline__ void write16(int r, int c, int sig, typename Vt<E>::g16 x) const
+    {
+        *reinterpret_cast<typename Vt<E>::g16 *>(p + at(r, c, sig)) = x;
+    }
+    __device__ __forceinline__ void write1(int r, int c, int sig, E x) const { p[at(r, c, sig)] = x; }
+};
+
+// Shapes and swizzles shared by the chunk kernels.
+template <typename T, int D, int C>
+struct Geo {
+    using E = T;
+    static constexpr int U = Vt<E>::U;       // elements per 16 bytes (== per global vector load)
+    static constexpr int DT = D / 32;        // 32-wide feature tiles
+    static constexpr int CT = C / 32;        // 32-row token tiles per chunk
+    static constexpr int KBD = D / 16;       // K-blocks over features
+    static constexpr int KBC = C / 16;       // K-blocks over chunk tokens
+    static constexpr int NST = DT * DT;      // 32x32 state tiles
+    static constexpr int MAXST = (NST + 3) / 4;  // state tiles per wave
+    static constexpr int GPR = D / U;        // 16-byte groups per token row
+    static constexpr int NGRP = C * GPR;     // 16-byte groups per chunk per tensor
+    static constexpr int LDV = (NGRP + kThreads - 1) / kThreads;  // groups per thread
+    // swizzles: token-major tiles (rows = tokens or state columns, D columns)
+    __device__ static int sig_rowD(int r) { return r % (D / U); }
+    // feature-major tiles (rows = features, C token columns)
+    __device__ static int sig_rowC(int f) { return (f + f / U) % (C / U); }
+};
+
+// Loads the 16-byte groups of one chunk of a [N][D] sequence (zeros past N).
+template <typename T, int D, int C, int L>
+__device__ __forceinline__ void load_chunk(typename Vt<T>::g16 (&r)[L], const T *base, int t0, int N, int tid)
+{
+    using G = Geo<T, D, C>;
+    static_assert(L == G::LDV, "register array size");
+#pragma unroll
+    for (int l = 0; l < G::LDV; ++l) {
+        const int e = tid + l * kThreads;
+        const int t = e / G::GPR, q = e % G::GPR;
+        typename Vt<T>::g16 x = {};
+        if (e < G::NGRP && t0 + t < N)
+            x = *reinterpret_cast<const typename Vt<T>::g16 *>(base + (size_t)(t0 + t) * D + q * G::U);
+        r[l] = x;
+    }
+}
+
+// Writes a staged chunk to LDS: phi(K) row-major (optional), phi(K)^T, V^T.
+// Tokens at or past N get phi(k) = 0 so that they add nothing to any sum.
+template <typename T, int D, int C, bool ROWK, int L>
+__device__ __forceinline__ void stage_chunk(const typename Vt<T>::g16 (&kr)[L], const typename Vt<T>::g16 (&vr)[L],
+                                            LdsTile<T, D> sK, LdsTile<T, C> sKT, LdsTile<T, C> sVT,
+                                            int t0, int N, int tid)
+{
+    using G = Geo<T, D, C>;
+    static_assert(L == G::LDV, "register array size");
+#pragma unroll
+    for (int l = 0; l < G::LDV; ++l) {
+        const int e = tid + l * kThreads;
+        if (e < G::NGRP) {
+            const int t = e / G::GPR, q = e % G::GPR;
+            const bool valid = t0 + t < N;
+            typename Vt<T>::g16 fk;
+#pragma unroll
+            for (int i = 0; i < G::U; ++i) fk[i] = valid ? (T)phi((float)kr[l][i]) : (T)0.f;
+            if constexpr (ROWK) sK.write16(t, q * G::U, G::sig_rowD(t), fk);
+#pragma unroll
+            for (int i = 0; i < G::U; ++i) {
+                const int f = q * G::U + i;
+                sKT.write1(f, t, G::sig_rowC(f), fk[i]);
+                sVT.write1(f, t, G::sig_rowC(f), vr[l][i]);
+            }
+        }
+    }
+}
+
+// S tile (it, jt) += phi(K)^T V over the chunk; optionally the column sums
+// of phi(K) for features it*32 + n (returned per lane, both half-waves equal).
+template <typename T, int D, int C>
+__device__ __forceinline__ float state_update(f32x16 &acc, int it, int jt, bool want_z,
+                                              LdsTile<T, C> sKT, LdsTile<T, C> sVT, int h, int n)
+{
+    using G = Geo<T, D, C>;
+    const int fi = it * 32 + n, fj = jt * 32 + n;
+    float zs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < G::KBC; ++kb) {
+        const auto a = sKT.read8(fi, kb * 16 + h * 8, G::sig_rowC(fi));
+        const auto b = sVT.read8(fj, kb * 16 + h * 8, G::sig_rowC(fj));
+        mma(acc, a, b);
+        if (want_z) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) zs += (float)a[s];
+        }
+    }
+    if (want_z) zs += __shfl_xor(zs, 32);
+    return zs;
+}
+
+// -------------------------------------------------------------- seg_totals
+
+template <typename T, int D, int C>
+__global__ __launch_bounds__(kThreads) void k_seg_totals(const T *__restrict__ k, const T *__restrict__ v,
+                                                         float *__restrict__ ws, int N, int seg_len,
+                                                         int nslots)
+{
+    using G = Geo<T, D, C>;
+    __shared__ __attribute__((aligned(16))) T smKT[D * C];
+    __shared__ __attribute__((aligned(16))) T smVT[D * C];
+    LdsTile<T, D> sK{nullptr};
+    LdsTile<T, C> sKT{smKT}, sVT{smVT};
+
+    const int seq = blockIdx.x / nslots, p = blockIdx.x % nslots;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
+    const T *kb = k + (size_t)seq * N * D;
+    const T *vb = v + (size_t)seq * N * D;
+    const int s0 = p * seg_len, s1 = min(N, s0 + seg_len);
+    const int nch = (s1 - s0 + C - 1) / C;
+
+    f32x16 acc[G::MAXST];
+    float zacc[G::MAXST];
+#pragma unroll
+    for (int i = 0; i < G::MAXST; ++i) {
+        acc[i] = f32x16{};
+        zacc[i] = 0.f;
+    }
+    typename Vt<T>::g16 kr[G::LDV], vr[G::LDV];
+    // Walk the segment backwards: the main pass then starts on the chunks
+    // read most recently, which are the likeliest still to be cached.
+    load_chunk<T, D, C>(kr, kb, s0 + (nch - 1) * C, N, tid);
+    load_chunk<T, D, C>(vr, vb, s0 + (nch - 1) * C, N, tid);
+    for (int c = nch - 1; c >= 0; --c) {
+        const int t0 = s0 + c * C;
+        stage_chunk<T, D, C, false>(kr, vr, sK, sKT, sVT, t0, N, tid);
+        __syncthreads();
+        if (c > 0) {
+            load_chunk<T, D, C>(kr, kb, t0 - C, N, tid);
+            load_chunk<T, D, C>(vr, vb, t0 - C, N, tid);
+        }
+#pragma unroll
+        for (int i = 0; i < G::MAXST; ++i) {
+            const int st = w + 4 * i;
+            if (st < G::NST) {
+                const int it = st / G::DT, jt = st % G::DT;
+                zacc[i] += state_update<T, D, C>(acc[i], it, jt, jt == 0, sKT, sVT, h, n);
+            }
+        }
+        __syncthreads();
+    }
+    float *out = ws + ((size_t)seq * nslots + p) * (size_t)D * (D + 1);
+#pragma unroll
+    for (int i = 0; i < G::MAXST; ++i) {
+        const int st = w + 4 * i;
+        if (st < G::NST) {
+            const int it = st / G::DT, jt = st % G::DT;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = it * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                out[(size_t)row * D + jt * 32 + n] = acc[i][r];
+            }
+            if (jt == 0 && h == 0) out[(size_t)D * D + it * 32 + n] = zacc[i];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- seg_scan
+//
+// ws holds nslots partials of E = D*D + D floats per sequence.  mode 0:
+// inclusive prefix along the slots, in place.  mode 1: the sum, written to
+// slot 0 and, when given, to state_out / z_out.
+__global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, int nslots, int D, int mode,
+                                                       float *__restrict__ state_out, float *__restrict__ z_out)
+{
+    const int E = D * D + D;
+    const int seq = blockIdx.y;
+    const int e = blockIdx.x * kThreads + threadIdx.x;
+    if (e >= E) return;
+    float *base = ws + (size_t)seq * nslots * E + e;
+    float acc = 0.f;
+    for (int p = 0; p < nslots; ++p) {
+        acc += base[(size_t)p * E];
+        if (mode == 0) base[(size_t)p * E] = acc;
+    }
+    if (mode == 1) {
+        base[0] = acc;
+        if (e < D * D) {
+            if (state_out) state_out[(size_t)seq * D * D + e] = acc;
+        } else if (z_out) {
+            z_out[(size_t)seq * D + (e - D * D)] = acc;
+        }
+    }
+}
+
+// ----------------------------------------------------------- causal_chunks
+
+// Unit i of wave w (a unit is one query head and one 32-row query tile of
+// the chunk).  Snake order pairs early and late tiles on the same wave so
+// that the causal triangle's work is spread evenly.
+__device__ __forceinline__ int unit_of(int w, int i) { return 8 * (i >> 1) + ((i & 1) ? 7 - w : w); }
+
+template <typename T, int D, int C>
+__global__ __launch_bounds__(kThreads) void k_causal_chunks(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ out,
+    const float *__restrict__ ws, float *__restrict__ state_out, float *__restrict__ z_out,
+    int H, int Hkv, int N, int G, int P, int seg_len, int normalise)
+{
+    using Gm = Geo<T, D, C>;
+    using v8 = typename Vt<T>::v8;
+    using g16 = typename Vt<T>::g16;
+    constexpr int U = Gm::U;
+    constexpr int QV = 8 / U;  // 16-byte groups per 8-element fragment
+
+    __shared__ __attribute__((aligned(16))) T smK[C * D];
+    __shared__ __attribute__((aligned(16))) T smKT[D * C];
+    __shared__ __attribute__((aligned(16))) T smVT[D * C];
+    __shared__ __attribute__((aligned(16))) T smST[D * D];
+    __shared__ float smZ[D];
+    LdsTile<T, D> sK{smK}, sST{smST};
+    LdsTile<T, C> sKT{smKT}, sVT{smVT};
+
+    const int seq = blockIdx.x / P, p = blockIdx.x % P;
+    const int b = seq / Hkv, gk = seq % Hkv;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
+    const T *kb = k + (size_t)seq * N * D;
+    const T *vb = v + (size_t)seq * N * D;
+    const T *qb = q + ((size_t)b * H + (size_t)gk * G) * N * D;  // head g of the group: + g * N * D
+    T *ob = out + ((size_t)b * H + (size_t)gk * G) * N * D;
+    const int s0 = p * seg_len, s1 = min(N, s0 + seg_len);
+    const int nch = (s1 - s0 + C - 1) / C;
+    const int NU = G * Gm::CT;
+
+    // ---- the state this segment starts from
+    f32x16 S[Gm::MAXST];
+    float zr[Gm::MAXST];
+    const float *init = p > 0 ? ws + ((size_t)seq * (P - 1) + (p - 1)) * (size_t)D * (D + 1) : nullptr;
+#pragma unroll
+    for (int i = 0; i < Gm::MAXST; ++i) {
+        S[i] = f32x16{};
+        zr[i] = 0.f;
+        const int st = w + 4 * i;
+        if (st < Gm::NST && init) {
+            const int it = st / Gm::DT, jt = st % Gm::DT;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[i][r] = init[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n];
+            if (jt == 0) zr[i] = init[(size_t)D * D + it * 32 + n];
+        }
+    }
+    // Publish S^T and z to LDS.
+    auto publish_state = [&]() {
+#pragma unroll
+        for (int i = 0; i < Gm::MAXST; ++i) {
+            const int st = w + 4 * i;
+            if (st < Gm::NST) {
+                const int it = st / Gm::DT, jt = st % Gm::DT;
+                const int row = jt * 32 + n;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    f32x4 x{S[i][4 * q4], S[i][4 * q4 + 1], S[i][4 * q4 + 2], S[i][4 * q4 + 3]};
+                    sST.write4(row, it * 32 + 8 * q4 + 4 * h, Gm::sig_rowD(row), cvt4<T>(x));
+                }
+                if (jt == 0 && h == 0) smZ[it * 32 + n] = zr[i];
+            }
+        }
+    };
+    publish_state();
+
+    // ---- prefetch of the first chunk
+    g16 kr[Gm::LDV], vr[Gm::LDV];
+    g16 qr[Gm::KBD * QV];  // raw q of this wave's first unit, fetched one chunk ahead
+    auto load_q = [&](auto &dst, int u, int t0) {
+        const int g = u / Gm::CT, r = u % Gm::CT;
+        const int t = t0 + r * 32 + n;
+        const T *src = qb + (size_t)g * N * D + (size_t)t * D;
+#pragma unroll
+        for (int kb = 0; kb < Gm::KBD; ++kb) {
+#pragma unroll
+            for (int j = 0; j < QV; ++j) {
+                g16 x = {};
+                if (t < N) x = *reinterpret_cast<const g16 *>(src + kb * 16 + h * 8 + j * U);
+                dst[kb * QV + j] = x;
+            }
+        }
+    };
+    if (nch > 0) {
+        load_chunk<T, D, C>(kr, kb, s0, N, tid);
+        load_chunk<T, D, C>(vr, vb, s0, N, tid);
+        if (unit_of(w, 0) < NU) load_q(qr, unit_of(w, 0), s0);
+    }
+
+    for (int c = 0; c < nch; ++c) {
+        const int t0 = s0 + c * C;
+        stage_chunk<T, D, C, true>(kr, vr, sK, sKT, sVT, t0, N, tid);
+        __syncthreads();
+        if (c + 1 < nch) {
+            load_chunk<T, D, C>(kr, kb, t0 + C, N, tid);
+            load_chunk<T, D, C>(vr, vb, t0 + C, N, tid);
+        }
+
+        // ---- query tiles of this chunk
+        for (int ui = 0;; ++ui) {
+            const int u = unit_of(w, ui);
+            if (u >= NU) break;
+            const int g = u / Gm::CT, r = u % Gm::CT;
+            if (t0 + r * 32 >= N) continue;  // tile entirely past the end
+            g16 qx[Gm::KBD * QV];
+            if (ui > 0) load_q(qx, u, t0);
+            // phi(q) fragments: lane (h, n) holds query n, features kb*16 + 8h + s.
+            v8 qf[Gm::KBD];
+            float dq = 0.f;  // phi(q) . z over this half-wave's features
+#pragma unroll
+            for (int kb = 0; kb < Gm::KBD; ++kb) {
+                float f[8];
+#pragma unroll
+                for (int j = 0; j < QV; ++j)
+#pragma unroll
+                    for (int s = 0; s < U; ++s) f[j * U + s] = phi((float)(ui > 0 ? qx : qr)[kb * QV + j][s]);
+                qf[kb] = cvt8<T>(f);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) dq += (float)qf[kb][s] * smZ[kb * 16 + h * 8 + s];
+            }
+            // Next chunk's first unit can be fetched now that qr is consumed.
+            if (ui == 0 && c + 1 < nch) load_q(qr, u, t0 + C);
+
+            f32x16 O[Gm::DT];
+#pragma unroll
+            for (int ct = 0; ct < Gm::DT; ++ct) O[ct] = f32x16{};
+            float dsum = 0.f;
+            for (int kt = 0; kt <= r; ++kt) {
+                // Pt[key][query] = phi(K) phi(Q)^T for key tile kt, query tile r.
+                f32x16 Pt = f32x16{};
+                const int krow = kt * 32 + n;
+#pragma unroll
+                for (int kb = 0; kb < Gm::KBD; ++kb) mma(Pt, sK.read8(krow, kb * 16 + h * 8, Gm::sig_rowD(krow)), qf[kb]);
+                // Accumulator reg i holds key 8(i/4) + 4h + i%4 of tile kt for query n.
+                float pv[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int kl = 8 * (i / 4) + 4 * h + (i % 4);
+                    pv[i] = (kt == r && kl > n) ? 0.f : Pt[i];
+                }
+                v8 pb0 = cvt8<T>(pv), pb1 = cvt8<T>(pv + 8);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) dsum += (float)pb0[s] + (float)pb1[s];
+                // O^T[feature][query] += V^T[feature][keys] Pt[keys][query]; the key held
+                // in slot s of K-block kb2 is 16 kb2 + 8 (s/4) + 4h + s%4.
+#pragma unroll
+                for (int ct = 0; ct < Gm::DT; ++ct) {
+                    const int f = ct * 32 + n;
+                    const int sg = Gm::sig_rowC(f);
+                    mma(O[ct], cat(sVT.read4(f, kt * 32 + 4 * h, sg), sVT.read4(f, kt * 32 + 8 + 4 * h, sg)), pb0);
+                    mma(O[ct], cat(sVT.read4(f, kt * 32 + 16 + 4 * h, sg), sVT.read4(f, kt * 32 + 24 + 4 * h, sg)), pb1);
+                }
+            }
+            // Carried state: O^T += S^T phi(Q)^T.
+#pragma unroll
+            for (int ct = 0; ct < Gm::DT; ++ct) {
+                const int j = ct * 32 + n;
+#pragma unroll
+                for (int kb = 0; kb < Gm::KBD; ++kb) mma(O[ct], sST.read8(j, kb * 16 + h * 8, Gm::sig_rowD(j)), qf[kb]);
+            }
+            float den = dsum + dq;
+            den += __shfl_xor(den, 32);
+            const float inv = normalise ? 1.f / den : 1.f;
+            const int t = t0 + r * 32 + n;
+            if (t < N) {
+                T *dst = ob + (size_t)g * N * D + (size_t)t * D;
+#pragma unroll
+                for (int ct = 0; ct < Gm::DT; ++ct)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        f32x4 x{O[ct][4 * q4] * inv, O[ct][4 * q4 + 1] * inv, O[ct][4 * q4 + 2] * inv,
+                                O[ct][4 * q4 + 3] * inv};
+                        *reinterpret_cast<typename Vt<T>::v4 *>(dst + ct * 32 + 8 * q4 + 4 * h) = cvt4<T>(x);
+                    }
+            }
+        }
+
+        // ---- S += phi(K)^T V, z += column sums of phi(K)
+#pragma unroll
+        for (int i = 0; i < Gm::MAXST; ++i) {
+            const int st = w + 4 * i;
+            if (st < Gm::NST) {
+                const int it = st / Gm::DT, jt = st % Gm::DT;
+                zr[i] += state_update<T, D, C>(S[i], it, jt, jt == 0, sKT, sVT, h, n);
+            }
+        }
+        __syncthreads();
+        publish_state();
+    }
+
+    if (p == P - 1 && state_out) {
+        float *so = state_out + (size_t)seq * D * D;
+#pragma unroll
+        for (int i = 0; i < Gm::MAXST; ++i) {
+            const int st = w + 4 * i;
+            if (st < Gm::NST) {
+                const int it = st / Gm::DT, jt = st % Gm::DT;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) so[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n] = S[i][r];
+            }
+        }
+    }
+    if (p == P - 1 && z_out) {
+#pragma unroll
+        for (int i = 0; i < Gm::MAXST; ++i) {
+            const int st = w + 4 * i;
+            if (st < Gm::NST && st % Gm::DT == 0 && h == 0) z_out[(size_t)seq * D + (st / Gm::DT) * 32 + n] = zr[i];
+        }
+    }
+}
+
+// --------------------------------------------------------- noncausal_apply
+//
+// One workgroup per (sequence, block of 128 tokens); every wave takes whole
+// query tiles (head, 32 rows).  S and z are the sums left in slot 0 of ws.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restrict__ q, T *__restrict__ out,
+                                                              const float *__restrict__ ws, int nslots, int H,
+                                                              int Hkv, int N, int G, int nblk, int normalise)
+{
+    constexpr int TQ = 128;
+    using Gm = Geo<T, D, 32>;
+    using v8 = typename Vt<T>::v8;
+    using g16 = typename Vt<T>::g16;
+    constexpr int U = Gm::U;
+    constexpr int QV = 8 / U;
+    __shared__ __attribute__((aligned(16))) T smST[D * D];
+    __shared__ float smZ[D];
+    LdsTile<T, D> sST{smST};
+
+    const int seq = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+    const int b = seq / Hkv, gk = seq % Hkv;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
+    const float *S = ws + (size_t)seq * nslots * (size_t)D * (D + 1);
+    // S^T into LDS: element (row j, col i) = S[i][j].
+    for (int e = tid; e < D * D; e += kThreads) {
+        const int i = e / D, j = e % D;
+        smST[sST.at(j, i, Gm::sig_rowD(j))] = (T)S[e];
+    }
+    for (int e = tid; e < D; e += kThreads) smZ[e] = S[(size_t)D * D + e];
+    __syncthreads();
+
+    const T *qb = q + ((size_t)b * H + (size_t)gk * G) * N * D;
+    T *ob = out + ((size_t)b * H + (size_t)gk * G) * N * D;
+    const int NU = G * (TQ / 32);
+    for (int u = w; u < NU; u += 4) {
+        const int g = u / (TQ / 32), r = u % (TQ / 32);
+        const int t = blk * TQ + r * 32 + n;
+        if (blk * TQ + r * 32 >= N) continue;
+        const T *src = qb + (size_t)g * N * D + (size_t)t * D;
+        v8 qf[Gm::KBD];
+        float dq = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < Gm::KBD; ++kb) {
+            float f[8];
+#pragma unroll
+            for (int j = 0; j < QV; ++j) {
+                g16 x = {};
+                if (t < N) x = *reinterpret_cast<const g16 *>(src + kb * 16 + h * 8 + j * U);
+#pragma unroll
+                for (int s = 0; s < U; ++s) f[j * U + s] = phi((float)x[s]);
+            }
+            qf[kb] = cvt8<T>(f);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) dq += (float)qf[kb][s] * smZ[kb * 16 + h * 8 + s];
+        }
+        f32x16 O[Gm::DT];
+#pragma unroll
+        for (int ct = 0; ct < Gm::DT; ++ct) {
+            O[ct] = f32x16{};
+            const int j = ct * 32 + n;
+#pragma unroll
+            for (int kb = 0; kb < Gm::KBD; ++kb) mma(O[ct], sST.read8(j, kb * 16 + h * 8, Gm::sig_rowD(j)), qf[kb]);
+        }
+        dq += __shfl_xor(dq, 32);
+        const float inv = normalise ? 1.f / dq : 1.f;
+        if (t < N) {
+            T *dst = ob + (size_t)g * N * D + (size_t)t * D;
+#pragma unroll
+            for (int ct = 0; ct < Gm::DT; ++ct)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    f32x4 x{O[ct][4 * q4] * inv, O[ct][4 * q4 + 1] * inv, O[ct][4 * q4 + 2] * inv,
+                            O[ct][4 * q4 + 3] * inv};
+                    *reinterpret_cast<typename Vt<T>::v4 *>(dst + ct * 32 + 8 * q4 + 4 * h) = cvt4<T>(x);
+                }
+        }
+    }
+}
+
+// ------------------------------------------------------------- decode_step
+//
+// One workgroup per (batch, kv head).  Thread tid owns the float4 column
+// group tid % (D/4) of rows tid / (D/4) + RG * i: it reads those state
+// elements once, adds phi(k)_i v_j, writes them back and keeps partial
+// phi(q)^T S sums for up to 4 query heads at a time.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ state, float *__restrict__ z,
+                                                          const T *__restrict__ q, const T *__restrict__ k,
+                                                          const T *__restrict__ v, T *__restrict__ out, int H,
+                                                          int Hkv, int G, int normalise)
+{
+    constexpr int C4 = D / 4;            // float4 groups per row
+    constexpr int RG = kThreads / C4;    // row groups
+    constexpr int NV = D / RG;           // rows per thread
+    constexpr int HB = 4;                // query heads per pass
+    __shared__ float sk[D], sv[D], sz[D];
+    __shared__ float sq[HB][D];
+    __shared__ __attribute__((aligned(16))) float red[RG][HB][D];
+
+    const int seq = blockIdx.x;
+    const int b = seq / Hkv, gk = seq % Hkv;
+    const int tid = threadIdx.x, c4 = tid % C4, rg = tid / C4;
+    float *Sb = state + (size_t)seq * D * D;
+    if (tid < D) {
+        const float fk = phi((float)k[(size_t)seq * D + tid]);
+        sk[tid] = fk;
+        sv[tid] = (float)v[(size_t)seq * D + tid];
+        if (normalise) {
+            const float zn = z[(size_t)seq * D + tid] + fk;
+            z[(size_t)seq * D + tid] = zn;
+            sz[tid] = zn;
+        }
+    }
+    __syncthreads();
+    f32x4 Sr[NV];
+    const f32x4 vv{sv[4 * c4], sv[4 * c4 + 1], sv[4 * c4 + 2], sv[4 * c4 + 3]};
+#pragma unroll
+    for (int i = 0; i < NV; ++i) Sr[i] = *reinterpret_cast<const f32x4 *>(Sb + (size_t)(rg + RG * i) * D + 4 * c4);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const float fk = sk[rg + RG * i];
+        Sr[i] += fk * vv;
+        *reinterpret_cast<f32x4 *>(Sb + (size_t)(rg + RG * i) * D + 4 * c4) = Sr[i];
+    }
+    for (int g0 = 0; g0 < G; g0 += HB) {
+        const int nh = min(HB, G - g0);
+        for (int e = tid; e < nh * D; e += kThreads) {
+            const int hh = e / D, i = e % D;
+            sq[hh][i] = phi((float)q[((size_t)b * H + (size_t)gk * G + g0 + hh) * D + i]);
+        }
+        __syncthreads();
+        for (int hh = 0; hh < nh; ++hh) {
+            f32x4 acc{};
+#pragma unroll
+            for (int i = 0; i < NV; ++i) acc += sq[hh][rg + RG * i] * Sr[i];
+            *reinterpret_cast<f32x4 *>(&red[rg][hh][4 * c4]) = acc;
+        }
+        __syncthreads();
+        for (int e = tid; e < nh * D; e += kThreads) {
+            const int hh = e / D, j = e % D;
+            float num = 0.f;
+            for (int r = 0; r < RG; ++r) num += red[r][hh][j];
+            float o = num;
+            if (normalise) {
+                float den = 0.f;
+                for (int i = 0; i < D; ++i) den += sq[hh][i] * sz[i];
+                o = num / den;
+            }
+            out[((size_t)b * H + (size_t)gk * G + g0 + hh) * D + j] = (T)o;
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void k_fill_zero(float *__restrict__ p, size_t n)
+{
+    for (size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kThreads) p[i] = 0.f;
+}
+
+// -------------------------------------------------------------- launchers
+
+int launch_status()
+{
+    return hipGetLastError() == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+}
+
+template <typename T, int D, int C>
+int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out, float *state_out,
+            float *z_out, float *ws, int normalise, hipStream_t st)
+{
+    const T *qq = static_cast<const T *>(q);
+    const T *kk = static_cast<const T *>(k);
+    const T *vv = static_cast<const T *>(v);
+    T *oo = static_cast<T *>(out);
+    const int P = pl.segments;
+    const int E = D * D + D;
+    if (pl.causal) {
+        if (P > 1) {
+            hipLaunchKernelGGL((k_seg_totals<T, D, C>), dim3(pl.nseq * (P - 1)), dim3(kThreads), 0, st, kk, vv, ws,
+                               pl.N, pl.seg_len, P - 1);
+            if (P > 2)
+                hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st,
+                                   ws, P - 1, D, 0, (float *)nullptr, (float *)nullptr);
+        }
+        hipLaunchKernelGGL((k_causal_chunks<T, D, C>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo,
+                           (const float *)ws, state_out, z_out, pl.H, pl.Hkv, pl.N, pl.G, P, pl.seg_len, normalise);
+    } else {
+        hipLaunchKernelGGL((k_seg_totals<T, D, C>), dim3(pl.nseq * P), dim3(kThreads), 0, st, kk, vv, ws, pl.N,
+                           pl.seg_len, P);
+        hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, ws, P,
+                           D, 1, state_out, z_out);
+        const int nblk = (pl.N + 127) / 128;
+        hipLaunchKernelGGL((k_noncausal_apply<T, D>), dim3(pl.nseq * nblk), dim3(kThreads), 0, st, qq, oo,
+                           (const float *)ws, P, pl.H, pl.Hkv, pl.N, pl.G, nblk, normalise);
+    }
+    return launch_status();
+}
+
+template <typename T, int D, int C>
+constexpr bool lds_fits() { return sizeof(T) * (3 * C * D + D * D) + 4 * D <= 160 * 1024; }
+
+template <typename T, int D>
+int dispatch_chunk(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,
+                   float *state_out, float *z_out, float *ws, int normalise, hipStream_t st)
+{
+    switch (pl.chunk) {
+    case 32:
+        if constexpr (lds_fits<T, D, 32>()) return run_fwd<T, D, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st);
+        break;
+    case 64:
+        if constexpr (lds_fits<T, D, 64>()) return run_fwd<T, D, 64>(pl, q, k, v, out, state_out, z_out, ws, normalise, st);
+        break;
+    case 128:
+        if constexpr (lds_fits<T, D, 128>()) return run_fwd<T, D, 128>(pl, q, k, v, out, state_out, z_out, ws, normalise, st);
+        break;
+    case 256:
+        if constexpr (lds_fits<T, D, 256>()) return run_fwd<T, D, 256>(pl, q, k, v, out, state_out, z_out, ws, normalise, st);
+        break;
+    }
+    return LINATTN_ERR_UNSUPPORTED;
+}
+
+template <typename T>
+int dispatch_d(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,
+               float *state_out, float *z_out, float *ws, int normalise, hipStream_t st)
+{
+    switch (pl.d) {
+    case 32: return dispatch_chunk<T, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st);
+    case 64: return dispatch_chunk<T, 64>(pl, q, k, v, out, state_out, z_out, ws, normalise, st);
+    case 128: return dispatch_chunk<T, 128>(pl, q, k, v, out, state_out, z_out, ws, normalise, st);
+    }
+    return LINATTN_ERR_UNSUPPORTED;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <typename T>
+int run_decode(float *state, float *z, const void *q, const void *k, const void *v, void *out, int B, int H,
+               int Hkv, int d, int normalise, hipStream_t st)
+{
+    const int G = H / Hkv;
+    const dim3 grid(B * Hkv), block(kThreads);
+    const T *qq = static_cast<const T *>(q);
+    const T *kk = static_cast<const T *>(k);
+    const T *vv = static_cast<const T *>(v);
+    T *oo = static_cast<T *>(out);
+    switch (d) {
+    case 32: hipLaunchKernelGGL((k_decode_step<T, 32>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise); break;
+    case 64: hipLaunchKernelGGL((k_decode_step<T, 64>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise); break;
+    case 128: hipLaunchKernelGGL((k_decode_step<T, 128>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise); break;
+    default: return LINATTN_ERR_UNSUPPORTED;
+    }
+    return launch_status();
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+
+extern "C" {
+
+int linattn_abi_version(void) { return LINATTN_ABI_VERSION; }
+
+const char *linattn_status_string(int status)
+{
+    switch (status) {
+    case LINATTN_OK: return "ok";
+    case LINATTN_ERR_NULL: return "a required pointer is NULL";
+    case LINATTN_ERR_SHAPE: return "invalid shape (B, H, Hkv, N, d) or H % Hkv != 0";
+    case LINATTN_ERR_DTYPE: return "unsupported dtype";
+    case LINATTN_ERR_UNSUPPORTED: return "unsupported head dimension or chunk size";
+    case LINATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case LINATTN_ERR_HIP: return "HIP launch failed";
+    case LINATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
+    }
+    return "unknown status";
+}
+
+int linattn_fwd_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int chunk, int *chunk_out,
+                     int *segments_out)
+{
+    linattn::Plan pl;
+    const int rc = linattn::make_plan(B, H, Hkv, N, d, causal, dtype, chunk, &pl);
+    if (rc != LINATTN_OK) return rc;
+    if (chunk_out) *chunk_out = pl.chunk;
+    if (segments_out) *segments_out = pl.segments;
+    return LINATTN_OK;
+}
+
+size_t linattn_fwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int causal, int dtype, int chunk)
+{
+    linattn::Plan pl;
+    if (linattn::make_plan(B, H, Hkv, N, d, causal, dtype, chunk, &pl) != LINATTN_OK) return (size_t)-1;
+    return pl.ws_bytes;
+}
+
+int linattn_fwd(const void *q, const void *k, const void *v, void *out, int B, int H, int Hkv, int N, int d,
+                int causal, int normalise, int dtype, float *state_out, float *z_out, int chunk, void *workspace,
+                size_t workspace_bytes, hipStream_t stream)
+{
+    linattn::Plan pl;
+    const int rc = linattn::make_plan(B, H, Hkv, N, d, causal, dtype, chunk, &pl);
+    if (rc != LINATTN_OK) return rc;
+    if (B == 0) return LINATTN_OK;
+    if (N > 0 && (!q || !k || !v || !out)) return LINATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(state_out) ||
+        !aligned16(z_out) || !aligned16(workspace))
+        return LINATTN_ERR_ALIGN;
+    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LINATTN_ERR_WORKSPACE;
+    if (N == 0) {
+        // No keys: the state and normaliser are zero; there is no output row.
+        if (state_out)
+            hipLaunchKernelGGL(k_fill_zero, dim3(256), dim3(kThreads), 0, stream, state_out, (size_t)pl.nseq * d * d);
+        if (z_out) hipLaunchKernelGGL(k_fill_zero, dim3(16), dim3(kThreads), 0, stream, z_out, (size_t)pl.nseq * d);
+        return launch_status();
+    }
+    float *ws = static_cast<float *>(workspace);
+    if (dtype == LINATTN_BF16) return dispatch_d<bf16>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream);
+    return dispatch_d<float>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream);
+}
+
+int linattn_decode_step(float *state, float *z, const void *q, const void *k, const void *v, void *out, int B, int H,
+                        int Hkv, int d, int normalise, int dtype, hipStream_t stream)
+{
+    if (dtype != LINATTN_F32 && dtype != LINATTN_BF16) return LINATTN_ERR_DTYPE;
+    if (B < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || (int64_t)B * Hkv > INT32_MAX) return LINATTN_ERR_SHAPE;
+    if (d != 32 && d != 64 && d != 128) return LINATTN_ERR_UNSUPPORTED;
+    if (B == 0) return LINATTN_OK;
+    if (!state || !q || !k || !v || !out || (normalise && !z)) return LINATTN_ERR_NULL;
+    if (!aligned16(state) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return LINATTN_ERR_ALIGN;
+    if (dtype == LINATTN_BF16) return run_decode<bf16>(state, z, q, k, v, out, B, H, Hkv, d, normalise ? 1 : 0, stream);
+    return run_decode<float>(state, z, q, k, v, out, B, H, Hkv, d, normalise ? 1 : 0, stream);
+}
+
+}  // extern "C"

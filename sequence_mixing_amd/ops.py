@@ -1,0 +1,63 @@
+"""Torch-facing wrappers over the C ABI: allocate outputs / workspace, check status.
+
+Allocation and stream plumbing only; the computation is the library's.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (LINATTN_BF16, LINATTN_F32, LinattnError, linattn_decode_step, linattn_fwd,
+               linattn_fwd_workspace_bytes)
+
+_DT = {torch.float32: LINATTN_F32, torch.bfloat16: LINATTN_BF16}
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise TypeError(f"unsupported dtype {t}")
+    return _DT[t]
+
+
+def workspace(B, H, Hkv, N, d, causal, dtype: torch.dtype, chunk=0, device="cuda") -> torch.Tensor | None:
+    n = linattn_fwd_workspace_bytes(B, H, Hkv, N, d, causal, dtype_code(dtype), chunk)
+    if n < 0:
+        raise LinattnError(-2, "linattn_fwd_workspace_bytes")
+    return torch.empty((n + 3) // 4, dtype=torch.float32, device=device) if n > 0 else None
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=True, normalise=True, chunk=0,
+        want_state=False, out=None, ws=None, stream=None):
+    """O = phi(Q)(phi(K)^T V) through ``linattn_fwd``; q [B,H,N,d], k/v [B,Hkv,N,d] on the GPU."""
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    for t in (q, k, v):
+        if not (t.is_cuda and t.is_contiguous() and t.dtype == q.dtype):
+            raise ValueError("q, k, v must be contiguous device tensors of one dtype")
+    if k.shape != (B, Hkv, N, d) or v.shape != (B, Hkv, N, d):
+        raise ValueError("k and v must be [B, Hkv, N, d]")
+    code = dtype_code(q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    S = z = None
+    if want_state:
+        S = torch.empty(B, Hkv, d, d, dtype=torch.float32, device=q.device)
+        z = torch.empty(B, Hkv, d, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(B, H, Hkv, N, d, causal, q.dtype, chunk, q.device)
+    nbytes = ws.numel() * 4 if ws is not None else 0
+    rc = linattn_fwd(q, k, v, out, B, H, Hkv, N, d, causal, normalise, code, S, z, chunk, ws, nbytes, stream)
+    if rc != 0:
+        raise LinattnError(rc, "linattn_fwd")
+    return (out, S, z) if want_state else out
+
+
+def decode_step(state: torch.Tensor, z: torch.Tensor | None, q, k, v, normalise=True, out=None, stream=None):
+    """One recurrent step through ``linattn_decode_step``; state [B,Hkv,d,d] and z [B,Hkv,d] fp32, in place."""
+    B, H, d = q.shape
+    Hkv = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    rc = linattn_decode_step(state, z, q, k, v, out, B, H, Hkv, d, normalise, dtype_code(q.dtype), stream)
+    if rc != 0:
+        raise LinattnError(rc, "linattn_decode_step")
+    return out

@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and validates arguments / plans launches on the host.
+
+Only calls that return before any HIP call are made here (argument errors,
+workspace sizing, planning); nothing is launched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sequence_mixing_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+F32, BF16 = la.LINATTN_F32, la.LINATTN_BF16
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(linattn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for n in ("linattn_fwd", "linattn_decode_step", "linattn_fwd_workspace_bytes", "linattn_fwd_plan",
+              "linattn_status_string", "linattn_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = la.load()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", la.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (linattn_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-fsyntax-only", "-x", "c", "-std=c99", "-D__HIP_PLATFORM_AMD__",
+                        "-I/opt/rocm/include", HEADER], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_version_and_status_strings():
+    assert la.linattn_abi_version() == 1
+    for code in [0, -1, -2, -3, -4, -5, -6, -7]:
+        assert la.linattn_status_string(code) and la.linattn_status_string(code) != "unknown status"
+    assert la.linattn_status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 3, 2, 16, 64, 1, F32, 0), -2),     # H % Hkv != 0
+    ((-1, 2, 2, 16, 64, 1, F32, 0), -2),    # B < 0
+    ((1, 2, 2, -5, 64, 1, F32, 0), -2),     # N < 0
+    ((1, 0, 1, 16, 64, 1, F32, 0), -2),     # H == 0
+    ((1, 2, 2, 16, 48, 1, F32, 0), -4),     # d unsupported
+    ((1, 2, 2, 16, 256, 1, BF16, 0), -4),   # d unsupported
+    ((1, 2, 2, 16, 64, 1, F32, 96), -4),    # chunk unsupported
+    ((1, 2, 2, 16, 128, 1, F32, 128), -4),  # fp32 d=128 chunk 128 exceeds LDS
+    ((1, 2, 2, 16, 64, 1, 7, 0), -3),       # dtype
+])
+def test_plan_rejects(args, code):
+    rc, _, _ = la.linattn_fwd_plan(*args)
+    assert rc == code
+    assert la.linattn_fwd_workspace_bytes(*args) == -1
+
+
+def test_fwd_rejects_before_launch():
+    # Argument errors return before anything touches the GPU.
+    assert la.linattn_fwd(None, None, None, None, 1, 3, 2, 16, 64, 1, 1, F32, stream=0) == -2
+    assert la.linattn_fwd(None, None, None, None, 1, 2, 2, 16, 64, 1, 1, F32, stream=0) == -1
+    assert la.linattn_fwd(16, 16, 16, 16, 1, 2, 2, 16, 64, 1, 1, 9, stream=0) == -3
+    assert la.linattn_fwd(16, 16, 16, 16, 1, 2, 2, 16, 40, 1, 1, F32, stream=0) == -4
+    assert la.linattn_fwd(17, 16, 16, 16, 1, 2, 2, 16, 64, 1, 1, F32, stream=0) == -7
+    # 4096 tokens need a workspace; none given.
+    assert la.linattn_fwd(16, 16, 16, 16, 2, 8, 8, 4096, 64, 1, 1, F32, stream=0) == -5
+    need = la.linattn_fwd_workspace_bytes(2, 8, 8, 4096, 64, 1, F32)
+    assert la.linattn_fwd(16, 16, 16, 16, 2, 8, 8, 4096, 64, 1, 1, F32, workspace=16, workspace_bytes=need - 4,
+                          stream=0) == -5
+    # B == 0 is a valid no-op.
+    assert la.linattn_fwd(None, None, None, None, 0, 2, 2, 16, 64, 1, 1, F32, stream=0) == 0
+
+
+def test_decode_rejects_before_launch():
+    assert la.linattn_decode_step(16, 16, 16, 16, 16, 16, 1, 3, 2, 64, 1, F32, stream=0) == -2
+    assert la.linattn_decode_step(16, 16, 16, 16, 16, 16, 1, 2, 2, 48, 1, F32, stream=0) == -4
+    assert la.linattn_decode_step(16, 16, 16, 16, 16, 16, 1, 2, 2, 64, 1, 4, stream=0) == -3
+    assert la.linattn_decode_step(16, None, 16, 16, 16, 16, 1, 2, 2, 64, 1, F32, stream=0) == -1
+    assert la.linattn_decode_step(None, 16, 16, 16, 16, 16, 1, 2, 2, 64, 1, F32, stream=0) == -1
+    assert la.linattn_decode_step(16, 16, 24, 16, 16, 16, 1, 2, 2, 64, 1, F32, stream=0) == -7
+    assert la.linattn_decode_step(None, None, None, None, None, None, 0, 2, 2, 64, 1, F32, stream=0) == 0
+
+
+def plan(B, H, Hkv, N, d, causal, dtype, chunk=0):
+    rc, c, p = la.linattn_fwd_plan(B, H, Hkv, N, d, causal, dtype, chunk)
+    assert rc == 0
+    return c, p
+
+
+def test_plan_covers_every_token_with_whole_chunks():
+    for N in [1, 7, 31, 32, 33, 100, 257, 4096, 4097, 65536]:
+        for chunk in [32, 64, 128, 256]:
+            for nseq in [1, 2, 16, 64]:
+                c, P = plan(nseq, 1, 1, N, 64, 1, BF16, chunk)
+                assert c == chunk
+                nch = -(-N // c)
+                seg_chunks = -(-nch // max(1, min(nch, -(-512 // nseq))))
+                assert P == -(-N // (seg_chunks * c))
+                assert 1 <= P <= nch
+                assert (P - 1) * seg_chunks * c < N <= P * seg_chunks * c
+
+
+def test_workspace_formula():
+    for (B, H, Hkv, N, d, causal, dt) in [(2, 8, 8, 4096, 64, 1, F32), (2, 8, 8, 65536, 64, 1, BF16),
+                                          (1, 32, 8, 32768, 128, 1, BF16), (2, 8, 8, 4096, 64, 0, F32),
+                                          (1, 2, 2, 256, 32, 1, F32), (3, 4, 2, 7, 64, 0, BF16)]:
+        c, P = plan(B, H, Hkv, N, d, causal, dt)
+        slots = P - 1 if causal else P
+        assert la.linattn_fwd_workspace_bytes(B, H, Hkv, N, d, causal, dt) == B * Hkv * slots * d * (d + 1) * 4
+    assert la.linattn_fwd_workspace_bytes(1, 1, 1, 0, 64, 1, F32) == 0
+    assert la.linattn_fwd_workspace_bytes(0, 1, 1, 100, 64, 1, F32) == 0
+
+
+def test_auto_chunk_choices():
+    assert plan(2, 8, 8, 65536, 64, 1, BF16)[0] == 128
+    assert plan(1, 32, 8, 32768, 128, 1, BF16)[0] == 64
+    assert plan(1, 2, 2, 256, 32, 1, F32)[0] in (32, 64, 128)
+    assert plan(1, 2, 2, 256, 128, 1, F32)[0] == 32

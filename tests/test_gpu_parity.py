@@ -1,0 +1,277 @@
+"""GPU parity: the HIP library (called through the C ABI) against the fp64 oracle.
+
+Bar (per output row r = (b, h, t)): e_r = max_j |O_gpu - O_ref| / max_j |O_ref|
+must be <= 1e-4 for fp32 inputs and <= 2e-2 for bf16 inputs with fp32
+accumulation.  States and normalisers use the same metric per matrix / vector.
+
+Sizes: small ragged shapes in full (several chunks, segments and a ragged
+tail), every workload at its full size, with the oracle evaluated on sampled
+(batch, kv head) sequences where a full oracle run would take minutes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sequence_mixing_amd as la
+from linattn_inputs import DECODE, WORKLOADS, DecodeStream, make_qkv, workload_qkv
+from sequence_mixing_amd import ops
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def rows_rel_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    g = got.reshape(-1, got.shape[-1])
+    r = ref.reshape(-1, ref.shape[-1])
+    if g.size == 0:
+        return 0.0
+    den = np.abs(r).max(axis=1)
+    den = np.where(den == 0, 1.0, den)
+    return float((np.abs(g - r).max(axis=1) / den).max())
+
+
+def mat_rel_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    lead = got.shape[:2]
+    g = got.reshape(int(np.prod(lead)), -1)
+    r = ref.reshape(int(np.prod(lead)), -1)
+    den = np.abs(r).max(axis=1)
+    den = np.where(den == 0, 1.0, den)
+    return float((np.abs(g - r).max(axis=1) / den).max())
+
+
+def gpu(t):
+    return t.contiguous().cuda()
+
+
+def host(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def run_case(B, H, Hkv, N, d, dtype, causal, normalise, chunk=0, seed=0, check_state=True):
+    q, k, v = make_qkv(B, H, Hkv, N, d, dtype, seed)
+    print(f"case B{B} H{H} Hkv{Hkv} N{N} d{d} {dtype} causal={causal} norm={normalise} chunk={chunk} seed={seed}",
+          flush=True)
+    out, S, z = ops.fwd(gpu(q), gpu(k), gpu(v), causal=causal, normalise=normalise, chunk=chunk, want_state=True)
+    torch.cuda.synchronize()
+    ref, Sr, zr = oracle.ref_fwd(q, k, v, causal=causal, normalise=normalise, want_state=True)
+    tol = TOL[dtype]
+    e = rows_rel_err(host(out), ref)
+    assert e <= tol, f"output rel err {e:.3e} > {tol}"
+    if check_state and N > 0:
+        es, ez = mat_rel_err(host(S), Sr), mat_rel_err(host(z), zr)
+        assert es <= tol and ez <= tol, f"state rel err {es:.3e}, z rel err {ez:.3e}"
+    return e
+
+
+# ------------------------------------------------------------- small shapes
+
+SMALL = [
+    # B, H, Hkv, N, d, dtype
+    (1, 2, 2, 256, 32, "f32"),
+    (1, 1, 1, 1, 64, "f32"),
+    (2, 2, 2, 7, 64, "bf16"),
+    (1, 2, 1, 100, 64, "f32"),
+    (2, 4, 2, 257, 64, "bf16"),
+    (1, 4, 4, 1000, 32, "bf16"),
+    (1, 4, 1, 333, 128, "bf16"),
+    (1, 2, 2, 300, 128, "f32"),
+    (3, 6, 3, 515, 64, "f32"),
+    (1, 8, 2, 2049, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dH%dK%dN%dd%d%s" % s)
+@pytest.mark.parametrize("causal", [1, 0])
+@pytest.mark.parametrize("normalise", [1, 0])
+def test_small_shapes(shape, causal, normalise):
+    B, H, Hkv, N, d, dtype = shape
+    run_case(B, H, Hkv, N, d, dtype, causal, normalise, seed=N + d)
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 128, 256])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_every_chunk_size(chunk, dtype):
+    rc, _, _ = la.linattn_fwd_plan(2, 4, 2, 1100, 64, 1, ops.dtype_code(getattr(torch, {"f32": "float32", "bf16": "bfloat16"}[dtype])), chunk)
+    if rc != 0:
+        pytest.skip("chunk does not fit LDS for this dtype")
+    run_case(2, 4, 2, 1100, 64, dtype, 1, 1, chunk=chunk, seed=chunk)
+
+
+def test_config1_full():
+    w = WORKLOADS["cfg1"]
+    for normalise in (1, 0):
+        for chunk in (0, 32, 64, 128, 256):
+            run_case(w.B, w.H, w.Hkv, w.N, w.d, w.dtype, 1, normalise, chunk=chunk, seed=w.seed)
+
+
+def test_empty_and_zero_batch():
+    q = torch.zeros(1, 2, 0, 64, device="cuda")
+    out, S, z = ops.fwd(q, q.clone(), q.clone(), want_state=True)
+    torch.cuda.synchronize()
+    assert out.shape == (1, 2, 0, 64) and not S.any() and not z.any()
+    q = torch.zeros(0, 2, 16, 64, device="cuda")
+    assert ops.fwd(q, q.clone(), q.clone()).shape == (0, 2, 16, 64)
+
+
+# ------------------------------------------------------- workloads, full size
+
+@pytest.mark.parametrize("causal", [1, 0])
+@pytest.mark.parametrize("normalise", [1, 0])
+def test_config2_full(causal, normalise):
+    w = WORKLOADS["cfg2"]
+    run_case(w.B, w.H, w.Hkv, w.N, w.d, w.dtype, causal, normalise, seed=w.seed)
+
+
+@pytest.mark.parametrize("normalise", [1, 0])
+def test_config3_full(normalise):
+    w = WORKLOADS["cfg3"]
+    run_case(w.B, w.H, w.Hkv, w.N, w.d, w.dtype, 1, normalise, seed=w.seed)
+
+
+def sampled_check(w, out, S, z, seqs, normalise, q, k, v):
+    """Oracle on the sampled (b, kv head) sequences only; all their query heads."""
+    tol = TOL[w.dtype]
+    G = w.G
+    for (b, g) in seqs:
+        hs = slice(g * G, (g + 1) * G)
+        ref, Sr, zr = oracle.ref_fwd(q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
+                                     causal=True, normalise=normalise, want_state=True)
+        e = rows_rel_err(host(out[b:b + 1, hs]), ref)
+        es = mat_rel_err(host(S[b:b + 1, g:g + 1]), Sr)
+        ez = mat_rel_err(host(z[b:b + 1, g:g + 1]), zr)
+        print(f"  seq b={b} g={g}: out {e:.2e} state {es:.2e} z {ez:.2e}", flush=True)
+        assert e <= tol and es <= tol and ez <= tol
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_config4_full_sampled(chunk):
+    w = WORKLOADS["cfg4"]
+    q, k, v = workload_qkv(w)
+    print(f"cfg4 chunk={chunk}", flush=True)
+    out, S, z = ops.fwd(gpu(q), gpu(k), gpu(v), causal=True, normalise=True, chunk=chunk, want_state=True)
+    torch.cuda.synchronize()
+    sampled_check(w, out, S, z, [(0, 0), (1, 7)], True, q, k, v)
+
+
+def test_config5_prefill_full_sampled():
+    w = WORKLOADS["cfg5"]
+    q, k, v = workload_qkv(w)
+    print("cfg5 prefill", flush=True)
+    out, S, z = ops.fwd(gpu(q), gpu(k), gpu(v), causal=True, normalise=True, want_state=True)
+    torch.cuda.synchronize()
+    sampled_check(w, out, S, z, [(0, 0), (0, 5)], True, q, k, v)
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("normalise", [1, 0])
+def test_decode_step_same_start_state(dtype, d, normalise):
+    """The decode kernel against the oracle from an identical (nonzero) start state."""
+    B, H, Hkv = 3, 8, 2
+    q0, k0, v0 = make_qkv(B, Hkv, Hkv, 50, d, dtype, 77 + d)
+    _, S, z = ops.fwd(gpu(q0), gpu(k0), gpu(v0), want_state=True)
+    Sr, zr = host(S).copy(), host(z).copy()
+    stream = DecodeStream(B, H, Hkv, d, dtype, 5 + d)
+    for step in range(4):
+        q, k, v = stream.next()
+        o = ops.decode_step(S, z if normalise else None, gpu(q), gpu(k), gpu(v), normalise=normalise)
+        ref = oracle.ref_decode_step(Sr, zr if normalise else None, q, k, v, normalise=normalise)
+        torch.cuda.synchronize()
+        tol = 1e-5 if dtype == "f32" else TOL[dtype]
+        assert rows_rel_err(host(o), ref) <= tol
+        assert mat_rel_err(host(S), Sr) <= 1e-5
+        if normalise:
+            assert mat_rel_err(host(z), zr) <= 1e-6
+
+
+def test_decode_continues_prefill_on_gpu():
+    """Prefill(N) then one decode step equals row N of prefill(N + 1)."""
+    B, H, Hkv, N, d = 2, 8, 2, 777, 64
+    q, k, v = make_qkv(B, H, Hkv, N + 1, d, "f32", 91)
+    full = ops.fwd(gpu(q), gpu(k), gpu(v))
+    _, S, z = ops.fwd(gpu(q[:, :, :N]), gpu(k[:, :, :N]), gpu(v[:, :, :N]), want_state=True)
+    o = ops.decode_step(S, z, gpu(q[:, :, N]), gpu(k[:, :, N]), gpu(v[:, :, N]))
+    torch.cuda.synchronize()
+    assert rows_rel_err(host(o), host(full[:, :, N])) <= 1e-4
+
+
+def test_config5_decode_1024_steps_sampled():
+    """GQA prefill, its state replicated into 64 slots, then 1024 decode steps at batch 64.
+
+    The GPU runs the whole batch; the oracle follows slots 0 and 63 end to end
+    (its own prefill state, its own decode steps) over all 1024 steps.
+    """
+    w, dw = WORKLOADS["cfg5"], DECODE
+    q, k, v = workload_qkv(w)
+    _, S1, z1 = ops.fwd(gpu(q), gpu(k), gpu(v), want_state=True)
+    _, Sr1, zr1 = oracle.ref_fwd(q[:, :8], k[:, :2], v[:, :2], want_state=True)  # kv heads 0, 1 only
+    del q, k, v
+    S = S1.expand(dw.B, -1, -1, -1).contiguous()
+    z = z1.expand(dw.B, -1, -1).contiguous()
+    slots = [0, 63]
+    # Oracle state for the sampled slots: kv heads 0 and 1 only (heads are independent).
+    Sr = np.ascontiguousarray(np.repeat(Sr1, len(slots), axis=0))
+    zr = np.ascontiguousarray(np.repeat(zr1, len(slots), axis=0))
+    stream = DecodeStream(dw.B, dw.H, dw.Hkv, dw.d, dw.dtype, dw.seed)
+    worst = 0.0
+    for step in range(1024):
+        qs, ks, vs = stream.next()
+        o = ops.decode_step(S, z, gpu(qs), gpu(ks), gpu(vs))
+        ref = oracle.ref_decode_step(Sr, zr, qs[slots, :8], ks[slots, :2], vs[slots, :2], normalise=True)
+        e = rows_rel_err(host(o[slots, :8]), ref)
+        worst = max(worst, e)
+        assert e <= TOL["bf16"], f"step {step}: {e:.3e}"
+    print(f"decode worst rel err over 1024 steps: {worst:.3e}", flush=True)
+
+
+# ---------------------------------------------------------- structure on GPU
+
+def test_causality_bitwise():
+    q, k, v = make_qkv(1, 4, 2, 1500, 64, "bf16", 5)
+    a = ops.fwd(gpu(q), gpu(k), gpu(v))
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    q2[:, :, 900:] = 3.0
+    k2[:, :, 900:] = -1.0
+    v2[:, :, 900:] = 7.0
+    b = ops.fwd(gpu(q2), gpu(k2), gpu(v2))
+    torch.cuda.synchronize()
+    assert torch.equal(a[:, :, :900], b[:, :, :900])
+
+
+def test_deterministic():
+    q, k, v = make_qkv(2, 8, 8, 4096, 64, "bf16", 6)
+    a = ops.fwd(gpu(q), gpu(k), gpu(v))
+    b = ops.fwd(gpu(q), gpu(k), gpu(v))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_gqa_matches_repeated_kv():
+    q, k, v = make_qkv(1, 8, 2, 1000, 64, "f32", 8)
+    a = ops.fwd(gpu(q), gpu(k), gpu(v))
+    b = ops.fwd(gpu(q), gpu(torch.repeat_interleave(k, 4, dim=1)), gpu(torch.repeat_interleave(v, 4, dim=1)))
+    torch.cuda.synchronize()
+    assert rows_rel_err(host(a), host(b)) <= 1e-5
+
+
+def test_chunk_invariance():
+    q, k, v = make_qkv(2, 8, 8, 3000, 64, "bf16", 9)
+    outs = [host(ops.fwd(gpu(q), gpu(k), gpu(v), chunk=c)) for c in (64, 128, 256)]
+    for o in outs[1:]:
+        assert rows_rel_err(o, outs[0]) <= 2e-2
+
+
+def test_last_causal_row_equals_noncausal():
+    q, k, v = make_qkv(2, 4, 2, 999, 64, "f32", 10)
+    c = ops.fwd(gpu(q), gpu(k), gpu(v), causal=True)
+    n = ops.fwd(gpu(q), gpu(k), gpu(v), causal=False)
+    torch.cuda.synchronize()
+    assert rows_rel_err(host(c[:, :, -1]), host(n[:, :, -1])) <= 1e-4
