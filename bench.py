@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Throughput of causal linear attention (phi = ELU + 1) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2] [--chunk 0]
+
+A step is one ``linattn_fwd`` call (causal, normaliser on) over the whole
+batch of the chosen workload: segment totals, their prefix scan and the
+chunked main pass.  Inputs are seeded N(0, 1) tensors already resident on
+the GPU.  The W warm-up steps are untimed; the K timed steps run back to
+back between two device synchronisations, and HIP events recorded by the
+library on its stream give each stage's duration.
+
+Printed: ONE JSON line.  ``value`` is tokens (B * N) per second of wall time
+over the K steps.  ``roofline`` prices the dominant kernel (the chunked main
+pass) against HBM: algorithmic bytes (Q, K, V read once, O written once) per
+launch over its mean event-timed duration.  ``cpu_baseline`` is the fp64
+oracle on the same workload timed on this host.  ``rows`` holds the other
+workloads measured the same way (non-causal, bf16 N=16384 and N=65536 with
+the chunk sweep, the GQA prefill and its 1024-step decode).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0                               # MI355X HBM3E, GB/s
+MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}       # dense MFMA, flop/s
+ESZ = {"f32": 4, "bf16": 2}
+
+
+def fwd_bytes(w) -> int:
+    """Algorithmic bytes of one forward: q, k, v read once and out written once."""
+    e = ESZ[w.dtype]
+    return e * w.N * w.d * w.B * (2 * w.H + 2 * w.Hkv)
+
+
+def fwd_flops(w) -> float:
+    """The recurrence only: per kv-head token 2d^2 + 2d, per query-head token 2d^2 + 4d."""
+    d = w.d
+    return float(w.B * w.N) * (w.Hkv * (2 * d * d + 2 * d) + w.H * (2 * d * d + 4 * d))
+
+
+def decode_bytes(B, H, Hkv, d, dtype) -> int:
+    """State and normaliser read and written once, q/out/k/v once per step."""
+    e = ESZ[dtype]
+    return B * Hkv * (2 * d * d * 4 + 2 * d * 4) + e * d * (2 * B * H + 2 * B * Hkv)
+
+
+def roofline(nbytes, flops, seconds, dtype, kernel):
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / MFMA_PEAK[dtype]
+    if t_hbm >= t_mfma:
+        ach = nbytes / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel}
+    ach = flops / seconds / 1e12
+    peak = MFMA_PEAK[dtype] / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(ach / peak, 4), "traffic": None, "kernel": kernel}
+
+
+class Hip:
+    """The few HIP runtime calls the benchmark needs for events (plumbing only)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def ms(self, a, b) -> float:
+        out = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return out.value
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, stream) == 0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_name(w, chunk, causal):
+    t = {"f32": "float", "bf16": "bf16"}[w.dtype]
+    return (f"k_causal_chunks<{t},{w.d},{chunk}>" if causal else f"k_noncausal_apply<{t},{w.d}>")
+
+
+def time_fwd(la, hip, torch, w, q, k, v, out, ws, ws_bytes, causal, chunk, steps, warmup, stream, flush=None):
+    """Runs warm-up + timed steps; returns dict of wall and per-stage event times."""
+    dt = la.LINATTN_BF16 if w.dtype == "bf16" else la.LINATTN_F32
+    evs = [[hip.event() for _ in range(4)] for _ in range(steps)]
+    warm = [hip.event() for _ in range(4)]
+
+    def call(ev):
+        rc = la.linattn_fwd_timed(q, k, v, out, w.B, w.H, w.Hkv, w.N, w.d, causal, 1, dt, None, None, chunk,
+                                  ws, ws_bytes, stream, events=ev)
+        if rc != 0:
+            raise la.LinattnError(rc, "linattn_fwd_timed")
+
+    for _ in range(warmup):
+        call(warm)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if flush is not None:
+            flush()
+        call(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = [[hip.ms(e[j], e[j + 1]) for j in range(3)] for e in evs]
+    mean = [sum(s[j] for s in st) / steps for j in range(3)]
+    step_ms = sum(sum(s) for s in st) / steps
+    return {"wall_s": wall, "stage_ms": mean, "step_event_ms": step_ms}
+
+
+def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, cold):
+    """One workload measured; returns a summary dict."""
+    from linattn_inputs import workload_qkv
+    from sequence_mixing_amd import ops
+
+    q, k, v = (t.cuda() for t in workload_qkv(w))
+    out = torch.empty_like(q)
+    ws = ops.workspace(w.B, w.H, w.Hkv, w.N, w.d, causal, q.dtype, chunk)
+    ws_bytes = ws.numel() * 4 if ws is not None else 0
+    dt = la.LINATTN_BF16 if w.dtype == "bf16" else la.LINATTN_F32
+    _, c, P = la.linattn_fwd_plan(w.B, w.H, w.Hkv, w.N, w.d, causal, dt, chunk)
+    r = time_fwd(la, hip, torch, w, q, k, v, out, ws, ws_bytes, causal, chunk, steps, warmup, stream)
+    nb, fl = fwd_bytes(w), fwd_flops(w)
+    k3 = r["stage_ms"][2] / 1e3
+    row = {
+        "causal": bool(causal), "chunk": c, "segments": P,
+        "ms_per_step": round(r["wall_s"] / steps * 1e3, 5),
+        "tokens_per_s": round(w.B * w.N * steps / r["wall_s"], 1),
+        "stage_us": {"seg_totals": round(r["stage_ms"][0] * 1e3, 2), "seg_scan": round(r["stage_ms"][1] * 1e3, 2),
+                     "main": round(r["stage_ms"][2] * 1e3, 2)},
+        "roofline_main": roofline(nb, fl, k3, w.dtype, kernel_name(w, c, causal)),
+        "roofline_path": roofline(nb, fl, r["step_event_ms"] / 1e3, w.dtype, "whole step (all stages)"),
+    }
+    if cold:
+        # Same steps with the 256 MiB memory-side cache flushed before each one
+        # (a 512 MiB write outside the timed events), so every input comes from HBM.
+        scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+        rc = time_fwd(la, hip, torch, w, q, k, v, out, ws, ws_bytes, causal, chunk, max(5, steps // 4), 2, stream,
+                      flush=lambda: scratch.fill_(1.0))
+        row["cold_stage_us"] = {"seg_totals": round(rc["stage_ms"][0] * 1e3, 2),
+                                "seg_scan": round(rc["stage_ms"][1] * 1e3, 2),
+                                "main": round(rc["stage_ms"][2] * 1e3, 2)}
+        row["cold_roofline_path"] = roofline(nb, fl, rc["step_event_ms"] / 1e3, w.dtype, "whole step, cold cache")
+        del scratch
+    del q, k, v, out, ws
+    return row
+
+
+def decode_row(la, hip, torch, steps_total, stream):
+    """GQA prefill (N=32768), state replicated into 64 slots, 1024 decode steps."""
+    from linattn_inputs import DECODE, WORKLOADS, DecodeStream, workload_qkv
+    from sequence_mixing_amd import ops
+
+    w, dw = WORKLOADS["cfg5"], DECODE
+    q, k, v = (t.cuda() for t in workload_qkv(w))
+    _, S1, z1 = ops.fwd(q, k, v, want_state=True)
+    del q, k, v
+    S = S1.expand(dw.B, -1, -1, -1).contiguous()
+    z = z1.expand(dw.B, -1, -1).contiguous()
+    gen = DecodeStream(dw.B, dw.H, dw.Hkv, dw.d, dw.dtype, dw.seed)
+    qs, ks, vs = [], [], []
+    for _ in range(steps_total):
+        a, b, c = gen.next()
+        qs.append(a)
+        ks.append(b)
+        vs.append(c)
+    qs, ks, vs = torch.stack(qs).cuda(), torch.stack(ks).cuda(), torch.stack(vs).cuda()
+    out = torch.empty(steps_total, dw.B, dw.H, dw.d, dtype=qs.dtype, device="cuda")
+    dt = la.LINATTN_BF16
+    ev = [hip.event() for _ in range(steps_total + 1)]
+    # eager pass with an event between consecutive steps: per-kernel durations
+    S0, z0 = S.clone(), z.clone()
+    hip.record(ev[0], stream)
+    for t in range(steps_total):
+        rc = la.linattn_decode_step(S, z, qs[t], ks[t], vs[t], out[t], dw.B, dw.H, dw.Hkv, dw.d, 1, dt, stream)
+        assert rc == 0
+        hip.record(ev[t + 1], stream)
+    torch.cuda.synchronize()
+    per = [hip.ms(ev[t], ev[t + 1]) for t in range(steps_total)]
+    k_us = sum(per) / steps_total * 1e3
+    # whole 1024-step loop replayed as one HIP graph: per-step throughput
+    S.copy_(S0)
+    z.copy_(z0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(steps_total):
+            la.linattn_decode_step(S, z, qs[t], ks[t], vs[t], out[t], dw.B, dw.H, dw.Hkv, dw.d, 1, dt, None)
+    S.copy_(S0)
+    z.copy_(z0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nb = decode_bytes(dw.B, dw.H, dw.Hkv, dw.d, dw.dtype)
+    fl = float(dw.B) * (dw.Hkv * (2 * dw.d ** 2 + 2 * dw.d) + dw.H * (2 * dw.d ** 2 + 4 * dw.d))
+    res = {
+        "batch": dw.B, "steps": steps_total,
+        "graph_us_per_step": round(wall / steps_total * 1e6, 2),
+        "tokens_per_s": round(dw.B * steps_total / wall, 1),
+        "kernel_us": round(k_us, 2),
+        "roofline": roofline(nb, fl, k_us / 1e6, "bf16", "k_decode_step<bf16,128>"),
+        "note": "state (32 MiB fp32) fits the 256 MiB memory-side cache; it is read and written every step",
+    }
+    del S, z, qs, ks, vs, out, g
+    return res
+
+
+def cpu_baseline(w, seconds):
+    """The fp64 oracle on the whole workload, repeated until `seconds` have passed."""
+    import numpy as np
+
+    import oracle
+    from linattn_inputs import workload_qkv
+
+    q, k, v = (np.ascontiguousarray(t.double().numpy()) for t in workload_qkv(w))
+    threads = oracle.default_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.ref_fwd(q, k, v, causal=True, normalise=True, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    return {"value": round(w.B * w.N * reps / el, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole workload ({w.B}x{w.N} tokens, {w.H} heads), {reps} reps in {el:.1f} s, fp64 C, "
+                      f"{threads} threads over (batch, kv head, 16-column block)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="cfg2", choices=["cfg1", "cfg2", "cfg3", "cfg4", "cfg5"])
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--rows", type=int, default=1, help="also measure the other workloads (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the sharded path is not part of this library.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sequence_mixing_amd as la
+    from linattn_inputs import WORKLOADS
+
+    la.load()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+    w = WORKLOADS[args.workload]
+    log(f"workload {args.workload}: {w.name}; steps {args.steps}, warmup {args.warmup}")
+
+    head = fwd_row(la, hip, torch, w, 1, args.chunk, args.steps, args.warmup, stream, cold=True)
+    log("headline", json.dumps(head))
+    rows = {}
+    if args.rows:
+        if args.workload == "cfg2":
+            rows["cfg2_noncausal"] = fwd_row(la, hip, torch, w, 0, args.chunk, 20, 5, stream, cold=True)
+            log("cfg2_noncausal", json.dumps(rows["cfg2_noncausal"]))
+        for name, chunk in (("cfg3", 0), ("cfg4_c64", 64), ("cfg4_c128", 128), ("cfg4_c256", 256), ("cfg5_prefill", 0)):
+            key = name.split("_")[0] if name != "cfg5_prefill" else "cfg5"
+            rows[name] = fwd_row(la, hip, torch, WORKLOADS[key], 1, chunk, 20, 5, stream, cold=True)
+            log(name, json.dumps(rows[name]))
+        rows["cfg5_decode"] = decode_row(la, hip, torch, 1024, stream)
+        log("cfg5_decode", json.dumps(rows["cfg5_decode"]))
+
+    cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    if cpu:
+        log("cpu_baseline", json.dumps(cpu))
+
+    tok_s = head["tokens_per_s"]
+    res = {
+        "metric": "causal linear-attn fwd tokens/s (B2 H8 d64) + % of MFMA/HBM roofline",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded N(0,1) q, k, v (no dataset involved)",
+        "config": {"workload": f"{args.workload}: {w.name}, causal, normaliser on", "B": w.B, "H": w.H,
+                   "Hkv": w.Hkv, "N": w.N, "d": w.d, "chunk": head["chunk"], "segments": head["segments"]},
+        "roofline": head["roofline_main"],
+        "roofline_path": head["roofline_path"],
+        "stage_us": head["stage_us"],
+        "cold": {"stage_us": head.get("cold_stage_us"), "roofline_path": head.get("cold_roofline_path")},
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -93,6 +93,23 @@ int linattn_fwd(const void *q, const void *k, const void *v, void *out,
                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * linattn_fwd_timed - linattn_fwd with stage timing for profilers and
+ * benchmarks.  Identical work and results; in addition it records
+ * events[0] on `stream` before the first stage, events[1] before the second,
+ * events[2] before the third and events[3] after the last.  The stages are:
+ *   causal:     segment totals, segment prefix scan, chunked main pass;
+ *   non-causal: segment totals, sum of the totals, application to the queries.
+ * A stage the plan does not need is skipped (its two events coincide).
+ * `events` points to n_events == 4 events created by the caller
+ * (hipEventCreate); otherwise LINATTN_ERR_NULL is returned.
+ */
+int linattn_fwd_timed(const void *q, const void *k, const void *v, void *out,
+                      int B, int H, int Hkv, int N, int d, int causal, int normalise, int dtype,
+                      float *state_out, float *z_out, int chunk,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream,
+                      hipEvent_t *events, int n_events);
+
+/*
  * linattn_fwd_workspace_bytes - scratch size linattn_fwd needs for these
  * arguments (0 when none).  Returns (size_t)-1 for invalid arguments.
  * The scratch holds one fp32 partial state and normaliser, d*(d+1) floats,

@@ -46,6 +46,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() also drains
+// every outstanding global load (vmcnt), which would stall the register
+// prefetch of the next chunk at each barrier; here only LDS traffic
+// (lgkmcnt) is waited for, and the prefetched loads stay in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // phi(x) = ELU(x) + 1 (alpha = 1): x + 1 for x > 0, exp(x) otherwise.
 __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void k_seg_totals(const T *__restrict__ k
     for (int c = nch - 1; c >= 0; --c) {
         const int t0 = s0 + c * C;
         stage_chunk<T, D, C, false>(kr, vr, sK, sKT, sVT, t0, N, tid);
-        __syncthreads();
+        lds_barrier();
         if (c > 0) {
             load_chunk<T, D, C>(kr, kb, t0 - C, N, tid);
             load_chunk<T, D, C>(vr, vb, t0 - C, N, tid);
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void k_seg_totals(const T *__restrict__ k
                 zacc[i] += state_update<T, D, C>(acc[i], it, jt, jt == 0, sKT, sVT, h, n);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
     float *out = ws + ((size_t)seq * nslots + p) * (size_t)D * (D + 1);
 #pragma unroll
@@ -304,9 +310,17 @@ __global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, i
     if (e >= E) return;
     float *base = ws + (size_t)seq * nslots * E + e;
     float acc = 0.f;
-    for (int p = 0; p < nslots; ++p) {
-        acc += base[(size_t)p * E];
-        if (mode == 0) base[(size_t)p * E] = acc;
+    // Batches of independent loads, then the running sum over the batch.
+    constexpr int BATCH = 16;
+    for (int p0 = 0; p0 < nslots; p0 += BATCH) {
+        float x[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) x[j] = p0 + j < nslots ? base[(size_t)(p0 + j) * E] : 0.f;
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            acc += x[j];
+            if (mode == 0 && p0 + j < nslots) base[(size_t)(p0 + j) * E] = acc;
+        }
     }
     if (mode == 1) {
         base[0] = acc;
@@ -417,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void k_causal_chunks(
     for (int c = 0; c < nch; ++c) {
         const int t0 = s0 + c * C;
         stage_chunk<T, D, C, true>(kr, vr, sK, sKT, sVT, t0, N, tid);
-        __syncthreads();
+        lds_barrier();
         if (c + 1 < nch) {
             load_chunk<T, D, C>(kr, kb, t0 + C, N, tid);
             load_chunk<T, D, C>(vr, vb, t0 + C, N, tid);
@@ -511,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void k_causal_chunks(
                 zr[i] += state_update<T, D, C>(S[i], it, jt, jt == 0, sKT, sVT, h, n);
             }
         }
-        __syncthreads();
+        lds_barrier();
         publish_state();
     }
 
@@ -702,9 +716,15 @@ int launch_status()
     return hipGetLastError() == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
 }
 
+// ev (nullable): 4 events recorded before each of the three stages and after the last.
+int record(hipEvent_t *ev, int i, hipStream_t st)
+{
+    return (ev && hipEventRecord(ev[i], st) != hipSuccess) ? LINATTN_ERR_HIP : LINATTN_OK;
+}
+
 template <typename T, int D, int C>
 int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out, float *state_out,
-            float *z_out, float *ws, int normalise, hipStream_t st)
+            float *z_out, float *ws, int normalise, hipStream_t st, hipEvent_t *ev)
 {
     const T *qq = static_cast<const T *>(q);
     const T *kk = static_cast<const T *>(k);
@@ -712,25 +732,30 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
     T *oo = static_cast<T *>(out);
     const int P = pl.segments;
     const int E = D * D + D;
+    if (record(ev, 0, st)) return LINATTN_ERR_HIP;
     if (pl.causal) {
-        if (P > 1) {
+        if (P > 1)
             hipLaunchKernelGGL((k_seg_totals<T, D, C>), dim3(pl.nseq * (P - 1)), dim3(kThreads), 0, st, kk, vv, ws,
                                pl.N, pl.seg_len, P - 1);
-            if (P > 2)
-                hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st,
-                                   ws, P - 1, D, 0, (float *)nullptr, (float *)nullptr);
-        }
+        if (record(ev, 1, st)) return LINATTN_ERR_HIP;
+        if (P > 2)
+            hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, ws,
+                               P - 1, D, 0, (float *)nullptr, (float *)nullptr);
+        if (record(ev, 2, st)) return LINATTN_ERR_HIP;
         hipLaunchKernelGGL((k_causal_chunks<T, D, C>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo,
                            (const float *)ws, state_out, z_out, pl.H, pl.Hkv, pl.N, pl.G, P, pl.seg_len, normalise);
     } else {
         hipLaunchKernelGGL((k_seg_totals<T, D, C>), dim3(pl.nseq * P), dim3(kThreads), 0, st, kk, vv, ws, pl.N,
                            pl.seg_len, P);
+        if (record(ev, 1, st)) return LINATTN_ERR_HIP;
         hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, ws, P,
                            D, 1, state_out, z_out);
+        if (record(ev, 2, st)) return LINATTN_ERR_HIP;
         const int nblk = (pl.N + 127) / 128;
         hipLaunchKernelGGL((k_noncausal_apply<T, D>), dim3(pl.nseq * nblk), dim3(kThreads), 0, st, qq, oo,
                            (const float *)ws, P, pl.H, pl.Hkv, pl.N, pl.G, nblk, normalise);
     }
+    if (record(ev, 3, st)) return LINATTN_ERR_HIP;
     return launch_status();
 }
 
@@ -739,20 +764,20 @@ constexpr bool lds_fits() { return sizeof(T) * (3 * C * D + D * D) + 4 * D <= 16
 
 template <typename T, int D>
 int dispatch_chunk(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,
-                   float *state_out, float *z_out, float *ws, int normalise, hipStream_t st)
+                   float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, hipEvent_t *ev)
 {
     switch (pl.chunk) {
     case 32:
-        if constexpr (lds_fits<T, D, 32>()) return run_fwd<T, D, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st);
+        if constexpr (lds_fits<T, D, 32>()) return run_fwd<T, D, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
         break;
     case 64:
-        if constexpr (lds_fits<T, D, 64>()) return run_fwd<T, D, 64>(pl, q, k, v, out, state_out, z_out, ws, normalise, st);
+        if constexpr (lds_fits<T, D, 64>()) return run_fwd<T, D, 64>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
         break;
     case 128:
-        if constexpr (lds_fits<T, D, 128>()) return run_fwd<T, D, 128>(pl, q, k, v, out, state_out, z_out, ws, normalise, st);
+        if constexpr (lds_fits<T, D, 128>()) return run_fwd<T, D, 128>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
         break;
     case 256:
-        if constexpr (lds_fits<T, D, 256>()) return run_fwd<T, D, 256>(pl, q, k, v, out, state_out, z_out, ws, normalise, st);
+        if constexpr (lds_fits<T, D, 256>()) return run_fwd<T, D, 256>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
         break;
     }
     return LINATTN_ERR_UNSUPPORTED;
@@ -760,12 +785,12 @@ int dispatch_chunk(const linattn::Plan &pl, const void *q, const void *k, const 
 
 template <typename T>
 int dispatch_d(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,
-               float *state_out, float *z_out, float *ws, int normalise, hipStream_t st)
+               float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, hipEvent_t *ev)
 {
     switch (pl.d) {
-    case 32: return dispatch_chunk<T, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st);
-    case 64: return dispatch_chunk<T, 64>(pl, q, k, v, out, state_out, z_out, ws, normalise, st);
-    case 128: return dispatch_chunk<T, 128>(pl, q, k, v, out, state_out, z_out, ws, normalise, st);
+    case 32: return dispatch_chunk<T, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
+    case 64: return dispatch_chunk<T, 64>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
+    case 128: return dispatch_chunk<T, 128>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
     }
     return LINATTN_ERR_UNSUPPORTED;
 }
@@ -832,9 +857,12 @@ size_t linattn_fwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int caus
     return pl.ws_bytes;
 }
 
-int linattn_fwd(const void *q, const void *k, const void *v, void *out, int B, int H, int Hkv, int N, int d,
-                int causal, int normalise, int dtype, float *state_out, float *z_out, int chunk, void *workspace,
-                size_t workspace_bytes, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+int fwd_impl(const void *q, const void *k, const void *v, void *out, int B, int H, int Hkv, int N, int d, int causal,
+             int normalise, int dtype, float *state_out, float *z_out, int chunk, void *workspace,
+             size_t workspace_bytes, hipStream_t stream, hipEvent_t *ev)
 {
     linattn::Plan pl;
     const int rc = linattn::make_plan(B, H, Hkv, N, d, causal, dtype, chunk, &pl);
@@ -853,8 +881,39 @@ int linattn_fwd(const void *q, const void *k, const void *v, void *out, int B, i
         return launch_status();
     }
     float *ws = static_cast<float *>(workspace);
-    if (dtype == LINATTN_BF16) return dispatch_d<bf16>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream);
-    return dispatch_d<float>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream);
+    if (dtype == LINATTN_BF16)
+        return dispatch_d<bf16>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream, ev);
+    return dispatch_d<float>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream, ev);
+}
+}  // namespace
+
+extern "C" {
+
+int linattn_fwd(const void *q, const void *k, const void *v, void *out, int B, int H, int Hkv, int N, int d,
+                int causal, int normalise, int dtype, float *state_out, float *z_out, int chunk, void *workspace,
+                size_t workspace_bytes, hipStream_t stream)
+{
+    return fwd_impl(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_out, z_out, chunk, workspace,
+                    workspace_bytes, stream, nullptr);
+}
+
+int linattn_fwd_timed(const void *q, const void *k, const void *v, void *out, int B, int H, int Hkv, int N, int d,
+                      int causal, int normalise, int dtype, float *state_out, float *z_out, int chunk,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events, int n_events)
+{
+    if (!events || n_events != 4) return LINATTN_ERR_NULL;
+    for (int i = 0; i < 4; ++i)
+        if (!events[i]) return LINATTN_ERR_NULL;
+    if (B > 0 && N > 0)
+        return fwd_impl(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_out, z_out, chunk,
+                        workspace, workspace_bytes, stream, events);
+    // Nothing to stage: every event marks the same point.
+    const int rc = fwd_impl(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_out, z_out, chunk,
+                            workspace, workspace_bytes, stream, nullptr);
+    if (rc != LINATTN_OK) return rc;
+    for (int i = 0; i < 4; ++i)
+        if (record(events, i, stream)) return LINATTN_ERR_HIP;
+    return LINATTN_OK;
 }
 
 int linattn_decode_step(float *state, float *z, const void *q, const void *k, const void *v, void *out, int B, int H,
