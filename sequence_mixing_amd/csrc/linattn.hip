@@ -52,8 +52,12 @@ constexpr int kThreads = 256;
 // (lgkmcnt) is waited for, and the prefetched loads stay in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// phi(x) = ELU(x) + 1 (alpha = 1): x + 1 for x > 0, exp(x) otherwise.
-__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+// phi(x) = ELU(x) + 1 (alpha = 1): x + 1 for x > 0, exp(x) otherwise,
+// written without a branch as max(x, 0) + exp(min(x, 0)) (one v_exp_f32).
+__device__ __forceinline__ float phi(float x)
+{
+    return fmaxf(x, 0.f) + __builtin_amdgcn_exp2f(fminf(x, 0.f) * 1.44269504088896340736f);
+}
 
 // ------------------------------------------------------------------ types
 
@@ -107,58 +111,92 @@ template <> __device__ __forceinline__ f32x4 cvt4<float>(f32x4 x) { return x; }
 
 // ---------------------------------------------------------- LDS tiles
 //
-// Tiles are stored row-major with 16-byte groups permuted inside each row:
-// element (r, c) lives at r * COLS + (c ^ (sig(r) * U)).  The XOR moves whole
-// 16-byte groups, so 4- and 8-element runs that start on a 4-aligned column
-// stay contiguous (fp32: an 8-run spans two groups and is read as two).
+// Row-major tiles whose 16-byte groups are XOR-permuted per row: element
+// (r, c) lives at r * COLS + (c ^ (sig(r) * U)), sig(r) = r % (COLS / U).
+// Runs of 4 or 8 elements starting on a 4-aligned column stay contiguous
+// (an fp32 8-run spans two groups and is read as two), and both row walks
+// and column walks spread over the LDS banks.
 
 template <typename E, int COLS>
-struct LdsTile {
+struct Tile {
     E *p;
     static constexpr int U = Vt<E>::U;
-    __device__ __forceinline__ int at(int r, int c, int sig) const { return r * COLS + (c ^ (sig * U)); }
-    __device__ __forceinline__ typename Vt<E>::v8 read8(int r, int c, int sig) const
+    static constexpr int NG = COLS / U;
+    __device__ __forceinline__ static int sig(int r) { return r % NG; }
+    __device__ __forceinline__ int at(int r, int c) const { return r * COLS + (c ^ (sig(r) * U)); }
+    __device__ __forceinline__ typename Vt<E>::v8 read8(int r, int c) const
     {
         if constexpr (U == 8) {
-            return *reinterpret_cast<const bf16x8 *>(p + at(r, c, sig));
+            return *reinterpret_cast<const bf16x8 *>(p + at(r, c));
         } else {
-            return cat(*reinterpret_cast<const f32x4 *>(p + at(r, c, sig)),
-                       *reinterpret_cast<const f32x4 *>(p + at(r, c + 4, sig)));
+            return cat(*reinterpret_cast<const f32x4 *>(p + at(r, c)), *reinterpret_cast<const f32x4 *>(p + at(r, c + 4)));
         }
     }
-    __device__ __forceinline__ typename Vt<E>::v4 read4(int r, int c, int sig) const
+    __device__ __forceinline__ void write4(int r, int c, typename Vt<E>::v4 x) const
     {
-        return *reinterpret_cast<const typename Vt<E>::v4 *>(p + at(r, c, sig));
+        *reinterpret_cast<typename Vt<E>::v4 *>(p + at(r, c)) = x;
     }
-    __device__ __forceinline__ void write4(int r, int c, int sig, typename Vt<E>::v4 x) const
+    __device__ __forceinline__ void write16(int r, int c, typename Vt<E>::g16 x) const
     {
-        *reinterpret_cast<typename Vt<E>::v4 *>(p + at(r, c, sig)) = x;
+        *reinterpret_cast<typename Vt<E>::g16 *>(p + at(r, c)) = x;
     }
-    __device__ __forceinline__ void write16(int r, int c, int sig, typename Vt<E>::g16 x) const
-    {
-        *reinterpret_cast<typename Vt<E>::g16 *>(p + at(r, c, sig)) = x;
-    }
-    __device__ __forceinline__ void write1(int r, int c, int sig, E x) const { p[at(r, c, sig)] = x; }
 };
 
-// Shapes and swizzles shared by the chunk kernels.
+// Column fragment of an MFMA operand out of a row-major tile: lane
+// (h = lane/32, x = lane%32) gets rows ra + e and rb + e (e = 0..3; ra, rb
+// depend on h only) of column col + x, as slots 0..3 and 4..7.
+//
+// bf16 uses ds_read_b64_tr_b16: inside each 16-lane group, lane j receives
+// element j%4 of the 8-byte reads issued by lanes j/4, j/4+4, j/4+8, j/4+12,
+// so lane j supplies the address of row r0 + j/4, columns c0 + 4(j%4).
+// fp32 reads one word per slot (32 lanes walk consecutive columns).
+template <int COLS>
+__device__ __forceinline__ bf16x8 colfrag(const Tile<bf16, COLS> &t, int ra, int rb, int col, int lane)
+{
+    const int j = lane & 15;
+    const int c0 = col + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+    typedef __attribute__((address_space(3))) bf16x4 *lds4;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4)(t.p + t.at(ra + (j >> 2), c0)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4)(t.p + t.at(rb + (j >> 2), c0)));
+    return cat(lo, hi);
+}
+template <int COLS>
+__device__ __forceinline__ f32x8 colfrag(const Tile<float, COLS> &t, int ra, int rb, int col, int lane)
+{
+    const int c = col + (lane & 31);
+    f32x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = t.p[t.at(ra + e, c)];
+        r[4 + e] = t.p[t.at(rb + e, c)];
+    }
+    return r;
+}
+
+// Shapes shared by the chunk kernels.
 template <typename T, int D, int C>
 struct Geo {
-    using E = T;
-    static constexpr int U = Vt<E>::U;       // elements per 16 bytes (== per global vector load)
+    static constexpr int U = Vt<T>::U;       // elements per 16 bytes (one global vector load)
     static constexpr int DT = D / 32;        // 32-wide feature tiles
     static constexpr int CT = C / 32;        // 32-row token tiles per chunk
     static constexpr int KBD = D / 16;       // K-blocks over features
-    static constexpr int KBC = C / 16;       // K-blocks over chunk tokens
     static constexpr int NST = DT * DT;      // 32x32 state tiles
     static constexpr int MAXST = (NST + 3) / 4;  // state tiles per wave
     static constexpr int GPR = D / U;        // 16-byte groups per token row
     static constexpr int NGRP = C * GPR;     // 16-byte groups per chunk per tensor
     static constexpr int LDV = (NGRP + kThreads - 1) / kThreads;  // groups per thread
-    // swizzles: token-major tiles (rows = tokens or state columns, D columns)
-    __device__ static int sig_rowD(int r) { return r % (D / U); }
-    // feature-major tiles (rows = features, C token columns)
-    __device__ static int sig_rowC(int f) { return (f + f / U) % (C / U); }
+    static constexpr int QV = 8 / U;         // 16-byte groups per 8-element fragment
+    static constexpr size_t KV_BYTES = (size_t)C * D * sizeof(T);
+    static constexpr size_t ST_BYTES = (size_t)CT * D * D * sizeof(T) + (size_t)CT * D * 4;
+    // Double-buffer the K/V tiles when two workgroups still fit on a CU (or
+    // when even one buffer would not leave room for two).
+    static constexpr size_t LDS_CU = 160 * 1024;
+    static constexpr bool FITS = 2 * KV_BYTES + ST_BYTES <= LDS_CU;
+    static constexpr bool DB = 4 * KV_BYTES + ST_BYTES <= LDS_CU / 2 ||
+                               (2 * KV_BYTES + ST_BYTES > LDS_CU / 2 && 4 * KV_BYTES + ST_BYTES <= LDS_CU);
+    // State tile i of wave w is st = w * MAXST + i (d = 128: row block w);
+    // only tile 0 of a wave can sit in column block 0 and own z.
+    __device__ static int tile_of(int w, int i) { return w * MAXST + i; }
 };
 
 // Loads the 16-byte groups of one chunk of a [N][D] sequence (zeros past N).
@@ -167,123 +205,141 @@ __device__ __forceinline__ void load_chunk(typename Vt<T>::g16 (&r)[L], const T 
 {
     using G = Geo<T, D, C>;
     static_assert(L == G::LDV, "register array size");
+    using g16 = typename Vt<T>::g16;
+    if (t0 + C <= N && G::NGRP % kThreads == 0) {
 #pragma unroll
-    for (int l = 0; l < G::LDV; ++l) {
-        const int e = tid + l * kThreads;
-        const int t = e / G::GPR, q = e % G::GPR;
-        typename Vt<T>::g16 x = {};
-        if (e < G::NGRP && t0 + t < N)
-            x = *reinterpret_cast<const typename Vt<T>::g16 *>(base + (size_t)(t0 + t) * D + q * G::U);
-        r[l] = x;
+        for (int l = 0; l < G::LDV; ++l) {
+            const int e = tid + l * kThreads;
+            r[l] = *reinterpret_cast<const g16 *>(base + (size_t)(t0 + e / G::GPR) * D + (e % G::GPR) * G::U);
+        }
+    } else {
+#pragma unroll
+        for (int l = 0; l < G::LDV; ++l) {
+            const int e = tid + l * kThreads;
+            const int t = e / G::GPR, q = e % G::GPR;
+            g16 x = {};
+            if (e < G::NGRP && t0 + t < N) x = *reinterpret_cast<const g16 *>(base + (size_t)(t0 + t) * D + q * G::U);
+            r[l] = x;
+        }
     }
 }
 
-// Writes a staged chunk to LDS: phi(K) row-major (optional), phi(K)^T, V^T.
-// Tokens at or past N get phi(k) = 0 so that they add nothing to any sum.
-template <typename T, int D, int C, bool ROWK, int L>
-__device__ __forceinline__ void stage_chunk(const typename Vt<T>::g16 (&kr)[L], const typename Vt<T>::g16 (&vr)[L],
-                                            LdsTile<T, D> sK, LdsTile<T, C> sKT, LdsTile<T, C> sVT,
-                                            int t0, int N, int tid)
+// Writes a staged chunk to LDS: phi(K) and V, both row-major.  Tokens at or
+// past N get phi(k) = 0 (and v = 0) so that they add nothing to any sum.
+template <typename T, int D, int C, int L>
+__device__ __forceinline__ void stage_rows(const typename Vt<T>::g16 (&kr)[L], const typename Vt<T>::g16 (&vr)[L],
+                                           Tile<T, D> sK, Tile<T, D> sV, int t0, int N, int tid)
 {
     using G = Geo<T, D, C>;
     static_assert(L == G::LDV, "register array size");
+    const bool full = t0 + C <= N;
 #pragma unroll
     for (int l = 0; l < G::LDV; ++l) {
         const int e = tid + l * kThreads;
-        if (e < G::NGRP) {
+        if (G::NGRP % kThreads == 0 || e < G::NGRP) {
             const int t = e / G::GPR, q = e % G::GPR;
-            const bool valid = t0 + t < N;
             typename Vt<T>::g16 fk;
 #pragma unroll
-            for (int i = 0; i < G::U; ++i) fk[i] = valid ? (T)phi((float)kr[l][i]) : (T)0.f;
-            if constexpr (ROWK) sK.write16(t, q * G::U, G::sig_rowD(t), fk);
-#pragma unroll
-            for (int i = 0; i < G::U; ++i) {
-                const int f = q * G::U + i;
-                sKT.write1(f, t, G::sig_rowC(f), fk[i]);
-                sVT.write1(f, t, G::sig_rowC(f), vr[l][i]);
-            }
+            for (int i = 0; i < G::U; ++i) fk[i] = (T)phi((float)kr[l][i]);
+            if (!full && t0 + t >= N) fk = typename Vt<T>::g16{};
+            sK.write16(t, q * G::U, fk);
+            sV.write16(t, q * G::U, vr[l]);
         }
     }
 }
 
-// S tile (it, jt) += phi(K)^T V over the chunk; optionally the column sums
-// of phi(K) for features it*32 + n (returned per lane, both half-waves equal).
-template <typename T, int D, int C>
-__device__ __forceinline__ float state_update(f32x16 &acc, int it, int jt, bool want_z,
-                                              LdsTile<T, C> sKT, LdsTile<T, C> sVT, int h, int n)
+// A K-block operand whose every slot is 1 (for column sums on MFMA).
+template <typename T> __device__ __forceinline__ typename Vt<T>::v8 ones8()
 {
-    using G = Geo<T, D, C>;
-    const int fi = it * 32 + n, fj = jt * 32 + n;
+    typename Vt<T>::v8 o;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) o[s] = (T)1.f;
+    return o;
+}
+
+// State tile (it, jt) += phi(K)^T V over the 32 tokens of key tile kt.
+// The K-block of 16 tokens kb2 puts token kt*32 + 16 kb2 + 8h + s in slot s.
+// When want_z, the column sums of phi(K) are formed too: bf16 adds 1 phi(K)
+// into Z on the matrix core (every accumulator register of lane (h, x) then
+// holds sum_t phi(k_t) of feature it*32 + x); fp32 returns this half-wave's
+// partial sum for feature it*32 + x (the caller adds the other half).
+template <typename T, int D>
+__device__ __forceinline__ float tile_state_update(f32x16 &acc, f32x16 &Z, bool want_z, int it, int jt, int kt,
+                                                   Tile<T, D> sK, Tile<T, D> sV, int lane)
+{
+    const int h = lane >> 5;
     float zs = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < G::KBC; ++kb) {
-        const auto a = sKT.read8(fi, kb * 16 + h * 8, G::sig_rowC(fi));
-        const auto b = sVT.read8(fj, kb * 16 + h * 8, G::sig_rowC(fj));
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const int r0 = kt * 32 + 16 * kb2 + 8 * h;
+        const auto a = colfrag(sK, r0, r0 + 4, it * 32, lane);
+        const auto b = colfrag(sV, r0, r0 + 4, jt * 32, lane);
         mma(acc, a, b);
         if (want_z) {
+            if constexpr (sizeof(T) == 2) {
+                mma(Z, ones8<T>(), a);
+            } else {
 #pragma unroll
-            for (int s = 0; s < 8; ++s) zs += (float)a[s];
+                for (int s = 0; s < 8; ++s) zs += a[s];
+            }
         }
     }
-    if (want_z) zs += __shfl_xor(zs, 32);
     return zs;
 }
 
 // -------------------------------------------------------------- seg_totals
-
-template <typename T, int D, int C>
-__global__ __launch_bounds__(kThreads) void k_seg_totals(const T *__restrict__ k, const T *__restrict__ v,
-                                                         float *__restrict__ ws, int N, int seg_len,
-                                                         int nslots)
+//
+// One workgroup per (sequence, segment): T_p = phi(K_p)^T V_p and
+// sum phi(K_p), written as fp32 partials ws[seq][p] = [S (d x d) | z (d)].
+// Chunks of C1 tokens, double-buffered in LDS (one barrier per chunk).
+template <typename T, int D, int C1>
+__global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict__ k, const T *__restrict__ v,
+                                                            float *__restrict__ ws, int N, int seg_len, int nslots)
 {
-    using G = Geo<T, D, C>;
-    __shared__ __attribute__((aligned(16))) T smKT[D * C];
-    __shared__ __attribute__((aligned(16))) T smVT[D * C];
-    LdsTile<T, D> sK{nullptr};
-    LdsTile<T, C> sKT{smKT}, sVT{smVT};
+    using G = Geo<T, D, C1>;
+    __shared__ __attribute__((aligned(16))) T smK[2][C1 * D];
+    __shared__ __attribute__((aligned(16))) T smV[2][C1 * D];
 
     const int seq = blockIdx.x / nslots, p = blockIdx.x % nslots;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
     const T *kb = k + (size_t)seq * N * D;
     const T *vb = v + (size_t)seq * N * D;
     const int s0 = p * seg_len, s1 = min(N, s0 + seg_len);
-    const int nch = (s1 - s0 + C - 1) / C;
+    const int nch = (s1 - s0 + C1 - 1) / C1;
 
-    f32x16 acc[G::MAXST];
-    float zacc[G::MAXST];
+    f32x16 acc[G::MAXST], Z = f32x16{};
+    float zacc = 0.f;
 #pragma unroll
-    for (int i = 0; i < G::MAXST; ++i) {
-        acc[i] = f32x16{};
-        zacc[i] = 0.f;
-    }
+    for (int i = 0; i < G::MAXST; ++i) acc[i] = f32x16{};
     typename Vt<T>::g16 kr[G::LDV], vr[G::LDV];
     // Walk the segment backwards: the main pass then starts on the chunks
     // read most recently, which are the likeliest still to be cached.
-    load_chunk<T, D, C>(kr, kb, s0 + (nch - 1) * C, N, tid);
-    load_chunk<T, D, C>(vr, vb, s0 + (nch - 1) * C, N, tid);
-    for (int c = nch - 1; c >= 0; --c) {
-        const int t0 = s0 + c * C;
-        stage_chunk<T, D, C, false>(kr, vr, sK, sKT, sVT, t0, N, tid);
-        lds_barrier();
+    load_chunk<T, D, C1>(kr, kb, s0 + (nch - 1) * C1, N, tid);
+    load_chunk<T, D, C1>(vr, vb, s0 + (nch - 1) * C1, N, tid);
+    for (int ci = 0; ci < nch; ++ci) {
+        const int c = nch - 1 - ci, buf = ci & 1;
+        const Tile<T, D> sK{smK[buf]}, sV{smV[buf]};
+        stage_rows<T, D, C1>(kr, vr, sK, sV, s0 + c * C1, N, tid);
         if (c > 0) {
-            load_chunk<T, D, C>(kr, kb, t0 - C, N, tid);
-            load_chunk<T, D, C>(vr, vb, t0 - C, N, tid);
+            load_chunk<T, D, C1>(kr, kb, s0 + (c - 1) * C1, N, tid);
+            load_chunk<T, D, C1>(vr, vb, s0 + (c - 1) * C1, N, tid);
         }
+        lds_barrier();
 #pragma unroll
         for (int i = 0; i < G::MAXST; ++i) {
-            const int st = w + 4 * i;
+            const int st = G::tile_of(w, i);
             if (st < G::NST) {
                 const int it = st / G::DT, jt = st % G::DT;
-                zacc[i] += state_update<T, D, C>(acc[i], it, jt, jt == 0, sKT, sVT, h, n);
+#pragma unroll
+                for (int kt = 0; kt < G::CT; ++kt)
+                    zacc += tile_state_update<T, D>(acc[i], Z, i == 0 && jt == 0, it, jt, kt, sK, sV, lane);
             }
         }
-        lds_barrier();
     }
     float *out = ws + ((size_t)seq * nslots + p) * (size_t)D * (D + 1);
 #pragma unroll
     for (int i = 0; i < G::MAXST; ++i) {
-        const int st = w + 4 * i;
+        const int st = G::tile_of(w, i);
         if (st < G::NST) {
             const int it = st / G::DT, jt = st % G::DT;
 #pragma unroll
@@ -291,7 +347,10 @@ __global__ __launch_bounds__(kThreads) void k_seg_totals(const T *__restrict__ k
                 const int row = it * 32 + 8 * (r / 4) + 4 * h + (r % 4);
                 out[(size_t)row * D + jt * 32 + n] = acc[i][r];
             }
-            if (jt == 0 && h == 0) out[(size_t)D * D + it * 32 + n] = zacc[i];
+            if (i == 0 && jt == 0) {
+                const float z = sizeof(T) == 2 ? Z[0] : zacc + __shfl_xor(zacc, 32);
+                if (h == 0) out[(size_t)D * D + it * 32 + n] = z;
+            }
         }
     }
 }
@@ -333,14 +392,23 @@ __global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, i
 }
 
 // ----------------------------------------------------------- causal_chunks
-
-// Unit i of wave w (a unit is one query head and one 32-row query tile of
-// the chunk).  Snake order pairs early and late tiles on the same wave so
-// that the causal triangle's work is spread evenly.
-__device__ __forceinline__ int unit_of(int w, int i) { return 8 * (i >> 1) + ((i & 1) ? 7 - w : w); }
-
+//
+// One workgroup per (sequence, segment), walking the segment in chunks of C
+// tokens.  Per chunk:
+//   phase 1  every state tile's owner wave publishes S^T and z to LDS before
+//            each 32-token key tile of the chunk and then adds that tile's
+//            phi(K)^T V (MFMA): copy kt is the state seen by query tile kt
+//            (all keys before it).  The chunk's prefix over its key tiles is
+//            thus formed by the owners, and no query tile needs an
+//            off-diagonal key tile.
+//   phase 2  every unit (query head g, query tile r, output column group cg)
+//            computes O^T = V^T (M . phi(K) phi(Q)^T) on the diagonal 32x32
+//            tile plus S_r^T phi(Q)^T, the denominator, and stores.
+// K/V tiles are double-buffered when LDS allows (the next chunk is staged
+// during phase 2, two barriers per chunk), otherwise staged after phase 2
+// (three barriers).
 template <typename T, int D, int C>
-__global__ __launch_bounds__(kThreads) void k_causal_chunks(
+__global__ __launch_bounds__(kThreads, D * sizeof(T) <= 128 ? 2 : 1) void k_causal_chunks(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ out,
     const float *__restrict__ ws, float *__restrict__ state_out, float *__restrict__ z_out,
     int H, int Hkv, int N, int G, int P, int seg_len, int normalise)
@@ -348,205 +416,256 @@ __global__ __launch_bounds__(kThreads) void k_causal_chunks(
     using Gm = Geo<T, D, C>;
     using v8 = typename Vt<T>::v8;
     using g16 = typename Vt<T>::g16;
-    constexpr int U = Gm::U;
-    constexpr int QV = 8 / U;  // 16-byte groups per 8-element fragment
+    constexpr bool BF = sizeof(T) == 2;
+    constexpr int U = Gm::U, QV = Gm::QV, CT = Gm::CT, DT = Gm::DT, KBD = Gm::KBD;
+    constexpr int NB = Gm::DB ? 2 : 1;
+    // Units per wave whose q is fetched a chunk ahead (chunks of 128+ tokens
+    // give every wave a query tile of its own already for one head).
+    constexpr int MAXQ = (D * sizeof(T) <= 128 && C < 128) ? 2 : 1;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-    __shared__ __attribute__((aligned(16))) T smK[C * D];
-    __shared__ __attribute__((aligned(16))) T smKT[D * C];
-    __shared__ __attribute__((aligned(16))) T smVT[D * C];
-    __shared__ __attribute__((aligned(16))) T smST[D * D];
-    __shared__ float smZ[D];
-    LdsTile<T, D> sK{smK}, sST{smST};
-    LdsTile<T, C> sKT{smKT}, sVT{smVT};
+    __shared__ __attribute__((aligned(16))) T smK[NB][C * D];
+    __shared__ __attribute__((aligned(16))) T smV[NB][C * D];
+    __shared__ __attribute__((aligned(16))) T smST[CT][D * D];
+    __shared__ __attribute__((aligned(16))) T smZ[CT][D];
 
     const int seq = blockIdx.x / P, p = blockIdx.x % P;
     const int b = seq / Hkv, gk = seq % Hkv;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
     const T *kb = k + (size_t)seq * N * D;
     const T *vb = v + (size_t)seq * N * D;
-    const T *qb = q + ((size_t)b * H + (size_t)gk * G) * N * D;  // head g of the group: + g * N * D
+    const T *qb = q + ((size_t)b * H + (size_t)gk * G) * N * D;
     T *ob = out + ((size_t)b * H + (size_t)gk * G) * N * D;
     const int s0 = p * seg_len, s1 = min(N, s0 + seg_len);
     const int nch = (s1 - s0 + C - 1) / C;
-    const int NU = G * Gm::CT;
+    // Units: (head g, query tile r, column group cg); NCG column groups when
+    // the chunk has fewer than four (head, tile) pairs for the four waves.
+    const int GR = G * CT;
+    const int NCG = GR >= 4 ? 1 : (4 / GR < DT ? 4 / GR : DT);
+    const int NU = GR * NCG;
+    const int CPG = DT / NCG;  // column tiles per group
 
     // ---- the state this segment starts from
-    f32x16 S[Gm::MAXST];
-    float zr[Gm::MAXST];
+    f32x16 S[Gm::MAXST], Z = f32x16{};
+    float zr = 0.f;
     const float *init = p > 0 ? ws + ((size_t)seq * (P - 1) + (p - 1)) * (size_t)D * (D + 1) : nullptr;
 #pragma unroll
     for (int i = 0; i < Gm::MAXST; ++i) {
         S[i] = f32x16{};
-        zr[i] = 0.f;
-        const int st = w + 4 * i;
+        const int st = Gm::tile_of(w, i);
         if (st < Gm::NST && init) {
-            const int it = st / Gm::DT, jt = st % Gm::DT;
+            const int it = st / DT, jt = st % DT;
 #pragma unroll
             for (int r = 0; r < 16; ++r) S[i][r] = init[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n];
-            if (jt == 0) zr[i] = init[(size_t)D * D + it * 32 + n];
+            if (i == 0 && jt == 0) zr = init[(size_t)D * D + it * 32 + n];
         }
     }
-    // Publish S^T and z to LDS.
-    auto publish_state = [&]() {
 #pragma unroll
-        for (int i = 0; i < Gm::MAXST; ++i) {
-            const int st = w + 4 * i;
-            if (st < Gm::NST) {
-                const int it = st / Gm::DT, jt = st % Gm::DT;
-                const int row = jt * 32 + n;
+    for (int r = 0; r < 16; ++r) Z[r] = zr;
+    // Causal mask of the diagonal tile for packed bf16 pairs: accumulator reg
+    // i holds key 8(i/4) + 4h + i%4 for query n.
+    uint32_t mk[8];
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    f32x4 x{S[i][4 * q4], S[i][4 * q4 + 1], S[i][4 * q4 + 2], S[i][4 * q4 + 3]};
-                    sST.write4(row, it * 32 + 8 * q4 + 4 * h, Gm::sig_rowD(row), cvt4<T>(x));
-                }
-                if (jt == 0 && h == 0) smZ[it * 32 + n] = zr[i];
-            }
-        }
-    };
-    publish_state();
+    for (int pp = 0; pp < 8; ++pp) {
+        const int i0 = 2 * pp, i1 = 2 * pp + 1;
+        const uint32_t m0 = (8 * (i0 / 4) + 4 * h + (i0 % 4) <= n) ? 0xFFFFu : 0u;
+        const uint32_t m1 = (8 * (i1 / 4) + 4 * h + (i1 % 4) <= n) ? 0xFFFF0000u : 0u;
+        mk[pp] = m0 | m1;
+    }
 
-    // ---- prefetch of the first chunk
     g16 kr[Gm::LDV], vr[Gm::LDV];
-    g16 qr[Gm::KBD * QV];  // raw q of this wave's first unit, fetched one chunk ahead
-    auto load_q = [&](auto &dst, int u, int t0) {
-        const int g = u / Gm::CT, r = u % Gm::CT;
+    g16 qr[MAXQ][KBD * QV];
+    auto load_q = [&](g16 *dst, int u, int t0) {
+        const int g = u / (CT * NCG), r = (u / NCG) % CT;
         const int t = t0 + r * 32 + n;
         const T *src = qb + (size_t)g * N * D + (size_t)t * D;
+        if (t0 + r * 32 + 32 <= N) {
 #pragma unroll
-        for (int kb = 0; kb < Gm::KBD; ++kb) {
+            for (int kq = 0; kq < KBD; ++kq)
 #pragma unroll
-            for (int j = 0; j < QV; ++j) {
-                g16 x = {};
-                if (t < N) x = *reinterpret_cast<const g16 *>(src + kb * 16 + h * 8 + j * U);
-                dst[kb * QV + j] = x;
-            }
+                for (int j = 0; j < QV; ++j) dst[kq * QV + j] = *reinterpret_cast<const g16 *>(src + kq * 16 + h * 8 + j * U);
+        } else {
+#pragma unroll
+            for (int kq = 0; kq < KBD; ++kq)
+#pragma unroll
+                for (int j = 0; j < QV; ++j) {
+                    g16 x = {};
+                    if (t < N) x = *reinterpret_cast<const g16 *>(src + kq * 16 + h * 8 + j * U);
+                    dst[kq * QV + j] = x;
+                }
         }
     };
-    if (nch > 0) {
-        load_chunk<T, D, C>(kr, kb, s0, N, tid);
-        load_chunk<T, D, C>(vr, vb, s0, N, tid);
-        if (unit_of(w, 0) < NU) load_q(qr, unit_of(w, 0), s0);
+
+    // ---- prologue: chunk 0 staged, chunk 1 and the first q tiles in flight
+    load_chunk<T, D, C>(kr, kb, s0, N, tid);
+    load_chunk<T, D, C>(vr, vb, s0, N, tid);
+#pragma unroll
+    for (int i = 0; i < MAXQ; ++i)
+        if (w + 4 * i < NU) load_q(qr[i], w + 4 * i, s0);
+    stage_rows<T, D, C>(kr, vr, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, s0, N, tid);
+    if (nch > 1) {
+        load_chunk<T, D, C>(kr, kb, s0 + C, N, tid);
+        load_chunk<T, D, C>(vr, vb, s0 + C, N, tid);
     }
+    lds_barrier();
 
     for (int c = 0; c < nch; ++c) {
         const int t0 = s0 + c * C;
-        stage_chunk<T, D, C, true>(kr, vr, sK, sKT, sVT, t0, N, tid);
+        const int buf = Gm::DB ? (c & 1) : 0;
+        const Tile<T, D> sK{smK[buf]}, sV{smV[buf]};
+
+        // ---- phase 1: per key tile, publish the state then absorb the tile
+#pragma unroll
+        for (int i = 0; i < Gm::MAXST; ++i) {
+            const int st = Gm::tile_of(w, i);
+            if (st < Gm::NST) {
+                const int it = st / DT, jt = st % DT;
+                const bool zown = i == 0 && jt == 0;
+                const int row = jt * 32 + n;
+                float zs = 0.f;
+#pragma unroll
+                for (int kt = 0; kt < CT; ++kt) {
+                    const Tile<T, D> sST{smST[kt]};
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        f32x4 x{S[i][4 * q4], S[i][4 * q4 + 1], S[i][4 * q4 + 2], S[i][4 * q4 + 3]};
+                        sST.write4(row, it * 32 + 8 * q4 + 4 * h, cvt4<T>(x));
+                    }
+                    if (zown && h == 0) smZ[kt][it * 32 + n] = (T)(BF ? Z[0] : zr + zs);
+                    const float dz = tile_state_update<T, D>(S[i], Z, zown, it, jt, kt, sK, sV, lane);
+                    if (!BF && zown) zs += dz + __shfl_xor(dz, 32);
+                }
+                if (zown) zr += zs;
+            }
+        }
         lds_barrier();
+
+        // ---- the next chunk: stage it into the free buffer, fetch the one after
         if (c + 1 < nch) {
-            load_chunk<T, D, C>(kr, kb, t0 + C, N, tid);
-            load_chunk<T, D, C>(vr, vb, t0 + C, N, tid);
+            if (Gm::DB) {
+                stage_rows<T, D, C>(kr, vr, Tile<T, D>{smK[buf ^ 1]}, Tile<T, D>{smV[buf ^ 1]}, t0 + C, N, tid);
+                if (c + 2 < nch) {
+                    load_chunk<T, D, C>(kr, kb, t0 + 2 * C, N, tid);
+                    load_chunk<T, D, C>(vr, vb, t0 + 2 * C, N, tid);
+                }
+            }
         }
 
-        // ---- query tiles of this chunk
-        for (int ui = 0;; ++ui) {
-            const int u = unit_of(w, ui);
-            if (u >= NU) break;
-            const int g = u / Gm::CT, r = u % Gm::CT;
-            if (t0 + r * 32 >= N) continue;  // tile entirely past the end
-            g16 qx[Gm::KBD * QV];
-            if (ui > 0) load_q(qx, u, t0);
-            // phi(q) fragments: lane (h, n) holds query n, features kb*16 + 8h + s.
-            v8 qf[Gm::KBD];
-            float dq = 0.f;  // phi(q) . z over this half-wave's features
+        // ---- phase 2: query tiles
+        auto unit = [&](int u, const g16 *qsrc, g16 *qnext) {
+            const int g = u / (CT * NCG), r = (u / NCG) % CT, cg = u % NCG;
+            if (t0 + r * 32 >= N) return;  // tile entirely past the end
+            // phi(q) fragments: lane (h, n) holds query n, features kq*16 + 8h + s.
+            v8 qf[KBD];
 #pragma unroll
-            for (int kb = 0; kb < Gm::KBD; ++kb) {
+            for (int kq = 0; kq < KBD; ++kq) {
                 float f[8];
 #pragma unroll
                 for (int j = 0; j < QV; ++j)
 #pragma unroll
-                    for (int s = 0; s < U; ++s) f[j * U + s] = phi((float)(ui > 0 ? qx : qr)[kb * QV + j][s]);
-                qf[kb] = cvt8<T>(f);
-#pragma unroll
-                for (int s = 0; s < 8; ++s) dq += (float)qf[kb][s] * smZ[kb * 16 + h * 8 + s];
+                    for (int s = 0; s < U; ++s) f[j * U + s] = phi((float)qsrc[kq * QV + j][s]);
+                qf[kq] = cvt8<T>(f);
             }
-            // Next chunk's first unit can be fetched now that qr is consumed.
-            if (ui == 0 && c + 1 < nch) load_q(qr, u, t0 + C);
+            if (qnext && c + 1 < nch) load_q(qnext, u, t0 + C);
 
-            f32x16 O[Gm::DT];
+            // Pt[key][query] = phi(K) phi(Q)^T on the diagonal tile; accumulator
+            // reg i holds key 8(i/4) + 4h + i%4 of the tile for query n.
+            f32x16 Pt = f32x16{};
 #pragma unroll
-            for (int ct = 0; ct < Gm::DT; ++ct) O[ct] = f32x16{};
-            float dsum = 0.f;
-            for (int kt = 0; kt <= r; ++kt) {
-                // Pt[key][query] = phi(K) phi(Q)^T for key tile kt, query tile r.
-                f32x16 Pt = f32x16{};
-                const int krow = kt * 32 + n;
+            for (int kq = 0; kq < KBD; ++kq) mma(Pt, sK.read8(r * 32 + n, kq * 16 + h * 8), qf[kq]);
+            v8 pb0, pb1;
+            float den;
+            if constexpr (BF) {
+                pb0 = __builtin_convertvector(
+                    f32x8{Pt[0], Pt[1], Pt[2], Pt[3], Pt[4], Pt[5], Pt[6], Pt[7]}, bf16x8);
+                pb1 = __builtin_convertvector(
+                    f32x8{Pt[8], Pt[9], Pt[10], Pt[11], Pt[12], Pt[13], Pt[14], Pt[15]}, bf16x8);
+                pb0 = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, pb0) & u32x4{mk[0], mk[1], mk[2], mk[3]});
+                pb1 = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, pb1) & u32x4{mk[4], mk[5], mk[6], mk[7]});
+                // den = 1^T (masked Pt) + z_r . phi(q), both on the matrix core:
+                // every row of the product equals the denominator of query n.
+                f32x16 Dn = f32x16{};
+                mma(Dn, ones8<T>(), pb0);
+                mma(Dn, ones8<T>(), pb1);
 #pragma unroll
-                for (int kb = 0; kb < Gm::KBD; ++kb) mma(Pt, sK.read8(krow, kb * 16 + h * 8, Gm::sig_rowD(krow)), qf[kb]);
-                // Accumulator reg i holds key 8(i/4) + 4h + i%4 of tile kt for query n.
+                for (int kq = 0; kq < KBD; ++kq)
+                    mma(Dn, *reinterpret_cast<const v8 *>(&smZ[r][kq * 16 + h * 8]), qf[kq]);
+                den = Dn[0];
+            } else {
                 float pv[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int kl = 8 * (i / 4) + 4 * h + (i % 4);
-                    pv[i] = (kt == r && kl > n) ? 0.f : Pt[i];
-                }
-                v8 pb0 = cvt8<T>(pv), pb1 = cvt8<T>(pv + 8);
+                for (int i = 0; i < 16; ++i) pv[i] = (8 * (i / 4) + 4 * h + (i % 4) > n) ? 0.f : Pt[i];
+                pb0 = cvt8<T>(pv);
+                pb1 = cvt8<T>(pv + 8);
+                float ds = 0.f;
 #pragma unroll
-                for (int s = 0; s < 8; ++s) dsum += (float)pb0[s] + (float)pb1[s];
-                // O^T[feature][query] += V^T[feature][keys] Pt[keys][query]; the key held
-                // in slot s of K-block kb2 is 16 kb2 + 8 (s/4) + 4h + s%4.
+                for (int s = 0; s < 8; ++s) ds += (float)pb0[s] + (float)pb1[s];
 #pragma unroll
-                for (int ct = 0; ct < Gm::DT; ++ct) {
-                    const int f = ct * 32 + n;
-                    const int sg = Gm::sig_rowC(f);
-                    mma(O[ct], cat(sVT.read4(f, kt * 32 + 4 * h, sg), sVT.read4(f, kt * 32 + 8 + 4 * h, sg)), pb0);
-                    mma(O[ct], cat(sVT.read4(f, kt * 32 + 16 + 4 * h, sg), sVT.read4(f, kt * 32 + 24 + 4 * h, sg)), pb1);
-                }
+                for (int kq = 0; kq < KBD; ++kq)
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) ds += (float)qf[kq][s] * (float)smZ[r][kq * 16 + h * 8 + s];
+                den = ds + __shfl_xor(ds, 32);
             }
-            // Carried state: O^T += S^T phi(Q)^T.
-#pragma unroll
-            for (int ct = 0; ct < Gm::DT; ++ct) {
-                const int j = ct * 32 + n;
-#pragma unroll
-                for (int kb = 0; kb < Gm::KBD; ++kb) mma(O[ct], sST.read8(j, kb * 16 + h * 8, Gm::sig_rowD(j)), qf[kb]);
-            }
-            float den = dsum + dq;
-            den += __shfl_xor(den, 32);
             const float inv = normalise ? 1.f / den : 1.f;
             const int t = t0 + r * 32 + n;
-            if (t < N) {
-                T *dst = ob + (size_t)g * N * D + (size_t)t * D;
+            const Tile<T, D> sST{smST[r]};
+            T *dst = ob + (size_t)g * N * D + (size_t)t * D;
+            for (int cc = 0; cc < CPG; ++cc) {
+                const int ct = cg * CPG + cc;
+                // O^T[feature][query] = V^T Pt (slot s of K-block kb2 holds key
+                // 16 kb2 + 8 (s/4) + 4h + s%4) + S_r^T phi(Q)^T.
+                f32x16 O = f32x16{};
+                mma(O, colfrag(sV, r * 32 + 4 * h, r * 32 + 8 + 4 * h, ct * 32, lane), pb0);
+                mma(O, colfrag(sV, r * 32 + 16 + 4 * h, r * 32 + 24 + 4 * h, ct * 32, lane), pb1);
 #pragma unroll
-                for (int ct = 0; ct < Gm::DT; ++ct)
+                for (int kq = 0; kq < KBD; ++kq) mma(O, sST.read8(ct * 32 + n, kq * 16 + h * 8), qf[kq]);
+                if (t < N) {
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
-                        f32x4 x{O[ct][4 * q4] * inv, O[ct][4 * q4 + 1] * inv, O[ct][4 * q4 + 2] * inv,
-                                O[ct][4 * q4 + 3] * inv};
+                        f32x4 x{O[4 * q4] * inv, O[4 * q4 + 1] * inv, O[4 * q4 + 2] * inv, O[4 * q4 + 3] * inv};
                         *reinterpret_cast<typename Vt<T>::v4 *>(dst + ct * 32 + 8 * q4 + 4 * h) = cvt4<T>(x);
                     }
+                }
             }
+        };
+#pragma unroll
+        for (int i = 0; i < MAXQ; ++i)
+            if (w + 4 * i < NU) unit(w + 4 * i, qr[i], qr[i]);
+        for (int u = w + 4 * MAXQ; u < NU; u += 4) {
+            g16 qx[KBD * QV];
+            load_q(qx, u, t0);
+            unit(u, qx, nullptr);
         }
 
-        // ---- S += phi(K)^T V, z += column sums of phi(K)
-#pragma unroll
-        for (int i = 0; i < Gm::MAXST; ++i) {
-            const int st = w + 4 * i;
-            if (st < Gm::NST) {
-                const int it = st / Gm::DT, jt = st % Gm::DT;
-                zr[i] += state_update<T, D, C>(S[i], it, jt, jt == 0, sKT, sVT, h, n);
+        if (c + 1 < nch) {
+            if (!Gm::DB) {
+                // Single buffer: everyone is done with this chunk before it is overwritten.
+                lds_barrier();
+                stage_rows<T, D, C>(kr, vr, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, t0 + C, N, tid);
+                if (c + 2 < nch) {
+                    load_chunk<T, D, C>(kr, kb, t0 + 2 * C, N, tid);
+                    load_chunk<T, D, C>(vr, vb, t0 + 2 * C, N, tid);
+                }
             }
+            lds_barrier();
         }
-        lds_barrier();
-        publish_state();
     }
 
     if (p == P - 1 && state_out) {
         float *so = state_out + (size_t)seq * D * D;
 #pragma unroll
         for (int i = 0; i < Gm::MAXST; ++i) {
-            const int st = w + 4 * i;
+            const int st = Gm::tile_of(w, i);
             if (st < Gm::NST) {
-                const int it = st / Gm::DT, jt = st % Gm::DT;
+                const int it = st / DT, jt = st % DT;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) so[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n] = S[i][r];
             }
         }
     }
     if (p == P - 1 && z_out) {
-#pragma unroll
-        for (int i = 0; i < Gm::MAXST; ++i) {
-            const int st = w + 4 * i;
-            if (st < Gm::NST && st % Gm::DT == 0 && h == 0) z_out[(size_t)seq * D + (st / Gm::DT) * 32 + n] = zr[i];
-        }
+        const int st = Gm::tile_of(w, 0);
+        if (st < Gm::NST && st % DT == 0 && h == 0) z_out[(size_t)seq * D + (st / DT) * 32 + n] = BF ? Z[0] : zr;
     }
 }
 
@@ -567,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restric
     constexpr int QV = 8 / U;
     __shared__ __attribute__((aligned(16))) T smST[D * D];
     __shared__ float smZ[D];
-    LdsTile<T, D> sST{smST};
+    const Tile<T, D> sST{smST};
 
     const int seq = blockIdx.x / nblk, blk = blockIdx.x % nblk;
     const int b = seq / Hkv, gk = seq % Hkv;
@@ -576,7 +695,7 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restric
     // S^T into LDS: element (row j, col i) = S[i][j].
     for (int e = tid; e < D * D; e += kThreads) {
         const int i = e / D, j = e % D;
-        smST[sST.at(j, i, Gm::sig_rowD(j))] = (T)S[e];
+        smST[sST.at(j, i)] = (T)S[e];
     }
     for (int e = tid; e < D; e += kThreads) smZ[e] = S[(size_t)D * D + e];
     __syncthreads();
@@ -611,7 +730,7 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restric
             O[ct] = f32x16{};
             const int j = ct * 32 + n;
 #pragma unroll
-            for (int kb = 0; kb < Gm::KBD; ++kb) mma(O[ct], sST.read8(j, kb * 16 + h * 8, Gm::sig_rowD(j)), qf[kb]);
+            for (int kb = 0; kb < Gm::KBD; ++kb) mma(O[ct], sST.read8(j, kb * 16 + h * 8), qf[kb]);
         }
         dq += __shfl_xor(dq, 32);
         const float inv = normalise ? 1.f / dq : 1.f;
@@ -726,6 +845,9 @@ template <typename T, int D, int C>
 int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out, float *state_out,
             float *z_out, float *ws, int normalise, hipStream_t st, hipEvent_t *ev)
 {
+    // Totals pass: chunks of at most 64 tokens and 64 KiB of double-buffered K/V.
+    constexpr int C1a = 65536 / (4 * D * (int)sizeof(T));
+    constexpr int C1 = C < C1a ? (C < 64 ? C : 64) : (C1a < 64 ? C1a : 64);
     const T *qq = static_cast<const T *>(q);
     const T *kk = static_cast<const T *>(k);
     const T *vv = static_cast<const T *>(v);
@@ -735,7 +857,7 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
     if (record(ev, 0, st)) return LINATTN_ERR_HIP;
     if (pl.causal) {
         if (P > 1)
-            hipLaunchKernelGGL((k_seg_totals<T, D, C>), dim3(pl.nseq * (P - 1)), dim3(kThreads), 0, st, kk, vv, ws,
+            hipLaunchKernelGGL((k_seg_totals<T, D, C1>), dim3(pl.nseq * (P - 1)), dim3(kThreads), 0, st, kk, vv, ws,
                                pl.N, pl.seg_len, P - 1);
         if (record(ev, 1, st)) return LINATTN_ERR_HIP;
         if (P > 2)
@@ -745,7 +867,7 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
         hipLaunchKernelGGL((k_causal_chunks<T, D, C>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo,
                            (const float *)ws, state_out, z_out, pl.H, pl.Hkv, pl.N, pl.G, P, pl.seg_len, normalise);
     } else {
-        hipLaunchKernelGGL((k_seg_totals<T, D, C>), dim3(pl.nseq * P), dim3(kThreads), 0, st, kk, vv, ws, pl.N,
+        hipLaunchKernelGGL((k_seg_totals<T, D, C1>), dim3(pl.nseq * P), dim3(kThreads), 0, st, kk, vv, ws, pl.N,
                            pl.seg_len, P);
         if (record(ev, 1, st)) return LINATTN_ERR_HIP;
         hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, ws, P,
@@ -760,7 +882,7 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
 }
 
 template <typename T, int D, int C>
-constexpr bool lds_fits() { return sizeof(T) * (3 * C * D + D * D) + 4 * D <= 160 * 1024; }
+constexpr bool lds_fits() { return Geo<T, D, C>::FITS; }
 
 template <typename T, int D>
 int dispatch_chunk(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,

@@ -18,20 +18,22 @@ bool valid_chunk(int c) { return c == 32 || c == 64 || c == 128 || c == 256; }
 size_t chunk_kernel_lds_bytes(int dtype, int d, int chunk)
 {
     const size_t e = dtype == LINATTN_BF16 ? 2 : 4;
-    // phi(K) row-major, phi(K) transposed, V transposed: chunk x d each;
-    // the state transposed: d x d; the normaliser: d floats.
-    return e * (3 * (size_t)chunk * d + (size_t)d * d) + 4 * (size_t)d;
+    // phi(K) and V tiles (chunk x d each, single-buffered at least), one
+    // transposed state copy (d x d) and one normaliser (d floats) per
+    // 32-token key tile of the chunk.
+    const size_t tiles = (size_t)chunk / 32;
+    return e * 2 * (size_t)chunk * d + tiles * (e * (size_t)d * d + 4 * (size_t)d);
 }
 
 int auto_chunk(int dtype, int d, int G, int causal)
 {
     (void)causal;
-    // One query tile of 32 rows per wave per chunk keeps all four waves busy
-    // (4 / G tiles of 32 tokens), within the LDS budget.
+    (void)G;
+    // The chunk only sets how many query tiles share one pass over the
+    // state copies; 64 tokens keep the K/V tiles double-buffered in LDS.
     int c = 128;
-    if (G >= 4) c = 64;
-    if (G >= 8) c = 32;
-    if (dtype == LINATTN_F32 && d == 128) c = 32;
+    if (d >= 128) c = 32;
+    if (dtype == LINATTN_F32) c = 32;
     while (c > 32 && chunk_kernel_lds_bytes(dtype, d, c) > kLdsLimit) c /= 2;
     return c;
 }

@@ -61,7 +61,7 @@ def test_version_and_status_strings():
     ((1, 2, 2, 16, 48, 1, F32, 0), -4),     # d unsupported
     ((1, 2, 2, 16, 256, 1, BF16, 0), -4),   # d unsupported
     ((1, 2, 2, 16, 64, 1, F32, 96), -4),    # chunk unsupported
-    ((1, 2, 2, 16, 128, 1, F32, 128), -4),  # fp32 d=128 chunk 128 exceeds LDS
+    ((1, 2, 2, 16, 128, 1, BF16, 256), -4), # bf16 d=128 chunk 256 exceeds LDS
     ((1, 2, 2, 16, 64, 1, 7, 0), -3),       # dtype
 ])
 def test_plan_rejects(args, code):
@@ -127,7 +127,9 @@ def test_workspace_formula():
 
 
 def test_auto_chunk_choices():
-    assert plan(2, 8, 8, 65536, 64, 1, BF16)[0] == 128
-    assert plan(1, 32, 8, 32768, 128, 1, BF16)[0] == 64
-    assert plan(1, 2, 2, 256, 32, 1, F32)[0] in (32, 64, 128)
-    assert plan(1, 2, 2, 256, 128, 1, F32)[0] == 32
+    for args in [(2, 8, 8, 65536, 64, 1, BF16), (1, 32, 8, 32768, 128, 1, BF16), (2, 8, 8, 4096, 64, 1, F32),
+                 (1, 2, 2, 256, 32, 1, F32), (1, 2, 2, 256, 128, 1, F32)]:
+        c, _ = plan(*args)
+        assert c in (32, 64, 128, 256)
+        # the automatic choice is always one the explicit argument accepts
+        assert la.linattn_fwd_plan(*args, c)[0] == 0
