@@ -241,7 +241,9 @@ __device__ __forceinline__ void stage_rows(const typename Vt<T>::g16 (&kr)[L], c
             typename Vt<T>::g16 fk;
 #pragma unroll
             for (int i = 0; i < G::U; ++i) fk[i] = (T)phi((float)kr[l][i]);
-            if (!full && t0 + t >= N) fk = typename Vt<T>::g16{};
+            if (!full) {
+                if (t0 + t >= N) fk = typename Vt<T>::g16{};
+            }
             sK.write16(t, q * G::U, fk);
             sV.write16(t, q * G::U, vr[l]);
         }
@@ -259,16 +261,17 @@ template <typename T> __device__ __forceinline__ typename Vt<T>::v8 ones8()
 
 // State tile (it, jt) += phi(K)^T V over the 32 tokens of key tile kt.
 // The K-block of 16 tokens kb2 puts token kt*32 + 16 kb2 + 8h + s in slot s.
-// When want_z, the column sums of phi(K) are formed too: bf16 adds 1 phi(K)
-// into Z on the matrix core (every accumulator register of lane (h, x) then
-// holds sum_t phi(k_t) of feature it*32 + x); fp32 returns this half-wave's
-// partial sum for feature it*32 + x (the caller adds the other half).
+// When want_z it also returns the tile's column sum of phi(K) for feature
+// it*32 + lane%32: bf16 forms it on the matrix core (1 phi(K) into a scratch
+// accumulator whose every register then holds the sum), fp32 adds on the
+// vector ALUs and returns this half-wave's part (the caller adds the other).
 template <typename T, int D>
-__device__ __forceinline__ float tile_state_update(f32x16 &acc, f32x16 &Z, bool want_z, int it, int jt, int kt,
-                                                   Tile<T, D> sK, Tile<T, D> sV, int lane)
+__device__ __forceinline__ float tile_state_update(f32x16 &acc, bool want_z, int it, int jt, int kt, Tile<T, D> sK,
+                                                   Tile<T, D> sV, int lane)
 {
     const int h = lane >> 5;
     float zs = 0.f;
+    f32x16 Z = f32x16{};
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
         const int r0 = kt * 32 + 16 * kb2 + 8 * h;
@@ -284,6 +287,7 @@ __device__ __forceinline__ float tile_state_update(f32x16 &acc, f32x16 &Z, bool 
             }
         }
     }
+    if constexpr (sizeof(T) == 2) zs = Z[0];
     return zs;
 }
 
@@ -307,24 +311,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
     const int s0 = p * seg_len, s1 = min(N, s0 + seg_len);
     const int nch = (s1 - s0 + C1 - 1) / C1;
 
-    f32x16 acc[G::MAXST], Z = f32x16{};
+    f32x16 acc[G::MAXST];
     float zacc = 0.f;
 #pragma unroll
     for (int i = 0; i < G::MAXST; ++i) acc[i] = f32x16{};
-    typename Vt<T>::g16 kr[G::LDV], vr[G::LDV];
-    // Walk the segment backwards: the main pass then starts on the chunks
-    // read most recently, which are the likeliest still to be cached.
-    load_chunk<T, D, C1>(kr, kb, s0 + (nch - 1) * C1, N, tid);
-    load_chunk<T, D, C1>(vr, vb, s0 + (nch - 1) * C1, N, tid);
-    for (int ci = 0; ci < nch; ++ci) {
-        const int c = nch - 1 - ci, buf = ci & 1;
+    // Two chunks in flight: register sets A and B alternate, chunk ci + 2 is
+    // requested as soon as chunk ci has been staged.
+    typename Vt<T>::g16 kA[G::LDV], vA[G::LDV], kB[G::LDV], vB[G::LDV];
+    load_chunk<T, D, C1>(kA, kb, s0, N, tid);
+    load_chunk<T, D, C1>(vA, vb, s0, N, tid);
+    if (nch > 1) {
+        load_chunk<T, D, C1>(kB, kb, s0 + C1, N, tid);
+        load_chunk<T, D, C1>(vB, vb, s0 + C1, N, tid);
+    }
+    auto absorb = [&](int buf) {
         const Tile<T, D> sK{smK[buf]}, sV{smV[buf]};
-        stage_rows<T, D, C1>(kr, vr, sK, sV, s0 + c * C1, N, tid);
-        if (c > 0) {
-            load_chunk<T, D, C1>(kr, kb, s0 + (c - 1) * C1, N, tid);
-            load_chunk<T, D, C1>(vr, vb, s0 + (c - 1) * C1, N, tid);
-        }
-        lds_barrier();
 #pragma unroll
         for (int i = 0; i < G::MAXST; ++i) {
             const int st = G::tile_of(w, i);
@@ -332,8 +333,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
                 const int it = st / G::DT, jt = st % G::DT;
 #pragma unroll
                 for (int kt = 0; kt < G::CT; ++kt)
-                    zacc += tile_state_update<T, D>(acc[i], Z, i == 0 && jt == 0, it, jt, kt, sK, sV, lane);
+                    zacc += tile_state_update<T, D>(acc[i], i == 0 && jt == 0, it, jt, kt, sK, sV, lane);
             }
+        }
+    };
+    for (int ci = 0; ci < nch; ci += 2) {
+        stage_rows<T, D, C1>(kA, vA, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, s0 + ci * C1, N, tid);
+        if (ci + 2 < nch) {
+            load_chunk<T, D, C1>(kA, kb, s0 + (ci + 2) * C1, N, tid);
+            load_chunk<T, D, C1>(vA, vb, s0 + (ci + 2) * C1, N, tid);
+        }
+        lds_barrier();
+        absorb(0);
+        if (ci + 1 < nch) {
+            stage_rows<T, D, C1>(kB, vB, Tile<T, D>{smK[1]}, Tile<T, D>{smV[1]}, s0 + (ci + 1) * C1, N, tid);
+            if (ci + 3 < nch) {
+                load_chunk<T, D, C1>(kB, kb, s0 + (ci + 3) * C1, N, tid);
+                load_chunk<T, D, C1>(vB, vb, s0 + (ci + 3) * C1, N, tid);
+            }
+            lds_barrier();
+            absorb(1);
         }
     }
     float *out = ws + ((size_t)seq * nslots + p) * (size_t)D * (D + 1);
@@ -348,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
                 out[(size_t)row * D + jt * 32 + n] = acc[i][r];
             }
             if (i == 0 && jt == 0) {
-                const float z = sizeof(T) == 2 ? Z[0] : zacc + __shfl_xor(zacc, 32);
+                const float z = sizeof(T) == 2 ? zacc : zacc + __shfl_xor(zacc, 32);
                 if (h == 0) out[(size_t)D * D + it * 32 + n] = z;
             }
         }
@@ -370,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, i
     float *base = ws + (size_t)seq * nslots * E + e;
     float acc = 0.f;
     // Batches of independent loads, then the running sum over the batch.
-    constexpr int BATCH = 16;
+    constexpr int BATCH = 32;
     for (int p0 = 0; p0 < nslots; p0 += BATCH) {
         float x[BATCH];
 #pragma unroll
@@ -393,279 +412,279 @@ __global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, i
 
 // ----------------------------------------------------------- causal_chunks
 //
-// One workgroup per (sequence, segment), walking the segment in chunks of C
-// tokens.  Per chunk:
+// One workgroup per (sequence, block of GT query heads, segment), walking the
+// segment in chunks of C tokens.  Per chunk:
+//   staging  phi(K), V and phi(Q) of the chunk go to LDS (row-major).  The
+//            output of the previous chunk, parked in the phi(Q) rows, is
+//            stored to HBM just before those rows are overwritten.
 //   phase 1  every state tile's owner wave publishes S^T and z to LDS before
-//            each 32-token key tile of the chunk and then adds that tile's
-//            phi(K)^T V (MFMA): copy kt is the state seen by query tile kt
-//            (all keys before it).  The chunk's prefix over its key tiles is
-//            thus formed by the owners, and no query tile needs an
-//            off-diagonal key tile.
-//   phase 2  every unit (query head g, query tile r, output column group cg)
-//            computes O^T = V^T (M . phi(K) phi(Q)^T) on the diagonal 32x32
-//            tile plus S_r^T phi(Q)^T, the denominator, and stores.
-// K/V tiles are double-buffered when LDS allows (the next chunk is staged
-// during phase 2, two barriers per chunk), otherwise staged after phase 2
-// (three barriers).
-template <typename T, int D, int C>
-__global__ __launch_bounds__(kThreads, D * sizeof(T) <= 128 ? 2 : 1) void k_causal_chunks(
+//            every RPC-th 32-token key tile and adds each tile's phi(K)^T V
+//            (MFMA): copy j is the state seen by query tiles j*RPC ..
+//            j*RPC + RPC - 1 (all keys before key tile j*RPC).
+//   phase 2  every unit (query head g, query tile r) computes
+//            O^T = V^T (M . phi(K) phi(Q)^T) on the diagonal 32x32 tile, plus
+//            the unmasked tiles between its state copy and the diagonal
+//            (none when RPC = 1, at most one when RPC = 2), plus S_j^T phi(Q)^T,
+//            and the denominator; it parks O in its own phi(Q) rows.
+// Global memory is touched only during staging: one wait there covers loads
+// and stores issued a whole chunk earlier, and the compute phases never wait
+// on memory.
+template <typename T, int D, int C, int GT>
+struct Main {
+    static constexpr int U = Vt<T>::U;
+    static constexpr int CT = C / 32, DT = D / 32, KBD = D / 16;
+    static constexpr int NST = DT * DT, MAXST = (NST + 3) / 4;
+    static constexpr int GPR = D / U;                // 16-byte groups per row
+    static constexpr int KVG = C * GPR;              // groups of one K (or V) chunk
+    static constexpr int QG = GT * C * GPR;          // groups of the chunk's q rows
+    static constexpr int LK = (KVG + kThreads - 1) / kThreads;
+    static constexpr int LQ = (QG + kThreads - 1) / kThreads;
+    static constexpr int NU = GT * CT;               // units per chunk
+    static constexpr linattn::MainShape SH = linattn::main_shape((int)sizeof(T), D, C, GT);
+    static constexpr int NSC = SH.nsc;
+    static constexpr int RPC = CT / NSC;
+    static constexpr bool FITS = SH.fits;
+    static constexpr int OCC = SH.occ;
+    __device__ static int tile_of(int w, int i) { return w * MAXST + i; }
+};
+
+template <typename T, int D, int C, int GT>
+__global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_chunks(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ out,
     const float *__restrict__ ws, float *__restrict__ state_out, float *__restrict__ z_out,
     int H, int Hkv, int N, int G, int P, int seg_len, int normalise)
 {
-    using Gm = Geo<T, D, C>;
+    using M = Main<T, D, C, GT>;
     using v8 = typename Vt<T>::v8;
     using g16 = typename Vt<T>::g16;
     constexpr bool BF = sizeof(T) == 2;
-    constexpr int U = Gm::U, QV = Gm::QV, CT = Gm::CT, DT = Gm::DT, KBD = Gm::KBD;
-    constexpr int NB = Gm::DB ? 2 : 1;
-    // Units per wave whose q is fetched a chunk ahead (chunks of 128+ tokens
-    // give every wave a query tile of its own already for one head).
-    constexpr int MAXQ = (D * sizeof(T) <= 128 && C < 128) ? 2 : 1;
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int U = M::U, CT = M::CT, DT = M::DT, KBD = M::KBD, GPR = M::GPR, NSC = M::NSC, RPC = M::RPC;
 
-    __shared__ __attribute__((aligned(16))) T smK[NB][C * D];
-    __shared__ __attribute__((aligned(16))) T smV[NB][C * D];
-    __shared__ __attribute__((aligned(16))) T smST[CT][D * D];
-    __shared__ __attribute__((aligned(16))) T smZ[CT][D];
+    __shared__ __attribute__((aligned(16))) T smK[C * D];
+    __shared__ __attribute__((aligned(16))) T smV[C * D];
+    __shared__ __attribute__((aligned(16))) T smQ[GT * C * D];
+    __shared__ __attribute__((aligned(16))) T smST[NSC][D * D];
+    __shared__ __attribute__((aligned(16))) T smZ[NSC][D];
+    const Tile<T, D> sK{smK}, sV{smV}, sQ{smQ};
 
-    const int seq = blockIdx.x / P, p = blockIdx.x % P;
+    const int HB = G / GT;
+    const int p = blockIdx.x % P, hb = (blockIdx.x / P) % HB, seq = blockIdx.x / (P * HB);
     const int b = seq / Hkv, gk = seq % Hkv;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
     const T *kb = k + (size_t)seq * N * D;
     const T *vb = v + (size_t)seq * N * D;
-    const T *qb = q + ((size_t)b * H + (size_t)gk * G) * N * D;
-    T *ob = out + ((size_t)b * H + (size_t)gk * G) * N * D;
+    const size_t head0 = (size_t)b * H + (size_t)gk * G + (size_t)hb * GT;  // first query head of the block
+    const T *qb = q + head0 * N * D;
+    T *ob = out + head0 * N * D;
     const int s0 = p * seg_len, s1 = min(N, s0 + seg_len);
     const int nch = (s1 - s0 + C - 1) / C;
-    // Units: (head g, query tile r, column group cg); NCG column groups when
-    // the chunk has fewer than four (head, tile) pairs for the four waves.
-    const int GR = G * CT;
-    const int NCG = GR >= 4 ? 1 : (4 / GR < DT ? 4 / GR : DT);
-    const int NU = GR * NCG;
-    const int CPG = DT / NCG;  // column tiles per group
 
-    // ---- the state this segment starts from
-    f32x16 S[Gm::MAXST], Z = f32x16{};
+    // ---- the state this segment starts from (state tile i of wave w is w*MAXST + i)
+    f32x16 S[M::MAXST];
     float zr = 0.f;
     const float *init = p > 0 ? ws + ((size_t)seq * (P - 1) + (p - 1)) * (size_t)D * (D + 1) : nullptr;
 #pragma unroll
-    for (int i = 0; i < Gm::MAXST; ++i) {
+    for (int i = 0; i < M::MAXST; ++i) {
         S[i] = f32x16{};
-        const int st = Gm::tile_of(w, i);
-        if (st < Gm::NST && init) {
+        const int st = M::tile_of(w, i);
+        if (st < M::NST && init) {
             const int it = st / DT, jt = st % DT;
 #pragma unroll
             for (int r = 0; r < 16; ++r) S[i][r] = init[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n];
             if (i == 0 && jt == 0) zr = init[(size_t)D * D + it * 32 + n];
         }
     }
+    // ---- staging: raw K, V, q of a chunk in registers, one chunk ahead
+    g16 kr[M::LK], vr[M::LK], qr[M::LQ];
+    auto load_all = [&](int t0) {
+        load_chunk<T, D, C>(kr, kb, t0, N, tid);
+        load_chunk<T, D, C>(vr, vb, t0, N, tid);
+        const bool full = t0 + C <= N;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) Z[r] = zr;
-    // Causal mask of the diagonal tile for packed bf16 pairs: accumulator reg
-    // i holds key 8(i/4) + 4h + i%4 for query n.
-    uint32_t mk[8];
+        for (int l = 0; l < M::LQ; ++l) {
+            const int e = tid + l * kThreads;
+            const int row = e / GPR, qq = e % GPR;  // row = g * C + token
+            const int g = row / C, t = row % C;
+            g16 x = {};
+            if ((M::QG % kThreads == 0 || e < M::QG) && (full || t0 + t < N))
+                x = *reinterpret_cast<const g16 *>(qb + (size_t)g * N * D + (size_t)(t0 + t) * D + qq * U);
+            qr[l] = x;
+        }
+    };
+    // Stores the output parked in the q rows (chunk starting at t_prev; none
+    // when t_prev < 0) and stages phi(q) of the chunk starting at t0 there.
+    auto stage_q = [&](int t_prev, int t0) {
 #pragma unroll
-    for (int pp = 0; pp < 8; ++pp) {
-        const int i0 = 2 * pp, i1 = 2 * pp + 1;
-        const uint32_t m0 = (8 * (i0 / 4) + 4 * h + (i0 % 4) <= n) ? 0xFFFFu : 0u;
-        const uint32_t m1 = (8 * (i1 / 4) + 4 * h + (i1 % 4) <= n) ? 0xFFFF0000u : 0u;
-        mk[pp] = m0 | m1;
-    }
-
-    g16 kr[Gm::LDV], vr[Gm::LDV];
-    g16 qr[MAXQ][KBD * QV];
-    auto load_q = [&](g16 *dst, int u, int t0) {
-        const int g = u / (CT * NCG), r = (u / NCG) % CT;
-        const int t = t0 + r * 32 + n;
-        const T *src = qb + (size_t)g * N * D + (size_t)t * D;
-        if (t0 + r * 32 + 32 <= N) {
-#pragma unroll
-            for (int kq = 0; kq < KBD; ++kq)
-#pragma unroll
-                for (int j = 0; j < QV; ++j) dst[kq * QV + j] = *reinterpret_cast<const g16 *>(src + kq * 16 + h * 8 + j * U);
-        } else {
-#pragma unroll
-            for (int kq = 0; kq < KBD; ++kq)
-#pragma unroll
-                for (int j = 0; j < QV; ++j) {
-                    g16 x = {};
-                    if (t < N) x = *reinterpret_cast<const g16 *>(src + kq * 16 + h * 8 + j * U);
-                    dst[kq * QV + j] = x;
+        for (int l = 0; l < M::LQ; ++l) {
+            const int e = tid + l * kThreads;
+            if (M::QG % kThreads == 0 || e < M::QG) {
+                const int row = e / GPR, qq = e % GPR;
+                const int g = row / C, t = row % C;
+                if (t_prev >= 0 && t_prev + t < N) {
+                    const g16 o = *reinterpret_cast<const g16 *>(smQ + sQ.at(row, qq * U));
+                    *reinterpret_cast<g16 *>(ob + (size_t)g * N * D + (size_t)(t_prev + t) * D + qq * U) = o;
                 }
+                if (t0 >= 0) {
+                    g16 fq;
+#pragma unroll
+                    for (int i = 0; i < U; ++i) fq[i] = (T)phi((float)qr[l][i]);
+                    sQ.write16(row, qq * U, fq);
+                }
+            }
         }
     };
 
-    // ---- prologue: chunk 0 staged, chunk 1 and the first q tiles in flight
-    load_chunk<T, D, C>(kr, kb, s0, N, tid);
-    load_chunk<T, D, C>(vr, vb, s0, N, tid);
-#pragma unroll
-    for (int i = 0; i < MAXQ; ++i)
-        if (w + 4 * i < NU) load_q(qr[i], w + 4 * i, s0);
-    stage_rows<T, D, C>(kr, vr, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, s0, N, tid);
-    if (nch > 1) {
-        load_chunk<T, D, C>(kr, kb, s0 + C, N, tid);
-        load_chunk<T, D, C>(vr, vb, s0 + C, N, tid);
-    }
+    // ---- prologue: chunk 0 staged, chunk 1 in flight
+    load_all(s0);
+    stage_rows<T, D, C>(kr, vr, sK, sV, s0, N, tid);
+    stage_q(-1, s0);
+    if (nch > 1) load_all(s0 + C);
     lds_barrier();
 
     for (int c = 0; c < nch; ++c) {
         const int t0 = s0 + c * C;
-        const int buf = Gm::DB ? (c & 1) : 0;
-        const Tile<T, D> sK{smK[buf]}, sV{smV[buf]};
 
-        // ---- phase 1: per key tile, publish the state then absorb the tile
+        // ---- phase 1: publish the state before every RPC-th key tile, absorb each tile
 #pragma unroll
-        for (int i = 0; i < Gm::MAXST; ++i) {
-            const int st = Gm::tile_of(w, i);
-            if (st < Gm::NST) {
+        for (int i = 0; i < M::MAXST; ++i) {
+            const int st = M::tile_of(w, i);
+            if (st < M::NST) {
                 const int it = st / DT, jt = st % DT;
                 const bool zown = i == 0 && jt == 0;
                 const int row = jt * 32 + n;
                 float zs = 0.f;
 #pragma unroll
                 for (int kt = 0; kt < CT; ++kt) {
-                    const Tile<T, D> sST{smST[kt]};
+                    if (kt % RPC == 0) {
+                        const Tile<T, D> sST{smST[kt / RPC]};
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        f32x4 x{S[i][4 * q4], S[i][4 * q4 + 1], S[i][4 * q4 + 2], S[i][4 * q4 + 3]};
-                        sST.write4(row, it * 32 + 8 * q4 + 4 * h, cvt4<T>(x));
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            f32x4 x{S[i][4 * q4], S[i][4 * q4 + 1], S[i][4 * q4 + 2], S[i][4 * q4 + 3]};
+                            sST.write4(row, it * 32 + 8 * q4 + 4 * h, cvt4<T>(x));
+                        }
+                        if (zown && h == 0) smZ[kt / RPC][it * 32 + n] = (T)(zr + zs);
                     }
-                    if (zown && h == 0) smZ[kt][it * 32 + n] = (T)(BF ? Z[0] : zr + zs);
-                    const float dz = tile_state_update<T, D>(S[i], Z, zown, it, jt, kt, sK, sV, lane);
-                    if (!BF && zown) zs += dz + __shfl_xor(dz, 32);
+                    const float dz = tile_state_update<T, D>(S[i], zown, it, jt, kt, sK, sV, lane);
+                    if (zown) zs += BF ? dz : dz + __shfl_xor(dz, 32);
                 }
                 if (zown) zr += zs;
             }
         }
         lds_barrier();
 
-        // ---- the next chunk: stage it into the free buffer, fetch the one after
-        if (c + 1 < nch) {
-            if (Gm::DB) {
-                stage_rows<T, D, C>(kr, vr, Tile<T, D>{smK[buf ^ 1]}, Tile<T, D>{smV[buf ^ 1]}, t0 + C, N, tid);
-                if (c + 2 < nch) {
-                    load_chunk<T, D, C>(kr, kb, t0 + 2 * C, N, tid);
-                    load_chunk<T, D, C>(vr, vb, t0 + 2 * C, N, tid);
-                }
-            }
-        }
-
         // ---- phase 2: query tiles
-        auto unit = [&](int u, const g16 *qsrc, g16 *qnext) {
-            const int g = u / (CT * NCG), r = (u / NCG) % CT, cg = u % NCG;
-            if (t0 + r * 32 >= N) return;  // tile entirely past the end
+        for (int u = w; u < M::NU; u += 4) {
+            const int g = u / CT, r = u % CT;
+            if (t0 + r * 32 >= N) continue;  // tile entirely past the end
+            const int j = r / RPC;
+            const bool off = r % RPC != 0;   // one unmasked key tile r-1 before the diagonal
+            const int qrow = g * C + r * 32 + n;
             // phi(q) fragments: lane (h, n) holds query n, features kq*16 + 8h + s.
             v8 qf[KBD];
 #pragma unroll
-            for (int kq = 0; kq < KBD; ++kq) {
-                float f[8];
+            for (int kq = 0; kq < KBD; ++kq) qf[kq] = sQ.read8(qrow, kq * 16 + h * 8);
+            // Pt[key][query] = phi(K) phi(Q)^T; accumulator reg i holds key
+            // 8(i/4) + 4h + i%4 of the tile for query n.
+            v8 pb0, pb1, po0 = v8{}, po1 = v8{};
+            {
+                f32x16 Pt = f32x16{};
 #pragma unroll
-                for (int j = 0; j < QV; ++j)
+                for (int kq = 0; kq < KBD; ++kq) mma(Pt, sK.read8(r * 32 + n, kq * 16 + h * 8), qf[kq]);
+                // Causal mask: accumulator reg i holds key 8(i/4) + 4h + i%4 of the
+                // tile for query n; keep keys <= n.
+                const int kmax = n - 4 * h;
+                float pv[16];
 #pragma unroll
-                    for (int s = 0; s < U; ++s) f[j * U + s] = phi((float)qsrc[kq * QV + j][s]);
-                qf[kq] = cvt8<T>(f);
+                for (int i = 0; i < 16; ++i) pv[i] = (8 * (i / 4) + (i % 4) <= kmax) ? Pt[i] : 0.f;
+                pb0 = cvt8<T>(pv);
+                pb1 = cvt8<T>(pv + 8);
             }
-            if (qnext && c + 1 < nch) load_q(qnext, u, t0 + C);
-
-            // Pt[key][query] = phi(K) phi(Q)^T on the diagonal tile; accumulator
-            // reg i holds key 8(i/4) + 4h + i%4 of the tile for query n.
-            f32x16 Pt = f32x16{};
+            if (off) {
+                f32x16 Po = f32x16{};
 #pragma unroll
-            for (int kq = 0; kq < KBD; ++kq) mma(Pt, sK.read8(r * 32 + n, kq * 16 + h * 8), qf[kq]);
-            v8 pb0, pb1;
+                for (int kq = 0; kq < KBD; ++kq) mma(Po, sK.read8(r * 32 - 32 + n, kq * 16 + h * 8), qf[kq]);
+                float ov[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) ov[i] = Po[i];
+                po0 = cvt8<T>(ov);
+                po1 = cvt8<T>(ov + 8);
+            }
             float den;
             if constexpr (BF) {
-                pb0 = __builtin_convertvector(
-                    f32x8{Pt[0], Pt[1], Pt[2], Pt[3], Pt[4], Pt[5], Pt[6], Pt[7]}, bf16x8);
-                pb1 = __builtin_convertvector(
-                    f32x8{Pt[8], Pt[9], Pt[10], Pt[11], Pt[12], Pt[13], Pt[14], Pt[15]}, bf16x8);
-                pb0 = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, pb0) & u32x4{mk[0], mk[1], mk[2], mk[3]});
-                pb1 = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, pb1) & u32x4{mk[4], mk[5], mk[6], mk[7]});
-                // den = 1^T (masked Pt) + z_r . phi(q), both on the matrix core:
+                // den = 1^T (masked Pt) + 1^T Po + z_j . phi(q), on the matrix core:
                 // every row of the product equals the denominator of query n.
                 f32x16 Dn = f32x16{};
                 mma(Dn, ones8<T>(), pb0);
                 mma(Dn, ones8<T>(), pb1);
+                if (off) {
+                    mma(Dn, ones8<T>(), po0);
+                    mma(Dn, ones8<T>(), po1);
+                }
 #pragma unroll
                 for (int kq = 0; kq < KBD; ++kq)
-                    mma(Dn, *reinterpret_cast<const v8 *>(&smZ[r][kq * 16 + h * 8]), qf[kq]);
+                    mma(Dn, *reinterpret_cast<const v8 *>(&smZ[j][kq * 16 + h * 8]), qf[kq]);
                 den = Dn[0];
             } else {
-                float pv[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) pv[i] = (8 * (i / 4) + 4 * h + (i % 4) > n) ? 0.f : Pt[i];
-                pb0 = cvt8<T>(pv);
-                pb1 = cvt8<T>(pv + 8);
                 float ds = 0.f;
 #pragma unroll
-                for (int s = 0; s < 8; ++s) ds += (float)pb0[s] + (float)pb1[s];
+                for (int s = 0; s < 8; ++s) ds += (float)pb0[s] + (float)pb1[s] + (float)po0[s] + (float)po1[s];
 #pragma unroll
                 for (int kq = 0; kq < KBD; ++kq)
 #pragma unroll
-                    for (int s = 0; s < 8; ++s) ds += (float)qf[kq][s] * (float)smZ[r][kq * 16 + h * 8 + s];
+                    for (int s = 0; s < 8; ++s) ds += (float)qf[kq][s] * (float)smZ[j][kq * 16 + h * 8 + s];
                 den = ds + __shfl_xor(ds, 32);
             }
             const float inv = normalise ? 1.f / den : 1.f;
-            const int t = t0 + r * 32 + n;
-            const Tile<T, D> sST{smST[r]};
-            T *dst = ob + (size_t)g * N * D + (size_t)t * D;
-            for (int cc = 0; cc < CPG; ++cc) {
-                const int ct = cg * CPG + cc;
+            const Tile<T, D> sST{smST[j]};
+#pragma unroll
+            for (int ct = 0; ct < DT; ++ct) {
                 // O^T[feature][query] = V^T Pt (slot s of K-block kb2 holds key
-                // 16 kb2 + 8 (s/4) + 4h + s%4) + S_r^T phi(Q)^T.
+                // 16 kb2 + 8 (s/4) + 4h + s%4) + V^T Po + S_j^T phi(Q)^T.
                 f32x16 O = f32x16{};
                 mma(O, colfrag(sV, r * 32 + 4 * h, r * 32 + 8 + 4 * h, ct * 32, lane), pb0);
                 mma(O, colfrag(sV, r * 32 + 16 + 4 * h, r * 32 + 24 + 4 * h, ct * 32, lane), pb1);
+                if (off) {
+                    mma(O, colfrag(sV, r * 32 - 32 + 4 * h, r * 32 - 24 + 4 * h, ct * 32, lane), po0);
+                    mma(O, colfrag(sV, r * 32 - 16 + 4 * h, r * 32 - 8 + 4 * h, ct * 32, lane), po1);
+                }
 #pragma unroll
                 for (int kq = 0; kq < KBD; ++kq) mma(O, sST.read8(ct * 32 + n, kq * 16 + h * 8), qf[kq]);
-                if (t < N) {
+                // Park O in this unit's own q rows (no other unit reads them).
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        f32x4 x{O[4 * q4] * inv, O[4 * q4 + 1] * inv, O[4 * q4 + 2] * inv, O[4 * q4 + 3] * inv};
-                        *reinterpret_cast<typename Vt<T>::v4 *>(dst + ct * 32 + 8 * q4 + 4 * h) = cvt4<T>(x);
-                    }
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    f32x4 x{O[4 * q4] * inv, O[4 * q4 + 1] * inv, O[4 * q4 + 2] * inv, O[4 * q4 + 3] * inv};
+                    sQ.write4(qrow, ct * 32 + 8 * q4 + 4 * h, cvt4<T>(x));
                 }
             }
-        };
-#pragma unroll
-        for (int i = 0; i < MAXQ; ++i)
-            if (w + 4 * i < NU) unit(w + 4 * i, qr[i], qr[i]);
-        for (int u = w + 4 * MAXQ; u < NU; u += 4) {
-            g16 qx[KBD * QV];
-            load_q(qx, u, t0);
-            unit(u, qx, nullptr);
         }
+        lds_barrier();
 
+        // ---- staging of the next chunk (and the stores of this one)
         if (c + 1 < nch) {
-            if (!Gm::DB) {
-                // Single buffer: everyone is done with this chunk before it is overwritten.
-                lds_barrier();
-                stage_rows<T, D, C>(kr, vr, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, t0 + C, N, tid);
-                if (c + 2 < nch) {
-                    load_chunk<T, D, C>(kr, kb, t0 + 2 * C, N, tid);
-                    load_chunk<T, D, C>(vr, vb, t0 + 2 * C, N, tid);
-                }
-            }
+            stage_rows<T, D, C>(kr, vr, sK, sV, t0 + C, N, tid);
+            stage_q(t0, t0 + C);
+            if (c + 2 < nch) load_all(t0 + 2 * C);
             lds_barrier();
+        } else {
+            stage_q(t0, -1);
         }
     }
 
     if (p == P - 1 && state_out) {
         float *so = state_out + (size_t)seq * D * D;
 #pragma unroll
-        for (int i = 0; i < Gm::MAXST; ++i) {
-            const int st = Gm::tile_of(w, i);
-            if (st < Gm::NST) {
+        for (int i = 0; i < M::MAXST; ++i) {
+            const int st = M::tile_of(w, i);
+            if (hb == 0 && st < M::NST) {
                 const int it = st / DT, jt = st % DT;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) so[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n] = S[i][r];
             }
         }
     }
-    if (p == P - 1 && z_out) {
-        const int st = Gm::tile_of(w, 0);
-        if (st < Gm::NST && st % DT == 0 && h == 0) z_out[(size_t)seq * D + (st / DT) * 32 + n] = BF ? Z[0] : zr;
+    if (p == P - 1 && z_out && hb == 0) {
+        const int st = M::tile_of(w, 0);
+        if (st < M::NST && st % DT == 0 && h == 0) z_out[(size_t)seq * D + (st / DT) * 32 + n] = zr;
     }
 }
 
@@ -845,9 +864,10 @@ template <typename T, int D, int C>
 int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out, float *state_out,
             float *z_out, float *ws, int normalise, hipStream_t st, hipEvent_t *ev)
 {
-    // Totals pass: chunks of at most 64 tokens and 64 KiB of double-buffered K/V.
+    // Totals pass: chunks of at most 128 tokens and 64 KiB of double-buffered
+    // K/V (enough bytes in flight per workgroup to stream at full bandwidth).
     constexpr int C1a = 65536 / (4 * D * (int)sizeof(T));
-    constexpr int C1 = C < C1a ? (C < 64 ? C : 64) : (C1a < 64 ? C1a : 64);
+    constexpr int C1 = C < C1a ? (C < 128 ? C : 128) : (C1a < 128 ? C1a : 128);
     const T *qq = static_cast<const T *>(q);
     const T *kk = static_cast<const T *>(k);
     const T *vv = static_cast<const T *>(v);
@@ -864,8 +884,25 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
             hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, ws,
                                P - 1, D, 0, (float *)nullptr, (float *)nullptr);
         if (record(ev, 2, st)) return LINATTN_ERR_HIP;
-        hipLaunchKernelGGL((k_causal_chunks<T, D, C>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo,
-                           (const float *)ws, state_out, z_out, pl.H, pl.Hkv, pl.N, pl.G, P, pl.seg_len, normalise);
+        const dim3 grid(pl.nseq * (pl.G / pl.gt) * P);
+        switch (pl.gt) {
+#define LINATTN_MAIN(GT)                                                                                            \
+    case GT:                                                                                                       \
+        if constexpr (Main<T, D, C, GT>::FITS) {                                                                   \
+            hipLaunchKernelGGL((k_causal_chunks<T, D, C, GT>), grid, dim3(kThreads), 0, st, qq, kk, vv, oo,         \
+                               (const float *)ws, state_out, z_out, pl.H, pl.Hkv, pl.N, pl.G, P, pl.seg_len,       \
+                               normalise);                                                                         \
+            break;                                                                                                 \
+        } else {                                                                                                   \
+            return LINATTN_ERR_UNSUPPORTED;                                                                        \
+        }
+            LINATTN_MAIN(1)
+            LINATTN_MAIN(2)
+            LINATTN_MAIN(4)
+            LINATTN_MAIN(8)
+#undef LINATTN_MAIN
+        default: return LINATTN_ERR_UNSUPPORTED;
+        }
     } else {
         hipLaunchKernelGGL((k_seg_totals<T, D, C1>), dim3(pl.nseq * P), dim3(kThreads), 0, st, kk, vv, ws, pl.N,
                            pl.seg_len, P);
@@ -882,7 +919,10 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
 }
 
 template <typename T, int D, int C>
-constexpr bool lds_fits() { return Geo<T, D, C>::FITS; }
+constexpr bool chunk_ok()
+{
+    return Main<T, D, C, 1>::FITS || Main<T, D, C, 2>::FITS || Main<T, D, C, 4>::FITS || Main<T, D, C, 8>::FITS;
+}
 
 template <typename T, int D>
 int dispatch_chunk(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,
@@ -890,16 +930,16 @@ int dispatch_chunk(const linattn::Plan &pl, const void *q, const void *k, const 
 {
     switch (pl.chunk) {
     case 32:
-        if constexpr (lds_fits<T, D, 32>()) return run_fwd<T, D, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
+        if constexpr (chunk_ok<T, D, 32>()) return run_fwd<T, D, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
         break;
     case 64:
-        if constexpr (lds_fits<T, D, 64>()) return run_fwd<T, D, 64>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
+        if constexpr (chunk_ok<T, D, 64>()) return run_fwd<T, D, 64>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
         break;
     case 128:
-        if constexpr (lds_fits<T, D, 128>()) return run_fwd<T, D, 128>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
+        if constexpr (chunk_ok<T, D, 128>()) return run_fwd<T, D, 128>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
         break;
     case 256:
-        if constexpr (lds_fits<T, D, 256>()) return run_fwd<T, D, 256>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
+        if constexpr (chunk_ok<T, D, 256>()) return run_fwd<T, D, 256>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
         break;
     }
     return LINATTN_ERR_UNSUPPORTED;

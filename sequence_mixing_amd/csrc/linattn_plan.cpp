@@ -8,34 +8,35 @@
 namespace linattn {
 
 namespace {
-constexpr size_t kLdsLimit = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kTargetWorkgroups = 512;    // two waves of workgroups over 256 CUs
 
 bool valid_d(int d) { return d == 32 || d == 64 || d == 128; }
 bool valid_chunk(int c) { return c == 32 || c == 64 || c == 128 || c == 256; }
 }  // namespace
 
-size_t chunk_kernel_lds_bytes(int dtype, int d, int chunk)
+int heads_per_block(int dtype, int d, int chunk, int G)
 {
-    const size_t e = dtype == LINATTN_BF16 ? 2 : 4;
-    // phi(K) and V tiles (chunk x d each, single-buffered at least), one
-    // transposed state copy (d x d) and one normaliser (d floats) per
-    // 32-token key tile of the chunk.
-    const size_t tiles = (size_t)chunk / 32;
-    return e * 2 * (size_t)chunk * d + tiles * (e * (size_t)d * d + 4 * (size_t)d);
+    const int e = dtype == LINATTN_BF16 ? 2 : 4;
+    for (int gt = 8; gt >= 1; gt /= 2)
+        if (G % gt == 0 && main_shape(e, d, chunk, gt).fits) return gt;
+    return 0;
 }
 
 int auto_chunk(int dtype, int d, int G, int causal)
 {
     (void)causal;
-    (void)G;
-    // The chunk only sets how many query tiles share one pass over the
-    // state copies; 64 tokens keep the K/V tiles double-buffered in LDS.
-    int c = 128;
-    if (d >= 128) c = 32;
-    if (dtype == LINATTN_F32) c = 32;
-    while (c > 32 && chunk_kernel_lds_bytes(dtype, d, c) > kLdsLimit) c /= 2;
-    return c;
+    // Prefer the most query heads per workgroup (K and V are then read once
+    // per head block), then about 128 query rows per chunk, which gives the
+    // four waves one 32-row query tile each.
+    for (int gt = 8; gt >= 1; gt /= 2) {
+        if (G % gt != 0) continue;
+        const int pref[4] = {128 / gt >= 32 ? 128 / gt : 32, 64, 32, 128};
+        for (int i = 0; i < 4; ++i) {
+            const int c = pref[i];
+            if (heads_per_block(dtype, d, c, G) == gt) return c;
+        }
+    }
+    return 0;
 }
 
 int make_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int chunk, Plan *p)
@@ -47,13 +48,16 @@ int make_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int ch
     if (chunk != 0 && !valid_chunk(chunk)) return LINATTN_ERR_UNSUPPORTED;
     const int G = H / Hkv;
     const int C = chunk ? chunk : auto_chunk(dtype, d, G, causal);
-    if (chunk_kernel_lds_bytes(dtype, d, C) > kLdsLimit) return LINATTN_ERR_UNSUPPORTED;
+    if (C == 0) return LINATTN_ERR_UNSUPPORTED;
+    const int gt = heads_per_block(dtype, d, C, G);
+    if (gt == 0) return LINATTN_ERR_UNSUPPORTED;
 
     Plan q{};
     q.B = B; q.H = H; q.Hkv = Hkv; q.N = N; q.d = d; q.G = G;
     q.causal = causal ? 1 : 0;
     q.dtype = dtype;
     q.chunk = C;
+    q.gt = gt;
     q.nseq = B * Hkv;
     q.segments = 0;
     q.seg_len = 0;

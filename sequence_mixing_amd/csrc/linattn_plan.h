@@ -5,6 +5,41 @@
 
 namespace linattn {
 
+// Shape of one chunk-kernel instantiation: e = element bytes, D head
+// dimension, C tokens per chunk, GT query heads per workgroup.  LDS holds
+// phi(K), V and phi(Q) of a chunk ((2 + GT) C D elements) plus nsc copies of
+// the transposed state (D x D) and of z (D); nsc is one copy per 32-token key
+// tile, or one per two key tiles when that keeps two workgroups on a CU.
+struct MainShape {
+    int nsc;      // state copies per chunk
+    int occ;      // workgroups per CU the kernel is built for (1 or 2)
+    int lq;       // 16-byte q groups each thread stages per chunk
+    bool fits;    // buildable: LDS within 160 KiB, lq <= 8, at most 2 key tiles per copy
+    unsigned long lds;
+};
+
+constexpr unsigned long main_lds(int e, int D, int C, int GT, int nsc)
+{
+    return (unsigned long)e * ((unsigned long)(2 + GT) * C * D + (unsigned long)nsc * D * D + (unsigned long)nsc * D);
+}
+
+constexpr MainShape main_shape(int e, int D, int C, int GT)
+{
+    const unsigned long half = 80 * 1024, full = 160 * 1024;
+    const int ct = C / 32;
+    const int occ_reg = D * e <= 128 ? 2 : 1;  // register budget allows two workgroups
+    int nsc = ct;
+    if (occ_reg == 2 && main_lds(e, D, C, GT, ct) <= half) nsc = ct;
+    else if (occ_reg == 2 && ct >= 2 && main_lds(e, D, C, GT, ct / 2) <= half) nsc = ct / 2;
+    else if (main_lds(e, D, C, GT, ct) <= full) nsc = ct;
+    else nsc = ct >= 2 ? ct / 2 : 1;
+    const unsigned long lds = main_lds(e, D, C, GT, nsc);
+    const int u = 16 / e;
+    const int lq = (GT * C * (D / u) + 255) / 256;
+    MainShape m{nsc, (occ_reg == 2 && lds <= half) ? 2 : 1, lq, lds <= full && lq <= 8 && ct / nsc <= 2, lds};
+    return m;
+}
+
 // How one linattn_fwd call is split into kernel launches.
 //
 // A sequence (one batch entry and kv head) of N tokens is cut into `segments`
@@ -17,6 +52,7 @@ namespace linattn {
 struct Plan {
     int B, H, Hkv, N, d, G, causal, dtype;
     int chunk;       // tokens per intra-chunk block
+    int gt;          // query heads per workgroup of the chunk kernel (divides G)
     int nseq;        // B * Hkv independent (batch, kv head) sequences
     int segments;    // segments per sequence
     int seg_len;     // tokens per segment (multiple of chunk)
@@ -24,8 +60,9 @@ struct Plan {
     size_t ws_bytes; // workspace bytes: nseq * ws_slots * d * (d + 1) * 4
 };
 
-// Bytes of LDS the chunk kernel needs for (dtype, d, chunk).
-size_t chunk_kernel_lds_bytes(int dtype, int d, int chunk);
+// Query heads per workgroup for (dtype, d, chunk, G): the largest of 8, 4,
+// 2, 1 that divides G and whose kernel shape fits; 0 if none fits.
+int heads_per_block(int dtype, int d, int chunk, int G);
 
 // Chunk size used when the caller passes chunk = 0.
 int auto_chunk(int dtype, int d, int G, int causal);

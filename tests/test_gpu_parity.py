@@ -83,6 +83,10 @@ SMALL = [
     (1, 2, 2, 300, 128, "f32"),
     (3, 6, 3, 515, 64, "f32"),
     (1, 8, 2, 2049, 128, "bf16"),
+    (2, 6, 2, 300, 64, "bf16"),     # G = 3: three one-head blocks per kv head
+    (1, 6, 1, 777, 64, "bf16"),     # G = 6: head blocks of 2
+    (1, 8, 1, 500, 64, "f32"),      # G = 8
+    (1, 16, 2, 333, 128, "bf16"),   # G = 8 at d = 128: head blocks of 4
 ]
 
 
