@@ -6,17 +6,21 @@
 A step is one ``linattn_fwd`` call (causal, normaliser on) over the whole
 batch of the chosen workload: segment totals, their prefix scan and the
 chunked main pass.  Inputs are seeded N(0, 1) tensors already resident on
-the GPU.  The W warm-up steps are untimed; the K timed steps run back to
-back between two device synchronisations, and HIP events recorded by the
-library on its stream give each stage's duration.
+the GPU.  After W untimed warm-up steps, the K steps are captured once as a
+HIP graph (untimed) and replayed between two device synchronisations; the
+output of the replay is checked bitwise against an eager call.  The same K
+steps are also run as plain eager calls (host launch cost included) and
+once more through ``linattn_fwd_timed``, whose HIP events on the library's
+stream give each stage's duration.
 
 Printed: ONE JSON line.  ``value`` is tokens (B * N) per second of wall time
-over the K steps.  ``roofline`` prices the dominant kernel (the chunked main
-pass) against HBM: algorithmic bytes (Q, K, V read once, O written once) per
-launch over its mean event-timed duration.  ``cpu_baseline`` is the fp64
-oracle on the same workload timed on this host.  ``rows`` holds the other
-workloads measured the same way (non-causal, bf16 N=16384 and N=65536 with
-the chunk sweep, the GQA prefill and its 1024-step decode).
+over the K replayed steps (the eager rate is under ``eager``).  ``roofline``
+prices the dominant kernel (the chunked main pass) against HBM: algorithmic
+bytes (Q, K, V read once, O written once) per launch over its mean
+event-timed duration.  ``cpu_baseline`` is the fp64 oracle on the same
+workload timed on this host.  ``rows`` holds the other workloads measured
+the same way (non-causal, bf16 N=16384 and N=65536 with the chunk sweep, the
+GQA prefill and its 1024-step decode).
 """
 from __future__ import annotations
 
@@ -96,32 +100,84 @@ def kernel_name(w, chunk, causal):
     return (f"k_causal_chunks<{t},{w.d},{chunk}>" if causal else f"k_noncausal_apply<{t},{w.d}>")
 
 
-def time_fwd(la, hip, torch, w, q, k, v, out, ws, ws_bytes, causal, chunk, steps, warmup, stream, flush=None):
-    """Runs warm-up + timed steps; returns dict of wall and per-stage event times."""
+def fwd_args(la, w, q, k, v, out, ws, ws_bytes, causal, chunk):
     dt = la.LINATTN_BF16 if w.dtype == "bf16" else la.LINATTN_F32
+    return (q, k, v, out, w.B, w.H, w.Hkv, w.N, w.d, causal, 1, dt, None, None, chunk, ws, ws_bytes)
+
+
+def time_stages(la, hip, torch, args, steps, warmup, stream, flush=None):
+    """Steps through linattn_fwd_timed: HIP events on the library's stream around each stage."""
     evs = [[hip.event() for _ in range(4)] for _ in range(steps)]
     warm = [hip.event() for _ in range(4)]
 
     def call(ev):
-        rc = la.linattn_fwd_timed(q, k, v, out, w.B, w.H, w.Hkv, w.N, w.d, causal, 1, dt, None, None, chunk,
-                                  ws, ws_bytes, stream, events=ev)
+        rc = la.linattn_fwd_timed(*args, stream, events=ev)
         if rc != 0:
             raise la.LinattnError(rc, "linattn_fwd_timed")
 
     for _ in range(warmup):
         call(warm)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
         if flush is not None:
             flush()
         call(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     st = [[hip.ms(e[j], e[j + 1]) for j in range(3)] for e in evs]
     mean = [sum(s[j] for s in st) / steps for j in range(3)]
-    step_ms = sum(sum(s) for s in st) / steps
-    return {"wall_s": wall, "stage_ms": mean, "step_event_ms": step_ms}
+    return {"stage_ms": mean, "step_event_ms": sum(sum(s) for s in st) / steps}
+
+
+def time_eager(la, torch, args, steps, warmup, stream):
+    """K plain linattn_fwd calls back to back between two synchronisations (host launch cost included)."""
+    for _ in range(warmup):
+        rc = la.linattn_fwd(*args, stream)
+        if rc != 0:
+            raise la.LinattnError(rc, "linattn_fwd")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        la.linattn_fwd(*args, stream)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def time_graph(la, hip, torch, args, out, steps):
+    """The K steps captured once as a HIP graph and replayed: per-step time without host launch cost.
+
+    Also checks that the replay leaves the same output as an eager call (bitwise:
+    the kernels are deterministic)."""
+    la.linattn_fwd(*args, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    out.zero_()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        la.linattn_fwd(*args, side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream().cuda_stream
+        for _ in range(steps):
+            rc = la.linattn_fwd(*args, cap)
+            if rc != 0:
+                raise la.LinattnError(rc, "linattn_fwd (graph capture)")
+    g.replay()
+    torch.cuda.synchronize()
+    out.zero_()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hip.record(e0, stream)
+    g.replay()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    same = bool(torch.equal(out, ref))
+    del g
+    return {"event_ms": hip.ms(e0, e1) / steps, "ms": wall * 1e3 / steps, "matches_eager": same}
 
 
 def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, cold):
@@ -135,17 +191,22 @@ def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, cold):
     ws_bytes = ws.numel() * 4 if ws is not None else 0
     dt = la.LINATTN_BF16 if w.dtype == "bf16" else la.LINATTN_F32
     _, c, P = la.linattn_fwd_plan(w.B, w.H, w.Hkv, w.N, w.d, causal, dt, chunk)
-    r = time_fwd(la, hip, torch, w, q, k, v, out, ws, ws_bytes, causal, chunk, steps, warmup, stream)
+    args = fwd_args(la, w, q, k, v, out, ws, ws_bytes, causal, chunk)
+    eager_s = time_eager(la, torch, args, steps, warmup, stream)
+    gr = time_graph(la, hip, torch, args, out, steps)
+    r = time_stages(la, hip, torch, args, steps, warmup, stream)
     nb, fl = fwd_bytes(w), fwd_flops(w)
     k3 = r["stage_ms"][2] / 1e3
     row = {
         "causal": bool(causal), "chunk": c, "segments": P,
-        "ms_per_step": round(r["wall_s"] / steps * 1e3, 5),
-        "tokens_per_s": round(w.B * w.N * steps / r["wall_s"], 1),
+        "ms_per_step": round(gr["ms"], 5),
+        "tokens_per_s": round(w.B * w.N / (gr["ms"] / 1e3), 1),
+        "graph_matches_eager": gr["matches_eager"],
+        "eager": {"ms_per_step": round(eager_s * 1e3, 5), "tokens_per_s": round(w.B * w.N / eager_s, 1)},
         "stage_us": {"seg_totals": round(r["stage_ms"][0] * 1e3, 2), "seg_scan": round(r["stage_ms"][1] * 1e3, 2),
                      "main": round(r["stage_ms"][2] * 1e3, 2)},
         "roofline_main": roofline(nb, fl, k3, w.dtype, kernel_name(w, c, causal)),
-        "roofline_path": roofline(nb, fl, r["step_event_ms"] / 1e3, w.dtype, "whole step (all stages)"),
+        "roofline_path": roofline(nb, fl, gr["event_ms"] / 1e3, w.dtype, "whole step (graph replay, events)"),
     }
     if cold:
         # Same steps with the 256 MiB memory-side cache swept before each one
@@ -154,12 +215,13 @@ def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, cold):
         # whose write-back would be billed to the next kernel.
         scratch = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
         sink = torch.empty((), dtype=torch.float32, device="cuda")
-        rc = time_fwd(la, hip, torch, w, q, k, v, out, ws, ws_bytes, causal, chunk, max(5, steps // 4), 2, stream,
-                      flush=lambda: torch.sum(scratch, dim=0, out=sink))
+        rc = time_stages(la, hip, torch, args, max(5, steps // 4), 2, stream,
+                         flush=lambda: torch.sum(scratch, dim=0, out=sink))
         row["cold_stage_us"] = {"seg_totals": round(rc["stage_ms"][0] * 1e3, 2),
                                 "seg_scan": round(rc["stage_ms"][1] * 1e3, 2),
                                 "main": round(rc["stage_ms"][2] * 1e3, 2)}
-        row["cold_roofline_path"] = roofline(nb, fl, rc["step_event_ms"] / 1e3, w.dtype, "whole step, cold cache")
+        row["cold_roofline_path"] = roofline(nb, fl, rc["step_event_ms"] / 1e3, w.dtype,
+                                             "sum of stage events, cold cache")
         del scratch, sink
     del q, k, v, out, ws
     return row
@@ -186,39 +248,48 @@ def decode_row(la, hip, torch, steps_total, stream):
     qs, ks, vs = torch.stack(qs).cuda(), torch.stack(ks).cuda(), torch.stack(vs).cuda()
     out = torch.empty(steps_total, dw.B, dw.H, dw.d, dtype=qs.dtype, device="cuda")
     dt = la.LINATTN_BF16
-    ev = [hip.event() for _ in range(steps_total + 1)]
-    # eager pass with an event between consecutive steps: per-kernel durations
+    # eager pass (host launch cost included): one event pair around the loop
     S0, z0 = S.clone(), z.clone()
-    hip.record(ev[0], stream)
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
     for t in range(steps_total):
         rc = la.linattn_decode_step(S, z, qs[t], ks[t], vs[t], out[t], dw.B, dw.H, dw.Hkv, dw.d, 1, dt, stream)
         assert rc == 0
-        hip.record(ev[t + 1], stream)
+    hip.record(e1, stream)
     torch.cuda.synchronize()
-    per = [hip.ms(ev[t], ev[t + 1]) for t in range(steps_total)]
-    k_us = sum(per) / steps_total * 1e3
-    # whole 1024-step loop replayed as one HIP graph: per-step throughput
+    eager_us = hip.ms(e0, e1) / steps_total * 1e3
+    ref = out.clone()
+    # the same 1024 steps captured as one HIP graph and replayed from the same
+    # start state: per-step kernel time with no host in the loop
     S.copy_(S0)
     z.copy_(z0)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream().cuda_stream
         for t in range(steps_total):
-            la.linattn_decode_step(S, z, qs[t], ks[t], vs[t], out[t], dw.B, dw.H, dw.Hkv, dw.d, 1, dt, None)
+            la.linattn_decode_step(S, z, qs[t], ks[t], vs[t], out[t], dw.B, dw.H, dw.Hkv, dw.d, 1, dt, cap)
     S.copy_(S0)
     z.copy_(z0)
+    out.zero_()
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
     t0 = time.perf_counter()
+    hip.record(e0, stream)
     g.replay()
+    hip.record(e1, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    k_us = hip.ms(e0, e1) / steps_total * 1e3
+    same = bool(torch.equal(out, ref))
     nb = decode_bytes(dw.B, dw.H, dw.Hkv, dw.d, dw.dtype)
     fl = float(dw.B) * (dw.Hkv * (2 * dw.d ** 2 + 2 * dw.d) + dw.H * (2 * dw.d ** 2 + 4 * dw.d))
     res = {
         "batch": dw.B, "steps": steps_total,
-        "graph_us_per_step": round(wall / steps_total * 1e6, 2),
+        "graph_us_per_step": round(k_us, 2),
         "tokens_per_s": round(dw.B * steps_total / wall, 1),
-        "kernel_us": round(k_us, 2),
-        "roofline": roofline(nb, fl, k_us / 1e6, "bf16", "k_decode_step<bf16,128>"),
+        "graph_matches_eager": same,
+        "eager_us_per_step": round(eager_us, 2),
+        "roofline": roofline(nb, fl, k_us / 1e6, "bf16", "k_decode_step<bf16,128> (graph replay, per step)"),
         "note": "state (32 MiB fp32) fits the 256 MiB memory-side cache; it is read and written every step",
     }
     del S, z, qs, ks, vs, out, g
@@ -249,8 +320,8 @@ def cpu_baseline(w, seconds):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="cfg2", choices=["cfg1", "cfg2", "cfg3", "cfg4", "cfg5"])
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--rows", type=int, default=1, help="also measure the other workloads (0 = skip)")
@@ -295,6 +366,8 @@ def main():
         log("cpu_baseline", json.dumps(cpu))
 
     tok_s = head["tokens_per_s"]
+    if not head["graph_matches_eager"]:
+        raise SystemExit("graph replay output differs from the eager call")
     res = {
         "metric": "causal linear-attn fwd tokens/s (B2 H8 d64) + % of MFMA/HBM roofline",
         "value": tok_s,
@@ -309,7 +382,9 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic: seeded N(0,1) q, k, v (no dataset involved)",
         "config": {"workload": f"{args.workload}: {w.name}, causal, normaliser on", "B": w.B, "H": w.H,
-                   "Hkv": w.Hkv, "N": w.N, "d": w.d, "chunk": head["chunk"], "segments": head["segments"]},
+                   "Hkv": w.Hkv, "N": w.N, "d": w.d, "chunk": head["chunk"], "segments": head["segments"],
+                   "launch": "the K steps captured as one HIP graph and replayed (eager figures under 'eager')"},
+        "eager": head["eager"],
         "roofline": head["roofline_main"],
         "roofline_path": head["roofline_path"],
         "stage_us": head["stage_us"],

@@ -541,8 +541,15 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
     if (nch > 1) load_all(s0 + C);
     lds_barrier();
 
+    const bool carry_out = p == P - 1 && (state_out || z_out);
     for (int c = 0; c < nch; ++c) {
         const int t0 = s0 + c * C;
+        // Key tiles holding tokens < N; tiles past them add nothing and no
+        // query reads a copy published there.  In the last chunk of a
+        // segment the state after the last published copy is needed only
+        // when it is returned to the caller.
+        const int kt_valid = min(CT, (N - t0 + 31) / 32);
+        const int kt_upd = (c + 1 < nch || carry_out) ? kt_valid : min(kt_valid, RPC * (NSC - 1));
 
         // ---- phase 1: publish the state before every RPC-th key tile, absorb each tile
 #pragma unroll
@@ -555,7 +562,7 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
                 float zs = 0.f;
 #pragma unroll
                 for (int kt = 0; kt < CT; ++kt) {
-                    if (kt % RPC == 0) {
+                    if (kt % RPC == 0 && kt < kt_valid) {
                         const Tile<T, D> sST{smST[kt / RPC]};
 #pragma unroll
                         for (int q4 = 0; q4 < 4; ++q4) {
@@ -564,8 +571,10 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
                         }
                         if (zown && h == 0) smZ[kt / RPC][it * 32 + n] = (T)(zr + zs);
                     }
-                    const float dz = tile_state_update<T, D>(S[i], zown, it, jt, kt, sK, sV, lane);
-                    if (zown) zs += BF ? dz : dz + __shfl_xor(dz, 32);
+                    if (kt < kt_upd) {
+                        const float dz = tile_state_update<T, D>(S[i], zown, it, jt, kt, sK, sV, lane);
+                        if (zown) zs += BF ? dz : dz + __shfl_xor(dz, 32);
+                    }
                 }
                 if (zown) zr += zs;
             }
@@ -770,9 +779,12 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restric
 // ------------------------------------------------------------- decode_step
 //
 // One workgroup per (batch, kv head).  Thread tid owns the float4 column
-// group tid % (D/4) of rows tid / (D/4) + RG * i: it reads those state
-// elements once, adds phi(k)_i v_j, writes them back and keeps partial
-// phi(q)^T S sums for up to 4 query heads at a time.
+// group tid % (D/4) of rows tid / (D/4) + RG * i.  All global loads are
+// issued first (the state block, then k, v, z and the G query rows), so a
+// step costs one memory round trip: the state is updated with phi(k)_i v_j
+// in registers and written back, partial phi(q)^T S sums for 4 query heads
+// at a time are reduced through LDS, and each head's denominator is one
+// wave reduction.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ state, float *__restrict__ z,
                                                           const T *__restrict__ q, const T *__restrict__ k,
@@ -782,63 +794,82 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
     constexpr int C4 = D / 4;            // float4 groups per row
     constexpr int RG = kThreads / C4;    // row groups
     constexpr int NV = D / RG;           // rows per thread
-    constexpr int HB = 4;                // query heads per pass
+    constexpr int HB = 4;                // query heads per reduction pass
+    constexpr int GMAX = 32;             // query heads staged per pass of the outer loop
     __shared__ float sk[D], sv[D], sz[D];
-    __shared__ float sq[HB][D];
+    __shared__ float sq[GMAX][D];
+    __shared__ float sden[GMAX];
     __shared__ __attribute__((aligned(16))) float red[RG][HB][D];
 
     const int seq = blockIdx.x;
     const int b = seq / Hkv, gk = seq % Hkv;
-    const int tid = threadIdx.x, c4 = tid % C4, rg = tid / C4;
+    const int tid = threadIdx.x, c4 = tid % C4, rg = tid / C4, lane = tid & 63, wv = tid >> 6;
     float *Sb = state + (size_t)seq * D * D;
-    if (tid < D) {
-        const float fk = phi((float)k[(size_t)seq * D + tid]);
-        sk[tid] = fk;
-        sv[tid] = (float)v[(size_t)seq * D + tid];
-        if (normalise) {
-            const float zn = z[(size_t)seq * D + tid] + fk;
-            z[(size_t)seq * D + tid] = zn;
-            sz[tid] = zn;
-        }
-    }
-    __syncthreads();
+    const T *qb = q + ((size_t)b * H + (size_t)gk * G) * D;
+
     f32x4 Sr[NV];
-    const f32x4 vv{sv[4 * c4], sv[4 * c4 + 1], sv[4 * c4 + 2], sv[4 * c4 + 3]};
 #pragma unroll
     for (int i = 0; i < NV; ++i) Sr[i] = *reinterpret_cast<const f32x4 *>(Sb + (size_t)(rg + RG * i) * D + 4 * c4);
+    const int g_first = G < GMAX ? G : GMAX;
+    if (tid < D) {
+        sk[tid] = phi((float)k[(size_t)seq * D + tid]);
+        sv[tid] = (float)v[(size_t)seq * D + tid];
+        if (normalise) sz[tid] = z[(size_t)seq * D + tid];
+    }
+    for (int e = tid; e < g_first * D; e += kThreads) sq[e / D][e % D] = phi((float)qb[e]);
+    __syncthreads();
+
+    const f32x4 vv{sv[4 * c4], sv[4 * c4 + 1], sv[4 * c4 + 2], sv[4 * c4 + 3]};
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const float fk = sk[rg + RG * i];
-        Sr[i] += fk * vv;
+        Sr[i] += sk[rg + RG * i] * vv;
         *reinterpret_cast<f32x4 *>(Sb + (size_t)(rg + RG * i) * D + 4 * c4) = Sr[i];
     }
-    for (int g0 = 0; g0 < G; g0 += HB) {
-        const int nh = min(HB, G - g0);
-        for (int e = tid; e < nh * D; e += kThreads) {
-            const int hh = e / D, i = e % D;
-            sq[hh][i] = phi((float)q[((size_t)b * H + (size_t)gk * G + g0 + hh) * D + i]);
+    if (normalise && tid < D) {
+        const float zn = sz[tid] + sk[tid];
+        z[(size_t)seq * D + tid] = zn;
+        sz[tid] = zn;
+    }
+
+    for (int g0 = 0; g0 < G; g0 += GMAX) {
+        const int gn = G - g0 < GMAX ? G - g0 : GMAX;
+        if (g0 > 0) {
+            __syncthreads();
+            for (int e = tid; e < gn * D; e += kThreads) sq[e / D][e % D] = phi((float)qb[(size_t)g0 * D + e]);
         }
         __syncthreads();
-        for (int hh = 0; hh < nh; ++hh) {
-            f32x4 acc{};
+        // Denominators: wave wv reduces phi(q_g) . z for heads g = wv, wv + 4, ...
+        if (normalise) {
+            for (int g = wv; g < gn; g += 4) {
+                float a = 0.f;
+                for (int i = lane; i < D; i += 64) a += sq[g][i] * sz[i];
 #pragma unroll
-            for (int i = 0; i < NV; ++i) acc += sq[hh][rg + RG * i] * Sr[i];
-            *reinterpret_cast<f32x4 *>(&red[rg][hh][4 * c4]) = acc;
-        }
-        __syncthreads();
-        for (int e = tid; e < nh * D; e += kThreads) {
-            const int hh = e / D, j = e % D;
-            float num = 0.f;
-            for (int r = 0; r < RG; ++r) num += red[r][hh][j];
-            float o = num;
-            if (normalise) {
-                float den = 0.f;
-                for (int i = 0; i < D; ++i) den += sq[hh][i] * sz[i];
-                o = num / den;
+                for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o);
+                if (lane == 0) sden[g] = a;
             }
-            out[((size_t)b * H + (size_t)gk * G + g0 + hh) * D + j] = (T)o;
         }
-        __syncthreads();
+        for (int h0 = 0; h0 < gn; h0 += HB) {
+            const int nh = gn - h0 < HB ? gn - h0 : HB;
+#pragma unroll
+            for (int hh = 0; hh < HB; ++hh) {
+                if (hh < nh) {
+                    f32x4 acc{};
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) acc += sq[h0 + hh][rg + RG * i] * Sr[i];
+                    *reinterpret_cast<f32x4 *>(&red[rg][hh][4 * c4]) = acc;
+                }
+            }
+            __syncthreads();
+            for (int e = tid; e < nh * D; e += kThreads) {
+                const int hh = e / D, j = e % D;
+                float num = 0.f;
+#pragma unroll
+                for (int r = 0; r < RG; ++r) num += red[r][hh][j];
+                const float o = normalise ? num / sden[h0 + hh] : num;
+                out[((size_t)b * H + (size_t)gk * G + g0 + h0 + hh) * D + j] = (T)o;
+            }
+            __syncthreads();
+        }
     }
 }
 

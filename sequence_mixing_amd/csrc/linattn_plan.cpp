@@ -8,7 +8,8 @@
 namespace linattn {
 
 namespace {
-constexpr int kTargetWorkgroups = 512;    // two waves of workgroups over 256 CUs
+constexpr int kCUs = 256;
+constexpr int kTargetWorkgroups = 2 * kCUs;  // non-causal partial sums: two workgroups per CU
 
 bool valid_d(int d) { return d == 32 || d == 64 || d == 128; }
 bool valid_chunk(int c) { return c == 32 || c == 64 || c == 128 || c == 256; }
@@ -65,7 +66,13 @@ int make_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int ch
     q.ws_bytes = 0;
     if (B > 0 && N > 0) {
         const int nchunks = (N + C - 1) / C;
-        int P = (kTargetWorkgroups + q.nseq - 1) / q.nseq;
+        // Causal: one resident round of chunk-kernel workgroups (as many per
+        // CU as its occupancy allows), so every workgroup walks several
+        // chunks with the next one in flight instead of a second round
+        // starting cold.
+        const int e = dtype == LINATTN_BF16 ? 2 : 4;
+        const int tgt = q.causal ? kCUs * main_shape(e, d, C, gt).occ : kTargetWorkgroups;
+        int P = (tgt + q.nseq - 1) / q.nseq;
         if (P < 1) P = 1;
         if (P > nchunks) P = nchunks;
         const int seg_chunks = (nchunks + P - 1) / P;

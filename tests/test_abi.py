@@ -109,10 +109,14 @@ def test_plan_covers_every_token_with_whole_chunks():
                 c, P = plan(nseq, 1, 1, N, 64, 1, BF16, chunk)
                 assert c == chunk
                 nch = -(-N // c)
-                seg_chunks = -(-nch // max(1, min(nch, -(-512 // nseq))))
-                assert P == -(-N // (seg_chunks * c))
                 assert 1 <= P <= nch
-                assert (P - 1) * seg_chunks * c < N <= P * seg_chunks * c
+                # Segments are whole chunks: some segment length s chunks covers N
+                # with P segments, the last one non-empty.
+                assert any((P - 1) * s * c < N <= P * s * c for s in range(1, nch + 1))
+                # Enough workgroups to spread over the chip (one or two per CU),
+                # never more than two per CU.
+                assert nseq * P <= 512 + nseq
+                assert nseq * P >= min(nseq * nch, 128)
 
 
 def test_workspace_formula():

@@ -196,6 +196,25 @@ def test_decode_step_same_start_state(dtype, d, normalise):
             assert mat_rel_err(host(z), zr) <= 1e-6
 
 
+@pytest.mark.parametrize("B,H,Hkv,d,dtype", [(2, 40, 1, 128, "bf16"), (3, 6, 2, 64, "f32"), (1, 3, 3, 32, "bf16"),
+                                              (2, 70, 2, 64, "bf16")])
+def test_decode_step_head_groups(B, H, Hkv, d, dtype):
+    """Query-head groups that are not a multiple of 4, or larger than one staging pass (32 heads)."""
+    q0, k0, v0 = make_qkv(B, Hkv, Hkv, 20, d, dtype, 31 + H)
+    _, S, z = ops.fwd(gpu(q0), gpu(k0), gpu(v0), want_state=True)
+    Sr, zr = host(S).copy(), host(z).copy()
+    stream = DecodeStream(B, H, Hkv, d, dtype, 9 + H)
+    for step in range(3):
+        q, k, v = stream.next()
+        o = ops.decode_step(S, z, gpu(q), gpu(k), gpu(v))
+        ref = oracle.ref_decode_step(Sr, zr, q, k, v, normalise=True)
+        torch.cuda.synchronize()
+        tol = 1e-5 if dtype == "f32" else TOL[dtype]
+        assert rows_rel_err(host(o), ref) <= tol
+        assert mat_rel_err(host(S), Sr) <= 1e-5
+        assert mat_rel_err(host(z), zr) <= 1e-6
+
+
 def test_decode_continues_prefill_on_gpu():
     """Prefill(N) then one decode step equals row N of prefill(N + 1)."""
     B, H, Hkv, N, d = 2, 8, 2, 777, 64
