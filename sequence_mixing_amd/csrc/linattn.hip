@@ -44,7 +44,36 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
+
+// ------------------------------------------------------- buffer accesses
+//
+// Raw buffer loads/stores through a scalar descriptor (base, size in bytes).
+// The hardware checks every lane's byte offset against the size: loads out
+// of range return zero and stores out of range are dropped.  Tails and
+// masked lanes therefore need no branches, every staging step issues the
+// same instructions, and the compiler can wait for exactly the loads a step
+// consumes while later ones stay in flight.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr unsigned kOutOfRange = 0x80000000u;  // beyond every size used here (< 2^31)
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, int bytes)
+{
+    // Word 3: 32-bit data format (raw access, no swizzle, no format conversion).
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+template <typename G> __device__ __forceinline__ G buf_load16(Rsrc r, unsigned off)
+{
+    static_assert(sizeof(G) == 16, "16-byte group");
+    return __builtin_bit_cast(G, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+template <typename G> __device__ __forceinline__ void buf_store16(Rsrc r, unsigned off, G x)
+{
+    static_assert(sizeof(G) == 16, "16-byte group");
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
+}
 
 // Workgroup barrier for LDS hand-offs only.  __syncthreads() also drains
 // every outstanding global load (vmcnt), which would stall the register
@@ -224,15 +253,16 @@ __device__ __forceinline__ void load_chunk(typename Vt<T>::g16 (&r)[L], const T 
     }
 }
 
-// Writes a staged chunk to LDS: phi(K) and V, both row-major.  Tokens at or
-// past N get phi(k) = 0 (and v = 0) so that they add nothing to any sum.
+// Writes a staged chunk to LDS: phi(K) and V, both row-major.  Only the
+// first `rows` tokens are real; the others get phi(k) = 0 (their v is zero
+// too) so that they add nothing to any sum.
 template <typename T, int D, int C, int L>
 __device__ __forceinline__ void stage_rows(const typename Vt<T>::g16 (&kr)[L], const typename Vt<T>::g16 (&vr)[L],
-                                           Tile<T, D> sK, Tile<T, D> sV, int t0, int N, int tid)
+                                           Tile<T, D> sK, Tile<T, D> sV, int rows, int tid)
 {
     using G = Geo<T, D, C>;
     static_assert(L == G::LDV, "register array size");
-    const bool full = t0 + C <= N;
+    const bool full = rows >= C;
 #pragma unroll
     for (int l = 0; l < G::LDV; ++l) {
         const int e = tid + l * kThreads;
@@ -242,7 +272,7 @@ __device__ __forceinline__ void stage_rows(const typename Vt<T>::g16 (&kr)[L], c
 #pragma unroll
             for (int i = 0; i < G::U; ++i) fk[i] = (T)phi((float)kr[l][i]);
             if (!full) {
-                if (t0 + t >= N) fk = typename Vt<T>::g16{};
+                if (t >= rows) fk = typename Vt<T>::g16{};
             }
             sK.write16(t, q * G::U, fk);
             sV.write16(t, q * G::U, vr[l]);
@@ -316,14 +346,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
 #pragma unroll
     for (int i = 0; i < G::MAXST; ++i) acc[i] = f32x16{};
     // Two chunks in flight: register sets A and B alternate, chunk ci + 2 is
-    // requested as soon as chunk ci has been staged.
-    typename Vt<T>::g16 kA[G::LDV], vA[G::LDV], kB[G::LDV], vB[G::LDV];
-    load_chunk<T, D, C1>(kA, kb, s0, N, tid);
-    load_chunk<T, D, C1>(vA, vb, s0, N, tid);
-    if (nch > 1) {
-        load_chunk<T, D, C1>(kB, kb, s0 + C1, N, tid);
-        load_chunk<T, D, C1>(vB, vb, s0 + C1, N, tid);
-    }
+    // requested as soon as chunk ci has been staged.  Buffer loads: chunks
+    // past the segment read nothing, tokens past N read zeros.
+    using g16 = typename Vt<T>::g16;
+    constexpr int E = (int)sizeof(T);
+    g16 kA[G::LDV], vA[G::LDV], kB[G::LDV], vB[G::LDV];
+    auto rows_at = [&](int t0) { return t0 < s1 ? min(C1, s1 - t0) : 0; };
+    auto load = [&](g16 (&kr)[G::LDV], g16 (&vr)[G::LDV], int t0) {
+        const int rows = rows_at(t0);
+        const Rsrc rk = make_rsrc(kb + (size_t)t0 * D, rows * D * E);
+        const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, rows * D * E);
+#pragma unroll
+        for (int l = 0; l < G::LDV; ++l) {
+            const unsigned off = (unsigned)(tid + l * kThreads) * 16u;
+            kr[l] = buf_load16<g16>(rk, off);
+            vr[l] = buf_load16<g16>(rv, off);
+        }
+    };
+    load(kA, vA, s0);
+    __builtin_amdgcn_sched_barrier(0);  // keep chunk 0's loads ahead of chunk 1's, as in the loop
+    load(kB, vB, s0 + C1);
     auto absorb = [&](int buf) {
         const Tile<T, D> sK{smK[buf]}, sV{smV[buf]};
 #pragma unroll
@@ -337,23 +379,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
             }
         }
     };
+    // Chunks in pairs; with an odd count the last pair's second chunk lies
+    // past the segment and adds zeros (every step issues the same loads).
     for (int ci = 0; ci < nch; ci += 2) {
-        stage_rows<T, D, C1>(kA, vA, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, s0 + ci * C1, N, tid);
-        if (ci + 2 < nch) {
-            load_chunk<T, D, C1>(kA, kb, s0 + (ci + 2) * C1, N, tid);
-            load_chunk<T, D, C1>(vA, vb, s0 + (ci + 2) * C1, N, tid);
-        }
+        stage_rows<T, D, C1>(kA, vA, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, rows_at(s0 + ci * C1), tid);
+        load(kA, vA, s0 + (ci + 2) * C1);
         lds_barrier();
         absorb(0);
-        if (ci + 1 < nch) {
-            stage_rows<T, D, C1>(kB, vB, Tile<T, D>{smK[1]}, Tile<T, D>{smV[1]}, s0 + (ci + 1) * C1, N, tid);
-            if (ci + 3 < nch) {
-                load_chunk<T, D, C1>(kB, kb, s0 + (ci + 3) * C1, N, tid);
-                load_chunk<T, D, C1>(vB, vb, s0 + (ci + 3) * C1, N, tid);
-            }
-            lds_barrier();
-            absorb(1);
-        }
+        stage_rows<T, D, C1>(kB, vB, Tile<T, D>{smK[1]}, Tile<T, D>{smV[1]}, rows_at(s0 + (ci + 1) * C1), tid);
+        load(kB, vB, s0 + (ci + 3) * C1);
+        lds_barrier();
+        absorb(1);
     }
     float *out = ws + ((size_t)seq * nslots + p) * (size_t)D * (D + 1);
 #pragma unroll
@@ -445,6 +481,7 @@ struct Main {
     static constexpr int RPC = CT / NSC;
     static constexpr bool FITS = SH.fits;
     static constexpr int OCC = SH.occ;
+    static_assert(SH.lk == LK && SH.lq == LQ, "staging shape");
     __device__ static int tile_of(int w, int i) { return w * MAXST + i; }
 };
 
@@ -495,50 +532,79 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
         }
     }
     // ---- staging: raw K, V, q of a chunk in registers, one chunk ahead
-    g16 kr[M::LK], vr[M::LK], qr[M::LQ];
-    auto load_all = [&](int t0) {
-        load_chunk<T, D, C>(kr, kb, t0, N, tid);
-        load_chunk<T, D, C>(vr, vb, t0, N, tid);
-        const bool full = t0 + C <= N;
+    // Raw K, V, q of the next chunk in registers: loaded one chunk ahead.
+    constexpr int E = (int)sizeof(T);
+    struct Regs {
+        g16 k[M::LK], v[M::LK], q[M::LQ];
+    };
+    Regs ra;
+    // q / out group l of this thread: byte offset from (head block, token t0)
+    // and its token row within the chunk (qt = C marks a group past the block).
+    unsigned qoff[M::LQ];
+    int qt[M::LQ];
+#pragma unroll
+    for (int l = 0; l < M::LQ; ++l) {
+        const int e = tid + l * kThreads;
+        const int row = e / GPR, qq = e % GPR;
+        const int g = row / C, t = row % C;
+        const bool in = M::QG % kThreads == 0 || e < M::QG;
+        qoff[l] = (unsigned)((g * N + t) * D + qq * U) * E;
+        qt[l] = in ? t : C;
+    }
+    const int qspan = GT * N * D;  // elements of the head block's q (and out)
+    // Loads chunk [t0, t0 + C) of K, V and q; nothing (zeros) when the chunk
+    // lies past the segment (t0 >= s1), zeros for tokens past N.
+    auto load_all = [&](Regs &r, int t0) {
+        const int rows = t0 < s1 ? min(C, N - t0) : 0;
+        const Rsrc rk = make_rsrc(kb + (size_t)t0 * D, rows * D * E);
+        const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, rows * D * E);
+#pragma unroll
+        for (int l = 0; l < M::LK; ++l) {
+            const unsigned off = (unsigned)(tid + l * kThreads) * 16u;
+            r.k[l] = buf_load16<g16>(rk, off);
+            r.v[l] = buf_load16<g16>(rv, off);
+        }
+        const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, rows ? (qspan - t0 * D) * E : 0);
+#pragma unroll
+        for (int l = 0; l < M::LQ; ++l) r.q[l] = buf_load16<g16>(rq, qt[l] < rows ? qoff[l] : kOutOfRange);
+    };
+    // The output parked in the q rows: read into registers before phi(q) of
+    // the next chunk overwrites them, stored after the next loads are issued
+    // (so the stores may still be in flight when those loads are consumed).
+    auto read_out = [&](g16 (&o)[M::LQ]) {
 #pragma unroll
         for (int l = 0; l < M::LQ; ++l) {
             const int e = tid + l * kThreads;
-            const int row = e / GPR, qq = e % GPR;  // row = g * C + token
-            const int g = row / C, t = row % C;
-            g16 x = {};
-            if ((M::QG % kThreads == 0 || e < M::QG) && (full || t0 + t < N))
-                x = *reinterpret_cast<const g16 *>(qb + (size_t)g * N * D + (size_t)(t0 + t) * D + qq * U);
-            qr[l] = x;
+            const int row = (M::QG % kThreads == 0 || e < M::QG) ? e / GPR : 0, qq = e % GPR;
+            o[l] = *reinterpret_cast<const g16 *>(smQ + sQ.at(row, qq * U));
         }
     };
-    // Stores the output parked in the q rows (chunk starting at t_prev; none
-    // when t_prev < 0) and stages phi(q) of the chunk starting at t0 there.
-    auto stage_q = [&](int t_prev, int t0) {
+    auto store_out = [&](const g16 (&o)[M::LQ], int t_prev) {
+        const int rows = min(C, N - t_prev);
+        const Rsrc ro = make_rsrc(ob + (size_t)t_prev * D, (qspan - t_prev * D) * E);
+#pragma unroll
+        for (int l = 0; l < M::LQ; ++l) buf_store16<g16>(ro, qt[l] < rows ? qoff[l] : kOutOfRange, o[l]);
+    };
+    // phi(q) of the staged chunk into the q rows.
+    auto stage_q = [&](const Regs &r) {
 #pragma unroll
         for (int l = 0; l < M::LQ; ++l) {
             const int e = tid + l * kThreads;
             if (M::QG % kThreads == 0 || e < M::QG) {
                 const int row = e / GPR, qq = e % GPR;
-                const int g = row / C, t = row % C;
-                if (t_prev >= 0 && t_prev + t < N) {
-                    const g16 o = *reinterpret_cast<const g16 *>(smQ + sQ.at(row, qq * U));
-                    *reinterpret_cast<g16 *>(ob + (size_t)g * N * D + (size_t)(t_prev + t) * D + qq * U) = o;
-                }
-                if (t0 >= 0) {
-                    g16 fq;
+                g16 fq;
 #pragma unroll
-                    for (int i = 0; i < U; ++i) fq[i] = (T)phi((float)qr[l][i]);
-                    sQ.write16(row, qq * U, fq);
-                }
+                for (int i = 0; i < U; ++i) fq[i] = (T)phi((float)r.q[l][i]);
+                sQ.write16(row, qq * U, fq);
             }
         }
     };
 
     // ---- prologue: chunk 0 staged, chunk 1 in flight
-    load_all(s0);
-    stage_rows<T, D, C>(kr, vr, sK, sV, s0, N, tid);
-    stage_q(-1, s0);
-    if (nch > 1) load_all(s0 + C);
+    load_all(ra, s0);
+    stage_rows<T, D, C>(ra.k, ra.v, sK, sV, min(C, N - s0), tid);
+    stage_q(ra);
+    load_all(ra, s0 + C);
     lds_barrier();
 
     const bool carry_out = p == P - 1 && (state_out || z_out);
@@ -668,14 +734,18 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
         }
         lds_barrier();
 
-        // ---- staging of the next chunk (and the stores of this one)
+        // ---- staging of the next chunk (and the stores of this one); the
+        // registers are refilled with the chunk after it
+        g16 o[M::LQ];
+        read_out(o);
         if (c + 1 < nch) {
-            stage_rows<T, D, C>(kr, vr, sK, sV, t0 + C, N, tid);
-            stage_q(t0, t0 + C);
-            if (c + 2 < nch) load_all(t0 + 2 * C);
+            stage_rows<T, D, C>(ra.k, ra.v, sK, sV, min(C, N - t0 - C), tid);
+            stage_q(ra);
+            load_all(ra, t0 + 2 * C);  // past the segment: no access
+            store_out(o, t0);
             lds_barrier();
         } else {
-            stage_q(t0, -1);
+            store_out(o, t0);
         }
     }
 

@@ -50,8 +50,14 @@ int make_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int ch
     const int G = H / Hkv;
     const int C = chunk ? chunk : auto_chunk(dtype, d, G, causal);
     if (C == 0) return LINATTN_ERR_UNSUPPORTED;
-    const int gt = heads_per_block(dtype, d, C, G);
+    int gt = heads_per_block(dtype, d, C, G);
     if (gt == 0) return LINATTN_ERR_UNSUPPORTED;
+    // The chunk kernel addresses a head block's q and out (gt * N * d
+    // elements) with 32-bit byte offsets: fewer heads per block for very long
+    // sequences, and an error when one head alone exceeds 2 GiB.
+    const int64_t esz = dtype == LINATTN_BF16 ? 2 : 4;
+    while (gt > 1 && (int64_t)gt * N * d * esz > INT32_MAX) gt /= 2;
+    if ((int64_t)N * d * esz > INT32_MAX) return LINATTN_ERR_SHAPE;
 
     Plan q{};
     q.B = B; q.H = H; q.Hkv = Hkv; q.N = N; q.d = d; q.G = G;

@@ -10,9 +10,12 @@ namespace linattn {
 // phi(K), V and phi(Q) of a chunk ((2 + GT) C D elements) plus nsc copies of
 // the transposed state (D x D) and of z (D); nsc is one copy per 32-token key
 // tile, or one per two key tiles when that keeps two workgroups on a CU.
+// Each thread stages lk + lk + lq 16-byte groups (raw K, V and q of the
+// next chunk, 4 registers each).
 struct MainShape {
     int nsc;      // state copies per chunk
     int occ;      // workgroups per CU the kernel is built for (1 or 2)
+    int lk;       // 16-byte K (and V) groups each thread stages per chunk
     int lq;       // 16-byte q groups each thread stages per chunk
     bool fits;    // buildable: LDS within 160 KiB, lq <= 8, at most 2 key tiles per copy
     unsigned long lds;
@@ -27,16 +30,21 @@ constexpr MainShape main_shape(int e, int D, int C, int GT)
 {
     const unsigned long half = 80 * 1024, full = 160 * 1024;
     const int ct = C / 32;
-    const int occ_reg = D * e <= 128 ? 2 : 1;  // register budget allows two workgroups
+    const int u = 16 / e;
+    const int lk = (C * (D / u) + 255) / 256;
+    const int lq = (GT * C * (D / u) + 255) / 256;
+    const int stage_regs = 4 * (2 * lk + lq);
+    // Two workgroups per CU leave 256 registers per lane: enough for the
+    // 16-bit kernels up to d = 64 with at most 48 staging registers.
+    const int occ_reg = (D * e <= 128 && stage_regs <= 48) ? 2 : 1;
     int nsc = ct;
     if (occ_reg == 2 && main_lds(e, D, C, GT, ct) <= half) nsc = ct;
     else if (occ_reg == 2 && ct >= 2 && main_lds(e, D, C, GT, ct / 2) <= half) nsc = ct / 2;
     else if (main_lds(e, D, C, GT, ct) <= full) nsc = ct;
     else nsc = ct >= 2 ? ct / 2 : 1;
     const unsigned long lds = main_lds(e, D, C, GT, nsc);
-    const int u = 16 / e;
-    const int lq = (GT * C * (D / u) + 255) / 256;
-    MainShape m{nsc, (occ_reg == 2 && lds <= half) ? 2 : 1, lq, lds <= full && lq <= 8 && ct / nsc <= 2, lds};
+    const int occ = (occ_reg == 2 && lds <= half) ? 2 : 1;
+    MainShape m{nsc, occ, lk, lq, lds <= full && lq <= 8 && ct / nsc <= 2, lds};
     return m;
 }
 
