@@ -866,8 +866,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
     constexpr int NV = D / RG;           // rows per thread
     constexpr int HB = 4;                // query heads per reduction pass
     constexpr int GMAX = 32;             // query heads staged per pass of the outer loop
-    __shared__ float sk[D], sv[D], sz[D];
-    __shared__ float sq[GMAX][D];
+    constexpr int QGR = (GMAX * D / Vt<T>::U + kThreads - 1) / kThreads;  // q groups per thread per pass
+    constexpr int QPAD = QGR * kThreads * Vt<T>::U > GMAX * D ? QGR * kThreads * Vt<T>::U : GMAX * D;
+    // Padded so that every thread writes its loaded group (the compiler would
+    // otherwise sink a load into the branch that guards its write, behind the
+    // state loads): only the first D (or G * D) entries are read.
+    constexpr int KPAD = kThreads * Vt<T>::U;
+    __shared__ float sk[KPAD], sv[KPAD], sz[kThreads * 4];
+    __shared__ float sqf[QPAD];  // phi(q) of head g at sqf[g * D + i]
     __shared__ float sden[GMAX];
     __shared__ __attribute__((aligned(16))) float red[RG][HB][D];
 
@@ -877,42 +883,67 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
     float *Sb = state + (size_t)seq * D * D;
     const T *qb = q + ((size_t)b * H + (size_t)gk * G) * D;
 
+    // The small operands first (k, v, z, the first query heads, as 16-byte
+    // buffer loads that read zeros past their end), then the state rows:
+    // waiting for the small ones leaves every state load in flight, and each
+    // state row is updated and stored as soon as it lands, so the stores
+    // overlap the remaining loads.
+    using g16 = typename Vt<T>::g16;
+    constexpr int U = Vt<T>::U;                             // elements per 16 bytes
+    constexpr int E = (int)sizeof(T);
+    const int g_first = G < GMAX ? G : GMAX;
+    const unsigned off = (unsigned)tid * 16u;
+    const g16 kg = buf_load16<g16>(make_rsrc(k + (size_t)seq * D, D * E), off);
+    const g16 vg = buf_load16<g16>(make_rsrc(v + (size_t)seq * D, D * E), off);
+    const f32x4 zg = buf_load16<f32x4>(make_rsrc(normalise ? z + (size_t)seq * D : nullptr, normalise ? D * 4 : 0), off);
+    g16 qg[QGR];
+    const Rsrc rq = make_rsrc(qb, g_first * D * E);
+#pragma unroll
+    for (int j = 0; j < QGR; ++j) qg[j] = buf_load16<g16>(rq, off + (unsigned)j * kThreads * 16u);
+    __builtin_amdgcn_sched_barrier(0);  // small loads stay ahead of the state loads
     f32x4 Sr[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) Sr[i] = *reinterpret_cast<const f32x4 *>(Sb + (size_t)(rg + RG * i) * D + 4 * c4);
-    const int g_first = G < GMAX ? G : GMAX;
-    if (tid < D) {
-        sk[tid] = phi((float)k[(size_t)seq * D + tid]);
-        sv[tid] = (float)v[(size_t)seq * D + tid];
-        if (normalise) sz[tid] = z[(size_t)seq * D + tid];
+    for (int i = 0; i < NV; ++i) {
+        Sr[i] = *reinterpret_cast<const f32x4 *>(Sb + (size_t)(rg + RG * i) * D + 4 * c4);
+        __builtin_amdgcn_sched_barrier(0);  // state rows issued in the order they are consumed
     }
-    for (int e = tid; e < g_first * D; e += kThreads) sq[e / D][e % D] = phi((float)qb[e]);
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        sk[tid * U + i] = phi((float)kg[i]);
+        sv[tid * U + i] = (float)vg[i];
+    }
+#pragma unroll
+    for (int j = 0; j < QGR; ++j) {
+        const int e0 = (tid + j * kThreads) * U;
+#pragma unroll
+        for (int i = 0; i < U; ++i) sqf[e0 + i] = phi((float)qg[j][i]);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sz[tid * 4 + i] = zg[i] + sk[tid * 4 + i];
 
     const f32x4 vv{sv[4 * c4], sv[4 * c4 + 1], sv[4 * c4 + 2], sv[4 * c4 + 3]};
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         Sr[i] += sk[rg + RG * i] * vv;
         *reinterpret_cast<f32x4 *>(Sb + (size_t)(rg + RG * i) * D + 4 * c4) = Sr[i];
+        __builtin_amdgcn_sched_barrier(0);  // rows in load order: each store waits for its own row only
     }
-    if (normalise && tid < D) {
-        const float zn = sz[tid] + sk[tid];
-        z[(size_t)seq * D + tid] = zn;
-        sz[tid] = zn;
-    }
+    lds_barrier();
+    if (normalise && tid < D) z[(size_t)seq * D + tid] = sz[tid];
 
     for (int g0 = 0; g0 < G; g0 += GMAX) {
         const int gn = G - g0 < GMAX ? G - g0 : GMAX;
         if (g0 > 0) {
+            lds_barrier();
+            for (int e = tid; e < gn * D; e += kThreads) sqf[e] = phi((float)qb[(size_t)g0 * D + e]);
             __syncthreads();
-            for (int e = tid; e < gn * D; e += kThreads) sq[e / D][e % D] = phi((float)qb[(size_t)g0 * D + e]);
         }
-        __syncthreads();
         // Denominators: wave wv reduces phi(q_g) . z for heads g = wv, wv + 4, ...
         if (normalise) {
             for (int g = wv; g < gn; g += 4) {
                 float a = 0.f;
-                for (int i = lane; i < D; i += 64) a += sq[g][i] * sz[i];
+                for (int i = lane; i < D; i += 64) a += sqf[g * D + i] * sz[i];
 #pragma unroll
                 for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o);
                 if (lane == 0) sden[g] = a;
@@ -925,7 +956,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
                 if (hh < nh) {
                     f32x4 acc{};
 #pragma unroll
-                    for (int i = 0; i < NV; ++i) acc += sq[h0 + hh][rg + RG * i] * Sr[i];
+                    for (int i = 0; i < NV; ++i) acc += sqf[(h0 + hh) * D + rg + RG * i] * Sr[i];
                     *reinterpret_cast<f32x4 *>(&red[rg][hh][4 * c4]) = acc;
                 }
             }
