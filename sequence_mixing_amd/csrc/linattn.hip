@@ -256,26 +256,26 @@ __device__ __forceinline__ void load_chunk(typename Vt<T>::g16 (&r)[L], const T 
 // Writes a staged chunk to LDS: phi(K) and V, both row-major.  Only the
 // first `rows` tokens are real; the others get phi(k) = 0 (their v is zero
 // too) so that they add nothing to any sum.
-template <typename T, int D, int C, int L>
+template <typename T, int D, int C, int TH, int L>
 __device__ __forceinline__ void stage_rows(const typename Vt<T>::g16 (&kr)[L], const typename Vt<T>::g16 (&vr)[L],
                                            Tile<T, D> sK, Tile<T, D> sV, int rows, int tid)
 {
-    using G = Geo<T, D, C>;
-    static_assert(L == G::LDV, "register array size");
+    constexpr int U = Vt<T>::U, GPR = D / U, NGRP = C * GPR;
+    static_assert(L == (NGRP + TH - 1) / TH, "register array size");
     const bool full = rows >= C;
 #pragma unroll
-    for (int l = 0; l < G::LDV; ++l) {
-        const int e = tid + l * kThreads;
-        if (G::NGRP % kThreads == 0 || e < G::NGRP) {
-            const int t = e / G::GPR, q = e % G::GPR;
+    for (int l = 0; l < L; ++l) {
+        const int e = tid + l * TH;
+        if (NGRP % TH == 0 || e < NGRP) {
+            const int t = e / GPR, q = e % GPR;
             typename Vt<T>::g16 fk;
 #pragma unroll
-            for (int i = 0; i < G::U; ++i) fk[i] = (T)phi((float)kr[l][i]);
+            for (int i = 0; i < U; ++i) fk[i] = (T)phi((float)kr[l][i]);
             if (!full) {
                 if (t >= rows) fk = typename Vt<T>::g16{};
             }
-            sK.write16(t, q * G::U, fk);
-            sV.write16(t, q * G::U, vr[l]);
+            sK.write16(t, q * U, fk);
+            sV.write16(t, q * U, vr[l]);
         }
     }
 }
@@ -382,11 +382,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
     // Chunks in pairs; with an odd count the last pair's second chunk lies
     // past the segment and adds zeros (every step issues the same loads).
     for (int ci = 0; ci < nch; ci += 2) {
-        stage_rows<T, D, C1>(kA, vA, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, rows_at(s0 + ci * C1), tid);
+        stage_rows<T, D, C1, kThreads>(kA, vA, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, rows_at(s0 + ci * C1), tid);
         load(kA, vA, s0 + (ci + 2) * C1);
         lds_barrier();
         absorb(0);
-        stage_rows<T, D, C1>(kB, vB, Tile<T, D>{smK[1]}, Tile<T, D>{smV[1]}, rows_at(s0 + (ci + 1) * C1), tid);
+        stage_rows<T, D, C1, kThreads>(kB, vB, Tile<T, D>{smK[1]}, Tile<T, D>{smV[1]}, rows_at(s0 + (ci + 1) * C1), tid);
         load(kB, vB, s0 + (ci + 3) * C1);
         lds_barrier();
         absorb(1);
@@ -467,26 +467,34 @@ __global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, i
 // on memory.
 template <typename T, int D, int C, int GT>
 struct Main {
+    static constexpr linattn::MainShape SH = linattn::main_shape((int)sizeof(T), D, C, GT);
+    static constexpr int NW = SH.nw, TH = 64 * NW;   // waves and threads per workgroup
     static constexpr int U = Vt<T>::U;
     static constexpr int CT = C / 32, DT = D / 32, KBD = D / 16;
-    static constexpr int NST = DT * DT, MAXST = (NST + 3) / 4;
+    static constexpr int NST = DT * DT, MAXST = (NST + NW - 1) / NW;
     static constexpr int GPR = D / U;                // 16-byte groups per row
     static constexpr int KVG = C * GPR;              // groups of one K (or V) chunk
     static constexpr int QG = GT * C * GPR;          // groups of the chunk's q rows
-    static constexpr int LK = (KVG + kThreads - 1) / kThreads;
-    static constexpr int LQ = (QG + kThreads - 1) / kThreads;
-    static constexpr int NU = GT * CT;               // units per chunk
-    static constexpr linattn::MainShape SH = linattn::main_shape((int)sizeof(T), D, C, GT);
+    static constexpr int LK = (KVG + TH - 1) / TH;
+    static constexpr int LQ = (QG + TH - 1) / TH;
+    static constexpr int NU = GT * CT;               // units (query head, 32-row query tile) per chunk
+    // With fewer units than waves, a unit's output columns are split over
+    // PARTS waves (each recomputes the unit's scores and denominator).
+    static constexpr int PARTS = NU >= NW ? 1 : (NW / NU < DT ? NW / NU : DT);
+    static constexpr int NWI = NU * PARTS;           // phase-2 work items
+    static constexpr int CTP = DT / PARTS;           // 32-column output tiles per item
     static constexpr int NSC = SH.nsc;
     static constexpr int RPC = CT / NSC;
     static constexpr bool FITS = SH.fits;
     static constexpr int OCC = SH.occ;
     static_assert(SH.lk == LK && SH.lq == LQ, "staging shape");
+    static_assert(DT % PARTS == 0 && (PARTS == 1 || NWI <= NW), "phase-2 split");
+    static_assert(DT % MAXST == 0 || NST <= NW, "z owner: every column-0 state tile is some wave's first");
     __device__ static int tile_of(int w, int i) { return w * MAXST + i; }
 };
 
 template <typename T, int D, int C, int GT>
-__global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_chunks(
+__global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) void k_causal_chunks(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ out,
     const float *__restrict__ ws, float *__restrict__ state_out, float *__restrict__ z_out,
     int H, int Hkv, int N, int G, int P, int seg_len, int normalise)
@@ -496,6 +504,7 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
     using g16 = typename Vt<T>::g16;
     constexpr bool BF = sizeof(T) == 2;
     constexpr int U = M::U, CT = M::CT, DT = M::DT, KBD = M::KBD, GPR = M::GPR, NSC = M::NSC, RPC = M::RPC;
+    constexpr int NW = M::NW, TH = M::TH;
 
     __shared__ __attribute__((aligned(16))) T smK[C * D];
     __shared__ __attribute__((aligned(16))) T smV[C * D];
@@ -544,10 +553,10 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
     int qt[M::LQ];
 #pragma unroll
     for (int l = 0; l < M::LQ; ++l) {
-        const int e = tid + l * kThreads;
+        const int e = tid + l * TH;
         const int row = e / GPR, qq = e % GPR;
         const int g = row / C, t = row % C;
-        const bool in = M::QG % kThreads == 0 || e < M::QG;
+        const bool in = M::QG % TH == 0 || e < M::QG;
         qoff[l] = (unsigned)((g * N + t) * D + qq * U) * E;
         qt[l] = in ? t : C;
     }
@@ -560,7 +569,7 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
         const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, rows * D * E);
 #pragma unroll
         for (int l = 0; l < M::LK; ++l) {
-            const unsigned off = (unsigned)(tid + l * kThreads) * 16u;
+            const unsigned off = (unsigned)(tid + l * TH) * 16u;
             r.k[l] = buf_load16<g16>(rk, off);
             r.v[l] = buf_load16<g16>(rv, off);
         }
@@ -574,8 +583,8 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
     auto read_out = [&](g16 (&o)[M::LQ]) {
 #pragma unroll
         for (int l = 0; l < M::LQ; ++l) {
-            const int e = tid + l * kThreads;
-            const int row = (M::QG % kThreads == 0 || e < M::QG) ? e / GPR : 0, qq = e % GPR;
+            const int e = tid + l * TH;
+            const int row = (M::QG % TH == 0 || e < M::QG) ? e / GPR : 0, qq = e % GPR;
             o[l] = *reinterpret_cast<const g16 *>(smQ + sQ.at(row, qq * U));
         }
     };
@@ -589,8 +598,8 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
     auto stage_q = [&](const Regs &r) {
 #pragma unroll
         for (int l = 0; l < M::LQ; ++l) {
-            const int e = tid + l * kThreads;
-            if (M::QG % kThreads == 0 || e < M::QG) {
+            const int e = tid + l * TH;
+            if (M::QG % TH == 0 || e < M::QG) {
                 const int row = e / GPR, qq = e % GPR;
                 g16 fq;
 #pragma unroll
@@ -602,7 +611,7 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
 
     // ---- prologue: chunk 0 staged, chunk 1 in flight
     load_all(ra, s0);
-    stage_rows<T, D, C>(ra.k, ra.v, sK, sV, min(C, N - s0), tid);
+    stage_rows<T, D, C, TH>(ra.k, ra.v, sK, sV, min(C, N - s0), tid);
     stage_q(ra);
     load_all(ra, s0 + C);
     lds_barrier();
@@ -648,16 +657,18 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
         lds_barrier();
 
         // ---- phase 2: query tiles
-        for (int u = w; u < M::NU; u += 4) {
+        // phi(q) fragments of unit u: lane (h, n) holds query n, features kq*16 + 8h + s.
+        auto unit_qf = [&](int u, v8 (&qf)[KBD]) {
+            const int qrow = (u / CT) * C + (u % CT) * 32 + n;
+#pragma unroll
+            for (int kq = 0; kq < KBD; ++kq) qf[kq] = sQ.read8(qrow, kq * 16 + h * 8);
+        };
+        // Output columns ct0 .. ct0 + CTP - 1 of unit u, parked in its q rows.
+        auto unit_run = [&](int u, int ct0, const v8 (&qf)[KBD]) {
             const int g = u / CT, r = u % CT;
-            if (t0 + r * 32 >= N) continue;  // tile entirely past the end
             const int j = r / RPC;
             const bool off = r % RPC != 0;   // one unmasked key tile r-1 before the diagonal
             const int qrow = g * C + r * 32 + n;
-            // phi(q) fragments: lane (h, n) holds query n, features kq*16 + 8h + s.
-            v8 qf[KBD];
-#pragma unroll
-            for (int kq = 0; kq < KBD; ++kq) qf[kq] = sQ.read8(qrow, kq * 16 + h * 8);
             // Pt[key][query] = phi(K) phi(Q)^T; accumulator reg i holds key
             // 8(i/4) + 4h + i%4 of the tile for query n.
             v8 pb0, pb1, po0 = v8{}, po1 = v8{};
@@ -712,7 +723,7 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
             const float inv = normalise ? 1.f / den : 1.f;
             const Tile<T, D> sST{smST[j]};
 #pragma unroll
-            for (int ct = 0; ct < DT; ++ct) {
+            for (int ct = ct0; ct < ct0 + M::CTP; ++ct) {
                 // O^T[feature][query] = V^T Pt (slot s of K-block kb2 holds key
                 // 16 kb2 + 8 (s/4) + 4h + s%4) + V^T Po + S_j^T phi(Q)^T.
                 f32x16 O = f32x16{};
@@ -724,13 +735,30 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
                 }
 #pragma unroll
                 for (int kq = 0; kq < KBD; ++kq) mma(O, sST.read8(ct * 32 + n, kq * 16 + h * 8), qf[kq]);
-                // Park O in this unit's own q rows (no other unit reads them).
+                // Park O in this unit's own q rows (every reader of them has read its phi(q)).
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     f32x4 x{O[4 * q4] * inv, O[4 * q4 + 1] * inv, O[4 * q4 + 2] * inv, O[4 * q4 + 3] * inv};
                     sQ.write4(qrow, ct * 32 + 8 * q4 + 4 * h, cvt4<T>(x));
                 }
             }
+        };
+        if constexpr (M::PARTS == 1) {
+            for (int u = w; u < M::NU; u += NW) {
+                if (t0 + (u % CT) * 32 >= N) continue;  // tile entirely past the end
+                v8 qf[KBD];
+                unit_qf(u, qf);
+                unit_run(u, 0, qf);
+            }
+        } else {
+            // One item per wave: every part reads the unit's phi(q) before
+            // any part parks output columns in those rows.
+            const int u = w / M::PARTS;
+            const bool has = w < M::NWI && t0 + (u % CT) * 32 < N;
+            v8 qf[KBD];
+            if (has) unit_qf(u, qf);
+            lds_barrier();
+            if (has) unit_run(u, (w % M::PARTS) * M::CTP, qf);
         }
         lds_barrier();
 
@@ -739,7 +767,7 @@ __global__ __launch_bounds__(kThreads, (Main<T, D, C, GT>::OCC)) void k_causal_c
         g16 o[M::LQ];
         read_out(o);
         if (c + 1 < nch) {
-            stage_rows<T, D, C>(ra.k, ra.v, sK, sV, min(C, N - t0 - C), tid);
+            stage_rows<T, D, C, TH>(ra.k, ra.v, sK, sV, min(C, N - t0 - C), tid);
             stage_q(ra);
             load_all(ra, t0 + 2 * C);  // past the segment: no access
             store_out(o, t0);
@@ -1021,9 +1049,9 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
 #define LINATTN_MAIN(GT)                                                                                            \
     case GT:                                                                                                       \
         if constexpr (Main<T, D, C, GT>::FITS) {                                                                   \
-            hipLaunchKernelGGL((k_causal_chunks<T, D, C, GT>), grid, dim3(kThreads), 0, st, qq, kk, vv, oo,         \
-                               (const float *)ws, state_out, z_out, pl.H, pl.Hkv, pl.N, pl.G, P, pl.seg_len,       \
-                               normalise);                                                                         \
+            hipLaunchKernelGGL((k_causal_chunks<T, D, C, GT>), grid, dim3(Main<T, D, C, GT>::TH), 0, st, qq, kk,   \
+                               vv, oo, (const float *)ws, state_out, z_out, pl.H, pl.Hkv, pl.N, pl.G, P,           \
+                               pl.seg_len, normalise);                                                             \
             break;                                                                                                 \
         } else {                                                                                                   \
             return LINATTN_ERR_UNSUPPORTED;                                                                        \

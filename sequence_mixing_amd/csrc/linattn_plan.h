@@ -11,13 +11,17 @@ namespace linattn {
 // the transposed state (D x D) and of z (D); nsc is one copy per 32-token key
 // tile, or one per two key tiles when that keeps two workgroups on a CU.
 // Each thread stages lk + lk + lq 16-byte groups (raw K, V and q of the
-// next chunk, 4 registers each).
+// next chunk, 4 registers each).  A workgroup has 4 waves, or 8 when it is
+// alone on its CU with 16-bit data (two waves per SIMD then hide each
+// other's waits; fp32 keeps 4 since its scores would be recomputed).
 struct MainShape {
     int nsc;      // state copies per chunk
     int occ;      // workgroups per CU the kernel is built for (1 or 2)
+    int nw;       // waves per workgroup (4 or 8)
     int lk;       // 16-byte K (and V) groups each thread stages per chunk
     int lq;       // 16-byte q groups each thread stages per chunk
-    bool fits;    // buildable: LDS within 160 KiB, lq <= 8, at most 2 key tiles per copy
+    bool fits;    // buildable: LDS within 160 KiB, at most 8 q groups per thread of 4 waves
+                  // (a register budget), at most 2 key tiles per copy
     unsigned long lds;
 };
 
@@ -31,9 +35,9 @@ constexpr MainShape main_shape(int e, int D, int C, int GT)
     const unsigned long half = 80 * 1024, full = 160 * 1024;
     const int ct = C / 32;
     const int u = 16 / e;
-    const int lk = (C * (D / u) + 255) / 256;
-    const int lq = (GT * C * (D / u) + 255) / 256;
-    const int stage_regs = 4 * (2 * lk + lq);
+    const int lk4 = (C * (D / u) + 255) / 256;
+    const int lq4 = (GT * C * (D / u) + 255) / 256;
+    const int stage_regs = 4 * (2 * lk4 + lq4);
     // Two workgroups per CU leave 256 registers per lane: enough for the
     // 16-bit kernels up to d = 64 with at most 48 staging registers.
     const int occ_reg = (D * e <= 128 && stage_regs <= 48) ? 2 : 1;
@@ -44,7 +48,11 @@ constexpr MainShape main_shape(int e, int D, int C, int GT)
     else nsc = ct >= 2 ? ct / 2 : 1;
     const unsigned long lds = main_lds(e, D, C, GT, nsc);
     const int occ = (occ_reg == 2 && lds <= half) ? 2 : 1;
-    MainShape m{nsc, occ, lk, lq, lds <= full && lq <= 8 && ct / nsc <= 2, lds};
+    const int nw = (occ == 1 && e == 2) ? 8 : 4;
+    const int th = 64 * nw;
+    const int lk = (C * (D / u) + th - 1) / th;
+    const int lq = (GT * C * (D / u) + th - 1) / th;
+    MainShape m{nsc, occ, nw, lk, lq, lds <= full && lq4 <= 8 && ct / nsc <= 2, lds};
     return m;
 }
 
