@@ -484,10 +484,12 @@ struct Main {
     static constexpr int NWI = NU * PARTS;           // phase-2 work items
     static constexpr int CTP = DT / PARTS;           // 32-column output tiles per item
     static constexpr int NSC = SH.nsc;
-    static constexpr int RPC = CT / NSC;
+    static constexpr bool SHIFT = SH.shift;          // copy j = state after key tile j (fp32 only)
+    static constexpr int RPC = SHIFT ? 1 : CT / NSC;
     static constexpr bool FITS = SH.fits;
     static constexpr int OCC = SH.occ;
     static_assert(SH.lk == LK && SH.lq == LQ, "staging shape");
+    static_assert(!SHIFT || (sizeof(T) == 4 && NSC == CT - 1), "shifted copies");
     static_assert(DT % PARTS == 0 && (PARTS == 1 || NWI <= NW), "phase-2 split");
     static_assert(DT % MAXST == 0 || NST <= NW, "z owner: every column-0 state tile is some wave's first");
     __device__ static int tile_of(int w, int i) { return w * MAXST + i; }
@@ -624,9 +626,11 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         // segment the state after the last published copy is needed only
         // when it is returned to the caller.
         const int kt_valid = min(CT, (N - t0 + 31) / 32);
-        const int kt_upd = (c + 1 < nch || carry_out) ? kt_valid : min(kt_valid, RPC * (NSC - 1));
+        const int kt_upd = (c + 1 < nch || carry_out) ? kt_valid
+                                                      : min(kt_valid, M::SHIFT ? CT - 1 : RPC * (NSC - 1));
 
-        // ---- phase 1: publish the state before every RPC-th key tile, absorb each tile
+        // ---- phase 1: publish the state before every RPC-th key tile (after
+        // each of tiles 0 .. CT-2 with shifted copies), absorb each tile
 #pragma unroll
         for (int i = 0; i < M::MAXST; ++i) {
             const int st = M::tile_of(w, i);
@@ -635,21 +639,23 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                 const bool zown = i == 0 && jt == 0;
                 const int row = jt * 32 + n;
                 float zs = 0.f;
+                auto publish = [&](int slot) {
+                    const Tile<T, D> sST{smST[slot]};
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        f32x4 x{S[i][4 * q4], S[i][4 * q4 + 1], S[i][4 * q4 + 2], S[i][4 * q4 + 3]};
+                        sST.write4(row, it * 32 + 8 * q4 + 4 * h, cvt4<T>(x));
+                    }
+                    if (zown && h == 0) smZ[slot][it * 32 + n] = (T)(zr + zs);
+                };
 #pragma unroll
                 for (int kt = 0; kt < CT; ++kt) {
-                    if (kt % RPC == 0 && kt < kt_valid) {
-                        const Tile<T, D> sST{smST[kt / RPC]};
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4) {
-                            f32x4 x{S[i][4 * q4], S[i][4 * q4 + 1], S[i][4 * q4 + 2], S[i][4 * q4 + 3]};
-                            sST.write4(row, it * 32 + 8 * q4 + 4 * h, cvt4<T>(x));
-                        }
-                        if (zown && h == 0) smZ[kt / RPC][it * 32 + n] = (T)(zr + zs);
-                    }
+                    if (!M::SHIFT && kt % RPC == 0 && kt < kt_valid) publish(kt / RPC);
                     if (kt < kt_upd) {
                         const float dz = tile_state_update<T, D>(S[i], zown, it, jt, kt, sK, sV, lane);
                         if (zown) zs += BF ? dz : dz + __shfl_xor(dz, 32);
                     }
+                    if (M::SHIFT && kt < CT - 1 && kt < kt_valid) publish(kt);
                 }
                 if (zown) zr += zs;
             }
@@ -666,7 +672,11 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         // Output columns ct0 .. ct0 + CTP - 1 of unit u, parked in its q rows.
         auto unit_run = [&](int u, int ct0, const v8 (&qf)[KBD]) {
             const int g = u / CT, r = u % CT;
-            const int j = r / RPC;
+            // Shifted copies: tile r >= 1 reads copy r - 1 (keys before tile r);
+            // tile 0 reads copy 0 (keys of tile 0 included) and subtracts the
+            // keys of its diagonal tile that come after the query.
+            const int j = M::SHIFT ? (r > 0 ? r - 1 : 0) : r / RPC;
+            const bool sub = M::SHIFT && r == 0;
             const bool off = r % RPC != 0;   // one unmasked key tile r-1 before the diagonal
             const int qrow = g * C + r * 32 + n;
             // Pt[key][query] = phi(K) phi(Q)^T; accumulator reg i holds key
@@ -677,11 +687,14 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
 #pragma unroll
                 for (int kq = 0; kq < KBD; ++kq) mma(Pt, sK.read8(r * 32 + n, kq * 16 + h * 8), qf[kq]);
                 // Causal mask: accumulator reg i holds key 8(i/4) + 4h + i%4 of the
-                // tile for query n; keep keys <= n.
+                // tile for query n; keep keys <= n (or, subtracting, -Pt for keys > n).
                 const int kmax = n - 4 * h;
                 float pv[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) pv[i] = (8 * (i / 4) + (i % 4) <= kmax) ? Pt[i] : 0.f;
+                for (int i = 0; i < 16; ++i) {
+                    const bool le = 8 * (i / 4) + (i % 4) <= kmax;
+                    pv[i] = sub ? (le ? 0.f : -Pt[i]) : (le ? Pt[i] : 0.f);
+                }
                 pb0 = cvt8<T>(pv);
                 pb1 = cvt8<T>(pv + 8);
             }

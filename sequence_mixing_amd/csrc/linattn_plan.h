@@ -9,7 +9,8 @@ namespace linattn {
 // dimension, C tokens per chunk, GT query heads per workgroup.  LDS holds
 // phi(K), V and phi(Q) of a chunk ((2 + GT) C D elements) plus nsc copies of
 // the transposed state (D x D) and of z (D); nsc is one copy per 32-token key
-// tile, or one per two key tiles when that keeps two workgroups on a CU.
+// tile, or one per two key tiles when that keeps two workgroups on a CU (or
+// when one per tile does not fit; fp32 then drops only the first copy).
 // Each thread stages lk + lk + lq 16-byte groups (raw K, V and q of the
 // next chunk, 4 registers each).  A workgroup has 4 waves, or 8 when it is
 // alone on its CU with 16-bit data (two waves per SIMD then hide each
@@ -20,6 +21,7 @@ struct MainShape {
     int nw;       // waves per workgroup (4 or 8)
     int lk;       // 16-byte K (and V) groups each thread stages per chunk
     int lq;       // 16-byte q groups each thread stages per chunk
+    bool shift;   // fp32 copies taken after key tiles 0 .. ct-2 instead of before 0 .. ct-1
     bool fits;    // buildable: LDS within 160 KiB, at most 8 q groups per thread of 4 waves
                   // (a register budget), at most 2 key tiles per copy
     unsigned long lds;
@@ -42,17 +44,24 @@ constexpr MainShape main_shape(int e, int D, int C, int GT)
     // 16-bit kernels up to d = 64 with at most 48 staging registers.
     const int occ_reg = (D * e <= 128 && stage_regs <= 48) ? 2 : 1;
     int nsc = ct;
+    bool shift = false;
     if (occ_reg == 2 && main_lds(e, D, C, GT, ct) <= half) nsc = ct;
     else if (occ_reg == 2 && ct >= 2 && main_lds(e, D, C, GT, ct / 2) <= half) nsc = ct / 2;
     else if (main_lds(e, D, C, GT, ct) <= full) nsc = ct;
-    else nsc = ct >= 2 ? ct / 2 : 1;
+    else if (e == 4 && ct > 2 && main_lds(e, D, C, GT, ct - 1) <= full) {
+        // fp32: the copy before key tile 0 is dropped; query tile 0 reads the
+        // copy after tile 0 and subtracts its keys later than the query
+        // (exact enough in fp32), so no tile needs an unmasked neighbour.
+        nsc = ct - 1;
+        shift = true;
+    } else nsc = ct >= 2 ? ct / 2 : 1;
     const unsigned long lds = main_lds(e, D, C, GT, nsc);
     const int occ = (occ_reg == 2 && lds <= half) ? 2 : 1;
     const int nw = (occ == 1 && e == 2) ? 8 : 4;
     const int th = 64 * nw;
     const int lk = (C * (D / u) + th - 1) / th;
     const int lq = (GT * C * (D / u) + th - 1) / th;
-    MainShape m{nsc, occ, nw, lk, lq, lds <= full && lq4 <= 8 && ct / nsc <= 2, lds};
+    MainShape m{nsc, occ, nw, lk, lq, shift, lds <= full && lq4 <= 8 && (shift || ct / nsc <= 2), lds};
     return m;
 }
 
