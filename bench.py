@@ -11,7 +11,9 @@ HIP graph (untimed) and replayed between two device synchronisations; the
 output of the replay is checked bitwise against an eager call.  The same K
 steps are also run as plain eager calls (host launch cost included) and
 once more through ``linattn_fwd_timed``, whose HIP events on the library's
-stream give each stage's duration.
+stream give each stage's duration (the chunked pass launched 10 times back
+to back inside its event pair, so that its per-launch time carries no event
+overhead).
 
 Printed: ONE JSON line.  ``value`` is tokens (B * N) per second of wall time
 over the K replayed steps (the eager rate is under ``eager``).  ``roofline``
@@ -54,17 +56,18 @@ def decode_bytes(B, H, Hkv, d, dtype) -> int:
     return B * Hkv * (2 * d * d * 4 + 2 * d * 4) + e * d * (2 * B * H + 2 * B * Hkv)
 
 
-def roofline(nbytes, flops, seconds, dtype, kernel):
+def roofline(nbytes, flops, seconds, dtype, kernel, traffic=None):
+    """traffic: measured HBM bytes per launch (PMC, calibrated) or None."""
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = flops / MFMA_PEAK[dtype]
     if t_hbm >= t_mfma:
         ach = nbytes / seconds / 1e9
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel}
     ach = flops / seconds / 1e12
     peak = MFMA_PEAK[dtype] / 1e12
     return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(ach / peak, 4), "traffic": None, "kernel": kernel}
+            "frac": round(ach / peak, 4), "traffic": traffic, "kernel": kernel}
 
 
 class Hip:
@@ -91,6 +94,38 @@ class Hip:
         assert self.lib.hipEventRecord(e, stream) == 0
 
 
+SOURCES = ["sequence_mixing_amd/csrc/linattn.hip", "sequence_mixing_amd/csrc/linattn_plan.h",
+           "sequence_mixing_amd/csrc/linattn_plan.cpp"]
+
+
+def measured_traffic(workload: str, key_prefix: str):
+    """HBM bytes per launch of a kernel from the committed PMC summary of this workload.
+
+    The summaries (profiles/traffic_*.txt) record the SHA-256 of the kernel
+    sources they were taken on; after any change to those sources the figure is
+    stale and None is returned."""
+    import glob
+
+    from sequence_mixing_amd.profsum import sources_sha256
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        sha = sources_sha256([os.path.join(root, f) for f in SOURCES])
+    except OSError:
+        return None
+    for path in glob.glob(os.path.join(root, "profiles", "traffic_*.txt")):
+        for line in open(path):
+            if not line.startswith("json: "):
+                continue
+            rec = json.loads(line[6:])
+            if rec.get("workload") != workload or rec.get("sources_sha256") != sha:
+                continue
+            hits = [v for k, v in rec["bytes_per_launch"].items() if k.startswith(key_prefix)]
+            if len(hits) == 1:
+                return hits[0]
+    return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -105,13 +140,16 @@ def fwd_args(la, w, q, k, v, out, ws, ws_bytes, causal, chunk):
     return (q, k, v, out, w.B, w.H, w.Hkv, w.N, w.d, causal, 1, dt, None, None, chunk, ws, ws_bytes)
 
 
-def time_stages(la, hip, torch, args, steps, warmup, stream, flush=None):
-    """Steps through linattn_fwd_timed: HIP events on the library's stream around each stage."""
+def time_stages(la, hip, torch, args, steps, warmup, stream, flush=None, reps=1):
+    """Steps through linattn_fwd_timed: HIP events on the library's stream around each stage.
+
+    The last stage (the chunked pass) runs `reps` times back to back inside its
+    event pair and is reported per launch."""
     evs = [[hip.event() for _ in range(4)] for _ in range(steps)]
     warm = [hip.event() for _ in range(4)]
 
     def call(ev):
-        rc = la.linattn_fwd_timed(*args, stream, events=ev)
+        rc = la.linattn_fwd_timed(*args, stream, events=ev, reps=reps)
         if rc != 0:
             raise la.LinattnError(rc, "linattn_fwd_timed")
 
@@ -123,7 +161,7 @@ def time_stages(la, hip, torch, args, steps, warmup, stream, flush=None):
             flush()
         call(evs[i])
     torch.cuda.synchronize()
-    st = [[hip.ms(e[j], e[j + 1]) for j in range(3)] for e in evs]
+    st = [[hip.ms(e[0], e[1]), hip.ms(e[1], e[2]), hip.ms(e[2], e[3]) / reps] for e in evs]
     mean = [sum(s[j] for s in st) / steps for j in range(3)]
     return {"stage_ms": mean, "step_event_ms": sum(sum(s) for s in st) / steps}
 
@@ -180,7 +218,7 @@ def time_graph(la, hip, torch, args, out, steps):
     return {"event_ms": hip.ms(e0, e1) / steps, "ms": wall * 1e3 / steps, "matches_eager": same}
 
 
-def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, cold):
+def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, cold, tag=""):
     """One workload measured; returns a summary dict."""
     from linattn_inputs import workload_qkv
     from sequence_mixing_amd import ops
@@ -194,7 +232,7 @@ def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, cold):
     args = fwd_args(la, w, q, k, v, out, ws, ws_bytes, causal, chunk)
     eager_s = time_eager(la, torch, args, steps, warmup, stream)
     gr = time_graph(la, hip, torch, args, out, steps)
-    r = time_stages(la, hip, torch, args, steps, warmup, stream)
+    r = time_stages(la, hip, torch, args, steps, warmup, stream, reps=10)
     nb, fl = fwd_bytes(w), fwd_flops(w)
     k3 = r["stage_ms"][2] / 1e3
     row = {
@@ -205,7 +243,8 @@ def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, cold):
         "eager": {"ms_per_step": round(eager_s * 1e3, 5), "tokens_per_s": round(w.B * w.N / eager_s, 1)},
         "stage_us": {"seg_totals": round(r["stage_ms"][0] * 1e3, 2), "seg_scan": round(r["stage_ms"][1] * 1e3, 2),
                      "main": round(r["stage_ms"][2] * 1e3, 2)},
-        "roofline_main": roofline(nb, fl, k3, w.dtype, kernel_name(w, c, causal)),
+        "roofline_main": roofline(nb, fl, k3, w.dtype, kernel_name(w, c, causal),
+                                  measured_traffic(tag, kernel_name(w, c, causal)[:-1] + ",") if causal else None),
         "roofline_path": roofline(nb, fl, gr["event_ms"] / 1e3, w.dtype, "whole step (graph replay, events)"),
     }
     if cold:
@@ -289,7 +328,8 @@ def decode_row(la, hip, torch, steps_total, stream):
         "tokens_per_s": round(dw.B * steps_total / wall, 1),
         "graph_matches_eager": same,
         "eager_us_per_step": round(eager_us, 2),
-        "roofline": roofline(nb, fl, k_us / 1e6, "bf16", "k_decode_step<bf16,128> (graph replay, per step)"),
+        "roofline": roofline(nb, fl, k_us / 1e6, "bf16", "k_decode_step<bf16,128> (graph replay, per step)",
+                             measured_traffic("decode", "k_decode_step<bf16,128>")),
         "note": "state (32 MiB fp32) fits the 256 MiB memory-side cache; it is read and written every step",
     }
     del S, z, qs, ks, vs, out, g
@@ -347,7 +387,7 @@ def main():
     w = WORKLOADS[args.workload]
     log(f"workload {args.workload}: {w.name}; steps {args.steps}, warmup {args.warmup}")
 
-    head = fwd_row(la, hip, torch, w, 1, args.chunk, args.steps, args.warmup, stream, cold=True)
+    head = fwd_row(la, hip, torch, w, 1, args.chunk, args.steps, args.warmup, stream, cold=True, tag=args.workload)
     log("headline", json.dumps(head))
     rows = {}
     if args.rows:

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 1
+#define LINATTN_ABI_VERSION 2
 
 enum { LINATTN_F32 = 0, LINATTN_BF16 = 1 };
 
@@ -94,20 +94,25 @@ int linattn_fwd(const void *q, const void *k, const void *v, void *out,
 
 /*
  * linattn_fwd_timed - linattn_fwd with stage timing for profilers and
- * benchmarks.  Identical work and results; in addition it records
- * events[0] on `stream` before the first stage, events[1] before the second,
- * events[2] before the third and events[3] after the last.  The stages are:
+ * benchmarks.  Identical results; in addition it records events[0] on
+ * `stream` before the first stage, events[1] before the second, events[2]
+ * before the third and events[3] after the last.  The stages are:
  *   causal:     segment totals, segment prefix scan, chunked main pass;
  *   non-causal: segment totals, sum of the totals, application to the queries.
  * A stage the plan does not need is skipped (its two events coincide).
+ * The last stage reads only the inputs and the workspace, so it is launched
+ * `reps` (>= 1) times back to back between events[2] and events[3], with
+ * the same result: (events[3] - events[2]) / reps is then its duration per
+ * launch without the cost of recording an event around every launch.
  * `events` points to n_events == 4 events created by the caller
- * (hipEventCreate); otherwise LINATTN_ERR_NULL is returned.
+ * (hipEventCreate); otherwise LINATTN_ERR_NULL is returned.  reps < 1 is
+ * LINATTN_ERR_SHAPE.
  */
 int linattn_fwd_timed(const void *q, const void *k, const void *v, void *out,
                       int B, int H, int Hkv, int N, int d, int causal, int normalise, int dtype,
                       float *state_out, float *z_out, int chunk,
                       void *workspace, size_t workspace_bytes, hipStream_t stream,
-                      hipEvent_t *events, int n_events);
+                      hipEvent_t *events, int n_events, int reps);
 
 /*
  * linattn_fwd_workspace_bytes - scratch size linattn_fwd needs for these

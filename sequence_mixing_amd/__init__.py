@@ -56,7 +56,7 @@ def load():
         lib.linattn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i, vp, sz, vp]
         lib.linattn_fwd_timed.restype = i
         lib.linattn_fwd_timed.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i, vp, sz, vp,
-                                          ctypes.POINTER(vp), i]
+                                          ctypes.POINTER(vp), i, i]
         lib.linattn_fwd_workspace_bytes.restype = sz
         lib.linattn_fwd_workspace_bytes.argtypes = [i] * 8
         lib.linattn_fwd_plan.restype = i
@@ -99,12 +99,12 @@ def linattn_fwd(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_o
 
 
 def linattn_fwd_timed(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_out=None, z_out=None,
-                      chunk=0, workspace=None, workspace_bytes=0, stream=None, events=()) -> int:
+                      chunk=0, workspace=None, workspace_bytes=0, stream=None, events=(), reps=1) -> int:
     """C ``linattn_fwd_timed``; ``events`` are 4 raw hipEvent_t handles (ints)."""
     arr = (ctypes.c_void_p * len(events))(*events) if events else None
     return load().linattn_fwd_timed(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, N, d, int(causal),
                                     int(normalise), dtype, _ptr(state_out), _ptr(z_out), chunk, _ptr(workspace),
-                                    workspace_bytes, _stream(stream), arr, len(events))
+                                    workspace_bytes, _stream(stream), arr, len(events), reps)
 
 
 def linattn_fwd_workspace_bytes(B, H, Hkv, N, d, causal, dtype, chunk=0) -> int:

@@ -1027,15 +1027,20 @@ int launch_status()
     return hipGetLastError() == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
 }
 
-// ev (nullable): 4 events recorded before each of the three stages and after the last.
-int record(hipEvent_t *ev, int i, hipStream_t st)
+// Stage timing (nullable): 4 events recorded before each of the three stages
+// and after the last; the last stage is launched `reps` times in between.
+struct Timing {
+    hipEvent_t *ev;
+    int reps;
+};
+int record(const Timing *t, int i, hipStream_t st)
 {
-    return (ev && hipEventRecord(ev[i], st) != hipSuccess) ? LINATTN_ERR_HIP : LINATTN_OK;
+    return (t && hipEventRecord(t->ev[i], st) != hipSuccess) ? LINATTN_ERR_HIP : LINATTN_OK;
 }
 
 template <typename T, int D, int C>
 int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out, float *state_out,
-            float *z_out, float *ws, int normalise, hipStream_t st, hipEvent_t *ev)
+            float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev)
 {
     // Totals pass: chunks of at most 128 tokens and 64 KiB of double-buffered
     // K/V (enough bytes in flight per workgroup to stream at full bandwidth).
@@ -1058,7 +1063,7 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
                                P - 1, D, 0, (float *)nullptr, (float *)nullptr);
         if (record(ev, 2, st)) return LINATTN_ERR_HIP;
         const dim3 grid(pl.nseq * (pl.G / pl.gt) * P);
-        switch (pl.gt) {
+        for (int rep = 0; rep < (ev ? ev->reps : 1); ++rep) switch (pl.gt) {
 #define LINATTN_MAIN(GT)                                                                                            \
     case GT:                                                                                                       \
         if constexpr (Main<T, D, C, GT>::FITS) {                                                                   \
@@ -1084,8 +1089,9 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
                            D, 1, state_out, z_out);
         if (record(ev, 2, st)) return LINATTN_ERR_HIP;
         const int nblk = (pl.N + 127) / 128;
-        hipLaunchKernelGGL((k_noncausal_apply<T, D>), dim3(pl.nseq * nblk), dim3(kThreads), 0, st, qq, oo,
-                           (const float *)ws, P, pl.H, pl.Hkv, pl.N, pl.G, nblk, normalise);
+        for (int rep = 0; rep < (ev ? ev->reps : 1); ++rep)
+            hipLaunchKernelGGL((k_noncausal_apply<T, D>), dim3(pl.nseq * nblk), dim3(kThreads), 0, st, qq, oo,
+                               (const float *)ws, P, pl.H, pl.Hkv, pl.N, pl.G, nblk, normalise);
     }
     if (record(ev, 3, st)) return LINATTN_ERR_HIP;
     return launch_status();
@@ -1099,7 +1105,7 @@ constexpr bool chunk_ok()
 
 template <typename T, int D>
 int dispatch_chunk(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,
-                   float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, hipEvent_t *ev)
+                   float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev)
 {
     switch (pl.chunk) {
     case 32:
@@ -1120,7 +1126,7 @@ int dispatch_chunk(const linattn::Plan &pl, const void *q, const void *k, const 
 
 template <typename T>
 int dispatch_d(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,
-               float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, hipEvent_t *ev)
+               float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev)
 {
     switch (pl.d) {
     case 32: return dispatch_chunk<T, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
@@ -1197,7 +1203,7 @@ size_t linattn_fwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int caus
 namespace {
 int fwd_impl(const void *q, const void *k, const void *v, void *out, int B, int H, int Hkv, int N, int d, int causal,
              int normalise, int dtype, float *state_out, float *z_out, int chunk, void *workspace,
-             size_t workspace_bytes, hipStream_t stream, hipEvent_t *ev)
+             size_t workspace_bytes, hipStream_t stream, const Timing *ev)
 {
     linattn::Plan pl;
     const int rc = linattn::make_plan(B, H, Hkv, N, d, causal, dtype, chunk, &pl);
@@ -1234,20 +1240,23 @@ int linattn_fwd(const void *q, const void *k, const void *v, void *out, int B, i
 
 int linattn_fwd_timed(const void *q, const void *k, const void *v, void *out, int B, int H, int Hkv, int N, int d,
                       int causal, int normalise, int dtype, float *state_out, float *z_out, int chunk,
-                      void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events, int n_events)
+                      void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events, int n_events,
+                      int reps)
 {
     if (!events || n_events != 4) return LINATTN_ERR_NULL;
     for (int i = 0; i < 4; ++i)
         if (!events[i]) return LINATTN_ERR_NULL;
+    if (reps < 1) return LINATTN_ERR_SHAPE;
+    const Timing t{events, reps};
     if (B > 0 && N > 0)
         return fwd_impl(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_out, z_out, chunk,
-                        workspace, workspace_bytes, stream, events);
+                        workspace, workspace_bytes, stream, &t);
     // Nothing to stage: every event marks the same point.
     const int rc = fwd_impl(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_out, z_out, chunk,
                             workspace, workspace_bytes, stream, nullptr);
     if (rc != LINATTN_OK) return rc;
     for (int i = 0; i < 4; ++i)
-        if (record(events, i, stream)) return LINATTN_ERR_HIP;
+        if (record(&t, i, stream)) return LINATTN_ERR_HIP;
     return LINATTN_OK;
 }
 

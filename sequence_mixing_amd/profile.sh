@@ -1,0 +1,52 @@
+#!/bin/bash
+# Regenerates the rocprofv3 summaries kept under profiles/ (run from the
+# repository root on a machine with the GPU; raw output goes to $1).
+#
+#   bash sequence_mixing_amd/profile.sh <raw-output-dir>
+#
+# 1. kernel trace + stats of the default bench run (every workload row) and
+#    of the headline workload alone;
+# 2. FETCH_SIZE then WRITE_SIZE (one counter per run) for the headline
+#    workload's kernels and for the decode kernel, and the same two counters
+#    for a plain 256 MiB copy, which calibrates them into bytes.
+# The summaries are written next to the raw output as *.txt.
+set -euo pipefail
+OUT=${1:?raw output directory}
+mkdir -p "$OUT"
+export TMPDIR=${TMPDIR:-/tmp}
+SRC="sequence_mixing_amd/csrc/linattn.hip sequence_mixing_amd/csrc/linattn_plan.h sequence_mixing_amd/csrc/linattn_plan.cpp"
+KR="k_causal_chunks|k_seg_totals|k_seg_scan|k_noncausal_apply"
+
+step() { echo "== $*"; }
+
+step "trace: default bench"
+C1="rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace_all -o run -- python3 bench.py --cpu-seconds 2"
+timeout -k 10 600 $C1 > "$OUT/trace_all.json" 2> "$OUT/trace_all.err"
+step "trace: headline workload"
+C2="rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace_cfg2 -o run -- python3 bench.py --rows 0 --cpu-seconds 0"
+timeout -k 10 300 $C2 > "$OUT/trace_cfg2.json" 2> "$OUT/trace_cfg2.err"
+for ctr in FETCH_SIZE WRITE_SIZE; do
+    step "$ctr: headline workload"
+    timeout -s KILL 200 rocprofv3 --pmc $ctr --kernel-include-regex "$KR" -f csv -d $OUT/${ctr}_cfg2 -o run -- \
+        python3 bench.py --rows 0 --steps 5 --warmup 2 --cpu-seconds 0 > "$OUT/${ctr}_cfg2.out" 2>&1
+    step "$ctr: decode"
+    timeout -s KILL 300 rocprofv3 --pmc $ctr --kernel-include-regex "k_decode_step" -f csv -d $OUT/${ctr}_decode -o run -- \
+        python3 bench.py --rows 1 --steps 5 --warmup 2 --cpu-seconds 0 > "$OUT/${ctr}_decode.out" 2>&1
+    step "$ctr: copy calibration"
+    timeout -s KILL 90 rocprofv3 --pmc $ctr -f csv -d $OUT/${ctr}_copy -o run -- \
+        python3 -m sequence_mixing_amd.calib_copy 256 > "$OUT/${ctr}_copy.out" 2>&1
+done
+
+PMC="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --kernel-include-regex '<kernels>' -f csv -- python3 bench.py --steps 5 --warmup 2 --cpu-seconds 0 (--rows 0 headline, --rows 1 decode); calibration: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 -m sequence_mixing_amd.calib_copy 256"
+python3 -m sequence_mixing_amd.profsum "$OUT/trace_all/run_kernel_stats.csv" "$C1" \
+    "all kernels of the default bench run (every workload row; bench JSON in the same run)" > "$OUT/kernels_all_workloads.txt"
+python3 -m sequence_mixing_amd.profsum "$OUT/trace_cfg2/run_kernel_stats.csv" "$C2" \
+    "headline workload: causal fp32 B2 H8 N4096 d64 (k_causal_chunks<float,64,128,1> dominant)" > "$OUT/k_causal_chunks_f32_B2H8N4096d64.txt"
+python3 -m sequence_mixing_amd.profsum traffic cfg2 "$OUT/FETCH_SIZE_cfg2/run_counter_collection.csv" \
+    "$OUT/WRITE_SIZE_cfg2/run_counter_collection.csv" "$OUT/FETCH_SIZE_copy/run_counter_collection.csv" \
+    "$OUT/WRITE_SIZE_copy/run_counter_collection.csv" 256 "$PMC" $SRC > "$OUT/traffic_cfg2_f32_B2H8N4096d64.txt"
+python3 -m sequence_mixing_amd.profsum traffic decode "$OUT/FETCH_SIZE_decode/run_counter_collection.csv" \
+    "$OUT/WRITE_SIZE_decode/run_counter_collection.csv" "$OUT/FETCH_SIZE_copy/run_counter_collection.csv" \
+    "$OUT/WRITE_SIZE_copy/run_counter_collection.csv" 256 "$PMC" $SRC > "$OUT/traffic_decode_bf16_B64H32Hkv8d128.txt"
+grep -h "^headline\|^cfg" "$OUT/trace_all.err" > "$OUT/bench_rows_under_trace.txt" || true
+step "done"

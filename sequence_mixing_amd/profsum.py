@@ -1,6 +1,13 @@
-"""Format a rocprofv3 ``--stats`` kernel summary (``*_kernel_stats.csv``) as a short text table.
+"""Short text summaries of rocprofv3 output.
 
-    python -m sequence_mixing_amd.profsum <kernel_stats.csv> "<command that produced it>" [title]
+    python -m sequence_mixing_amd.profsum <kernel_stats.csv> "<command>" [title]
+        a ``--kernel-trace --stats`` kernel table.
+    python -m sequence_mixing_amd.profsum traffic <workload> <fetch.csv> <write.csv> <copy_fetch.csv> \
+            <copy_write.csv> <copy_MiB> "<commands>" <source files...>
+        HBM bytes per launch of every kernel in a ``--pmc FETCH_SIZE`` and a
+        ``--pmc WRITE_SIZE`` run, each counter scaled by what it reads for a
+        plain copy of known size, plus a machine-readable line keyed by the
+        SHA-256 of the kernel sources (a later source change voids it).
 """
 from __future__ import annotations
 
@@ -13,12 +20,77 @@ def summarize(path: str, command: str, title: str = "") -> str:
     lines = [f"# {title}" if title else "# rocprofv3 kernel summary", "", f"command: {command}", "",
              f"{'kernel':<72} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'total%':>7}"]
     for r in rows:
-        name = r["Name"].replace("(anonymous namespace)::", "")
-        name = name.split("(")[0] if not name.startswith("void at::") else name[:60]
+        name = r["Name"]
+        name = kernel_key(name) if ("::k_" in name or name.startswith("_ZN12_GLOBAL")) else name[:60]
         lines.append(f"{name[:72]:<72} {int(r['Calls']):>6} {float(r['AverageNs'])/1e3:>9.2f} "
                      f"{float(r['MinNs'])/1e3:>9.2f} {float(r['MaxNs'])/1e3:>9.2f} {float(r['Percentage']):>7.2f}")
     return "\n".join(lines) + "\n"
 
 
+def kernel_key(name: str) -> str:
+    """'k_causal_chunks<float,64,128,1>' from a demangled or an Itanium-mangled kernel name."""
+    import re
+
+    if "::k_" in name:
+        return name.split("::", 1)[1].split("(")[0].replace(" ", "")
+    m = re.match(r"_ZN12_GLOBAL__N_1\d+(k_\w+?)I(.*?)EEv", name)
+    if not m:
+        return name.split("(")[0][:72]
+    args, rest = [], m.group(2)
+    for tok in re.findall(r"DF16b|Li-?\d+E|f|d|i", rest):
+        args.append({"DF16b": "bf16", "f": "float", "d": "double", "i": "int"}.get(tok, tok[2:-1]))
+    return f"{m.group(1)}<{','.join(args)}>"
+
+
+def _per_dispatch(path: str, counter: str) -> dict:
+    """Mean counter value (KiB) per dispatch, by kernel name."""
+    tot, n = {}, {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        k = r["Kernel_Name"]
+        tot[k] = tot.get(k, 0.0) + float(r["Counter_Value"])
+        n.setdefault(k, set()).add(r["Dispatch_Id"])
+    return {k: tot[k] / len(n[k]) for k in tot}
+
+
+def sources_sha256(files) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def traffic(workload, fetch, write, cfetch, cwrite, copy_mib, commands, sources) -> str:
+    import json
+
+    f, w = _per_dispatch(fetch, "FETCH_SIZE"), _per_dispatch(write, "WRITE_SIZE")
+    cf, cw = _per_dispatch(cfetch, "FETCH_SIZE"), _per_dispatch(cwrite, "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+    # the copy kernel is the one whose reading is largest in the calibration run
+    ff = copy_kib / max(cf.values())
+    fw = copy_kib / max(cw.values())
+    lines = [f"# HBM traffic per launch, workload {workload} (rocprofv3 PMC, calibrated)", "",
+             f"commands: {commands}", "",
+             f"calibration: a plain copy of {copy_mib} MiB reads {max(cf.values()):.0f} KiB FETCH_SIZE and "
+             f"{max(cw.values()):.0f} KiB WRITE_SIZE per launch: factors {ff:.3f} (fetch) and {fw:.3f} (write)", "",
+             f"{'kernel':<72} {'fetch_MB':>10} {'write_MB':>10} {'total_MB':>10}"]
+    table = {}
+    for k in sorted(set(f) & set(w)):
+        rb, wb = f[k] * ff * 1024.0, w[k] * fw * 1024.0
+        short = kernel_key(k)
+        lines.append(f"{short:<72} {rb / 1e6:>10.2f} {wb / 1e6:>10.2f} {(rb + wb) / 1e6:>10.2f}")
+        table[short] = round(rb + wb)
+    lines += ["", "json: " + json.dumps({"workload": workload, "sources_sha256": sources_sha256(sources),
+                                         "bytes_per_launch": table})]
+    return "\n".join(lines) + "\n"
+
+
 if __name__ == "__main__":
-    print(summarize(sys.argv[1], sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""), end="")
+    if sys.argv[1] == "traffic":
+        a = sys.argv[2:]
+        print(traffic(a[0], a[1], a[2], a[3], a[4], float(a[5]), a[6], a[7:]), end="")
+    else:
+        print(summarize(sys.argv[1], sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""), end="")

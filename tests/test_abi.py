@@ -47,7 +47,10 @@ def test_header_compiles_as_c():
 
 
 def test_version_and_status_strings():
-    assert la.linattn_abi_version() == 1
+    import re
+
+    declared = int(re.search(r"#define LINATTN_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert la.linattn_abi_version() == declared
     for code in [0, -1, -2, -3, -4, -5, -6, -7]:
         assert la.linattn_status_string(code) and la.linattn_status_string(code) != "unknown status"
     assert la.linattn_status_string(12345) == "unknown status"

@@ -298,3 +298,29 @@ def test_last_causal_row_equals_noncausal():
     n = ops.fwd(gpu(q), gpu(k), gpu(v), causal=False)
     torch.cuda.synchronize()
     assert rows_rel_err(host(c[:, :, -1]), host(n[:, :, -1])) <= 1e-4
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_timed_entry_point_with_repeats_matches_plain_call(causal):
+    """linattn_fwd_timed (last stage launched 3 times) leaves exactly the output of linattn_fwd."""
+    B, H, Hkv, N, d = 2, 8, 2, 900, 64
+    q, k, v = (t.contiguous().cuda() for t in make_qkv(B, H, Hkv, N, d, "bf16", 333))
+    ref, S_ref, z_ref = ops.fwd(q, k, v, causal=causal, want_state=True)
+    out = torch.empty_like(q)
+    S = torch.empty_like(S_ref)
+    z = torch.empty_like(z_ref)
+    ws = ops.workspace(B, H, Hkv, N, d, causal, q.dtype)
+    nbytes = ws.numel() * 4 if ws is not None else 0
+    hip = __import__("ctypes").CDLL("libamdhip64.so")
+    evs = []
+    for _ in range(4):
+        e = __import__("ctypes").c_void_p()
+        assert hip.hipEventCreate(__import__("ctypes").byref(e)) == 0
+        evs.append(e.value)
+    rc = la.linattn_fwd_timed(q, k, v, out, B, H, Hkv, N, d, causal, 1, la.LINATTN_BF16, S, z, 0, ws, nbytes,
+                              None, events=evs, reps=3)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and torch.equal(S, S_ref) and torch.equal(z, z_ref)
+    assert la.linattn_fwd_timed(q, k, v, out, B, H, Hkv, N, d, causal, 1, la.LINATTN_BF16, S, z, 0, ws, nbytes,
+                                None, events=evs, reps=0) == -2
