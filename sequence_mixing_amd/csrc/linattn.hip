@@ -629,6 +629,20 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         const int kt_upd = (c + 1 < nch || carry_out) ? kt_valid
                                                       : min(kt_valid, M::SHIFT ? CT - 1 : RPC * (NSC - 1));
 
+        // ---- with output columns split over waves (one item per wave), the
+        // item's phi(q) fragments are read now: the barrier after phase 1
+        // then orders every such read before any part parks output there.
+        const int u_split = w / M::PARTS;
+        const bool has_split = M::PARTS > 1 && w < M::NWI && t0 + (u_split % CT) * 32 < N;
+        v8 qf_split[KBD];
+        if constexpr (M::PARTS > 1) {
+            if (has_split) {
+                const int qrow = (u_split / CT) * C + (u_split % CT) * 32 + n;
+#pragma unroll
+                for (int kq = 0; kq < KBD; ++kq) qf_split[kq] = sQ.read8(qrow, kq * 16 + h * 8);
+            }
+        }
+
         // ---- phase 1: publish the state before every RPC-th key tile (after
         // each of tiles 0 .. CT-2 with shifted copies), absorb each tile
 #pragma unroll
@@ -764,14 +778,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                 unit_run(u, 0, qf);
             }
         } else {
-            // One item per wave: every part reads the unit's phi(q) before
-            // any part parks output columns in those rows.
-            const int u = w / M::PARTS;
-            const bool has = w < M::NWI && t0 + (u % CT) * 32 < N;
-            v8 qf[KBD];
-            if (has) unit_qf(u, qf);
-            lds_barrier();
-            if (has) unit_run(u, (w % M::PARTS) * M::CTP, qf);
+            if (has_split) unit_run(u_split, (w % M::PARTS) * M::CTP, qf_split);
         }
         lds_barrier();
 
