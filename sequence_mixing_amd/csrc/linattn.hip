@@ -1045,14 +1045,51 @@ int record(const Timing *t, int i, hipStream_t st)
     return (t && hipEventRecord(t->ev[i], st) != hipSuccess) ? LINATTN_ERR_HIP : LINATTN_OK;
 }
 
+// Totals pass with chunks of c1 tokens (32, 64 or 128; at most 16 KiB of K per
+// chunk, so that two chunks of K and V double-buffer in 64 KiB of LDS).
+template <typename T, int D>
+int launch_totals(int c1, unsigned nblocks, hipStream_t st, const T *k, const T *v, float *ws, int N, int seg_len,
+                  int nslots)
+{
+    constexpr int cap = 65536 / (4 * D * (int)sizeof(T));
+    switch (c1) {
+    case 32:
+        hipLaunchKernelGGL((k_seg_totals<T, D, 32>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len, nslots);
+        return LINATTN_OK;
+    case 64:
+        if constexpr (64 <= cap) {
+            hipLaunchKernelGGL((k_seg_totals<T, D, 64>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len,
+                               nslots);
+            return LINATTN_OK;
+        }
+        break;
+    case 128:
+        if constexpr (128 <= cap) {
+            hipLaunchKernelGGL((k_seg_totals<T, D, 128>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len,
+                               nslots);
+            return LINATTN_OK;
+        }
+        break;
+    }
+    return LINATTN_ERR_UNSUPPORTED;
+}
+
+template <typename T, int D>
+int totals_chunk(int seg_len)
+{
+    constexpr int cap = 65536 / (4 * D * (int)sizeof(T));
+    int c1 = cap < 128 ? cap : 128;
+    while (c1 > 32 && seg_len % c1 != 0) c1 /= 2;  // segments are whole chunks of the pass
+    return c1;
+}
+
 template <typename T, int D, int C>
 int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out, float *state_out,
             float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev)
 {
-    // Totals pass: chunks of at most 128 tokens and 64 KiB of double-buffered
-    // K/V (enough bytes in flight per workgroup to stream at full bandwidth).
-    constexpr int C1a = 65536 / (4 * D * (int)sizeof(T));
-    constexpr int C1 = C < C1a ? (C < 128 ? C : 128) : (C1a < 128 ? C1a : 128);
+    // Totals pass: its own chunk size, the largest that divides the segments
+    // (up to 128 tokens), independent of the main pass's chunk.
+    const int c1 = totals_chunk<T, D>(pl.seg_len);
     const T *qq = static_cast<const T *>(q);
     const T *kk = static_cast<const T *>(k);
     const T *vv = static_cast<const T *>(v);
@@ -1061,9 +1098,8 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
     const int E = D * D + D;
     if (record(ev, 0, st)) return LINATTN_ERR_HIP;
     if (pl.causal) {
-        if (P > 1)
-            hipLaunchKernelGGL((k_seg_totals<T, D, C1>), dim3(pl.nseq * (P - 1)), dim3(kThreads), 0, st, kk, vv, ws,
-                               pl.N, pl.seg_len, P - 1);
+        if (P > 1 && launch_totals<T, D>(c1, pl.nseq * (P - 1), st, kk, vv, ws, pl.N, pl.seg_len, P - 1))
+            return LINATTN_ERR_UNSUPPORTED;
         if (record(ev, 1, st)) return LINATTN_ERR_HIP;
         if (P > 2)
             hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, ws,
@@ -1089,8 +1125,7 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
         default: return LINATTN_ERR_UNSUPPORTED;
         }
     } else {
-        hipLaunchKernelGGL((k_seg_totals<T, D, C1>), dim3(pl.nseq * P), dim3(kThreads), 0, st, kk, vv, ws, pl.N,
-                           pl.seg_len, P);
+        if (launch_totals<T, D>(c1, pl.nseq * P, st, kk, vv, ws, pl.N, pl.seg_len, P)) return LINATTN_ERR_UNSUPPORTED;
         if (record(ev, 1, st)) return LINATTN_ERR_HIP;
         hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, ws, P,
                            D, 1, state_out, z_out);
