@@ -28,10 +28,13 @@ int auto_chunk(int dtype, int d, int G, int causal)
     (void)causal;
     // Prefer the most query heads per workgroup (K and V are then read once
     // per head block), then about 128 query rows per chunk, which gives the
-    // four waves one 32-row query tile each.
+    // four waves one 32-row query tile each; fp32 prefers 64-token chunks,
+    // whose tiles leave room for eight waves.
+    const bool f32 = dtype == LINATTN_F32;
     for (int gt = 8; gt >= 1; gt /= 2) {
         if (G % gt != 0) continue;
-        const int pref[4] = {128 / gt >= 32 ? 128 / gt : 32, 64, 32, 128};
+        const int rows = 128 / gt >= 32 ? 128 / gt : 32;  // about 128 query rows, at least one tile
+        const int pref[4] = {f32 ? 64 : rows, f32 ? rows : 64, 32, 128};
         for (int i = 0; i < 4; ++i) {
             const int c = pref[i];
             if (heads_per_block(dtype, d, c, G) == gt) return c;

@@ -13,8 +13,9 @@ namespace linattn {
 // when one per tile does not fit; fp32 then drops only the first copy).
 // Each thread stages lk + lk + lq 16-byte groups (raw K, V and q of the
 // next chunk, 4 registers each).  A workgroup has 4 waves, or 8 when it is
-// alone on its CU with 16-bit data (two waves per SIMD then hide each
-// other's waits; fp32 keeps 4 since its scores would be recomputed).
+// alone on its CU (two waves per SIMD then hide each other's waits) and the
+// data are 16-bit or the fp32 tiles are small enough (d <= 64, d * C <= 4096)
+// for two waves' registers.
 struct MainShape {
     int nsc;      // state copies per chunk
     int occ;      // workgroups per CU the kernel is built for (1 or 2)
@@ -35,6 +36,7 @@ constexpr unsigned long main_lds(int e, int D, int C, int GT, int nsc)
 constexpr MainShape main_shape(int e, int D, int C, int GT)
 {
     const unsigned long half = 80 * 1024, full = 160 * 1024;
+    if (C < 32 || D < 32) return MainShape{1, 1, 4, 1, 1, false, false, 0};  // not a kernel shape
     const int ct = C / 32;
     const int u = 16 / e;
     const int lk4 = (C * (D / u) + 255) / 256;
@@ -57,7 +59,7 @@ constexpr MainShape main_shape(int e, int D, int C, int GT)
     } else nsc = ct >= 2 ? ct / 2 : 1;
     const unsigned long lds = main_lds(e, D, C, GT, nsc);
     const int occ = (occ_reg == 2 && lds <= half) ? 2 : 1;
-    const int nw = (occ == 1 && e == 2) ? 8 : 4;
+    const int nw = (occ == 1 && (e == 2 || (D <= 64 && D * C <= 4096))) ? 8 : 4;
     const int th = 64 * nw;
     const int lk = (C * (D / u) + th - 1) / th;
     const int lq = (GT * C * (D / u) + th - 1) / th;

@@ -140,3 +140,12 @@ def test_auto_chunk_choices():
         assert c in (32, 64, 128, 256)
         # the automatic choice is always one the explicit argument accepts
         assert la.linattn_fwd_plan(*args, c)[0] == 0
+    # every group size, head dimension and dtype (planning runs on the host:
+    # a bad automatic choice would show up here, not on the GPU)
+    for dt in (F32, BF16):
+        for d in (32, 64, 128):
+            for G in (1, 2, 3, 4, 5, 6, 8, 12, 16, 32):
+                for causal in (0, 1):
+                    rc, c, P = la.linattn_fwd_plan(2, 2 * G, 2, 1000, d, causal, dt, 0)
+                    assert rc == 0 and c in (32, 64, 128, 256), (dt, d, G, causal, rc, c)
+                    assert la.linattn_fwd_workspace_bytes(2, 2 * G, 2, 1000, d, causal, dt) >= 0
