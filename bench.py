@@ -357,6 +357,54 @@ def cpu_baseline(w, seconds):
                       f"{threads} threads over (batch, kv head, 16-column block)"}
 
 
+def row_oracle(w, causal, seconds, max_tokens=2048):
+    """The fp64 oracle on a bounded sample of a workload: the first `max_tokens`
+    tokens of every (batch, kv head) sequence with all their query heads.  The
+    recurrence's cost per token does not depend on how many came before, so
+    tokens/s of the sample is the whole workload's rate."""
+    import numpy as np
+
+    import oracle
+    from linattn_inputs import workload_qkv
+
+    n = min(w.N, max_tokens)
+    q, k, v = (np.ascontiguousarray(t[:, :, :n].double().numpy()) for t in workload_qkv(w))
+    threads = oracle.default_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.ref_fwd(q, k, v, causal=bool(causal), normalise=True, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    return {"value": round(w.B * n * reps / el, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {w.N} tokens of all {w.B * w.Hkv} sequences ({w.H} query heads), "
+                      f"{reps} reps in {el:.1f} s"}
+
+
+def decode_oracle(seconds):
+    """The fp64 oracle's decode step at batch 64 (state from zero: the cost does not depend on it)."""
+    import numpy as np
+
+    import oracle
+    from linattn_inputs import DECODE, DecodeStream
+
+    dw = DECODE
+    S = np.zeros((dw.B, dw.Hkv, dw.d, dw.d))
+    z = np.zeros((dw.B, dw.Hkv, dw.d))
+    gen = DecodeStream(dw.B, dw.H, dw.Hkv, dw.d, dw.dtype, dw.seed)
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        qs, ks, vs = gen.next()
+        oracle.ref_decode_step(S, z, qs, ks, vs, normalise=True)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or steps >= 1024:
+            break
+    return {"value": round(dw.B * steps / el, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} decode steps at batch {dw.B} in {el:.1f} s (single thread)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -393,12 +441,18 @@ def main():
     if args.rows:
         if args.workload == "cfg2":
             rows["cfg2_noncausal"] = fwd_row(la, hip, torch, w, 0, args.chunk, 20, 5, stream, cold=True)
+            if args.cpu_seconds > 0:
+                rows["cfg2_noncausal"]["cpu_oracle"] = row_oracle(w, 0, min(2.0, args.cpu_seconds))
             log("cfg2_noncausal", json.dumps(rows["cfg2_noncausal"]))
         for name, chunk in (("cfg3", 0), ("cfg4_c64", 64), ("cfg4_c128", 128), ("cfg4_c256", 256), ("cfg5_prefill", 0)):
             key = name.split("_")[0] if name != "cfg5_prefill" else "cfg5"
             rows[name] = fwd_row(la, hip, torch, WORKLOADS[key], 1, chunk, 20, 5, stream, cold=True)
+            if args.cpu_seconds > 0 and name != "cfg4_c64" and name != "cfg4_c256":
+                rows[name]["cpu_oracle"] = row_oracle(WORKLOADS[key], 1, min(2.0, args.cpu_seconds))
             log(name, json.dumps(rows[name]))
         rows["cfg5_decode"] = decode_row(la, hip, torch, 1024, stream)
+        if args.cpu_seconds > 0:
+            rows["cfg5_decode"]["cpu_oracle"] = decode_oracle(min(2.0, args.cpu_seconds))
         log("cfg5_decode", json.dumps(rows["cfg5_decode"]))
 
     cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None

@@ -53,6 +53,8 @@ def _load():
         lib.linattn_ref_phi.argtypes = [ctypes.c_double]
         lib.linattn_ref_fwd.restype = ctypes.c_int
         lib.linattn_ref_fwd.argtypes = [dp, dp, dp, dp] + [ctypes.c_int] * 7 + [dp, dp, ctypes.c_int]
+        lib.linattn_ref_fwd_from.restype = ctypes.c_int
+        lib.linattn_ref_fwd_from.argtypes = [dp, dp, dp, dp] + [ctypes.c_int] * 7 + [dp, dp, dp, dp, ctypes.c_int]
         lib.linattn_ref_decode_step.restype = ctypes.c_int
         lib.linattn_ref_decode_step.argtypes = [dp] * 6 + [ctypes.c_int] * 5
         _lib = lib
@@ -87,23 +89,29 @@ def phi(x: float) -> float:
 
 
 def ref_fwd(q, k, v, causal: bool = True, normalise: bool = True,
-            want_state: bool = False, nthreads: int | None = None):
+            want_state: bool = False, nthreads: int | None = None, state_in=None, z_in=None):
     """Forward pass.  q [B,H,N,d], k/v [B,Hkv,N,d] -> out [B,H,N,d] (fp64).
 
     With ``want_state`` also returns S_N [B,Hkv,d,d] and z_N [B,Hkv,d].
+    ``state_in`` [B,Hkv,d,d] / ``z_in`` [B,Hkv,d] (optional): the sums of
+    earlier tokens that S and z start from (zero when omitted).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = q.shape
     Hkv = k.shape[1]
     assert k.shape == (B, Hkv, N, d) and v.shape == (B, Hkv, N, d)
+    Si = None if state_in is None else _f64(state_in)
+    zi = None if z_in is None else _f64(z_in)
+    assert Si is None or Si.shape == (B, Hkv, d, d)
+    assert zi is None or zi.shape == (B, Hkv, d)
     out = np.zeros((B, H, N, d), dtype=np.float64)
     S = np.zeros((B, Hkv, d, d), dtype=np.float64) if want_state else None
     z = np.zeros((B, Hkv, d), dtype=np.float64) if want_state else None
-    rc = _load().linattn_ref_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, N, d,
-                                 int(bool(causal)), int(bool(normalise)), _ptr(S), _ptr(z),
-                                 nthreads or default_threads())
+    rc = _load().linattn_ref_fwd_from(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, N, d,
+                                      int(bool(causal)), int(bool(normalise)), _ptr(Si), _ptr(zi),
+                                      _ptr(S), _ptr(z), nthreads or default_threads())
     if rc != 0:
-        raise ValueError(f"linattn_ref_fwd rejected its arguments (rc={rc})")
+        raise ValueError(f"linattn_ref_fwd_from rejected its arguments (rc={rc})")
     return (out, S, z) if want_state else out
 
 

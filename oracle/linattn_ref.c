@@ -27,6 +27,9 @@
  *     head h reads key/value head floor(h / (H / Hkv)).
  *   - decode: one token appended to a carried (S, z); the state is updated
  *     first and then read, so the new token sees itself (s <= t).
+ *   - continuation (README "Features", the KV-cache-reuse item: a prompt's
+ *     state carried into later tokens): the same forward pass with S and z
+ *     starting from given sums of earlier tokens instead of zero.
  *
  * Readings where the pages are silent: no 1/sqrt(d) scale, no epsilon in the
  * denominator, d_k = d_v = d, layouts q/out [B][H][N][d], k/v [B][Hkv][N][d],
@@ -52,6 +55,7 @@ double linattn_ref_phi(double x)
 
 typedef struct {
     const double *q, *k, *v;
+    const double *state_in, *z_in; /* starting sums, or NULL for zero */
     double *out, *state_out, *z_out;
     int B, H, Hkv, N, d, causal, normalise;
     int nitems, nthreads, tid;
@@ -69,6 +73,15 @@ static void fwd_item(const fwd_job *J, int item)
 
     double *S = calloc((size_t)d * w, sizeof(double)); /* S[i][jj] */
     double *z = calloc((size_t)d, sizeof(double));
+    if (J->state_in) {
+        const double *si = J->state_in + ((size_t)b * J->Hkv + g) * (size_t)d * d;
+        for (int i = 0; i < d; ++i)
+            for (int jj = 0; jj < w; ++jj) S[(size_t)i * w + jj] = si[(size_t)i * d + j0 + jj];
+    }
+    if (J->z_in) {
+        const double *zi = J->z_in + ((size_t)b * J->Hkv + g) * (size_t)d;
+        for (int i = 0; i < d; ++i) z[i] = zi[i];
+    }
     double *f = malloc((size_t)d * sizeof(double));
     double *p = malloc((size_t)d * sizeof(double));
 
@@ -132,13 +145,15 @@ static void *fwd_worker(void *arg)
 }
 
 /*
- * Forward pass.  All arrays are contiguous fp64 host arrays in the layouts
- * given above.  state_out / z_out may be NULL.  Returns 0, or -1 on invalid
- * arguments (nothing is written then).
+ * Forward pass continuing from state_in [B][Hkv][d][d] and z_in [B][Hkv][d]
+ * (either may be NULL for zero).  All arrays are contiguous fp64 host arrays
+ * in the layouts given above.  state_out / z_out may be NULL.  Returns 0, or
+ * -1 on invalid arguments (nothing is written then).
  */
-int linattn_ref_fwd(const double *q, const double *k, const double *v, double *out,
-                    int B, int H, int Hkv, int N, int d, int causal, int normalise,
-                    double *state_out, double *z_out, int nthreads)
+int linattn_ref_fwd_from(const double *q, const double *k, const double *v, double *out,
+                         int B, int H, int Hkv, int N, int d, int causal, int normalise,
+                         const double *state_in, const double *z_in,
+                         double *state_out, double *z_out, int nthreads)
 {
     if (!q || !k || !v || !out) return -1;
     if (B < 0 || H <= 0 || Hkv <= 0 || N < 0 || d <= 0 || H % Hkv != 0) return -1;
@@ -151,7 +166,7 @@ int linattn_ref_fwd(const double *q, const double *k, const double *v, double *o
     fwd_job *jobs = malloc((size_t)nthreads * sizeof(fwd_job));
     pthread_t *th = malloc((size_t)nthreads * sizeof(pthread_t));
     for (int t = 0; t < nthreads; ++t) {
-        fwd_job J = {q, k, v, out, state_out, z_out, B, H, Hkv, N, d, causal, normalise,
+        fwd_job J = {q, k, v, state_in, z_in, out, state_out, z_out, B, H, Hkv, N, d, causal, normalise,
                      nitems, nthreads, t};
         jobs[t] = J;
     }
@@ -161,6 +176,15 @@ int linattn_ref_fwd(const double *q, const double *k, const double *v, double *o
     free(jobs);
     free(th);
     return 0;
+}
+
+/* Forward pass from zero sums (see linattn_ref_fwd_from). */
+int linattn_ref_fwd(const double *q, const double *k, const double *v, double *out,
+                    int B, int H, int Hkv, int N, int d, int causal, int normalise,
+                    double *state_out, double *z_out, int nthreads)
+{
+    return linattn_ref_fwd_from(q, k, v, out, B, H, Hkv, N, d, causal, normalise, NULL, NULL, state_out, z_out,
+                                nthreads);
 }
 
 /*

@@ -336,3 +336,53 @@ def test_empty_sequence():
     q, k, v = make_qkv(1, 2, 2, 0, 4, "f32", 1)
     out, S, z = oracle.ref_fwd(q, k, v, want_state=True)
     assert out.shape == (1, 2, 0, 4) and not S.any() and not z.any()
+
+
+
+# ------------------------------------------------------------- continuation
+
+@settings(max_examples=25, deadline=None)
+@given(shapes, st.booleans(), st.booleans(), st.floats(0.0, 1.0))
+def test_continuation_from_state_equals_one_pass(shape, causal, normalise, frac):
+    """Split a sequence anywhere: the second part run from the first part's
+    (S, z) reproduces the one-pass rows, state and normaliser (the plain
+    oracle being pinned above, this pins the continuation against it)."""
+    B, (H, Hkv), N, d, seed = shape
+    q, k, v = make_qkv(B, H, Hkv, N, d, "f32", seed)
+    n1 = int(round(frac * N))
+    whole, S, z = oracle.ref_fwd(q, k, v, causal=causal, normalise=normalise, want_state=True, nthreads=2)
+    _, S1, z1 = oracle.ref_fwd(q[:, :, :n1], k[:, :, :n1], v[:, :, :n1], causal=True, want_state=True, nthreads=2)
+    o2, S2, z2 = oracle.ref_fwd(q[:, :, n1:], k[:, :, n1:], v[:, :, n1:], causal=causal, normalise=normalise,
+                                want_state=True, nthreads=2, state_in=S1, z_in=z1)
+    # The continuation performs the same additions in the same order as the
+    # one-pass run, so the match is exact.
+    assert np.array_equal(o2, whole[:, :, n1:])
+    assert np.array_equal(S2, S) and np.array_equal(z2, z)
+
+
+def test_continuation_from_zero_state_is_the_plain_pass():
+    q, k, v = make_qkv(2, 4, 2, 37, 8, "f32", 5)
+    Hkv, d = 2, 8
+    plain = oracle.ref_fwd(q, k, v)
+    from_zero = oracle.ref_fwd(q, k, v, state_in=np.zeros((2, Hkv, d, d)), z_in=np.zeros((2, Hkv, d)))
+    assert np.array_equal(plain, from_zero)
+
+
+def test_continuation_closed_form_constant_keys():
+    """K = 0 (phi(k) = 1) after a start state (S0, z0): o_t = (phi(q_t)^T S0 + sum_{s<=t} v_s (phi(q_t).1))
+    / (phi(q_t) . z0 + t |phi(q_t)|_1)."""
+    rng = np.random.default_rng(11)
+    B, H, N, d = 1, 1, 9, 4
+    q = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    k = np.zeros((B, H, N, d))
+    S0 = rng.random((B, H, d, d))
+    z0 = rng.random((B, H, d)) + 0.5
+    got = oracle.ref_fwd(q, k, v, state_in=S0, z_in=z0)
+    fq = phi_lib(q[0, 0])
+    cs = np.cumsum(v[0, 0], axis=0)
+    for t in range(N):
+        l1 = fq[t].sum()
+        num = fq[t] @ S0[0, 0] + cs[t] * l1
+        den = fq[t] @ z0[0, 0] + (t + 1) * l1
+        assert np.allclose(got[0, 0, t], num / den, rtol=1e-13, atol=0)

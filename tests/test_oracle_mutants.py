@@ -76,6 +76,10 @@ MUTANTS = {
         "for (int t = 0; t < N - 1; ++t) {\n            for (int i = 0; i < d; ++i) f[i] = linattn_ref_phi(kb"),
     "decode_skips_z_update": lambda s: s.replace("if (zz) zz[i] += f[i];", ""),
     "decode_reads_before_update": _decode_reads_before_update,
+    "continuation_ignores_z_in": lambda s: s.replace("for (int i = 0; i < d; ++i) z[i] = zi[i];",
+                                                     "for (int i = 0; i < d; ++i) z[i] = 0.0 * zi[i];"),
+    "continuation_state_in_transposed": lambda s: s.replace(
+        "S[(size_t)i * w + jj] = si[(size_t)i * d + j0 + jj];", "S[(size_t)i * w + jj] = si[(size_t)(j0 + jj) * d + i];"),
 }
 
 
