@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 2
+#define LINATTN_ABI_VERSION 3
 
 enum { LINATTN_F32 = 0, LINATTN_BF16 = 1 };
 
@@ -91,6 +91,31 @@ int linattn_fwd(const void *q, const void *k, const void *v, void *out,
                 int B, int H, int Hkv, int N, int d, int causal, int normalise, int dtype,
                 float *state_out, float *z_out, int chunk,
                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * linattn_fwd_from_state - linattn_fwd for sequences that continue earlier
+ * tokens (README "Features", the KV-cache-reuse item: a prompt's state
+ * carried into the tokens that follow it; chunked prefill).  The running
+ * sums start from the given ones instead of zero:
+ *   S_t = state_in + sum_{s<=t} phi(k_s) v_s^T,  z_t = z_in + sum_{s<=t} phi(k_s)
+ * (non-causal: the sums over all N keys are added to them).  Running a
+ * sequence in pieces, each from the previous piece's state_out / z_out,
+ * gives the rows of one call over the whole sequence (up to the order of
+ * summation).
+ *
+ *   state_in    device fp32 [B][Hkv][d][d], required; read only.
+ *   z_in        device fp32 [B][Hkv][d]; read only.  NULL means zero and is
+ *               allowed only when normalise == 0.
+ * All other arguments, the workspace size (linattn_fwd_workspace_bytes with
+ * the same arguments) and the error behaviour are those of linattn_fwd;
+ * state_out / z_out may alias neither state_in nor z_in.  With N == 0,
+ * state_out / z_out receive copies of state_in / z_in.
+ */
+int linattn_fwd_from_state(const void *q, const void *k, const void *v, void *out,
+                           int B, int H, int Hkv, int N, int d, int causal, int normalise, int dtype,
+                           const float *state_in, const float *z_in,
+                           float *state_out, float *z_out, int chunk,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * linattn_fwd_timed - linattn_fwd with stage timing for profilers and

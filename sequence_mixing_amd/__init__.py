@@ -16,7 +16,7 @@ import os
 
 __all__ = [
     "LINATTN_F32", "LINATTN_BF16", "LINATTN_OK", "LinattnError", "library_path", "load",
-    "linattn_fwd", "linattn_fwd_timed", "linattn_fwd_workspace_bytes", "linattn_fwd_plan", "linattn_decode_step",
+    "linattn_fwd", "linattn_fwd_from_state", "linattn_fwd_timed", "linattn_fwd_workspace_bytes", "linattn_fwd_plan", "linattn_decode_step",
     "linattn_status_string", "linattn_abi_version",
 ]
 
@@ -54,6 +54,8 @@ def load():
         vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         lib.linattn_fwd.restype = i
         lib.linattn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i, vp, sz, vp]
+        lib.linattn_fwd_from_state.restype = i
+        lib.linattn_fwd_from_state.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp, vp, i, vp, sz, vp]
         lib.linattn_fwd_timed.restype = i
         lib.linattn_fwd_timed.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i, vp, sz, vp,
                                           ctypes.POINTER(vp), i, i]
@@ -96,6 +98,15 @@ def linattn_fwd(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_o
     return load().linattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, N, d, int(causal),
                               int(normalise), dtype, _ptr(state_out), _ptr(z_out), chunk, _ptr(workspace),
                               workspace_bytes, _stream(stream))
+
+
+def linattn_fwd_from_state(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_in, z_in,
+                           state_out=None, z_out=None, chunk=0, workspace=None, workspace_bytes=0,
+                           stream=None) -> int:
+    """C ``linattn_fwd_from_state``; returns the status code (0 = ok)."""
+    return load().linattn_fwd_from_state(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, N, d, int(causal),
+                                         int(normalise), dtype, _ptr(state_in), _ptr(z_in), _ptr(state_out),
+                                         _ptr(z_out), chunk, _ptr(workspace), workspace_bytes, _stream(stream))
 
 
 def linattn_fwd_timed(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_out=None, z_out=None,

@@ -414,16 +414,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
 //
 // ws holds nslots partials of E = D*D + D floats per sequence.  mode 0:
 // inclusive prefix along the slots, in place.  mode 1: the sum, written to
-// slot 0 and, when given, to state_out / z_out.
+// slot 0 and, when given, to state_out / z_out.  Both start from s_in / z_in
+// (the sums of earlier tokens) when given.
 __global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, int nslots, int D, int mode,
-                                                       float *__restrict__ state_out, float *__restrict__ z_out)
+                                                       float *__restrict__ state_out, float *__restrict__ z_out,
+                                                       const float *__restrict__ s_in, const float *__restrict__ z_in)
 {
     const int E = D * D + D;
     const int seq = blockIdx.y;
     const int e = blockIdx.x * kThreads + threadIdx.x;
     if (e >= E) return;
     float *base = ws + (size_t)seq * nslots * E + e;
+    // the sums start from the given ones (continuation), else from zero
     float acc = 0.f;
+    if (e < D * D) {
+        if (s_in) acc = s_in[(size_t)seq * D * D + e];
+    } else if (z_in) {
+        acc = z_in[(size_t)seq * D + (e - D * D)];
+    }
     // Batches of independent loads, then the running sum over the batch.
     constexpr int BATCH = 32;
     for (int p0 = 0; p0 < nslots; p0 += BATCH) {
@@ -499,7 +507,8 @@ template <typename T, int D, int C, int GT>
 __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) void k_causal_chunks(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ out,
     const float *__restrict__ ws, float *__restrict__ state_out, float *__restrict__ z_out,
-    int H, int Hkv, int N, int G, int P, int seg_len, int normalise)
+    int H, int Hkv, int N, int G, int P, int seg_len, int normalise, const float *__restrict__ s_in,
+    const float *__restrict__ z_in)
 {
     using M = Main<T, D, C, GT>;
     using v8 = typename Vt<T>::v8;
@@ -530,16 +539,23 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
     // ---- the state this segment starts from (state tile i of wave w is w*MAXST + i)
     f32x16 S[M::MAXST];
     float zr = 0.f;
-    const float *init = p > 0 ? ws + ((size_t)seq * (P - 1) + (p - 1)) * (size_t)D * (D + 1) : nullptr;
+    // segment p > 0: the scanned sums in slot p - 1; segment 0: the start
+    // sums of a continuation, or zero
+    const float *init = p > 0 ? ws + ((size_t)seq * (P - 1) + (p - 1)) * (size_t)D * (D + 1)
+                              : (s_in ? s_in + (size_t)seq * D * D : nullptr);
+    const float *initz = p > 0 ? init + (size_t)D * D : (z_in ? z_in + (size_t)seq * D : nullptr);
 #pragma unroll
     for (int i = 0; i < M::MAXST; ++i) {
         S[i] = f32x16{};
         const int st = M::tile_of(w, i);
-        if (st < M::NST && init) {
+        if (st < M::NST) {
             const int it = st / DT, jt = st % DT;
+            if (init) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) S[i][r] = init[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n];
-            if (i == 0 && jt == 0) zr = init[(size_t)D * D + it * 32 + n];
+                for (int r = 0; r < 16; ++r)
+                    S[i][r] = init[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n];
+            }
+            if (initz && i == 0 && jt == 0) zr = initz[it * 32 + n];
         }
     }
     // ---- staging: raw K, V, q of a chunk in registers, one chunk ahead
@@ -1022,9 +1038,12 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
     }
 }
 
-__global__ void k_fill_zero(float *__restrict__ p, size_t n)
+// p[i] = src ? src[i] : 0 (a kernel rather than a memset node, so that the
+// call can be captured in a graph).
+__global__ void k_fill_copy(float *__restrict__ p, const float *__restrict__ src, size_t n)
 {
-    for (size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kThreads) p[i] = 0.f;
+    for (size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kThreads)
+        p[i] = src ? src[i] : 0.f;
 }
 
 // -------------------------------------------------------------- launchers
@@ -1033,6 +1052,12 @@ int launch_status()
 {
     return hipGetLastError() == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
 }
+
+// Sums of earlier tokens a forward pass continues from (both nullable).
+struct Start {
+    const float *S;
+    const float *z;
+};
 
 // Stage timing (nullable): 4 events recorded before each of the three stages
 // and after the last; the last stage is launched `reps` times in between.
@@ -1085,7 +1110,7 @@ int totals_chunk(int seg_len)
 
 template <typename T, int D, int C>
 int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out, float *state_out,
-            float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev)
+            float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev, const Start &s0)
 {
     // Totals pass: its own chunk size, the largest that divides the segments
     // (up to 128 tokens), independent of the main pass's chunk.
@@ -1101,9 +1126,10 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
         if (P > 1 && launch_totals<T, D>(c1, pl.nseq * (P - 1), st, kk, vv, ws, pl.N, pl.seg_len, P - 1))
             return LINATTN_ERR_UNSUPPORTED;
         if (record(ev, 1, st)) return LINATTN_ERR_HIP;
-        if (P > 2)
+        // the scan also adds the start sums of a continuation into every slot
+        if (P > 2 || (P == 2 && (s0.S || s0.z)))
             hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, ws,
-                               P - 1, D, 0, (float *)nullptr, (float *)nullptr);
+                               P - 1, D, 0, (float *)nullptr, (float *)nullptr, s0.S, s0.z);
         if (record(ev, 2, st)) return LINATTN_ERR_HIP;
         const dim3 grid(pl.nseq * (pl.G / pl.gt) * P);
         for (int rep = 0; rep < (ev ? ev->reps : 1); ++rep) switch (pl.gt) {
@@ -1112,7 +1138,7 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
         if constexpr (Main<T, D, C, GT>::FITS) {                                                                   \
             hipLaunchKernelGGL((k_causal_chunks<T, D, C, GT>), grid, dim3(Main<T, D, C, GT>::TH), 0, st, qq, kk,   \
                                vv, oo, (const float *)ws, state_out, z_out, pl.H, pl.Hkv, pl.N, pl.G, P,           \
-                               pl.seg_len, normalise);                                                             \
+                               pl.seg_len, normalise, s0.S, s0.z);                                                 \
             break;                                                                                                 \
         } else {                                                                                                   \
             return LINATTN_ERR_UNSUPPORTED;                                                                        \
@@ -1128,7 +1154,7 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
         if (launch_totals<T, D>(c1, pl.nseq * P, st, kk, vv, ws, pl.N, pl.seg_len, P)) return LINATTN_ERR_UNSUPPORTED;
         if (record(ev, 1, st)) return LINATTN_ERR_HIP;
         hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, ws, P,
-                           D, 1, state_out, z_out);
+                           D, 1, state_out, z_out, s0.S, s0.z);
         if (record(ev, 2, st)) return LINATTN_ERR_HIP;
         const int nblk = (pl.N + 127) / 128;
         for (int rep = 0; rep < (ev ? ev->reps : 1); ++rep)
@@ -1147,20 +1173,21 @@ constexpr bool chunk_ok()
 
 template <typename T, int D>
 int dispatch_chunk(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,
-                   float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev)
+                   float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev,
+                   const Start &s0)
 {
     switch (pl.chunk) {
     case 32:
-        if constexpr (chunk_ok<T, D, 32>()) return run_fwd<T, D, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
+        if constexpr (chunk_ok<T, D, 32>()) return run_fwd<T, D, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
         break;
     case 64:
-        if constexpr (chunk_ok<T, D, 64>()) return run_fwd<T, D, 64>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
+        if constexpr (chunk_ok<T, D, 64>()) return run_fwd<T, D, 64>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
         break;
     case 128:
-        if constexpr (chunk_ok<T, D, 128>()) return run_fwd<T, D, 128>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
+        if constexpr (chunk_ok<T, D, 128>()) return run_fwd<T, D, 128>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
         break;
     case 256:
-        if constexpr (chunk_ok<T, D, 256>()) return run_fwd<T, D, 256>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
+        if constexpr (chunk_ok<T, D, 256>()) return run_fwd<T, D, 256>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
         break;
     }
     return LINATTN_ERR_UNSUPPORTED;
@@ -1168,12 +1195,13 @@ int dispatch_chunk(const linattn::Plan &pl, const void *q, const void *k, const 
 
 template <typename T>
 int dispatch_d(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,
-               float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev)
+               float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev,
+               const Start &s0)
 {
     switch (pl.d) {
-    case 32: return dispatch_chunk<T, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
-    case 64: return dispatch_chunk<T, 64>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
-    case 128: return dispatch_chunk<T, 128>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev);
+    case 32: return dispatch_chunk<T, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+    case 64: return dispatch_chunk<T, 64>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+    case 128: return dispatch_chunk<T, 128>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
     }
     return LINATTN_ERR_UNSUPPORTED;
 }
@@ -1245,7 +1273,7 @@ size_t linattn_fwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int caus
 namespace {
 int fwd_impl(const void *q, const void *k, const void *v, void *out, int B, int H, int Hkv, int N, int d, int causal,
              int normalise, int dtype, float *state_out, float *z_out, int chunk, void *workspace,
-             size_t workspace_bytes, hipStream_t stream, const Timing *ev)
+             size_t workspace_bytes, hipStream_t stream, const Timing *ev, const Start &s0 = Start{nullptr, nullptr})
 {
     linattn::Plan pl;
     const int rc = linattn::make_plan(B, H, Hkv, N, d, causal, dtype, chunk, &pl);
@@ -1257,16 +1285,17 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, int B, int 
         return LINATTN_ERR_ALIGN;
     if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LINATTN_ERR_WORKSPACE;
     if (N == 0) {
-        // No keys: the state and normaliser are zero; there is no output row.
+        // No keys: the state and normaliser are the start sums (zero unless
+        // continuing); there is no output row.
         if (state_out)
-            hipLaunchKernelGGL(k_fill_zero, dim3(256), dim3(kThreads), 0, stream, state_out, (size_t)pl.nseq * d * d);
-        if (z_out) hipLaunchKernelGGL(k_fill_zero, dim3(16), dim3(kThreads), 0, stream, z_out, (size_t)pl.nseq * d);
+            hipLaunchKernelGGL(k_fill_copy, dim3(256), dim3(kThreads), 0, stream, state_out, s0.S, (size_t)pl.nseq * d * d);
+        if (z_out) hipLaunchKernelGGL(k_fill_copy, dim3(16), dim3(kThreads), 0, stream, z_out, s0.z, (size_t)pl.nseq * d);
         return launch_status();
     }
     float *ws = static_cast<float *>(workspace);
     if (dtype == LINATTN_BF16)
-        return dispatch_d<bf16>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream, ev);
-    return dispatch_d<float>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream, ev);
+        return dispatch_d<bf16>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream, ev, s0);
+    return dispatch_d<float>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream, ev, s0);
 }
 }  // namespace
 
@@ -1278,6 +1307,18 @@ int linattn_fwd(const void *q, const void *k, const void *v, void *out, int B, i
 {
     return fwd_impl(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_out, z_out, chunk, workspace,
                     workspace_bytes, stream, nullptr);
+}
+
+int linattn_fwd_from_state(const void *q, const void *k, const void *v, void *out, int B, int H, int Hkv, int N,
+                           int d, int causal, int normalise, int dtype, const float *state_in, const float *z_in,
+                           float *state_out, float *z_out, int chunk, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream)
+{
+    if (B > 0 && (!state_in || (normalise && !z_in))) return LINATTN_ERR_NULL;
+    if ((state_out && (const float *)state_out == state_in) || (z_out && z_in && (const float *)z_out == z_in))
+        return LINATTN_ERR_SHAPE;  // the start sums are read while the final ones are written
+    return fwd_impl(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_out, z_out, chunk, workspace,
+                    workspace_bytes, stream, nullptr, Start{state_in, z_in});
 }
 
 int linattn_fwd_timed(const void *q, const void *k, const void *v, void *out, int B, int H, int Hkv, int N, int d,

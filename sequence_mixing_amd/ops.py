@@ -6,7 +6,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (LINATTN_BF16, LINATTN_F32, LinattnError, linattn_decode_step, linattn_fwd,
+from . import (LINATTN_BF16, LINATTN_F32, LinattnError, linattn_decode_step, linattn_fwd, linattn_fwd_from_state,
                linattn_fwd_workspace_bytes)
 
 _DT = {torch.float32: LINATTN_F32, torch.bfloat16: LINATTN_BF16}
@@ -26,8 +26,9 @@ def workspace(B, H, Hkv, N, d, causal, dtype: torch.dtype, chunk=0, device="cuda
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=True, normalise=True, chunk=0,
-        want_state=False, out=None, ws=None, stream=None):
-    """O = phi(Q)(phi(K)^T V) through ``linattn_fwd``; q [B,H,N,d], k/v [B,Hkv,N,d] on the GPU."""
+        want_state=False, out=None, ws=None, stream=None, state_in=None, z_in=None):
+    """O = phi(Q)(phi(K)^T V) through ``linattn_fwd`` (``linattn_fwd_from_state`` when
+    ``state_in`` is given); q [B,H,N,d], k/v [B,Hkv,N,d] on the GPU."""
     B, H, N, d = q.shape
     Hkv = k.shape[1]
     for t in (q, k, v):
@@ -45,6 +46,16 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=True, normalis
     if ws is None:
         ws = workspace(B, H, Hkv, N, d, causal, q.dtype, chunk, q.device)
     nbytes = ws.numel() * 4 if ws is not None else 0
+    if state_in is not None:
+        starts = ((state_in, (B, Hkv, d, d)),) + (((z_in, (B, Hkv, d)),) if z_in is not None else ())
+        for t, shape in starts:
+            if not (t.is_cuda and t.is_contiguous() and t.dtype == torch.float32 and t.shape == shape):
+                raise ValueError("state_in / z_in must be contiguous fp32 device tensors [B,Hkv,d,d] / [B,Hkv,d]")
+        rc = linattn_fwd_from_state(q, k, v, out, B, H, Hkv, N, d, causal, normalise, code, state_in, z_in, S, z,
+                                    chunk, ws, nbytes, stream)
+        if rc != 0:
+            raise LinattnError(rc, "linattn_fwd_from_state")
+        return (out, S, z) if want_state else out
     rc = linattn_fwd(q, k, v, out, B, H, Hkv, N, d, causal, normalise, code, S, z, chunk, ws, nbytes, stream)
     if rc != 0:
         raise LinattnError(rc, "linattn_fwd")

@@ -324,3 +324,100 @@ def test_timed_entry_point_with_repeats_matches_plain_call(causal):
     assert torch.equal(out, ref) and torch.equal(S, S_ref) and torch.equal(z, z_ref)
     assert la.linattn_fwd_timed(q, k, v, out, B, H, Hkv, N, d, causal, 1, la.LINATTN_BF16, S, z, 0, ws, nbytes,
                                 None, events=evs, reps=0) == -2
+
+
+# ------------------------------------------- continuing from given start sums
+
+def start_sums(B, Hkv, d, dtype, seed, n_prefix=300):
+    """Sums of a seeded prefix of n_prefix tokens (oracle, fp64), rounded to fp32 for both sides."""
+    qp, kp, vp = make_qkv(B, Hkv, Hkv, n_prefix, d, dtype, seed)
+    _, S, z = oracle.ref_fwd(qp, kp, vp, causal=True, want_state=True)
+    return torch.from_numpy(S).float(), torch.from_numpy(z).float()
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,dtype,chunk", [
+    (1, 2, 2, 100, 64, "f32", 0),
+    (2, 4, 2, 257, 64, "bf16", 0),
+    (1, 4, 1, 333, 128, "bf16", 0),
+    (1, 8, 2, 2049, 128, "bf16", 0),
+    (3, 6, 3, 515, 64, "f32", 32),
+    (1, 2, 2, 1, 32, "f32", 0),
+    (2, 8, 8, 1000, 32, "bf16", 64),
+    (1, 16, 2, 700, 128, "bf16", 0),
+])
+@pytest.mark.parametrize("causal", [1, 0])
+@pytest.mark.parametrize("normalise", [1, 0])
+def test_continuation_matches_oracle(B, H, Hkv, N, d, dtype, chunk, causal, normalise):
+    q, k, v = make_qkv(B, H, Hkv, N, d, dtype, 71 + N)
+    S0, z0 = start_sums(B, Hkv, d, dtype, 5 + d)
+    rc, c, P = la.linattn_fwd_plan(B, H, Hkv, N, d, causal, ops.dtype_code(q.dtype), chunk)
+    print(f"continuation B{B} H{H} Hkv{Hkv} N{N} d{d} {dtype} causal={causal} norm={normalise} "
+          f"chunk={c} segments={P}", flush=True)
+    assert rc == 0
+    out, S, z = ops.fwd(gpu(q), gpu(k), gpu(v), causal=causal, normalise=normalise, chunk=chunk, want_state=True,
+                        state_in=gpu(S0), z_in=gpu(z0) if normalise else None)
+    torch.cuda.synchronize()
+    ref, Sr, zr = oracle.ref_fwd(q, k, v, causal=causal, normalise=normalise, want_state=True,
+                                 state_in=S0, z_in=z0 if normalise else None)
+    tol = TOL[dtype]
+    e = rows_rel_err(host(out), ref)
+    assert e <= tol, f"output rel err {e:.3e} > {tol}"
+    es = mat_rel_err(host(S), Sr)
+    assert es <= tol, f"state rel err {es:.3e}"
+    if normalise:
+        ez = mat_rel_err(host(z), zr)
+        assert ez <= tol, f"z rel err {ez:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_in_pieces_equals_one_pass(dtype):
+    """A sequence run in four uneven pieces, each from the last piece's sums, gives the one-pass rows."""
+    B, H, Hkv, N, d = 2, 8, 2, 3001, 128 if dtype == "bf16" else 64
+    q, k, v = (gpu(t) for t in make_qkv(B, H, Hkv, N, d, dtype, 808))
+    print(f"pieces B{B} H{H} Hkv{Hkv} N{N} d{d} {dtype}", flush=True)
+    whole, S_w, z_w = ops.fwd(q, k, v, want_state=True)
+    cuts = [0, 1, 1000, 1777, N]
+    S = torch.zeros(B, Hkv, d, d, device="cuda")
+    z = torch.zeros(B, Hkv, d, device="cuda")
+    outs = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        sl = (slice(None), slice(None), slice(a, b))
+        o, S, z = ops.fwd(q[sl].contiguous(), k[sl].contiguous(), v[sl].contiguous(), want_state=True,
+                          state_in=S, z_in=z)
+        outs.append(o)
+    torch.cuda.synchronize()
+    pieces = torch.cat(outs, dim=2)
+    tol = TOL[dtype]
+    assert rows_rel_err(host(pieces), host(whole)) <= tol
+    assert mat_rel_err(host(S), host(S_w)) <= 1e-4 and mat_rel_err(host(z), host(z_w)) <= 1e-4
+    ref = oracle.ref_fwd(*(t.cpu() for t in (q, k, v)), causal=True)
+    assert rows_rel_err(host(pieces), ref) <= tol
+
+
+def test_continuation_edge_cases():
+    B, H, Hkv, d = 1, 4, 2, 64
+    S0, z0 = start_sums(B, Hkv, d, "f32", 3)
+    S0, z0 = gpu(S0), gpu(z0)
+    # N == 0: the final sums are the start sums, bit for bit
+    q = torch.zeros(B, H, 0, d, device="cuda")
+    kv = torch.zeros(B, Hkv, 0, d, device="cuda")
+    for causal in (1, 0):
+        out, S, z = ops.fwd(q, kv, kv.clone(), causal=causal, want_state=True, state_in=S0, z_in=z0)
+        torch.cuda.synchronize()
+        assert out.shape == q.shape and torch.equal(S, S0) and torch.equal(z, z0)
+    q, k, v = (gpu(t) for t in make_qkv(B, H, Hkv, 50, d, "f32", 4))
+    out = torch.empty_like(q)
+    S, z = torch.empty_like(S0), torch.empty_like(z0)
+    ws = ops.workspace(B, H, Hkv, 50, d, 1, q.dtype)
+    nbytes = ws.numel() * 4 if ws is not None else 0
+    f32 = la.LINATTN_F32
+    call = lambda si, zi, so, zo, norm: la.linattn_fwd_from_state(q, k, v, out, B, H, Hkv, 50, d, 1, norm, f32,
+                                                                  si, zi, so, zo, 0, ws, nbytes)
+    assert call(None, z0, S, z, 1) == -1          # state_in is required
+    assert call(S0, None, S, z, 1) == -1          # z_in is required when normalising
+    assert call(S0, z0, S0, z, 1) == -2           # outputs may not alias the start sums
+    assert call(S0, z0, S, z0, 1) == -2
+    assert call(S0, None, S, z, 0) == 0           # without normalisation z starts from zero
+    torch.cuda.synchronize()
+    _, Sr, zr = oracle.ref_fwd(*(t.cpu() for t in (q, k, v)), normalise=False, want_state=True, state_in=S0.cpu())
+    assert mat_rel_err(host(S), Sr) <= 1e-4 and mat_rel_err(host(z), zr) <= 1e-4
