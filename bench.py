@@ -266,6 +266,70 @@ def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, cold, tag="
     return row
 
 
+def pieces_row(la, hip, torch, w, pieces, steps):
+    """The causal prefill of w run as `pieces` equal pieces through linattn_fwd_from_state,
+    each piece starting from the sums the previous one ended with (chunked prefill).
+
+    The whole chain (all pieces) is one step; steps are captured as one HIP graph."""
+    from linattn_inputs import workload_qkv
+    from sequence_mixing_amd import ops
+
+    q, k, v = (t.cuda() for t in workload_qkv(w))
+    n = w.N // pieces
+    assert n * pieces == w.N
+    dt = la.LINATTN_BF16 if w.dtype == "bf16" else la.LINATTN_F32
+    sl = [(slice(None), slice(None), slice(i * n, (i + 1) * n)) for i in range(pieces)]
+    qs, ks, vs = ([t[s].contiguous() for s in sl] for t in (q, k, v))
+    outs = [torch.empty_like(x) for x in qs]
+    S = [torch.zeros(w.B, w.Hkv, w.d, w.d, device="cuda") for _ in range(2)]
+    z = [torch.zeros(w.B, w.Hkv, w.d, device="cuda") for _ in range(2)]
+    S0 = torch.zeros_like(S[0])
+    z0 = torch.zeros_like(z[0])
+    ws = ops.workspace(w.B, w.H, w.Hkv, n, w.d, 1, q.dtype)
+    ws_bytes = ws.numel() * 4 if ws is not None else 0
+    _, c, P = la.linattn_fwd_plan(w.B, w.H, w.Hkv, n, w.d, 1, dt, 0)
+
+    def chain(st):
+        for i in range(pieces):
+            si, zi = (S0, z0) if i == 0 else (S[(i - 1) % 2], z[(i - 1) % 2])
+            rc = la.linattn_fwd_from_state(qs[i], ks[i], vs[i], outs[i], w.B, w.H, w.Hkv, n, w.d, 1, 1, dt, si, zi,
+                                           S[i % 2], z[i % 2], 0, ws, ws_bytes, st)
+            if rc != 0:
+                raise la.LinattnError(rc, "linattn_fwd_from_state")
+
+    chain(torch.cuda.current_stream().cuda_stream)
+    whole = ops.fwd(q, k, v)
+    torch.cuda.synchronize()
+    got = torch.cat(outs, dim=2).float()
+    ref = whole.float()
+    err = ((got - ref).abs().amax(-1) / ref.abs().amax(-1).clamp_min(1e-30)).max().item()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        chain(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream().cuda_stream
+        for _ in range(steps):
+            chain(cap)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    g.replay()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(e0, e1) / steps
+    del g
+    nb, fl = fwd_bytes(w), fwd_flops(w)
+    return {"pieces": pieces, "piece_tokens": n, "chunk": c, "segments_per_piece": P,
+            "ms_per_step": round(ms, 5), "tokens_per_s": round(w.B * w.N / (ms / 1e3), 1),
+            "max_row_rel_diff_vs_one_pass": err,
+            "roofline_path": roofline(nb, fl, ms / 1e3, w.dtype, "whole chain (graph replay, events)")}
+
+
 def decode_row(la, hip, torch, steps_total, stream):
     """GQA prefill (N=32768), state replicated into 64 slots, 1024 decode steps."""
     from linattn_inputs import DECODE, WORKLOADS, DecodeStream, workload_qkv
@@ -450,6 +514,8 @@ def main():
             if args.cpu_seconds > 0 and name != "cfg4_c64" and name != "cfg4_c256":
                 rows[name]["cpu_oracle"] = row_oracle(WORKLOADS[key], 1, min(2.0, args.cpu_seconds))
             log(name, json.dumps(rows[name]))
+        rows["cfg5_prefill_4_pieces"] = pieces_row(la, hip, torch, WORKLOADS["cfg5"], 4, 20)
+        log("cfg5_prefill_4_pieces", json.dumps(rows["cfg5_prefill_4_pieces"]))
         rows["cfg5_decode"] = decode_row(la, hip, torch, 1024, stream)
         if args.cpu_seconds > 0:
             rows["cfg5_decode"]["cpu_oracle"] = decode_oracle(min(2.0, args.cpu_seconds))

@@ -41,7 +41,7 @@ PMC="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --kernel-include-regex '<kerne
 python3 -m sequence_mixing_amd.profsum "$OUT/trace_all/run_kernel_stats.csv" "$C1" \
     "all kernels of the default bench run (every workload row; bench JSON in the same run)" > "$OUT/kernels_all_workloads.txt"
 python3 -m sequence_mixing_amd.profsum "$OUT/trace_cfg2/run_kernel_stats.csv" "$C2" \
-    "headline workload: causal fp32 B2 H8 N4096 d64 (k_causal_chunks<float,64,128,1> dominant)" > "$OUT/k_causal_chunks_f32_B2H8N4096d64.txt"
+    "headline workload: causal fp32 B2 H8 N4096 d64 (k_causal_chunks dominant)" > "$OUT/k_causal_chunks_f32_B2H8N4096d64.txt"
 python3 -m sequence_mixing_amd.profsum traffic cfg2 "$OUT/FETCH_SIZE_cfg2/run_counter_collection.csv" \
     "$OUT/WRITE_SIZE_cfg2/run_counter_collection.csv" "$OUT/FETCH_SIZE_copy/run_counter_collection.csv" \
     "$OUT/WRITE_SIZE_copy/run_counter_collection.csv" 256 "$PMC" $SRC > "$OUT/traffic_cfg2_f32_B2H8N4096d64.txt"
