@@ -9,7 +9,9 @@ double precision), this module only converts arrays and calls it.
 Definition followed (LinearTile 1.0.0 README, "How It Works"; causal form
 from its "Features" list and Katharopoulos et al. 2020 cited under its
 "Reference" section): O = phi(Q) (phi(K)^T V), phi = ELU + 1, causal rows
-see keys s <= t, optional normaliser phi(q_t) . z_t.
+see keys s <= t, optional normaliser phi(q_t) . z_t.  The backward pass is the
+chain rule on that definition, with the reverse-time walk of a running sum
+(Stream efficiency essay, section 4.2).
 """
 from __future__ import annotations
 
@@ -55,6 +57,10 @@ def _load():
         lib.linattn_ref_fwd.argtypes = [dp, dp, dp, dp] + [ctypes.c_int] * 7 + [dp, dp, ctypes.c_int]
         lib.linattn_ref_fwd_from.restype = ctypes.c_int
         lib.linattn_ref_fwd_from.argtypes = [dp, dp, dp, dp] + [ctypes.c_int] * 7 + [dp, dp, dp, dp, ctypes.c_int]
+        lib.linattn_ref_dphi.restype = ctypes.c_double
+        lib.linattn_ref_dphi.argtypes = [ctypes.c_double]
+        lib.linattn_ref_bwd.restype = ctypes.c_int
+        lib.linattn_ref_bwd.argtypes = [dp] * 8 + [ctypes.c_int] * 8
         lib.linattn_ref_decode_step.restype = ctypes.c_int
         lib.linattn_ref_decode_step.argtypes = [dp] * 6 + [ctypes.c_int] * 5
         _lib = lib
@@ -113,6 +119,28 @@ def ref_fwd(q, k, v, causal: bool = True, normalise: bool = True,
     if rc != 0:
         raise ValueError(f"linattn_ref_fwd_from rejected its arguments (rc={rc})")
     return (out, S, z) if want_state else out
+
+
+def ref_bwd(q, k, v, out, dout, causal: bool = True, normalise: bool = True, nthreads: int | None = None):
+    """Backward pass.  q/out/dout [B,H,N,d], k/v [B,Hkv,N,d] -> (dq, dk, dv) in fp64.
+
+    ``out`` is the forward output the gradient of the normaliser uses (may be
+    None when ``normalise`` is false)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    o = None if out is None else _f64(out)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, d) and v.shape == (B, Hkv, N, d) and dout.shape == q.shape
+    assert o is None or o.shape == q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    rc = _load().linattn_ref_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 B, H, Hkv, N, d, int(bool(causal)), int(bool(normalise)),
+                                 nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"linattn_ref_bwd rejected its arguments (rc={rc})")
+    return dq, dk, dv
 
 
 def ref_decode_step(S: np.ndarray, z: np.ndarray | None, q, k, v, normalise: bool = True):

@@ -30,6 +30,11 @@
  *   - continuation (README "Features", the KV-cache-reuse item: a prompt's
  *     state carried into later tokens): the same forward pass with S and z
  *     starting from given sums of earlier tokens instead of zero.
+ *   - backward (the README's project layout names a backward module and its
+ *     test without their content; the Stream efficiency essay, section 4.2,
+ *     gives the pattern of a running-sum recurrence differentiated by a
+ *     reverse-time scan): dQ, dK, dV of the forward above for a given output
+ *     gradient dO, by the chain rule, written out at linattn_ref_bwd.
  *
  * Readings where the pages are silent: no 1/sqrt(d) scale, no epsilon in the
  * denominator, d_k = d_v = d, layouts q/out [B][H][N][d], k/v [B][Hkv][N][d],
@@ -231,5 +236,179 @@ int linattn_ref_decode_step(double *state, double *z, const double *q, const dou
     }
     free(f);
     free(p);
+    return 0;
+}
+
+/* d phi / dx: 1 for x > 0, exp(x) otherwise (both sides give 1 at 0). */
+double linattn_ref_dphi(double x)
+{
+    return x > 0.0 ? 1.0 : exp(x);
+}
+
+typedef struct {
+    const double *q, *k, *v, *out, *dout;
+    double *dq, *dk, *dv;
+    int B, H, Hkv, N, d, causal, normalise;
+    int nitems, nthreads, tid;
+} bwd_job;
+
+/*
+ * One item: batch b, kv head g with its G query heads.
+ *
+ * With a_t = phi(q_t), b_s = phi(k_s) and, for the normalised output
+ * o_t = num_t / den_t (num_t = S_t^T a_t, den_t = a_t . z_t), the loss
+ * gradient dO_t enters through
+ *     g_t = dO_t / den_t              (gradient of num_t)
+ *     h_t = -(dO_t . o_t) / den_t     (gradient of den_t)
+ * (normalise == 0: g_t = dO_t, h_t = 0).  Then, with "t sees s" meaning
+ * s <= t (causal) or every pair (non-causal):
+ *     da_t = S_t g_t + h_t z_t                       (S_t, z_t as seen by t)
+ *     dv_s = sum_{t sees s} (a_t . b_s) g_t     = R_s^T b_s
+ *     db_s = sum_{t sees s} (g_t . v_s + h_t) a_t = R_s v_s + r_s
+ * where R_s = sum_{t sees s} a_t g_t^T and r_s = sum_{t sees s} h_t a_t,
+ * summed over the G query heads of the group as well.  Finally
+ * dq = da * phi'(q), dk = db * phi'(k).  The forward walk gives da (and g,
+ * h, which it keeps); a reverse walk accumulates R, r for dk and dv.
+ */
+static void bwd_item(const bwd_job *J, int item)
+{
+    const int d = J->d, N = J->N, G = J->H / J->Hkv;
+    const int b = item / J->Hkv, g = item % J->Hkv;
+    double *S = calloc((size_t)d * d, sizeof(double));
+    double *z = calloc((size_t)d, sizeof(double));
+    double *R = calloc((size_t)d * d, sizeof(double));
+    double *r = calloc((size_t)d, sizeof(double));
+    double *f = malloc((size_t)d * sizeof(double));
+    double *p = malloc((size_t)d * sizeof(double));
+    double *gs = malloc((size_t)G * N * d * sizeof(double) + 1);
+    double *hs = malloc((size_t)G * N * sizeof(double) + 1);
+
+    const double *kb = J->k + ((size_t)b * J->Hkv + g) * (size_t)N * d;
+    const double *vb = J->v + ((size_t)b * J->Hkv + g) * (size_t)N * d;
+    double *dkb = J->dk + ((size_t)b * J->Hkv + g) * (size_t)N * d;
+    double *dvb = J->dv + ((size_t)b * J->Hkv + g) * (size_t)N * d;
+#define ROW(base, hh, t) ((base) + (((size_t)b * J->H + (hh)) * N + (t)) * d)
+
+    /* absorb key t into (S, z) */
+#define ABSORB(t)                                                                                          \
+    do {                                                                                                   \
+        for (int i = 0; i < d; ++i) f[i] = linattn_ref_phi(kb[(size_t)(t) * d + i]);                     \
+        for (int i = 0; i < d; ++i) {                                                                      \
+            for (int j = 0; j < d; ++j) S[(size_t)i * d + j] += f[i] * vb[(size_t)(t) * d + j];          \
+            z[i] += f[i];                                                                                  \
+        }                                                                                                  \
+    } while (0)
+
+    if (!J->causal)
+        for (int t = 0; t < N; ++t) ABSORB(t);
+    /* forward walk: den, g, h and dq */
+    for (int t = 0; t < N; ++t) {
+        if (J->causal) ABSORB(t);
+        for (int hh = 0; hh < G; ++hh) {
+            const int h = g * G + hh;
+            const double *qt = ROW(J->q, h, t), *dot = ROW(J->dout, h, t);
+            double *gt = gs + ((size_t)hh * N + t) * d;
+            for (int i = 0; i < d; ++i) p[i] = linattn_ref_phi(qt[i]);
+            double hval = 0.0;
+            if (J->normalise) {
+                const double *ot = ROW(J->out, h, t);
+                double den = 0.0, dov = 0.0;
+                for (int i = 0; i < d; ++i) den += p[i] * z[i];
+                for (int j = 0; j < d; ++j) dov += dot[j] * ot[j];
+                for (int j = 0; j < d; ++j) gt[j] = dot[j] / den;
+                hval = -dov / den;
+            } else {
+                for (int j = 0; j < d; ++j) gt[j] = dot[j];
+            }
+            hs[(size_t)hh * N + t] = hval;
+            double *dqt = ROW(J->dq, h, t);
+            for (int i = 0; i < d; ++i) {
+                double da = hval * z[i];
+                for (int j = 0; j < d; ++j) da += S[(size_t)i * d + j] * gt[j];
+                dqt[i] = da * linattn_ref_dphi(qt[i]);
+            }
+        }
+    }
+#undef ABSORB
+
+    /* gather every query of the group into (R, r) */
+#define GATHER(t)                                                                                          \
+    do {                                                                                                   \
+        for (int hh = 0; hh < G; ++hh) {                                                                   \
+            const double *qt = ROW(J->q, g * G + hh, (t));                                                 \
+            const double *gt = gs + ((size_t)hh * N + (t)) * d;                                            \
+            const double hval = hs[(size_t)hh * N + (t)];                                                  \
+            for (int i = 0; i < d; ++i) p[i] = linattn_ref_phi(qt[i]);                                     \
+            for (int i = 0; i < d; ++i) {                                                                  \
+                for (int j = 0; j < d; ++j) R[(size_t)i * d + j] += p[i] * gt[j];                          \
+                r[i] += hval * p[i];                                                                       \
+            }                                                                                              \
+        }                                                                                                  \
+    } while (0)
+
+    if (!J->causal)
+        for (int t = 0; t < N; ++t) GATHER(t);
+    /* reverse walk: key s is seen by queries t >= s */
+    for (int s = N - 1; s >= 0; --s) {
+        if (J->causal) GATHER(s);
+        const double *ks = kb + (size_t)s * d, *vs = vb + (size_t)s * d;
+        for (int i = 0; i < d; ++i) f[i] = linattn_ref_phi(ks[i]);
+        for (int j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i) acc += R[(size_t)i * d + j] * f[i];
+            dvb[(size_t)s * d + j] = acc;
+        }
+        for (int i = 0; i < d; ++i) {
+            double acc = r[i];
+            for (int j = 0; j < d; ++j) acc += R[(size_t)i * d + j] * vs[j];
+            dkb[(size_t)s * d + i] = acc * linattn_ref_dphi(ks[i]);
+        }
+    }
+#undef GATHER
+#undef ROW
+    free(S);
+    free(z);
+    free(R);
+    free(r);
+    free(f);
+    free(p);
+    free(gs);
+    free(hs);
+}
+
+static void *bwd_worker(void *arg)
+{
+    const bwd_job *J = (const bwd_job *)arg;
+    for (int item = J->tid; item < J->nitems; item += J->nthreads) bwd_item(J, item);
+    return NULL;
+}
+
+/*
+ * Backward pass: dq [B][H][N][d], dk and dv [B][Hkv][N][d] for the output
+ * gradient dout [B][H][N][d].  out is the forward output (the normalised
+ * gradient uses dO . o); it may be NULL when normalise == 0.  Returns 0, or
+ * -1 on invalid arguments.
+ */
+int linattn_ref_bwd(const double *q, const double *k, const double *v, const double *out,
+                    const double *dout, double *dq, double *dk, double *dv,
+                    int B, int H, int Hkv, int N, int d, int causal, int normalise, int nthreads)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || (normalise && !out)) return -1;
+    if (B < 0 || H <= 0 || Hkv <= 0 || N < 0 || d <= 0 || H % Hkv != 0) return -1;
+    if (B == 0 || N == 0) return 0;
+    const int nitems = B * Hkv;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > nitems) nthreads = nitems;
+    bwd_job *jobs = malloc((size_t)nthreads * sizeof(bwd_job));
+    pthread_t *th = malloc((size_t)nthreads * sizeof(pthread_t));
+    for (int t = 0; t < nthreads; ++t) {
+        bwd_job J = {q, k, v, out, dout, dq, dk, dv, B, H, Hkv, N, d, causal, normalise, nitems, nthreads, t};
+        jobs[t] = J;
+    }
+    for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, bwd_worker, &jobs[t]);
+    bwd_worker(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+    free(jobs);
+    free(th);
     return 0;
 }

@@ -2,8 +2,9 @@
 
 Each case copies ``oracle/linattn_ref.c``, plants one plausible slip (a dropped
 term, a wrong index, an exclusive mask, a different GQA head map, a
-transposed state read, ...), compiles the copy into a temporary library and
-runs the oracle pin suite against it in a child process.  The suite must fail
+transposed state read, a flipped gradient sign, ...), compiles the copy into a
+temporary library and runs the oracle pin suites (forward and backward)
+against it in a child process.  The suite must fail
 for every mutant; a mutant that survives means the pins have a blind spot.
 The real oracle source is never modified.
 """
@@ -58,6 +59,18 @@ def _decode_reads_before_update(src: str) -> str:
     return src.replace(anchor, anchor + DECODE_UPDATE, 1)
 
 
+BWD_GATHER = "        if (J->causal) GATHER(s);\n"
+BWD_DK_STORE = """            dkb[(size_t)s * d + i] = acc * linattn_ref_dphi(ks[i]);
+        }
+"""
+
+
+def _bwd_exclusive_reverse_walk(src: str) -> str:
+    """Gather query s into (R, r) after key s is read: key s would miss query s."""
+    assert BWD_GATHER in src and BWD_DK_STORE in src
+    return src.replace(BWD_GATHER, "", 1).replace(BWD_DK_STORE, BWD_DK_STORE + BWD_GATHER, 1)
+
+
 MUTANTS = {
     "phi_drops_plus_one": lambda s: s.replace("x > 0.0 ? x + 1.0 : exp(x)", "x > 0.0 ? x : exp(x)"),
     "phi_negative_branch_is_plain_elu": lambda s: s.replace("x > 0.0 ? x + 1.0 : exp(x)",
@@ -80,6 +93,15 @@ MUTANTS = {
                                                      "for (int i = 0; i < d; ++i) z[i] = 0.0 * zi[i];"),
     "continuation_state_in_transposed": lambda s: s.replace(
         "S[(size_t)i * w + jj] = si[(size_t)i * d + j0 + jj];", "S[(size_t)i * w + jj] = si[(size_t)(j0 + jj) * d + i];"),
+    "bwd_normaliser_gradient_sign": lambda s: s.replace("hval = -dov / den;", "hval = dov / den;"),
+    "bwd_dq_drops_normaliser_term": lambda s: s.replace("double da = hval * z[i];", "double da = 0.0 * z[i];"),
+    "bwd_exclusive_reverse_walk": _bwd_exclusive_reverse_walk,
+    "bwd_dphi_branches_swapped": lambda s: s.replace("return x > 0.0 ? 1.0 : exp(x);",
+                                                     "return x > 0.0 ? exp(x) : 1.0;"),
+    "bwd_dk_drops_normaliser_sum": lambda s: s.replace("double acc = r[i];", "double acc = 0.0 * r[i];"),
+    "bwd_dv_reads_R_transposed": lambda s: s.replace("acc += R[(size_t)i * d + j] * f[i];",
+                                                     "acc += R[(size_t)j * d + i] * f[i];"),
+    "bwd_gradient_not_divided_by_denominator": lambda s: s.replace("gt[j] = dot[j] / den;", "gt[j] = dot[j];"),
 }
 
 
@@ -95,6 +117,6 @@ def test_pins_catch_mutant(name, tmp_path):
                     "-lm", "-lpthread"], check=True)
     env = dict(os.environ, LINATTN_REF_LIB=str(so_path))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                        os.path.join(ROOT, "tests", "test_oracle.py"), os.path.join(ROOT, "tests", "test_oracle_bwd.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the oracle pins:\n{r.stdout[-2000:]}"
