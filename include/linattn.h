@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 3
+#define LINATTN_ABI_VERSION 4
 
 enum { LINATTN_F32 = 0, LINATTN_BF16 = 1 };
 
@@ -185,6 +185,40 @@ const char *linattn_status_string(int status);
 
 /* LINATTN_ABI_VERSION of the built library. */
 int linattn_abi_version(void);
+
+/*
+ * linattn_bwd - gradients of linattn_fwd (the README's project layout names a
+ * backward module; the gradient is the chain rule on the "How It Works"
+ * definition, with the reverse-time walk of a running sum described in the
+ * Stream efficiency essay, section 4.2).
+ *
+ * For the output gradient dout = dL/dout of o_t = num_t / den_t (or num_t
+ * when normalise == 0), with a = phi(q), b = phi(k):
+ *     g_t = dout_t / den_t,   h_t = -(dout_t . out_t) / den_t
+ *     dq_t = (S_t g_t + h_t z_t) * phi'(q_t)
+ *     dv_s = R_s^T b_s,   dk_s = (R_s v_s + r_s) * phi'(k_s)
+ * where S_t, z_t are the forward's running sums seen by t and
+ * R_s = sum a_t g_t^T, r_s = sum h_t a_t over the queries t that see key s
+ * (t >= s causal, all t non-causal) and over the G query heads of the kv
+ * group (GQA: dk, dv are summed over the group).  phi'(x) = 1 for x > 0,
+ * exp(x) otherwise.
+ *
+ *   q, out, dout    device, dtype, [B][H][N][d]; out is the forward output
+ *                   (used for h only; may be NULL when normalise == 0).
+ *   k, v            device, dtype, [B][Hkv][N][d].
+ *   dq              device, dtype, [B][H][N][d], written.
+ *   dk, dv          device, dtype, [B][Hkv][N][d], written.
+ *   causal, normalise, dtype   as in linattn_fwd (fp32 accumulation).
+ *   workspace       device scratch of linattn_bwd_workspace_bytes() bytes,
+ *                   16-byte aligned, owned by the caller; overwritten.
+ * The outputs may not alias any input or each other.  All pointers 16-byte
+ * aligned.  Asynchronous on `stream`; argument errors are returned before
+ * any launch (LINATTN_ERR_*), launch failures as LINATTN_ERR_HIP.
+ */
+size_t linattn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int causal, int dtype);
+int linattn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                void *dq, void *dk, void *dv, int B, int H, int Hkv, int N, int d, int causal,
+                int normalise, int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

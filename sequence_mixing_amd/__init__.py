@@ -17,7 +17,7 @@ import os
 __all__ = [
     "LINATTN_F32", "LINATTN_BF16", "LINATTN_OK", "LinattnError", "library_path", "load",
     "linattn_fwd", "linattn_fwd_from_state", "linattn_fwd_timed", "linattn_fwd_workspace_bytes", "linattn_fwd_plan", "linattn_decode_step",
-    "linattn_status_string", "linattn_abi_version",
+    "linattn_status_string", "linattn_abi_version", "linattn_bwd", "linattn_bwd_workspace_bytes",
 ]
 
 LINATTN_F32 = 0
@@ -65,6 +65,10 @@ def load():
         lib.linattn_fwd_plan.argtypes = [i] * 8 + [ctypes.POINTER(i), ctypes.POINTER(i)]
         lib.linattn_decode_step.restype = i
         lib.linattn_decode_step.argtypes = [vp] * 6 + [i] * 6 + [vp]
+        lib.linattn_bwd.restype = i
+        lib.linattn_bwd.argtypes = [vp] * 8 + [i] * 8 + [vp, sz, vp]
+        lib.linattn_bwd_workspace_bytes.restype = sz
+        lib.linattn_bwd_workspace_bytes.argtypes = [i] * 7
         lib.linattn_status_string.restype = ctypes.c_char_p
         lib.linattn_status_string.argtypes = [i]
         lib.linattn_abi_version.restype = i
@@ -135,6 +139,20 @@ def linattn_decode_step(state, z, q, k, v, out, B, H, Hkv, d, normalise, dtype, 
     """C ``linattn_decode_step``; returns the status code (0 = ok)."""
     return load().linattn_decode_step(_ptr(state), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, d,
                                       int(normalise), dtype, _stream(stream))
+
+
+def linattn_bwd(q, k, v, out, dout, dq, dk, dv, B, H, Hkv, N, d, causal, normalise, dtype, workspace=None,
+                workspace_bytes=0, stream=None) -> int:
+    """C ``linattn_bwd``; returns the status code (0 = ok)."""
+    return load().linattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H,
+                              Hkv, N, d, int(causal), int(normalise), dtype, _ptr(workspace), workspace_bytes,
+                              _stream(stream))
+
+
+def linattn_bwd_workspace_bytes(B, H, Hkv, N, d, causal, dtype) -> int:
+    """C ``linattn_bwd_workspace_bytes``; returns -1 for invalid arguments."""
+    r = load().linattn_bwd_workspace_bytes(B, H, Hkv, N, d, int(causal), dtype)
+    return -1 if r == ctypes.c_size_t(-1).value else r
 
 
 def linattn_status_string(code: int) -> str:

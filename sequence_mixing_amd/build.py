@@ -22,7 +22,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]
-SOURCES = [os.path.join(CSRC, "linattn.hip"), os.path.join(CSRC, "linattn_plan.cpp")]
+SOURCES = [os.path.join(CSRC, "linattn.hip"), os.path.join(CSRC, "linattn_bwd.hip"),
+           os.path.join(CSRC, "linattn_plan.cpp")]
 
 
 def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str = LIB) -> str:

@@ -33,426 +33,10 @@
 #include <stdint.h>
 
 #include "linattn.h"
+#include "linattn_kern.h"
 #include "linattn_plan.h"
 
 namespace {
-
-typedef __bf16 bf16;
-typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kThreads = 256;
-
-// ------------------------------------------------------- buffer accesses
-//
-// Raw buffer loads/stores through a scalar descriptor (base, size in bytes).
-// The hardware checks every lane's byte offset against the size: loads out
-// of range return zero and stores out of range are dropped.  Tails and
-// masked lanes therefore need no branches, every staging step issues the
-// same instructions, and the compiler can wait for exactly the loads a step
-// consumes while later ones stay in flight.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr unsigned kOutOfRange = 0x80000000u;  // beyond every size used here (< 2^31)
-
-__device__ __forceinline__ Rsrc make_rsrc(const void *base, int bytes)
-{
-    // Word 3: 32-bit data format (raw access, no swizzle, no format conversion).
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
-}
-template <typename G> __device__ __forceinline__ G buf_load16(Rsrc r, unsigned off)
-{
-    static_assert(sizeof(G) == 16, "16-byte group");
-    return __builtin_bit_cast(G, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-template <typename G> __device__ __forceinline__ void buf_store16(Rsrc r, unsigned off, G x)
-{
-    static_assert(sizeof(G) == 16, "16-byte group");
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
-}
-
-// Workgroup barrier for LDS hand-offs only.  __syncthreads() also drains
-// every outstanding global load (vmcnt), which would stall the register
-// prefetch of the next chunk at each barrier; here only LDS traffic
-// (lgkmcnt) is waited for, and the prefetched loads stay in flight.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// phi(x) = ELU(x) + 1 (alpha = 1): x + 1 for x > 0, exp(x) otherwise,
-// written without a branch as max(x, 0) + exp(min(x, 0)) (one v_exp_f32).
-__device__ __forceinline__ float phi(float x)
-{
-    return fmaxf(x, 0.f) + __builtin_amdgcn_exp2f(fminf(x, 0.f) * 1.44269504088896340736f);
-}
-
-// ------------------------------------------------------------------ types
-
-template <typename E> struct Vt;
-template <> struct Vt<bf16> {
-    using v8 = bf16x8;  // 8 consecutive elements: one MFMA operand fragment
-    using v4 = bf16x4;
-    using g16 = bf16x8; // one 16-byte group
-    static constexpr int U = 8;  // elements per 16 bytes
-};
-template <> struct Vt<float> {
-    using v8 = f32x8;
-    using v4 = f32x4;
-    using g16 = f32x4;
-    static constexpr int U = 4;
-};
-
-// acc += A(32 x 16) * B(16 x 32) for one K-block of 16.
-__device__ __forceinline__ void mma(f32x16 &acc, const bf16x8 &a, const bf16x8 &b)
-{
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-}
-__device__ __forceinline__ void mma(f32x16 &acc, const f32x8 &a, const f32x8 &b)
-{
-#pragma unroll
-    for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], acc, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 cat(const bf16x4 &a, const bf16x4 &b)
-{
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-__device__ __forceinline__ f32x8 cat(const f32x4 &a, const f32x4 &b)
-{
-    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-template <typename E> __device__ __forceinline__ typename Vt<E>::v8 cvt8(const float *x);
-template <> __device__ __forceinline__ bf16x8 cvt8<bf16>(const float *x)
-{
-    f32x8 f{x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
-    return __builtin_convertvector(f, bf16x8);
-}
-template <> __device__ __forceinline__ f32x8 cvt8<float>(const float *x)
-{
-    return f32x8{x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
-}
-template <typename E> __device__ __forceinline__ typename Vt<E>::v4 cvt4(f32x4 x);
-template <> __device__ __forceinline__ bf16x4 cvt4<bf16>(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
-template <> __device__ __forceinline__ f32x4 cvt4<float>(f32x4 x) { return x; }
-
-// ---------------------------------------------------------- LDS tiles
-//
-// Row-major tiles whose 16-byte groups are XOR-permuted per row: element
-// (r, c) lives at r * COLS + (c ^ (sig(r) * U)), sig(r) = r % (COLS / U).
-// Runs of 4 or 8 elements starting on a 4-aligned column stay contiguous
-// (an fp32 8-run spans two groups and is read as two), and both row walks
-// and column walks spread over the LDS banks.
-
-template <typename E, int COLS>
-struct Tile {
-    E *p;
-    static constexpr int U = Vt<E>::U;
-    static constexpr int NG = COLS / U;
-    __device__ __forceinline__ static int sig(int r) { return r % NG; }
-    __device__ __forceinline__ int at(int r, int c) const { return r * COLS + (c ^ (sig(r) * U)); }
-    __device__ __forceinline__ typename Vt<E>::v8 read8(int r, int c) const
-    {
-        if constexpr (U == 8) {
-            return *reinterpret_cast<const bf16x8 *>(p + at(r, c));
-        } else {
-            return cat(*reinterpret_cast<const f32x4 *>(p + at(r, c)), *reinterpret_cast<const f32x4 *>(p + at(r, c + 4)));
-        }
-    }
-    __device__ __forceinline__ void write4(int r, int c, typename Vt<E>::v4 x) const
-    {
-        *reinterpret_cast<typename Vt<E>::v4 *>(p + at(r, c)) = x;
-    }
-    __device__ __forceinline__ void write16(int r, int c, typename Vt<E>::g16 x) const
-    {
-        *reinterpret_cast<typename Vt<E>::g16 *>(p + at(r, c)) = x;
-    }
-};
-
-// Column fragment of an MFMA operand out of a row-major tile: lane
-// (h = lane/32, x = lane%32) gets rows ra + e and rb + e (e = 0..3; ra, rb
-// depend on h only) of column col + x, as slots 0..3 and 4..7.
-//
-// bf16 uses ds_read_b64_tr_b16: inside each 16-lane group, lane j receives
-// element j%4 of the 8-byte reads issued by lanes j/4, j/4+4, j/4+8, j/4+12,
-// so lane j supplies the address of row r0 + j/4, columns c0 + 4(j%4).
-// fp32 reads one word per slot (32 lanes walk consecutive columns).
-template <int COLS>
-__device__ __forceinline__ bf16x8 colfrag(const Tile<bf16, COLS> &t, int ra, int rb, int col, int lane)
-{
-    const int j = lane & 15;
-    const int c0 = col + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
-    typedef __attribute__((address_space(3))) bf16x4 *lds4;
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4)(t.p + t.at(ra + (j >> 2), c0)));
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4)(t.p + t.at(rb + (j >> 2), c0)));
-    return cat(lo, hi);
-}
-template <int COLS>
-__device__ __forceinline__ f32x8 colfrag(const Tile<float, COLS> &t, int ra, int rb, int col, int lane)
-{
-    const int c = col + (lane & 31);
-    f32x8 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        r[e] = t.p[t.at(ra + e, c)];
-        r[4 + e] = t.p[t.at(rb + e, c)];
-    }
-    return r;
-}
-
-// Shapes shared by the chunk kernels.
-template <typename T, int D, int C>
-struct Geo {
-    static constexpr int U = Vt<T>::U;       // elements per 16 bytes (one global vector load)
-    static constexpr int DT = D / 32;        // 32-wide feature tiles
-    static constexpr int CT = C / 32;        // 32-row token tiles per chunk
-    static constexpr int KBD = D / 16;       // K-blocks over features
-    static constexpr int NST = DT * DT;      // 32x32 state tiles
-    static constexpr int MAXST = (NST + 3) / 4;  // state tiles per wave
-    static constexpr int GPR = D / U;        // 16-byte groups per token row
-    static constexpr int NGRP = C * GPR;     // 16-byte groups per chunk per tensor
-    static constexpr int LDV = (NGRP + kThreads - 1) / kThreads;  // groups per thread
-    static constexpr int QV = 8 / U;         // 16-byte groups per 8-element fragment
-    static constexpr size_t KV_BYTES = (size_t)C * D * sizeof(T);
-    static constexpr size_t ST_BYTES = (size_t)CT * D * D * sizeof(T) + (size_t)CT * D * 4;
-    // Double-buffer the K/V tiles when two workgroups still fit on a CU (or
-    // when even one buffer would not leave room for two).
-    static constexpr size_t LDS_CU = 160 * 1024;
-    static constexpr bool FITS = 2 * KV_BYTES + ST_BYTES <= LDS_CU;
-    static constexpr bool DB = 4 * KV_BYTES + ST_BYTES <= LDS_CU / 2 ||
-                               (2 * KV_BYTES + ST_BYTES > LDS_CU / 2 && 4 * KV_BYTES + ST_BYTES <= LDS_CU);
-    // State tile i of wave w is st = w * MAXST + i (d = 128: row block w);
-    // only tile 0 of a wave can sit in column block 0 and own z.
-    __device__ static int tile_of(int w, int i) { return w * MAXST + i; }
-};
-
-// Loads the 16-byte groups of one chunk of a [N][D] sequence (zeros past N).
-template <typename T, int D, int C, int L>
-__device__ __forceinline__ void load_chunk(typename Vt<T>::g16 (&r)[L], const T *base, int t0, int N, int tid)
-{
-    using G = Geo<T, D, C>;
-    static_assert(L == G::LDV, "register array size");
-    using g16 = typename Vt<T>::g16;
-    if (t0 + C <= N && G::NGRP % kThreads == 0) {
-#pragma unroll
-        for (int l = 0; l < G::LDV; ++l) {
-            const int e = tid + l * kThreads;
-            r[l] = *reinterpret_cast<const g16 *>(base + (size_t)(t0 + e / G::GPR) * D + (e % G::GPR) * G::U);
-        }
-    } else {
-#pragma unroll
-        for (int l = 0; l < G::LDV; ++l) {
-            const int e = tid + l * kThreads;
-            const int t = e / G::GPR, q = e % G::GPR;
-            g16 x = {};
-            if (e < G::NGRP && t0 + t < N) x = *reinterpret_cast<const g16 *>(base + (size_t)(t0 + t) * D + q * G::U);
-            r[l] = x;
-        }
-    }
-}
-
-// Writes a staged chunk to LDS: phi(K) and V, both row-major.  Only the
-// first `rows` tokens are real; the others get phi(k) = 0 (their v is zero
-// too) so that they add nothing to any sum.
-template <typename T, int D, int C, int TH, int L>
-__device__ __forceinline__ void stage_rows(const typename Vt<T>::g16 (&kr)[L], const typename Vt<T>::g16 (&vr)[L],
-                                           Tile<T, D> sK, Tile<T, D> sV, int rows, int tid)
-{
-    constexpr int U = Vt<T>::U, GPR = D / U, NGRP = C * GPR;
-    static_assert(L == (NGRP + TH - 1) / TH, "register array size");
-    const bool full = rows >= C;
-#pragma unroll
-    for (int l = 0; l < L; ++l) {
-        const int e = tid + l * TH;
-        if (NGRP % TH == 0 || e < NGRP) {
-            const int t = e / GPR, q = e % GPR;
-            typename Vt<T>::g16 fk;
-#pragma unroll
-            for (int i = 0; i < U; ++i) fk[i] = (T)phi((float)kr[l][i]);
-            if (!full) {
-                if (t >= rows) fk = typename Vt<T>::g16{};
-            }
-            sK.write16(t, q * U, fk);
-            sV.write16(t, q * U, vr[l]);
-        }
-    }
-}
-
-// A K-block operand whose every slot is 1 (for column sums on MFMA).
-template <typename T> __device__ __forceinline__ typename Vt<T>::v8 ones8()
-{
-    typename Vt<T>::v8 o;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) o[s] = (T)1.f;
-    return o;
-}
-
-// State tile (it, jt) += phi(K)^T V over the 32 tokens of key tile kt.
-// The K-block of 16 tokens kb2 puts token kt*32 + 16 kb2 + 8h + s in slot s.
-// When want_z it also returns the tile's column sum of phi(K) for feature
-// it*32 + lane%32: bf16 forms it on the matrix core (1 phi(K) into a scratch
-// accumulator whose every register then holds the sum), fp32 adds on the
-// vector ALUs and returns this half-wave's part (the caller adds the other).
-template <typename T, int D>
-__device__ __forceinline__ float tile_state_update(f32x16 &acc, bool want_z, int it, int jt, int kt, Tile<T, D> sK,
-                                                   Tile<T, D> sV, int lane)
-{
-    const int h = lane >> 5;
-    float zs = 0.f;
-    f32x16 Z = f32x16{};
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const int r0 = kt * 32 + 16 * kb2 + 8 * h;
-        const auto a = colfrag(sK, r0, r0 + 4, it * 32, lane);
-        const auto b = colfrag(sV, r0, r0 + 4, jt * 32, lane);
-        mma(acc, a, b);
-        if (want_z) {
-            if constexpr (sizeof(T) == 2) {
-                mma(Z, ones8<T>(), a);
-            } else {
-#pragma unroll
-                for (int s = 0; s < 8; ++s) zs += a[s];
-            }
-        }
-    }
-    if constexpr (sizeof(T) == 2) zs = Z[0];
-    return zs;
-}
-
-// -------------------------------------------------------------- seg_totals
-//
-// One workgroup per (sequence, segment): T_p = phi(K_p)^T V_p and
-// sum phi(K_p), written as fp32 partials ws[seq][p] = [S (d x d) | z (d)].
-// Chunks of C1 tokens, double-buffered in LDS (one barrier per chunk).
-template <typename T, int D, int C1>
-__global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict__ k, const T *__restrict__ v,
-                                                            float *__restrict__ ws, int N, int seg_len, int nslots)
-{
-    using G = Geo<T, D, C1>;
-    __shared__ __attribute__((aligned(16))) T smK[2][C1 * D];
-    __shared__ __attribute__((aligned(16))) T smV[2][C1 * D];
-
-    const int seq = blockIdx.x / nslots, p = blockIdx.x % nslots;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
-    const T *kb = k + (size_t)seq * N * D;
-    const T *vb = v + (size_t)seq * N * D;
-    const int s0 = p * seg_len, s1 = min(N, s0 + seg_len);
-    const int nch = (s1 - s0 + C1 - 1) / C1;
-
-    f32x16 acc[G::MAXST];
-    float zacc = 0.f;
-#pragma unroll
-    for (int i = 0; i < G::MAXST; ++i) acc[i] = f32x16{};
-    // Two chunks in flight: register sets A and B alternate, chunk ci + 2 is
-    // requested as soon as chunk ci has been staged.  Buffer loads: chunks
-    // past the segment read nothing, tokens past N read zeros.
-    using g16 = typename Vt<T>::g16;
-    constexpr int E = (int)sizeof(T);
-    g16 kA[G::LDV], vA[G::LDV], kB[G::LDV], vB[G::LDV];
-    auto rows_at = [&](int t0) { return t0 < s1 ? min(C1, s1 - t0) : 0; };
-    auto load = [&](g16 (&kr)[G::LDV], g16 (&vr)[G::LDV], int t0) {
-        const int rows = rows_at(t0);
-        const Rsrc rk = make_rsrc(kb + (size_t)t0 * D, rows * D * E);
-        const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, rows * D * E);
-#pragma unroll
-        for (int l = 0; l < G::LDV; ++l) {
-            const unsigned off = (unsigned)(tid + l * kThreads) * 16u;
-            kr[l] = buf_load16<g16>(rk, off);
-            vr[l] = buf_load16<g16>(rv, off);
-        }
-    };
-    load(kA, vA, s0);
-    __builtin_amdgcn_sched_barrier(0);  // keep chunk 0's loads ahead of chunk 1's, as in the loop
-    load(kB, vB, s0 + C1);
-    auto absorb = [&](int buf) {
-        const Tile<T, D> sK{smK[buf]}, sV{smV[buf]};
-#pragma unroll
-        for (int i = 0; i < G::MAXST; ++i) {
-            const int st = G::tile_of(w, i);
-            if (st < G::NST) {
-                const int it = st / G::DT, jt = st % G::DT;
-#pragma unroll
-                for (int kt = 0; kt < G::CT; ++kt)
-                    zacc += tile_state_update<T, D>(acc[i], i == 0 && jt == 0, it, jt, kt, sK, sV, lane);
-            }
-        }
-    };
-    // Chunks in pairs; with an odd count the last pair's second chunk lies
-    // past the segment and adds zeros (every step issues the same loads).
-    for (int ci = 0; ci < nch; ci += 2) {
-        stage_rows<T, D, C1, kThreads>(kA, vA, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, rows_at(s0 + ci * C1), tid);
-        load(kA, vA, s0 + (ci + 2) * C1);
-        lds_barrier();
-        absorb(0);
-        stage_rows<T, D, C1, kThreads>(kB, vB, Tile<T, D>{smK[1]}, Tile<T, D>{smV[1]}, rows_at(s0 + (ci + 1) * C1), tid);
-        load(kB, vB, s0 + (ci + 3) * C1);
-        lds_barrier();
-        absorb(1);
-    }
-    float *out = ws + ((size_t)seq * nslots + p) * (size_t)D * (D + 1);
-#pragma unroll
-    for (int i = 0; i < G::MAXST; ++i) {
-        const int st = G::tile_of(w, i);
-        if (st < G::NST) {
-            const int it = st / G::DT, jt = st % G::DT;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = it * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                out[(size_t)row * D + jt * 32 + n] = acc[i][r];
-            }
-            if (i == 0 && jt == 0) {
-                const float z = sizeof(T) == 2 ? zacc : zacc + __shfl_xor(zacc, 32);
-                if (h == 0) out[(size_t)D * D + it * 32 + n] = z;
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------- seg_scan
-//
-// ws holds nslots partials of E = D*D + D floats per sequence.  mode 0:
-// inclusive prefix along the slots, in place.  mode 1: the sum, written to
-// slot 0 and, when given, to state_out / z_out.  Both start from s_in / z_in
-// (the sums of earlier tokens) when given.
-__global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, int nslots, int D, int mode,
-                                                       float *__restrict__ state_out, float *__restrict__ z_out,
-                                                       const float *__restrict__ s_in, const float *__restrict__ z_in)
-{
-    const int E = D * D + D;
-    const int seq = blockIdx.y;
-    const int e = blockIdx.x * kThreads + threadIdx.x;
-    if (e >= E) return;
-    float *base = ws + (size_t)seq * nslots * E + e;
-    // the sums start from the given ones (continuation), else from zero
-    float acc = 0.f;
-    if (e < D * D) {
-        if (s_in) acc = s_in[(size_t)seq * D * D + e];
-    } else if (z_in) {
-        acc = z_in[(size_t)seq * D + (e - D * D)];
-    }
-    // Batches of independent loads, then the running sum over the batch.
-    constexpr int BATCH = 32;
-    for (int p0 = 0; p0 < nslots; p0 += BATCH) {
-        float x[BATCH];
-#pragma unroll
-        for (int j = 0; j < BATCH; ++j) x[j] = p0 + j < nslots ? base[(size_t)(p0 + j) * E] : 0.f;
-#pragma unroll
-        for (int j = 0; j < BATCH; ++j) {
-            acc += x[j];
-            if (mode == 0 && p0 + j < nslots) base[(size_t)(p0 + j) * E] = acc;
-        }
-    }
-    if (mode == 1) {
-        base[0] = acc;
-        if (e < D * D) {
-            if (state_out) state_out[(size_t)seq * D * D + e] = acc;
-        } else if (z_out) {
-            z_out[(size_t)seq * D + (e - D * D)] = acc;
-        }
-    }
-}
 
 // ----------------------------------------------------------- causal_chunks
 //
@@ -1048,10 +632,6 @@ __global__ void k_fill_copy(float *__restrict__ p, const float *__restrict__ src
 
 // -------------------------------------------------------------- launchers
 
-int launch_status()
-{
-    return hipGetLastError() == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
-}
 
 // Sums of earlier tokens a forward pass continues from (both nullable).
 struct Start {
@@ -1070,43 +650,7 @@ int record(const Timing *t, int i, hipStream_t st)
     return (t && hipEventRecord(t->ev[i], st) != hipSuccess) ? LINATTN_ERR_HIP : LINATTN_OK;
 }
 
-// Totals pass with chunks of c1 tokens (32, 64 or 128; at most 16 KiB of K per
-// chunk, so that two chunks of K and V double-buffer in 64 KiB of LDS).
-template <typename T, int D>
-int launch_totals(int c1, unsigned nblocks, hipStream_t st, const T *k, const T *v, float *ws, int N, int seg_len,
-                  int nslots)
-{
-    constexpr int cap = 65536 / (4 * D * (int)sizeof(T));
-    switch (c1) {
-    case 32:
-        hipLaunchKernelGGL((k_seg_totals<T, D, 32>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len, nslots);
-        return LINATTN_OK;
-    case 64:
-        if constexpr (64 <= cap) {
-            hipLaunchKernelGGL((k_seg_totals<T, D, 64>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len,
-                               nslots);
-            return LINATTN_OK;
-        }
-        break;
-    case 128:
-        if constexpr (128 <= cap) {
-            hipLaunchKernelGGL((k_seg_totals<T, D, 128>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len,
-                               nslots);
-            return LINATTN_OK;
-        }
-        break;
-    }
-    return LINATTN_ERR_UNSUPPORTED;
-}
 
-template <typename T, int D>
-int totals_chunk(int seg_len)
-{
-    constexpr int cap = 65536 / (4 * D * (int)sizeof(T));
-    int c1 = cap < 128 ? cap : 128;
-    while (c1 > 32 && seg_len % c1 != 0) c1 /= 2;  // segments are whole chunks of the pass
-    return c1;
-}
 
 template <typename T, int D, int C>
 int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out, float *state_out,
@@ -1206,7 +750,6 @@ int dispatch_d(const linattn::Plan &pl, const void *q, const void *k, const void
     return LINATTN_ERR_UNSUPPORTED;
 }
 
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <typename T>
 int run_decode(float *state, float *z, const void *q, const void *k, const void *v, void *out, int B, int H,

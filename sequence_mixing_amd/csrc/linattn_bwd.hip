@@ -1,0 +1,726 @@
+// linattn_bwd.hip - backward pass of phi = ELU+1 linear attention (gfx950).
+//
+// The forward pass (LinearTile 1.0.0 README, "How It Works", with the causal
+// and GQA items of its "Features" list) is o_t = num_t / den_t with
+// a_t = phi(q_t), b_s = phi(k_s), num_t = S_t^T a_t, den_t = a_t . z_t and the
+// running sums S_t = sum_{s<=t} b_s v_s^T, z_t = sum_{s<=t} b_s.  Its gradient
+// for an output gradient dO (the chain rule; the README's project layout
+// names a backward module without its content, and the Stream efficiency
+// essay, section 4.2, differentiates a running-sum recurrence by a
+// reverse-time scan, the pattern used for dK and dV here):
+//   g_t = dO_t / den_t,  h_t = -(dO_t . o_t) / den_t      (normalise == 0:
+//                                                          g_t = dO_t, h_t = 0)
+//   dq_t = (S_t g_t + h_t z_t) * phi'(q_t)
+//   dv_s = R_s^T b_s,  dk_s = (R_s v_s + r_s) * phi'(k_s)
+// with R_s = sum_{t>=s} a_t g_t^T and r_s = sum_{t>=s} h_t a_t over the query
+// heads of the kv group (non-causal: every sum runs over the whole sequence).
+// phi'(x) = 1 for x > 0 and exp(x) = phi(x) otherwise, i.e. min(1, phi(x)).
+//
+// Launches (one workgroup = 4 wave64s; chunks of 32 tokens):
+//   seg_totals, seg_scan   the forward's segment sums of b v^T and b, giving
+//                          each dq segment its starting S and z;
+//   bwd_dq                 per (sequence, query head, segment): walks the
+//                          segment forwards.  Per chunk, on MFMA:
+//                          den (1 . masked B A^T plus a . z), then
+//                          dA^T = B^T (M .* (V G^T + h)) + S G^T; writes dq
+//                          and den (kept for the next passes);
+//   bwd_dkv<totals>        per (sequence, segment): sum of a g^T and h a over
+//                          the segment and the group's heads;
+//   seg_scan (suffix)      gives each segment the sums of the later ones;
+//   bwd_dkv                per (sequence, segment): walks the segment
+//                          backwards.  Per chunk and head, on MFMA:
+//                          dV^T += G^T (M .* A B^T), dB^T += A^T (M .* (G V^T + h)),
+//                          R += A^T G; then dV^T += R^T B^T, dB^T += R V^T + r.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "linattn.h"
+#include "linattn_kern.h"
+
+namespace {
+
+constexpr int kBC = 32;  // tokens per chunk (one 32-row MFMA tile)
+
+// Shapes of the backward kernels for element type T and head dimension D.
+template <typename T, int D>
+struct BGeo {
+    static constexpr int U = Vt<T>::U;          // elements per 16-byte group
+    static constexpr int GPR = D / U;           // groups per token row
+    static constexpr int NGRP = kBC * GPR;      // groups per chunk of one tensor
+    static constexpr int LDV = (NGRP + kThreads - 1) / kThreads;
+    static constexpr int DT = D / 32;
+    static constexpr int KBD = D / 16;          // K-blocks over features
+    static constexpr int NST = DT * DT;
+    static constexpr int MAXST = (NST + 3) / 4;
+    static constexpr int E = (int)sizeof(T);
+    __device__ static int tile_of(int w, int i) { return w * MAXST + i; }
+};
+
+template <typename T> __device__ __forceinline__ typename Vt<T>::g16 to_g16(const float *x);
+template <> __device__ __forceinline__ bf16x8 to_g16<bf16>(const float *x) { return cvt8<bf16>(x); }
+template <> __device__ __forceinline__ f32x4 to_g16<float>(const float *x) { return f32x4{x[0], x[1], x[2], x[3]}; }
+
+// Registers base..base+7 of an accumulator as one operand fragment (rows
+// 16 kb + 4h + e and 16 kb + 8 + 4h + e for base = 8 kb): an accumulator
+// fed back as the B operand of the next product.
+template <typename T> __device__ __forceinline__ typename Vt<T>::v8 acc8(const f32x16 &m, int base)
+{
+    float x[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) x[s] = m[base + s];
+    return cvt8<T>(x);
+}
+
+// Low part of a 16-bit operand: x - (float)round(x), rounded.  For bf16 the
+// pair (hi, lo) carries x to about 2^-16 relative, so a product of two split
+// operands taken as hi*hi + hi*lo + lo*hi is close to an fp32 product; fp32
+// operands need no low part.
+template <typename T> __device__ __forceinline__ typename Vt<T>::g16 to_g16_lo(const float *x)
+{
+    float r[Vt<T>::U];
+#pragma unroll
+    for (int i = 0; i < Vt<T>::U; ++i) r[i] = x[i] - (float)(T)x[i];
+    return to_g16<T>(r);
+}
+template <typename T> __device__ __forceinline__ typename Vt<T>::v8 acc8_lo(const f32x16 &m, int base)
+{
+    float x[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) x[s] = m[base + s] - (float)(T)m[base + s];
+    return cvt8<T>(x);
+}
+
+// Sum over the GPR consecutive lanes that hold one token row.
+template <int GPR> __device__ __forceinline__ float row_sum(float x)
+{
+#pragma unroll
+    for (int m = GPR / 2; m >= 1; m /= 2) x += __shfl_xor(x, m);
+    return x;
+}
+
+// Row-major accumulator tile (it, jt) of a d x d sum, written to an LDS tile
+// in the operand type: lane (h, n) register r holds row it*32 + 8(r/4) + 4h + r%4,
+// column jt*32 + n.
+template <typename T, int D>
+__device__ __forceinline__ void publish_tile(const f32x16 &acc, Tile<T, D> t, int it, int jt, int lane)
+{
+    const int h = lane >> 5, n = lane & 31;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t.p[t.at(it * 32 + 8 * (r / 4) + 4 * h + (r % 4), jt * 32 + n)] = (T)acc[r];
+}
+
+// ----------------------------------------------------------------- bwd_dq
+//
+// S (d x d, fp32) lives in MFMA accumulators over the four waves as in the
+// forward; the waves read it through an LDS copy refreshed once per chunk.
+// z lives in LDS (two copies: before and after the chunk).
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void k_bwd_dq(const T *__restrict__ q, const T *__restrict__ k,
+                                                      const T *__restrict__ v, const T *__restrict__ o,
+                                                      const T *__restrict__ dout, T *__restrict__ dq,
+                                                      float *__restrict__ den_out, const float *__restrict__ ws,
+                                                      int H, int Hkv, int N, int G, int P, int seg_len, int causal,
+                                                      int normalise)
+{
+    using BG = BGeo<T, D>;
+    using g16 = typename Vt<T>::g16;
+    constexpr int U = BG::U, GPR = BG::GPR, LDV = BG::LDV, E = BG::E;
+    __shared__ __attribute__((aligned(16))) T smA[kBC * D];
+    __shared__ __attribute__((aligned(16))) T smB[kBC * D];
+    __shared__ __attribute__((aligned(16))) T smV[kBC * D];
+    __shared__ __attribute__((aligned(16))) T smG[kBC * D];
+    __shared__ __attribute__((aligned(16))) T smO[kBC * D];
+    __shared__ __attribute__((aligned(16))) T smS[D * D];
+    // bf16: low parts of b and g.  dq of the first tokens of a normalised
+    // sequence is a small difference of the value and normaliser terms, so the
+    // intra-chunk products take both operands split (see to_g16_lo).
+    constexpr bool SPLIT = sizeof(T) == 2;
+    __shared__ __attribute__((aligned(16))) T smBl[SPLIT ? kBC * D : 8];
+    __shared__ __attribute__((aligned(16))) T smGl[SPLIT ? kBC * D : 8];
+    __shared__ float sZ[2][D];
+    __shared__ float sDen0[kBC], sDen[kBC], sDov[kBC], sH[kBC];
+    const Tile<T, D> sA{smA}, sB{smB}, sV{smV}, sG{smG}, sO{smO}, sS{smS}, sBl{smBl}, sGl{smGl};
+
+    const int p = blockIdx.x % P;
+    const int qh = blockIdx.x / P;  // b * H + head
+    const int b = qh / H, head = qh % H, g = head / G;
+    const int sq = b * Hkv + g;     // (batch, kv head) sequence
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
+    const T *qb = q + (size_t)qh * N * D;
+    const T *ob = o + (size_t)qh * N * D;
+    const T *db = dout + (size_t)qh * N * D;
+    T *dqb = dq + (size_t)qh * N * D;
+    const T *kb = k + (size_t)sq * N * D;
+    const T *vb = v + (size_t)sq * N * D;
+    const int s0 = p * seg_len, s1 = min(N, s0 + seg_len);
+    const int nch = (s1 - s0 + kBC - 1) / kBC;
+
+    // Starting sums: causal segment p > 0 reads the inclusive prefix of the
+    // segments before it (slot p - 1); non-causal reads the total (slot 0).
+    const float *init = nullptr;
+    if (!causal) init = ws + (size_t)sq * P * D * (D + 1);
+    else if (p > 0) init = ws + ((size_t)sq * (P - 1) + (p - 1)) * (size_t)D * (D + 1);
+    f32x16 S[BG::MAXST];
+#pragma unroll
+    for (int i = 0; i < BG::MAXST; ++i) {
+        S[i] = f32x16{};
+        const int st = BG::tile_of(w, i);
+        if (init && st < BG::NST) {
+            const int it = st / BG::DT, jt = st % BG::DT;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                S[i][r] = init[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n];
+        }
+    }
+    for (int i = tid; i < D; i += kThreads) sZ[0][i] = init ? init[(size_t)D * D + i] : 0.f;
+    if (!causal) {
+        // the sums are the same for every chunk: one copy
+#pragma unroll
+        for (int i = 0; i < BG::MAXST; ++i) {
+            const int st = BG::tile_of(w, i);
+            if (st < BG::NST) publish_tile<T, D>(S[i], sS, st / BG::DT, st % BG::DT, lane);
+        }
+    }
+    __syncthreads();
+
+    g16 dr[LDV];
+    for (int c = 0; c < nch; ++c) {
+        const int t0 = s0 + c * kBC, rows = min(kBC, s1 - t0);
+        const int zc = causal ? (c & 1) : 0;
+        // ---- stage: phi(q), phi(k), v to LDS; dO kept in registers; row dots
+        {
+            const unsigned bytes = (unsigned)(rows * D * E);
+            const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, bytes), rk = make_rsrc(kb + (size_t)t0 * D, bytes);
+            const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, bytes), rd = make_rsrc(db + (size_t)t0 * D, bytes);
+            const Rsrc ro = make_rsrc(ob + (size_t)t0 * D, normalise ? bytes : 0u);
+            g16 qr[LDV], kr[LDV], vr[LDV], orr[LDV];
+#pragma unroll
+            for (int l = 0; l < LDV; ++l) {
+                const unsigned off = (unsigned)(tid + l * kThreads) * 16u;
+                qr[l] = buf_load16<g16>(rq, off);
+                kr[l] = buf_load16<g16>(rk, off);
+                vr[l] = buf_load16<g16>(rv, off);
+                dr[l] = buf_load16<g16>(rd, off);
+                orr[l] = buf_load16<g16>(ro, off);
+            }
+#pragma unroll
+            for (int l = 0; l < LDV; ++l) {
+                const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
+                float a[U], bk[U], dinter = 0.f, dov = 0.f;
+#pragma unroll
+                for (int i = 0; i < U; ++i) {
+                    a[i] = phi((float)qr[l][i]);
+                    bk[i] = t < rows ? phi((float)kr[l][i]) : 0.f;
+                    dov += (float)dr[l][i] * (float)orr[l][i];
+                }
+                if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
+#pragma unroll
+                    for (int i = 0; i < U; ++i) dinter += a[i] * sZ[zc][cq + i];
+                    sA.write16(t, cq, to_g16<T>(a));
+                    sB.write16(t, cq, to_g16<T>(bk));
+                    if constexpr (SPLIT) sBl.write16(t, cq, to_g16_lo<T>(bk));
+                    sV.write16(t, cq, vr[l]);
+                }
+                dinter = row_sum<GPR>(dinter);
+                dov = row_sum<GPR>(dov);
+                if ((BG::NGRP % kThreads == 0 || e < BG::NGRP) && e % GPR == 0) {
+                    sDen0[t] = dinter;
+                    sDov[t] = dov;
+                }
+            }
+        }
+        __syncthreads();
+        // ---- den (wave 0), S copy before this chunk, z after it
+        if (w == 0 && normalise) {
+            float intra = 0.f;
+            if (causal) {
+                f32x16 Pt = f32x16{};  // Pt[s][t] = b_s . a_t
+#pragma unroll
+                for (int kk = 0; kk < BG::KBD; ++kk) mma(Pt, sB.read8(n, kk * 16 + 8 * h), sA.read8(n, kk * 16 + 8 * h));
+#pragma unroll
+                for (int r = 0; r < 16; ++r) intra += (8 * (r / 4) + 4 * h + (r % 4)) <= n ? Pt[r] : 0.f;
+                intra += __shfl_xor(intra, 32);
+            }
+            if (h == 0) sDen[n] = sDen0[n] + intra;
+        }
+        if (causal) {
+#pragma unroll
+            for (int i = 0; i < BG::MAXST; ++i) {
+                const int st = BG::tile_of(w, i);
+                if (st < BG::NST) publish_tile<T, D>(S[i], sS, st / BG::DT, st % BG::DT, lane);
+            }
+            for (int i = tid; i < D; i += kThreads) {
+                float zz = sZ[zc][i];
+                for (int t = 0; t < kBC; ++t) {
+                    zz += (float)sB.p[sB.at(t, i)];
+                    if constexpr (SPLIT) zz += (float)sBl.p[sBl.at(t, i)];
+                }
+                sZ[zc ^ 1][i] = zz;
+            }
+        }
+        __syncthreads();
+        // ---- g and h
+#pragma unroll
+        for (int l = 0; l < LDV; ++l) {
+            const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
+            if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
+                const float den = normalise ? sDen[t] : 1.f;
+                const float inv = t < rows ? 1.f / den : 0.f;
+                float gg[U];
+#pragma unroll
+                for (int i = 0; i < U; ++i) gg[i] = (float)dr[l][i] * inv;
+                sG.write16(t, cq, to_g16<T>(gg));
+                if constexpr (SPLIT) sGl.write16(t, cq, to_g16_lo<T>(gg));
+                if (e % GPR == 0) {
+                    sH[t] = normalise ? -sDov[t] * inv : 0.f;
+                    if (normalise && t < rows) den_out[(size_t)qh * N + t0 + t] = den;
+                }
+            }
+        }
+        __syncthreads();
+        // ---- dA^T tiles (one 32-feature block per unit) and the state update
+        for (int it = w; it < BG::DT; it += 4) {
+            f32x16 acc = f32x16{};
+            const float hn = sH[n];
+            if (causal) {
+                f32x16 M = f32x16{};  // M[s][t] = v_s . g_t + h_t for s <= t
+#pragma unroll
+                for (int kk = 0; kk < BG::KBD; ++kk) {
+                    const auto vf = sV.read8(n, kk * 16 + 8 * h);
+                    mma(M, vf, sG.read8(n, kk * 16 + 8 * h));
+                    if constexpr (SPLIT) mma(M, vf, sGl.read8(n, kk * 16 + 8 * h));
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) M[r] = (8 * (r / 4) + 4 * h + (r % 4)) <= n ? M[r] + hn : 0.f;
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2) {
+                    const int ra = 16 * kb2 + 4 * h;
+                    const auto bh = colfrag(sB, ra, ra + 8, it * 32, lane);
+                    mma(acc, bh, acc8<T>(M, 8 * kb2));
+                    if constexpr (SPLIT) {
+                        mma(acc, bh, acc8_lo<T>(M, 8 * kb2));
+                        mma(acc, colfrag(sBl, ra, ra + 8, it * 32, lane), acc8<T>(M, 8 * kb2));
+                    }
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < BG::KBD; ++kk)
+                mma(acc, sS.read8(it * 32 + n, kk * 16 + 8 * h), sG.read8(n, kk * 16 + 8 * h));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = it * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                const float da = acc[r] + hn * sZ[zc][i];
+                sO.p[sO.at(n, i)] = (T)(da * fminf(1.f, (float)sA.p[sA.at(n, i)]));
+            }
+        }
+        if (causal) {
+#pragma unroll
+            for (int i = 0; i < BG::MAXST; ++i) {
+                const int st = BG::tile_of(w, i);
+                if (st < BG::NST) tile_state_update<T, D>(S[i], false, st / BG::DT, st % BG::DT, 0, sB, sV, lane);
+            }
+        }
+        __syncthreads();
+        // ---- store dq rows
+        {
+            const Rsrc rdq = make_rsrc(dqb + (size_t)t0 * D, rows * D * E);
+#pragma unroll
+            for (int l = 0; l < LDV; ++l) {
+                const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
+                if (BG::NGRP % kThreads == 0 || e < BG::NGRP)
+                    buf_store16<g16>(rdq, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sO.p + sO.at(t, cq)));
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- bwd_dkv
+//
+// TOTALS: per (sequence, segment) the sums R = sum a g^T and r = sum h a over
+// the segment's tokens and the group's query heads, written to ws_r.
+// Otherwise: the segment walked backwards from the sums of the later
+// segments; per chunk the intra-chunk terms of every head, then the carried
+// terms, then dk and dv are stored.
+template <typename T, int D, bool TOTALS>
+__global__ __launch_bounds__(kThreads) void k_bwd_dkv(const T *__restrict__ q, const T *__restrict__ k,
+                                                       const T *__restrict__ v, const T *__restrict__ o,
+                                                       const T *__restrict__ dout, const float *__restrict__ den,
+                                                       T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ ws_r,
+                                                       int H, int Hkv, int N, int G, int P, int seg_len, int causal,
+                                                       int normalise, int nslots, int first_seg)
+{
+    using BG = BGeo<T, D>;
+    using g16 = typename Vt<T>::g16;
+    constexpr int U = BG::U, GPR = BG::GPR, LDV = BG::LDV, E = BG::E;
+    __shared__ __attribute__((aligned(16))) T smA[kBC * D];
+    __shared__ __attribute__((aligned(16))) T smG[kBC * D];
+    __shared__ __attribute__((aligned(16))) T smB[TOTALS ? 16 / sizeof(T) : kBC * D];
+    __shared__ __attribute__((aligned(16))) T smV[TOTALS ? 16 / sizeof(T) : kBC * D];
+    __shared__ __attribute__((aligned(16))) T smR[TOTALS ? 16 / sizeof(T) : D * D];
+    __shared__ float sH[kBC], sr[D];
+    const Tile<T, D> sA{smA}, sG{smG}, sB{smB}, sV{smV}, sR{smR};
+    const Tile<T, D> sOK{smA}, sOV{smG};  // dk, dv rows, once the heads are done
+
+    const int sq = blockIdx.x / nslots;                // (batch, kv head) sequence
+    const int pseg = blockIdx.x % nslots + first_seg;  // segment
+    const int bb = sq / Hkv, g = sq % Hkv;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
+    const int s0 = pseg * seg_len, s1 = min(N, s0 + seg_len);
+    const int nch = (s1 - s0 + kBC - 1) / kBC;
+    const T *kb = k + (size_t)sq * N * D;
+    const T *vb = v + (size_t)sq * N * D;
+
+    // R tiles in accumulators, r[i] in thread i (i < D).
+    const float *init = nullptr;
+    if (!TOTALS) {
+        if (!causal) init = ws_r + (size_t)sq * P * D * (D + 1);
+        else if (pseg < P - 1) init = ws_r + ((size_t)sq * (P - 1) + pseg) * (size_t)D * (D + 1);
+    }
+    f32x16 R[BG::MAXST];
+#pragma unroll
+    for (int i = 0; i < BG::MAXST; ++i) {
+        R[i] = f32x16{};
+        const int st = BG::tile_of(w, i);
+        if (init && st < BG::NST) {
+            const int it = st / BG::DT, jt = st % BG::DT;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                R[i][r] = init[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n];
+        }
+    }
+    float rr = (init && tid < D) ? init[(size_t)D * D + tid] : 0.f;
+
+    // output units: dv^T feature block u (u < DT) or dk^T feature block u - DT
+    constexpr int NU = 2 * BG::DT, MAXU = (NU + 3) / 4;
+    f32x16 out[MAXU];
+
+    for (int cc = nch - 1; cc >= 0; --cc) {
+        const int t0 = s0 + cc * kBC, rows = min(kBC, s1 - t0);
+        const unsigned bytes = (unsigned)(rows * D * E);
+        if (!TOTALS) {
+#pragma unroll
+            for (int u = 0; u < MAXU; ++u) out[u] = f32x16{};
+            const Rsrc rk = make_rsrc(kb + (size_t)t0 * D, bytes), rv = make_rsrc(vb + (size_t)t0 * D, bytes);
+            g16 kr[LDV], vr[LDV];
+#pragma unroll
+            for (int l = 0; l < LDV; ++l) {
+                const unsigned off = (unsigned)(tid + l * kThreads) * 16u;
+                kr[l] = buf_load16<g16>(rk, off);
+                vr[l] = buf_load16<g16>(rv, off);
+            }
+#pragma unroll
+            for (int l = 0; l < LDV; ++l) {
+                const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
+                if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
+                    float bk[U];
+#pragma unroll
+                    for (int i = 0; i < U; ++i) bk[i] = t < rows ? phi((float)kr[l][i]) : 0.f;
+                    sB.write16(t, cq, to_g16<T>(bk));
+                    sV.write16(t, cq, vr[l]);
+                }
+            }
+            // carried sums of the later tokens, as they stand before this chunk
+            if (causal || cc == nch - 1) {
+#pragma unroll
+                for (int i = 0; i < BG::MAXST; ++i) {
+                    const int st = BG::tile_of(w, i);
+                    if (st < BG::NST) publish_tile<T, D>(R[i], sR, st / BG::DT, st % BG::DT, lane);
+                }
+                if (tid < D) sr[tid] = rr;
+            }
+            __syncthreads();
+        }
+        // non-causal: the carried sums are the totals and no head adds to them here
+        const int nheads = (!TOTALS && !causal) ? 0 : G;
+        for (int hh = 0; hh < nheads; ++hh) {
+            const int qh = bb * H + g * G + hh;
+            // ---- stage phi(q), g, h of this head
+            {
+                const T *qb = q + ((size_t)qh * N + t0) * D, *db = dout + ((size_t)qh * N + t0) * D;
+                const T *ob = o + ((size_t)qh * N + t0) * D;
+                const Rsrc rq = make_rsrc(qb, bytes), rd = make_rsrc(db, bytes), ro = make_rsrc(ob, normalise ? bytes : 0u);
+                g16 qr[LDV], dr[LDV], orr[LDV];
+#pragma unroll
+                for (int l = 0; l < LDV; ++l) {
+                    const unsigned off = (unsigned)(tid + l * kThreads) * 16u;
+                    qr[l] = buf_load16<g16>(rq, off);
+                    dr[l] = buf_load16<g16>(rd, off);
+                    orr[l] = buf_load16<g16>(ro, off);
+                }
+#pragma unroll
+                for (int l = 0; l < LDV; ++l) {
+                    const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
+                    const bool real = t < rows;
+                    const float dn = (normalise && real && (BG::NGRP % kThreads == 0 || e < BG::NGRP))
+                                         ? den[(size_t)qh * N + t0 + t] : 1.f;
+                    const float inv = real ? 1.f / dn : 0.f;
+                    float a[U], gg[U], dov = 0.f;
+#pragma unroll
+                    for (int i = 0; i < U; ++i) {
+                        a[i] = real ? phi((float)qr[l][i]) : 0.f;
+                        gg[i] = (float)dr[l][i] * inv;
+                        dov += (float)dr[l][i] * (float)orr[l][i];
+                    }
+                    dov = row_sum<GPR>(dov);
+                    if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
+                        sA.write16(t, cq, to_g16<T>(a));
+                        sG.write16(t, cq, to_g16<T>(gg));
+                        if (e % GPR == 0) sH[t] = normalise ? -dov * inv : 0.f;
+                    }
+                }
+            }
+            __syncthreads();
+            // ---- intra-chunk terms (causal), then R += A^T G, r += A^T h
+            if (!TOTALS && causal) {
+#pragma unroll
+                for (int u = 0; u < MAXU; ++u) {
+                    const int unit = w + 4 * u;
+                    if (unit < NU) {
+                        f32x16 M = f32x16{};
+                        if (unit < BG::DT) {
+                            // M[t][s] = a_t . b_s for t >= s
+#pragma unroll
+                            for (int kk = 0; kk < BG::KBD; ++kk)
+                                mma(M, sA.read8(n, kk * 16 + 8 * h), sB.read8(n, kk * 16 + 8 * h));
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) M[r] = (8 * (r / 4) + 4 * h + (r % 4)) >= n ? M[r] : 0.f;
+                        } else {
+                            // M[t][s] = g_t . v_s + h_t for t >= s
+#pragma unroll
+                            for (int kk = 0; kk < BG::KBD; ++kk)
+                                mma(M, sG.read8(n, kk * 16 + 8 * h), sV.read8(n, kk * 16 + 8 * h));
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int t = 8 * (r / 4) + 4 * h + (r % 4);
+                                M[r] = t >= n ? M[r] + sH[t] : 0.f;
+                            }
+                        }
+                        // dv^T[j][s] += sum_t g_t[j] M[t][s];  dk^T[i][s] += sum_t a_t[i] M[t][s]
+                        const Tile<T, D> &src = unit < BG::DT ? sG : sA;
+                        const int col = (unit < BG::DT ? unit : unit - BG::DT) * 32;
+#pragma unroll
+                        for (int kb2 = 0; kb2 < 2; ++kb2) {
+                            const int ra = 16 * kb2 + 4 * h;
+                            mma(out[u], colfrag(src, ra, ra + 8, col, lane), acc8<T>(M, 8 * kb2));
+                        }
+                    }
+                }
+            }
+            if (TOTALS || causal) {
+#pragma unroll
+                for (int i = 0; i < BG::MAXST; ++i) {
+                    const int st = BG::tile_of(w, i);
+                    if (st < BG::NST) tile_state_update<T, D>(R[i], false, st / BG::DT, st % BG::DT, 0, sA, sG, lane);
+                }
+                if (tid < D) {
+                    float x = 0.f;
+                    for (int t = 0; t < kBC; ++t) x += sH[t] * (float)sA.p[sA.at(t, tid)];
+                    rr += x;
+                }
+            }
+            __syncthreads();
+        }
+        if (!TOTALS) {
+            // ---- carried terms and the outputs of this chunk
+#pragma unroll
+            for (int u = 0; u < MAXU; ++u) {
+                const int unit = w + 4 * u;
+                if (unit < NU) {
+                    if (unit < BG::DT) {
+                        // dv^T[j][s] += sum_i R[i][j] b_s[i]
+#pragma unroll
+                        for (int kk = 0; kk < BG::KBD; ++kk) {
+                            const int ra = kk * 16 + 8 * h;
+                            mma(out[u], colfrag(sR, ra, ra + 4, unit * 32, lane), sB.read8(n, ra));
+                        }
+                    } else {
+                        // dk^T[i][s] += sum_j R[i][j] v_s[j]
+#pragma unroll
+                        for (int kk = 0; kk < BG::KBD; ++kk)
+                            mma(out[u], sR.read8((unit - BG::DT) * 32 + n, kk * 16 + 8 * h), sV.read8(n, kk * 16 + 8 * h));
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < MAXU; ++u) {
+                const int unit = w + 4 * u;
+                if (unit < NU) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int f = (unit < BG::DT ? unit : unit - BG::DT) * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                        if (unit < BG::DT) {
+                            sOV.p[sOV.at(n, f)] = (T)out[u][r];
+                        } else {
+                            const float dbv = out[u][r] + sr[f];
+                            sOK.p[sOK.at(n, f)] = (T)(dbv * fminf(1.f, (float)sB.p[sB.at(n, f)]));
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            const Rsrc rdk = make_rsrc(dk + ((size_t)sq * N + t0) * D, bytes);
+            const Rsrc rdv = make_rsrc(dv + ((size_t)sq * N + t0) * D, bytes);
+#pragma unroll
+            for (int l = 0; l < LDV; ++l) {
+                const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
+                if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
+                    buf_store16<g16>(rdk, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sOK.p + sOK.at(t, cq)));
+                    buf_store16<g16>(rdv, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sOV.p + sOV.at(t, cq)));
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (TOTALS) {
+        float *dst = ws_r + ((size_t)sq * nslots + (blockIdx.x % nslots)) * (size_t)D * (D + 1);
+#pragma unroll
+        for (int i = 0; i < BG::MAXST; ++i) {
+            const int st = BG::tile_of(w, i);
+            if (st < BG::NST) {
+                const int it = st / BG::DT, jt = st % BG::DT;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dst[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n] = R[i][r];
+            }
+        }
+        if (tid < D) dst[(size_t)D * D + tid] = rr;
+    }
+}
+
+// ------------------------------------------------------------------ plan
+
+struct BwdPlan {
+    int nseq, G, P, seg_len, fwd_slots, r_slots;
+    size_t off_den, off_r, bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int bwd_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, BwdPlan *pl)
+{
+    if (B < 0 || H <= 0 || Hkv <= 0 || N < 0 || H % Hkv != 0) return LINATTN_ERR_SHAPE;
+    if (dtype != LINATTN_F32 && dtype != LINATTN_BF16) return LINATTN_ERR_DTYPE;
+    if (d != 32 && d != 64 && d != 128) return LINATTN_ERR_UNSUPPORTED;
+    const int e = dtype == LINATTN_BF16 ? 2 : 4;
+    if ((long long)N * d * e > 0x7fffffffLL) return LINATTN_ERR_SHAPE;
+    BwdPlan p{};
+    p.nseq = B * Hkv;
+    p.G = H / Hkv;
+    // Segments: about 512 workgroups for the dk/dv walk (one per sequence and
+    // segment), segments whole chunks of 32 tokens.
+    const int nchunks = (N + kBC - 1) / kBC;
+    int P = p.nseq > 0 ? (512 + p.nseq - 1) / p.nseq : 1;
+    if (P > nchunks) P = nchunks;
+    if (P < 1) P = 1;
+    p.seg_len = ((nchunks + P - 1) / P) * kBC;
+    p.P = N > 0 ? (N + p.seg_len - 1) / p.seg_len : 1;
+    p.fwd_slots = causal ? p.P - 1 : p.P;
+    p.r_slots = p.fwd_slots;
+    const size_t part = (size_t)d * (d + 1) * 4;
+    const size_t fwd = align256((size_t)p.nseq * p.fwd_slots * part);
+    p.off_den = fwd;
+    p.off_r = p.off_den + align256((size_t)B * H * N * 4);
+    p.bytes = p.off_r + align256((size_t)p.nseq * p.r_slots * part);
+    *pl = p;
+    return LINATTN_OK;
+}
+
+template <typename T, int D>
+int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void *k, const void *v, const void *o,
+            const void *dout, void *dq, void *dk, void *dv, int causal, int normalise, char *ws, hipStream_t st)
+{
+    const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k), *vv = static_cast<const T *>(v);
+    const T *oo = static_cast<const T *>(o ? o : q);  // not read when normalise == 0
+    const T *dd = static_cast<const T *>(dout);
+    float *wf = reinterpret_cast<float *>(ws);
+    float *wden = reinterpret_cast<float *>(ws + pl.off_den);
+    float *wr = reinterpret_cast<float *>(ws + pl.off_r);
+    const int P = pl.P, E = D * D + D;
+    const int c1 = totals_chunk<T, D>(pl.seg_len);
+    // 1. forward sums at the segment starts (or their total)
+    if (causal) {
+        if (P > 1 && launch_totals<T, D>(c1, pl.nseq * (P - 1), st, kk, vv, wf, N, pl.seg_len, P - 1))
+            return LINATTN_ERR_UNSUPPORTED;
+        if (P > 2)
+            hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, wf,
+                               P - 1, D, 0, (float *)nullptr, (float *)nullptr, (const float *)nullptr,
+                               (const float *)nullptr);
+    } else {
+        if (launch_totals<T, D>(c1, pl.nseq * P, st, kk, vv, wf, N, pl.seg_len, P)) return LINATTN_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, wf, P, D,
+                           1, (float *)nullptr, (float *)nullptr, (const float *)nullptr, (const float *)nullptr);
+    }
+    // 2. dq (and den)
+    hipLaunchKernelGGL((k_bwd_dq<T, D>), dim3(pl.nseq * pl.G * P), dim3(kThreads), 0, st, qq, kk, vv, oo, dd,
+                       static_cast<T *>(dq), wden, (const float *)wf, H, Hkv, N, pl.G, P, pl.seg_len, causal,
+                       normalise);
+    // 3. sums of a g^T and h a per segment: causal segments 1..P-1, suffix scan
+    if (causal) {
+        if (P > 1) {
+            hipLaunchKernelGGL((k_bwd_dkv<T, D, true>), dim3(pl.nseq * (P - 1)), dim3(kThreads), 0, st, qq, kk, vv,
+                               oo, dd, (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P,
+                               pl.seg_len, causal, normalise, P - 1, 1);
+            if (P > 2)
+                hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st,
+                                   wr, P - 1, D, 2, (float *)nullptr, (float *)nullptr, (const float *)nullptr,
+                                   (const float *)nullptr);
+        }
+    } else {
+        hipLaunchKernelGGL((k_bwd_dkv<T, D, true>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo, dd,
+                           (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P, pl.seg_len,
+                           causal, normalise, P, 0);
+        hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, wr, P, D,
+                           1, (float *)nullptr, (float *)nullptr, (const float *)nullptr, (const float *)nullptr);
+    }
+    // 4. dk, dv
+    hipLaunchKernelGGL((k_bwd_dkv<T, D, false>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo, dd,
+                       (const float *)wden, static_cast<T *>(dk), static_cast<T *>(dv), wr, H, Hkv, N, pl.G, P,
+                       pl.seg_len, causal, normalise, P, 0);
+    return launch_status();
+}
+
+template <typename T>
+int dispatch_bwd(const BwdPlan &pl, int d, int H, int Hkv, int N, const void *q, const void *k, const void *v,
+                 const void *o, const void *dout, void *dq, void *dk, void *dv, int causal, int normalise, char *ws,
+                 hipStream_t st)
+{
+    switch (d) {
+    case 32: return run_bwd<T, 32>(pl, H, Hkv, N, q, k, v, o, dout, dq, dk, dv, causal, normalise, ws, st);
+    case 64: return run_bwd<T, 64>(pl, H, Hkv, N, q, k, v, o, dout, dq, dk, dv, causal, normalise, ws, st);
+    case 128: return run_bwd<T, 128>(pl, H, Hkv, N, q, k, v, o, dout, dq, dk, dv, causal, normalise, ws, st);
+    }
+    return LINATTN_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t linattn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int causal, int dtype)
+{
+    BwdPlan pl;
+    if (bwd_plan(B, H, Hkv, N, d, causal ? 1 : 0, dtype, &pl) != LINATTN_OK) return (size_t)-1;
+    return pl.bytes;
+}
+
+int linattn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout, void *dq, void *dk,
+                void *dv, int B, int H, int Hkv, int N, int d, int causal, int normalise, int dtype, void *workspace,
+                size_t workspace_bytes, hipStream_t stream)
+{
+    BwdPlan pl;
+    causal = causal ? 1 : 0;
+    normalise = normalise ? 1 : 0;
+    const int rc = bwd_plan(B, H, Hkv, N, d, causal, dtype, &pl);
+    if (rc != LINATTN_OK) return rc;
+    if (B == 0 || N == 0) return LINATTN_OK;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || (normalise && !out)) return LINATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+        return LINATTN_ERR_ALIGN;
+    if (!workspace || workspace_bytes < pl.bytes) return LINATTN_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    if (dtype == LINATTN_BF16)
+        return dispatch_bwd<bf16>(pl, d, H, Hkv, N, q, k, v, out, dout, dq, dk, dv, causal, normalise, ws, stream);
+    return dispatch_bwd<float>(pl, d, H, Hkv, N, q, k, v, out, dout, dq, dk, dv, causal, normalise, ws, stream);
+}
+
+}  // extern "C"

@@ -6,8 +6,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (LINATTN_BF16, LINATTN_F32, LinattnError, linattn_decode_step, linattn_fwd, linattn_fwd_from_state,
-               linattn_fwd_workspace_bytes)
+from . import (LINATTN_BF16, LINATTN_F32, LinattnError, linattn_bwd, linattn_bwd_workspace_bytes,
+               linattn_decode_step, linattn_fwd, linattn_fwd_from_state, linattn_fwd_workspace_bytes)
 
 _DT = {torch.float32: LINATTN_F32, torch.bfloat16: LINATTN_BF16}
 
@@ -60,6 +60,29 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=True, normalis
     if rc != 0:
         raise LinattnError(rc, "linattn_fwd")
     return (out, S, z) if want_state else out
+
+
+def bwd(q, k, v, out, dout, causal=True, normalise=True, ws=None, stream=None, grads=None):
+    """dQ, dK, dV through ``linattn_bwd``; q/out/dout [B,H,N,d], k/v [B,Hkv,N,d] on the GPU."""
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    for t in (q, k, v, dout) + ((out,) if normalise else ()):
+        if not (t.is_cuda and t.is_contiguous() and t.dtype == q.dtype):
+            raise ValueError("q, k, v, out, dout must be contiguous device tensors of one dtype")
+    if k.shape != (B, Hkv, N, d) or v.shape != (B, Hkv, N, d) or dout.shape != q.shape:
+        raise ValueError("k, v must be [B, Hkv, N, d] and dout [B, H, N, d]")
+    code = dtype_code(q.dtype)
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    nbytes = linattn_bwd_workspace_bytes(B, H, Hkv, N, d, causal, code)
+    if nbytes < 0:
+        raise LinattnError(-2, "linattn_bwd_workspace_bytes")
+    if ws is None:
+        ws = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=q.device)
+    rc = linattn_bwd(q, k, v, out if normalise else None, dout, dq, dk, dv, B, H, Hkv, N, d, causal, normalise, code,
+                     ws, ws.numel() * 4, stream)
+    if rc != 0:
+        raise LinattnError(rc, "linattn_bwd")
+    return dq, dk, dv
 
 
 def decode_step(state: torch.Tensor, z: torch.Tensor | None, q, k, v, normalise=True, out=None, stream=None):

@@ -149,3 +149,18 @@ def test_auto_chunk_choices():
                     rc, c, P = la.linattn_fwd_plan(2, 2 * G, 2, 1000, d, causal, dt, 0)
                     assert rc == 0 and c in (32, 64, 128, 256), (dt, d, G, causal, rc, c)
                     assert la.linattn_fwd_workspace_bytes(2, 2 * G, 2, 1000, d, causal, dt) >= 0
+
+
+def test_bwd_workspace_and_validation_without_gpu():
+    """Argument checks of the backward run before any launch."""
+    f32, bf = la.LINATTN_F32, la.LINATTN_BF16
+    assert la.linattn_bwd_workspace_bytes(1, 2, 2, 64, 48, 1, f32) == -1       # d not supported
+    assert la.linattn_bwd_workspace_bytes(1, 3, 2, 64, 64, 1, f32) == -1       # H % Hkv != 0
+    assert la.linattn_bwd_workspace_bytes(1, 2, 2, 64, 64, 1, 7) == -1         # dtype
+    # causal: forward sums, den and the suffix sums of (P - 1) segments; grows with B*H*N for den
+    a = la.linattn_bwd_workspace_bytes(2, 8, 8, 4096, 64, 1, f32)
+    b = la.linattn_bwd_workspace_bytes(2, 8, 8, 8192, 64, 1, bf)
+    assert 0 < a < b
+    assert la.linattn_bwd(None, None, None, None, None, None, None, None, 0, 2, 2, 64, 64, 1, 1, f32, stream=0) == 0
+    assert la.linattn_bwd(None, None, None, None, None, None, None, None, 1, 2, 2, 64, 64, 1, 1, f32, stream=0) == -1
+    assert la.linattn_bwd(None, None, None, None, None, None, None, None, 1, 2, 2, 64, 40, 1, 1, f32, stream=0) == -4
