@@ -330,6 +330,85 @@ def pieces_row(la, hip, torch, w, pieces, steps):
             "roofline_path": roofline(nb, fl, ms / 1e3, w.dtype, "whole chain (graph replay, events)")}
 
 
+def bwd_bytes(w) -> int:
+    """Algorithmic HBM bytes of the backward: q, o, dO read and dq written per query
+    head; k, v read and dk, dv written per kv head (each once)."""
+    e = 2 if w.dtype == "bf16" else 4
+    return w.B * w.N * w.d * e * (4 * w.H + 4 * w.Hkv)
+
+
+def bwd_row(la, hip, torch, w, causal, steps):
+    """linattn_bwd on a workload: all its launches as one step, K steps in one HIP graph."""
+    from linattn_inputs import randn, workload_qkv
+    from sequence_mixing_amd import ops
+
+    q, k, v = (t.cuda() for t in workload_qkv(w))
+    dout = randn((w.B, w.H, w.N, w.d), w.seed + 1).to(q.dtype).cuda()
+    out = ops.fwd(q, k, v, causal=causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dt = la.LINATTN_BF16 if w.dtype == "bf16" else la.LINATTN_F32
+    nb = la.linattn_bwd_workspace_bytes(w.B, w.H, w.Hkv, w.N, w.d, causal, dt)
+    ws = torch.empty(nb // 4 + 1, dtype=torch.float32, device="cuda")
+
+    def call(st):
+        rc = la.linattn_bwd(q, k, v, out, dout, dq, dk, dv, w.B, w.H, w.Hkv, w.N, w.d, causal, 1, dt, ws, nb, st)
+        if rc != 0:
+            raise la.LinattnError(rc, "linattn_bwd")
+
+    call(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (dq, dk, dv)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream().cuda_stream
+        for _ in range(steps):
+            call(cap)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    g.replay()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(e0, e1) / steps
+    same = all(torch.equal(a, b) for a, b in zip(ref, (dq, dk, dv)))
+    del g
+    nb_alg = bwd_bytes(w)
+    return {"causal": bool(causal), "ms_per_step": round(ms, 5), "tokens_per_s": round(w.B * w.N / (ms / 1e3), 1),
+            "graph_matches_eager": same,
+            "roofline_path": roofline(nb_alg, 0.0, ms / 1e3, w.dtype, "whole backward (graph replay, events)")}
+
+
+def bwd_oracle(w, causal, seconds, max_tokens=1024):
+    """The fp64 oracle's backward on the first `max_tokens` tokens of every sequence."""
+    import numpy as np
+
+    import oracle
+    from linattn_inputs import randn, workload_qkv
+
+    n = min(w.N, max_tokens)
+    q, k, v = (np.ascontiguousarray(t[:, :, :n].double().numpy()) for t in workload_qkv(w))
+    dout = np.ascontiguousarray(randn((w.B, w.H, w.N, w.d), w.seed + 1)[:, :, :n].double().numpy())
+    threads = oracle.default_threads()
+    o = oracle.ref_fwd(q, k, v, causal=bool(causal), nthreads=threads)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.ref_bwd(q, k, v, o, dout, causal=bool(causal), nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    return {"value": round(w.B * n * reps / el, 1), "unit": "tokens/s", "cores": min(threads, w.B * w.Hkv),
+            "kind": "oracle", "sample": f"backward of the first {n} of {w.N} tokens of all {w.B * w.Hkv} sequences, "
+                                        f"{reps} reps in {el:.1f} s"}
+
+
 def decode_row(la, hip, torch, steps_total, stream):
     """GQA prefill (N=32768), state replicated into 64 slots, 1024 decode steps."""
     from linattn_inputs import DECODE, WORKLOADS, DecodeStream, workload_qkv
@@ -516,6 +595,11 @@ def main():
             log(name, json.dumps(rows[name]))
         rows["cfg5_prefill_4_pieces"] = pieces_row(la, hip, torch, WORKLOADS["cfg5"], 4, 20)
         log("cfg5_prefill_4_pieces", json.dumps(rows["cfg5_prefill_4_pieces"]))
+        for name, key in (("cfg2_bwd", "cfg2"), ("cfg3_bwd", "cfg3"), ("cfg5_bwd", "cfg5")):
+            rows[name] = bwd_row(la, hip, torch, WORKLOADS[key], 1, 10)
+            if args.cpu_seconds > 0:
+                rows[name]["cpu_oracle"] = bwd_oracle(WORKLOADS[key], 1, min(2.0, args.cpu_seconds))
+            log(name, json.dumps(rows[name]))
         rows["cfg5_decode"] = decode_row(la, hip, torch, 1024, stream)
         if args.cpu_seconds > 0:
             rows["cfg5_decode"]["cpu_oracle"] = decode_oracle(min(2.0, args.cpu_seconds))

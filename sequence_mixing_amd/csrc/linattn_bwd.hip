@@ -16,12 +16,16 @@
 // heads of the kv group (non-causal: every sum runs over the whole sequence).
 // phi'(x) = 1 for x > 0 and exp(x) = phi(x) otherwise, i.e. min(1, phi(x)).
 //
+// Workgroups hand data over through LDS with lds_barrier(), which leaves the
+// global loads of the next head or chunk in flight across the barrier.
+//
 // Launches (one workgroup = 4 wave64s; chunks of 32 tokens):
 //   seg_totals, seg_scan   the forward's segment sums of b v^T and b, giving
 //                          each dq segment its starting S and z;
-//   bwd_dq                 per (sequence, query head, segment): walks the
-//                          segment forwards.  Per chunk, on MFMA:
-//                          den (1 . masked B A^T plus a . z), then
+//   bwd_dq                 per (sequence, segment): walks the segment
+//                          forwards, serving the G query heads of the group.
+//                          Per chunk: z_t of every token (LDS prefix); per
+//                          head: den = a . z_t, then on MFMA
 //                          dA^T = B^T (M .* (V G^T + h)) + S G^T; writes dq
 //                          and den (kept for the next passes);
 //   bwd_dkv<totals>        per (sequence, segment): sum of a g^T and h a over
@@ -109,11 +113,52 @@ __device__ __forceinline__ void publish_tile(const f32x16 &acc, Tile<T, D> t, in
     for (int r = 0; r < 16; ++r) t.p[t.at(it * 32 + 8 * (r / 4) + 4 * h + (r % 4), jt * 32 + n)] = (T)acc[r];
 }
 
+// Buffer descriptor from values that are the same in every lane (chunk start,
+// row counts): read from the first lane, so the descriptor stays in scalar
+// registers even where the compiler computed its fields with vector
+// instructions (a descriptor in vector registers makes it loop over lanes).
+__device__ __forceinline__ Rsrc make_rsrc_u(const void *base, int bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return make_rsrc(reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(bytes));
+}
+
+// Loads one chunk of a [N][D] row-major sequence (tokens t0 .. t0 + rows - 1;
+// zeros elsewhere, also for rows <= 0, without touching memory).
+template <typename T, int D, int L>
+__device__ __forceinline__ void load_rows(typename Vt<T>::g16 (&r)[L], const T *base, int t0, int rows, int tid)
+{
+    using g16 = typename Vt<T>::g16;
+    static_assert(L == BGeo<T, D>::LDV, "register array size");
+    const Rsrc rs = make_rsrc_u(base + (size_t)t0 * D, rows > 0 ? rows * D * (int)sizeof(T) : 0);
+#pragma unroll
+    for (int l = 0; l < L; ++l) r[l] = buf_load16<g16>(rs, (unsigned)(tid + l * kThreads) * 16u);
+}
+
+// One float per staged group: x[t0 + row of the group] (zero past rows).
+template <typename T, int D, int L>
+__device__ __forceinline__ void load_row_scalars(float (&r)[L], const float *base, int t0, int rows, int tid)
+{
+    using BG = BGeo<T, D>;
+    static_assert(L == BG::LDV, "register array size");
+    const Rsrc rs = make_rsrc_u(base + t0, rows > 0 ? rows * 4 : 0);
+#pragma unroll
+    for (int l = 0; l < BG::LDV; ++l) {
+        const int e = tid + l * kThreads;
+        r[l] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (unsigned)(e / BG::GPR) * 4u, 0, 0));
+    }
+}
+
 // ----------------------------------------------------------------- bwd_dq
 //
-// S (d x d, fp32) lives in MFMA accumulators over the four waves as in the
-// forward; the waves read it through an LDS copy refreshed once per chunk.
-// z lives in LDS (two copies: before and after the chunk).
+// One workgroup per (batch, kv head, segment) walks the segment forwards and
+// serves the G query heads of the group.  Per chunk: phi(k), v to LDS, the
+// state copy S (d x d, fp32 in MFMA accumulators over the four waves) and the
+// inclusive z_t of every token.  Per head: den_t = phi(q_t) . z_t, g, h, then
+// dA^T on MFMA.  The next head's (or chunk's) rows are requested into
+// registers while the current one is computed.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void k_bwd_dq(const T *__restrict__ q, const T *__restrict__ k,
                                                       const T *__restrict__ v, const T *__restrict__ o,
@@ -124,36 +169,36 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(const T *__restrict__ q, co
 {
     using BG = BGeo<T, D>;
     using g16 = typename Vt<T>::g16;
-    constexpr int U = BG::U, GPR = BG::GPR, LDV = BG::LDV, E = BG::E;
-    __shared__ __attribute__((aligned(16))) T smA[kBC * D];
-    __shared__ __attribute__((aligned(16))) T smB[kBC * D];
-    __shared__ __attribute__((aligned(16))) T smV[kBC * D];
-    __shared__ __attribute__((aligned(16))) T smG[kBC * D];
-    __shared__ __attribute__((aligned(16))) T smO[kBC * D];
-    __shared__ __attribute__((aligned(16))) T smS[D * D];
+    constexpr int U = BG::U, GPR = BG::GPR, LDV = BG::LDV;
     // bf16: low parts of b and g.  dq of the first tokens of a normalised
     // sequence is a small difference of the value and normaliser terms, so the
     // intra-chunk products take both operands split (see to_g16_lo).
     constexpr bool SPLIT = sizeof(T) == 2;
+    __shared__ __attribute__((aligned(16))) T smB[kBC * D];
+    __shared__ __attribute__((aligned(16))) T smV[kBC * D];
+    __shared__ __attribute__((aligned(16))) T smS[D * D];
+    __shared__ __attribute__((aligned(16))) T smA[kBC * D];
+    __shared__ __attribute__((aligned(16))) T smG[kBC * D];
+    // fp32 at d = 128 would exceed the 160 KiB of LDS with its own output
+    // tile: the dq rows then go into the g tile, after a barrier.
+    constexpr bool OWN_O = !(sizeof(T) == 4 && D == 128);
+    __shared__ __attribute__((aligned(16))) T smO[OWN_O ? kBC * D : 8];
     __shared__ __attribute__((aligned(16))) T smBl[SPLIT ? kBC * D : 8];
     __shared__ __attribute__((aligned(16))) T smGl[SPLIT ? kBC * D : 8];
-    __shared__ float sZ[2][D];
-    __shared__ float sDen0[kBC], sDen[kBC], sDov[kBC], sH[kBC];
-    const Tile<T, D> sA{smA}, sB{smB}, sV{smV}, sG{smG}, sO{smO}, sS{smS}, sBl{smBl}, sGl{smGl};
+    __shared__ __attribute__((aligned(16))) float sZt[kBC * D];  // z_t of every token of the chunk, [t][i]
+    __shared__ float sZp[D];                                      // z before the chunk
+    __shared__ float sH[kBC];
+    const Tile<T, D> sA{smA}, sB{smB}, sV{smV}, sG{smG}, sO{OWN_O ? smO : smG}, sS{smS}, sBl{smBl}, sGl{smGl};
 
-    const int p = blockIdx.x % P;
-    const int qh = blockIdx.x / P;  // b * H + head
-    const int b = qh / H, head = qh % H, g = head / G;
-    const int sq = b * Hkv + g;     // (batch, kv head) sequence
+    const int sq = blockIdx.x / P, p = blockIdx.x % P;  // (batch, kv head) sequence, segment
+    const int bb = sq / Hkv, g = sq % Hkv;
+    const int qh0 = bb * H + g * G;                       // first query head of the group
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
-    const T *qb = q + (size_t)qh * N * D;
-    const T *ob = o + (size_t)qh * N * D;
-    const T *db = dout + (size_t)qh * N * D;
-    T *dqb = dq + (size_t)qh * N * D;
     const T *kb = k + (size_t)sq * N * D;
     const T *vb = v + (size_t)sq * N * D;
     const int s0 = p * seg_len, s1 = min(N, s0 + seg_len);
     const int nch = (s1 - s0 + kBC - 1) / kBC;
+    auto rows_of = [&](int c) { return c < nch ? min(kBC, s1 - (s0 + c * kBC)) : 0; };
 
     // Starting sums: causal segment p > 0 reads the inclusive prefix of the
     // segments before it (slot p - 1); non-causal reads the total (slot 0).
@@ -172,163 +217,170 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(const T *__restrict__ q, co
                 S[i][r] = init[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n];
         }
     }
-    for (int i = tid; i < D; i += kThreads) sZ[0][i] = init ? init[(size_t)D * D + i] : 0.f;
+    float zrun = (init && tid < D) ? init[(size_t)D * D + tid] : 0.f;
     if (!causal) {
-        // the sums are the same for every chunk: one copy
+        // the sums are the same for every token: one copy of S, z_t = z
 #pragma unroll
         for (int i = 0; i < BG::MAXST; ++i) {
             const int st = BG::tile_of(w, i);
             if (st < BG::NST) publish_tile<T, D>(S[i], sS, st / BG::DT, st % BG::DT, lane);
         }
+        for (int i = tid; i < D; i += kThreads) sZp[i] = init[(size_t)D * D + i];
+        for (int e = tid; e < kBC * D; e += kThreads) sZt[e] = init[(size_t)D * D + e % D];
     }
-    __syncthreads();
 
-    g16 dr[LDV];
+    g16 kr[LDV], vr[LDV], qr[LDV], orr[LDV], dr[LDV];
+    load_rows<T, D>(kr, kb, s0, rows_of(0), tid);
+    load_rows<T, D>(vr, vb, s0, rows_of(0), tid);
+    load_rows<T, D>(qr, q + (size_t)qh0 * N * D, s0, rows_of(0), tid);
+    load_rows<T, D>(orr, o + (size_t)qh0 * N * D, s0, normalise ? rows_of(0) : 0, tid);
+    load_rows<T, D>(dr, dout + (size_t)qh0 * N * D, s0, rows_of(0), tid);
+
     for (int c = 0; c < nch; ++c) {
-        const int t0 = s0 + c * kBC, rows = min(kBC, s1 - t0);
-        const int zc = causal ? (c & 1) : 0;
-        // ---- stage: phi(q), phi(k), v to LDS; dO kept in registers; row dots
-        {
-            const unsigned bytes = (unsigned)(rows * D * E);
-            const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, bytes), rk = make_rsrc(kb + (size_t)t0 * D, bytes);
-            const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, bytes), rd = make_rsrc(db + (size_t)t0 * D, bytes);
-            const Rsrc ro = make_rsrc(ob + (size_t)t0 * D, normalise ? bytes : 0u);
-            g16 qr[LDV], kr[LDV], vr[LDV], orr[LDV];
+        const int t0 = s0 + c * kBC, rows = rows_of(c);
+        // ---- phi(k), v of the chunk to LDS; the next chunk's rows requested
 #pragma unroll
-            for (int l = 0; l < LDV; ++l) {
-                const unsigned off = (unsigned)(tid + l * kThreads) * 16u;
-                qr[l] = buf_load16<g16>(rq, off);
-                kr[l] = buf_load16<g16>(rk, off);
-                vr[l] = buf_load16<g16>(rv, off);
-                dr[l] = buf_load16<g16>(rd, off);
-                orr[l] = buf_load16<g16>(ro, off);
-            }
+        for (int l = 0; l < LDV; ++l) {
+            const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
+            if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
+                float bk[U];
 #pragma unroll
-            for (int l = 0; l < LDV; ++l) {
-                const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
-                float a[U], bk[U], dinter = 0.f, dov = 0.f;
-#pragma unroll
-                for (int i = 0; i < U; ++i) {
-                    a[i] = phi((float)qr[l][i]);
-                    bk[i] = t < rows ? phi((float)kr[l][i]) : 0.f;
-                    dov += (float)dr[l][i] * (float)orr[l][i];
-                }
-                if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
-#pragma unroll
-                    for (int i = 0; i < U; ++i) dinter += a[i] * sZ[zc][cq + i];
-                    sA.write16(t, cq, to_g16<T>(a));
-                    sB.write16(t, cq, to_g16<T>(bk));
-                    if constexpr (SPLIT) sBl.write16(t, cq, to_g16_lo<T>(bk));
-                    sV.write16(t, cq, vr[l]);
-                }
-                dinter = row_sum<GPR>(dinter);
-                dov = row_sum<GPR>(dov);
-                if ((BG::NGRP % kThreads == 0 || e < BG::NGRP) && e % GPR == 0) {
-                    sDen0[t] = dinter;
-                    sDov[t] = dov;
-                }
+                for (int i = 0; i < U; ++i) bk[i] = t < rows ? phi((float)kr[l][i]) : 0.f;
+                sB.write16(t, cq, to_g16<T>(bk));
+                if constexpr (SPLIT) sBl.write16(t, cq, to_g16_lo<T>(bk));
+                sV.write16(t, cq, vr[l]);
             }
         }
-        __syncthreads();
-        // ---- den (wave 0), S copy before this chunk, z after it
-        if (w == 0 && normalise) {
-            float intra = 0.f;
-            if (causal) {
-                f32x16 Pt = f32x16{};  // Pt[s][t] = b_s . a_t
-#pragma unroll
-                for (int kk = 0; kk < BG::KBD; ++kk) mma(Pt, sB.read8(n, kk * 16 + 8 * h), sA.read8(n, kk * 16 + 8 * h));
-#pragma unroll
-                for (int r = 0; r < 16; ++r) intra += (8 * (r / 4) + 4 * h + (r % 4)) <= n ? Pt[r] : 0.f;
-                intra += __shfl_xor(intra, 32);
-            }
-            if (h == 0) sDen[n] = sDen0[n] + intra;
-        }
+        load_rows<T, D>(kr, kb, t0 + kBC, rows_of(c + 1), tid);
+        load_rows<T, D>(vr, vb, t0 + kBC, rows_of(c + 1), tid);
         if (causal) {
 #pragma unroll
             for (int i = 0; i < BG::MAXST; ++i) {
                 const int st = BG::tile_of(w, i);
                 if (st < BG::NST) publish_tile<T, D>(S[i], sS, st / BG::DT, st % BG::DT, lane);
             }
-            for (int i = tid; i < D; i += kThreads) {
-                float zz = sZ[zc][i];
-                for (int t = 0; t < kBC; ++t) {
-                    zz += (float)sB.p[sB.at(t, i)];
-                    if constexpr (SPLIT) zz += (float)sBl.p[sBl.at(t, i)];
-                }
-                sZ[zc ^ 1][i] = zz;
-            }
         }
-        __syncthreads();
-        // ---- g and h
-#pragma unroll
-        for (int l = 0; l < LDV; ++l) {
-            const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
-            if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
-                const float den = normalise ? sDen[t] : 1.f;
-                const float inv = t < rows ? 1.f / den : 0.f;
-                float gg[U];
-#pragma unroll
-                for (int i = 0; i < U; ++i) gg[i] = (float)dr[l][i] * inv;
-                sG.write16(t, cq, to_g16<T>(gg));
-                if constexpr (SPLIT) sGl.write16(t, cq, to_g16_lo<T>(gg));
-                if (e % GPR == 0) {
-                    sH[t] = normalise ? -sDov[t] * inv : 0.f;
-                    if (normalise && t < rows) den_out[(size_t)qh * N + t0 + t] = den;
-                }
+        lds_barrier();
+        // ---- z before the chunk and z_t after each of its tokens
+        if (causal && tid < D) {
+            float z = zrun;
+            sZp[tid] = z;
+            for (int t = 0; t < kBC; ++t) {
+                z += (float)sB.p[sB.at(t, tid)];
+                if constexpr (SPLIT) z += (float)sBl.p[sBl.at(t, tid)];
+                sZt[t * D + tid] = z;
             }
+            zrun = z;
         }
-        __syncthreads();
-        // ---- dA^T tiles (one 32-feature block per unit) and the state update
-        for (int it = w; it < BG::DT; it += 4) {
-            f32x16 acc = f32x16{};
-            const float hn = sH[n];
-            if (causal) {
-                f32x16 M = f32x16{};  // M[s][t] = v_s . g_t + h_t for s <= t
+        lds_barrier();
+        for (int hh = 0; hh < G; ++hh) {
+            const int qh = qh0 + hh;
+            // ---- a, den, g, h of this head; the next head's rows requested
+            {
+                const Rsrc rden = make_rsrc_u(den_out + (size_t)qh * N + t0, normalise ? rows * 4 : 0);
 #pragma unroll
-                for (int kk = 0; kk < BG::KBD; ++kk) {
-                    const auto vf = sV.read8(n, kk * 16 + 8 * h);
-                    mma(M, vf, sG.read8(n, kk * 16 + 8 * h));
-                    if constexpr (SPLIT) mma(M, vf, sGl.read8(n, kk * 16 + 8 * h));
+                for (int l = 0; l < LDV; ++l) {
+                    const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
+                    const bool grp = BG::NGRP % kThreads == 0 || e < BG::NGRP;
+                    float a[U], den = 0.f, dov = 0.f;
+#pragma unroll
+                    for (int i = 0; i < U; ++i) {
+                        a[i] = phi((float)qr[l][i]);
+                        dov += (float)dr[l][i] * (float)orr[l][i];
+                    }
+                    if (grp) {
+#pragma unroll
+                        for (int i = 0; i < U; ++i) den += a[i] * sZt[t * D + cq + i];
+                    }
+                    den = row_sum<GPR>(den);
+                    dov = row_sum<GPR>(dov);
+                    const float inv = t < rows ? (normalise ? 1.f / den : 1.f) : 0.f;
+                    float gg[U];
+#pragma unroll
+                    for (int i = 0; i < U; ++i) gg[i] = (float)dr[l][i] * inv;
+                    if (grp) {
+                        sA.write16(t, cq, to_g16<T>(a));
+                        sG.write16(t, cq, to_g16<T>(gg));
+                        if constexpr (SPLIT) sGl.write16(t, cq, to_g16_lo<T>(gg));
+                        if (e % GPR == 0) sH[t] = normalise ? -dov * inv : 0.f;
+                    }
+                    // den for the dk/dv pass (one lane per row; the others' offsets are out of range)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, den), rden,
+                                                          (grp && e % GPR == 0) ? (unsigned)t * 4u : kOutOfRange, 0, 0);
                 }
+                const int nh = hh + 1 < G ? hh + 1 : 0, nc = hh + 1 < G ? c : c + 1;
+                const size_t nq = (size_t)(qh0 + nh) * N * D;
+                const int nt0 = s0 + nc * kBC, nrows = rows_of(nc);
+                load_rows<T, D>(qr, q + nq, nt0, nrows, tid);
+                load_rows<T, D>(orr, o + nq, nt0, normalise ? nrows : 0, tid);
+                load_rows<T, D>(dr, dout + nq, nt0, nrows, tid);
+            }
+            lds_barrier();
+            // ---- dA^T tiles (one 32-feature block per unit); the state update after the last head
+            constexpr int MAXI = (BG::DT + 3) / 4;
+            f32x16 dacc[MAXI];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) M[r] = (8 * (r / 4) + 4 * h + (r % 4)) <= n ? M[r] + hn : 0.f;
+            for (int ui = 0; ui < MAXI; ++ui) {
+                const int it = w + 4 * ui;
+                if (it >= BG::DT) break;
+                f32x16 acc = f32x16{};
+                const float hn = sH[n];
+                if (causal) {
+                    f32x16 M = f32x16{};  // M[s][t] = v_s . g_t + h_t for s <= t
 #pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2) {
-                    const int ra = 16 * kb2 + 4 * h;
-                    const auto bh = colfrag(sB, ra, ra + 8, it * 32, lane);
-                    mma(acc, bh, acc8<T>(M, 8 * kb2));
-                    if constexpr (SPLIT) {
-                        mma(acc, bh, acc8_lo<T>(M, 8 * kb2));
-                        mma(acc, colfrag(sBl, ra, ra + 8, it * 32, lane), acc8<T>(M, 8 * kb2));
+                    for (int kk = 0; kk < BG::KBD; ++kk) {
+                        const auto vf = sV.read8(n, kk * 16 + 8 * h);
+                        mma(M, vf, sG.read8(n, kk * 16 + 8 * h));
+                        if constexpr (SPLIT) mma(M, vf, sGl.read8(n, kk * 16 + 8 * h));
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) M[r] = (8 * (r / 4) + 4 * h + (r % 4)) <= n ? M[r] + hn : 0.f;
+#pragma unroll
+                    for (int kb2 = 0; kb2 < 2; ++kb2) {
+                        const int ra = 16 * kb2 + 4 * h;
+                        const auto bh = colfrag(sB, ra, ra + 8, it * 32, lane);
+                        mma(acc, bh, acc8<T>(M, 8 * kb2));
+                        if constexpr (SPLIT) {
+                            mma(acc, bh, acc8_lo<T>(M, 8 * kb2));
+                            mma(acc, colfrag(sBl, ra, ra + 8, it * 32, lane), acc8<T>(M, 8 * kb2));
+                        }
                     }
                 }
+#pragma unroll
+                for (int kk = 0; kk < BG::KBD; ++kk)
+                    mma(acc, sS.read8(it * 32 + n, kk * 16 + 8 * h), sG.read8(n, kk * 16 + 8 * h));
+                dacc[ui] = acc;
             }
+            if constexpr (!OWN_O) lds_barrier();  // every read of the g tile is done
 #pragma unroll
-            for (int kk = 0; kk < BG::KBD; ++kk)
-                mma(acc, sS.read8(it * 32 + n, kk * 16 + 8 * h), sG.read8(n, kk * 16 + 8 * h));
+            for (int ui = 0; ui < MAXI; ++ui) {
+                const int it = w + 4 * ui;
+                if (it >= BG::DT) break;
+                const float hn = sH[n];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = it * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                const float da = acc[r] + hn * sZ[zc][i];
-                sO.p[sO.at(n, i)] = (T)(da * fminf(1.f, (float)sA.p[sA.at(n, i)]));
+                for (int r = 0; r < 16; ++r) {
+                    const int i = it * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                    const float da = dacc[ui][r] + hn * sZp[i];
+                    sO.p[sO.at(n, i)] = (T)(da * fminf(1.f, (float)sA.p[sA.at(n, i)]));
+                }
             }
-        }
-        if (causal) {
+            if (causal && hh == G - 1) {
 #pragma unroll
-            for (int i = 0; i < BG::MAXST; ++i) {
-                const int st = BG::tile_of(w, i);
-                if (st < BG::NST) tile_state_update<T, D>(S[i], false, st / BG::DT, st % BG::DT, 0, sB, sV, lane);
+                for (int i = 0; i < BG::MAXST; ++i) {
+                    const int st = BG::tile_of(w, i);
+                    if (st < BG::NST) tile_state_update<T, D>(S[i], false, st / BG::DT, st % BG::DT, 0, sB, sV, lane);
+                }
             }
-        }
-        __syncthreads();
-        // ---- store dq rows
-        {
-            const Rsrc rdq = make_rsrc(dqb + (size_t)t0 * D, rows * D * E);
+            lds_barrier();
+            // ---- dq rows of this head
+            {
+                const Rsrc rdq = make_rsrc_u(dq + ((size_t)qh * N + t0) * D, rows * D * (int)sizeof(T));
 #pragma unroll
-            for (int l = 0; l < LDV; ++l) {
-                const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
-                if (BG::NGRP % kThreads == 0 || e < BG::NGRP)
-                    buf_store16<g16>(rdq, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sO.p + sO.at(t, cq)));
+                for (int l = 0; l < LDV; ++l) {
+                    const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
+                    if (BG::NGRP % kThreads == 0 || e < BG::NGRP)
+                        buf_store16<g16>(rdq, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sO.p + sO.at(t, cq)));
+                }
             }
         }
     }
@@ -340,7 +392,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(const T *__restrict__ q, co
 // the segment's tokens and the group's query heads, written to ws_r.
 // Otherwise: the segment walked backwards from the sums of the later
 // segments; per chunk the intra-chunk terms of every head, then the carried
-// terms, then dk and dv are stored.
+// terms, then dk and dv are stored.  R lives in MFMA accumulators over the
+// waves; r in per-thread partial sums (column tid % D, a slice of the rows).
 template <typename T, int D, bool TOTALS>
 __global__ __launch_bounds__(kThreads) void k_bwd_dkv(const T *__restrict__ q, const T *__restrict__ k,
                                                        const T *__restrict__ v, const T *__restrict__ o,
@@ -351,26 +404,30 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv(const T *__restrict__ q, c
 {
     using BG = BGeo<T, D>;
     using g16 = typename Vt<T>::g16;
-    constexpr int U = BG::U, GPR = BG::GPR, LDV = BG::LDV, E = BG::E;
+    constexpr int U = BG::U, GPR = BG::GPR, LDV = BG::LDV;
+    constexpr int RS = kThreads / D;  // row slices of the r partial sums
     __shared__ __attribute__((aligned(16))) T smA[kBC * D];
     __shared__ __attribute__((aligned(16))) T smG[kBC * D];
     __shared__ __attribute__((aligned(16))) T smB[TOTALS ? 16 / sizeof(T) : kBC * D];
     __shared__ __attribute__((aligned(16))) T smV[TOTALS ? 16 / sizeof(T) : kBC * D];
     __shared__ __attribute__((aligned(16))) T smR[TOTALS ? 16 / sizeof(T) : D * D];
-    __shared__ float sH[kBC], sr[D];
+    __shared__ float sH[kBC], sRp[RS * D];
     const Tile<T, D> sA{smA}, sG{smG}, sB{smB}, sV{smV}, sR{smR};
     const Tile<T, D> sOK{smA}, sOV{smG};  // dk, dv rows, once the heads are done
 
     const int sq = blockIdx.x / nslots;                // (batch, kv head) sequence
     const int pseg = blockIdx.x % nslots + first_seg;  // segment
     const int bb = sq / Hkv, g = sq % Hkv;
+    const int qh0 = bb * H + g * G;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
     const int s0 = pseg * seg_len, s1 = min(N, s0 + seg_len);
     const int nch = (s1 - s0 + kBC - 1) / kBC;
     const T *kb = k + (size_t)sq * N * D;
     const T *vb = v + (size_t)sq * N * D;
+    // chunks are visited last to first: step j is chunk nch - 1 - j
+    auto t0_of = [&](int j) { return s0 + (nch - 1 - j) * kBC; };
+    auto rows_of = [&](int j) { return j < nch ? min(kBC, s1 - t0_of(j)) : 0; };
 
-    // R tiles in accumulators, r[i] in thread i (i < D).
     const float *init = nullptr;
     if (!TOTALS) {
         if (!causal) init = ws_r + (size_t)sq * P * D * (D + 1);
@@ -388,26 +445,33 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv(const T *__restrict__ q, c
                 R[i][r] = init[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n];
         }
     }
-    float rr = (init && tid < D) ? init[(size_t)D * D + tid] : 0.f;
+    // r partial: column tid % D over rows (tid / D) * (kBC / RS) ..; slice 0 holds the start value
+    const int rcol = tid % D, rsl = tid / D;
+    float rpart = (init && rsl == 0) ? init[(size_t)D * D + rcol] : 0.f;
 
-    // output units: dv^T feature block u (u < DT) or dk^T feature block u - DT
     constexpr int NU = 2 * BG::DT, MAXU = (NU + 3) / 4;
     f32x16 out[MAXU];
+    const int nheads = (!TOTALS && !causal) ? 0 : G;
 
-    for (int cc = nch - 1; cc >= 0; --cc) {
-        const int t0 = s0 + cc * kBC, rows = min(kBC, s1 - t0);
-        const unsigned bytes = (unsigned)(rows * D * E);
+    g16 kr[LDV], vr[LDV], qr[LDV], orr[LDV], dr[LDV];
+    float dn[LDV];
+    if (!TOTALS) {
+        load_rows<T, D>(kr, kb, t0_of(0), rows_of(0), tid);
+        load_rows<T, D>(vr, vb, t0_of(0), rows_of(0), tid);
+    }
+    {
+        const int r0 = nheads > 0 ? rows_of(0) : 0;
+        load_rows<T, D>(qr, q + (size_t)qh0 * N * D, t0_of(0), r0, tid);
+        load_rows<T, D>(orr, o + (size_t)qh0 * N * D, t0_of(0), normalise ? r0 : 0, tid);
+        load_rows<T, D>(dr, dout + (size_t)qh0 * N * D, t0_of(0), r0, tid);
+        load_row_scalars<T, D>(dn, den + (size_t)qh0 * N, t0_of(0), normalise ? r0 : 0, tid);
+    }
+
+    for (int j = 0; j < nch; ++j) {
+        const int t0 = t0_of(j), rows = rows_of(j);
         if (!TOTALS) {
 #pragma unroll
             for (int u = 0; u < MAXU; ++u) out[u] = f32x16{};
-            const Rsrc rk = make_rsrc(kb + (size_t)t0 * D, bytes), rv = make_rsrc(vb + (size_t)t0 * D, bytes);
-            g16 kr[LDV], vr[LDV];
-#pragma unroll
-            for (int l = 0; l < LDV; ++l) {
-                const unsigned off = (unsigned)(tid + l * kThreads) * 16u;
-                kr[l] = buf_load16<g16>(rk, off);
-                vr[l] = buf_load16<g16>(rv, off);
-            }
 #pragma unroll
             for (int l = 0; l < LDV; ++l) {
                 const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
@@ -419,57 +483,50 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv(const T *__restrict__ q, c
                     sV.write16(t, cq, vr[l]);
                 }
             }
-            // carried sums of the later tokens, as they stand before this chunk
-            if (causal || cc == nch - 1) {
+            load_rows<T, D>(kr, kb, t0_of(j + 1), rows_of(j + 1), tid);
+            load_rows<T, D>(vr, vb, t0_of(j + 1), rows_of(j + 1), tid);
+            // the carried sums of the later tokens, as they stand before this chunk
+            if (causal || j == 0) {
 #pragma unroll
                 for (int i = 0; i < BG::MAXST; ++i) {
                     const int st = BG::tile_of(w, i);
                     if (st < BG::NST) publish_tile<T, D>(R[i], sR, st / BG::DT, st % BG::DT, lane);
                 }
-                if (tid < D) sr[tid] = rr;
+                sRp[rsl * D + rcol] = rpart;
             }
-            __syncthreads();
+            lds_barrier();
         }
-        // non-causal: the carried sums are the totals and no head adds to them here
-        const int nheads = (!TOTALS && !causal) ? 0 : G;
         for (int hh = 0; hh < nheads; ++hh) {
-            const int qh = bb * H + g * G + hh;
-            // ---- stage phi(q), g, h of this head
-            {
-                const T *qb = q + ((size_t)qh * N + t0) * D, *db = dout + ((size_t)qh * N + t0) * D;
-                const T *ob = o + ((size_t)qh * N + t0) * D;
-                const Rsrc rq = make_rsrc(qb, bytes), rd = make_rsrc(db, bytes), ro = make_rsrc(ob, normalise ? bytes : 0u);
-                g16 qr[LDV], dr[LDV], orr[LDV];
+            // ---- a, g, h of this head; the next head's (or chunk's) rows requested
 #pragma unroll
-                for (int l = 0; l < LDV; ++l) {
-                    const unsigned off = (unsigned)(tid + l * kThreads) * 16u;
-                    qr[l] = buf_load16<g16>(rq, off);
-                    dr[l] = buf_load16<g16>(rd, off);
-                    orr[l] = buf_load16<g16>(ro, off);
+            for (int l = 0; l < LDV; ++l) {
+                const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
+                const bool real = t < rows;
+                const float inv = real ? (normalise ? 1.f / dn[l] : 1.f) : 0.f;
+                float a[U], gg[U], dov = 0.f;
+#pragma unroll
+                for (int i = 0; i < U; ++i) {
+                    a[i] = real ? phi((float)qr[l][i]) : 0.f;
+                    gg[i] = (float)dr[l][i] * inv;
+                    dov += (float)dr[l][i] * (float)orr[l][i];
                 }
-#pragma unroll
-                for (int l = 0; l < LDV; ++l) {
-                    const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
-                    const bool real = t < rows;
-                    const float dn = (normalise && real && (BG::NGRP % kThreads == 0 || e < BG::NGRP))
-                                         ? den[(size_t)qh * N + t0 + t] : 1.f;
-                    const float inv = real ? 1.f / dn : 0.f;
-                    float a[U], gg[U], dov = 0.f;
-#pragma unroll
-                    for (int i = 0; i < U; ++i) {
-                        a[i] = real ? phi((float)qr[l][i]) : 0.f;
-                        gg[i] = (float)dr[l][i] * inv;
-                        dov += (float)dr[l][i] * (float)orr[l][i];
-                    }
-                    dov = row_sum<GPR>(dov);
-                    if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
-                        sA.write16(t, cq, to_g16<T>(a));
-                        sG.write16(t, cq, to_g16<T>(gg));
-                        if (e % GPR == 0) sH[t] = normalise ? -dov * inv : 0.f;
-                    }
+                dov = row_sum<GPR>(dov);
+                if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
+                    sA.write16(t, cq, to_g16<T>(a));
+                    sG.write16(t, cq, to_g16<T>(gg));
+                    if (e % GPR == 0) sH[t] = normalise ? -dov * inv : 0.f;
                 }
             }
-            __syncthreads();
+            {
+                const int nh = hh + 1 < G ? hh + 1 : 0, nj = hh + 1 < G ? j : j + 1;
+                const size_t nq = (size_t)(qh0 + nh);
+                const int nt0 = t0_of(nj), nrows = rows_of(nj);
+                load_rows<T, D>(qr, q + nq * N * D, nt0, nrows, tid);
+                load_rows<T, D>(orr, o + nq * N * D, nt0, normalise ? nrows : 0, tid);
+                load_rows<T, D>(dr, dout + nq * N * D, nt0, nrows, tid);
+                load_row_scalars<T, D>(dn, den + nq * N, nt0, normalise ? nrows : 0, tid);
+            }
+            lds_barrier();
             // ---- intra-chunk terms (causal), then R += A^T G, r += A^T h
             if (!TOTALS && causal) {
 #pragma unroll
@@ -506,19 +563,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv(const T *__restrict__ q, c
                     }
                 }
             }
-            if (TOTALS || causal) {
 #pragma unroll
-                for (int i = 0; i < BG::MAXST; ++i) {
-                    const int st = BG::tile_of(w, i);
-                    if (st < BG::NST) tile_state_update<T, D>(R[i], false, st / BG::DT, st % BG::DT, 0, sA, sG, lane);
-                }
-                if (tid < D) {
-                    float x = 0.f;
-                    for (int t = 0; t < kBC; ++t) x += sH[t] * (float)sA.p[sA.at(t, tid)];
-                    rr += x;
-                }
+            for (int i = 0; i < BG::MAXST; ++i) {
+                const int st = BG::tile_of(w, i);
+                if (st < BG::NST) tile_state_update<T, D>(R[i], false, st / BG::DT, st % BG::DT, 0, sA, sG, lane);
             }
-            __syncthreads();
+#pragma unroll
+            for (int t = rsl * (kBC / RS); t < (rsl + 1) * (kBC / RS); ++t) rpart += sH[t] * (float)sA.p[sA.at(t, rcol)];
+            lds_barrier();
         }
         if (!TOTALS) {
             // ---- carried terms and the outputs of this chunk
@@ -551,15 +603,17 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv(const T *__restrict__ q, c
                         if (unit < BG::DT) {
                             sOV.p[sOV.at(n, f)] = (T)out[u][r];
                         } else {
-                            const float dbv = out[u][r] + sr[f];
-                            sOK.p[sOK.at(n, f)] = (T)(dbv * fminf(1.f, (float)sB.p[sB.at(n, f)]));
+                            float rf = 0.f;
+#pragma unroll
+                            for (int sl = 0; sl < RS; ++sl) rf += sRp[sl * D + f];
+                            sOK.p[sOK.at(n, f)] = (T)((out[u][r] + rf) * fminf(1.f, (float)sB.p[sB.at(n, f)]));
                         }
                     }
                 }
             }
-            __syncthreads();
-            const Rsrc rdk = make_rsrc(dk + ((size_t)sq * N + t0) * D, bytes);
-            const Rsrc rdv = make_rsrc(dv + ((size_t)sq * N + t0) * D, bytes);
+            lds_barrier();
+            const Rsrc rdk = make_rsrc_u(dk + ((size_t)sq * N + t0) * D, rows * D * (int)sizeof(T));
+            const Rsrc rdv = make_rsrc_u(dv + ((size_t)sq * N + t0) * D, rows * D * (int)sizeof(T));
 #pragma unroll
             for (int l = 0; l < LDV; ++l) {
                 const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
@@ -568,7 +622,6 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv(const T *__restrict__ q, c
                     buf_store16<g16>(rdv, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sOV.p + sOV.at(t, cq)));
                 }
             }
-            __syncthreads();
         }
     }
     if (TOTALS) {
@@ -582,7 +635,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv(const T *__restrict__ q, c
                 for (int r = 0; r < 16; ++r) dst[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n] = R[i][r];
             }
         }
-        if (tid < D) dst[(size_t)D * D + tid] = rr;
+        sRp[rsl * D + rcol] = rpart;
+        lds_barrier();
+        if (tid < D) {
+            float rf = 0.f;
+            for (int sl = 0; sl < RS; ++sl) rf += sRp[sl * D + tid];
+            dst[(size_t)D * D + tid] = rf;
+        }
     }
 }
 
@@ -650,7 +709,7 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
                            1, (float *)nullptr, (float *)nullptr, (const float *)nullptr, (const float *)nullptr);
     }
     // 2. dq (and den)
-    hipLaunchKernelGGL((k_bwd_dq<T, D>), dim3(pl.nseq * pl.G * P), dim3(kThreads), 0, st, qq, kk, vv, oo, dd,
+    hipLaunchKernelGGL((k_bwd_dq<T, D>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo, dd,
                        static_cast<T *>(dq), wden, (const float *)wf, H, Hkv, N, pl.G, P, pl.seg_len, causal,
                        normalise);
     // 3. sums of a g^T and h a per segment: causal segments 1..P-1, suffix scan
