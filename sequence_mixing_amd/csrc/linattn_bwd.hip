@@ -57,6 +57,11 @@ struct BGeo {
     static constexpr int NST = DT * DT;
     static constexpr int MAXST = (NST + 3) / 4;
     static constexpr int E = (int)sizeof(T);
+    // Two workgroups per CU (two waves per SIMD hide each other's waits) where
+    // the registers allow it without spilling: the dq walk up to d = 64, the
+    // dk/dv walk (two sets of output accumulators) up to 128 bytes per row.
+    static constexpr int OCC_DQ = D <= 64 ? 2 : 1;
+    static constexpr int OCC_DKV = D * E <= 128 ? 2 : 1;
     __device__ static int tile_of(int w, int i) { return w * MAXST + i; }
 };
 
@@ -160,7 +165,7 @@ __device__ __forceinline__ void load_row_scalars(float (&r)[L], const float *bas
 // dA^T on MFMA.  The next head's (or chunk's) rows are requested into
 // registers while the current one is computed.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void k_bwd_dq(const T *__restrict__ q, const T *__restrict__ k,
+__global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const T *__restrict__ q, const T *__restrict__ k,
                                                       const T *__restrict__ v, const T *__restrict__ o,
                                                       const T *__restrict__ dout, T *__restrict__ dq,
                                                       float *__restrict__ den_out, const float *__restrict__ ws,
@@ -395,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(const T *__restrict__ q, co
 // terms, then dk and dv are stored.  R lives in MFMA accumulators over the
 // waves; r in per-thread partial sums (column tid % D, a slice of the rows).
 template <typename T, int D, bool TOTALS>
-__global__ __launch_bounds__(kThreads) void k_bwd_dkv(const T *__restrict__ q, const T *__restrict__ k,
+__global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(const T *__restrict__ q, const T *__restrict__ k,
                                                        const T *__restrict__ v, const T *__restrict__ o,
                                                        const T *__restrict__ dout, const float *__restrict__ den,
                                                        T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ ws_r,
