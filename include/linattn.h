@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 4
+#define LINATTN_ABI_VERSION 5
 
 enum { LINATTN_F32 = 0, LINATTN_BF16 = 1 };
 
@@ -116,6 +116,37 @@ int linattn_fwd_from_state(const void *q, const void *k, const void *v, void *ou
                            const float *state_in, const float *z_in,
                            float *state_out, float *z_out, int chunk,
                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * linattn_fwd_packed - linattn_fwd for a packed batch of sequences of
+ * different lengths, with no padding (README "Features": variable sequence
+ * length).  Sequence b owns tokens [cu_seqlens[b], cu_seqlens[b+1]) of
+ * `total`, and every sequence is an independent forward pass (its own S and
+ * z from zero; causal or not, normalised or not as for linattn_fwd).
+ *
+ *   q, out      device, dtype: the sequences' [H][n_b][d] blocks one after
+ *               another (sequence b from element H * cu_seqlens[b] * d);
+ *               H * total * d elements in all.
+ *   k, v        device, dtype: likewise [Hkv][n_b][d] blocks, from element
+ *               Hkv * cu_seqlens[b] * d.
+ *   cu_seqlens  device int32 [nseqs + 1], non-decreasing, cu_seqlens[0] = 0,
+ *               cu_seqlens[nseqs] = total.  Read on the device only (the
+ *               call can be captured in a graph).  Offsets that break these
+ *               rules give unspecified rows but no access outside the
+ *               buffers: they are clamped to [0, total] and made
+ *               non-decreasing.
+ *   state_out, z_out  nullable: [nseqs][Hkv][d][d] and [nseqs][Hkv][d] fp32
+ *               final sums per sequence (zero for an empty sequence).
+ *   workspace   linattn_fwd_packed_workspace_bytes() bytes (depends on
+ *               nseqs, total and the shape, not on the lengths).
+ * Other arguments and errors as for linattn_fwd.
+ */
+size_t linattn_fwd_packed_workspace_bytes(int nseqs, int H, int Hkv, int total, int d, int causal, int dtype,
+                                          int chunk);
+int linattn_fwd_packed(const void *q, const void *k, const void *v, void *out, const int *cu_seqlens,
+                       int nseqs, int total, int H, int Hkv, int d, int causal, int normalise, int dtype,
+                       float *state_out, float *z_out, int chunk, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
 
 /*
  * linattn_fwd_timed - linattn_fwd with stage timing for profilers and

@@ -18,6 +18,7 @@ __all__ = [
     "LINATTN_F32", "LINATTN_BF16", "LINATTN_OK", "LinattnError", "library_path", "load",
     "linattn_fwd", "linattn_fwd_from_state", "linattn_fwd_timed", "linattn_fwd_workspace_bytes", "linattn_fwd_plan", "linattn_decode_step",
     "linattn_status_string", "linattn_abi_version", "linattn_bwd", "linattn_bwd_workspace_bytes",
+    "linattn_fwd_packed", "linattn_fwd_packed_workspace_bytes",
 ]
 
 LINATTN_F32 = 0
@@ -65,6 +66,10 @@ def load():
         lib.linattn_fwd_plan.argtypes = [i] * 8 + [ctypes.POINTER(i), ctypes.POINTER(i)]
         lib.linattn_decode_step.restype = i
         lib.linattn_decode_step.argtypes = [vp] * 6 + [i] * 6 + [vp]
+        lib.linattn_fwd_packed.restype = i
+        lib.linattn_fwd_packed.argtypes = [vp] * 5 + [i] * 8 + [vp, vp, i, vp, sz, vp]
+        lib.linattn_fwd_packed_workspace_bytes.restype = sz
+        lib.linattn_fwd_packed_workspace_bytes.argtypes = [i] * 8
         lib.linattn_bwd.restype = i
         lib.linattn_bwd.argtypes = [vp] * 8 + [i] * 8 + [vp, sz, vp]
         lib.linattn_bwd_workspace_bytes.restype = sz
@@ -139,6 +144,20 @@ def linattn_decode_step(state, z, q, k, v, out, B, H, Hkv, d, normalise, dtype, 
     """C ``linattn_decode_step``; returns the status code (0 = ok)."""
     return load().linattn_decode_step(_ptr(state), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, d,
                                       int(normalise), dtype, _stream(stream))
+
+
+def linattn_fwd_packed(q, k, v, out, cu_seqlens, nseqs, total, H, Hkv, d, causal, normalise, dtype, state_out=None,
+                       z_out=None, chunk=0, workspace=None, workspace_bytes=0, stream=None) -> int:
+    """C ``linattn_fwd_packed``; returns the status code (0 = ok)."""
+    return load().linattn_fwd_packed(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens), nseqs, total, H, Hkv, d,
+                                     int(causal), int(normalise), dtype, _ptr(state_out), _ptr(z_out), chunk,
+                                     _ptr(workspace), workspace_bytes, _stream(stream))
+
+
+def linattn_fwd_packed_workspace_bytes(nseqs, H, Hkv, total, d, causal, dtype, chunk=0) -> int:
+    """C ``linattn_fwd_packed_workspace_bytes``; returns -1 for invalid arguments."""
+    r = load().linattn_fwd_packed_workspace_bytes(nseqs, H, Hkv, total, d, int(causal), dtype, chunk)
+    return -1 if r == ctypes.c_size_t(-1).value else r
 
 
 def linattn_bwd(q, k, v, out, dout, dq, dk, dv, B, H, Hkv, N, d, causal, normalise, dtype, workspace=None,

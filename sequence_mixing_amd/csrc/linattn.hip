@@ -92,7 +92,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ out,
     const float *__restrict__ ws, float *__restrict__ state_out, float *__restrict__ z_out,
     int H, int Hkv, int N, int G, int P, int seg_len, int normalise, const float *__restrict__ s_in,
-    const float *__restrict__ z_in)
+    const float *__restrict__ z_in, Packed pk)
 {
     using M = Main<T, D, C, GT>;
     using v8 = typename Vt<T>::v8;
@@ -109,14 +109,38 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
     const Tile<T, D> sK{smK}, sV{smV}, sQ{smQ};
 
     const int HB = G / GT;
-    const int p = blockIdx.x % P, hb = (blockIdx.x / P) % HB, seq = blockIdx.x / (P * HB);
-    const int b = seq / Hkv, gk = seq % Hkv;
+    // Dense batch: blocks run over (sequence, head block, segment).  Packed
+    // batch: over (kv head, head block, segment of all sequences), with the
+    // sequence's length in place of N and its segment count in place of P.
+    int p, hb, seq, np = P;
+    size_t kbase, qbase, slot0;
+    if (!pk.tab) {
+        p = blockIdx.x % P;
+        hb = (blockIdx.x / P) % HB;
+        seq = blockIdx.x / (P * HB);
+        const int b = seq / Hkv, gk = seq % Hkv;
+        kbase = (size_t)seq * N * D;
+        qbase = ((size_t)b * H + (size_t)gk * G + (size_t)hb * GT) * N * D;  // first query head of the block
+        slot0 = (size_t)seq * (P - 1);
+    } else {
+        SegLoc r;
+        const int rest = blockIdx.x / pk.nsmax;
+        hb = rest % HB;
+        const int gk = rest / HB;
+        if (!packed_locate(pk, blockIdx.x % pk.nsmax, r)) return;
+        p = r.p;
+        np = r.np;
+        N = r.n;
+        seq = r.b * Hkv + gk;
+        kbase = ((size_t)r.off * Hkv + (size_t)gk * r.n) * D;
+        qbase = ((size_t)r.off * H + (size_t)(gk * G + hb * GT) * r.n) * D;
+        slot0 = packed_slot0(r, gk, Hkv, 1);
+    }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
-    const T *kb = k + (size_t)seq * N * D;
-    const T *vb = v + (size_t)seq * N * D;
-    const size_t head0 = (size_t)b * H + (size_t)gk * G + (size_t)hb * GT;  // first query head of the block
-    const T *qb = q + head0 * N * D;
-    T *ob = out + head0 * N * D;
+    const T *kb = k + kbase;
+    const T *vb = v + kbase;
+    const T *qb = q + qbase;
+    T *ob = out + qbase;
     const int s0 = p * seg_len, s1 = min(N, s0 + seg_len);
     const int nch = (s1 - s0 + C - 1) / C;
 
@@ -125,7 +149,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
     float zr = 0.f;
     // segment p > 0: the scanned sums in slot p - 1; segment 0: the start
     // sums of a continuation, or zero
-    const float *init = p > 0 ? ws + ((size_t)seq * (P - 1) + (p - 1)) * (size_t)D * (D + 1)
+    const float *init = p > 0 ? ws + (slot0 + (p - 1)) * (size_t)D * (D + 1)
                               : (s_in ? s_in + (size_t)seq * D * D : nullptr);
     const float *initz = p > 0 ? init + (size_t)D * D : (z_in ? z_in + (size_t)seq * D : nullptr);
 #pragma unroll
@@ -218,7 +242,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
     load_all(ra, s0 + C);
     lds_barrier();
 
-    const bool carry_out = p == P - 1 && (state_out || z_out);
+    const bool carry_out = p == np - 1 && (state_out || z_out);
     for (int c = 0; c < nch; ++c) {
         const int t0 = s0 + c * C;
         // Key tiles holding tokens < N; tiles past them add nothing and no
@@ -397,7 +421,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         }
     }
 
-    if (p == P - 1 && state_out) {
+    if (p == np - 1 && state_out) {
         float *so = state_out + (size_t)seq * D * D;
 #pragma unroll
         for (int i = 0; i < M::MAXST; ++i) {
@@ -409,7 +433,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
             }
         }
     }
-    if (p == P - 1 && z_out && hb == 0) {
+    if (p == np - 1 && z_out && hb == 0) {
         const int st = M::tile_of(w, 0);
         if (st < M::NST && st % DT == 0 && h == 0) z_out[(size_t)seq * D + (st / DT) * 32 + n] = zr;
     }
@@ -422,7 +446,8 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restrict__ q, T *__restrict__ out,
                                                               const float *__restrict__ ws, int nslots, int H,
-                                                              int Hkv, int N, int G, int nblk, int normalise)
+                                                              int Hkv, int N, int G, int nblk, int normalise,
+                                                              Packed pk, int seg_len)
 {
     constexpr int TQ = 128;
     using Gm = Geo<T, D, 32>;
@@ -434,10 +459,29 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restric
     __shared__ float smZ[D];
     const Tile<T, D> sST{smST};
 
-    const int seq = blockIdx.x / nblk, blk = blockIdx.x % nblk;
-    const int b = seq / Hkv, gk = seq % Hkv;
+    // Dense batch: blocks run over (sequence, 128-token block).  Packed batch
+    // (segments of seg_len tokens, a multiple of 128): over (kv head, segment
+    // of all sequences, 128-token block of the segment).
+    int blk;
+    size_t qbase, slot0;
+    if (!pk.tab) {
+        const int seq = blockIdx.x / nblk, b = seq / Hkv, gk = seq % Hkv;
+        blk = blockIdx.x % nblk;
+        qbase = ((size_t)b * H + (size_t)gk * G) * N * D;
+        slot0 = (size_t)seq * nslots;
+    } else {
+        const int bps = seg_len / TQ, j = blockIdx.x % bps, rest = blockIdx.x / bps;
+        const int gk = rest / pk.nsmax;
+        SegLoc r;
+        if (!packed_locate(pk, rest % pk.nsmax, r)) return;
+        blk = r.p * bps + j;
+        N = r.n;
+        if (blk * TQ >= N) return;
+        qbase = ((size_t)r.off * H + (size_t)gk * G * r.n) * D;
+        slot0 = packed_slot0(r, gk, Hkv, 0);
+    }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
-    const float *S = ws + (size_t)seq * nslots * (size_t)D * (D + 1);
+    const float *S = ws + slot0 * (size_t)D * (D + 1);
     // S^T into LDS: element (row j, col i) = S[i][j].
     for (int e = tid; e < D * D; e += kThreads) {
         const int i = e / D, j = e % D;
@@ -446,8 +490,8 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restric
     for (int e = tid; e < D; e += kThreads) smZ[e] = S[(size_t)D * D + e];
     __syncthreads();
 
-    const T *qb = q + ((size_t)b * H + (size_t)gk * G) * N * D;
-    T *ob = out + ((size_t)b * H + (size_t)gk * G) * N * D;
+    const T *qb = q + qbase;
+    T *ob = out + qbase;
     const int NU = G * (TQ / 32);
     for (int u = w; u < NU; u += 4) {
         const int g = u / (TQ / 32), r = u % (TQ / 32);
@@ -663,26 +707,37 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
     const T *kk = static_cast<const T *>(k);
     const T *vv = static_cast<const T *>(v);
     T *oo = static_cast<T *>(out);
-    const int P = pl.segments;
+    const int P = pl.segments;  // packed: the segments the launches are sized for
     const int E = D * D + D;
+    const dim3 scan_grid((E + kThreads - 1) / kThreads, pl.nseq);
+    Packed pk{nullptr, 0, 0};
     if (record(ev, 0, st)) return LINATTN_ERR_HIP;
+    if (pl.packed) {
+        int *tab = reinterpret_cast<int *>(reinterpret_cast<char *>(ws) + pl.tab_off);
+        hipLaunchKernelGGL(k_pack_plan, dim3(1), dim3(kThreads), 0, st, pl.cu, pl.nb, pl.N, pl.seg_len, P, tab);
+        pk = Packed{tab, pl.nb, P};
+    }
     if (pl.causal) {
-        if (P > 1 && launch_totals<T, D>(c1, pl.nseq * (P - 1), st, kk, vv, ws, pl.N, pl.seg_len, P - 1))
+        if (pl.packed) {
+            if (launch_totals<T, D>(c1, pl.Hkv * P, st, kk, vv, ws, pl.N, pl.seg_len, 1, pk, pl.Hkv, 1))
+                return LINATTN_ERR_UNSUPPORTED;
+        } else if (P > 1 && launch_totals<T, D>(c1, pl.nseq * (P - 1), st, kk, vv, ws, pl.N, pl.seg_len, P - 1)) {
             return LINATTN_ERR_UNSUPPORTED;
+        }
         if (record(ev, 1, st)) return LINATTN_ERR_HIP;
         // the scan also adds the start sums of a continuation into every slot
-        if (P > 2 || (P == 2 && (s0.S || s0.z)))
-            hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, ws,
-                               P - 1, D, 0, (float *)nullptr, (float *)nullptr, s0.S, s0.z);
+        if (pl.packed || P > 2 || (P == 2 && (s0.S || s0.z)))
+            hipLaunchKernelGGL(k_seg_scan, scan_grid, dim3(kThreads), 0, st, ws, P - 1, D, 0, (float *)nullptr,
+                               (float *)nullptr, s0.S, s0.z, pk, pl.Hkv);
         if (record(ev, 2, st)) return LINATTN_ERR_HIP;
-        const dim3 grid(pl.nseq * (pl.G / pl.gt) * P);
+        const dim3 grid((pl.packed ? pl.Hkv : pl.nseq) * (pl.G / pl.gt) * P);
         for (int rep = 0; rep < (ev ? ev->reps : 1); ++rep) switch (pl.gt) {
 #define LINATTN_MAIN(GT)                                                                                            \
     case GT:                                                                                                       \
         if constexpr (Main<T, D, C, GT>::FITS) {                                                                   \
             hipLaunchKernelGGL((k_causal_chunks<T, D, C, GT>), grid, dim3(Main<T, D, C, GT>::TH), 0, st, qq, kk,   \
                                vv, oo, (const float *)ws, state_out, z_out, pl.H, pl.Hkv, pl.N, pl.G, P,           \
-                               pl.seg_len, normalise, s0.S, s0.z);                                                 \
+                               pl.seg_len, normalise, s0.S, s0.z, pk);                                             \
             break;                                                                                                 \
         } else {                                                                                                   \
             return LINATTN_ERR_UNSUPPORTED;                                                                        \
@@ -695,15 +750,18 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
         default: return LINATTN_ERR_UNSUPPORTED;
         }
     } else {
-        if (launch_totals<T, D>(c1, pl.nseq * P, st, kk, vv, ws, pl.N, pl.seg_len, P)) return LINATTN_ERR_UNSUPPORTED;
+        if (launch_totals<T, D>(c1, (pl.packed ? pl.Hkv : pl.nseq) * P, st, kk, vv, ws, pl.N, pl.seg_len, P, pk,
+                                pl.Hkv, 0))
+            return LINATTN_ERR_UNSUPPORTED;
         if (record(ev, 1, st)) return LINATTN_ERR_HIP;
-        hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, ws, P,
-                           D, 1, state_out, z_out, s0.S, s0.z);
+        hipLaunchKernelGGL(k_seg_scan, scan_grid, dim3(kThreads), 0, st, ws, P, D, 1, state_out, z_out, s0.S, s0.z, pk,
+                           pl.Hkv);
         if (record(ev, 2, st)) return LINATTN_ERR_HIP;
         const int nblk = (pl.N + 127) / 128;
+        const unsigned grid = pl.packed ? (unsigned)(pl.Hkv * P * (pl.seg_len / 128)) : (unsigned)(pl.nseq * nblk);
         for (int rep = 0; rep < (ev ? ev->reps : 1); ++rep)
-            hipLaunchKernelGGL((k_noncausal_apply<T, D>), dim3(pl.nseq * nblk), dim3(kThreads), 0, st, qq, oo,
-                               (const float *)ws, P, pl.H, pl.Hkv, pl.N, pl.G, nblk, normalise);
+            hipLaunchKernelGGL((k_noncausal_apply<T, D>), dim3(grid), dim3(kThreads), 0, st, qq, oo,
+                               (const float *)ws, P, pl.H, pl.Hkv, pl.N, pl.G, nblk, normalise, pk, pl.seg_len);
     }
     if (record(ev, 3, st)) return LINATTN_ERR_HIP;
     return launch_status();
@@ -816,12 +874,17 @@ size_t linattn_fwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int caus
 namespace {
 int fwd_impl(const void *q, const void *k, const void *v, void *out, int B, int H, int Hkv, int N, int d, int causal,
              int normalise, int dtype, float *state_out, float *z_out, int chunk, void *workspace,
-             size_t workspace_bytes, hipStream_t stream, const Timing *ev, const Start &s0 = Start{nullptr, nullptr})
+             size_t workspace_bytes, hipStream_t stream, const Timing *ev, const Start &s0 = Start{nullptr, nullptr},
+             bool packed = false, const int *cu = nullptr)
 {
+    // packed: B sequences of N tokens in all, delimited by cu[0..B] (device)
     linattn::Plan pl;
-    const int rc = linattn::make_plan(B, H, Hkv, N, d, causal, dtype, chunk, &pl);
+    const int rc = packed ? linattn::make_plan_packed(B, H, Hkv, N, d, causal, dtype, chunk, &pl)
+                          : linattn::make_plan(B, H, Hkv, N, d, causal, dtype, chunk, &pl);
     if (rc != LINATTN_OK) return rc;
     if (B == 0) return LINATTN_OK;
+    if (packed && !cu) return LINATTN_ERR_NULL;
+    pl.cu = cu;
     if (N > 0 && (!q || !k || !v || !out)) return LINATTN_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(state_out) ||
         !aligned16(z_out) || !aligned16(workspace))
@@ -862,6 +925,22 @@ int linattn_fwd_from_state(const void *q, const void *k, const void *v, void *ou
         return LINATTN_ERR_SHAPE;  // the start sums are read while the final ones are written
     return fwd_impl(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_out, z_out, chunk, workspace,
                     workspace_bytes, stream, nullptr, Start{state_in, z_in});
+}
+
+size_t linattn_fwd_packed_workspace_bytes(int nseqs, int H, int Hkv, int total, int d, int causal, int dtype,
+                                          int chunk)
+{
+    linattn::Plan pl;
+    if (linattn::make_plan_packed(nseqs, H, Hkv, total, d, causal, dtype, chunk, &pl) != LINATTN_OK) return (size_t)-1;
+    return pl.ws_bytes;
+}
+
+int linattn_fwd_packed(const void *q, const void *k, const void *v, void *out, const int *cu_seqlens, int nseqs,
+                       int total, int H, int Hkv, int d, int causal, int normalise, int dtype, float *state_out,
+                       float *z_out, int chunk, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return fwd_impl(q, k, v, out, nseqs, H, Hkv, total, d, causal, normalise, dtype, state_out, z_out, chunk,
+                    workspace, workspace_bytes, stream, nullptr, Start{nullptr, nullptr}, true, cu_seqlens);
 }
 
 int linattn_fwd_timed(const void *q, const void *k, const void *v, void *out, int B, int H, int Hkv, int N, int d,

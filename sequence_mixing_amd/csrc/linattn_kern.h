@@ -297,21 +297,133 @@ __device__ __forceinline__ float tile_state_update(f32x16 &acc, bool want_z, int
 
 // -------------------------------------------------------------- seg_totals
 //
+// ---------------------------------------------------------- packed batches
+//
+// A packed batch holds nb sequences of different lengths with no padding
+// (README "Features": variable sequence length): sequence b owns tokens
+// [cu[b], cu[b+1]) of `total`, stored head-major per sequence (q and out:
+// [H][n_b][d] from element H * cu[b] * d; k and v: [Hkv][n_b][d] from
+// Hkv * cu[b] * d).  Sequences are cut into segments of seg_len tokens as in
+// a dense batch; k_pack_plan writes the tables the kernels locate their
+// segment with, into the workspace (ints):
+//   segpre[nb + 1]  segments of the sequences before b
+//   off[nb], len[nb]  token offset and length of sequence b
+//   segb[nsmax]     the sequence of every segment
+// The boundaries are clamped to [0, total] and made non-decreasing first, so
+// malformed offsets give wrong rows but never an access out of range; every
+// sequence has at least one segment (an empty one still writes its state).
+struct Packed {
+    const int *tab;  // the tables above; nullptr for a dense batch
+    int nb, nsmax;   // sequences; segments the launches are sized for
+};
+struct SegLoc {
+    int b, p, n, np, sb, off;  // sequence, segment in it, its tokens, its segments, segments before it, token offset
+};
+__device__ __forceinline__ bool packed_locate(const Packed &pk, int s, SegLoc &r)
+{
+    const int *segpre = pk.tab, *off = pk.tab + pk.nb + 1, *len = off + pk.nb, *segb = len + pk.nb;
+    if (s >= min(segpre[pk.nb], pk.nsmax)) return false;
+    const int b = segb[s];
+    r.b = b;
+    r.sb = segpre[b];
+    r.np = segpre[b + 1] - r.sb;
+    r.p = s - r.sb;
+    r.off = off[b];
+    r.n = len[b];
+    return true;
+}
+// First workspace slot of (sequence b, kv head g): every sequence keeps
+// np - 1 partial sums per kv head (causal) or np (non-causal), sequence-major
+// as in a dense batch.
+__device__ __forceinline__ size_t packed_slot0(const SegLoc &r, int g, int Hkv, int causal)
+{
+    return (size_t)(r.sb - causal * r.b) * Hkv + (size_t)g * (r.np - causal);
+}
+
+// One workgroup: builds the tables of a packed batch from cu[0..nb].
+__global__ __launch_bounds__(kThreads) void k_pack_plan(const int *__restrict__ cu, int nb, int total, int seg_len,
+                                                        int nsmax, int *__restrict__ tab)
+{
+    __shared__ int sred[kThreads];
+    int *segpre = tab, *off = tab + nb + 1, *len = off + nb, *segb = len + nb;
+    const int tid = threadIdx.x;
+    const int per = (nb + kThreads - 1) / kThreads;
+    const int b0 = min(nb, tid * per), b1 = min(nb, b0 + per);
+    auto clampt = [&](int x) { return x < 0 ? 0 : (x > total ? total : x); };
+    // boundary j is the running maximum of cu[0..j], clamped to [0, total]
+    int m = -2147483647 - 1;
+    for (int j = b0 + 1; j <= b1; ++j) m = max(m, cu[j]);
+    sred[tid] = m;
+    __syncthreads();
+    if (tid == 0) {
+        int run = cu[0];
+        for (int t = 0; t < kThreads; ++t) {
+            const int x = sred[t];
+            sred[t] = run;  // maximum of cu[0 .. b0 of thread t]
+            run = max(run, x);
+        }
+    }
+    __syncthreads();
+    int run = sred[tid], nseg = 0;
+    for (int b = b0; b < b1; ++b) {
+        const int lo = clampt(run);
+        run = max(run, cu[b + 1]);
+        const int hi = clampt(run);
+        off[b] = lo;
+        len[b] = hi - lo;
+        nseg += hi > lo ? (hi - lo + seg_len - 1) / seg_len : 1;
+    }
+    __syncthreads();
+    sred[tid] = nseg;
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int t = 0; t < kThreads; ++t) {
+            const int x = sred[t];
+            sred[t] = acc;
+            acc += x;
+        }
+        segpre[nb] = acc;
+    }
+    __syncthreads();
+    int sbase = sred[tid];
+    for (int b = b0; b < b1; ++b) {
+        segpre[b] = sbase;
+        const int np = len[b] > 0 ? (len[b] + seg_len - 1) / seg_len : 1;
+        for (int s = sbase; s < sbase + np && s < nsmax; ++s) segb[s] = b;
+        sbase += np;
+    }
+}
+
 // One workgroup per (sequence, segment): T_p = phi(K_p)^T V_p and
 // sum phi(K_p), written as fp32 partials ws[seq][p] = [S (d x d) | z (d)].
 // Chunks of C1 tokens, double-buffered in LDS (one barrier per chunk).
+// Packed batches (pk.tab set): one workgroup per (kv head, segment of all
+// sequences); the last segment of a causal sequence has nothing to do.
 template <typename T, int D, int C1>
 __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict__ k, const T *__restrict__ v,
-                                                            float *__restrict__ ws, int N, int seg_len, int nslots)
+                                                            float *__restrict__ ws, int N, int seg_len, int nslots,
+                                                            Packed pk, int Hkv, int causal)
 {
     using G = Geo<T, D, C1>;
     __shared__ __attribute__((aligned(16))) T smK[2][C1 * D];
     __shared__ __attribute__((aligned(16))) T smV[2][C1 * D];
 
-    const int seq = blockIdx.x / nslots, p = blockIdx.x % nslots;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
+    int seq = blockIdx.x / nslots, p = blockIdx.x % nslots;
     const T *kb = k + (size_t)seq * N * D;
     const T *vb = v + (size_t)seq * N * D;
+    size_t slot = (size_t)seq * nslots + p;
+    if (pk.tab) {
+        SegLoc r;
+        const int gk = blockIdx.x / pk.nsmax;
+        if (!packed_locate(pk, blockIdx.x % pk.nsmax, r) || (causal && r.p == r.np - 1)) return;
+        p = r.p;
+        N = r.n;
+        kb = k + ((size_t)r.off * Hkv + (size_t)gk * r.n) * D;
+        vb = v + ((size_t)r.off * Hkv + (size_t)gk * r.n) * D;
+        slot = packed_slot0(r, gk, Hkv, causal) + r.p;
+    }
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
     const int s0 = p * seg_len, s1 = min(N, s0 + seg_len);
     const int nch = (s1 - s0 + C1 - 1) / C1;
 
@@ -365,7 +477,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
         lds_barrier();
         absorb(1);
     }
-    float *out = ws + ((size_t)seq * nslots + p) * (size_t)D * (D + 1);
+    float *out = ws + slot * (size_t)D * (D + 1);
 #pragma unroll
     for (int i = 0; i < G::MAXST; ++i) {
         const int st = G::tile_of(w, i);
@@ -391,15 +503,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
 // slot 0 and, when given, to state_out / z_out.  mode 2: inclusive suffix
 // (slot p gets the sum of slots p..nslots-1), in place.  Modes 0 and 1 start
 // from s_in / z_in (the sums of earlier tokens) when given.
+// Packed batches: blockIdx.y = b * Hkv + kv head, and sequence b's own slots.
 __global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, int nslots, int D, int mode,
                                                        float *__restrict__ state_out, float *__restrict__ z_out,
-                                                       const float *__restrict__ s_in, const float *__restrict__ z_in)
+                                                       const float *__restrict__ s_in, const float *__restrict__ z_in,
+                                                       Packed pk = Packed{nullptr, 0, 0}, int Hkv = 1)
 {
     const int E = D * D + D;
     const int seq = blockIdx.y;
     const int e = blockIdx.x * kThreads + threadIdx.x;
     if (e >= E) return;
     float *base = ws + (size_t)seq * nslots * E + e;
+    if (pk.tab) {
+        const int b = seq / Hkv, gk = seq % Hkv, causal = mode != 1;
+        SegLoc r;
+        r.b = b;
+        r.sb = pk.tab[b];
+        r.np = pk.tab[b + 1] - r.sb;
+        nslots = r.np - causal;
+        base = ws + packed_slot0(r, gk, Hkv, causal) * E + e;
+    }
     // the sums start from the given ones (continuation), else from zero
     float acc = 0.f;
     if (e < D * D) {
@@ -444,24 +567,25 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // chunk, so that two chunks of K and V double-buffer in 64 KiB of LDS).
 template <typename T, int D>
 int launch_totals(int c1, unsigned nblocks, hipStream_t st, const T *k, const T *v, float *ws, int N, int seg_len,
-                  int nslots)
+                  int nslots, Packed pk = Packed{nullptr, 0, 0}, int Hkv = 1, int causal = 1)
 {
     constexpr int cap = 65536 / (4 * D * (int)sizeof(T));
     switch (c1) {
     case 32:
-        hipLaunchKernelGGL((k_seg_totals<T, D, 32>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len, nslots);
+        hipLaunchKernelGGL((k_seg_totals<T, D, 32>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len, nslots,
+                           pk, Hkv, causal);
         return LINATTN_OK;
     case 64:
         if constexpr (64 <= cap) {
             hipLaunchKernelGGL((k_seg_totals<T, D, 64>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len,
-                               nslots);
+                               nslots, pk, Hkv, causal);
             return LINATTN_OK;
         }
         break;
     case 128:
         if constexpr (128 <= cap) {
             hipLaunchKernelGGL((k_seg_totals<T, D, 128>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len,
-                               nslots);
+                               nslots, pk, Hkv, causal);
             return LINATTN_OK;
         }
         break;

@@ -95,4 +95,46 @@ int make_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int ch
     return LINATTN_OK;
 }
 
+int make_plan_packed(int nb, int H, int Hkv, int total, int d, int causal, int dtype, int chunk, Plan *p)
+{
+    Plan q{};
+    // Shapes, chunk and head block as for one sequence of `total` tokens.
+    const int rc = make_plan(nb > 0 ? 1 : 0, H, Hkv, total, d, causal, dtype, chunk, &q);
+    if (rc != LINATTN_OK) return rc;
+    if (nb < 0) return LINATTN_ERR_SHAPE;
+    q.B = nb;
+    q.nb = nb;
+    q.nseq = nb * Hkv;
+    q.packed = 1;
+    q.segments = q.seg_len = q.ws_slots = 0;
+    q.ws_bytes = 0;
+    q.tab_off = 0;
+    if (nb > 0 && total > 0) {
+        const int C = q.chunk;
+        const int e = dtype == LINATTN_BF16 ? 2 : 4;
+        const int hb = q.G / q.gt;
+        // Workgroups as for a dense batch: one resident round of the chunk
+        // kernel (causal) or 512 partial sums (non-causal), over all kv heads.
+        const int tgt = q.causal ? kCUs * main_shape(e, d, C, q.gt).occ : kTargetWorkgroups;
+        const int per = q.causal ? Hkv * hb : Hkv;
+        const int nseg = (tgt + per - 1) / per;
+        // The non-causal output pass takes 128-token blocks of a segment.
+        const int unit = q.causal ? C : (C > 128 ? C : 128);
+        int64_t len = ((int64_t)total + nseg - 1) / nseg;
+        len = (len + unit - 1) / unit * unit;
+        q.seg_len = (int)len;
+        const int64_t nsmax = ((int64_t)total + len - 1) / len + nb;
+        const int64_t slots = (int64_t)Hkv * nsmax;
+        const int64_t tab_ints = 3 * (int64_t)nb + 1 + nsmax;
+        if (nsmax > INT32_MAX / 2 || slots > INT32_MAX / 2) return LINATTN_ERR_SHAPE;
+        q.segments = (int)nsmax;
+        q.ws_slots = (int)nsmax;
+        const size_t slot_bytes = (size_t)slots * (size_t)d * (d + 1) * sizeof(float);
+        q.tab_off = (slot_bytes + 255) / 256 * 256;
+        q.ws_bytes = q.tab_off + (size_t)tab_ints * sizeof(int);
+    }
+    *p = q;
+    return LINATTN_OK;
+}
+
 }  // namespace linattn

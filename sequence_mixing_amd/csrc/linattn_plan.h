@@ -84,7 +84,12 @@ struct Plan {
     int segments;    // segments per sequence
     int seg_len;     // tokens per segment (multiple of chunk)
     int ws_slots;    // fp32 partial states per sequence held in the workspace
-    size_t ws_bytes; // workspace bytes: nseq * ws_slots * d * (d + 1) * 4
+    size_t ws_bytes; // workspace bytes: nseq * ws_slots * d * (d + 1) * 4 (dense)
+    // packed batches (sequences of different lengths, no padding)
+    int packed;      // 1: N is the total token count and segments an upper bound
+    int nb;          // sequences
+    size_t tab_off;  // byte offset of the segment tables in the workspace
+    const int *cu = nullptr;  // device sequence offsets of a packed batch (set by the caller of the plan)
 };
 
 // Query heads per workgroup for (dtype, d, chunk, G): the largest of 8, 4,
@@ -96,5 +101,12 @@ int auto_chunk(int dtype, int d, int G, int causal);
 
 // Fills `p` and returns LINATTN_OK or an error code (see linattn.h).
 int make_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int chunk, Plan *p);
+
+// Plan of a packed batch of nb sequences with `total` tokens in all: one
+// segment length for every sequence, launches sized for `segments` =
+// ceil(total / seg_len) + nb segments (each sequence adds at most one partial
+// segment), the workspace sized for that many partial states per kv head
+// plus the segment tables.
+int make_plan_packed(int nb, int H, int Hkv, int total, int d, int causal, int dtype, int chunk, Plan *p);
 
 }  // namespace linattn

@@ -7,7 +7,8 @@ from __future__ import annotations
 import torch
 
 from . import (LINATTN_BF16, LINATTN_F32, LinattnError, linattn_bwd, linattn_bwd_workspace_bytes,
-               linattn_decode_step, linattn_fwd, linattn_fwd_from_state, linattn_fwd_workspace_bytes)
+               linattn_decode_step, linattn_fwd, linattn_fwd_from_state, linattn_fwd_packed,
+               linattn_fwd_packed_workspace_bytes, linattn_fwd_workspace_bytes)
 
 _DT = {torch.float32: LINATTN_F32, torch.bfloat16: LINATTN_BF16}
 
@@ -59,6 +60,55 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=True, normalis
     rc = linattn_fwd(q, k, v, out, B, H, Hkv, N, d, causal, normalise, code, S, z, chunk, ws, nbytes, stream)
     if rc != 0:
         raise LinattnError(rc, "linattn_fwd")
+    return (out, S, z) if want_state else out
+
+
+def pack(seqs):
+    """Concatenates per-sequence tensors [heads, n_b, d] (one dtype and device) into the
+    packed layout: a flat tensor holding each sequence's head-major block in turn, and
+    cu_seqlens (int32, nseqs + 1 token offsets) on the same device."""
+    cu = [0]
+    for x in seqs:
+        cu.append(cu[-1] + x.shape[1])
+    flat = torch.cat([x.contiguous().reshape(-1) for x in seqs]) if seqs else torch.empty(0)
+    return flat, torch.tensor(cu, dtype=torch.int32, device=flat.device)
+
+
+def unpack(flat, cu, heads, d):
+    """Inverse of pack: the list of [heads, n_b, d] views of a packed tensor."""
+    cu = [int(x) for x in cu]
+    return [flat[heads * a * d: heads * b * d].view(heads, b - a, d) for a, b in zip(cu[:-1], cu[1:])]
+
+
+def fwd_packed(q, k, v, cu_seqlens, H, Hkv, d, causal=True, normalise=True, chunk=0, want_state=False, out=None,
+               ws=None, stream=None):
+    """linattn_fwd_packed on packed tensors (see pack): q of H * total * d elements, k and v
+    of Hkv * total * d; cu_seqlens an int32 device tensor of nseqs + 1 offsets."""
+    nseqs = cu_seqlens.numel() - 1
+    total = q.numel() // (H * d)
+    for t in (q, k, v):
+        if not (t.is_cuda and t.is_contiguous() and t.dtype == q.dtype):
+            raise ValueError("q, k, v must be contiguous device tensors of one dtype")
+    if q.numel() != H * total * d or k.numel() != Hkv * total * d or v.numel() != k.numel():
+        raise ValueError("q must hold H * total * d elements and k, v Hkv * total * d")
+    if not (cu_seqlens.is_cuda and cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous int32 device tensor")
+    code = dtype_code(q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    S = z = None
+    if want_state:
+        S = torch.empty(nseqs, Hkv, d, d, dtype=torch.float32, device=q.device)
+        z = torch.empty(nseqs, Hkv, d, dtype=torch.float32, device=q.device)
+    nbytes = linattn_fwd_packed_workspace_bytes(nseqs, H, Hkv, total, d, causal, code, chunk)
+    if nbytes < 0:
+        raise LinattnError(-2, "linattn_fwd_packed_workspace_bytes")
+    if ws is None:
+        ws = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=q.device)
+    rc = linattn_fwd_packed(q, k, v, out, cu_seqlens, nseqs, total, H, Hkv, d, causal, normalise, code, S, z, chunk,
+                            ws, ws.numel() * 4, stream)
+    if rc != 0:
+        raise LinattnError(rc, "linattn_fwd_packed")
     return (out, S, z) if want_state else out
 
 

@@ -164,3 +164,16 @@ def test_bwd_workspace_and_validation_without_gpu():
     assert la.linattn_bwd(None, None, None, None, None, None, None, None, 0, 2, 2, 64, 64, 1, 1, f32, stream=0) == 0
     assert la.linattn_bwd(None, None, None, None, None, None, None, None, 1, 2, 2, 64, 64, 1, 1, f32, stream=0) == -1
     assert la.linattn_bwd(None, None, None, None, None, None, None, None, 1, 2, 2, 64, 40, 1, 1, f32, stream=0) == -4
+
+
+def test_packed_argtypes_match_header():
+    """Every exported call's ctypes argument count equals the header's parameter count."""
+    hdr = open(os.path.join(ROOT, "include", "linattn.h")).read()
+    lib = la.load()
+    for name in ("linattn_fwd", "linattn_fwd_from_state", "linattn_fwd_packed", "linattn_fwd_timed",
+                 "linattn_bwd", "linattn_decode_step", "linattn_fwd_packed_workspace_bytes",
+                 "linattn_bwd_workspace_bytes", "linattn_fwd_workspace_bytes", "linattn_fwd_plan"):
+        m = re.search(r"\b" + name + r"\(([^)]*)\);", hdr)
+        assert m, name
+        nparams = len([p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"])
+        assert len(getattr(lib, name).argtypes) == nparams, name
