@@ -409,6 +409,79 @@ def bwd_oracle(w, causal, seconds, max_tokens=1024):
                                         f"{reps} reps in {el:.1f} s"}
 
 
+def packed_row(la, hip, torch, steps):
+    """linattn_fwd_packed on the seeded packed batch (sequences of different lengths, no
+    padding), K steps in one HIP graph; tokens/s counts real tokens only."""
+    from linattn_inputs import PACKED, packed_qkv
+    from sequence_mixing_amd import ops
+
+    P = PACKED
+    lens, seqs = packed_qkv(P)
+    qf, cu = ops.pack([s[0][0] for s in seqs])
+    kf, _ = ops.pack([s[1][0] for s in seqs])
+    vf, _ = ops.pack([s[2][0] for s in seqs])
+    qf, kf, vf, cu = qf.cuda(), kf.cuda(), vf.cuda(), cu.cuda()
+    total = sum(lens)
+    dt = la.LINATTN_BF16 if P["dtype"] == "bf16" else la.LINATTN_F32
+    nb = la.linattn_fwd_packed_workspace_bytes(len(lens), P["H"], P["Hkv"], total, P["d"], 1, dt)
+    ws = torch.empty(nb // 4 + 1, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(qf)
+
+    def call(st):
+        rc = la.linattn_fwd_packed(qf, kf, vf, out, cu, len(lens), total, P["H"], P["Hkv"], P["d"], 1, 1, dt,
+                                   None, None, 0, ws, nb, st)
+        if rc != 0:
+            raise la.LinattnError(rc, "linattn_fwd_packed")
+
+    call(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream().cuda_stream
+        for _ in range(steps):
+            call(cap)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    g.replay()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(e0, e1) / steps
+    same = bool(torch.equal(out, ref))
+    del g
+    e = 2 if P["dtype"] == "bf16" else 4
+    nbytes = total * P["d"] * e * (2 * P["H"] + 2 * P["Hkv"])
+    return {"workload": P["name"], "sequences": len(lens), "total_tokens": total, "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(total / (ms / 1e3), 1), "graph_matches_eager": same,
+            "roofline_path": roofline(nbytes, 0.0, ms / 1e3, P["dtype"], "whole packed forward (graph replay, events)")}
+
+
+def packed_oracle(seconds):
+    """The fp64 oracle on the first sequences of the packed batch, one after another."""
+    import oracle
+    from linattn_inputs import packed_qkv
+
+    lens, seqs = packed_qkv()
+    threads = oracle.default_threads()
+    done, t0 = 0, time.perf_counter()
+    for (q, k, v), n in zip(seqs, lens):
+        oracle.ref_fwd(q, k, v, nthreads=threads)
+        done += n
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(done / el, 1), "unit": "tokens/s", "cores": min(threads, 8), "kind": "oracle",
+            "sample": f"the first {done} tokens of the packed batch, sequence by sequence, in {el:.1f} s"}
+
+
 def decode_row(la, hip, torch, steps_total, stream):
     """GQA prefill (N=32768), state replicated into 64 slots, 1024 decode steps."""
     from linattn_inputs import DECODE, WORKLOADS, DecodeStream, workload_qkv
@@ -595,6 +668,10 @@ def main():
             log(name, json.dumps(rows[name]))
         rows["cfg5_prefill_4_pieces"] = pieces_row(la, hip, torch, WORKLOADS["cfg5"], 4, 20)
         log("cfg5_prefill_4_pieces", json.dumps(rows["cfg5_prefill_4_pieces"]))
+        rows["packed"] = packed_row(la, hip, torch, 20)
+        if args.cpu_seconds > 0:
+            rows["packed"]["cpu_oracle"] = packed_oracle(min(2.0, args.cpu_seconds))
+        log("packed", json.dumps(rows["packed"]))
         for name, key in (("cfg2_bwd", "cfg2"), ("cfg3_bwd", "cfg3"), ("cfg5_bwd", "cfg5")):
             rows[name] = bwd_row(la, hip, torch, WORKLOADS[key], 1, 10)
             if args.cpu_seconds > 0:

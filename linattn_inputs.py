@@ -11,7 +11,10 @@ Recipe (no dataset is involved; the pages measure on none):
     V [B,Hkv,N,d]; bf16 workloads round each with round-to-nearest-even
     (``.to(torch.bfloat16)``), and the oracle reads the rounded values;
   * decode: one generator per run, step-major: for every step draw q [B,H,d],
-    then k [B,Hkv,d], then v [B,Hkv,d].
+    then k [B,Hkv,d], then v [B,Hkv,d];
+  * packed batches: sequence lengths log-uniform in [lo, hi] from their own
+    seeded generator, then every sequence's q, k, v as a B = 1 prefill with
+    seed + 17 * index.
 """
 from __future__ import annotations
 
@@ -84,3 +87,25 @@ def randn(shape, seed: int, dtype: str = "f32"):
     """A single seeded N(0,1) tensor (for edge-case tests)."""
     g = torch.Generator("cpu").manual_seed(seed)
     return torch.randn(*shape, generator=g, dtype=torch.float32).to(DTYPES[dtype])
+
+
+# A packed batch of sequences of different lengths (head shape of cfg3):
+# 64 sequences, lengths log-uniform in [128, 4096].
+PACKED = dict(name="packed bf16 H8 d64, 64 sequences, lengths log-uniform 128..4096", dtype="bf16", H=8, Hkv=8, d=64,
+              nseqs=64, lo=128, hi=4096, seed=3003)
+
+
+def packed_lengths(nseqs: int, lo: int, hi: int, seed: int) -> list[int]:
+    """Seeded sequence lengths, log-uniform in [lo, hi]."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    u = torch.rand(nseqs, generator=g, dtype=torch.float64)
+    lens = torch.exp(torch.log(torch.tensor(float(lo))) + u * (torch.log(torch.tensor(float(hi))) -
+                                                               torch.log(torch.tensor(float(lo)))))
+    return [int(x) for x in lens.round().clamp(lo, hi)]
+
+
+def packed_qkv(p: dict = PACKED):
+    """Per-sequence (q, k, v), each [1, heads, n_b, d], for the packed batch p."""
+    lens = packed_lengths(p["nseqs"], p["lo"], p["hi"], p["seed"])
+    return lens, [make_qkv(1, p["H"], p["Hkv"], n, p["d"], p["dtype"], p["seed"] + 17 * i) for i, n in enumerate(lens)]
+
