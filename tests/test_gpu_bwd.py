@@ -136,7 +136,10 @@ def test_bwd_directional_derivative_matches_forward_differences():
     dq, dk, dv = ops.bwd(q, k, v, out, dout)
     gen = torch.Generator(device="cpu").manual_seed(43)
     dirs = [torch.randn(t.shape, generator=gen).cuda() for t in (q, k, v)]
-    eps = 1e-3
+    # fp32 outputs carry ~1e-6 relative rounding noise, so L does too: with a step of
+    # 1e-2 that noise and the O(eps^2) truncation stay near 1e-3 of the derivative,
+    # while a dropped term or a wrong sign would be off by O(1).
+    eps = 1e-2
     fd = 0.0
     for i in range(3):
         args = [q, k, v]
@@ -146,7 +149,7 @@ def test_bwd_directional_derivative_matches_forward_differences():
         ld = (ops.fwd(*(x.contiguous() for x in dn)).double() * dout.double()).sum()
         fd = float((lu - ld) / (2 * eps))
         an = float((dirs[i].double() * (dq, dk, dv)[i].double()).sum())
-        assert abs(an - fd) <= 2e-3 * max(1.0, abs(fd)), (i, an, fd)
+        assert abs(an - fd) <= 2e-2 * max(1.0, abs(fd)), (i, an, fd)
 
 
 def test_bwd_deterministic_and_gqa_sum():
