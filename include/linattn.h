@@ -25,9 +25,13 @@
  *   - Layouts are dense row-major: q and out [B][H][N][d]; k and v
  *     [B][Hkv][N][d]; a state S [B][Hkv][d][d] with S[i][j] = sum phi(k)_i v_j;
  *     a normaliser z [B][Hkv][d].
- *   - q, k, v and out share `dtype` (LINATTN_F32 or LINATTN_BF16).  Arithmetic
- *     accumulates in fp32 and the state is always fp32.  The output is
- *     rounded once, to nearest even, when stored.
+ *   - q, k, v and out share `dtype` (LINATTN_F32, LINATTN_BF16 or
+ *     LINATTN_F16; README "Features": mixed precision).  Arithmetic
+ *     accumulates in fp32 and the state is always fp32.  fp16 rows are read
+ *     and written as fp16 and enter the matrix cores as bf16, like bf16 rows
+ *     (bf16 keeps fp32's exponent range, so the operand copies of the running
+ *     sums, which grow with the sequence, cannot overflow as fp16 would).  The
+ *     output is rounded once, to nearest even, when stored.
  *   - Supported: d in {32, 64, 128}; H % Hkv == 0; every pointer 16-byte
  *     aligned; out must not alias q, k or v.
  *   - Errors: arguments are checked before anything is enqueued; a negative
@@ -45,15 +49,15 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 5
+#define LINATTN_ABI_VERSION 6
 
-enum { LINATTN_F32 = 0, LINATTN_BF16 = 1 };
+enum { LINATTN_F32 = 0, LINATTN_BF16 = 1, LINATTN_F16 = 2 };
 
 enum {
     LINATTN_OK = 0,
     LINATTN_ERR_NULL = -1,        /* a required pointer is NULL                       */
     LINATTN_ERR_SHAPE = -2,       /* B, H, Hkv, N or d out of range, or H % Hkv != 0  */
-    LINATTN_ERR_DTYPE = -3,       /* dtype is not LINATTN_F32 / LINATTN_BF16          */
+    LINATTN_ERR_DTYPE = -3,       /* dtype is not LINATTN_F32 / _BF16 / _F16          */
     LINATTN_ERR_UNSUPPORTED = -4, /* d or chunk not supported by the kernels          */
     LINATTN_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required       */
     LINATTN_ERR_HIP = -6,         /* a HIP launch or runtime call failed              */
@@ -75,7 +79,7 @@ enum {
  *   d           head dimension, 32, 64 or 128.
  *   causal      1 causal, 0 non-causal.
  *   normalise   1 divide by phi(q_t) . z_t, 0 return the numerator only.
- *   dtype       LINATTN_F32 or LINATTN_BF16.
+ *   dtype       LINATTN_F32, LINATTN_BF16 or LINATTN_F16.
  *   state_out   nullable device fp32 [B][Hkv][d][d]: receives S_N (all N keys).
  *   z_out       nullable device fp32 [B][Hkv][d]: receives z_N.
  *   chunk       tokens per intra-chunk block: 0 = automatic, else 32, 64, 128

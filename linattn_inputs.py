@@ -8,8 +8,9 @@ fed from here, so they see bit-identical inputs.
 Recipe (no dataset is involved; the pages measure on none):
   * generator: ``torch.Generator('cpu').manual_seed(seed)``;
   * prefill: draw fp32 ``randn`` for Q [B,H,N,d], then K [B,Hkv,N,d], then
-    V [B,Hkv,N,d]; bf16 workloads round each with round-to-nearest-even
-    (``.to(torch.bfloat16)``), and the oracle reads the rounded values;
+    V [B,Hkv,N,d]; bf16 (or fp16) workloads round each with
+    round-to-nearest-even (``.to(torch.bfloat16)``), and the oracle reads the
+    rounded values;
   * decode: one generator per run, step-major: for every step draw q [B,H,d],
     then k [B,Hkv,d], then v [B,Hkv,d];
   * packed batches: sequence lengths log-uniform in [lo, hi] from their own
@@ -22,7 +23,7 @@ from dataclasses import dataclass
 
 import torch
 
-DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 @dataclass(frozen=True)

@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = [
-    "LINATTN_F32", "LINATTN_BF16", "LINATTN_OK", "LinattnError", "library_path", "load",
+    "LINATTN_F32", "LINATTN_BF16", "LINATTN_F16", "LINATTN_OK", "LinattnError", "library_path", "load",
     "linattn_fwd", "linattn_fwd_from_state", "linattn_fwd_timed", "linattn_fwd_workspace_bytes", "linattn_fwd_plan", "linattn_decode_step",
     "linattn_status_string", "linattn_abi_version", "linattn_bwd", "linattn_bwd_workspace_bytes",
     "linattn_fwd_packed", "linattn_fwd_packed_workspace_bytes",
@@ -23,6 +23,7 @@ __all__ = [
 
 LINATTN_F32 = 0
 LINATTN_BF16 = 1
+LINATTN_F16 = 2
 LINATTN_OK = 0
 ERRORS = {
     -1: "LINATTN_ERR_NULL", -2: "LINATTN_ERR_SHAPE", -3: "LINATTN_ERR_DTYPE",

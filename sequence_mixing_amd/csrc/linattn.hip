@@ -87,7 +87,7 @@ struct Main {
     __device__ static int tile_of(int w, int i) { return w * MAXST + i; }
 };
 
-template <typename T, int D, int C, int GT>
+template <typename T, int D, int C, int GT, typename IO>
 __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) void k_causal_chunks(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ out,
     const float *__restrict__ ws, float *__restrict__ state_out, float *__restrict__ z_out,
@@ -229,7 +229,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                 const int row = e / GPR, qq = e % GPR;
                 g16 fq;
 #pragma unroll
-                for (int i = 0; i < U; ++i) fq[i] = (T)phi((float)r.q[l][i]);
+                for (int i = 0; i < U; ++i) fq[i] = (T)phi(Io<T, IO>::f(r.q[l][i]));
                 sQ.write16(row, qq * U, fq);
             }
         }
@@ -237,7 +237,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
 
     // ---- prologue: chunk 0 staged, chunk 1 in flight
     load_all(ra, s0);
-    stage_rows<T, D, C, TH>(ra.k, ra.v, sK, sV, min(C, N - s0), tid);
+    stage_rows<T, D, C, TH, IO>(ra.k, ra.v, sK, sV, min(C, N - s0), tid);
     stage_q(ra);
     load_all(ra, s0 + C);
     lds_barrier();
@@ -390,7 +390,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     f32x4 x{O[4 * q4] * inv, O[4 * q4 + 1] * inv, O[4 * q4 + 2] * inv, O[4 * q4 + 3] * inv};
-                    sQ.write4(qrow, ct * 32 + 8 * q4 + 4 * h, cvt4<T>(x));
+                    sQ.write4(qrow, ct * 32 + 8 * q4 + 4 * h, out4<T, IO>(x));
                 }
             }
         };
@@ -411,7 +411,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         g16 o[M::LQ];
         read_out(o);
         if (c + 1 < nch) {
-            stage_rows<T, D, C, TH>(ra.k, ra.v, sK, sV, min(C, N - t0 - C), tid);
+            stage_rows<T, D, C, TH, IO>(ra.k, ra.v, sK, sV, min(C, N - t0 - C), tid);
             stage_q(ra);
             load_all(ra, t0 + 2 * C);  // past the segment: no access
             store_out(o, t0);
@@ -443,7 +443,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
 //
 // One workgroup per (sequence, block of 128 tokens); every wave takes whole
 // query tiles (head, 32 rows).  S and z are the sums left in slot 0 of ws.
-template <typename T, int D>
+template <typename T, int D, typename IO>
 __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restrict__ q, T *__restrict__ out,
                                                               const float *__restrict__ ws, int nslots, int H,
                                                               int Hkv, int N, int G, int nblk, int normalise,
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restric
                 g16 x = {};
                 if (t < N) x = *reinterpret_cast<const g16 *>(src + kb * 16 + h * 8 + j * U);
 #pragma unroll
-                for (int s = 0; s < U; ++s) f[j * U + s] = phi((float)x[s]);
+                for (int s = 0; s < U; ++s) f[j * U + s] = phi(Io<T, IO>::f(x[s]));
             }
             qf[kb] = cvt8<T>(f);
 #pragma unroll
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restric
                 for (int q4 = 0; q4 < 4; ++q4) {
                     f32x4 x{O[ct][4 * q4] * inv, O[ct][4 * q4 + 1] * inv, O[ct][4 * q4 + 2] * inv,
                             O[ct][4 * q4 + 3] * inv};
-                    *reinterpret_cast<typename Vt<T>::v4 *>(dst + ct * 32 + 8 * q4 + 4 * h) = cvt4<T>(x);
+                    *reinterpret_cast<typename Vt<T>::v4 *>(dst + ct * 32 + 8 * q4 + 4 * h) = out4<T, IO>(x);
                 }
         }
     }
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restric
 // in registers and written back, partial phi(q)^T S sums for 4 query heads
 // at a time are reduced through LDS, and each head's denominator is one
 // wave reduction.
-template <typename T, int D>
+template <typename T, int D, typename IO>
 __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ state, float *__restrict__ z,
                                                           const T *__restrict__ q, const T *__restrict__ k,
                                                           const T *__restrict__ v, T *__restrict__ out, int H,
@@ -601,14 +601,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
     }
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-        sk[tid * U + i] = phi((float)kg[i]);
-        sv[tid * U + i] = (float)vg[i];
+        sk[tid * U + i] = phi(Io<T, IO>::f(kg[i]));
+        sv[tid * U + i] = Io<T, IO>::f(vg[i]);
     }
 #pragma unroll
     for (int j = 0; j < QGR; ++j) {
         const int e0 = (tid + j * kThreads) * U;
 #pragma unroll
-        for (int i = 0; i < U; ++i) sqf[e0 + i] = phi((float)qg[j][i]);
+        for (int i = 0; i < U; ++i) sqf[e0 + i] = phi(Io<T, IO>::f(qg[j][i]));
     }
     lds_barrier();
 #pragma unroll
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
         const int gn = G - g0 < GMAX ? G - g0 : GMAX;
         if (g0 > 0) {
             lds_barrier();
-            for (int e = tid; e < gn * D; e += kThreads) sqf[e] = phi((float)qb[(size_t)g0 * D + e]);
+            for (int e = tid; e < gn * D; e += kThreads) sqf[e] = phi(Io<T, IO>::f(qb[(size_t)g0 * D + e]));
             __syncthreads();
         }
         // Denominators: wave wv reduces phi(q_g) . z for heads g = wv, wv + 4, ...
@@ -659,7 +659,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
 #pragma unroll
                 for (int r = 0; r < RG; ++r) num += red[r][hh][j];
                 const float o = normalise ? num / sden[h0 + hh] : num;
-                out[((size_t)b * H + (size_t)gk * G + g0 + h0 + hh) * D + j] = (T)o;
+                out[((size_t)b * H + (size_t)gk * G + g0 + h0 + hh) * D + j] = Io<T, IO>::out(o);
             }
             __syncthreads();
         }
@@ -696,7 +696,7 @@ int record(const Timing *t, int i, hipStream_t st)
 
 
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, typename IO>
 int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out, float *state_out,
             float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev, const Start &s0)
 {
@@ -719,9 +719,9 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
     }
     if (pl.causal) {
         if (pl.packed) {
-            if (launch_totals<T, D>(c1, pl.Hkv * P, st, kk, vv, ws, pl.N, pl.seg_len, 1, pk, pl.Hkv, 1))
+            if (launch_totals<T, D, IO>(c1, pl.Hkv * P, st, kk, vv, ws, pl.N, pl.seg_len, 1, pk, pl.Hkv, 1))
                 return LINATTN_ERR_UNSUPPORTED;
-        } else if (P > 1 && launch_totals<T, D>(c1, pl.nseq * (P - 1), st, kk, vv, ws, pl.N, pl.seg_len, P - 1)) {
+        } else if (P > 1 && launch_totals<T, D, IO>(c1, pl.nseq * (P - 1), st, kk, vv, ws, pl.N, pl.seg_len, P - 1)) {
             return LINATTN_ERR_UNSUPPORTED;
         }
         if (record(ev, 1, st)) return LINATTN_ERR_HIP;
@@ -735,7 +735,7 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
 #define LINATTN_MAIN(GT)                                                                                            \
     case GT:                                                                                                       \
         if constexpr (Main<T, D, C, GT>::FITS) {                                                                   \
-            hipLaunchKernelGGL((k_causal_chunks<T, D, C, GT>), grid, dim3(Main<T, D, C, GT>::TH), 0, st, qq, kk,   \
+            hipLaunchKernelGGL((k_causal_chunks<T, D, C, GT, IO>), grid, dim3(Main<T, D, C, GT>::TH), 0, st, qq, kk,   \
                                vv, oo, (const float *)ws, state_out, z_out, pl.H, pl.Hkv, pl.N, pl.G, P,           \
                                pl.seg_len, normalise, s0.S, s0.z, pk);                                             \
             break;                                                                                                 \
@@ -750,7 +750,7 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
         default: return LINATTN_ERR_UNSUPPORTED;
         }
     } else {
-        if (launch_totals<T, D>(c1, (pl.packed ? pl.Hkv : pl.nseq) * P, st, kk, vv, ws, pl.N, pl.seg_len, P, pk,
+        if (launch_totals<T, D, IO>(c1, (pl.packed ? pl.Hkv : pl.nseq) * P, st, kk, vv, ws, pl.N, pl.seg_len, P, pk,
                                 pl.Hkv, 0))
             return LINATTN_ERR_UNSUPPORTED;
         if (record(ev, 1, st)) return LINATTN_ERR_HIP;
@@ -760,7 +760,7 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
         const int nblk = (pl.N + 127) / 128;
         const unsigned grid = pl.packed ? (unsigned)(pl.Hkv * P * (pl.seg_len / 128)) : (unsigned)(pl.nseq * nblk);
         for (int rep = 0; rep < (ev ? ev->reps : 1); ++rep)
-            hipLaunchKernelGGL((k_noncausal_apply<T, D>), dim3(grid), dim3(kThreads), 0, st, qq, oo,
+            hipLaunchKernelGGL((k_noncausal_apply<T, D, IO>), dim3(grid), dim3(kThreads), 0, st, qq, oo,
                                (const float *)ws, P, pl.H, pl.Hkv, pl.N, pl.G, nblk, normalise, pk, pl.seg_len);
     }
     if (record(ev, 3, st)) return LINATTN_ERR_HIP;
@@ -773,43 +773,43 @@ constexpr bool chunk_ok()
     return Main<T, D, C, 1>::FITS || Main<T, D, C, 2>::FITS || Main<T, D, C, 4>::FITS || Main<T, D, C, 8>::FITS;
 }
 
-template <typename T, int D>
+template <typename T, int D, typename IO>
 int dispatch_chunk(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,
                    float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev,
                    const Start &s0)
 {
     switch (pl.chunk) {
     case 32:
-        if constexpr (chunk_ok<T, D, 32>()) return run_fwd<T, D, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+        if constexpr (chunk_ok<T, D, 32>()) return run_fwd<T, D, 32, IO>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
         break;
     case 64:
-        if constexpr (chunk_ok<T, D, 64>()) return run_fwd<T, D, 64>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+        if constexpr (chunk_ok<T, D, 64>()) return run_fwd<T, D, 64, IO>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
         break;
     case 128:
-        if constexpr (chunk_ok<T, D, 128>()) return run_fwd<T, D, 128>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+        if constexpr (chunk_ok<T, D, 128>()) return run_fwd<T, D, 128, IO>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
         break;
     case 256:
-        if constexpr (chunk_ok<T, D, 256>()) return run_fwd<T, D, 256>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+        if constexpr (chunk_ok<T, D, 256>()) return run_fwd<T, D, 256, IO>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
         break;
     }
     return LINATTN_ERR_UNSUPPORTED;
 }
 
-template <typename T>
+template <typename T, typename IO = T>
 int dispatch_d(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,
                float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev,
                const Start &s0)
 {
     switch (pl.d) {
-    case 32: return dispatch_chunk<T, 32>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
-    case 64: return dispatch_chunk<T, 64>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
-    case 128: return dispatch_chunk<T, 128>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+    case 32: return dispatch_chunk<T, 32, IO>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+    case 64: return dispatch_chunk<T, 64, IO>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+    case 128: return dispatch_chunk<T, 128, IO>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
     }
     return LINATTN_ERR_UNSUPPORTED;
 }
 
 
-template <typename T>
+template <typename T, typename IO = T>
 int run_decode(float *state, float *z, const void *q, const void *k, const void *v, void *out, int B, int H,
                int Hkv, int d, int normalise, hipStream_t st)
 {
@@ -820,9 +820,9 @@ int run_decode(float *state, float *z, const void *q, const void *k, const void 
     const T *vv = static_cast<const T *>(v);
     T *oo = static_cast<T *>(out);
     switch (d) {
-    case 32: hipLaunchKernelGGL((k_decode_step<T, 32>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise); break;
-    case 64: hipLaunchKernelGGL((k_decode_step<T, 64>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise); break;
-    case 128: hipLaunchKernelGGL((k_decode_step<T, 128>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise); break;
+    case 32: hipLaunchKernelGGL((k_decode_step<T, 32, IO>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise); break;
+    case 64: hipLaunchKernelGGL((k_decode_step<T, 64, IO>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise); break;
+    case 128: hipLaunchKernelGGL((k_decode_step<T, 128, IO>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise); break;
     default: return LINATTN_ERR_UNSUPPORTED;
     }
     return launch_status();
@@ -901,6 +901,8 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, int B, int 
     float *ws = static_cast<float *>(workspace);
     if (dtype == LINATTN_BF16)
         return dispatch_d<bf16>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream, ev, s0);
+    if (dtype == LINATTN_F16)
+        return dispatch_d<bf16, f16>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream, ev, s0);
     return dispatch_d<float>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream, ev, s0);
 }
 }  // namespace
@@ -968,7 +970,7 @@ int linattn_fwd_timed(const void *q, const void *k, const void *v, void *out, in
 int linattn_decode_step(float *state, float *z, const void *q, const void *k, const void *v, void *out, int B, int H,
                         int Hkv, int d, int normalise, int dtype, hipStream_t stream)
 {
-    if (dtype != LINATTN_F32 && dtype != LINATTN_BF16) return LINATTN_ERR_DTYPE;
+    if (dtype != LINATTN_F32 && dtype != LINATTN_BF16 && dtype != LINATTN_F16) return LINATTN_ERR_DTYPE;
     if (B < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || (int64_t)B * Hkv > INT32_MAX) return LINATTN_ERR_SHAPE;
     if (d != 32 && d != 64 && d != 128) return LINATTN_ERR_UNSUPPORTED;
     if (B == 0) return LINATTN_OK;
@@ -976,6 +978,8 @@ int linattn_decode_step(float *state, float *z, const void *q, const void *k, co
     if (!aligned16(state) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return LINATTN_ERR_ALIGN;
     if (dtype == LINATTN_BF16) return run_decode<bf16>(state, z, q, k, v, out, B, H, Hkv, d, normalise ? 1 : 0, stream);
+    if (dtype == LINATTN_F16)
+        return run_decode<bf16, f16>(state, z, q, k, v, out, B, H, Hkv, d, normalise ? 1 : 0, stream);
     return run_decode<float>(state, z, q, k, v, out, B, H, Hkv, d, normalise ? 1 : 0, stream);
 }
 

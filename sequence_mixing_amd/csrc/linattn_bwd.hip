@@ -164,7 +164,7 @@ __device__ __forceinline__ void load_row_scalars(float (&r)[L], const float *bas
 // inclusive z_t of every token.  Per head: den_t = phi(q_t) . z_t, g, h, then
 // dA^T on MFMA.  The next head's (or chunk's) rows are requested into
 // registers while the current one is computed.
-template <typename T, int D>
+template <typename T, int D, typename IO>
 __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const T *__restrict__ q, const T *__restrict__ k,
                                                       const T *__restrict__ v, const T *__restrict__ o,
                                                       const T *__restrict__ dout, T *__restrict__ dq,
@@ -190,10 +190,14 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
     __shared__ __attribute__((aligned(16))) T smO[OWN_O ? kBC * D : 8];
     __shared__ __attribute__((aligned(16))) T smBl[SPLIT ? kBC * D : 8];
     __shared__ __attribute__((aligned(16))) T smGl[SPLIT ? kBC * D : 8];
+    // fp16 rows: v itself is rounded to bf16 on staging, so it is split too
+    constexpr bool SPLITV = SPLIT && !std::is_same_v<T, IO>;
+    __shared__ __attribute__((aligned(16))) T smVl[SPLITV ? kBC * D : 8];
     __shared__ __attribute__((aligned(16))) float sZt[kBC * D];  // z_t of every token of the chunk, [t][i]
     __shared__ float sZp[D];                                      // z before the chunk
     __shared__ float sH[kBC];
     const Tile<T, D> sA{smA}, sB{smB}, sV{smV}, sG{smG}, sO{OWN_O ? smO : smG}, sS{smS}, sBl{smBl}, sGl{smGl};
+    const Tile<T, D> sVl{smVl};
 
     const int sq = blockIdx.x / P, p = blockIdx.x % P;  // (batch, kv head) sequence, segment
     const int bb = sq / Hkv, g = sq % Hkv;
@@ -250,10 +254,16 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
             if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
                 float bk[U];
 #pragma unroll
-                for (int i = 0; i < U; ++i) bk[i] = t < rows ? phi((float)kr[l][i]) : 0.f;
+                for (int i = 0; i < U; ++i) bk[i] = t < rows ? phi(Io<T, IO>::f(kr[l][i])) : 0.f;
                 sB.write16(t, cq, to_g16<T>(bk));
                 if constexpr (SPLIT) sBl.write16(t, cq, to_g16_lo<T>(bk));
-                sV.write16(t, cq, vr[l]);
+                sV.write16(t, cq, op16<T, IO>(vr[l]));
+                if constexpr (SPLITV) {
+                    float vf[U];
+#pragma unroll
+                    for (int ii = 0; ii < U; ++ii) vf[ii] = Io<T, IO>::f(vr[l][ii]);
+                    sVl.write16(t, cq, to_g16_lo<T>(vf));
+                }
             }
         }
         load_rows<T, D>(kr, kb, t0 + kBC, rows_of(c + 1), tid);
@@ -290,8 +300,8 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
                     float a[U], den = 0.f, dov = 0.f;
 #pragma unroll
                     for (int i = 0; i < U; ++i) {
-                        a[i] = phi((float)qr[l][i]);
-                        dov += (float)dr[l][i] * (float)orr[l][i];
+                        a[i] = phi(Io<T, IO>::f(qr[l][i]));
+                        dov += Io<T, IO>::f(dr[l][i]) * Io<T, IO>::f(orr[l][i]);
                     }
                     if (grp) {
 #pragma unroll
@@ -302,7 +312,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
                     const float inv = t < rows ? (normalise ? 1.f / den : 1.f) : 0.f;
                     float gg[U];
 #pragma unroll
-                    for (int i = 0; i < U; ++i) gg[i] = (float)dr[l][i] * inv;
+                    for (int i = 0; i < U; ++i) gg[i] = Io<T, IO>::f(dr[l][i]) * inv;
                     if (grp) {
                         sA.write16(t, cq, to_g16<T>(a));
                         sG.write16(t, cq, to_g16<T>(gg));
@@ -337,6 +347,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
                         const auto vf = sV.read8(n, kk * 16 + 8 * h);
                         mma(M, vf, sG.read8(n, kk * 16 + 8 * h));
                         if constexpr (SPLIT) mma(M, vf, sGl.read8(n, kk * 16 + 8 * h));
+                        if constexpr (SPLITV) mma(M, sVl.read8(n, kk * 16 + 8 * h), sG.read8(n, kk * 16 + 8 * h));
                     }
 #pragma unroll
                     for (int r = 0; r < 16; ++r) M[r] = (8 * (r / 4) + 4 * h + (r % 4)) <= n ? M[r] + hn : 0.f;
@@ -366,7 +377,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
                 for (int r = 0; r < 16; ++r) {
                     const int i = it * 32 + 8 * (r / 4) + 4 * h + (r % 4);
                     const float da = dacc[ui][r] + hn * sZp[i];
-                    sO.p[sO.at(n, i)] = (T)(da * fminf(1.f, (float)sA.p[sA.at(n, i)]));
+                    sO.p[sO.at(n, i)] = Io<T, IO>::out(da * fminf(1.f, (float)sA.p[sA.at(n, i)]));
                 }
             }
             if (causal && hh == G - 1) {
@@ -399,7 +410,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
 // segments; per chunk the intra-chunk terms of every head, then the carried
 // terms, then dk and dv are stored.  R lives in MFMA accumulators over the
 // waves; r in per-thread partial sums (column tid % D, a slice of the rows).
-template <typename T, int D, bool TOTALS>
+template <typename T, int D, bool TOTALS, typename IO>
 __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(const T *__restrict__ q, const T *__restrict__ k,
                                                        const T *__restrict__ v, const T *__restrict__ o,
                                                        const T *__restrict__ dout, const float *__restrict__ den,
@@ -483,9 +494,9 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
                 if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
                     float bk[U];
 #pragma unroll
-                    for (int i = 0; i < U; ++i) bk[i] = t < rows ? phi((float)kr[l][i]) : 0.f;
+                    for (int i = 0; i < U; ++i) bk[i] = t < rows ? phi(Io<T, IO>::f(kr[l][i])) : 0.f;
                     sB.write16(t, cq, to_g16<T>(bk));
-                    sV.write16(t, cq, vr[l]);
+                    sV.write16(t, cq, op16<T, IO>(vr[l]));
                 }
             }
             load_rows<T, D>(kr, kb, t0_of(j + 1), rows_of(j + 1), tid);
@@ -511,9 +522,9 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
                 float a[U], gg[U], dov = 0.f;
 #pragma unroll
                 for (int i = 0; i < U; ++i) {
-                    a[i] = real ? phi((float)qr[l][i]) : 0.f;
-                    gg[i] = (float)dr[l][i] * inv;
-                    dov += (float)dr[l][i] * (float)orr[l][i];
+                    a[i] = real ? phi(Io<T, IO>::f(qr[l][i])) : 0.f;
+                    gg[i] = Io<T, IO>::f(dr[l][i]) * inv;
+                    dov += Io<T, IO>::f(dr[l][i]) * Io<T, IO>::f(orr[l][i]);
                 }
                 dov = row_sum<GPR>(dov);
                 if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
@@ -606,12 +617,12 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
                     for (int r = 0; r < 16; ++r) {
                         const int f = (unit < BG::DT ? unit : unit - BG::DT) * 32 + 8 * (r / 4) + 4 * h + (r % 4);
                         if (unit < BG::DT) {
-                            sOV.p[sOV.at(n, f)] = (T)out[u][r];
+                            sOV.p[sOV.at(n, f)] = Io<T, IO>::out(out[u][r]);
                         } else {
                             float rf = 0.f;
 #pragma unroll
                             for (int sl = 0; sl < RS; ++sl) rf += sRp[sl * D + f];
-                            sOK.p[sOK.at(n, f)] = (T)((out[u][r] + rf) * fminf(1.f, (float)sB.p[sB.at(n, f)]));
+                            sOK.p[sOK.at(n, f)] = Io<T, IO>::out((out[u][r] + rf) * fminf(1.f, (float)sB.p[sB.at(n, f)]));
                         }
                     }
                 }
@@ -662,9 +673,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int bwd_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, BwdPlan *pl)
 {
     if (B < 0 || H <= 0 || Hkv <= 0 || N < 0 || H % Hkv != 0) return LINATTN_ERR_SHAPE;
-    if (dtype != LINATTN_F32 && dtype != LINATTN_BF16) return LINATTN_ERR_DTYPE;
+    if (dtype != LINATTN_F32 && dtype != LINATTN_BF16 && dtype != LINATTN_F16) return LINATTN_ERR_DTYPE;
     if (d != 32 && d != 64 && d != 128) return LINATTN_ERR_UNSUPPORTED;
-    const int e = dtype == LINATTN_BF16 ? 2 : 4;
+    const int e = dtype != LINATTN_F32 ? 2 : 4;
     if ((long long)N * d * e > 0x7fffffffLL) return LINATTN_ERR_SHAPE;
     BwdPlan p{};
     p.nseq = B * Hkv;
@@ -688,7 +699,7 @@ int bwd_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, BwdPlan
     return LINATTN_OK;
 }
 
-template <typename T, int D>
+template <typename T, int D, typename IO>
 int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void *k, const void *v, const void *o,
             const void *dout, void *dq, void *dk, void *dv, int causal, int normalise, char *ws, hipStream_t st)
 {
@@ -702,25 +713,25 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
     const int c1 = totals_chunk<T, D>(pl.seg_len);
     // 1. forward sums at the segment starts (or their total)
     if (causal) {
-        if (P > 1 && launch_totals<T, D>(c1, pl.nseq * (P - 1), st, kk, vv, wf, N, pl.seg_len, P - 1))
+        if (P > 1 && launch_totals<T, D, IO>(c1, pl.nseq * (P - 1), st, kk, vv, wf, N, pl.seg_len, P - 1))
             return LINATTN_ERR_UNSUPPORTED;
         if (P > 2)
             hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, wf,
                                P - 1, D, 0, (float *)nullptr, (float *)nullptr, (const float *)nullptr,
                                (const float *)nullptr);
     } else {
-        if (launch_totals<T, D>(c1, pl.nseq * P, st, kk, vv, wf, N, pl.seg_len, P)) return LINATTN_ERR_UNSUPPORTED;
+        if (launch_totals<T, D, IO>(c1, pl.nseq * P, st, kk, vv, wf, N, pl.seg_len, P)) return LINATTN_ERR_UNSUPPORTED;
         hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, wf, P, D,
                            1, (float *)nullptr, (float *)nullptr, (const float *)nullptr, (const float *)nullptr);
     }
     // 2. dq (and den)
-    hipLaunchKernelGGL((k_bwd_dq<T, D>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo, dd,
+    hipLaunchKernelGGL((k_bwd_dq<T, D, IO>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo, dd,
                        static_cast<T *>(dq), wden, (const float *)wf, H, Hkv, N, pl.G, P, pl.seg_len, causal,
                        normalise);
     // 3. sums of a g^T and h a per segment: causal segments 1..P-1, suffix scan
     if (causal) {
         if (P > 1) {
-            hipLaunchKernelGGL((k_bwd_dkv<T, D, true>), dim3(pl.nseq * (P - 1)), dim3(kThreads), 0, st, qq, kk, vv,
+            hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * (P - 1)), dim3(kThreads), 0, st, qq, kk, vv,
                                oo, dd, (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P,
                                pl.seg_len, causal, normalise, P - 1, 1);
             if (P > 2)
@@ -729,28 +740,28 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
                                    (const float *)nullptr);
         }
     } else {
-        hipLaunchKernelGGL((k_bwd_dkv<T, D, true>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo, dd,
+        hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo, dd,
                            (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P, pl.seg_len,
                            causal, normalise, P, 0);
         hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, wr, P, D,
                            1, (float *)nullptr, (float *)nullptr, (const float *)nullptr, (const float *)nullptr);
     }
     // 4. dk, dv
-    hipLaunchKernelGGL((k_bwd_dkv<T, D, false>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo, dd,
+    hipLaunchKernelGGL((k_bwd_dkv<T, D, false, IO>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo, dd,
                        (const float *)wden, static_cast<T *>(dk), static_cast<T *>(dv), wr, H, Hkv, N, pl.G, P,
                        pl.seg_len, causal, normalise, P, 0);
     return launch_status();
 }
 
-template <typename T>
+template <typename T, typename IO = T>
 int dispatch_bwd(const BwdPlan &pl, int d, int H, int Hkv, int N, const void *q, const void *k, const void *v,
                  const void *o, const void *dout, void *dq, void *dk, void *dv, int causal, int normalise, char *ws,
                  hipStream_t st)
 {
     switch (d) {
-    case 32: return run_bwd<T, 32>(pl, H, Hkv, N, q, k, v, o, dout, dq, dk, dv, causal, normalise, ws, st);
-    case 64: return run_bwd<T, 64>(pl, H, Hkv, N, q, k, v, o, dout, dq, dk, dv, causal, normalise, ws, st);
-    case 128: return run_bwd<T, 128>(pl, H, Hkv, N, q, k, v, o, dout, dq, dk, dv, causal, normalise, ws, st);
+    case 32: return run_bwd<T, 32, IO>(pl, H, Hkv, N, q, k, v, o, dout, dq, dk, dv, causal, normalise, ws, st);
+    case 64: return run_bwd<T, 64, IO>(pl, H, Hkv, N, q, k, v, o, dout, dq, dk, dv, causal, normalise, ws, st);
+    case 128: return run_bwd<T, 128, IO>(pl, H, Hkv, N, q, k, v, o, dout, dq, dk, dv, causal, normalise, ws, st);
     }
     return LINATTN_ERR_UNSUPPORTED;
 }
@@ -782,6 +793,8 @@ int linattn_bwd(const void *q, const void *k, const void *v, const void *out, co
         return LINATTN_ERR_ALIGN;
     if (!workspace || workspace_bytes < pl.bytes) return LINATTN_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
+    if (dtype == LINATTN_F16)
+        return dispatch_bwd<bf16, f16>(pl, d, H, Hkv, N, q, k, v, out, dout, dq, dk, dv, causal, normalise, ws, stream);
     if (dtype == LINATTN_BF16)
         return dispatch_bwd<bf16>(pl, d, H, Hkv, N, q, k, v, out, dout, dq, dk, dv, causal, normalise, ws, stream);
     return dispatch_bwd<float>(pl, d, H, Hkv, N, q, k, v, out, dout, dq, dk, dv, causal, normalise, ws, stream);

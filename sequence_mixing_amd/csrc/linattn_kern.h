@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "linattn.h"
 
 namespace {
@@ -98,6 +100,32 @@ __device__ __forceinline__ f32x8 cat(const f32x4 &a, const f32x4 &b)
     return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// ------------------------------------------------------------ input/output
+//
+// Rows in memory may be fp16 while the matrix-core operands of the 16-bit
+// kernels are bf16 (T = bf16, IO = fp16): bf16 keeps fp32's exponent range, so
+// the operand copies of the running sums (which grow with the sequence) stay
+// finite where fp16 would overflow.  Registers hold the raw 16-byte groups;
+// these convert them at the loads and stores.  IO = T is the plain case.
+typedef _Float16 f16;
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+template <typename T, typename IO> struct Io {
+    static_assert(std::is_same_v<T, IO> || (std::is_same_v<T, bf16> && std::is_same_v<IO, f16>), "I/O type");
+    static constexpr bool SAME = std::is_same_v<T, IO>;
+    // element (raw bits in a T) -> float
+    static __device__ __forceinline__ float f(T x)
+    {
+        if constexpr (SAME) return (float)x;
+        else return (float)__builtin_bit_cast(IO, x);
+    }
+    // float -> the stored element (IO bits in a T)
+    static __device__ __forceinline__ T out(float x)
+    {
+        if constexpr (SAME) return (T)x;
+        else return __builtin_bit_cast(T, (IO)x);
+    }
+};
+
 template <typename E> __device__ __forceinline__ typename Vt<E>::v8 cvt8(const float *x);
 template <> __device__ __forceinline__ bf16x8 cvt8<bf16>(const float *x)
 {
@@ -111,6 +139,25 @@ template <> __device__ __forceinline__ f32x8 cvt8<float>(const float *x)
 template <typename E> __device__ __forceinline__ typename Vt<E>::v4 cvt4(f32x4 x);
 template <> __device__ __forceinline__ bf16x4 cvt4<bf16>(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
 template <> __device__ __forceinline__ f32x4 cvt4<float>(f32x4 x) { return x; }
+
+// Four results -> four stored elements of I/O type IO (in T-typed storage).
+template <typename T, typename IO> __device__ __forceinline__ typename Vt<T>::v4 out4(f32x4 x)
+{
+    if constexpr (std::is_same_v<T, IO>) return cvt4<T>(x);
+    else return __builtin_bit_cast(bf16x4, __builtin_convertvector(x, f16x4));
+}
+// A raw 16-byte group of IO elements -> the same values as operands of type T.
+template <typename T, typename IO> __device__ __forceinline__ typename Vt<T>::g16 op16(const typename Vt<T>::g16 &g)
+{
+    if constexpr (std::is_same_v<T, IO>) {
+        return g;
+    } else {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = Io<T, IO>::f(g[i]);
+        return cvt8<T>(x);
+    }
+}
 
 // ---------------------------------------------------------- LDS tiles
 //
@@ -230,7 +277,7 @@ __device__ __forceinline__ void load_chunk(typename Vt<T>::g16 (&r)[L], const T 
 // Writes a staged chunk to LDS: phi(K) and V, both row-major.  Only the
 // first `rows` tokens are real; the others get phi(k) = 0 (their v is zero
 // too) so that they add nothing to any sum.
-template <typename T, int D, int C, int TH, int L>
+template <typename T, int D, int C, int TH, typename IO, int L>
 __device__ __forceinline__ void stage_rows(const typename Vt<T>::g16 (&kr)[L], const typename Vt<T>::g16 (&vr)[L],
                                            Tile<T, D> sK, Tile<T, D> sV, int rows, int tid)
 {
@@ -244,12 +291,12 @@ __device__ __forceinline__ void stage_rows(const typename Vt<T>::g16 (&kr)[L], c
             const int t = e / GPR, q = e % GPR;
             typename Vt<T>::g16 fk;
 #pragma unroll
-            for (int i = 0; i < U; ++i) fk[i] = (T)phi((float)kr[l][i]);
+            for (int i = 0; i < U; ++i) fk[i] = (T)phi(Io<T, IO>::f(kr[l][i]));
             if (!full) {
                 if (t >= rows) fk = typename Vt<T>::g16{};
             }
             sK.write16(t, q * U, fk);
-            sV.write16(t, q * U, vr[l]);
+            sV.write16(t, q * U, op16<T, IO>(vr[l]));
         }
     }
 }
@@ -400,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void k_pack_plan(const int *__restrict__ 
 // Chunks of C1 tokens, double-buffered in LDS (one barrier per chunk).
 // Packed batches (pk.tab set): one workgroup per (kv head, segment of all
 // sequences); the last segment of a causal sequence has nothing to do.
-template <typename T, int D, int C1>
+template <typename T, int D, int C1, typename IO>
 __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict__ k, const T *__restrict__ v,
                                                             float *__restrict__ ws, int N, int seg_len, int nslots,
                                                             Packed pk, int Hkv, int causal)
@@ -468,11 +515,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
     // Chunks in pairs; with an odd count the last pair's second chunk lies
     // past the segment and adds zeros (every step issues the same loads).
     for (int ci = 0; ci < nch; ci += 2) {
-        stage_rows<T, D, C1, kThreads>(kA, vA, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, rows_at(s0 + ci * C1), tid);
+        stage_rows<T, D, C1, kThreads, IO>(kA, vA, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, rows_at(s0 + ci * C1), tid);
         load(kA, vA, s0 + (ci + 2) * C1);
         lds_barrier();
         absorb(0);
-        stage_rows<T, D, C1, kThreads>(kB, vB, Tile<T, D>{smK[1]}, Tile<T, D>{smV[1]}, rows_at(s0 + (ci + 1) * C1), tid);
+        stage_rows<T, D, C1, kThreads, IO>(kB, vB, Tile<T, D>{smK[1]}, Tile<T, D>{smV[1]}, rows_at(s0 + (ci + 1) * C1), tid);
         load(kB, vB, s0 + (ci + 3) * C1);
         lds_barrier();
         absorb(1);
@@ -565,26 +612,26 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Totals pass with chunks of c1 tokens (32, 64 or 128; at most 16 KiB of K per
 // chunk, so that two chunks of K and V double-buffer in 64 KiB of LDS).
-template <typename T, int D>
+template <typename T, int D, typename IO = T>
 int launch_totals(int c1, unsigned nblocks, hipStream_t st, const T *k, const T *v, float *ws, int N, int seg_len,
                   int nslots, Packed pk = Packed{nullptr, 0, 0}, int Hkv = 1, int causal = 1)
 {
     constexpr int cap = 65536 / (4 * D * (int)sizeof(T));
     switch (c1) {
     case 32:
-        hipLaunchKernelGGL((k_seg_totals<T, D, 32>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len, nslots,
+        hipLaunchKernelGGL((k_seg_totals<T, D, 32, IO>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len, nslots,
                            pk, Hkv, causal);
         return LINATTN_OK;
     case 64:
         if constexpr (64 <= cap) {
-            hipLaunchKernelGGL((k_seg_totals<T, D, 64>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len,
+            hipLaunchKernelGGL((k_seg_totals<T, D, 64, IO>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len,
                                nslots, pk, Hkv, causal);
             return LINATTN_OK;
         }
         break;
     case 128:
         if constexpr (128 <= cap) {
-            hipLaunchKernelGGL((k_seg_totals<T, D, 128>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len,
+            hipLaunchKernelGGL((k_seg_totals<T, D, 128, IO>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len,
                                nslots, pk, Hkv, causal);
             return LINATTN_OK;
         }

@@ -6,11 +6,11 @@ from __future__ import annotations
 
 import torch
 
-from . import (LINATTN_BF16, LINATTN_F32, LinattnError, linattn_bwd, linattn_bwd_workspace_bytes,
+from . import (LINATTN_BF16, LINATTN_F16, LINATTN_F32, LinattnError, linattn_bwd, linattn_bwd_workspace_bytes,
                linattn_decode_step, linattn_fwd, linattn_fwd_from_state, linattn_fwd_packed,
                linattn_fwd_packed_workspace_bytes, linattn_fwd_workspace_bytes)
 
-_DT = {torch.float32: LINATTN_F32, torch.bfloat16: LINATTN_BF16}
+_DT = {torch.float32: LINATTN_F32, torch.bfloat16: LINATTN_BF16, torch.float16: LINATTN_F16}
 
 
 def dtype_code(t: torch.dtype) -> int:

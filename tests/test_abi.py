@@ -142,7 +142,7 @@ def test_auto_chunk_choices():
         assert la.linattn_fwd_plan(*args, c)[0] == 0
     # every group size, head dimension and dtype (planning runs on the host:
     # a bad automatic choice would show up here, not on the GPU)
-    for dt in (F32, BF16):
+    for dt in (F32, BF16, la.LINATTN_F16):
         for d in (32, 64, 128):
             for G in (1, 2, 3, 4, 5, 6, 8, 12, 16, 32):
                 for causal in (0, 1):
@@ -177,3 +177,12 @@ def test_packed_argtypes_match_header():
         assert m, name
         nparams = len([p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"])
         assert len(getattr(lib, name).argtypes) == nparams, name
+
+
+def test_fp16_plans_like_bf16():
+    """fp16 rows take the 16-bit kernels: the same chunk, segments and workspace as bf16."""
+    for args in [(2, 8, 8, 4096, 64, 1), (1, 32, 8, 32768, 128, 1), (2, 8, 8, 4096, 64, 0), (3, 6, 2, 777, 32, 1)]:
+        assert la.linattn_fwd_plan(*args, la.LINATTN_F16) == la.linattn_fwd_plan(*args, la.LINATTN_BF16)
+        assert la.linattn_fwd_workspace_bytes(*args, la.LINATTN_F16) == la.linattn_fwd_workspace_bytes(*args, la.LINATTN_BF16)
+        assert la.linattn_bwd_workspace_bytes(*args, la.LINATTN_F16) == la.linattn_bwd_workspace_bytes(*args, la.LINATTN_BF16)
+    assert la.linattn_fwd_plan(1, 2, 2, 16, 64, 1, 3)[0] == -3

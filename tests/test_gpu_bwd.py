@@ -23,8 +23,8 @@ pytestmark = pytest.mark.gpu
 # to bf16 (2^-9 relative), and dq, dk subtract the normaliser term from the
 # value term, which amplifies those roundings by a small factor; measured
 # worst rows stay under 2e-2, the bar is 3e-2.
-TOL = {"f32": 1e-4, "bf16": 3e-2}
-TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
+TOL = {"f32": 1e-4, "bf16": 3e-2, "f16": 3e-2}
+TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def rows_rel_err(got, ref, scale):
@@ -89,6 +89,8 @@ SMALL = [
     (2, 6, 2, 300, 64, "bf16"),
     (1, 8, 1, 500, 64, "f32"),
     (2, 2, 2, 7, 64, "bf16"),
+    (2, 4, 2, 257, 64, "f16"),
+    (1, 8, 2, 600, 128, "f16"),
 ]
 
 
