@@ -51,6 +51,8 @@ def _load():
             build(force=False)
         lib = ctypes.CDLL(path)
         dp = ctypes.POINTER(ctypes.c_double)
+        lib.linattn_ref_set_feature_map.restype = ctypes.c_int
+        lib.linattn_ref_set_feature_map.argtypes = [ctypes.c_int]
         lib.linattn_ref_phi.restype = ctypes.c_double
         lib.linattn_ref_phi.argtypes = [ctypes.c_double]
         lib.linattn_ref_fwd.restype = ctypes.c_int
@@ -89,13 +91,35 @@ def default_threads() -> int:
         return os.cpu_count() or 1
 
 
-def phi(x: float) -> float:
-    """phi(x) = ELU(x) + 1 with alpha = 1, evaluated by the C oracle."""
-    return _load().linattn_ref_phi(float(x))
+# Feature maps the oracle knows: the README's ELU + 1 (the default), ReLU, softplus.
+FEATURE_MAPS = {"elu1": 0, "relu": 1, "softplus": 2}
+
+
+def _use(phi_map: str):
+    if _load().linattn_ref_set_feature_map(FEATURE_MAPS[phi_map]) != 0:
+        raise ValueError(phi_map)
+
+
+def dphi(x: float, phi_map: str = "elu1") -> float:
+    """d phi / dx of the selected feature map, evaluated by the C oracle."""
+    _use(phi_map)
+    try:
+        return _load().linattn_ref_dphi(float(x))
+    finally:
+        _use("elu1")
+
+
+def phi(x: float, phi_map: str = "elu1") -> float:
+    """The selected feature map (default ELU + 1), evaluated by the C oracle."""
+    _use(phi_map)
+    try:
+        return _load().linattn_ref_phi(float(x))
+    finally:
+        _use("elu1")
 
 
 def ref_fwd(q, k, v, causal: bool = True, normalise: bool = True,
-            want_state: bool = False, nthreads: int | None = None, state_in=None, z_in=None):
+            want_state: bool = False, nthreads: int | None = None, state_in=None, z_in=None, phi_map: str = "elu1"):
     """Forward pass.  q [B,H,N,d], k/v [B,Hkv,N,d] -> out [B,H,N,d] (fp64).
 
     With ``want_state`` also returns S_N [B,Hkv,d,d] and z_N [B,Hkv,d].
@@ -113,15 +137,20 @@ def ref_fwd(q, k, v, causal: bool = True, normalise: bool = True,
     out = np.zeros((B, H, N, d), dtype=np.float64)
     S = np.zeros((B, Hkv, d, d), dtype=np.float64) if want_state else None
     z = np.zeros((B, Hkv, d), dtype=np.float64) if want_state else None
-    rc = _load().linattn_ref_fwd_from(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, N, d,
-                                      int(bool(causal)), int(bool(normalise)), _ptr(Si), _ptr(zi),
-                                      _ptr(S), _ptr(z), nthreads or default_threads())
+    _use(phi_map)
+    try:
+        rc = _load().linattn_ref_fwd_from(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, N, d,
+                                          int(bool(causal)), int(bool(normalise)), _ptr(Si), _ptr(zi),
+                                          _ptr(S), _ptr(z), nthreads or default_threads())
+    finally:
+        _use("elu1")
     if rc != 0:
         raise ValueError(f"linattn_ref_fwd_from rejected its arguments (rc={rc})")
     return (out, S, z) if want_state else out
 
 
-def ref_bwd(q, k, v, out, dout, causal: bool = True, normalise: bool = True, nthreads: int | None = None):
+def ref_bwd(q, k, v, out, dout, causal: bool = True, normalise: bool = True, nthreads: int | None = None,
+            phi_map: str = "elu1"):
     """Backward pass.  q/out/dout [B,H,N,d], k/v [B,Hkv,N,d] -> (dq, dk, dv) in fp64.
 
     ``out`` is the forward output the gradient of the normaliser uses (may be
@@ -135,15 +164,19 @@ def ref_bwd(q, k, v, out, dout, causal: bool = True, normalise: bool = True, nth
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    rc = _load().linattn_ref_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-                                 B, H, Hkv, N, d, int(bool(causal)), int(bool(normalise)),
-                                 nthreads or default_threads())
+    _use(phi_map)
+    try:
+        rc = _load().linattn_ref_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                     B, H, Hkv, N, d, int(bool(causal)), int(bool(normalise)),
+                                     nthreads or default_threads())
+    finally:
+        _use("elu1")
     if rc != 0:
         raise ValueError(f"linattn_ref_bwd rejected its arguments (rc={rc})")
     return dq, dk, dv
 
 
-def ref_decode_step(S: np.ndarray, z: np.ndarray | None, q, k, v, normalise: bool = True):
+def ref_decode_step(S: np.ndarray, z: np.ndarray | None, q, k, v, normalise: bool = True, phi_map: str = "elu1"):
     """One decode step; S [B,Hkv,d,d] and z [B,Hkv,d] (fp64) are updated in place.
 
     q [B,H,d], k/v [B,Hkv,d]; returns out [B,H,d] (fp64).
@@ -155,8 +188,12 @@ def ref_decode_step(S: np.ndarray, z: np.ndarray | None, q, k, v, normalise: boo
     B, H, d = q.shape
     Hkv = k.shape[1]
     out = np.zeros((B, H, d), dtype=np.float64)
-    rc = _load().linattn_ref_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                                         B, H, Hkv, d, int(bool(normalise)))
+    _use(phi_map)
+    try:
+        rc = _load().linattn_ref_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                             B, H, Hkv, d, int(bool(normalise)))
+    finally:
+        _use("elu1")
     if rc != 0:
         raise ValueError(f"linattn_ref_decode_step rejected its arguments (rc={rc})")
     return out

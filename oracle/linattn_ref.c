@@ -14,7 +14,8 @@
  *   - attention output O = phi(Q) (phi(K)^T V), i.e. the key/value product is
  *     formed first and then applied to the queries;
  *   - phi(x) = ELU(x) + 1 with the usual alpha = 1, so phi(x) = x + 1 for
- *     x > 0 and exp(x) otherwise (always positive);
+ *     x > 0 and exp(x) otherwise (always positive); ReLU and softplus may be
+ *     selected instead (README "Features", custom kernel plugins);
  *   - causal form (README "Features" list, the causal-masking item): query t
  *     only sees keys s <= t.  Written as a running state
  *         S_t = sum_{s<=t} phi(k_s) v_s^T   (d x d)
@@ -52,9 +53,25 @@
 
 #define REF_COLBLOCK 16
 
-/* phi(x) = ELU(x) + 1, alpha = 1. */
+/*
+ * The feature map (README "Features", custom kernel plugins: phi can be
+ * replaced).  0: ELU(x) + 1 with alpha = 1, the README's phi; 1: ReLU(x);
+ * 2: softplus(x) = log(1 + e^x).  Selected for every later call with
+ * linattn_ref_set_feature_map (the checker is driven from one thread).
+ */
+static int g_feature_map = 0;
+
+int linattn_ref_set_feature_map(int kind)
+{
+    if (kind < 0 || kind > 2) return -1;
+    g_feature_map = kind;
+    return 0;
+}
+
 double linattn_ref_phi(double x)
 {
+    if (g_feature_map == 1) return x > 0.0 ? x : 0.0;
+    if (g_feature_map == 2) return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
     return x > 0.0 ? x + 1.0 : exp(x);
 }
 
@@ -239,9 +256,12 @@ int linattn_ref_decode_step(double *state, double *z, const double *q, const dou
     return 0;
 }
 
-/* d phi / dx: 1 for x > 0, exp(x) otherwise (both sides give 1 at 0). */
+/* d phi / dx.  ELU + 1: 1 for x > 0, exp(x) otherwise (both sides give 1 at
+ * 0); ReLU: 1 for x > 0, else 0; softplus: the logistic function. */
 double linattn_ref_dphi(double x)
 {
+    if (g_feature_map == 1) return x > 0.0 ? 1.0 : 0.0;
+    if (g_feature_map == 2) return 1.0 / (1.0 + exp(-x));
     return x > 0.0 ? 1.0 : exp(x);
 }
 

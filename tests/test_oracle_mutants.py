@@ -102,6 +102,11 @@ MUTANTS = {
     "bwd_dv_reads_R_transposed": lambda s: s.replace("acc += R[(size_t)i * d + j] * f[i];",
                                                      "acc += R[(size_t)j * d + i] * f[i];"),
     "bwd_gradient_not_divided_by_denominator": lambda s: s.replace("gt[j] = dot[j] / den;", "gt[j] = dot[j];"),
+    "softplus_positive_branch_sign": lambda s: s.replace("x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x))",
+                                                         "x > 0.0 ? x + log1p(exp(x)) : log1p(exp(x))"),
+    "relu_keeps_negatives": lambda s: s.replace("if (g_feature_map == 1) return x > 0.0 ? x : 0.0;",
+                                                "if (g_feature_map == 1) return x > -0.5 ? x : 0.0;"),
+    "softplus_derivative_sign": lambda s: s.replace("return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(x));"),
 }
 
 
@@ -117,6 +122,7 @@ def test_pins_catch_mutant(name, tmp_path):
                     "-lm", "-lpthread"], check=True)
     env = dict(os.environ, LINATTN_REF_LIB=str(so_path))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle.py"), os.path.join(ROOT, "tests", "test_oracle_bwd.py")],
+                        os.path.join(ROOT, "tests", "test_oracle.py"), os.path.join(ROOT, "tests", "test_oracle_bwd.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_phi.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the oracle pins:\n{r.stdout[-2000:]}"
