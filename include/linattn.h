@@ -49,15 +49,22 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 6
+#define LINATTN_ABI_VERSION 7
 
 enum { LINATTN_F32 = 0, LINATTN_BF16 = 1, LINATTN_F16 = 2 };
+/* Feature maps phi (README "Features": custom kernel plugins, phi
+ * replaceable): ELU(x) + 1 (the README's, the default), ReLU(x) (a normalised
+ * row whose query or keys are all <= 0 divides by zero), softplus(x) =
+ * log(1 + e^x).  Every `dtype` argument below carries the element type in
+ * bits 0-7 and the feature map in bits 8-15: LINATTN_DTYPE(elem, phi). */
+enum { LINATTN_PHI_ELU1 = 0, LINATTN_PHI_RELU = 1, LINATTN_PHI_SOFTPLUS = 2 };
+#define LINATTN_DTYPE(elem, phi) ((elem) | ((phi) << 8))
 
 enum {
     LINATTN_OK = 0,
     LINATTN_ERR_NULL = -1,        /* a required pointer is NULL                       */
     LINATTN_ERR_SHAPE = -2,       /* B, H, Hkv, N or d out of range, or H % Hkv != 0  */
-    LINATTN_ERR_DTYPE = -3,       /* dtype is not LINATTN_F32 / _BF16 / _F16          */
+    LINATTN_ERR_DTYPE = -3,       /* unknown element type or feature map in dtype     */
     LINATTN_ERR_UNSUPPORTED = -4, /* d or chunk not supported by the kernels          */
     LINATTN_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required       */
     LINATTN_ERR_HIP = -6,         /* a HIP launch or runtime call failed              */

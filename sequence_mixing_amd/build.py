@@ -26,19 +26,38 @@ SOURCES = [os.path.join(CSRC, "linattn.hip"), os.path.join(CSRC, "linattn_bwd.hi
            os.path.join(CSRC, "linattn_plan.cpp")]
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str = LIB) -> str:
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; drop that noise.
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    return r.returncode, err
+
+
+def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str = LIB) -> str:
+    """Compiles every source to an object in parallel, then links the library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objs = [out + "." + os.path.basename(src) + ".o" for src in SOURCES]
+    cmds = [[HIPCC, *FLAGS, *(extra_flags or []), "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+    cmds = [[a for a in c if a != "-shared"] for c in cmds]
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        results = list(ex.map(_run, cmds))
+    for (rc, err), src in zip(results, SOURCES):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {os.path.basename(src)} ({rc}):\n{err}")
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+    tmp = out + ".tmp"
+    rc, err = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    for obj in objs:
+        if os.path.exists(obj):
+            os.remove(obj)
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{err}")
     os.replace(tmp, out)
     return out
 

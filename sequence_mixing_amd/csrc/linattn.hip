@@ -229,7 +229,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                 const int row = e / GPR, qq = e % GPR;
                 g16 fq;
 #pragma unroll
-                for (int i = 0; i < U; ++i) fq[i] = (T)phi(Io<T, IO>::f(r.q[l][i]));
+                for (int i = 0; i < U; ++i) fq[i] = (T)IO::phi::f(Io<T, IO>::f(r.q[l][i]));
                 sQ.write16(row, qq * U, fq);
             }
         }
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restric
                 g16 x = {};
                 if (t < N) x = *reinterpret_cast<const g16 *>(src + kb * 16 + h * 8 + j * U);
 #pragma unroll
-                for (int s = 0; s < U; ++s) f[j * U + s] = phi(Io<T, IO>::f(x[s]));
+                for (int s = 0; s < U; ++s) f[j * U + s] = IO::phi::f(Io<T, IO>::f(x[s]));
             }
             qf[kb] = cvt8<T>(f);
 #pragma unroll
@@ -601,14 +601,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
     }
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-        sk[tid * U + i] = phi(Io<T, IO>::f(kg[i]));
+        sk[tid * U + i] = IO::phi::f(Io<T, IO>::f(kg[i]));
         sv[tid * U + i] = Io<T, IO>::f(vg[i]);
     }
 #pragma unroll
     for (int j = 0; j < QGR; ++j) {
         const int e0 = (tid + j * kThreads) * U;
 #pragma unroll
-        for (int i = 0; i < U; ++i) sqf[e0 + i] = phi(Io<T, IO>::f(qg[j][i]));
+        for (int i = 0; i < U; ++i) sqf[e0 + i] = IO::phi::f(Io<T, IO>::f(qg[j][i]));
     }
     lds_barrier();
 #pragma unroll
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
         const int gn = G - g0 < GMAX ? G - g0 : GMAX;
         if (g0 > 0) {
             lds_barrier();
-            for (int e = tid; e < gn * D; e += kThreads) sqf[e] = phi(Io<T, IO>::f(qb[(size_t)g0 * D + e]));
+            for (int e = tid; e < gn * D; e += kThreads) sqf[e] = IO::phi::f(Io<T, IO>::f(qb[(size_t)g0 * D + e]));
             __syncthreads();
         }
         // Denominators: wave wv reduces phi(q_g) . z for heads g = wv, wv + 4, ...
@@ -795,7 +795,7 @@ int dispatch_chunk(const linattn::Plan &pl, const void *q, const void *k, const 
     return LINATTN_ERR_UNSUPPORTED;
 }
 
-template <typename T, typename IO = T>
+template <typename T, typename IO = Fmt<T, PhiElu1>>
 int dispatch_d(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,
                float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev,
                const Start &s0)
@@ -809,7 +809,7 @@ int dispatch_d(const linattn::Plan &pl, const void *q, const void *k, const void
 }
 
 
-template <typename T, typename IO = T>
+template <typename T, typename IO = Fmt<T, PhiElu1>>
 int run_decode(float *state, float *z, const void *q, const void *k, const void *v, void *out, int B, int H,
                int Hkv, int d, int normalise, hipStream_t st)
 {
@@ -899,11 +899,11 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, int B, int 
         return launch_status();
     }
     float *ws = static_cast<float *>(workspace);
-    if (dtype == LINATTN_BF16)
-        return dispatch_d<bf16>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream, ev, s0);
-    if (dtype == LINATTN_F16)
-        return dispatch_d<bf16, f16>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream, ev, s0);
-    return dispatch_d<float>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0, stream, ev, s0);
+    return with_format(dtype, [&](auto kind) {
+        using K = decltype(kind);
+        return dispatch_d<typename K::T, typename K::IO>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0,
+                                                         stream, ev, s0);
+    });
 }
 }  // namespace
 
@@ -970,17 +970,18 @@ int linattn_fwd_timed(const void *q, const void *k, const void *v, void *out, in
 int linattn_decode_step(float *state, float *z, const void *q, const void *k, const void *v, void *out, int B, int H,
                         int Hkv, int d, int normalise, int dtype, hipStream_t stream)
 {
-    if (dtype != LINATTN_F32 && dtype != LINATTN_BF16 && dtype != LINATTN_F16) return LINATTN_ERR_DTYPE;
+    if (!valid_dtype(dtype)) return LINATTN_ERR_DTYPE;
     if (B < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || (int64_t)B * Hkv > INT32_MAX) return LINATTN_ERR_SHAPE;
     if (d != 32 && d != 64 && d != 128) return LINATTN_ERR_UNSUPPORTED;
     if (B == 0) return LINATTN_OK;
     if (!state || !q || !k || !v || !out || (normalise && !z)) return LINATTN_ERR_NULL;
     if (!aligned16(state) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return LINATTN_ERR_ALIGN;
-    if (dtype == LINATTN_BF16) return run_decode<bf16>(state, z, q, k, v, out, B, H, Hkv, d, normalise ? 1 : 0, stream);
-    if (dtype == LINATTN_F16)
-        return run_decode<bf16, f16>(state, z, q, k, v, out, B, H, Hkv, d, normalise ? 1 : 0, stream);
-    return run_decode<float>(state, z, q, k, v, out, B, H, Hkv, d, normalise ? 1 : 0, stream);
+    return with_format(dtype, [&](auto kind) {
+        using K = decltype(kind);
+        return run_decode<typename K::T, typename K::IO>(state, z, q, k, v, out, B, H, Hkv, d, normalise ? 1 : 0,
+                                                         stream);
+    });
 }
 
 }  // extern "C"

@@ -14,7 +14,8 @@
 //   dv_s = R_s^T b_s,  dk_s = (R_s v_s + r_s) * phi'(k_s)
 // with R_s = sum_{t>=s} a_t g_t^T and r_s = sum_{t>=s} h_t a_t over the query
 // heads of the kv group (non-causal: every sum runs over the whole sequence).
-// phi'(x) = 1 for x > 0 and exp(x) = phi(x) otherwise, i.e. min(1, phi(x)).
+// phi'(x) is taken from phi(x) (the feature map's df): for ELU + 1, 1 for
+// x > 0 and exp(x) = phi(x) otherwise, i.e. min(1, phi(x)).
 //
 // Workgroups hand data over through LDS with lds_barrier(), which leaves the
 // global loads of the next head or chunk in flight across the barrier.
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
     __shared__ __attribute__((aligned(16))) T smBl[SPLIT ? kBC * D : 8];
     __shared__ __attribute__((aligned(16))) T smGl[SPLIT ? kBC * D : 8];
     // fp16 rows: v itself is rounded to bf16 on staging, so it is split too
-    constexpr bool SPLITV = SPLIT && !std::is_same_v<T, IO>;
+    constexpr bool SPLITV = SPLIT && !std::is_same_v<T, typename IO::elem>;
     __shared__ __attribute__((aligned(16))) T smVl[SPLITV ? kBC * D : 8];
     __shared__ __attribute__((aligned(16))) float sZt[kBC * D];  // z_t of every token of the chunk, [t][i]
     __shared__ float sZp[D];                                      // z before the chunk
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
             if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
                 float bk[U];
 #pragma unroll
-                for (int i = 0; i < U; ++i) bk[i] = t < rows ? phi(Io<T, IO>::f(kr[l][i])) : 0.f;
+                for (int i = 0; i < U; ++i) bk[i] = t < rows ? IO::phi::f(Io<T, IO>::f(kr[l][i])) : 0.f;
                 sB.write16(t, cq, to_g16<T>(bk));
                 if constexpr (SPLIT) sBl.write16(t, cq, to_g16_lo<T>(bk));
                 sV.write16(t, cq, op16<T, IO>(vr[l]));
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
                     float a[U], den = 0.f, dov = 0.f;
 #pragma unroll
                     for (int i = 0; i < U; ++i) {
-                        a[i] = phi(Io<T, IO>::f(qr[l][i]));
+                        a[i] = IO::phi::f(Io<T, IO>::f(qr[l][i]));
                         dov += Io<T, IO>::f(dr[l][i]) * Io<T, IO>::f(orr[l][i]);
                     }
                     if (grp) {
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
                 for (int r = 0; r < 16; ++r) {
                     const int i = it * 32 + 8 * (r / 4) + 4 * h + (r % 4);
                     const float da = dacc[ui][r] + hn * sZp[i];
-                    sO.p[sO.at(n, i)] = Io<T, IO>::out(da * fminf(1.f, (float)sA.p[sA.at(n, i)]));
+                    sO.p[sO.at(n, i)] = Io<T, IO>::out(da * IO::phi::df((float)sA.p[sA.at(n, i)]));
                 }
             }
             if (causal && hh == G - 1) {
@@ -494,7 +495,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
                 if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
                     float bk[U];
 #pragma unroll
-                    for (int i = 0; i < U; ++i) bk[i] = t < rows ? phi(Io<T, IO>::f(kr[l][i])) : 0.f;
+                    for (int i = 0; i < U; ++i) bk[i] = t < rows ? IO::phi::f(Io<T, IO>::f(kr[l][i])) : 0.f;
                     sB.write16(t, cq, to_g16<T>(bk));
                     sV.write16(t, cq, op16<T, IO>(vr[l]));
                 }
@@ -522,7 +523,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
                 float a[U], gg[U], dov = 0.f;
 #pragma unroll
                 for (int i = 0; i < U; ++i) {
-                    a[i] = real ? phi(Io<T, IO>::f(qr[l][i])) : 0.f;
+                    a[i] = real ? IO::phi::f(Io<T, IO>::f(qr[l][i])) : 0.f;
                     gg[i] = Io<T, IO>::f(dr[l][i]) * inv;
                     dov += Io<T, IO>::f(dr[l][i]) * Io<T, IO>::f(orr[l][i]);
                 }
@@ -622,7 +623,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
                             float rf = 0.f;
 #pragma unroll
                             for (int sl = 0; sl < RS; ++sl) rf += sRp[sl * D + f];
-                            sOK.p[sOK.at(n, f)] = Io<T, IO>::out((out[u][r] + rf) * fminf(1.f, (float)sB.p[sB.at(n, f)]));
+                            sOK.p[sOK.at(n, f)] = Io<T, IO>::out((out[u][r] + rf) * IO::phi::df((float)sB.p[sB.at(n, f)]));
                         }
                     }
                 }
@@ -673,9 +674,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int bwd_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, BwdPlan *pl)
 {
     if (B < 0 || H <= 0 || Hkv <= 0 || N < 0 || H % Hkv != 0) return LINATTN_ERR_SHAPE;
-    if (dtype != LINATTN_F32 && dtype != LINATTN_BF16 && dtype != LINATTN_F16) return LINATTN_ERR_DTYPE;
+    if (!valid_dtype(dtype)) return LINATTN_ERR_DTYPE;
     if (d != 32 && d != 64 && d != 128) return LINATTN_ERR_UNSUPPORTED;
-    const int e = dtype != LINATTN_F32 ? 2 : 4;
+    const int e = (dtype & 0xff) != LINATTN_F32 ? 2 : 4;
     if ((long long)N * d * e > 0x7fffffffLL) return LINATTN_ERR_SHAPE;
     BwdPlan p{};
     p.nseq = B * Hkv;
@@ -753,7 +754,7 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
     return launch_status();
 }
 
-template <typename T, typename IO = T>
+template <typename T, typename IO = Fmt<T, PhiElu1>>
 int dispatch_bwd(const BwdPlan &pl, int d, int H, int Hkv, int N, const void *q, const void *k, const void *v,
                  const void *o, const void *dout, void *dq, void *dk, void *dv, int causal, int normalise, char *ws,
                  hipStream_t st)
@@ -793,11 +794,11 @@ int linattn_bwd(const void *q, const void *k, const void *v, const void *out, co
         return LINATTN_ERR_ALIGN;
     if (!workspace || workspace_bytes < pl.bytes) return LINATTN_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
-    if (dtype == LINATTN_F16)
-        return dispatch_bwd<bf16, f16>(pl, d, H, Hkv, N, q, k, v, out, dout, dq, dk, dv, causal, normalise, ws, stream);
-    if (dtype == LINATTN_BF16)
-        return dispatch_bwd<bf16>(pl, d, H, Hkv, N, q, k, v, out, dout, dq, dk, dv, causal, normalise, ws, stream);
-    return dispatch_bwd<float>(pl, d, H, Hkv, N, q, k, v, out, dout, dq, dk, dv, causal, normalise, ws, stream);
+    return with_format(dtype, [&](auto kind) {
+        using K = decltype(kind);
+        return dispatch_bwd<typename K::T, typename K::IO>(pl, d, H, Hkv, N, q, k, v, out, dout, dq, dk, dv, causal,
+                                                           normalise, ws, stream);
+    });
 }
 
 }  // extern "C"

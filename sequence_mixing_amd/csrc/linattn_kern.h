@@ -57,12 +57,42 @@ template <typename G> __device__ __forceinline__ void buf_store16(Rsrc r, unsign
 // (lgkmcnt) is waited for, and the prefetched loads stay in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// phi(x) = ELU(x) + 1 (alpha = 1): x + 1 for x > 0, exp(x) otherwise,
-// written without a branch as max(x, 0) + exp(min(x, 0)) (one v_exp_f32).
-__device__ __forceinline__ float phi(float x)
-{
-    return fmaxf(x, 0.f) + __builtin_amdgcn_exp2f(fminf(x, 0.f) * 1.44269504088896340736f);
-}
+// ----------------------------------------------------------- feature maps
+//
+// phi is a template functor of every kernel (README "Features": custom
+// kernel plugins, phi replaceable): f(x), and phi'(x) written as a function of
+// phi(x) (df), which is what the backward keeps.  A new map is a struct with
+// these two members plus a code in the dispatch.
+//
+// ELU(x) + 1 (alpha = 1), the README's phi: x + 1 for x > 0, exp(x) otherwise,
+// written without a branch as max(x, 0) + exp(min(x, 0)) (one v_exp_f32);
+// phi' = 1 for x > 0, exp(x) = phi otherwise, i.e. min(1, phi).
+struct PhiElu1 {
+    static __device__ __forceinline__ float f(float x)
+    {
+        return fmaxf(x, 0.f) + __builtin_amdgcn_exp2f(fminf(x, 0.f) * 1.44269504088896340736f);
+    }
+    static __device__ __forceinline__ float df(float y) { return fminf(1.f, y); }
+};
+// ReLU: max(x, 0); phi' = 1 where phi > 0.  (A normalised row whose query or
+// keys are all <= 0 divides by zero.)
+struct PhiRelu {
+    static __device__ __forceinline__ float f(float x) { return fmaxf(x, 0.f); }
+    static __device__ __forceinline__ float df(float y) { return y > 0.f ? 1.f : 0.f; }
+};
+// softplus: log(1 + e^x) = max(x, 0) + log1p(e^-|x|); phi' = the logistic
+// function = 1 - e^-phi (written -expm1(-phi), exact for small phi).
+struct PhiSoftplus {
+    static __device__ __forceinline__ float f(float x) { return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))); }
+    static __device__ __forceinline__ float df(float y) { return -expm1f(-y); }
+};
+
+// Row format and feature map of a kernel instance: element type in memory
+// (float, bf16 or fp16) and phi.
+template <typename E, typename P> struct Fmt {
+    using elem = E;
+    using phi = P;
+};
 
 // ------------------------------------------------------------------ types
 
@@ -106,23 +136,25 @@ __device__ __forceinline__ f32x8 cat(const f32x4 &a, const f32x4 &b)
 // kernels are bf16 (T = bf16, IO = fp16): bf16 keeps fp32's exponent range, so
 // the operand copies of the running sums (which grow with the sequence) stay
 // finite where fp16 would overflow.  Registers hold the raw 16-byte groups;
-// these convert them at the loads and stores.  IO = T is the plain case.
+// these convert them at the loads and stores.  IO is a Fmt (below); its
+// element type equal to T is the plain case.
 typedef _Float16 f16;
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 template <typename T, typename IO> struct Io {
-    static_assert(std::is_same_v<T, IO> || (std::is_same_v<T, bf16> && std::is_same_v<IO, f16>), "I/O type");
-    static constexpr bool SAME = std::is_same_v<T, IO>;
+    using E = typename IO::elem;
+    static_assert(std::is_same_v<T, E> || (std::is_same_v<T, bf16> && std::is_same_v<E, f16>), "I/O type");
+    static constexpr bool SAME = std::is_same_v<T, E>;
     // element (raw bits in a T) -> float
     static __device__ __forceinline__ float f(T x)
     {
         if constexpr (SAME) return (float)x;
-        else return (float)__builtin_bit_cast(IO, x);
+        else return (float)__builtin_bit_cast(E, x);
     }
     // float -> the stored element (IO bits in a T)
     static __device__ __forceinline__ T out(float x)
     {
         if constexpr (SAME) return (T)x;
-        else return __builtin_bit_cast(T, (IO)x);
+        else return __builtin_bit_cast(T, (E)x);
     }
 };
 
@@ -143,13 +175,13 @@ template <> __device__ __forceinline__ f32x4 cvt4<float>(f32x4 x) { return x; }
 // Four results -> four stored elements of I/O type IO (in T-typed storage).
 template <typename T, typename IO> __device__ __forceinline__ typename Vt<T>::v4 out4(f32x4 x)
 {
-    if constexpr (std::is_same_v<T, IO>) return cvt4<T>(x);
+    if constexpr (std::is_same_v<T, typename IO::elem>) return cvt4<T>(x);
     else return __builtin_bit_cast(bf16x4, __builtin_convertvector(x, f16x4));
 }
 // A raw 16-byte group of IO elements -> the same values as operands of type T.
 template <typename T, typename IO> __device__ __forceinline__ typename Vt<T>::g16 op16(const typename Vt<T>::g16 &g)
 {
-    if constexpr (std::is_same_v<T, IO>) {
+    if constexpr (std::is_same_v<T, typename IO::elem>) {
         return g;
     } else {
         float x[8];
@@ -291,7 +323,7 @@ __device__ __forceinline__ void stage_rows(const typename Vt<T>::g16 (&kr)[L], c
             const int t = e / GPR, q = e % GPR;
             typename Vt<T>::g16 fk;
 #pragma unroll
-            for (int i = 0; i < U; ++i) fk[i] = (T)phi(Io<T, IO>::f(kr[l][i]));
+            for (int i = 0; i < U; ++i) fk[i] = (T)IO::phi::f(Io<T, IO>::f(kr[l][i]));
             if (!full) {
                 if (t >= rows) fk = typename Vt<T>::g16{};
             }
@@ -601,6 +633,42 @@ __global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, i
     }
 }
 
+// ------------------------------------------------------ format dispatch
+//
+// The `dtype` argument of the C ABI: element type in bits 0-7, feature map
+// in bits 8-15.  with_format calls fn(Kind<T, Fmt<elem, phi>>{}) for the
+// operand type T the element type computes in (float for fp32, bf16 for
+// both 16-bit formats).
+template <typename T_, typename IO_> struct Kind {
+    using T = T_;
+    using IO = IO_;
+};
+inline bool valid_dtype(int dtype)
+{
+    const int e = dtype & 0xff, m = dtype >> 8;
+    return dtype >= 0 && (e == LINATTN_F32 || e == LINATTN_BF16 || e == LINATTN_F16) &&
+           (m == LINATTN_PHI_ELU1 || m == LINATTN_PHI_RELU || m == LINATTN_PHI_SOFTPLUS);
+}
+template <class P, class Fn> int with_elem(int e, Fn &fn)
+{
+    switch (e) {
+    case LINATTN_F32: return fn(Kind<float, Fmt<float, P>>{});
+    case LINATTN_BF16: return fn(Kind<bf16, Fmt<bf16, P>>{});
+    case LINATTN_F16: return fn(Kind<bf16, Fmt<f16, P>>{});
+    }
+    return LINATTN_ERR_DTYPE;
+}
+template <class Fn> int with_format(int dtype, Fn fn)
+{
+    if (!valid_dtype(dtype)) return LINATTN_ERR_DTYPE;
+    switch (dtype >> 8) {
+    case LINATTN_PHI_ELU1: return with_elem<PhiElu1>(dtype & 0xff, fn);
+    case LINATTN_PHI_RELU: return with_elem<PhiRelu>(dtype & 0xff, fn);
+    case LINATTN_PHI_SOFTPLUS: return with_elem<PhiSoftplus>(dtype & 0xff, fn);
+    }
+    return LINATTN_ERR_DTYPE;
+}
+
 // -------------------------------------------------------------- launchers
 
 int launch_status()
@@ -612,7 +680,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Totals pass with chunks of c1 tokens (32, 64 or 128; at most 16 KiB of K per
 // chunk, so that two chunks of K and V double-buffer in 64 KiB of LDS).
-template <typename T, int D, typename IO = T>
+template <typename T, int D, typename IO = Fmt<T, PhiElu1>>
 int launch_totals(int c1, unsigned nblocks, hipStream_t st, const T *k, const T *v, float *ws, int N, int seg_len,
                   int nslots, Packed pk = Packed{nullptr, 0, 0}, int Hkv = 1, int causal = 1)
 {

@@ -17,7 +17,7 @@ bool valid_chunk(int c) { return c == 32 || c == 64 || c == 128 || c == 256; }
 
 int heads_per_block(int dtype, int d, int chunk, int G)
 {
-    const int e = dtype != LINATTN_F32 ? 2 : 4;
+    const int e = (dtype & 0xff) != LINATTN_F32 ? 2 : 4;
     for (int gt = 8; gt >= 1; gt /= 2)
         if (G % gt == 0 && main_shape(e, d, chunk, gt).fits) return gt;
     return 0;
@@ -30,7 +30,7 @@ int auto_chunk(int dtype, int d, int G, int causal)
     // per head block), then about 128 query rows per chunk, which gives the
     // four waves one 32-row query tile each; fp32 prefers 64-token chunks,
     // whose tiles leave room for eight waves.
-    const bool f32 = dtype == LINATTN_F32;
+    const bool f32 = (dtype & 0xff) == LINATTN_F32;
     for (int gt = 8; gt >= 1; gt /= 2) {
         if (G % gt != 0) continue;
         const int rows = 128 / gt >= 32 ? 128 / gt : 32;  // about 128 query rows, at least one tile
@@ -45,7 +45,9 @@ int auto_chunk(int dtype, int d, int G, int causal)
 
 int make_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int chunk, Plan *p)
 {
-    if (dtype != LINATTN_F32 && dtype != LINATTN_BF16 && dtype != LINATTN_F16) return LINATTN_ERR_DTYPE;
+    if (dtype < 0 || ((dtype & 0xff) != LINATTN_F32 && (dtype & 0xff) != LINATTN_BF16 && (dtype & 0xff) != LINATTN_F16) ||
+        (dtype >> 8) > LINATTN_PHI_SOFTPLUS)
+        return LINATTN_ERR_DTYPE;
     if (B < 0 || H <= 0 || Hkv <= 0 || N < 0 || d <= 0 || H % Hkv != 0) return LINATTN_ERR_SHAPE;
     if ((int64_t)B * H > INT32_MAX / 2 || (int64_t)N * d > INT32_MAX / 2) return LINATTN_ERR_SHAPE;
     if (!valid_d(d)) return LINATTN_ERR_UNSUPPORTED;
@@ -58,7 +60,7 @@ int make_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int ch
     // The chunk kernel addresses a head block's q and out (gt * N * d
     // elements) with 32-bit byte offsets: fewer heads per block for very long
     // sequences, and an error when one head alone exceeds 2 GiB.
-    const int64_t esz = dtype != LINATTN_F32 ? 2 : 4;
+    const int64_t esz = (dtype & 0xff) != LINATTN_F32 ? 2 : 4;
     while (gt > 1 && (int64_t)gt * N * d * esz > INT32_MAX) gt /= 2;
     if ((int64_t)N * d * esz > INT32_MAX) return LINATTN_ERR_SHAPE;
 
@@ -79,7 +81,7 @@ int make_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int ch
         // CU as its occupancy allows), so every workgroup walks several
         // chunks with the next one in flight instead of a second round
         // starting cold.
-        const int e = dtype != LINATTN_F32 ? 2 : 4;
+        const int e = (dtype & 0xff) != LINATTN_F32 ? 2 : 4;
         const int tgt = q.causal ? kCUs * main_shape(e, d, C, gt).occ : kTargetWorkgroups;
         int P = (tgt + q.nseq - 1) / q.nseq;
         if (P < 1) P = 1;
@@ -111,7 +113,7 @@ int make_plan_packed(int nb, int H, int Hkv, int total, int d, int causal, int d
     q.tab_off = 0;
     if (nb > 0 && total > 0) {
         const int C = q.chunk;
-        const int e = dtype != LINATTN_F32 ? 2 : 4;
+        const int e = (dtype & 0xff) != LINATTN_F32 ? 2 : 4;
         const int hb = q.G / q.gt;
         // Workgroups as for a dense batch: one resident round of the chunk
         // kernel (causal) or 512 partial sums (non-causal), over all kv heads.

@@ -13,10 +13,17 @@ from . import (LINATTN_BF16, LINATTN_F16, LINATTN_F32, LinattnError, linattn_bwd
 _DT = {torch.float32: LINATTN_F32, torch.bfloat16: LINATTN_BF16, torch.float16: LINATTN_F16}
 
 
-def dtype_code(t: torch.dtype) -> int:
+# feature maps (the `dtype` code's bits 8-15)
+PHI = {"elu1": 0, "relu": 1, "softplus": 2}
+
+
+def dtype_code(t: torch.dtype, phi: str = "elu1") -> int:
+    """The C ABI's dtype argument: element type, and the feature map in bits 8-15."""
     if t not in _DT:
         raise TypeError(f"unsupported dtype {t}")
-    return _DT[t]
+    if phi not in PHI:
+        raise ValueError(f"unknown feature map {phi}")
+    return _DT[t] | (PHI[phi] << 8)
 
 
 def workspace(B, H, Hkv, N, d, causal, dtype: torch.dtype, chunk=0, device="cuda") -> torch.Tensor | None:
@@ -27,7 +34,7 @@ def workspace(B, H, Hkv, N, d, causal, dtype: torch.dtype, chunk=0, device="cuda
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=True, normalise=True, chunk=0,
-        want_state=False, out=None, ws=None, stream=None, state_in=None, z_in=None):
+        want_state=False, out=None, ws=None, stream=None, state_in=None, z_in=None, phi="elu1"):
     """O = phi(Q)(phi(K)^T V) through ``linattn_fwd`` (``linattn_fwd_from_state`` when
     ``state_in`` is given); q [B,H,N,d], k/v [B,Hkv,N,d] on the GPU."""
     B, H, N, d = q.shape
@@ -37,7 +44,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=True, normalis
             raise ValueError("q, k, v must be contiguous device tensors of one dtype")
     if k.shape != (B, Hkv, N, d) or v.shape != (B, Hkv, N, d):
         raise ValueError("k and v must be [B, Hkv, N, d]")
-    code = dtype_code(q.dtype)
+    code = dtype_code(q.dtype, phi)
     if out is None:
         out = torch.empty_like(q)
     S = z = None
@@ -81,7 +88,7 @@ def unpack(flat, cu, heads, d):
 
 
 def fwd_packed(q, k, v, cu_seqlens, H, Hkv, d, causal=True, normalise=True, chunk=0, want_state=False, out=None,
-               ws=None, stream=None):
+               ws=None, stream=None, phi="elu1"):
     """linattn_fwd_packed on packed tensors (see pack): q of H * total * d elements, k and v
     of Hkv * total * d; cu_seqlens an int32 device tensor of nseqs + 1 offsets."""
     nseqs = cu_seqlens.numel() - 1
@@ -93,7 +100,7 @@ def fwd_packed(q, k, v, cu_seqlens, H, Hkv, d, causal=True, normalise=True, chun
         raise ValueError("q must hold H * total * d elements and k, v Hkv * total * d")
     if not (cu_seqlens.is_cuda and cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()):
         raise ValueError("cu_seqlens must be a contiguous int32 device tensor")
-    code = dtype_code(q.dtype)
+    code = dtype_code(q.dtype, phi)
     if out is None:
         out = torch.empty_like(q)
     S = z = None
@@ -112,7 +119,7 @@ def fwd_packed(q, k, v, cu_seqlens, H, Hkv, d, causal=True, normalise=True, chun
     return (out, S, z) if want_state else out
 
 
-def bwd(q, k, v, out, dout, causal=True, normalise=True, ws=None, stream=None, grads=None):
+def bwd(q, k, v, out, dout, causal=True, normalise=True, ws=None, stream=None, grads=None, phi="elu1"):
     """dQ, dK, dV through ``linattn_bwd``; q/out/dout [B,H,N,d], k/v [B,Hkv,N,d] on the GPU."""
     B, H, N, d = q.shape
     Hkv = k.shape[1]
@@ -121,7 +128,7 @@ def bwd(q, k, v, out, dout, causal=True, normalise=True, ws=None, stream=None, g
             raise ValueError("q, k, v, out, dout must be contiguous device tensors of one dtype")
     if k.shape != (B, Hkv, N, d) or v.shape != (B, Hkv, N, d) or dout.shape != q.shape:
         raise ValueError("k, v must be [B, Hkv, N, d] and dout [B, H, N, d]")
-    code = dtype_code(q.dtype)
+    code = dtype_code(q.dtype, phi)
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     nbytes = linattn_bwd_workspace_bytes(B, H, Hkv, N, d, causal, code)
     if nbytes < 0:
@@ -135,13 +142,14 @@ def bwd(q, k, v, out, dout, causal=True, normalise=True, ws=None, stream=None, g
     return dq, dk, dv
 
 
-def decode_step(state: torch.Tensor, z: torch.Tensor | None, q, k, v, normalise=True, out=None, stream=None):
+def decode_step(state: torch.Tensor, z: torch.Tensor | None, q, k, v, normalise=True, out=None, stream=None,
+                phi="elu1"):
     """One recurrent step through ``linattn_decode_step``; state [B,Hkv,d,d] and z [B,Hkv,d] fp32, in place."""
     B, H, d = q.shape
     Hkv = k.shape[1]
     if out is None:
         out = torch.empty_like(q)
-    rc = linattn_decode_step(state, z, q, k, v, out, B, H, Hkv, d, normalise, dtype_code(q.dtype), stream)
+    rc = linattn_decode_step(state, z, q, k, v, out, B, H, Hkv, d, normalise, dtype_code(q.dtype, phi), stream)
     if rc != 0:
         raise LinattnError(rc, "linattn_decode_step")
     return out
