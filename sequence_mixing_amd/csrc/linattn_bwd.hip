@@ -20,7 +20,8 @@
 // Workgroups hand data over through LDS with lds_barrier(), which leaves the
 // global loads of the next head or chunk in flight across the barrier.
 //
-// Launches (one workgroup = 4 wave64s; chunks of 32 tokens):
+// Launches (one workgroup = 4 wave64s, 8 for the dq walk at d = 128; chunks
+// of 32 tokens):
 //   seg_totals, seg_scan   the forward's segment sums of b v^T and b, giving
 //                          each dq segment its starting S and z;
 //   bwd_dq                 per (sequence, segment): walks the segment
@@ -46,17 +47,24 @@ namespace {
 
 constexpr int kBC = 32;  // tokens per chunk (one 32-row MFMA tile)
 
+// The dq walk runs 8 waves at d = 128 (two per SIMD): each wave carries half
+// the state tiles of a 4-wave workgroup and the two waves on a SIMD hide each
+// other's waits.  The dk/dv walk keeps 4 (with 8 its accumulators spill).
+constexpr int DQ_WAVES(int d) { return d == 128 ? 8 : 4; }
+
 // Shapes of the backward kernels for element type T and head dimension D.
-template <typename T, int D>
+template <typename T, int D, int NWAVES = 4>
 struct BGeo {
     static constexpr int U = Vt<T>::U;          // elements per 16-byte group
     static constexpr int GPR = D / U;           // groups per token row
     static constexpr int NGRP = kBC * GPR;      // groups per chunk of one tensor
-    static constexpr int LDV = (NGRP + kThreads - 1) / kThreads;
+    static constexpr int NW = NWAVES;
+    static constexpr int TH = 64 * NW;
+    static constexpr int LDV = (NGRP + TH - 1) / TH;
     static constexpr int DT = D / 32;
     static constexpr int KBD = D / 16;          // K-blocks over features
     static constexpr int NST = DT * DT;
-    static constexpr int MAXST = (NST + 3) / 4;
+    static constexpr int MAXST = (NST + NW - 1) / NW;
     static constexpr int E = (int)sizeof(T);
     // Two workgroups per CU (two waves per SIMD hide each other's waits) where
     // the registers allow it without spilling: the dq walk up to d = 64, the
@@ -133,26 +141,26 @@ __device__ __forceinline__ Rsrc make_rsrc_u(const void *base, int bytes)
 
 // Loads one chunk of a [N][D] row-major sequence (tokens t0 .. t0 + rows - 1;
 // zeros elsewhere, also for rows <= 0, without touching memory).
-template <typename T, int D, int L>
+template <typename T, int D, int TH, int L>
 __device__ __forceinline__ void load_rows(typename Vt<T>::g16 (&r)[L], const T *base, int t0, int rows, int tid)
 {
     using g16 = typename Vt<T>::g16;
-    static_assert(L == BGeo<T, D>::LDV, "register array size");
+    static_assert(L == BGeo<T, D, TH / 64>::LDV, "register array size");
     const Rsrc rs = make_rsrc_u(base + (size_t)t0 * D, rows > 0 ? rows * D * (int)sizeof(T) : 0);
 #pragma unroll
-    for (int l = 0; l < L; ++l) r[l] = buf_load16<g16>(rs, (unsigned)(tid + l * kThreads) * 16u);
+    for (int l = 0; l < L; ++l) r[l] = buf_load16<g16>(rs, (unsigned)(tid + l * TH) * 16u);
 }
 
 // One float per staged group: x[t0 + row of the group] (zero past rows).
-template <typename T, int D, int L>
+template <typename T, int D, int TH, int L>
 __device__ __forceinline__ void load_row_scalars(float (&r)[L], const float *base, int t0, int rows, int tid)
 {
-    using BG = BGeo<T, D>;
+    using BG = BGeo<T, D, TH / 64>;
     static_assert(L == BG::LDV, "register array size");
     const Rsrc rs = make_rsrc_u(base + t0, rows > 0 ? rows * 4 : 0);
 #pragma unroll
     for (int l = 0; l < BG::LDV; ++l) {
-        const int e = tid + l * kThreads;
+        const int e = tid + l * BG::TH;
         r[l] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (unsigned)(e / BG::GPR) * 4u, 0, 0));
     }
 }
@@ -166,14 +174,14 @@ __device__ __forceinline__ void load_row_scalars(float (&r)[L], const float *bas
 // dA^T on MFMA.  The next head's (or chunk's) rows are requested into
 // registers while the current one is computed.
 template <typename T, int D, typename IO>
-__global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const T *__restrict__ q, const T *__restrict__ k,
+__global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES(D)>::OCC_DQ)) void k_bwd_dq(const T *__restrict__ q, const T *__restrict__ k,
                                                       const T *__restrict__ v, const T *__restrict__ o,
                                                       const T *__restrict__ dout, T *__restrict__ dq,
                                                       float *__restrict__ den_out, const float *__restrict__ ws,
                                                       int H, int Hkv, int N, int G, int P, int seg_len, int causal,
                                                       int normalise)
 {
-    using BG = BGeo<T, D>;
+    using BG = BGeo<T, D, DQ_WAVES(D)>;
     using g16 = typename Vt<T>::g16;
     constexpr int U = BG::U, GPR = BG::GPR, LDV = BG::LDV;
     // bf16: low parts of b and g.  dq of the first tokens of a normalised
@@ -235,24 +243,24 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
             const int st = BG::tile_of(w, i);
             if (st < BG::NST) publish_tile<T, D>(S[i], sS, st / BG::DT, st % BG::DT, lane);
         }
-        for (int i = tid; i < D; i += kThreads) sZp[i] = init[(size_t)D * D + i];
-        for (int e = tid; e < kBC * D; e += kThreads) sZt[e] = init[(size_t)D * D + e % D];
+        for (int i = tid; i < D; i += BG::TH) sZp[i] = init[(size_t)D * D + i];
+        for (int e = tid; e < kBC * D; e += BG::TH) sZt[e] = init[(size_t)D * D + e % D];
     }
 
     g16 kr[LDV], vr[LDV], qr[LDV], orr[LDV], dr[LDV];
-    load_rows<T, D>(kr, kb, s0, rows_of(0), tid);
-    load_rows<T, D>(vr, vb, s0, rows_of(0), tid);
-    load_rows<T, D>(qr, q + (size_t)qh0 * N * D, s0, rows_of(0), tid);
-    load_rows<T, D>(orr, o + (size_t)qh0 * N * D, s0, normalise ? rows_of(0) : 0, tid);
-    load_rows<T, D>(dr, dout + (size_t)qh0 * N * D, s0, rows_of(0), tid);
+    load_rows<T, D, BG::TH>(kr, kb, s0, rows_of(0), tid);
+    load_rows<T, D, BG::TH>(vr, vb, s0, rows_of(0), tid);
+    load_rows<T, D, BG::TH>(qr, q + (size_t)qh0 * N * D, s0, rows_of(0), tid);
+    load_rows<T, D, BG::TH>(orr, o + (size_t)qh0 * N * D, s0, normalise ? rows_of(0) : 0, tid);
+    load_rows<T, D, BG::TH>(dr, dout + (size_t)qh0 * N * D, s0, rows_of(0), tid);
 
     for (int c = 0; c < nch; ++c) {
         const int t0 = s0 + c * kBC, rows = rows_of(c);
         // ---- phi(k), v of the chunk to LDS; the next chunk's rows requested
 #pragma unroll
         for (int l = 0; l < LDV; ++l) {
-            const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
-            if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
+            const int e = tid + l * BG::TH, t = e / GPR, cq = (e % GPR) * U;
+            if (BG::NGRP % BG::TH == 0 || e < BG::NGRP) {
                 float bk[U];
 #pragma unroll
                 for (int i = 0; i < U; ++i) bk[i] = t < rows ? IO::phi::f(Io<T, IO>::f(kr[l][i])) : 0.f;
@@ -267,8 +275,8 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
                 }
             }
         }
-        load_rows<T, D>(kr, kb, t0 + kBC, rows_of(c + 1), tid);
-        load_rows<T, D>(vr, vb, t0 + kBC, rows_of(c + 1), tid);
+        load_rows<T, D, BG::TH>(kr, kb, t0 + kBC, rows_of(c + 1), tid);
+        load_rows<T, D, BG::TH>(vr, vb, t0 + kBC, rows_of(c + 1), tid);
         if (causal) {
 #pragma unroll
             for (int i = 0; i < BG::MAXST; ++i) {
@@ -296,8 +304,8 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
                 const Rsrc rden = make_rsrc_u(den_out + (size_t)qh * N + t0, normalise ? rows * 4 : 0);
 #pragma unroll
                 for (int l = 0; l < LDV; ++l) {
-                    const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
-                    const bool grp = BG::NGRP % kThreads == 0 || e < BG::NGRP;
+                    const int e = tid + l * BG::TH, t = e / GPR, cq = (e % GPR) * U;
+                    const bool grp = BG::NGRP % BG::TH == 0 || e < BG::NGRP;
                     float a[U], den = 0.f, dov = 0.f;
 #pragma unroll
                     for (int i = 0; i < U; ++i) {
@@ -327,17 +335,17 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
                 const int nh = hh + 1 < G ? hh + 1 : 0, nc = hh + 1 < G ? c : c + 1;
                 const size_t nq = (size_t)(qh0 + nh) * N * D;
                 const int nt0 = s0 + nc * kBC, nrows = rows_of(nc);
-                load_rows<T, D>(qr, q + nq, nt0, nrows, tid);
-                load_rows<T, D>(orr, o + nq, nt0, normalise ? nrows : 0, tid);
-                load_rows<T, D>(dr, dout + nq, nt0, nrows, tid);
+                load_rows<T, D, BG::TH>(qr, q + nq, nt0, nrows, tid);
+                load_rows<T, D, BG::TH>(orr, o + nq, nt0, normalise ? nrows : 0, tid);
+                load_rows<T, D, BG::TH>(dr, dout + nq, nt0, nrows, tid);
             }
             lds_barrier();
             // ---- dA^T tiles (one 32-feature block per unit); the state update after the last head
-            constexpr int MAXI = (BG::DT + 3) / 4;
+            constexpr int MAXI = (BG::DT + BG::NW - 1) / BG::NW;
             f32x16 dacc[MAXI];
 #pragma unroll
             for (int ui = 0; ui < MAXI; ++ui) {
-                const int it = w + 4 * ui;
+                const int it = w + BG::NW * ui;
                 if (it >= BG::DT) break;
                 f32x16 acc = f32x16{};
                 const float hn = sH[n];
@@ -371,7 +379,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
             if constexpr (!OWN_O) lds_barrier();  // every read of the g tile is done
 #pragma unroll
             for (int ui = 0; ui < MAXI; ++ui) {
-                const int it = w + 4 * ui;
+                const int it = w + BG::NW * ui;
                 if (it >= BG::DT) break;
                 const float hn = sH[n];
 #pragma unroll
@@ -394,8 +402,8 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
                 const Rsrc rdq = make_rsrc_u(dq + ((size_t)qh * N + t0) * D, rows * D * (int)sizeof(T));
 #pragma unroll
                 for (int l = 0; l < LDV; ++l) {
-                    const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
-                    if (BG::NGRP % kThreads == 0 || e < BG::NGRP)
+                    const int e = tid + l * BG::TH, t = e / GPR, cq = (e % GPR) * U;
+                    if (BG::NGRP % BG::TH == 0 || e < BG::NGRP)
                         buf_store16<g16>(rdq, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sO.p + sO.at(t, cq)));
                 }
             }
@@ -412,7 +420,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DQ)) void k_bwd_dq(const
 // terms, then dk and dv are stored.  R lives in MFMA accumulators over the
 // waves; r in per-thread partial sums (column tid % D, a slice of the rows).
 template <typename T, int D, bool TOTALS, typename IO>
-__global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(const T *__restrict__ q, const T *__restrict__ k,
+__global__ __launch_bounds__((BGeo<T, D>::TH), (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(const T *__restrict__ q, const T *__restrict__ k,
                                                        const T *__restrict__ v, const T *__restrict__ o,
                                                        const T *__restrict__ dout, const float *__restrict__ den,
                                                        T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ ws_r,
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
     using BG = BGeo<T, D>;
     using g16 = typename Vt<T>::g16;
     constexpr int U = BG::U, GPR = BG::GPR, LDV = BG::LDV;
-    constexpr int RS = kThreads / D;  // row slices of the r partial sums
+    constexpr int RS = BG::TH / D;  // row slices of the r partial sums
     __shared__ __attribute__((aligned(16))) T smA[kBC * D];
     __shared__ __attribute__((aligned(16))) T smG[kBC * D];
     __shared__ __attribute__((aligned(16))) T smB[TOTALS ? 16 / sizeof(T) : kBC * D];
@@ -466,22 +474,22 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
     const int rcol = tid % D, rsl = tid / D;
     float rpart = (init && rsl == 0) ? init[(size_t)D * D + rcol] : 0.f;
 
-    constexpr int NU = 2 * BG::DT, MAXU = (NU + 3) / 4;
+    constexpr int NU = 2 * BG::DT, MAXU = (NU + BG::NW - 1) / BG::NW;
     f32x16 out[MAXU];
     const int nheads = (!TOTALS && !causal) ? 0 : G;
 
     g16 kr[LDV], vr[LDV], qr[LDV], orr[LDV], dr[LDV];
     float dn[LDV];
     if (!TOTALS) {
-        load_rows<T, D>(kr, kb, t0_of(0), rows_of(0), tid);
-        load_rows<T, D>(vr, vb, t0_of(0), rows_of(0), tid);
+        load_rows<T, D, BG::TH>(kr, kb, t0_of(0), rows_of(0), tid);
+        load_rows<T, D, BG::TH>(vr, vb, t0_of(0), rows_of(0), tid);
     }
     {
         const int r0 = nheads > 0 ? rows_of(0) : 0;
-        load_rows<T, D>(qr, q + (size_t)qh0 * N * D, t0_of(0), r0, tid);
-        load_rows<T, D>(orr, o + (size_t)qh0 * N * D, t0_of(0), normalise ? r0 : 0, tid);
-        load_rows<T, D>(dr, dout + (size_t)qh0 * N * D, t0_of(0), r0, tid);
-        load_row_scalars<T, D>(dn, den + (size_t)qh0 * N, t0_of(0), normalise ? r0 : 0, tid);
+        load_rows<T, D, BG::TH>(qr, q + (size_t)qh0 * N * D, t0_of(0), r0, tid);
+        load_rows<T, D, BG::TH>(orr, o + (size_t)qh0 * N * D, t0_of(0), normalise ? r0 : 0, tid);
+        load_rows<T, D, BG::TH>(dr, dout + (size_t)qh0 * N * D, t0_of(0), r0, tid);
+        load_row_scalars<T, D, BG::TH>(dn, den + (size_t)qh0 * N, t0_of(0), normalise ? r0 : 0, tid);
     }
 
     for (int j = 0; j < nch; ++j) {
@@ -491,8 +499,8 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
             for (int u = 0; u < MAXU; ++u) out[u] = f32x16{};
 #pragma unroll
             for (int l = 0; l < LDV; ++l) {
-                const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
-                if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
+                const int e = tid + l * BG::TH, t = e / GPR, cq = (e % GPR) * U;
+                if (BG::NGRP % BG::TH == 0 || e < BG::NGRP) {
                     float bk[U];
 #pragma unroll
                     for (int i = 0; i < U; ++i) bk[i] = t < rows ? IO::phi::f(Io<T, IO>::f(kr[l][i])) : 0.f;
@@ -500,8 +508,8 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
                     sV.write16(t, cq, op16<T, IO>(vr[l]));
                 }
             }
-            load_rows<T, D>(kr, kb, t0_of(j + 1), rows_of(j + 1), tid);
-            load_rows<T, D>(vr, vb, t0_of(j + 1), rows_of(j + 1), tid);
+            load_rows<T, D, BG::TH>(kr, kb, t0_of(j + 1), rows_of(j + 1), tid);
+            load_rows<T, D, BG::TH>(vr, vb, t0_of(j + 1), rows_of(j + 1), tid);
             // the carried sums of the later tokens, as they stand before this chunk
             if (causal || j == 0) {
 #pragma unroll
@@ -517,7 +525,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
             // ---- a, g, h of this head; the next head's (or chunk's) rows requested
 #pragma unroll
             for (int l = 0; l < LDV; ++l) {
-                const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
+                const int e = tid + l * BG::TH, t = e / GPR, cq = (e % GPR) * U;
                 const bool real = t < rows;
                 const float inv = real ? (normalise ? 1.f / dn[l] : 1.f) : 0.f;
                 float a[U], gg[U], dov = 0.f;
@@ -528,7 +536,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
                     dov += Io<T, IO>::f(dr[l][i]) * Io<T, IO>::f(orr[l][i]);
                 }
                 dov = row_sum<GPR>(dov);
-                if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
+                if (BG::NGRP % BG::TH == 0 || e < BG::NGRP) {
                     sA.write16(t, cq, to_g16<T>(a));
                     sG.write16(t, cq, to_g16<T>(gg));
                     if (e % GPR == 0) sH[t] = normalise ? -dov * inv : 0.f;
@@ -538,17 +546,17 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
                 const int nh = hh + 1 < G ? hh + 1 : 0, nj = hh + 1 < G ? j : j + 1;
                 const size_t nq = (size_t)(qh0 + nh);
                 const int nt0 = t0_of(nj), nrows = rows_of(nj);
-                load_rows<T, D>(qr, q + nq * N * D, nt0, nrows, tid);
-                load_rows<T, D>(orr, o + nq * N * D, nt0, normalise ? nrows : 0, tid);
-                load_rows<T, D>(dr, dout + nq * N * D, nt0, nrows, tid);
-                load_row_scalars<T, D>(dn, den + nq * N, nt0, normalise ? nrows : 0, tid);
+                load_rows<T, D, BG::TH>(qr, q + nq * N * D, nt0, nrows, tid);
+                load_rows<T, D, BG::TH>(orr, o + nq * N * D, nt0, normalise ? nrows : 0, tid);
+                load_rows<T, D, BG::TH>(dr, dout + nq * N * D, nt0, nrows, tid);
+                load_row_scalars<T, D, BG::TH>(dn, den + nq * N, nt0, normalise ? nrows : 0, tid);
             }
             lds_barrier();
             // ---- intra-chunk terms (causal), then R += A^T G, r += A^T h
             if (!TOTALS && causal) {
 #pragma unroll
                 for (int u = 0; u < MAXU; ++u) {
-                    const int unit = w + 4 * u;
+                    const int unit = w + BG::NW * u;
                     if (unit < NU) {
                         f32x16 M = f32x16{};
                         if (unit < BG::DT) {
@@ -593,7 +601,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
             // ---- carried terms and the outputs of this chunk
 #pragma unroll
             for (int u = 0; u < MAXU; ++u) {
-                const int unit = w + 4 * u;
+                const int unit = w + BG::NW * u;
                 if (unit < NU) {
                     if (unit < BG::DT) {
                         // dv^T[j][s] += sum_i R[i][j] b_s[i]
@@ -612,7 +620,7 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
             }
 #pragma unroll
             for (int u = 0; u < MAXU; ++u) {
-                const int unit = w + 4 * u;
+                const int unit = w + BG::NW * u;
                 if (unit < NU) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -633,8 +641,8 @@ __global__ __launch_bounds__(kThreads, (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(con
             const Rsrc rdv = make_rsrc_u(dv + ((size_t)sq * N + t0) * D, rows * D * (int)sizeof(T));
 #pragma unroll
             for (int l = 0; l < LDV; ++l) {
-                const int e = tid + l * kThreads, t = e / GPR, cq = (e % GPR) * U;
-                if (BG::NGRP % kThreads == 0 || e < BG::NGRP) {
+                const int e = tid + l * BG::TH, t = e / GPR, cq = (e % GPR) * U;
+                if (BG::NGRP % BG::TH == 0 || e < BG::NGRP) {
                     buf_store16<g16>(rdk, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sOK.p + sOK.at(t, cq)));
                     buf_store16<g16>(rdv, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sOV.p + sOV.at(t, cq)));
                 }
@@ -726,13 +734,13 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
                            1, (float *)nullptr, (float *)nullptr, (const float *)nullptr, (const float *)nullptr);
     }
     // 2. dq (and den)
-    hipLaunchKernelGGL((k_bwd_dq<T, D, IO>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo, dd,
+    hipLaunchKernelGGL((k_bwd_dq<T, D, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D, DQ_WAVES(D)>::TH), 0, st, qq, kk, vv, oo, dd,
                        static_cast<T *>(dq), wden, (const float *)wf, H, Hkv, N, pl.G, P, pl.seg_len, causal,
                        normalise);
     // 3. sums of a g^T and h a per segment: causal segments 1..P-1, suffix scan
     if (causal) {
         if (P > 1) {
-            hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * (P - 1)), dim3(kThreads), 0, st, qq, kk, vv,
+            hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * (P - 1)), dim3(BGeo<T, D>::TH), 0, st, qq, kk, vv,
                                oo, dd, (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P,
                                pl.seg_len, causal, normalise, P - 1, 1);
             if (P > 2)
@@ -741,14 +749,14 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
                                    (const float *)nullptr);
         }
     } else {
-        hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo, dd,
+        hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D>::TH), 0, st, qq, kk, vv, oo, dd,
                            (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P, pl.seg_len,
                            causal, normalise, P, 0);
         hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, wr, P, D,
                            1, (float *)nullptr, (float *)nullptr, (const float *)nullptr, (const float *)nullptr);
     }
     // 4. dk, dv
-    hipLaunchKernelGGL((k_bwd_dkv<T, D, false, IO>), dim3(pl.nseq * P), dim3(kThreads), 0, st, qq, kk, vv, oo, dd,
+    hipLaunchKernelGGL((k_bwd_dkv<T, D, false, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D>::TH), 0, st, qq, kk, vv, oo, dd,
                        (const float *)wden, static_cast<T *>(dk), static_cast<T *>(dv), wr, H, Hkv, N, pl.G, P,
                        pl.seg_len, causal, normalise, P, 0);
     return launch_status();
