@@ -49,8 +49,10 @@ constexpr int kBC = 32;  // tokens per chunk (one 32-row MFMA tile)
 
 // The dq walk runs 8 waves at d = 128 (two per SIMD): each wave carries half
 // the state tiles of a 4-wave workgroup and the two waves on a SIMD hide each
-// other's waits.  The dk/dv walk keeps 4 (with 8 its accumulators spill).
+// other's waits.  So does the dk/dv walk (its K-block loops unrolled by two,
+// so that its accumulators fit); its totals pass keeps 4.
 constexpr int DQ_WAVES(int d) { return d == 128 ? 8 : 4; }
+constexpr int DKV_WAVES(int d, bool totals) { return d == 128 && !totals ? 8 : 4; }
 
 // Shapes of the backward kernels for element type T and head dimension D.
 template <typename T, int D, int NWAVES = 4>
@@ -420,14 +422,14 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
 // terms, then dk and dv are stored.  R lives in MFMA accumulators over the
 // waves; r in per-thread partial sums (column tid % D, a slice of the rows).
 template <typename T, int D, bool TOTALS, typename IO>
-__global__ __launch_bounds__((BGeo<T, D>::TH), (BGeo<T, D>::OCC_DKV)) void k_bwd_dkv(const T *__restrict__ q, const T *__restrict__ k,
+__global__ __launch_bounds__((BGeo<T, D, DKV_WAVES(D, TOTALS)>::TH), (BGeo<T, D, DKV_WAVES(D, TOTALS)>::OCC_DKV)) void k_bwd_dkv(const T *__restrict__ q, const T *__restrict__ k,
                                                        const T *__restrict__ v, const T *__restrict__ o,
                                                        const T *__restrict__ dout, const float *__restrict__ den,
                                                        T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ ws_r,
                                                        int H, int Hkv, int N, int G, int P, int seg_len, int causal,
                                                        int normalise, int nslots, int first_seg)
 {
-    using BG = BGeo<T, D>;
+    using BG = BGeo<T, D, DKV_WAVES(D, TOTALS)>;
     using g16 = typename Vt<T>::g16;
     constexpr int U = BG::U, GPR = BG::GPR, LDV = BG::LDV;
     constexpr int RS = BG::TH / D;  // row slices of the r partial sums
@@ -561,14 +563,14 @@ __global__ __launch_bounds__((BGeo<T, D>::TH), (BGeo<T, D>::OCC_DKV)) void k_bwd
                         f32x16 M = f32x16{};
                         if (unit < BG::DT) {
                             // M[t][s] = a_t . b_s for t >= s
-#pragma unroll
+#pragma unroll 2
                             for (int kk = 0; kk < BG::KBD; ++kk)
                                 mma(M, sA.read8(n, kk * 16 + 8 * h), sB.read8(n, kk * 16 + 8 * h));
 #pragma unroll
                             for (int r = 0; r < 16; ++r) M[r] = (8 * (r / 4) + 4 * h + (r % 4)) >= n ? M[r] : 0.f;
                         } else {
                             // M[t][s] = g_t . v_s + h_t for t >= s
-#pragma unroll
+#pragma unroll 2
                             for (int kk = 0; kk < BG::KBD; ++kk)
                                 mma(M, sG.read8(n, kk * 16 + 8 * h), sV.read8(n, kk * 16 + 8 * h));
 #pragma unroll
@@ -605,14 +607,14 @@ __global__ __launch_bounds__((BGeo<T, D>::TH), (BGeo<T, D>::OCC_DKV)) void k_bwd
                 if (unit < NU) {
                     if (unit < BG::DT) {
                         // dv^T[j][s] += sum_i R[i][j] b_s[i]
-#pragma unroll
+#pragma unroll 2
                         for (int kk = 0; kk < BG::KBD; ++kk) {
                             const int ra = kk * 16 + 8 * h;
                             mma(out[u], colfrag(sR, ra, ra + 4, unit * 32, lane), sB.read8(n, ra));
                         }
                     } else {
                         // dk^T[i][s] += sum_j R[i][j] v_s[j]
-#pragma unroll
+#pragma unroll 2
                         for (int kk = 0; kk < BG::KBD; ++kk)
                             mma(out[u], sR.read8((unit - BG::DT) * 32 + n, kk * 16 + 8 * h), sV.read8(n, kk * 16 + 8 * h));
                     }
@@ -740,7 +742,7 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
     // 3. sums of a g^T and h a per segment: causal segments 1..P-1, suffix scan
     if (causal) {
         if (P > 1) {
-            hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * (P - 1)), dim3(BGeo<T, D>::TH), 0, st, qq, kk, vv,
+            hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * (P - 1)), dim3(BGeo<T, D, DKV_WAVES(D, true)>::TH), 0, st, qq, kk, vv,
                                oo, dd, (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P,
                                pl.seg_len, causal, normalise, P - 1, 1);
             if (P > 2)
@@ -749,14 +751,14 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
                                    (const float *)nullptr);
         }
     } else {
-        hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D>::TH), 0, st, qq, kk, vv, oo, dd,
+        hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D, DKV_WAVES(D, true)>::TH), 0, st, qq, kk, vv, oo, dd,
                            (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P, pl.seg_len,
                            causal, normalise, P, 0);
         hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, wr, P, D,
                            1, (float *)nullptr, (float *)nullptr, (const float *)nullptr, (const float *)nullptr);
     }
     // 4. dk, dv
-    hipLaunchKernelGGL((k_bwd_dkv<T, D, false, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D>::TH), 0, st, qq, kk, vv, oo, dd,
+    hipLaunchKernelGGL((k_bwd_dkv<T, D, false, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D, DKV_WAVES(D, false)>::TH), 0, st, qq, kk, vv, oo, dd,
                        (const float *)wden, static_cast<T *>(dk), static_cast<T *>(dv), wr, H, Hkv, N, pl.G, P,
                        pl.seg_len, causal, normalise, P, 0);
     return launch_status();
