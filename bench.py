@@ -94,8 +94,8 @@ class Hip:
         assert self.lib.hipEventRecord(e, stream) == 0
 
 
-SOURCES = ["sequence_mixing_amd/csrc/linattn.hip", "sequence_mixing_amd/csrc/linattn_plan.h",
-           "sequence_mixing_amd/csrc/linattn_plan.cpp"]
+SOURCES = ["sequence_mixing_amd/csrc/linattn.hip", "sequence_mixing_amd/csrc/linattn_kern.h",
+           "sequence_mixing_amd/csrc/linattn_plan.h", "sequence_mixing_amd/csrc/linattn_plan.cpp"]
 
 
 def measured_traffic(workload: str, key_prefix: str):
@@ -545,7 +545,7 @@ def decode_row(la, hip, torch, steps_total, stream):
         "graph_matches_eager": same,
         "eager_us_per_step": round(eager_us, 2),
         "roofline": roofline(nb, fl, k_us / 1e6, "bf16", "k_decode_step<bf16,128> (graph replay, per step)",
-                             measured_traffic("decode", "k_decode_step<bf16,128>")),
+                             measured_traffic("decode", "k_decode_step<bf16,128,")),
         "note": "state (32 MiB fp32) fits the 256 MiB memory-side cache; it is read and written every step",
     }
     del S, z, qs, ks, vs, out, g

@@ -28,18 +28,43 @@ def summarize(path: str, command: str, title: str = "") -> str:
 
 
 def kernel_key(name: str) -> str:
-    """'k_causal_chunks<float,64,128,1>' from a demangled or an Itanium-mangled kernel name."""
+    """'k_causal_chunks<float,64,128,1,float,elu1>' from a demangled or an Itanium-mangled
+    kernel name (template arguments in order; a row format Fmt<element, feature map>
+    becomes its element and the map's short name)."""
     import re
 
+    maps = {"PhiElu1": "elu1", "PhiRelu": "relu", "PhiSoftplus": "softplus"}
     if "::k_" in name:
-        return name.split("::", 1)[1].split("(")[0].replace(" ", "")
-    m = re.match(r"_ZN12_GLOBAL__N_1\d+(k_\w+?)I(.*?)EEv", name)
+        body = name.split("::", 1)[1]
+        body = re.sub(r"\(anonymous namespace\)::", "", body).split(">(")[0] + ">"
+        body = body.replace(" ", "").replace("__bf16", "bf16").replace("_Float16", "f16")
+        body = re.sub(r"Fmt<([^,<>]+),(Phi\w+)>", lambda m: m.group(1) + "," + maps.get(m.group(2), m.group(2)), body)
+        return body.replace(">>", ">")
+    m = re.match(r"_ZN12_GLOBAL__N_1(\d+)", name)
     if not m:
         return name.split("(")[0][:72]
-    args, rest = [], m.group(2)
-    for tok in re.findall(r"DF16b|Li-?\d+E|f|d|i", rest):
-        args.append({"DF16b": "bf16", "f": "float", "d": "double", "i": "int"}.get(tok, tok[2:-1]))
-    return f"{m.group(1)}<{','.join(args)}>"
+    n0 = m.end()
+    kname = name[n0:n0 + int(m.group(1))]
+    rest = name[n0 + int(m.group(1)):]
+    if not rest.startswith("I"):
+        return kname
+    m = re.match(r"(.*)", rest[1:])
+    args = []
+    toks = {"DF16b": "bf16", "DF16_": "f16", "f": "float", "d": "double", "i": "int"}
+    for tok in re.findall(r"Li-?\d+E|Lb[01]E|Phi\w+?E|DF16b|DF16_|NS_\d+FmtI|EE|[fdi]", m.group(1)):
+        if tok == "EE":
+            break  # end of the template arguments (what follows is the parameter list)
+        if tok.startswith("NS_"):
+            continue
+        if tok.startswith("Li"):
+            args.append(tok[2:-1])
+        elif tok.startswith("Lb"):
+            args.append("true" if tok[2] == "1" else "false")
+        elif tok.startswith("Phi"):
+            args.append(maps.get(tok[:-1], tok[:-1]))
+        else:
+            args.append(toks[tok])
+    return f"{kname}<{','.join(args)}>"
 
 
 def _per_dispatch(path: str, counter: str) -> dict:
