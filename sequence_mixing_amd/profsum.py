@@ -35,8 +35,10 @@ def kernel_key(name: str) -> str:
 
     maps = {"PhiElu1": "elu1", "PhiRelu": "relu", "PhiSoftplus": "softplus"}
     if "::k_" in name:
-        body = name.split("::", 1)[1]
-        body = re.sub(r"\(anonymous namespace\)::", "", body).split(">(")[0] + ">"
+        body = re.sub(r"\(anonymous namespace\)::", "", name.split("::", 1)[1])
+        if "<" not in body.split("(")[0]:
+            return body.split("(")[0]
+        body = body.split(">(")[0] + ">"
         body = body.replace(" ", "").replace("__bf16", "bf16").replace("_Float16", "f16")
         body = re.sub(r"Fmt<([^,<>]+),(Phi\w+)>", lambda m: m.group(1) + "," + maps.get(m.group(2), m.group(2)), body)
         return body.replace(">>", ">")
