@@ -244,9 +244,17 @@ def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, cold, tag="
         "stage_us": {"seg_totals": round(r["stage_ms"][0] * 1e3, 2), "seg_scan": round(r["stage_ms"][1] * 1e3, 2),
                      "main": round(r["stage_ms"][2] * 1e3, 2)},
         "roofline_main": roofline(nb, fl, k3, w.dtype, kernel_name(w, c, causal),
-                                  measured_traffic(tag, kernel_name(w, c, causal)[:-1] + ",") if causal else None),
+                                  measured_traffic(tag, kernel_name(w, c, causal)[:-1] + ",")),
         "roofline_path": roofline(nb, fl, gr["event_ms"] / 1e3, w.dtype, "whole step (graph replay, events)"),
     }
+    if not causal:
+        # pass 1, the reduction phi(K)^T V, sum phi(K) over every token: K and V
+        # read once (the partial sums it writes are not counted)
+        kv = 2 * w.B * w.Hkv * w.N * w.d * (2 if w.dtype == "bf16" else 4)
+        t = {"f32": "float", "bf16": "bf16"}[w.dtype]
+        row["roofline_reduction"] = roofline(kv, 0.0, r["stage_ms"][0] / 1e3, w.dtype,
+                                             f"k_seg_totals<{t},{w.d}> (pass 1)",
+                                             measured_traffic(tag, f"k_seg_totals<{t},{w.d},"))
     if cold:
         # Same steps with the 256 MiB memory-side cache swept before each one
         # by reading 512 MiB outside the timed events, so every input comes from
@@ -630,6 +638,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--rows", type=int, default=1, help="also measure the other workloads (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--causal", type=int, default=1,
+                    help="0: the timed workload runs the non-causal path instead (for profiling it alone)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -651,12 +661,14 @@ def main():
     w = WORKLOADS[args.workload]
     log(f"workload {args.workload}: {w.name}; steps {args.steps}, warmup {args.warmup}")
 
-    head = fwd_row(la, hip, torch, w, 1, args.chunk, args.steps, args.warmup, stream, cold=True, tag=args.workload)
+    tag = args.workload if args.causal else args.workload + "_noncausal"
+    head = fwd_row(la, hip, torch, w, args.causal, args.chunk, args.steps, args.warmup, stream, cold=True, tag=tag)
     log("headline", json.dumps(head))
     rows = {}
     if args.rows:
         if args.workload == "cfg2":
-            rows["cfg2_noncausal"] = fwd_row(la, hip, torch, w, 0, args.chunk, 20, 5, stream, cold=True)
+            rows["cfg2_noncausal"] = fwd_row(la, hip, torch, w, 0, args.chunk, 20, 5, stream, cold=True,
+                                             tag="cfg2_noncausal")
             if args.cpu_seconds > 0:
                 rows["cfg2_noncausal"]["cpu_oracle"] = row_oracle(w, 0, min(2.0, args.cpu_seconds))
             log("cfg2_noncausal", json.dumps(rows["cfg2_noncausal"]))
@@ -702,7 +714,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic: seeded N(0,1) q, k, v (no dataset involved)",
-        "config": {"workload": f"{args.workload}: {w.name}, causal, normaliser on", "B": w.B, "H": w.H,
+        "config": {"workload": f"{args.workload}: {w.name}, {'causal' if args.causal else 'non-causal'}, "
+                               "normaliser on", "B": w.B, "H": w.H,
                    "Hkv": w.Hkv, "N": w.N, "d": w.d, "chunk": head["chunk"], "segments": head["segments"],
                    "launch": "the K steps captured as one HIP graph and replayed (eager figures under 'eager')"},
         "eager": head["eager"],

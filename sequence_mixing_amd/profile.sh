@@ -7,8 +7,11 @@
 # 1. kernel trace + stats of the default bench run (every workload row) and
 #    of the headline workload alone;
 # 2. FETCH_SIZE then WRITE_SIZE (one counter per run) for the headline
-#    workload's kernels and for the decode kernel, and the same two counters
-#    for a plain 256 MiB copy, which calibrates them into bytes.
+#    workload's kernels, for the same workload run non-causal (the reduction
+#    pass and the apply pass), and for the decode kernel, and the same two
+#    counters for a plain 256 MiB copy, which calibrates them into bytes;
+# 3. one pass of SQ counters over every workload: matrix-core utilisation
+#    (MfmaUtil), matrix-core flops, and the waves' wait and LDS shares.
 # The summaries are written next to the raw output as *.txt.
 set -euo pipefail
 OUT=${1:?raw output directory}
@@ -29,6 +32,9 @@ for ctr in FETCH_SIZE WRITE_SIZE; do
     step "$ctr: headline workload"
     timeout -s KILL 200 rocprofv3 --pmc $ctr --kernel-include-regex "$KR" -f csv -d $OUT/${ctr}_cfg2 -o run -- \
         python3 bench.py --rows 0 --steps 5 --warmup 2 --cpu-seconds 0 > "$OUT/${ctr}_cfg2.out" 2>&1
+    step "$ctr: headline workload, non-causal"
+    timeout -s KILL 200 rocprofv3 --pmc $ctr --kernel-include-regex "$KR" -f csv -d $OUT/${ctr}_nc -o run -- \
+        python3 bench.py --causal 0 --rows 0 --steps 5 --warmup 2 --cpu-seconds 0 > "$OUT/${ctr}_nc.out" 2>&1
     step "$ctr: decode"
     timeout -s KILL 300 rocprofv3 --pmc $ctr --kernel-include-regex "k_decode_step" -f csv -d $OUT/${ctr}_decode -o run -- \
         python3 bench.py --rows 1 --steps 5 --warmup 2 --cpu-seconds 0 > "$OUT/${ctr}_decode.out" 2>&1
@@ -37,7 +43,13 @@ for ctr in FETCH_SIZE WRITE_SIZE; do
         python3 -m sequence_mixing_amd.calib_copy 256 > "$OUT/${ctr}_copy.out" 2>&1
 done
 
-PMC="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --kernel-include-regex '<kernels>' -f csv -- python3 bench.py --steps 5 --warmup 2 --cpu-seconds 0 (--rows 0 headline, --rows 1 decode); calibration: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 -m sequence_mixing_amd.calib_copy 256"
+CTRS="MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT"
+C3="rocprofv3 --pmc $CTRS --kernel-include-regex '$KR|k_decode_step|k_bwd' -f csv -d $OUT/counters_all -o run -- python3 bench.py --rows 1 --steps 5 --warmup 2 --cpu-seconds 0"
+step "counters: every workload"
+timeout -s KILL 500 rocprofv3 --pmc $CTRS --kernel-include-regex "$KR|k_decode_step|k_bwd" -f csv -d $OUT/counters_all -o run -- \
+    python3 bench.py --rows 1 --steps 5 --warmup 2 --cpu-seconds 0 > "$OUT/counters_all.out" 2>&1
+
+PMC="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --kernel-include-regex '<kernels>' -f csv -- python3 bench.py --steps 5 --warmup 2 --cpu-seconds 0 (--rows 0 headline, --causal 0 --rows 0 non-causal, --rows 1 decode); calibration: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 -m sequence_mixing_amd.calib_copy 256"
 python3 -m sequence_mixing_amd.profsum "$OUT/trace_all/run_kernel_stats.csv" "$C1" \
     "all kernels of the default bench run (every workload row; bench JSON in the same run)" > "$OUT/kernels_all_workloads.txt"
 python3 -m sequence_mixing_amd.profsum "$OUT/trace_cfg2/run_kernel_stats.csv" "$C2" \
@@ -45,6 +57,12 @@ python3 -m sequence_mixing_amd.profsum "$OUT/trace_cfg2/run_kernel_stats.csv" "$
 python3 -m sequence_mixing_amd.profsum traffic cfg2 "$OUT/FETCH_SIZE_cfg2/run_counter_collection.csv" \
     "$OUT/WRITE_SIZE_cfg2/run_counter_collection.csv" "$OUT/FETCH_SIZE_copy/run_counter_collection.csv" \
     "$OUT/WRITE_SIZE_copy/run_counter_collection.csv" 256 "$PMC" $SRC > "$OUT/traffic_cfg2_f32_B2H8N4096d64.txt"
+python3 -m sequence_mixing_amd.profsum traffic cfg2_noncausal "$OUT/FETCH_SIZE_nc/run_counter_collection.csv" \
+    "$OUT/WRITE_SIZE_nc/run_counter_collection.csv" "$OUT/FETCH_SIZE_copy/run_counter_collection.csv" \
+    "$OUT/WRITE_SIZE_copy/run_counter_collection.csv" 256 "$PMC" $SRC > "$OUT/traffic_cfg2_noncausal_f32_B2H8N4096d64.txt"
+python3 -m sequence_mixing_amd.profsum counters "$OUT/counters_all/run_counter_collection.csv" "$C3" \
+    "SQ counters per kernel over every workload of the default bench run (matrix-core use, waits, LDS)" \
+    > "$OUT/counters_all_workloads.txt"
 python3 -m sequence_mixing_amd.profsum traffic decode "$OUT/FETCH_SIZE_decode/run_counter_collection.csv" \
     "$OUT/WRITE_SIZE_decode/run_counter_collection.csv" "$OUT/FETCH_SIZE_copy/run_counter_collection.csv" \
     "$OUT/WRITE_SIZE_copy/run_counter_collection.csv" 256 "$PMC" $SRC > "$OUT/traffic_decode_bf16_B64H32Hkv8d128.txt"

@@ -8,6 +8,10 @@
         ``--pmc WRITE_SIZE`` run, each counter scaled by what it reads for a
         plain copy of known size, plus a machine-readable line keyed by the
         SHA-256 of the kernel sources (a later source change voids it).
+    python -m sequence_mixing_amd.profsum counters <counters.csv> "<command>" [title]
+        per-kernel means of a ``--pmc`` run of SQ counters: matrix-core
+        utilisation (MfmaUtil), matrix-core flops (MOPS x 512) over the
+        dispatch time, and where the waves spend their cycles.
 """
 from __future__ import annotations
 
@@ -115,8 +119,58 @@ def traffic(workload, fetch, write, cfetch, cwrite, copy_mib, commands, sources)
     return "\n".join(lines) + "\n"
 
 
+# Dense matrix-core peaks of MI355X (TFLOP/s) by operand type.
+PEAK_TFLOPS = {"F32": 157.3, "BF16": 2500.0, "F16": 2500.0}
+
+
+def counters(path: str, command: str, title: str = "") -> str:
+    """Per-kernel means over dispatches of a --pmc run.
+
+    MfmaUtil: percent of SIMD cycles the matrix core is busy (rocprofv3's
+    derived counter).  MOPS_<type> x 512 is the flop count of the matrix-core
+    instructions; divided by the dispatch's own duration (counters serialise
+    dispatches, so this is a per-launch figure) it gives TFLOP/s, priced
+    against the type's dense peak.  SQ_WAIT_ANY, SQ_ACTIVE_INST_LDS and
+    SQ_WAIT_INST_LDS are shares of SQ_WAVE_CYCLES (all in wave quad-cycles).
+    """
+    per = {}  # kernel -> dispatch -> {counter: value, "_ns": duration}
+    for r in csv.DictReader(open(path)):
+        k = kernel_key(r["Kernel_Name"])
+        d = per.setdefault(k, {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+
+    def mean(ds, c):
+        v = [d[c] for d in ds if c in d]
+        return sum(v) / len(v) if v else float("nan")
+
+    lines = [f"# {title}" if title else "# rocprofv3 counters", "", f"command: {command}", "",
+             f"{'kernel':<56} {'calls':>5} {'us':>8} {'MfmaUtil%':>9} {'mfma_TF/s':>9} {'of_peak':>7} "
+             f"{'wait%':>6} {'lds%':>6} {'ldswait%':>8} {'bankconf':>9}"]
+    for k in sorted(per):
+        ds = list(per[k].values())
+        us = mean(ds, "_ns") / 1e3
+        flops, peak = 0.0, None
+        for t in ("F32", "BF16", "F16"):
+            m = mean(ds, "SQ_INSTS_VALU_MFMA_MOPS_" + t)
+            if m == m and m > 0:
+                flops += m * 512.0
+                peak = PEAK_TFLOPS[t] if peak is None else min(peak, PEAK_TFLOPS[t])
+        tf = flops / (us * 1e-6) / 1e12 if us > 0 else 0.0
+        wc = mean(ds, "SQ_WAVE_CYCLES")
+        share = lambda c: 100.0 * mean(ds, c) / wc if wc == wc and wc > 0 else float("nan")
+        lines.append(f"{k[:56]:<56} {len(ds):>5} {us:>8.2f} {mean(ds, 'MfmaUtil'):>9.2f} {tf:>9.2f} "
+                     f"{(tf / peak if peak else 0.0):>7.3f} {share('SQ_WAIT_ANY'):>6.1f} "
+                     f"{share('SQ_ACTIVE_INST_LDS'):>6.1f} {share('SQ_WAIT_INST_LDS'):>8.1f} "
+                     f"{mean(ds, 'SQ_LDS_BANK_CONFLICT'):>9.0f}")
+    return "\n".join(lines) + "\n"
+
+
 if __name__ == "__main__":
-    if sys.argv[1] == "traffic":
+    if sys.argv[1] == "counters":
+        a = sys.argv[2:]
+        print(counters(a[0], a[1], a[2] if len(a) > 2 else ""), end="")
+    elif sys.argv[1] == "traffic":
         a = sys.argv[2:]
         print(traffic(a[0], a[1], a[2], a[3], a[4], float(a[5]), a[6], a[7:]), end="")
     else:
