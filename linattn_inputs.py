@@ -15,7 +15,10 @@ Recipe (no dataset is involved; the pages measure on none):
     then k [B,Hkv,d], then v [B,Hkv,d];
   * packed batches: sequence lengths log-uniform in [lo, hi] from their own
     seeded generator, then every sequence's q, k, v as a B = 1 prefill with
-    seed + 17 * index.
+    seed + 17 * index;
+  * decayed sums: the log-decay g [B,Hkv,N] (fp32) of every token is
+    logsigmoid(u) / 16 with u ~ N(0,1) from its own seeded generator (a gate
+    in (0, 1) close to 1: exp(g) is about 0.96 at u = 0).
 """
 from __future__ import annotations
 
@@ -110,3 +113,14 @@ def packed_qkv(p: dict = PACKED):
     lens = packed_lengths(p["nseqs"], p["lo"], p["hi"], p["seed"])
     return lens, [make_qkv(1, p["H"], p["Hkv"], n, p["d"], p["dtype"], p["seed"] + 17 * i) for i, n in enumerate(lens)]
 
+
+
+def make_decay(B: int, Hkv: int, N: int, seed: int):
+    """Log-decay g [B,Hkv,N] in fp32: logsigmoid(u) / 16, u ~ N(0,1) seeded (g < 0)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    u = torch.randn(B, Hkv, N, generator=gen, dtype=torch.float32)
+    return torch.nn.functional.logsigmoid(u) / 16.0
+
+
+# The decayed-sum workload: cfg3's shape with a per-token gate.
+DECAY = Workload("decayed causal bf16 B2 H8 N16384 d64", "bf16", 2, 8, 8, 16384, 64, 1006)

@@ -11,7 +11,10 @@ from its "Features" list and Katharopoulos et al. 2020 cited under its
 "Reference" section): O = phi(Q) (phi(K)^T V), phi = ELU + 1, causal rows
 see keys s <= t, optional normaliser phi(q_t) . z_t.  The backward pass is the
 chain rule on that definition, with the reverse-time walk of a running sum
-(Stream efficiency essay, section 4.2).
+(Stream efficiency essay, section 4.2).  The decayed variant multiplies the
+running sums by exp(g_t) before token t is added, the essay's scan form
+h_t = h_{t-1} a_t + b_t carried over to S and z (a reading: the pages give no
+decayed linear attention).
 """
 from __future__ import annotations
 
@@ -65,6 +68,10 @@ def _load():
         lib.linattn_ref_bwd.argtypes = [dp] * 8 + [ctypes.c_int] * 8
         lib.linattn_ref_decode_step.restype = ctypes.c_int
         lib.linattn_ref_decode_step.argtypes = [dp] * 6 + [ctypes.c_int] * 5
+        lib.linattn_ref_fwd_decay.restype = ctypes.c_int
+        lib.linattn_ref_fwd_decay.argtypes = [dp] * 5 + [ctypes.c_int] * 6 + [dp] * 4 + [ctypes.c_int]
+        lib.linattn_ref_decode_step_decay.restype = ctypes.c_int
+        lib.linattn_ref_decode_step_decay.argtypes = [dp] * 7 + [ctypes.c_int] * 5
         _lib = lib
     return _lib
 
@@ -196,4 +203,46 @@ def ref_decode_step(S: np.ndarray, z: np.ndarray | None, q, k, v, normalise: boo
         _use("elu1")
     if rc != 0:
         raise ValueError(f"linattn_ref_decode_step rejected its arguments (rc={rc})")
+    return out
+
+
+def ref_fwd_decay(q, k, v, g, normalise: bool = True, want_state: bool = False, nthreads: int | None = None,
+                  state_in=None, z_in=None):
+    """Causal forward pass with decayed sums.  g [B,Hkv,N] is the log-decay of
+    every token: S_t = exp(g_t) S_{t-1} + phi(k_t) v_t^T (z likewise).  Other
+    arguments and results as ref_fwd."""
+    q, k, v, gg = _f64(q), _f64(k), _f64(v), _f64(g)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, d) and v.shape == (B, Hkv, N, d) and gg.shape == (B, Hkv, N)
+    Si = None if state_in is None else _f64(state_in)
+    zi = None if z_in is None else _f64(z_in)
+    assert Si is None or Si.shape == (B, Hkv, d, d)
+    assert zi is None or zi.shape == (B, Hkv, d)
+    out = np.zeros((B, H, N, d), dtype=np.float64)
+    S = np.zeros((B, Hkv, d, d), dtype=np.float64) if want_state else None
+    z = np.zeros((B, Hkv, d), dtype=np.float64) if want_state else None
+    rc = _load().linattn_ref_fwd_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(gg), _ptr(out), B, H, Hkv, N, d,
+                                       int(bool(normalise)), _ptr(Si), _ptr(zi), _ptr(S), _ptr(z),
+                                       nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"linattn_ref_fwd_decay rejected its arguments (rc={rc})")
+    return (out, S, z) if want_state else out
+
+
+def ref_decode_step_decay(S: np.ndarray, z: np.ndarray | None, q, k, v, g, normalise: bool = True):
+    """One decode step with decayed sums; g [B,Hkv] is the token's log-decay.
+    S, z (fp64) are updated in place; returns out [B,H,d]."""
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    if z is not None:
+        assert z.dtype == np.float64 and z.flags.c_contiguous
+    q, k, v, gg = _f64(q), _f64(k), _f64(v), _f64(g)
+    B, H, d = q.shape
+    Hkv = k.shape[1]
+    assert gg.shape == (B, Hkv)
+    out = np.zeros((B, H, d), dtype=np.float64)
+    rc = _load().linattn_ref_decode_step_decay(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(gg), _ptr(out),
+                                               B, H, Hkv, d, int(bool(normalise)))
+    if rc != 0:
+        raise ValueError(f"linattn_ref_decode_step_decay rejected its arguments (rc={rc})")
     return out

@@ -31,6 +31,13 @@
  *   - continuation (README "Features", the KV-cache-reuse item: a prompt's
  *     state carried into later tokens): the same forward pass with S and z
  *     starting from given sums of earlier tokens instead of zero.
+ *   - decayed state (a reading: the pages define decay only for the scan of
+ *     the Stream efficiency essay, section 4.2, h_t = h_{t-1} a_t + b_t; for
+ *     linear attention the running sums take the same form): with a log-decay
+ *     g_t per (batch, kv head, token) and a_t = exp(g_t),
+ *         S_t = a_t S_{t-1} + phi(k_t) v_t^T,   z_t = a_t z_{t-1} + phi(k_t),
+ *     and o_t as above; causal only (linattn_ref_fwd_decay); decode likewise
+ *     (linattn_ref_decode_step_decay).  g = 0 everywhere is the plain form.
  *   - backward (the README's project layout names a backward module and its
  *     test without their content; the Stream efficiency essay, section 4.2,
  *     gives the pattern of a running-sum recurrence differentiated by a
@@ -78,6 +85,7 @@ double linattn_ref_phi(double x)
 typedef struct {
     const double *q, *k, *v;
     const double *state_in, *z_in; /* starting sums, or NULL for zero */
+    const double *g;               /* log-decay [B][Hkv][N], or NULL for none (causal only) */
     double *out, *state_out, *z_out;
     int B, H, Hkv, N, d, causal, normalise;
     int nitems, nthreads, tid;
@@ -121,8 +129,17 @@ static void fwd_item(const fwd_job *J, int item)
         }
     }
 
+    const double *gb = J->g ? J->g + ((size_t)b * J->Hkv + g) * (size_t)N : NULL;
     for (int t = 0; t < N; ++t) {
         if (J->causal) {
+            /* Decay the sums of the earlier tokens by a_t = exp(g_t). */
+            if (gb) {
+                const double a = exp(gb[t]);
+                for (int i = 0; i < d; ++i) {
+                    for (int jj = 0; jj < w; ++jj) S[(size_t)i * w + jj] *= a;
+                    z[i] *= a;
+                }
+            }
             /* Absorb token t before reading: query t sees keys s <= t. */
             for (int i = 0; i < d; ++i) f[i] = linattn_ref_phi(kb[(size_t)t * d + i]);
             for (int i = 0; i < d; ++i) {
@@ -172,12 +189,13 @@ static void *fwd_worker(void *arg)
  * in the layouts given above.  state_out / z_out may be NULL.  Returns 0, or
  * -1 on invalid arguments (nothing is written then).
  */
-int linattn_ref_fwd_from(const double *q, const double *k, const double *v, double *out,
-                         int B, int H, int Hkv, int N, int d, int causal, int normalise,
-                         const double *state_in, const double *z_in,
-                         double *state_out, double *z_out, int nthreads)
+static int fwd_run(const double *q, const double *k, const double *v, const double *g, double *out,
+                   int B, int H, int Hkv, int N, int d, int causal, int normalise,
+                   const double *state_in, const double *z_in,
+                   double *state_out, double *z_out, int nthreads)
 {
     if (!q || !k || !v || !out) return -1;
+    if (g && !causal) return -1;
     if (B < 0 || H <= 0 || Hkv <= 0 || N < 0 || d <= 0 || H % Hkv != 0) return -1;
     if (B == 0) return 0;
     const int ncb = (d + REF_COLBLOCK - 1) / REF_COLBLOCK;
@@ -188,7 +206,7 @@ int linattn_ref_fwd_from(const double *q, const double *k, const double *v, doub
     fwd_job *jobs = malloc((size_t)nthreads * sizeof(fwd_job));
     pthread_t *th = malloc((size_t)nthreads * sizeof(pthread_t));
     for (int t = 0; t < nthreads; ++t) {
-        fwd_job J = {q, k, v, state_in, z_in, out, state_out, z_out, B, H, Hkv, N, d, causal, normalise,
+        fwd_job J = {q, k, v, state_in, z_in, g, out, state_out, z_out, B, H, Hkv, N, d, causal, normalise,
                      nitems, nthreads, t};
         jobs[t] = J;
     }
@@ -198,6 +216,29 @@ int linattn_ref_fwd_from(const double *q, const double *k, const double *v, doub
     free(jobs);
     free(th);
     return 0;
+}
+
+int linattn_ref_fwd_from(const double *q, const double *k, const double *v, double *out,
+                         int B, int H, int Hkv, int N, int d, int causal, int normalise,
+                         const double *state_in, const double *z_in,
+                         double *state_out, double *z_out, int nthreads)
+{
+    return fwd_run(q, k, v, NULL, out, B, H, Hkv, N, d, causal, normalise, state_in, z_in, state_out, z_out,
+                   nthreads);
+}
+
+/*
+ * Causal forward pass with decayed sums: g [B][Hkv][N] holds the log-decay
+ * of every token (a_t = exp(g_t) multiplies S and z before token t is
+ * added).  Other arguments as linattn_ref_fwd_from.
+ */
+int linattn_ref_fwd_decay(const double *q, const double *k, const double *v, const double *g, double *out,
+                          int B, int H, int Hkv, int N, int d, int normalise,
+                          const double *state_in, const double *z_in,
+                          double *state_out, double *z_out, int nthreads)
+{
+    if (!g) return -1;
+    return fwd_run(q, k, v, g, out, B, H, Hkv, N, d, 1, normalise, state_in, z_in, state_out, z_out, nthreads);
 }
 
 /* Forward pass from zero sums (see linattn_ref_fwd_from). */
@@ -215,9 +256,9 @@ int linattn_ref_fwd(const double *q, const double *k, const double *v, double *o
  * when normalise == 0).  q/out are [B][H][d], k/v are [B][Hkv][d].
  * The state absorbs (k, v) first, then every query head of the group reads it.
  */
-int linattn_ref_decode_step(double *state, double *z, const double *q, const double *k,
-                            const double *v, double *out, int B, int H, int Hkv, int d,
-                            int normalise)
+static int decode_run(double *state, double *z, const double *q, const double *k,
+                      const double *v, const double *gd, double *out, int B, int H, int Hkv, int d,
+                      int normalise)
 {
     if (!state || !q || !k || !v || !out) return -1;
     if (normalise && !z) return -1;
@@ -231,6 +272,13 @@ int linattn_ref_decode_step(double *state, double *z, const double *q, const dou
             double *zz = z ? z + ((size_t)b * Hkv + g) * (size_t)d : NULL;
             const double *kt = k + ((size_t)b * Hkv + g) * (size_t)d;
             const double *vt = v + ((size_t)b * Hkv + g) * (size_t)d;
+            if (gd) {
+                const double a = exp(gd[(size_t)b * Hkv + g]);
+                for (int i = 0; i < d; ++i) {
+                    for (int j = 0; j < d; ++j) S[(size_t)i * d + j] *= a;
+                    if (zz) zz[i] *= a;
+                }
+            }
             for (int i = 0; i < d; ++i) f[i] = linattn_ref_phi(kt[i]);
             for (int i = 0; i < d; ++i) {
                 for (int j = 0; j < d; ++j) S[(size_t)i * d + j] += f[i] * vt[j];
@@ -254,6 +302,23 @@ int linattn_ref_decode_step(double *state, double *z, const double *q, const dou
     free(f);
     free(p);
     return 0;
+}
+
+int linattn_ref_decode_step(double *state, double *z, const double *q, const double *k,
+                            const double *v, double *out, int B, int H, int Hkv, int d,
+                            int normalise)
+{
+    return decode_run(state, z, q, k, v, NULL, out, B, H, Hkv, d, normalise);
+}
+
+/* One decode step with decayed sums: g [B][Hkv] is this token's log-decay;
+ * S and z are multiplied by exp(g) before the token is added. */
+int linattn_ref_decode_step_decay(double *state, double *z, const double *q, const double *k,
+                                  const double *v, const double *g, double *out, int B, int H, int Hkv, int d,
+                                  int normalise)
+{
+    if (!g) return -1;
+    return decode_run(state, z, q, k, v, g, out, B, H, Hkv, d, normalise);
 }
 
 /* d phi / dx.  ELU + 1: 1 for x > 0, exp(x) otherwise (both sides give 1 at

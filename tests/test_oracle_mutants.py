@@ -17,14 +17,12 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "linattn_ref.c")
 
-CAUSAL_ABSORB = """        if (J->causal) {
-            /* Absorb token t before reading: query t sees keys s <= t. */
+CAUSAL_ABSORB = """            /* Absorb token t before reading: query t sees keys s <= t. */
             for (int i = 0; i < d; ++i) f[i] = linattn_ref_phi(kb[(size_t)t * d + i]);
             for (int i = 0; i < d; ++i) {
                 for (int jj = 0; jj < w; ++jj) S[(size_t)i * w + jj] += f[i] * vb[(size_t)t * d + j0 + jj];
                 z[i] += f[i];
             }
-        }
 """
 
 
@@ -37,7 +35,7 @@ def _exclusive_mask(src: str) -> str:
         }
 """
     assert anchor in src
-    return src.replace(anchor, anchor + CAUSAL_ABSORB, 1)
+    return src.replace(anchor, anchor + "        if (J->causal) {\n" + CAUSAL_ABSORB + "        }\n", 1)
 
 
 DECODE_UPDATE = """            for (int i = 0; i < d; ++i) {
@@ -57,6 +55,29 @@ def _decode_reads_before_update(src: str) -> str:
 """
     assert anchor in src
     return src.replace(anchor, anchor + DECODE_UPDATE, 1)
+
+
+DECAY_BLOCK = """            if (gb) {
+                const double a = exp(gb[t]);
+                for (int i = 0; i < d; ++i) {
+                    for (int jj = 0; jj < w; ++jj) S[(size_t)i * w + jj] *= a;
+                    z[i] *= a;
+                }
+            }
+"""
+
+
+def _decay_after_absorb(src: str) -> str:
+    """Decay after token t is added: S_t = a_t (S_{t-1} + phi(k_t) v_t^T)."""
+    assert DECAY_BLOCK in src
+    src = src.replace(DECAY_BLOCK, "", 1)
+    anchor = """                z[i] += f[i];
+            }
+        }
+        for (int h = g * G; h < (g + 1) * G; ++h) {"""
+    assert anchor in src
+    return src.replace(anchor, anchor.replace("        }\n        for (int h", DECAY_BLOCK.replace("            ", "            ", 1)
+                                               + "        }\n        for (int h", 1), 1)
 
 
 BWD_GATHER = "        if (J->causal) GATHER(s);\n"
@@ -107,6 +128,14 @@ MUTANTS = {
     "relu_keeps_negatives": lambda s: s.replace("if (g_feature_map == 1) return x > 0.0 ? x : 0.0;",
                                                 "if (g_feature_map == 1) return x > -0.5 ? x : 0.0;"),
     "softplus_derivative_sign": lambda s: s.replace("return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(x));"),
+    "decay_applied_after_absorb": _decay_after_absorb,
+    "decay_skips_z": lambda s: s.replace("S[(size_t)i * w + jj] *= a;\n                    z[i] *= a;",
+                                         "S[(size_t)i * w + jj] *= a;\n"),
+    "decay_sign_flipped": lambda s: s.replace("const double a = exp(gb[t]);", "const double a = exp(-gb[t]);"),
+    "decay_reads_next_token": lambda s: s.replace("const double a = exp(gb[t]);",
+                                                  "const double a = exp(gb[t + 1 < N ? t + 1 : t]);"),
+    "decode_decay_skipped": lambda s: s.replace("const double a = exp(gd[(size_t)b * Hkv + g]);",
+                                                "const double a = 1.0 + 0.0 * gd[(size_t)b * Hkv + g];"),
 }
 
 
@@ -123,6 +152,7 @@ def test_pins_catch_mutant(name, tmp_path):
     env = dict(os.environ, LINATTN_REF_LIB=str(so_path))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle.py"), os.path.join(ROOT, "tests", "test_oracle_bwd.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_phi.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_phi.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_decay.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the oracle pins:\n{r.stdout[-2000:]}"
