@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 7
+#define LINATTN_ABI_VERSION 8
 
 enum { LINATTN_F32 = 0, LINATTN_BF16 = 1, LINATTN_F16 = 2 };
 /* Feature maps phi (README "Features": custom kernel plugins, phi
@@ -221,6 +221,48 @@ int linattn_fwd_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype,
 int linattn_decode_step(float *state, float *z, const void *q, const void *k, const void *v,
                         void *out, int B, int H, int Hkv, int d, int normalise, int dtype,
                         hipStream_t stream);
+
+/*
+ * linattn_fwd_decay - causal forward pass with decayed running sums.  The
+ * pages give decay only for the scan of the Stream efficiency essay
+ * (section 4.2: h_t = h_{t-1} a_t + b_t); taken over to the sums of linear
+ * attention with a log-decay g per (batch, kv head, token):
+ *     S_t = exp(g_t) S_{t-1} + phi(k_t) v_t^T,   z_t = exp(g_t) z_{t-1} + phi(k_t),
+ *     o_t = phi(q_t)^T S_t / (phi(q_t) . z_t)   (numerator only when normalise == 0),
+ * with S and z starting from state_in / z_in (zero when NULL).  g = 0
+ * everywhere gives linattn_fwd_from_state's rows; a query head reads its kv
+ * head's sums, so the decay is per kv head.
+ *
+ *   g           device fp32 [B][Hkv][N], read only, 4-byte aligned.  Meant for
+ *               g <= 0 (every factor in (0, 1]); larger values are not
+ *               checked and can overflow.  Values below -20 (factors under
+ *               2.1e-9) are taken as -20, so a reset (g = -inf) works; NaN
+ *               propagates.
+ *   state_in, z_in  device fp32 [B][Hkv][d][d] / [B][Hkv][d] or NULL (zero).
+ * The other arguments are those of linattn_fwd with causal = 1.  Supported:
+ * the default feature map (ELU + 1) in any element type, and every chunk
+ * except one that makes an fp32 kernel shift its state copies (fp32,
+ * d = 64, chunk 128): LINATTN_ERR_UNSUPPORTED otherwise.  The workspace is
+ * linattn_fwd_decay_workspace_bytes(B, H, Hkv, N, d, dtype, chunk) bytes:
+ * that of linattn_fwd plus one float per segment partial.  state_out /
+ * z_out may alias neither state_in nor z_in.
+ */
+int linattn_fwd_decay(const void *q, const void *k, const void *v, const float *g, void *out,
+                      int B, int H, int Hkv, int N, int d, int normalise, int dtype,
+                      const float *state_in, const float *z_in, float *state_out, float *z_out, int chunk,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+/* Workspace bytes linattn_fwd_decay needs; (size_t)-1 for arguments it rejects. */
+size_t linattn_fwd_decay_workspace_bytes(int B, int H, int Hkv, int N, int d, int dtype, int chunk);
+
+/*
+ * linattn_decode_step_decay - linattn_decode_step with decayed sums: for
+ * every batch b and kv head g the state and normaliser are first multiplied
+ * by exp(gd[b][g]), then the token is added and read as in
+ * linattn_decode_step.  gd: device fp32 [B][Hkv], read only, 4-byte aligned.
+ */
+int linattn_decode_step_decay(float *state, float *z, const void *q, const void *k, const void *v,
+                              const float *gd, void *out, int B, int H, int Hkv, int d, int normalise,
+                              int dtype, hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *linattn_status_string(int status);

@@ -75,6 +75,12 @@ def load():
         lib.linattn_bwd.argtypes = [vp] * 8 + [i] * 8 + [vp, sz, vp]
         lib.linattn_bwd_workspace_bytes.restype = sz
         lib.linattn_bwd_workspace_bytes.argtypes = [i] * 7
+        lib.linattn_fwd_decay.restype = i
+        lib.linattn_fwd_decay.argtypes = [vp] * 5 + [i] * 7 + [vp] * 4 + [i, vp, sz, vp]
+        lib.linattn_fwd_decay_workspace_bytes.restype = sz
+        lib.linattn_fwd_decay_workspace_bytes.argtypes = [i] * 7
+        lib.linattn_decode_step_decay.restype = i
+        lib.linattn_decode_step_decay.argtypes = [vp] * 7 + [i] * 6 + [vp]
         lib.linattn_status_string.restype = ctypes.c_char_p
         lib.linattn_status_string.argtypes = [i]
         lib.linattn_abi_version.restype = i
@@ -173,6 +179,26 @@ def linattn_bwd_workspace_bytes(B, H, Hkv, N, d, causal, dtype) -> int:
     """C ``linattn_bwd_workspace_bytes``; returns -1 for invalid arguments."""
     r = load().linattn_bwd_workspace_bytes(B, H, Hkv, N, d, int(causal), dtype)
     return -1 if r == ctypes.c_size_t(-1).value else r
+
+
+def linattn_fwd_decay(q, k, v, g, out, B, H, Hkv, N, d, normalise, dtype, state_in=None, z_in=None,
+                      state_out=None, z_out=None, chunk=0, workspace=None, workspace_bytes=0, stream=None) -> int:
+    """C ``linattn_fwd_decay``; returns the status code (0 = ok)."""
+    return load().linattn_fwd_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out), B, H, Hkv, N, d, int(normalise),
+                                    dtype, _ptr(state_in), _ptr(z_in), _ptr(state_out), _ptr(z_out), chunk,
+                                    _ptr(workspace), workspace_bytes, _stream(stream))
+
+
+def linattn_fwd_decay_workspace_bytes(B, H, Hkv, N, d, dtype, chunk=0) -> int:
+    """C ``linattn_fwd_decay_workspace_bytes``; returns -1 for arguments it rejects."""
+    r = load().linattn_fwd_decay_workspace_bytes(B, H, Hkv, N, d, dtype, chunk)
+    return -1 if r == ctypes.c_size_t(-1).value else r
+
+
+def linattn_decode_step_decay(state, z, q, k, v, g, out, B, H, Hkv, d, normalise, dtype, stream=None) -> int:
+    """C ``linattn_decode_step_decay``; returns the status code (0 = ok)."""
+    return load().linattn_decode_step_decay(_ptr(state), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out), B,
+                                            H, Hkv, d, int(normalise), dtype, _stream(stream))
 
 
 def linattn_status_string(code: int) -> str:

@@ -87,12 +87,15 @@ struct Main {
     __device__ static int tile_of(int w, int i) { return w * MAXST + i; }
 };
 
-template <typename T, int D, int C, int GT, typename IO>
+// DK: decayed sums (dense batches): gd [seq][N] holds the log-decay of every
+// token; the chunk's tile sums of g (DecayTab) scale the state update, the
+// scores within and next to the diagonal, and the state copy each query reads.
+template <typename T, int D, int C, int GT, typename IO, bool DK = false>
 __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) void k_causal_chunks(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ out,
     const float *__restrict__ ws, float *__restrict__ state_out, float *__restrict__ z_out,
     int H, int Hkv, int N, int G, int P, int seg_len, int normalise, const float *__restrict__ s_in,
-    const float *__restrict__ z_in, Packed pk)
+    const float *__restrict__ z_in, Packed pk, const float *__restrict__ gd = nullptr)
 {
     using M = Main<T, D, C, GT>;
     using v8 = typename Vt<T>::v8;
@@ -106,6 +109,8 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
     __shared__ __attribute__((aligned(16))) T smQ[GT * C * D];
     __shared__ __attribute__((aligned(16))) T smST[NSC][D * D];
     __shared__ __attribute__((aligned(16))) T smZ[NSC][D];
+    __shared__ __attribute__((aligned(16))) DecayTab<C> smDT;  // DK only
+    static_assert(!(DK && M::SHIFT), "decayed sums need one state copy per key tile or pair");
     const Tile<T, D> sK{smK}, sV{smV}, sQ{smQ};
 
     const int HB = G / GT;
@@ -171,7 +176,9 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
     constexpr int E = (int)sizeof(T);
     struct Regs {
         g16 k[M::LK], v[M::LK], q[M::LQ];
+        float g;  // DK: log-decay of token t0 + tid
     };
+    const float *gb = DK ? gd + (size_t)seq * N : nullptr;
     Regs ra;
     // q / out group l of this thread: byte offset from (head block, token t0)
     // and its token row within the chunk (qt = C marks a group past the block).
@@ -202,6 +209,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, rows ? (qspan - t0 * D) * E : 0);
 #pragma unroll
         for (int l = 0; l < M::LQ; ++l) r.q[l] = buf_load16<g16>(rq, qt[l] < rows ? qoff[l] : kOutOfRange);
+        if constexpr (DK) r.g = tid < rows ? gb[t0 + tid] : 0.f;
     };
     // The output parked in the q rows: read into registers before phi(q) of
     // the next chunk overwrites them, stored after the next loads are issued
@@ -239,6 +247,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
     load_all(ra, s0);
     stage_rows<T, D, C, TH, IO>(ra.k, ra.v, sK, sV, min(C, N - s0), tid);
     stage_q(ra);
+    if constexpr (DK) decay_stage<C>(smDT, ra.g, tid);
     load_all(ra, s0 + C);
     lds_barrier();
 
@@ -290,8 +299,16 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                 for (int kt = 0; kt < CT; ++kt) {
                     if (!M::SHIFT && kt % RPC == 0 && kt < kt_valid) publish(kt / RPC);
                     if (kt < kt_upd) {
-                        const float dz = tile_state_update<T, D>(S[i], zown, it, jt, kt, sK, sV, lane);
-                        if (zown) zs += BF ? dz : dz + __shfl_xor(dz, 32);
+                        if constexpr (DK) {
+                            // the sums fade over the tile, then its keys are added with their weights
+                            const float a = __builtin_amdgcn_exp2f(smDT.TL[kt] * kLog2e);
+                            S[i] *= a;
+                            const float dz = tile_state_update<T, D>(S[i], zown, it, jt, kt, sK, sV, lane, smDT.W);
+                            if (zown) zr = a * zr + (BF ? dz : dz + __shfl_xor(dz, 32));
+                        } else {
+                            const float dz = tile_state_update<T, D>(S[i], zown, it, jt, kt, sK, sV, lane);
+                            if (zown) zs += BF ? dz : dz + __shfl_xor(dz, 32);
+                        }
                     }
                     if (M::SHIFT && kt < CT - 1 && kt < kt_valid) publish(kt);
                 }
@@ -317,6 +334,21 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
             const bool sub = M::SHIFT && r == 0;
             const bool off = r % RPC != 0;   // one unmasked key tile r-1 before the diagonal
             const int qrow = g * C + r * 32 + n;
+            // DK: L of this query and of the 16 keys its lane holds (below),
+            // and the fade qs from the state copy to the query.
+            float lq = 0.f, qs = 1.f;
+            if constexpr (DK) {
+                lq = smDT.L[r * 32 + n];
+                qs = __builtin_amdgcn_exp2f((lq + (off ? smDT.TL[r - 1] : 0.f)) * kLog2e);
+            }
+            auto key_l = [&](int tile, float (&lk)[16]) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 x = *reinterpret_cast<const f32x4 *>(&smDT.L[tile * 32 + 8 * q4 + 4 * h]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) lk[4 * q4 + e] = x[e];
+                }
+            };
             // Pt[key][query] = phi(K) phi(Q)^T; accumulator reg i holds key
             // 8(i/4) + 4h + i%4 of the tile for query n.
             v8 pb0, pb1, po0 = v8{}, po1 = v8{};
@@ -328,10 +360,21 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                 // tile for query n; keep keys <= n (or, subtracting, -Pt for keys > n).
                 const int kmax = n - 4 * h;
                 float pv[16];
+                if constexpr (DK) {
+                    // kept scores fade by exp(L[query] - L[key]) (<= 1)
+                    float lk[16];
+                    key_l(r, lk);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const bool le = 8 * (i / 4) + (i % 4) <= kmax;
-                    pv[i] = sub ? (le ? 0.f : -Pt[i]) : (le ? Pt[i] : 0.f);
+                    for (int i = 0; i < 16; ++i) {
+                        const bool le = 8 * (i / 4) + (i % 4) <= kmax;
+                        pv[i] = le ? Pt[i] * __builtin_amdgcn_exp2f((lq - lk[i]) * kLog2e) : 0.f;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const bool le = 8 * (i / 4) + (i % 4) <= kmax;
+                        pv[i] = sub ? (le ? 0.f : -Pt[i]) : (le ? Pt[i] : 0.f);
+                    }
                 }
                 pb0 = cvt8<T>(pv);
                 pb1 = cvt8<T>(pv + 8);
@@ -341,8 +384,17 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
 #pragma unroll
                 for (int kq = 0; kq < KBD; ++kq) mma(Po, sK.read8(r * 32 - 32 + n, kq * 16 + h * 8), qf[kq]);
                 float ov[16];
+                if constexpr (DK) {
+                    // keys of the tile before: exp(L[query] + TL[r-1] - L[key])
+                    float lk[16];
+                    key_l(r - 1, lk);
+                    const float lt = lq + smDT.TL[r - 1];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) ov[i] = Po[i];
+                    for (int i = 0; i < 16; ++i) ov[i] = Po[i] * __builtin_amdgcn_exp2f((lt - lk[i]) * kLog2e);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) ov[i] = Po[i];
+                }
                 po0 = cvt8<T>(ov);
                 po1 = cvt8<T>(ov + 8);
             }
@@ -357,18 +409,29 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                     mma(Dn, ones8<T>(), po0);
                     mma(Dn, ones8<T>(), po1);
                 }
+                if constexpr (DK) {
+                    // the copy's z fades by qs: its own accumulator
+                    f32x16 Dz = f32x16{};
 #pragma unroll
-                for (int kq = 0; kq < KBD; ++kq)
-                    mma(Dn, *reinterpret_cast<const v8 *>(&smZ[j][kq * 16 + h * 8]), qf[kq]);
-                den = Dn[0];
+                    for (int kq = 0; kq < KBD; ++kq)
+                        mma(Dz, *reinterpret_cast<const v8 *>(&smZ[j][kq * 16 + h * 8]), qf[kq]);
+                    den = Dn[0] + qs * Dz[0];
+                } else {
+#pragma unroll
+                    for (int kq = 0; kq < KBD; ++kq)
+                        mma(Dn, *reinterpret_cast<const v8 *>(&smZ[j][kq * 16 + h * 8]), qf[kq]);
+                    den = Dn[0];
+                }
             } else {
                 float ds = 0.f;
 #pragma unroll
                 for (int s = 0; s < 8; ++s) ds += (float)pb0[s] + (float)pb1[s] + (float)po0[s] + (float)po1[s];
+                float dzs = 0.f;
 #pragma unroll
                 for (int kq = 0; kq < KBD; ++kq)
 #pragma unroll
-                    for (int s = 0; s < 8; ++s) ds += (float)qf[kq][s] * (float)smZ[j][kq * 16 + h * 8 + s];
+                    for (int s = 0; s < 8; ++s) (DK ? dzs : ds) += (float)qf[kq][s] * (float)smZ[j][kq * 16 + h * 8 + s];
+                if constexpr (DK) ds += qs * dzs;
                 den = ds + __shfl_xor(ds, 32);
             }
             const float inv = normalise ? 1.f / den : 1.f;
@@ -378,14 +441,22 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                 // O^T[feature][query] = V^T Pt (slot s of K-block kb2 holds key
                 // 16 kb2 + 8 (s/4) + 4h + s%4) + V^T Po + S_j^T phi(Q)^T.
                 f32x16 O = f32x16{};
+                if constexpr (DK) {
+                    // the copy's part first, faded by qs, then the keys of the chunk
+#pragma unroll
+                    for (int kq = 0; kq < KBD; ++kq) mma(O, sST.read8(ct * 32 + n, kq * 16 + h * 8), qf[kq]);
+                    O *= qs;
+                }
                 mma(O, colfrag(sV, r * 32 + 4 * h, r * 32 + 8 + 4 * h, ct * 32, lane), pb0);
                 mma(O, colfrag(sV, r * 32 + 16 + 4 * h, r * 32 + 24 + 4 * h, ct * 32, lane), pb1);
                 if (off) {
                     mma(O, colfrag(sV, r * 32 - 32 + 4 * h, r * 32 - 24 + 4 * h, ct * 32, lane), po0);
                     mma(O, colfrag(sV, r * 32 - 16 + 4 * h, r * 32 - 8 + 4 * h, ct * 32, lane), po1);
                 }
+                if constexpr (!DK) {
 #pragma unroll
-                for (int kq = 0; kq < KBD; ++kq) mma(O, sST.read8(ct * 32 + n, kq * 16 + h * 8), qf[kq]);
+                    for (int kq = 0; kq < KBD; ++kq) mma(O, sST.read8(ct * 32 + n, kq * 16 + h * 8), qf[kq]);
+                }
                 // Park O in this unit's own q rows (every reader of them has read its phi(q)).
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
@@ -413,6 +484,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         if (c + 1 < nch) {
             stage_rows<T, D, C, TH, IO>(ra.k, ra.v, sK, sV, min(C, N - t0 - C), tid);
             stage_q(ra);
+            if constexpr (DK) decay_stage<C>(smDT, ra.g, tid);
             load_all(ra, t0 + 2 * C);  // past the segment: no access
             store_out(o, t0);
             lds_barrier();
@@ -551,7 +623,8 @@ template <typename T, int D, typename IO>
 __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ state, float *__restrict__ z,
                                                           const T *__restrict__ q, const T *__restrict__ k,
                                                           const T *__restrict__ v, T *__restrict__ out, int H,
-                                                          int Hkv, int G, int normalise)
+                                                          int Hkv, int G, int normalise,
+                                                          const float *__restrict__ gd = nullptr)
 {
     constexpr int C4 = D / 4;            // float4 groups per row
     constexpr int RG = kThreads / C4;    // row groups
@@ -611,12 +684,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
         for (int i = 0; i < U; ++i) sqf[e0 + i] = IO::phi::f(Io<T, IO>::f(qg[j][i]));
     }
     lds_barrier();
+    // decayed sums: S and z fade by exp(g) before the token is added
+    const float fade = gd ? __builtin_amdgcn_exp2f(clamp_log_decay(gd[seq]) * kLog2e) : 1.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sz[tid * 4 + i] = zg[i] + sk[tid * 4 + i];
+    for (int i = 0; i < 4; ++i) sz[tid * 4 + i] = (gd ? fade * zg[i] : zg[i]) + sk[tid * 4 + i];
 
     const f32x4 vv{sv[4 * c4], sv[4 * c4 + 1], sv[4 * c4 + 2], sv[4 * c4 + 3]};
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
+        if (gd) Sr[i] *= fade;
         Sr[i] += sk[rg + RG * i] * vv;
         *reinterpret_cast<f32x4 *>(Sb + (size_t)(rg + RG * i) * D + 4 * c4) = Sr[i];
         __builtin_amdgcn_sched_barrier(0);  // rows in load order: each store waits for its own row only
@@ -681,6 +757,7 @@ __global__ void k_fill_copy(float *__restrict__ p, const float *__restrict__ src
 struct Start {
     const float *S;
     const float *z;
+    const float *g = nullptr;  // decayed sums: log-decay [seq][N] (dense causal only)
 };
 
 // Stage timing (nullable): 4 events recorded before each of the three stages
@@ -696,7 +773,7 @@ int record(const Timing *t, int i, hipStream_t st)
 
 
 
-template <typename T, int D, int C, typename IO>
+template <typename T, int D, int C, typename IO, bool DK = false>
 int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out, float *state_out,
             float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev, const Start &s0)
 {
@@ -717,27 +794,30 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
         hipLaunchKernelGGL(k_pack_plan, dim3(1), dim3(kThreads), 0, st, pl.cu, pl.nb, pl.N, pl.seg_len, P, tab);
         pk = Packed{tab, pl.nb, P};
     }
+    // decayed sums: each slot's summed log-decay, after the slots
+    float *gs = DK ? ws + (size_t)pl.nseq * pl.ws_slots * E : nullptr;
     if (pl.causal) {
         if (pl.packed) {
             if (launch_totals<T, D, IO>(c1, pl.Hkv * P, st, kk, vv, ws, pl.N, pl.seg_len, 1, pk, pl.Hkv, 1))
                 return LINATTN_ERR_UNSUPPORTED;
-        } else if (P > 1 && launch_totals<T, D, IO>(c1, pl.nseq * (P - 1), st, kk, vv, ws, pl.N, pl.seg_len, P - 1)) {
+        } else if (P > 1 && launch_totals<T, D, IO, DK>(c1, pl.nseq * (P - 1), st, kk, vv, ws, pl.N, pl.seg_len, P - 1,
+                                                          Packed{nullptr, 0, 0}, 1, 1, s0.g, gs)) {
             return LINATTN_ERR_UNSUPPORTED;
         }
         if (record(ev, 1, st)) return LINATTN_ERR_HIP;
         // the scan also adds the start sums of a continuation into every slot
         if (pl.packed || P > 2 || (P == 2 && (s0.S || s0.z)))
             hipLaunchKernelGGL(k_seg_scan, scan_grid, dim3(kThreads), 0, st, ws, P - 1, D, 0, (float *)nullptr,
-                               (float *)nullptr, s0.S, s0.z, pk, pl.Hkv);
+                               (float *)nullptr, s0.S, s0.z, pk, pl.Hkv, (const float *)gs);
         if (record(ev, 2, st)) return LINATTN_ERR_HIP;
         const dim3 grid((pl.packed ? pl.Hkv : pl.nseq) * (pl.G / pl.gt) * P);
         for (int rep = 0; rep < (ev ? ev->reps : 1); ++rep) switch (pl.gt) {
 #define LINATTN_MAIN(GT)                                                                                            \
     case GT:                                                                                                       \
-        if constexpr (Main<T, D, C, GT>::FITS) {                                                                   \
-            hipLaunchKernelGGL((k_causal_chunks<T, D, C, GT, IO>), grid, dim3(Main<T, D, C, GT>::TH), 0, st, qq, kk,   \
-                               vv, oo, (const float *)ws, state_out, z_out, pl.H, pl.Hkv, pl.N, pl.G, P,           \
-                               pl.seg_len, normalise, s0.S, s0.z, pk);                                             \
+        if constexpr (Main<T, D, C, GT>::FITS && !(DK && Main<T, D, C, GT>::SHIFT)) {                               \
+            hipLaunchKernelGGL((k_causal_chunks<T, D, C, GT, IO, DK>), grid, dim3(Main<T, D, C, GT>::TH), 0, st, qq,   \
+                               kk, vv, oo, (const float *)ws, state_out, z_out, pl.H, pl.Hkv, pl.N, pl.G, P,       \
+                               pl.seg_len, normalise, s0.S, s0.z, pk, s0.g);                                       \
             break;                                                                                                 \
         } else {                                                                                                   \
             return LINATTN_ERR_UNSUPPORTED;                                                                        \
@@ -749,6 +829,8 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
 #undef LINATTN_MAIN
         default: return LINATTN_ERR_UNSUPPORTED;
         }
+    } else if constexpr (DK) {
+        return LINATTN_ERR_UNSUPPORTED;  // decayed sums are causal only
     } else {
         if (launch_totals<T, D, IO>(c1, (pl.packed ? pl.Hkv : pl.nseq) * P, st, kk, vv, ws, pl.N, pl.seg_len, P, pk,
                                 pl.Hkv, 0))
@@ -773,45 +855,45 @@ constexpr bool chunk_ok()
     return Main<T, D, C, 1>::FITS || Main<T, D, C, 2>::FITS || Main<T, D, C, 4>::FITS || Main<T, D, C, 8>::FITS;
 }
 
-template <typename T, int D, typename IO>
+template <typename T, int D, typename IO, bool DK = false>
 int dispatch_chunk(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,
                    float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev,
                    const Start &s0)
 {
     switch (pl.chunk) {
     case 32:
-        if constexpr (chunk_ok<T, D, 32>()) return run_fwd<T, D, 32, IO>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+        if constexpr (chunk_ok<T, D, 32>()) return run_fwd<T, D, 32, IO, DK>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
         break;
     case 64:
-        if constexpr (chunk_ok<T, D, 64>()) return run_fwd<T, D, 64, IO>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+        if constexpr (chunk_ok<T, D, 64>()) return run_fwd<T, D, 64, IO, DK>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
         break;
     case 128:
-        if constexpr (chunk_ok<T, D, 128>()) return run_fwd<T, D, 128, IO>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+        if constexpr (chunk_ok<T, D, 128>()) return run_fwd<T, D, 128, IO, DK>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
         break;
     case 256:
-        if constexpr (chunk_ok<T, D, 256>()) return run_fwd<T, D, 256, IO>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+        if constexpr (chunk_ok<T, D, 256>()) return run_fwd<T, D, 256, IO, DK>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
         break;
     }
     return LINATTN_ERR_UNSUPPORTED;
 }
 
-template <typename T, typename IO = Fmt<T, PhiElu1>>
+template <typename T, typename IO = Fmt<T, PhiElu1>, bool DK = false>
 int dispatch_d(const linattn::Plan &pl, const void *q, const void *k, const void *v, void *out,
                float *state_out, float *z_out, float *ws, int normalise, hipStream_t st, const Timing *ev,
                const Start &s0)
 {
     switch (pl.d) {
-    case 32: return dispatch_chunk<T, 32, IO>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
-    case 64: return dispatch_chunk<T, 64, IO>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
-    case 128: return dispatch_chunk<T, 128, IO>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+    case 32: return dispatch_chunk<T, 32, IO, DK>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+    case 64: return dispatch_chunk<T, 64, IO, DK>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
+    case 128: return dispatch_chunk<T, 128, IO, DK>(pl, q, k, v, out, state_out, z_out, ws, normalise, st, ev, s0);
     }
     return LINATTN_ERR_UNSUPPORTED;
 }
 
 
 template <typename T, typename IO = Fmt<T, PhiElu1>>
-int run_decode(float *state, float *z, const void *q, const void *k, const void *v, void *out, int B, int H,
-               int Hkv, int d, int normalise, hipStream_t st)
+int run_decode(float *state, float *z, const void *q, const void *k, const void *v, const float *g, void *out, int B,
+               int H, int Hkv, int d, int normalise, hipStream_t st)
 {
     const int G = H / Hkv;
     const dim3 grid(B * Hkv), block(kThreads);
@@ -820,9 +902,9 @@ int run_decode(float *state, float *z, const void *q, const void *k, const void 
     const T *vv = static_cast<const T *>(v);
     T *oo = static_cast<T *>(out);
     switch (d) {
-    case 32: hipLaunchKernelGGL((k_decode_step<T, 32, IO>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise); break;
-    case 64: hipLaunchKernelGGL((k_decode_step<T, 64, IO>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise); break;
-    case 128: hipLaunchKernelGGL((k_decode_step<T, 128, IO>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise); break;
+    case 32: hipLaunchKernelGGL((k_decode_step<T, 32, IO>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise, g); break;
+    case 64: hipLaunchKernelGGL((k_decode_step<T, 64, IO>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise, g); break;
+    case 128: hipLaunchKernelGGL((k_decode_step<T, 128, IO>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise, g); break;
     default: return LINATTN_ERR_UNSUPPORTED;
     }
     return launch_status();
@@ -882,14 +964,17 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, int B, int 
     const int rc = packed ? linattn::make_plan_packed(B, H, Hkv, N, d, causal, dtype, chunk, &pl)
                           : linattn::make_plan(B, H, Hkv, N, d, causal, dtype, chunk, &pl);
     if (rc != LINATTN_OK) return rc;
+    const bool decay = s0.g != nullptr;
+    if (decay && (packed || !causal || !linattn::decay_ok(pl))) return LINATTN_ERR_UNSUPPORTED;
+    const size_t need = decay ? linattn::decay_ws_bytes(pl) : pl.ws_bytes;
     if (B == 0) return LINATTN_OK;
     if (packed && !cu) return LINATTN_ERR_NULL;
     pl.cu = cu;
     if (N > 0 && (!q || !k || !v || !out)) return LINATTN_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(state_out) ||
-        !aligned16(z_out) || !aligned16(workspace))
+        !aligned16(z_out) || !aligned16(workspace) || ((uintptr_t)s0.g & 3u))
         return LINATTN_ERR_ALIGN;
-    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LINATTN_ERR_WORKSPACE;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return LINATTN_ERR_WORKSPACE;
     if (N == 0) {
         // No keys: the state and normaliser are the start sums (zero unless
         // continuing); there is no output row.
@@ -901,6 +986,14 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, int B, int 
     float *ws = static_cast<float *>(workspace);
     return with_format(dtype, [&](auto kind) {
         using K = decltype(kind);
+        if (decay) {
+            // decayed sums are built for the default feature map only (decay_ok)
+            if constexpr (std::is_same_v<typename K::IO::phi, PhiElu1>)
+                return dispatch_d<typename K::T, typename K::IO, true>(pl, q, k, v, out, state_out, z_out, ws,
+                                                                       normalise ? 1 : 0, stream, ev, s0);
+            else
+                return (int)LINATTN_ERR_UNSUPPORTED;
+        }
         return dispatch_d<typename K::T, typename K::IO>(pl, q, k, v, out, state_out, z_out, ws, normalise ? 1 : 0,
                                                          stream, ev, s0);
     });
@@ -927,6 +1020,29 @@ int linattn_fwd_from_state(const void *q, const void *k, const void *v, void *ou
         return LINATTN_ERR_SHAPE;  // the start sums are read while the final ones are written
     return fwd_impl(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_out, z_out, chunk, workspace,
                     workspace_bytes, stream, nullptr, Start{state_in, z_in});
+}
+
+size_t linattn_fwd_decay_workspace_bytes(int B, int H, int Hkv, int N, int d, int dtype, int chunk)
+{
+    linattn::Plan pl;
+    if (linattn::make_plan(B, H, Hkv, N, d, 1, dtype, chunk, &pl) != LINATTN_OK || !linattn::decay_ok(pl))
+        return (size_t)-1;
+    return linattn::decay_ws_bytes(pl);
+}
+
+int linattn_fwd_decay(const void *q, const void *k, const void *v, const float *g, void *out, int B, int H, int Hkv,
+                      int N, int d, int normalise, int dtype, const float *state_in, const float *z_in,
+                      float *state_out, float *z_out, int chunk, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream)
+{
+    if (B > 0 && N > 0 && !g) return LINATTN_ERR_NULL;
+    if ((state_out && state_in && (const float *)state_out == state_in) ||
+        (z_out && z_in && (const float *)z_out == z_in))
+        return LINATTN_ERR_SHAPE;  // the start sums are read while the final ones are written
+    // a g pointer is what selects the decayed kernels: with N == 0 none is read
+    static const float no_tokens = 0.f;
+    return fwd_impl(q, k, v, out, B, H, Hkv, N, d, 1, normalise, dtype, state_out, z_out, chunk, workspace,
+                    workspace_bytes, stream, nullptr, Start{state_in, z_in, g ? g : &no_tokens});
 }
 
 size_t linattn_fwd_packed_workspace_bytes(int nseqs, int H, int Hkv, int total, int d, int causal, int dtype,
@@ -967,21 +1083,41 @@ int linattn_fwd_timed(const void *q, const void *k, const void *v, void *out, in
     return LINATTN_OK;
 }
 
-int linattn_decode_step(float *state, float *z, const void *q, const void *k, const void *v, void *out, int B, int H,
-                        int Hkv, int d, int normalise, int dtype, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+int decode_impl(float *state, float *z, const void *q, const void *k, const void *v, const float *g, void *out, int B,
+                int H, int Hkv, int d, int normalise, int dtype, hipStream_t stream)
 {
     if (!valid_dtype(dtype)) return LINATTN_ERR_DTYPE;
     if (B < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || (int64_t)B * Hkv > INT32_MAX) return LINATTN_ERR_SHAPE;
     if (d != 32 && d != 64 && d != 128) return LINATTN_ERR_UNSUPPORTED;
     if (B == 0) return LINATTN_OK;
     if (!state || !q || !k || !v || !out || (normalise && !z)) return LINATTN_ERR_NULL;
-    if (!aligned16(state) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    if (!aligned16(state) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        ((uintptr_t)g & 3u))
         return LINATTN_ERR_ALIGN;
     return with_format(dtype, [&](auto kind) {
         using K = decltype(kind);
-        return run_decode<typename K::T, typename K::IO>(state, z, q, k, v, out, B, H, Hkv, d, normalise ? 1 : 0,
+        return run_decode<typename K::T, typename K::IO>(state, z, q, k, v, g, out, B, H, Hkv, d, normalise ? 1 : 0,
                                                          stream);
     });
+}
+}  // namespace
+
+extern "C" {
+
+int linattn_decode_step(float *state, float *z, const void *q, const void *k, const void *v, void *out, int B, int H,
+                        int Hkv, int d, int normalise, int dtype, hipStream_t stream)
+{
+    return decode_impl(state, z, q, k, v, nullptr, out, B, H, Hkv, d, normalise, dtype, stream);
+}
+
+int linattn_decode_step_decay(float *state, float *z, const void *q, const void *k, const void *v, const float *g,
+                              void *out, int B, int H, int Hkv, int d, int normalise, int dtype, hipStream_t stream)
+{
+    if (B > 0 && !g) return LINATTN_ERR_NULL;
+    return decode_impl(state, z, q, k, v, g, out, B, H, Hkv, d, normalise, dtype, stream);
 }
 
 }  // extern "C"

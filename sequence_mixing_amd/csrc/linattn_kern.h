@@ -342,15 +342,83 @@ template <typename T> __device__ __forceinline__ typename Vt<T>::v8 ones8()
     return o;
 }
 
+// ----------------------------------------------------------- decayed sums
+//
+// Decayed running sums (a reading of the Stream efficiency essay, section
+// 4.2, whose scan is h_t = h_{t-1} a_t + b_t): with the log-decay g_t of
+// every (sequence, kv head, token), S_t = exp(g_t) S_{t-1} + phi(k_t) v_t^T
+// and z_t likewise.  Within a chunk every factor is taken from sums of g over
+// one 32-token tile, so each exponent is a short sum and never positive for
+// g <= 0:
+//   L[t]  sum of g over the tile's tokens up to and including t;
+//   TL[j] L at the last token of tile j (the tile's log-decay);
+//   W[t]  exp(TL[tile(t)] - L[t]): the weight of key t in the sums at the
+//         end of its tile.
+// Then the state after tile j is exp(TL[j]) (state before it) + sum_t W[t]
+// phi(k_t) v_t^T, key s reaches query t of the same tile with
+// exp(L[t] - L[s]) (s <= t), and the state before a query's tile reaches it
+// with exp(L[t]).
+// A factor is exp of a difference of two such sums, so its relative error is
+// about (|L[t]| + |L[s]|) 2^-24: log-decays below kMinLogDecay (a factor
+// under 2.1e-9, which fp32 running sums cannot tell from zero) are taken as
+// kMinLogDecay, keeping |L| <= 640 and every factor within ~4e-5.  NaN stays
+// NaN.
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kMinLogDecay = -20.f;
+__device__ __forceinline__ float clamp_log_decay(float g) { return g < kMinLogDecay ? kMinLogDecay : g; }
+
+template <int C> struct DecayTab {
+    float L[C];
+    float W[C];
+    float TL[C / 32];
+};
+
+// Fills the table from the log-decay gv of token tid (threads tid < C hold
+// one token each; tokens past the sequence or segment carry g = 0).
+template <int C>
+__device__ __forceinline__ void decay_stage(DecayTab<C> &dt, float gv, int tid)
+{
+    if (tid < C) {
+        float x = clamp_log_decay(gv);
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+            const float y = __shfl_up(x, o, 32);
+            if ((tid & 31) >= o) x += y;
+        }
+        const float tl = __shfl(x, 31, 32);
+        dt.L[tid] = x;
+        dt.W[tid] = __builtin_amdgcn_exp2f((tl - x) * kLog2e);
+        if ((tid & 31) == 31) dt.TL[tid >> 5] = x;
+    }
+}
+
+// Multiplies the 8 slots of a key fragment (tokens r0 .. r0 + 7) by their
+// weights W[r0 .. r0 + 7].
+template <typename T>
+__device__ __forceinline__ typename Vt<T>::v8 weigh8(const typename Vt<T>::v8 &a, const float *w)
+{
+    const f32x4 w0 = *reinterpret_cast<const f32x4 *>(w);
+    const f32x4 w1 = *reinterpret_cast<const f32x4 *>(w + 4);
+    float x[8];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        x[s] = (float)a[s] * w0[s];
+        x[4 + s] = (float)a[4 + s] * w1[s];
+    }
+    return cvt8<T>(x);
+}
+
 // State tile (it, jt) += phi(K)^T V over the 32 tokens of key tile kt.
 // The K-block of 16 tokens kb2 puts token kt*32 + 16 kb2 + 8h + s in slot s.
 // When want_z it also returns the tile's column sum of phi(K) for feature
 // it*32 + lane%32: bf16 forms it on the matrix core (1 phi(K) into a scratch
 // accumulator whose every register then holds the sum), fp32 adds on the
 // vector ALUs and returns this half-wave's part (the caller adds the other).
+// With a weight table W (decayed sums) every key is first multiplied by its
+// weight W[token].
 template <typename T, int D>
 __device__ __forceinline__ float tile_state_update(f32x16 &acc, bool want_z, int it, int jt, int kt, Tile<T, D> sK,
-                                                   Tile<T, D> sV, int lane)
+                                                   Tile<T, D> sV, int lane, const float *W = nullptr)
 {
     const int h = lane >> 5;
     float zs = 0.f;
@@ -358,7 +426,8 @@ __device__ __forceinline__ float tile_state_update(f32x16 &acc, bool want_z, int
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
         const int r0 = kt * 32 + 16 * kb2 + 8 * h;
-        const auto a = colfrag(sK, r0, r0 + 4, it * 32, lane);
+        auto a = colfrag(sK, r0, r0 + 4, it * 32, lane);
+        if (W) a = weigh8<T>(a, W + r0);
         const auto b = colfrag(sV, r0, r0 + 4, jt * 32, lane);
         mma(acc, a, b);
         if (want_z) {
@@ -479,14 +548,20 @@ __global__ __launch_bounds__(kThreads) void k_pack_plan(const int *__restrict__ 
 // Chunks of C1 tokens, double-buffered in LDS (one barrier per chunk).
 // Packed batches (pk.tab set): one workgroup per (kv head, segment of all
 // sequences); the last segment of a causal sequence has nothing to do.
-template <typename T, int D, int C1, typename IO>
+// DK (decayed sums, dense causal batches): gd [seq][N] is the log-decay; the
+// total is the decayed sum at the segment's end, and the segment's summed g
+// goes to gs[slot] for the scan.
+template <typename T, int D, int C1, typename IO, bool DK = false>
 __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict__ k, const T *__restrict__ v,
                                                             float *__restrict__ ws, int N, int seg_len, int nslots,
-                                                            Packed pk, int Hkv, int causal)
+                                                            Packed pk, int Hkv, int causal,
+                                                            const float *__restrict__ gd = nullptr,
+                                                            float *__restrict__ gs = nullptr)
 {
     using G = Geo<T, D, C1>;
     __shared__ __attribute__((aligned(16))) T smK[2][C1 * D];
     __shared__ __attribute__((aligned(16))) T smV[2][C1 * D];
+    __shared__ __attribute__((aligned(16))) DecayTab<C1> smD[DK ? 2 : 1];
 
     int seq = blockIdx.x / nslots, p = blockIdx.x % nslots;
     const T *kb = k + (size_t)seq * N * D;
@@ -517,6 +592,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
     constexpr int E = (int)sizeof(T);
     g16 kA[G::LDV], vA[G::LDV], kB[G::LDV], vB[G::LDV];
     auto rows_at = [&](int t0) { return t0 < s1 ? min(C1, s1 - t0) : 0; };
+    // log-decay of token t0 + tid (zero past the segment)
+    const float *gb = DK ? gd + (size_t)seq * N : nullptr;
+    float gA = 0.f, gB = 0.f, glog = 0.f;
+    auto load_g = [&](float &gr, int t0) {
+        if constexpr (DK) gr = tid < rows_at(t0) ? gb[t0 + tid] : 0.f;
+    };
     auto load = [&](g16 (&kr)[G::LDV], g16 (&vr)[G::LDV], int t0) {
         const int rows = rows_at(t0);
         const Rsrc rk = make_rsrc(kb + (size_t)t0 * D, rows * D * E);
@@ -529,8 +610,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
         }
     };
     load(kA, vA, s0);
+    load_g(gA, s0);
     __builtin_amdgcn_sched_barrier(0);  // keep chunk 0's loads ahead of chunk 1's, as in the loop
     load(kB, vB, s0 + C1);
+    load_g(gB, s0 + C1);
     auto absorb = [&](int buf) {
         const Tile<T, D> sK{smK[buf]}, sV{smV[buf]};
 #pragma unroll
@@ -539,22 +622,47 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
             if (st < G::NST) {
                 const int it = st / G::DT, jt = st % G::DT;
 #pragma unroll
-                for (int kt = 0; kt < G::CT; ++kt)
-                    zacc += tile_state_update<T, D>(acc[i], i == 0 && jt == 0, it, jt, kt, sK, sV, lane);
+                for (int kt = 0; kt < G::CT; ++kt) {
+                    if constexpr (DK) {
+                        // the sums so far fade over the tile, then its keys are added with their weights
+                        const float a = __builtin_amdgcn_exp2f(smD[buf].TL[kt] * kLog2e);
+                        acc[i] *= a;
+                        if (i == 0 && jt == 0) zacc *= a;
+                        zacc += tile_state_update<T, D>(acc[i], i == 0 && jt == 0, it, jt, kt, sK, sV, lane,
+                                                        smD[buf].W);
+                    } else {
+                        zacc += tile_state_update<T, D>(acc[i], i == 0 && jt == 0, it, jt, kt, sK, sV, lane);
+                    }
+                }
             }
+        }
+        if constexpr (DK) {
+#pragma unroll
+            for (int kt = 0; kt < G::CT; ++kt) glog += smD[buf].TL[kt];
         }
     };
     // Chunks in pairs; with an odd count the last pair's second chunk lies
     // past the segment and adds zeros (every step issues the same loads).
     for (int ci = 0; ci < nch; ci += 2) {
         stage_rows<T, D, C1, kThreads, IO>(kA, vA, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, rows_at(s0 + ci * C1), tid);
+        if constexpr (DK) {
+            decay_stage<C1>(smD[0], gA, tid);
+            load_g(gA, s0 + (ci + 2) * C1);
+        }
         load(kA, vA, s0 + (ci + 2) * C1);
         lds_barrier();
         absorb(0);
         stage_rows<T, D, C1, kThreads, IO>(kB, vB, Tile<T, D>{smK[1]}, Tile<T, D>{smV[1]}, rows_at(s0 + (ci + 1) * C1), tid);
+        if constexpr (DK) {
+            decay_stage<C1>(smD[1], gB, tid);
+            load_g(gB, s0 + (ci + 3) * C1);
+        }
         load(kB, vB, s0 + (ci + 3) * C1);
         lds_barrier();
         absorb(1);
+    }
+    if constexpr (DK) {
+        if (tid == 0) gs[slot] = glog;
     }
     float *out = ws + slot * (size_t)D * (D + 1);
 #pragma unroll
@@ -583,10 +691,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
 // (slot p gets the sum of slots p..nslots-1), in place.  Modes 0 and 1 start
 // from s_in / z_in (the sums of earlier tokens) when given.
 // Packed batches: blockIdx.y = b * Hkv + kv head, and sequence b's own slots.
+// Decayed sums (gs set, mode 0 only): slot p also has its segment's summed
+// log-decay gs[seq * nslots + p], and the prefix becomes the decayed one,
+// acc = exp(gs[p]) acc + slot p.
 __global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, int nslots, int D, int mode,
                                                        float *__restrict__ state_out, float *__restrict__ z_out,
                                                        const float *__restrict__ s_in, const float *__restrict__ z_in,
-                                                       Packed pk = Packed{nullptr, 0, 0}, int Hkv = 1)
+                                                       Packed pk = Packed{nullptr, 0, 0}, int Hkv = 1,
+                                                       const float *__restrict__ gs = nullptr)
 {
     const int E = D * D + D;
     const int seq = blockIdx.y;
@@ -617,6 +729,17 @@ __global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, i
         float x[BATCH];
 #pragma unroll
         for (int j = 0; j < BATCH; ++j) x[j] = p0 + j < nslots ? base[(size_t)slot(p0 + j) * E] : 0.f;
+        if (gs) {
+            const float *gq = gs + (size_t)seq * nslots;
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) {
+                if (p0 + j < nslots) {
+                    acc = __builtin_amdgcn_exp2f(gq[p0 + j] * kLog2e) * acc + x[j];
+                    base[(size_t)(p0 + j) * E] = acc;
+                }
+            }
+            continue;
+        }
 #pragma unroll
         for (int j = 0; j < BATCH; ++j) {
             acc += x[j];
@@ -680,27 +803,28 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Totals pass with chunks of c1 tokens (32, 64 or 128; at most 16 KiB of K per
 // chunk, so that two chunks of K and V double-buffer in 64 KiB of LDS).
-template <typename T, int D, typename IO = Fmt<T, PhiElu1>>
+template <typename T, int D, typename IO = Fmt<T, PhiElu1>, bool DK = false>
 int launch_totals(int c1, unsigned nblocks, hipStream_t st, const T *k, const T *v, float *ws, int N, int seg_len,
-                  int nslots, Packed pk = Packed{nullptr, 0, 0}, int Hkv = 1, int causal = 1)
+                  int nslots, Packed pk = Packed{nullptr, 0, 0}, int Hkv = 1, int causal = 1,
+                  const float *gd = nullptr, float *gs = nullptr)
 {
     constexpr int cap = 65536 / (4 * D * (int)sizeof(T));
     switch (c1) {
     case 32:
-        hipLaunchKernelGGL((k_seg_totals<T, D, 32, IO>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len, nslots,
-                           pk, Hkv, causal);
+        hipLaunchKernelGGL((k_seg_totals<T, D, 32, IO, DK>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len,
+                           nslots, pk, Hkv, causal, gd, gs);
         return LINATTN_OK;
     case 64:
         if constexpr (64 <= cap) {
-            hipLaunchKernelGGL((k_seg_totals<T, D, 64, IO>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len,
-                               nslots, pk, Hkv, causal);
+            hipLaunchKernelGGL((k_seg_totals<T, D, 64, IO, DK>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N,
+                               seg_len, nslots, pk, Hkv, causal, gd, gs);
             return LINATTN_OK;
         }
         break;
     case 128:
         if constexpr (128 <= cap) {
-            hipLaunchKernelGGL((k_seg_totals<T, D, 128, IO>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len,
-                               nslots, pk, Hkv, causal);
+            hipLaunchKernelGGL((k_seg_totals<T, D, 128, IO, DK>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N,
+                               seg_len, nslots, pk, Hkv, causal, gd, gs);
             return LINATTN_OK;
         }
         break;

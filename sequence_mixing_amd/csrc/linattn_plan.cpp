@@ -139,4 +139,15 @@ int make_plan_packed(int nb, int H, int Hkv, int total, int d, int causal, int d
     return LINATTN_OK;
 }
 
+bool decay_ok(const Plan &p)
+{
+    const int e = (p.dtype & 0xff) != LINATTN_F32 ? 2 : 4;
+    return p.causal && !p.packed && (p.dtype >> 8) == LINATTN_PHI_ELU1 && !main_shape(e, p.d, p.chunk, p.gt).shift;
+}
+
+size_t decay_ws_bytes(const Plan &p)
+{
+    return p.ws_bytes + (size_t)p.nseq * p.ws_slots * sizeof(float);
+}
+
 }  // namespace linattn

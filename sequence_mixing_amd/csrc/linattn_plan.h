@@ -109,4 +109,12 @@ int make_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int ch
 // plus the segment tables.
 int make_plan_packed(int nb, int H, int Hkv, int total, int d, int causal, int dtype, int chunk, Plan *p);
 
+// Decayed sums (a log-decay per token) run on a dense causal plan with the
+// default feature map and a chunk kernel that keeps one state copy per key
+// tile or pair of tiles (never the shifted fp32 copies).
+bool decay_ok(const Plan &p);
+// Their workspace: the plan's slots plus one float per slot (the segment's
+// summed log-decay), nseq * ws_slots * (d * (d + 1) + 1) * 4 bytes.
+size_t decay_ws_bytes(const Plan &p);
+
 }  // namespace linattn

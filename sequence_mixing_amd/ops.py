@@ -7,7 +7,8 @@ from __future__ import annotations
 import torch
 
 from . import (LINATTN_BF16, LINATTN_F16, LINATTN_F32, LinattnError, linattn_bwd, linattn_bwd_workspace_bytes,
-               linattn_decode_step, linattn_fwd, linattn_fwd_from_state, linattn_fwd_packed,
+               linattn_decode_step, linattn_decode_step_decay, linattn_fwd, linattn_fwd_decay,
+               linattn_fwd_decay_workspace_bytes, linattn_fwd_from_state, linattn_fwd_packed,
                linattn_fwd_packed_workspace_bytes, linattn_fwd_workspace_bytes)
 
 _DT = {torch.float32: LINATTN_F32, torch.bfloat16: LINATTN_BF16, torch.float16: LINATTN_F16}
@@ -67,6 +68,42 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=True, normalis
     rc = linattn_fwd(q, k, v, out, B, H, Hkv, N, d, causal, normalise, code, S, z, chunk, ws, nbytes, stream)
     if rc != 0:
         raise LinattnError(rc, "linattn_fwd")
+    return (out, S, z) if want_state else out
+
+
+def fwd_decay(q, k, v, g, normalise=True, chunk=0, want_state=False, out=None, ws=None, stream=None, state_in=None,
+              z_in=None):
+    """Causal forward pass with decayed sums through ``linattn_fwd_decay``: g [B,Hkv,N] fp32
+    is every token's log-decay (S_t = exp(g_t) S_{t-1} + phi(k_t) v_t^T, z likewise)."""
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    for t in (q, k, v):
+        if not (t.is_cuda and t.is_contiguous() and t.dtype == q.dtype):
+            raise ValueError("q, k, v must be contiguous device tensors of one dtype")
+    if k.shape != (B, Hkv, N, d) or v.shape != (B, Hkv, N, d):
+        raise ValueError("k and v must be [B, Hkv, N, d]")
+    if not (g.is_cuda and g.is_contiguous() and g.dtype == torch.float32 and g.shape == (B, Hkv, N)):
+        raise ValueError("g must be a contiguous fp32 device tensor [B, Hkv, N]")
+    for t, shape in ((state_in, (B, Hkv, d, d)), (z_in, (B, Hkv, d))):
+        if t is not None and not (t.is_cuda and t.is_contiguous() and t.dtype == torch.float32 and t.shape == shape):
+            raise ValueError("state_in / z_in must be contiguous fp32 device tensors [B,Hkv,d,d] / [B,Hkv,d]")
+    code = dtype_code(q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    S = z = None
+    if want_state:
+        S = torch.empty(B, Hkv, d, d, dtype=torch.float32, device=q.device)
+        z = torch.empty(B, Hkv, d, dtype=torch.float32, device=q.device)
+    if ws is None:
+        n = linattn_fwd_decay_workspace_bytes(B, H, Hkv, N, d, code, chunk)
+        if n < 0:
+            raise LinattnError(-4, "linattn_fwd_decay_workspace_bytes")
+        ws = torch.empty((n + 3) // 4, dtype=torch.float32, device=q.device) if n > 0 else None
+    nbytes = ws.numel() * 4 if ws is not None else 0
+    rc = linattn_fwd_decay(q, k, v, g, out, B, H, Hkv, N, d, normalise, code, state_in, z_in, S, z, chunk, ws, nbytes,
+                           stream)
+    if rc != 0:
+        raise LinattnError(rc, "linattn_fwd_decay")
     return (out, S, z) if want_state else out
 
 
@@ -152,4 +189,20 @@ def decode_step(state: torch.Tensor, z: torch.Tensor | None, q, k, v, normalise=
     rc = linattn_decode_step(state, z, q, k, v, out, B, H, Hkv, d, normalise, dtype_code(q.dtype, phi), stream)
     if rc != 0:
         raise LinattnError(rc, "linattn_decode_step")
+    return out
+
+
+def decode_step_decay(state: torch.Tensor, z: torch.Tensor | None, q, k, v, g, normalise=True, out=None,
+                      stream=None):
+    """One step through ``linattn_decode_step_decay``: S and z fade by exp(g) [B,Hkv] (fp32,
+    device), then absorb (k, v) and are read by q; state and z are updated in place."""
+    B, H, d = q.shape
+    Hkv = k.shape[1]
+    if not (g.is_cuda and g.is_contiguous() and g.dtype == torch.float32 and g.shape == (B, Hkv)):
+        raise ValueError("g must be a contiguous fp32 device tensor [B, Hkv]")
+    if out is None:
+        out = torch.empty_like(q)
+    rc = linattn_decode_step_decay(state, z, q, k, v, g, out, B, H, Hkv, d, normalise, dtype_code(q.dtype), stream)
+    if rc != 0:
+        raise LinattnError(rc, "linattn_decode_step_decay")
     return out

@@ -172,7 +172,8 @@ def test_packed_argtypes_match_header():
     lib = la.load()
     for name in ("linattn_fwd", "linattn_fwd_from_state", "linattn_fwd_packed", "linattn_fwd_timed",
                  "linattn_bwd", "linattn_decode_step", "linattn_fwd_packed_workspace_bytes",
-                 "linattn_bwd_workspace_bytes", "linattn_fwd_workspace_bytes", "linattn_fwd_plan"):
+                 "linattn_bwd_workspace_bytes", "linattn_fwd_workspace_bytes", "linattn_fwd_plan",
+                 "linattn_fwd_decay", "linattn_fwd_decay_workspace_bytes", "linattn_decode_step_decay"):
         m = re.search(r"\b" + name + r"\(([^)]*)\);", hdr)
         assert m, name
         nparams = len([p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"])
@@ -186,3 +187,27 @@ def test_fp16_plans_like_bf16():
         assert la.linattn_fwd_workspace_bytes(*args, la.LINATTN_F16) == la.linattn_fwd_workspace_bytes(*args, la.LINATTN_BF16)
         assert la.linattn_bwd_workspace_bytes(*args, la.LINATTN_F16) == la.linattn_bwd_workspace_bytes(*args, la.LINATTN_BF16)
     assert la.linattn_fwd_plan(1, 2, 2, 16, 64, 1, 3)[0] == -3
+
+
+def test_decay_validation_without_gpu():
+    """linattn_fwd_decay / its workspace size: argument checks before any launch."""
+    f32, bf = la.LINATTN_F32, la.LINATTN_BF16
+    relu = f32 | (1 << 8)
+    assert la.linattn_fwd_decay_workspace_bytes(1, 2, 2, 64, 64, relu, 0) == -1     # feature map
+    assert la.linattn_fwd_decay_workspace_bytes(1, 2, 2, 4096, 64, f32, 128) == -1  # shifted fp32 copies
+    for args in [(2, 8, 8, 4096, 64), (1, 32, 8, 32768, 128), (2, 8, 8, 16384, 64), (3, 6, 2, 777, 32)]:
+        for dt in (f32, bf):
+            rc, c, P = la.linattn_fwd_plan(*args, 1, dt, 0)
+            plain = la.linattn_fwd_workspace_bytes(*args, 1, dt, 0)
+            B, H, Hkv = args[:3]
+            # one float more per segment partial (the segment's summed log-decay)
+            assert la.linattn_fwd_decay_workspace_bytes(*args, dt, 0) == plain + B * Hkv * (P - 1) * 4
+    assert la.linattn_fwd_decay(None, None, None, None, None, 0, 2, 2, 64, 64, 1, f32, stream=0) == 0
+    assert la.linattn_fwd_decay(16, 16, 16, None, 16, 1, 2, 2, 64, 64, 1, f32, stream=0) == -1
+    assert la.linattn_fwd_decay(16, 16, 16, 16, 16, 1, 2, 2, 64, 64, 1, relu, stream=0) == -4
+    need = la.linattn_fwd_decay_workspace_bytes(2, 8, 8, 4096, 64, f32, 0)
+    assert la.linattn_fwd_decay(16, 16, 16, 16, 16, 2, 8, 8, 4096, 64, 1, f32, workspace=16,
+                                workspace_bytes=need - 4, stream=0) == -5
+    assert la.linattn_fwd_decay(16, 16, 16, 18, 16, 1, 2, 2, 64, 64, 1, f32, stream=0) == -7  # g misaligned
+    assert la.linattn_decode_step_decay(16, 16, 16, 16, 16, None, 16, 1, 2, 2, 64, 1, f32, stream=0) == -1
+    assert la.linattn_decode_step_decay(16, 16, 16, 16, 16, 18, 16, 1, 2, 2, 64, 1, f32, stream=0) == -7
