@@ -472,6 +472,93 @@ def packed_row(la, hip, torch, steps):
             "roofline_path": roofline(nbytes, 0.0, ms / 1e3, P["dtype"], "whole packed forward (graph replay, events)")}
 
 
+def graph_ms(hip, torch, call, out, steps):
+    """ms per call of `call(stream)` replayed `steps` times from one HIP graph, and
+    whether the replayed output equals the eager call's bitwise."""
+    call(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream().cuda_stream
+        for _ in range(steps):
+            call(cap)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    g.replay()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(e0, e1) / steps
+    same = bool(torch.equal(out, ref))
+    del g
+    return ms, same
+
+
+def decay_row(la, hip, torch, steps):
+    """linattn_fwd_decay on the decayed workload (cfg3's shape with a per-token gate), K
+    calls in one HIP graph, beside the plain forward pass of the same inputs."""
+    from linattn_inputs import DECAY, make_decay, make_qkv
+
+    w = DECAY
+    q, k, v = (t.cuda() for t in make_qkv(w.B, w.H, w.Hkv, w.N, w.d, w.dtype, w.seed))
+    g = make_decay(w.B, w.Hkv, w.N, w.seed + 1).cuda()
+    dt = la.LINATTN_BF16 if w.dtype == "bf16" else la.LINATTN_F32
+    nb = la.linattn_fwd_decay_workspace_bytes(w.B, w.H, w.Hkv, w.N, w.d, dt, 0)
+    ws = torch.empty(nb // 4 + 1, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+
+    def call(st):
+        rc = la.linattn_fwd_decay(q, k, v, g, out, w.B, w.H, w.Hkv, w.N, w.d, 1, dt, None, None, None, None, 0, ws,
+                                  nb, st)
+        if rc != 0:
+            raise la.LinattnError(rc, "linattn_fwd_decay")
+
+    def plain(st):
+        rc = la.linattn_fwd(q, k, v, out, w.B, w.H, w.Hkv, w.N, w.d, 1, 1, dt, None, None, 0, ws, nb, st)
+        if rc != 0:
+            raise la.LinattnError(rc, "linattn_fwd")
+
+    ms_plain, _ = graph_ms(hip, torch, plain, out, steps)
+    ms, same = graph_ms(hip, torch, call, out, steps)
+    nbytes = fwd_bytes(w) + 4 * w.B * w.Hkv * w.N  # + the log-decays
+    return {"workload": w.name, "ms_per_step": round(ms, 5), "tokens_per_s": round(w.B * w.N / (ms / 1e3), 1),
+            "graph_matches_eager": same, "plain_forward_ms": round(ms_plain, 5),
+            "roofline_path": roofline(nbytes, 0.0, ms / 1e3, w.dtype, "whole decayed forward (graph replay, events)")}
+
+
+def decay_oracle(seconds, max_tokens=2048):
+    """The fp64 oracle's decayed recurrence on the first tokens of every sequence of the
+    decayed workload (the cost per token does not depend on the position)."""
+    import numpy as np
+
+    import oracle
+    from linattn_inputs import DECAY, make_decay, make_qkv
+
+    w = DECAY
+    n = min(w.N, max_tokens)
+    q, k, v = (np.ascontiguousarray(t[:, :, :n].double().numpy())
+               for t in make_qkv(w.B, w.H, w.Hkv, w.N, w.d, w.dtype, w.seed))
+    g = np.ascontiguousarray(make_decay(w.B, w.Hkv, w.N, w.seed + 1)[:, :, :n].double().numpy())
+    threads = oracle.default_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.ref_fwd_decay(q, k, v, g, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    return {"value": round(w.B * n * reps / el, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {w.N} tokens of all {w.B * w.Hkv} sequences, {reps} reps in {el:.1f} s"}
+
+
 def packed_oracle(seconds):
     """The fp64 oracle on the first sequences of the packed batch, one after another."""
     import oracle
@@ -680,6 +767,10 @@ def main():
             log(name, json.dumps(rows[name]))
         rows["cfg5_prefill_4_pieces"] = pieces_row(la, hip, torch, WORKLOADS["cfg5"], 4, 20)
         log("cfg5_prefill_4_pieces", json.dumps(rows["cfg5_prefill_4_pieces"]))
+        rows["decay"] = decay_row(la, hip, torch, 20)
+        if args.cpu_seconds > 0:
+            rows["decay"]["cpu_oracle"] = decay_oracle(min(2.0, args.cpu_seconds))
+        log("decay", json.dumps(rows["decay"]))
         rows["packed"] = packed_row(la, hip, torch, 20)
         if args.cpu_seconds > 0:
             rows["packed"]["cpu_oracle"] = packed_oracle(min(2.0, args.cpu_seconds))
