@@ -2,7 +2,10 @@
 # Regenerates the rocprofv3 summaries kept under profiles/ (run from the
 # repository root on a machine with the GPU; raw output goes to $1).
 #
-#   bash sequence_mixing_amd/profile.sh <raw-output-dir>
+#   bash sequence_mixing_amd/profile.sh <raw-output-dir> [summaries]
+#
+# With "summaries" only the text summaries are written again from the raw
+# output already in the directory (no GPU needed).
 #
 # 1. kernel trace + stats of the default bench run (every workload row) and
 #    of the headline workload alone;
@@ -22,11 +25,14 @@ KR="k_causal_chunks|k_seg_totals|k_seg_scan|k_noncausal_apply"
 
 step() { echo "== $*"; }
 
-step "trace: default bench"
 C1="rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace_all -o run -- python3 bench.py --cpu-seconds 2"
+C2="rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace_cfg2 -o run -- python3 bench.py --rows 0 --cpu-seconds 0"
+CTRS="MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT"
+C3="rocprofv3 --pmc $CTRS --kernel-include-regex '$KR|k_decode_step|k_bwd' -f csv -d $OUT/counters_all -o run -- python3 bench.py --rows 1 --steps 5 --warmup 2 --cpu-seconds 0"
+if [ "${2:-}" != "summaries" ]; then
+step "trace: default bench"
 timeout -k 10 600 $C1 > "$OUT/trace_all.json" 2> "$OUT/trace_all.err"
 step "trace: headline workload"
-C2="rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace_cfg2 -o run -- python3 bench.py --rows 0 --cpu-seconds 0"
 timeout -k 10 300 $C2 > "$OUT/trace_cfg2.json" 2> "$OUT/trace_cfg2.err"
 for ctr in FETCH_SIZE WRITE_SIZE; do
     step "$ctr: headline workload"
@@ -43,11 +49,10 @@ for ctr in FETCH_SIZE WRITE_SIZE; do
         python3 -m sequence_mixing_amd.calib_copy 256 > "$OUT/${ctr}_copy.out" 2>&1
 done
 
-CTRS="MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT"
-C3="rocprofv3 --pmc $CTRS --kernel-include-regex '$KR|k_decode_step|k_bwd' -f csv -d $OUT/counters_all -o run -- python3 bench.py --rows 1 --steps 5 --warmup 2 --cpu-seconds 0"
 step "counters: every workload"
 timeout -s KILL 500 rocprofv3 --pmc $CTRS --kernel-include-regex "$KR|k_decode_step|k_bwd" -f csv -d $OUT/counters_all -o run -- \
     python3 bench.py --rows 1 --steps 5 --warmup 2 --cpu-seconds 0 > "$OUT/counters_all.out" 2>&1
+fi
 
 PMC="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --kernel-include-regex '<kernels>' -f csv -- python3 bench.py --steps 5 --warmup 2 --cpu-seconds 0 (--rows 0 headline, --causal 0 --rows 0 non-causal, --rows 1 decode); calibration: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 -m sequence_mixing_amd.calib_copy 256"
 python3 -m sequence_mixing_amd.profsum "$OUT/trace_all/run_kernel_stats.csv" "$C1" \
@@ -66,5 +71,5 @@ python3 -m sequence_mixing_amd.profsum counters "$OUT/counters_all/run_counter_c
 python3 -m sequence_mixing_amd.profsum traffic decode "$OUT/FETCH_SIZE_decode/run_counter_collection.csv" \
     "$OUT/WRITE_SIZE_decode/run_counter_collection.csv" "$OUT/FETCH_SIZE_copy/run_counter_collection.csv" \
     "$OUT/WRITE_SIZE_copy/run_counter_collection.csv" 256 "$PMC" $SRC > "$OUT/traffic_decode_bf16_B64H32Hkv8d128.txt"
-grep -h "^headline\|^cfg" "$OUT/trace_all.err" > "$OUT/bench_rows_under_trace.txt" || true
+grep -h "^headline\|^cfg\|^decay\|^packed" "$OUT/trace_all.err" > "$OUT/bench_rows_under_trace.txt" || true
 step "done"

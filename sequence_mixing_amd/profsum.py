@@ -54,12 +54,12 @@ def kernel_key(name: str) -> str:
     rest = name[n0 + int(m.group(1)):]
     if not rest.startswith("I"):
         return kname
-    m = re.match(r"(.*)", rest[1:])
+    # the template arguments end where the (void) kernel's parameter list begins
+    m = re.search(r"Ev[PKfi]", rest)
+    region = rest[1:m.start()] if m else rest[1:]
     args = []
     toks = {"DF16b": "bf16", "DF16_": "f16", "f": "float", "d": "double", "i": "int"}
-    for tok in re.findall(r"Li-?\d+E|Lb[01]E|Phi\w+?E|DF16b|DF16_|NS_\d+FmtI|EE|[fdi]", m.group(1)):
-        if tok == "EE":
-            break  # end of the template arguments (what follows is the parameter list)
+    for tok in re.findall(r"Li-?\d+E|Lb[01]E|Phi\w+?E|DF16b|DF16_|NS_\d+FmtI|[fdi]", region):
         if tok.startswith("NS_"):
             continue
         if tok.startswith("Li"):
