@@ -211,3 +211,11 @@ def test_decay_validation_without_gpu():
     assert la.linattn_fwd_decay(16, 16, 16, 18, 16, 1, 2, 2, 64, 64, 1, f32, stream=0) == -7  # g misaligned
     assert la.linattn_decode_step_decay(16, 16, 16, 16, 16, None, 16, 1, 2, 2, 64, 1, f32, stream=0) == -1
     assert la.linattn_decode_step_decay(16, 16, 16, 16, 16, 18, 16, 1, 2, 2, 64, 1, f32, stream=0) == -7
+
+
+def test_plan_size_limits():
+    """One head's q past 2 GiB is rejected; just below it plans (with fewer heads per block)."""
+    bf = la.LINATTN_BF16
+    assert la.linattn_fwd_plan(1, 1, 1, 1 << 23, 128, 1, bf, 0)[0] == -2
+    assert la.linattn_fwd_plan(1, 4, 1, (1 << 21) + 1000, 128, 1, bf, 0)[0] == 0
+    assert la.linattn_fwd_plan(1, 1, 1, (1 << 23) - 16, 128, 1, bf, 0)[0] == 0

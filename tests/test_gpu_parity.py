@@ -462,3 +462,33 @@ def test_fp16_decode_step():
     assert out.dtype == torch.float16
     assert rows_rel_err(host(out), ref) <= TOL["f16"]
     assert mat_rel_err(host(S), Sr) <= 1e-5
+
+
+# ------------------------------------------------------------- maximum size
+
+def test_head_block_past_two_gib():
+    """bf16, G = 4, d = 128, N just over 2^21: four query heads of q span more than
+    2 GiB, so the plan halves the heads per workgroup (32-bit offsets inside a block).
+    With k = 0 (phi(k) = 1) every normalised row is the prefix mean of v whatever q is,
+    a property that holds at any size; sampled rows (incl. the block's last ones, past
+    the 1 GiB and 2 GiB offsets) are checked against it in fp64 on the host."""
+    B, H, Hkv, d = 1, 4, 1, 128
+    N = (1 << 21) + 1000
+    assert H * N * d * 2 > 2**31 - 1
+    print(f"max-size case B{B} H{H} Hkv{Hkv} N{N} d{d} bf16", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(4242)
+    q = torch.randn(B, H, N, d, generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn(B, Hkv, N, d, generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.zeros_like(v)
+    out = ops.fwd(q, k, v)
+    torch.cuda.synchronize()
+    vh = v[0, 0].double().cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(0, 64), np.linspace(0, N - 1, 200).astype(np.int64),
+                                     np.arange(N - 64, N)]))
+    csum = np.cumsum(vh, axis=0)
+    ref = csum[rows] / (rows + 1)[:, None]
+    del q
+    o = out[0][:, torch.from_numpy(rows).cuda()].double().cpu().numpy()  # [H, rows, d]
+    for h in range(H):
+        e = rows_rel_err(o[h], ref)
+        assert e <= TOL["bf16"], f"head {h}: {e:.3e}"
