@@ -94,7 +94,7 @@ class Hip:
         assert self.lib.hipEventRecord(e, stream) == 0
 
 
-SOURCES = ["sequence_mixing_amd/csrc/linattn.hip", "sequence_mixing_amd/csrc/linattn_kern.h",
+SOURCES = ["sequence_mixing_amd/csrc/linattn_fmt.hip", "sequence_mixing_amd/csrc/linattn_kern.h",
            "sequence_mixing_amd/csrc/linattn_plan.h", "sequence_mixing_amd/csrc/linattn_plan.cpp"]
 
 

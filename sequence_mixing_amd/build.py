@@ -22,8 +22,14 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]
-SOURCES = [os.path.join(CSRC, "linattn.hip"), os.path.join(CSRC, "linattn_bwd.hip"),
-           os.path.join(CSRC, "linattn_plan.cpp")]
+# (source, extra defines): the forward/decode kernels are built once per
+# (feature map, element type), so the objects compile in parallel.
+_PHIS = ["LINATTN_PHI_ELU1", "LINATTN_PHI_RELU", "LINATTN_PHI_SOFTPLUS"]
+_ELEMS = ["LINATTN_F32", "LINATTN_BF16", "LINATTN_F16"]
+SOURCES = [(os.path.join(CSRC, "linattn_fmt.hip"), [f"-DLINATTN_FMT_PHI={p}", f"-DLINATTN_FMT_ELEM={e}"])
+           for p in _PHIS for e in _ELEMS] + [
+    (os.path.join(CSRC, "linattn_bwd.hip"), []), (os.path.join(CSRC, "linattn.hip"), []),
+    (os.path.join(CSRC, "linattn_plan.cpp"), [])]
 
 
 def _run(cmd):
@@ -38,15 +44,16 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
     """Compiles every source to an object in parallel, then links the library."""
     from concurrent.futures import ThreadPoolExecutor
 
-    objs = [out + "." + os.path.basename(src) + ".o" for src in SOURCES]
-    cmds = [[HIPCC, *FLAGS, *(extra_flags or []), "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+    objs = [f"{out}.{i}.{os.path.basename(src)}.o" for i, (src, _) in enumerate(SOURCES)]
+    cmds = [[HIPCC, *FLAGS, *(extra_flags or []), *defs, "-c", src, "-o", obj]
+            for (src, defs), obj in zip(SOURCES, objs)]
     cmds = [[a for a in c if a != "-shared"] for c in cmds]
     if verbose:
         for c in cmds:
             print(" ".join(c), flush=True)
-    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
         results = list(ex.map(_run, cmds))
-    for (rc, err), src in zip(results, SOURCES):
+    for (rc, err), (src, _) in zip(results, SOURCES):
         if rc != 0:
             raise RuntimeError(f"hipcc failed on {os.path.basename(src)} ({rc}):\n{err}")
         if verbose and err.strip():

@@ -20,7 +20,7 @@ set -euo pipefail
 OUT=${1:?raw output directory}
 mkdir -p "$OUT"
 export TMPDIR=${TMPDIR:-/tmp}
-SRC="sequence_mixing_amd/csrc/linattn.hip sequence_mixing_amd/csrc/linattn_kern.h sequence_mixing_amd/csrc/linattn_plan.h sequence_mixing_amd/csrc/linattn_plan.cpp"
+SRC="sequence_mixing_amd/csrc/linattn_fmt.hip sequence_mixing_amd/csrc/linattn_kern.h sequence_mixing_amd/csrc/linattn_plan.h sequence_mixing_amd/csrc/linattn_plan.cpp"
 KR="k_causal_chunks|k_seg_totals|k_seg_scan|k_noncausal_apply"
 
 step() { echo "== $*"; }
