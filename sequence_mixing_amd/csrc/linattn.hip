@@ -126,7 +126,7 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, int B, int 
     pl.cu = cu;
     if (N > 0 && (!q || !k || !v || !out)) return LINATTN_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(state_out) ||
-        !aligned16(z_out) || !aligned16(workspace) || ((uintptr_t)s0.g & 3u))
+        !aligned16(z_out) || !aligned16(workspace) || !aligned16(s0.S) || !aligned16(s0.z) || ((uintptr_t)s0.g & 3u))
         return LINATTN_ERR_ALIGN;
     if (need > 0 && (!workspace || workspace_bytes < need)) return LINATTN_ERR_WORKSPACE;
     if (N == 0) {

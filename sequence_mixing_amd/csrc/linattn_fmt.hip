@@ -93,6 +93,7 @@ struct Main {
     static constexpr int RPC = SHIFT ? 1 : CT / NSC;
     static constexpr bool FITS = SH.fits;
     static constexpr int OCC = SH.occ;
+    static constexpr bool PIPE = SH.pipe;            // compute on waves 0 .. NW/2-1, staging on the rest
     static_assert(SH.lk == LK && SH.lq == LQ, "staging shape");
     static_assert(!SHIFT || (sizeof(T) == 4 && NSC == CT - 1), "shifted copies");
     static_assert(DT % PARTS == 0 && (PARTS == 1 || NWI <= NW), "phase-2 split");
@@ -117,14 +118,18 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
     constexpr int U = M::U, CT = M::CT, DT = M::DT, KBD = M::KBD, GPR = M::GPR, NSC = M::NSC, RPC = M::RPC;
     constexpr int NW = M::NW, TH = M::TH;
 
-    __shared__ __attribute__((aligned(16))) T smK[C * D];
-    __shared__ __attribute__((aligned(16))) T smV[C * D];
-    __shared__ __attribute__((aligned(16))) T smQ[GT * C * D];
+    // PIPE: K, V and q double-buffered (staging waves fill one buffer while
+    // the compute waves work on the other)
+    constexpr bool PIPE = M::PIPE && !DK;
+    constexpr int NB = PIPE ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) T smK[NB][C * D];
+    __shared__ __attribute__((aligned(16))) T smV[NB][C * D];
+    __shared__ __attribute__((aligned(16))) T smQ[NB][GT * C * D];
     __shared__ __attribute__((aligned(16))) T smST[NSC][D * D];
     __shared__ __attribute__((aligned(16))) T smZ[NSC][D];
     __shared__ __attribute__((aligned(16))) DecayTab<C> smDT;  // DK only
     static_assert(!(DK && M::SHIFT), "decayed sums need one state copy per key tile or pair");
-    const Tile<T, D> sK{smK}, sV{smV}, sQ{smQ};
+    const Tile<T, D> sQ{smQ[0]};
 
     const int HB = G / GT;
     // Dense batch: blocks run over (sequence, head block, segment).  Packed
@@ -209,8 +214,9 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
     const int qspan = GT * N * D;  // elements of the head block's q (and out)
     // Loads chunk [t0, t0 + C) of K, V and q; nothing (zeros) when the chunk
     // lies past the segment (t0 >= s1), zeros for tokens past N.
-    auto load_all = [&](Regs &r, int t0) {
-        const int rows = t0 < s1 ? min(C, N - t0) : 0;
+    auto rows_at = [&](int t0) { return t0 < s1 ? min(C, N - t0) : 0; };
+    auto load_kv = [&](Regs &r, int t0) {
+        const int rows = rows_at(t0);
         const Rsrc rk = make_rsrc(kb + (size_t)t0 * D, rows * D * E);
         const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, rows * D * E);
 #pragma unroll
@@ -219,10 +225,17 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
             r.k[l] = buf_load16<g16>(rk, off);
             r.v[l] = buf_load16<g16>(rv, off);
         }
+    };
+    auto load_q = [&](Regs &r, int t0) {
+        const int rows = rows_at(t0);
         const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, rows ? (qspan - t0 * D) * E : 0);
 #pragma unroll
         for (int l = 0; l < M::LQ; ++l) r.q[l] = buf_load16<g16>(rq, qt[l] < rows ? qoff[l] : kOutOfRange);
-        if constexpr (DK) r.g = tid < rows ? gb[t0 + tid] : 0.f;
+    };
+    auto load_all = [&](Regs &r, int t0) {
+        load_kv(r, t0);
+        load_q(r, t0);
+        if constexpr (DK) r.g = tid < rows_at(t0) ? gb[t0 + tid] : 0.f;
     };
     // The output parked in the q rows: read into registers before phi(q) of
     // the next chunk overwrites them, stored after the next loads are issued
@@ -232,7 +245,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         for (int l = 0; l < M::LQ; ++l) {
             const int e = tid + l * TH;
             const int row = (M::QG % TH == 0 || e < M::QG) ? e / GPR : 0, qq = e % GPR;
-            o[l] = *reinterpret_cast<const g16 *>(smQ + sQ.at(row, qq * U));
+            o[l] = *reinterpret_cast<const g16 *>(sQ.p + sQ.at(row, qq * U));
         }
     };
     auto store_out = [&](const g16 (&o)[M::LQ], int t_prev) {
@@ -256,41 +269,21 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         }
     };
 
-    // ---- prologue: chunk 0 staged, chunk 1 in flight
-    load_all(ra, s0);
-    stage_rows<T, D, C, TH, IO>(ra.k, ra.v, sK, sV, min(C, N - s0), tid);
-    stage_q(ra);
-    if constexpr (DK) decay_stage<C>(smDT, ra.g, tid);
-    load_all(ra, s0 + C);
-    lds_barrier();
-
     const bool carry_out = p == np - 1 && (state_out || z_out);
-    for (int c = 0; c < nch; ++c) {
-        const int t0 = s0 + c * C;
-        // Key tiles holding tokens < N; tiles past them add nothing and no
-        // query reads a copy published there.  In the last chunk of a
-        // segment the state after the last published copy is needed only
-        // when it is returned to the caller.
-        const int kt_valid = min(CT, (N - t0 + 31) / 32);
-        const int kt_upd = (c + 1 < nch || carry_out) ? kt_valid
-                                                      : min(kt_valid, M::SHIFT ? CT - 1 : RPC * (NSC - 1));
-
-        // ---- with output columns split over waves (one item per wave), the
-        // item's phi(q) fragments are read now: the barrier after phase 1
-        // then orders every such read before any part parks output there.
-        const int u_split = w / M::PARTS;
-        const bool has_split = M::PARTS > 1 && w < M::NWI && t0 + (u_split % CT) * 32 < N;
-        v8 qf_split[KBD];
-        if constexpr (M::PARTS > 1) {
-            if (has_split) {
-                const int qrow = (u_split / CT) * C + (u_split % CT) * 32 + n;
-#pragma unroll
-                for (int kq = 0; kq < KBD; ++kq) qf_split[kq] = sQ.read8(qrow, kq * 16 + h * 8);
-            }
-        }
-
-        // ---- phase 1: publish the state before every RPC-th key tile (after
-        // each of tiles 0 .. CT-2 with shifted copies), absorb each tile
+    // Key tiles of the chunk at t0 holding tokens < N; tiles past them add
+    // nothing and no query reads a copy published there.  In the last chunk
+    // of a segment the state after the last published copy is needed only
+    // when it is returned to the caller.
+    auto kt_valid_of = [&](int t0) { return min(CT, (N - t0 + 31) / 32); };
+    auto kt_upd_of = [&](int c, int t0) {
+        const int kv = kt_valid_of(t0);
+        return (c + 1 < nch || carry_out) ? kv : min(kv, M::SHIFT ? CT - 1 : RPC * (NSC - 1));
+    };
+    // ---- phase 1 of chunk c (tokens from t0): every state tile's owner
+    // publishes the state before every RPC-th key tile (after each of tiles
+    // 0 .. CT-2 with shifted copies) and absorbs each tile of sK, sV.
+    auto phase1 = [&](int c, int t0, Tile<T, D> sK, Tile<T, D> sV) {
+        const int kt_valid = kt_valid_of(t0), kt_upd = kt_upd_of(c, t0);
 #pragma unroll
         for (int i = 0; i < M::MAXST; ++i) {
             const int st = M::tile_of(w, i);
@@ -328,184 +321,332 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                 if (zown) zr += zs;
             }
         }
-        lds_barrier();
+    };
 
-        // ---- phase 2: query tiles
-        // phi(q) fragments of unit u: lane (h, n) holds query n, features kq*16 + 8h + s.
-        auto unit_qf = [&](int u, v8 (&qf)[KBD]) {
-            const int qrow = (u / CT) * C + (u % CT) * 32 + n;
+    // ---- phase 2: query tiles
+    // phi(q) fragments of unit u: lane (h, n) holds query n, features kq*16 + 8h + s.
+    auto unit_qf = [&](int u, v8 (&qf)[KBD], Tile<T, D> sQ) {
+        const int qrow = (u / CT) * C + (u % CT) * 32 + n;
 #pragma unroll
-            for (int kq = 0; kq < KBD; ++kq) qf[kq] = sQ.read8(qrow, kq * 16 + h * 8);
+        for (int kq = 0; kq < KBD; ++kq) qf[kq] = sQ.read8(qrow, kq * 16 + h * 8);
+    };
+    // Output columns ct0 .. ct0 + CTP - 1 of unit u, parked in its q rows of
+    // sQ; the chunk's keys and values in sK, sV.
+    auto unit_run = [&](int u, int ct0, const v8 (&qf)[KBD], Tile<T, D> sK, Tile<T, D> sV, Tile<T, D> sQ) {
+        const int g = u / CT, r = u % CT;
+        // Shifted copies: tile r >= 1 reads copy r - 1 (keys before tile r);
+        // tile 0 reads copy 0 (keys of tile 0 included) and subtracts the
+        // keys of its diagonal tile that come after the query.
+        const int j = M::SHIFT ? (r > 0 ? r - 1 : 0) : r / RPC;
+        const bool sub = M::SHIFT && r == 0;
+        const bool off = r % RPC != 0;   // one unmasked key tile r-1 before the diagonal
+        const int qrow = g * C + r * 32 + n;
+        // DK: L of this query and of the 16 keys its lane holds (below),
+        // and the fade qs from the state copy to the query.
+        float lq = 0.f, qs = 1.f;
+        if constexpr (DK) {
+            lq = smDT.L[r * 32 + n];
+            qs = __builtin_amdgcn_exp2f((lq + (off ? smDT.TL[r - 1] : 0.f)) * kLog2e);
+        }
+        auto key_l = [&](int tile, float (&lk)[16]) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(&smDT.L[tile * 32 + 8 * q4 + 4 * h]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lk[4 * q4 + e] = x[e];
+            }
         };
-        // Output columns ct0 .. ct0 + CTP - 1 of unit u, parked in its q rows.
-        auto unit_run = [&](int u, int ct0, const v8 (&qf)[KBD]) {
-            const int g = u / CT, r = u % CT;
-            // Shifted copies: tile r >= 1 reads copy r - 1 (keys before tile r);
-            // tile 0 reads copy 0 (keys of tile 0 included) and subtracts the
-            // keys of its diagonal tile that come after the query.
-            const int j = M::SHIFT ? (r > 0 ? r - 1 : 0) : r / RPC;
-            const bool sub = M::SHIFT && r == 0;
-            const bool off = r % RPC != 0;   // one unmasked key tile r-1 before the diagonal
-            const int qrow = g * C + r * 32 + n;
-            // DK: L of this query and of the 16 keys its lane holds (below),
-            // and the fade qs from the state copy to the query.
-            float lq = 0.f, qs = 1.f;
+        // Pt[key][query] = phi(K) phi(Q)^T; accumulator reg i holds key
+        // 8(i/4) + 4h + i%4 of the tile for query n.
+        v8 pb0, pb1, po0 = v8{}, po1 = v8{};
+        {
+            f32x16 Pt = f32x16{};
+#pragma unroll
+            for (int kq = 0; kq < KBD; ++kq) mma(Pt, sK.read8(r * 32 + n, kq * 16 + h * 8), qf[kq]);
+            // Causal mask: accumulator reg i holds key 8(i/4) + 4h + i%4 of the
+            // tile for query n; keep keys <= n (or, subtracting, -Pt for keys > n).
+            const int kmax = n - 4 * h;
+            float pv[16];
             if constexpr (DK) {
-                lq = smDT.L[r * 32 + n];
-                qs = __builtin_amdgcn_exp2f((lq + (off ? smDT.TL[r - 1] : 0.f)) * kLog2e);
-            }
-            auto key_l = [&](int tile, float (&lk)[16]) {
+                // kept scores fade by exp(L[query] - L[key]) (<= 1)
+                float lk[16];
+                key_l(r, lk);
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const f32x4 x = *reinterpret_cast<const f32x4 *>(&smDT.L[tile * 32 + 8 * q4 + 4 * h]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) lk[4 * q4 + e] = x[e];
-                }
-            };
-            // Pt[key][query] = phi(K) phi(Q)^T; accumulator reg i holds key
-            // 8(i/4) + 4h + i%4 of the tile for query n.
-            v8 pb0, pb1, po0 = v8{}, po1 = v8{};
-            {
-                f32x16 Pt = f32x16{};
-#pragma unroll
-                for (int kq = 0; kq < KBD; ++kq) mma(Pt, sK.read8(r * 32 + n, kq * 16 + h * 8), qf[kq]);
-                // Causal mask: accumulator reg i holds key 8(i/4) + 4h + i%4 of the
-                // tile for query n; keep keys <= n (or, subtracting, -Pt for keys > n).
-                const int kmax = n - 4 * h;
-                float pv[16];
-                if constexpr (DK) {
-                    // kept scores fade by exp(L[query] - L[key]) (<= 1)
-                    float lk[16];
-                    key_l(r, lk);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const bool le = 8 * (i / 4) + (i % 4) <= kmax;
-                        pv[i] = le ? Pt[i] * __builtin_amdgcn_exp2f((lq - lk[i]) * kLog2e) : 0.f;
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const bool le = 8 * (i / 4) + (i % 4) <= kmax;
-                        pv[i] = sub ? (le ? 0.f : -Pt[i]) : (le ? Pt[i] : 0.f);
-                    }
-                }
-                pb0 = cvt8<T>(pv);
-                pb1 = cvt8<T>(pv + 8);
-            }
-            if (off) {
-                f32x16 Po = f32x16{};
-#pragma unroll
-                for (int kq = 0; kq < KBD; ++kq) mma(Po, sK.read8(r * 32 - 32 + n, kq * 16 + h * 8), qf[kq]);
-                float ov[16];
-                if constexpr (DK) {
-                    // keys of the tile before: exp(L[query] + TL[r-1] - L[key])
-                    float lk[16];
-                    key_l(r - 1, lk);
-                    const float lt = lq + smDT.TL[r - 1];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) ov[i] = Po[i] * __builtin_amdgcn_exp2f((lt - lk[i]) * kLog2e);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) ov[i] = Po[i];
-                }
-                po0 = cvt8<T>(ov);
-                po1 = cvt8<T>(ov + 8);
-            }
-            float den;
-            if constexpr (BF) {
-                // den = 1^T (masked Pt) + 1^T Po + z_j . phi(q), on the matrix core:
-                // every row of the product equals the denominator of query n.
-                f32x16 Dn = f32x16{};
-                mma(Dn, ones8<T>(), pb0);
-                mma(Dn, ones8<T>(), pb1);
-                if (off) {
-                    mma(Dn, ones8<T>(), po0);
-                    mma(Dn, ones8<T>(), po1);
-                }
-                if constexpr (DK) {
-                    // the copy's z fades by qs: its own accumulator
-                    f32x16 Dz = f32x16{};
-#pragma unroll
-                    for (int kq = 0; kq < KBD; ++kq)
-                        mma(Dz, *reinterpret_cast<const v8 *>(&smZ[j][kq * 16 + h * 8]), qf[kq]);
-                    den = Dn[0] + qs * Dz[0];
-                } else {
-#pragma unroll
-                    for (int kq = 0; kq < KBD; ++kq)
-                        mma(Dn, *reinterpret_cast<const v8 *>(&smZ[j][kq * 16 + h * 8]), qf[kq]);
-                    den = Dn[0];
+                for (int i = 0; i < 16; ++i) {
+                    const bool le = 8 * (i / 4) + (i % 4) <= kmax;
+                    pv[i] = le ? Pt[i] * __builtin_amdgcn_exp2f((lq - lk[i]) * kLog2e) : 0.f;
                 }
             } else {
-                float ds = 0.f;
 #pragma unroll
-                for (int s = 0; s < 8; ++s) ds += (float)pb0[s] + (float)pb1[s] + (float)po0[s] + (float)po1[s];
-                float dzs = 0.f;
+                for (int i = 0; i < 16; ++i) {
+                    const bool le = 8 * (i / 4) + (i % 4) <= kmax;
+                    pv[i] = sub ? (le ? 0.f : -Pt[i]) : (le ? Pt[i] : 0.f);
+                }
+            }
+            pb0 = cvt8<T>(pv);
+            pb1 = cvt8<T>(pv + 8);
+        }
+        if (off) {
+            f32x16 Po = f32x16{};
+#pragma unroll
+            for (int kq = 0; kq < KBD; ++kq) mma(Po, sK.read8(r * 32 - 32 + n, kq * 16 + h * 8), qf[kq]);
+            float ov[16];
+            if constexpr (DK) {
+                // keys of the tile before: exp(L[query] + TL[r-1] - L[key])
+                float lk[16];
+                key_l(r - 1, lk);
+                const float lt = lq + smDT.TL[r - 1];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) ov[i] = Po[i] * __builtin_amdgcn_exp2f((lt - lk[i]) * kLog2e);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) ov[i] = Po[i];
+            }
+            po0 = cvt8<T>(ov);
+            po1 = cvt8<T>(ov + 8);
+        }
+        float den;
+        if constexpr (BF) {
+            // den = 1^T (masked Pt) + 1^T Po + z_j . phi(q), on the matrix core:
+            // every row of the product equals the denominator of query n.
+            f32x16 Dn = f32x16{};
+            mma(Dn, ones8<T>(), pb0);
+            mma(Dn, ones8<T>(), pb1);
+            if (off) {
+                mma(Dn, ones8<T>(), po0);
+                mma(Dn, ones8<T>(), po1);
+            }
+            if constexpr (DK) {
+                // the copy's z fades by qs: its own accumulator
+                f32x16 Dz = f32x16{};
 #pragma unroll
                 for (int kq = 0; kq < KBD; ++kq)
+                    mma(Dz, *reinterpret_cast<const v8 *>(&smZ[j][kq * 16 + h * 8]), qf[kq]);
+                den = Dn[0] + qs * Dz[0];
+            } else {
 #pragma unroll
-                    for (int s = 0; s < 8; ++s) (DK ? dzs : ds) += (float)qf[kq][s] * (float)smZ[j][kq * 16 + h * 8 + s];
-                if constexpr (DK) ds += qs * dzs;
-                den = ds + __shfl_xor(ds, 32);
-            }
-            const float inv = normalise ? 1.f / den : 1.f;
-            const Tile<T, D> sST{smST[j]};
-#pragma unroll
-            for (int ct = ct0; ct < ct0 + M::CTP; ++ct) {
-                // O^T[feature][query] = V^T Pt (slot s of K-block kb2 holds key
-                // 16 kb2 + 8 (s/4) + 4h + s%4) + V^T Po + S_j^T phi(Q)^T.
-                f32x16 O = f32x16{};
-                if constexpr (DK) {
-                    // the copy's part first, faded by qs, then the keys of the chunk
-#pragma unroll
-                    for (int kq = 0; kq < KBD; ++kq) mma(O, sST.read8(ct * 32 + n, kq * 16 + h * 8), qf[kq]);
-                    O *= qs;
-                }
-                mma(O, colfrag(sV, r * 32 + 4 * h, r * 32 + 8 + 4 * h, ct * 32, lane), pb0);
-                mma(O, colfrag(sV, r * 32 + 16 + 4 * h, r * 32 + 24 + 4 * h, ct * 32, lane), pb1);
-                if (off) {
-                    mma(O, colfrag(sV, r * 32 - 32 + 4 * h, r * 32 - 24 + 4 * h, ct * 32, lane), po0);
-                    mma(O, colfrag(sV, r * 32 - 16 + 4 * h, r * 32 - 8 + 4 * h, ct * 32, lane), po1);
-                }
-                if constexpr (!DK) {
-#pragma unroll
-                    for (int kq = 0; kq < KBD; ++kq) mma(O, sST.read8(ct * 32 + n, kq * 16 + h * 8), qf[kq]);
-                }
-                // Park O in this unit's own q rows (every reader of them has read its phi(q)).
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    f32x4 x{O[4 * q4] * inv, O[4 * q4 + 1] * inv, O[4 * q4 + 2] * inv, O[4 * q4 + 3] * inv};
-                    sQ.write4(qrow, ct * 32 + 8 * q4 + 4 * h, out4<T, IO>(x));
-                }
-            }
-        };
-        if constexpr (M::PARTS == 1) {
-            for (int u = w; u < M::NU; u += NW) {
-                if (t0 + (u % CT) * 32 >= N) continue;  // tile entirely past the end
-                v8 qf[KBD];
-                unit_qf(u, qf);
-                unit_run(u, 0, qf);
+                for (int kq = 0; kq < KBD; ++kq)
+                    mma(Dn, *reinterpret_cast<const v8 *>(&smZ[j][kq * 16 + h * 8]), qf[kq]);
+                den = Dn[0];
             }
         } else {
-            if (has_split) unit_run(u_split, (w % M::PARTS) * M::CTP, qf_split);
+            float ds = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) ds += (float)pb0[s] + (float)pb1[s] + (float)po0[s] + (float)po1[s];
+            float dzs = 0.f;
+#pragma unroll
+            for (int kq = 0; kq < KBD; ++kq)
+#pragma unroll
+                for (int s = 0; s < 8; ++s) (DK ? dzs : ds) += (float)qf[kq][s] * (float)smZ[j][kq * 16 + h * 8 + s];
+            if constexpr (DK) ds += qs * dzs;
+            den = ds + __shfl_xor(ds, 32);
         }
+        const float inv = normalise ? 1.f / den : 1.f;
+        const Tile<T, D> sST{smST[j]};
+#pragma unroll
+        for (int ct = ct0; ct < ct0 + M::CTP; ++ct) {
+            // O^T[feature][query] = V^T Pt (slot s of K-block kb2 holds key
+            // 16 kb2 + 8 (s/4) + 4h + s%4) + V^T Po + S_j^T phi(Q)^T.
+            f32x16 O = f32x16{};
+            if constexpr (DK) {
+                // the copy's part first, faded by qs, then the keys of the chunk
+#pragma unroll
+                for (int kq = 0; kq < KBD; ++kq) mma(O, sST.read8(ct * 32 + n, kq * 16 + h * 8), qf[kq]);
+                O *= qs;
+            }
+            mma(O, colfrag(sV, r * 32 + 4 * h, r * 32 + 8 + 4 * h, ct * 32, lane), pb0);
+            mma(O, colfrag(sV, r * 32 + 16 + 4 * h, r * 32 + 24 + 4 * h, ct * 32, lane), pb1);
+            if (off) {
+                mma(O, colfrag(sV, r * 32 - 32 + 4 * h, r * 32 - 24 + 4 * h, ct * 32, lane), po0);
+                mma(O, colfrag(sV, r * 32 - 16 + 4 * h, r * 32 - 8 + 4 * h, ct * 32, lane), po1);
+            }
+            if constexpr (!DK) {
+#pragma unroll
+                for (int kq = 0; kq < KBD; ++kq) mma(O, sST.read8(ct * 32 + n, kq * 16 + h * 8), qf[kq]);
+            }
+            // Park O in this unit's own q rows (every reader of them has read its phi(q)).
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                f32x4 x{O[4 * q4] * inv, O[4 * q4 + 1] * inv, O[4 * q4 + 2] * inv, O[4 * q4 + 3] * inv};
+                sQ.write4(qrow, ct * 32 + 8 * q4 + 4 * h, out4<T, IO>(x));
+            }
+        }
+    };
+
+    if constexpr (!PIPE) {
+        const Tile<T, D> sK{smK[0]}, sV{smV[0]};
+        // ---- prologue: chunk 0 staged, chunk 1 in flight
+        load_all(ra, s0);
+        stage_rows<T, D, C, TH, IO>(ra.k, ra.v, sK, sV, min(C, N - s0), tid);
+        stage_q(ra);
+        if constexpr (DK) decay_stage<C>(smDT, ra.g, tid);
+        load_all(ra, s0 + C);
         lds_barrier();
 
-        // ---- staging of the next chunk (and the stores of this one); the
-        // registers are refilled with the chunk after it
-        g16 o[M::LQ];
-        read_out(o);
-        if (c + 1 < nch) {
-            stage_rows<T, D, C, TH, IO>(ra.k, ra.v, sK, sV, min(C, N - t0 - C), tid);
-            stage_q(ra);
-            if constexpr (DK) decay_stage<C>(smDT, ra.g, tid);
-            load_all(ra, t0 + 2 * C);  // past the segment: no access
-            store_out(o, t0);
+        for (int c = 0; c < nch; ++c) {
+            const int t0 = s0 + c * C;
+            // ---- with output columns split over waves (one item per wave), the
+            // item's phi(q) fragments are read now: the barrier after phase 1
+            // then orders every such read before any part parks output there.
+            const int u_split = w / M::PARTS;
+            const bool has_split = M::PARTS > 1 && w < M::NWI && t0 + (u_split % CT) * 32 < N;
+            v8 qf_split[KBD];
+            if constexpr (M::PARTS > 1) {
+                if (has_split) {
+                    const int qrow = (u_split / CT) * C + (u_split % CT) * 32 + n;
+#pragma unroll
+                    for (int kq = 0; kq < KBD; ++kq) qf_split[kq] = sQ.read8(qrow, kq * 16 + h * 8);
+                }
+            }
+
+            phase1(c, t0, sK, sV);
             lds_barrier();
+
+            if constexpr (M::PARTS == 1) {
+                for (int u = w; u < M::NU; u += NW) {
+                    if (t0 + (u % CT) * 32 >= N) continue;  // tile entirely past the end
+                    v8 qf[KBD];
+                    unit_qf(u, qf, sQ);
+                    unit_run(u, 0, qf, sK, sV, sQ);
+                }
+            } else {
+                if (has_split) unit_run(u_split, (w % M::PARTS) * M::CTP, qf_split, sK, sV, sQ);
+            }
+            lds_barrier();
+
+            // ---- staging of the next chunk (and the stores of this one); the
+            // registers are refilled with the chunk after it
+            g16 o[M::LQ];
+            read_out(o);
+            if (c + 1 < nch) {
+                stage_rows<T, D, C, TH, IO>(ra.k, ra.v, sK, sV, min(C, N - t0 - C), tid);
+                stage_q(ra);
+                if constexpr (DK) decay_stage<C>(smDT, ra.g, tid);
+                load_all(ra, t0 + 2 * C);  // past the segment: no access
+                store_out(o, t0);
+                lds_barrier();
+            } else {
+                store_out(o, t0);
+            }
+        }
+    } else {
+        // Staging waves (fp32 shapes whose state tiles and phase-2 items all
+        // sit on the first half of the waves): waves 0 .. NC-1 only compute
+        // (phase 1, then phase 2 of chunk c, from buffer c & 1) while waves
+        // NC .. NW-1 stage chunk c+1 into the other buffer, store the outputs
+        // of chunk c-1 and keep chunk c+2 in flight.  Each role runs its own
+        // loop (one pair of barriers per chunk in both), so the staging
+        // registers are not live in the compute code.
+        constexpr int NC = NW / 2, PTH = TH - 64 * NC;
+        constexpr int LKP = (M::KVG + PTH - 1) / PTH, LQP = (M::QG + PTH - 1) / PTH;
+        if (__builtin_amdgcn_readfirstlane(w) >= NC) {
+            const int pt = tid - 64 * NC;
+            g16 pk[LKP], pv[LKP], pq[LQP];
+            unsigned pqoff[LQP];
+            int pqt[LQP];
+#pragma unroll
+            for (int l = 0; l < LQP; ++l) {
+                const int e = pt + l * PTH;
+                const int row = e / GPR, qq = e % GPR;
+                pqoff[l] = (unsigned)(((row / C) * N + row % C) * D + qq * U) * E;
+                pqt[l] = (M::QG % PTH == 0 || e < M::QG) ? row % C : C;
+            }
+            auto p_load = [&](int t0) {
+                const int rows = rows_at(t0);
+                const Rsrc rk = make_rsrc(kb + (size_t)t0 * D, rows * D * E);
+                const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, rows * D * E);
+#pragma unroll
+                for (int l = 0; l < LKP; ++l) {
+                    const unsigned off = (unsigned)(pt + l * PTH) * 16u;
+                    pk[l] = buf_load16<g16>(rk, off);
+                    pv[l] = buf_load16<g16>(rv, off);
+                }
+                const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, rows ? (qspan - t0 * D) * E : 0);
+#pragma unroll
+                for (int l = 0; l < LQP; ++l) pq[l] = buf_load16<g16>(rq, pqt[l] < rows ? pqoff[l] : kOutOfRange);
+            };
+            auto p_stage_kv = [&](int b, int rows) {
+                stage_rows<T, D, C, PTH, IO>(pk, pv, Tile<T, D>{smK[b]}, Tile<T, D>{smV[b]}, rows, pt);
+            };
+            auto p_stage_q = [&](int b) {
+                const Tile<T, D> tq{smQ[b]};
+#pragma unroll
+                for (int l = 0; l < LQP; ++l) {
+                    const int e = pt + l * PTH;
+                    if (M::QG % PTH == 0 || e < M::QG) {
+                        g16 fq;
+#pragma unroll
+                        for (int i = 0; i < U; ++i) fq[i] = (T)IO::phi::f(Io<T, IO>::f(pq[l][i]));
+                        tq.write16(e / GPR, (e % GPR) * U, fq);
+                    }
+                }
+            };
+            // the outputs parked in the q rows of buffer b, stored as rows of chunk t_prev
+            auto p_out = [&](int b, int t_prev) {
+                const Tile<T, D> tq{smQ[b]};
+                g16 o[LQP];
+#pragma unroll
+                for (int l = 0; l < LQP; ++l) {
+                    const int e = pt + l * PTH;
+                    const int row = (M::QG % PTH == 0 || e < M::QG) ? e / GPR : 0;
+                    o[l] = *reinterpret_cast<const g16 *>(tq.p + tq.at(row, (e % GPR) * U));
+                }
+                const int rows = min(C, N - t_prev);
+                const Rsrc ro = make_rsrc(ob + (size_t)t_prev * D, (qspan - t_prev * D) * E);
+#pragma unroll
+                for (int l = 0; l < LQP; ++l) buf_store16<g16>(ro, pqt[l] < rows ? pqoff[l] : kOutOfRange, o[l]);
+            };
+            // ---- prologue: chunk 0 staged into buffer 0, chunk 1 requested
+            p_load(s0);
+            p_stage_kv(0, min(C, N - s0));
+            p_stage_q(0);
+            p_load(s0 + C);
+            lds_barrier();
+            for (int c = 0; c < nch; ++c) {
+                const int t0 = s0 + c * C, nb = (c + 1) & 1;
+                // while the compute waves run phase 1 of chunk c: K, V of chunk c+1
+                if (c + 1 < nch) p_stage_kv(nb, min(C, N - t0 - C));
+                lds_barrier();
+                // while they run phase 2: the outputs of chunk c-1 (parked in
+                // buffer nb) out, phi(q) of chunk c+1 in, chunk c+2 requested
+                if (c >= 1) p_out(nb, t0 - C);
+                if (c + 1 < nch) {
+                    p_stage_q(nb);
+                    p_load(t0 + 2 * C);  // past the segment: no access
+                }
+                lds_barrier();
+            }
+            if (nch > 0) p_out((nch - 1) & 1, s0 + (nch - 1) * C);
         } else {
-            store_out(o, t0);
+            lds_barrier();  // chunk 0 staged
+            for (int c = 0; c < nch; ++c) {
+                const int t0 = s0 + c * C, b = c & 1;
+                const Tile<T, D> tk{smK[b]}, tv{smV[b]}, tq{smQ[b]};
+                // with output columns split over waves, an item's phi(q)
+                // fragments are read before the barrier after phase 1 (no part
+                // parks output in the rows before then)
+                const int u_split = w / M::PARTS;
+                const bool has_split = M::PARTS > 1 && w < M::NWI && t0 + (u_split % CT) * 32 < N;
+                v8 qf_split[KBD];
+                if constexpr (M::PARTS > 1) {
+                    if (has_split) unit_qf(u_split, qf_split, tq);
+                }
+                phase1(c, t0, tk, tv);
+                lds_barrier();
+                if constexpr (M::PARTS == 1) {
+                    for (int u = w; u < M::NU; u += NC) {
+                        if (t0 + (u % CT) * 32 >= N) continue;  // tile entirely past the end
+                        v8 qf[KBD];
+                        unit_qf(u, qf, tq);
+                        unit_run(u, 0, qf, tk, tv, tq);
+                    }
+                } else {
+                    if (has_split) unit_run(u_split, (w % M::PARTS) * M::CTP, qf_split, tk, tv, tq);
+                }
+                lds_barrier();
+            }
         }
     }
-
     if (p == np - 1 && state_out) {
         float *so = state_out + (size_t)seq * D * D;
 #pragma unroll

@@ -26,6 +26,8 @@ struct MainShape {
     bool fits;    // buildable: LDS within 160 KiB, at most 8 q groups per thread of 4 waves
                   // (a register budget), at most 2 key tiles per copy
     unsigned long lds;
+    bool pipe;    // fp32, 8 waves: state tiles and phase-2 items on waves 0-3, which only compute;
+                  // waves 4-7 stage the next chunk meanwhile (K, V and q double-buffered)
 };
 
 constexpr unsigned long main_lds(int e, int D, int C, int GT, int nsc)
@@ -36,7 +38,7 @@ constexpr unsigned long main_lds(int e, int D, int C, int GT, int nsc)
 constexpr MainShape main_shape(int e, int D, int C, int GT)
 {
     const unsigned long half = 80 * 1024, full = 160 * 1024;
-    if (C < 32 || D < 32) return MainShape{1, 1, 4, 1, 1, false, false, 0};  // not a kernel shape
+    if (C < 32 || D < 32) return MainShape{1, 1, 4, 1, 1, false, false, 0, false};  // not a kernel shape
     const int ct = C / 32;
     const int u = 16 / e;
     const int lk4 = (C * (D / u) + 255) / 256;
@@ -63,7 +65,16 @@ constexpr MainShape main_shape(int e, int D, int C, int GT)
     const int th = 64 * nw;
     const int lk = (C * (D / u) + th - 1) / th;
     const int lq = (GT * C * (D / u) + th - 1) / th;
-    MainShape m{nsc, occ, nw, lk, lq, shift, lds <= full && lq4 <= 8 && (shift || ct / nsc <= 2), lds};
+    // Staging waves: every state tile and every phase-2 item (query tile,
+    // output-column part) on a wave of the first half of the workgroup, the
+    // second half staging; K, V and q double-buffered.
+    const int dt = D / 32, nu = GT * ct;
+    const int parts = nu >= nw ? 1 : (nw / nu < dt ? nw / nu : dt);
+    const unsigned long lds_pipe = (unsigned long)e * (4ul * C * D + 2ul * GT * C * D +
+                                                       (unsigned long)nsc * ((unsigned long)D * D + D));
+    const bool pipe = e == 4 && nw == 8 && !shift && dt * dt <= nw / 2 && nu * parts <= nw / 2 && lds_pipe <= full;
+    const unsigned long lds_used = pipe ? lds_pipe : lds;
+    MainShape m{nsc, occ, nw, lk, lq, shift, lds_used <= full && lq4 <= 8 && (shift || ct / nsc <= 2), lds_used, pipe};
     return m;
 }
 
