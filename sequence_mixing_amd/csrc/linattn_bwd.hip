@@ -727,12 +727,12 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
         if (P > 1 && launch_totals<T, D, IO>(c1, pl.nseq * (P - 1), st, kk, vv, wf, N, pl.seg_len, P - 1))
             return LINATTN_ERR_UNSUPPORTED;
         if (P > 2)
-            hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, wf,
+            hipLaunchKernelGGL(k_seg_scan, scan_grid(D, pl.nseq), dim3(kThreads), 0, st, wf,
                                P - 1, D, 0, (float *)nullptr, (float *)nullptr, (const float *)nullptr,
                                (const float *)nullptr);
     } else {
         if (launch_totals<T, D, IO>(c1, pl.nseq * P, st, kk, vv, wf, N, pl.seg_len, P)) return LINATTN_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, wf, P, D,
+        hipLaunchKernelGGL(k_seg_scan, scan_grid(D, pl.nseq), dim3(kThreads), 0, st, wf, P, D,
                            1, (float *)nullptr, (float *)nullptr, (const float *)nullptr, (const float *)nullptr);
     }
     // 2. dq (and den)
@@ -746,7 +746,7 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
                                oo, dd, (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P,
                                pl.seg_len, causal, normalise, P - 1, 1);
             if (P > 2)
-                hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st,
+                hipLaunchKernelGGL(k_seg_scan, scan_grid(D, pl.nseq), dim3(kThreads), 0, st,
                                    wr, P - 1, D, 2, (float *)nullptr, (float *)nullptr, (const float *)nullptr,
                                    (const float *)nullptr);
         }
@@ -754,7 +754,7 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
         hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D, DKV_WAVES(D, true)>::TH), 0, st, qq, kk, vv, oo, dd,
                            (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P, pl.seg_len,
                            causal, normalise, P, 0);
-        hipLaunchKernelGGL(k_seg_scan, dim3((E + kThreads - 1) / kThreads, pl.nseq), dim3(kThreads), 0, st, wr, P, D,
+        hipLaunchKernelGGL(k_seg_scan, scan_grid(D, pl.nseq), dim3(kThreads), 0, st, wr, P, D,
                            1, (float *)nullptr, (float *)nullptr, (const float *)nullptr, (const float *)nullptr);
     }
     // 4. dk, dv

@@ -916,7 +916,7 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
     T *oo = static_cast<T *>(out);
     const int P = pl.segments;  // packed: the segments the launches are sized for
     const int E = D * D + D;
-    const dim3 scan_grid((E + kThreads - 1) / kThreads, pl.nseq);
+    const dim3 sgrid = scan_grid(D, pl.nseq);
     Packed pk{nullptr, 0, 0};
     if (record(ev, 0, st)) return LINATTN_ERR_HIP;
     if (pl.packed) {
@@ -937,7 +937,7 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
         if (record(ev, 1, st)) return LINATTN_ERR_HIP;
         // the scan also adds the start sums of a continuation into every slot
         if (pl.packed || P > 2 || (P == 2 && (s0.S || s0.z)))
-            hipLaunchKernelGGL(k_seg_scan, scan_grid, dim3(kThreads), 0, st, ws, P - 1, D, 0, (float *)nullptr,
+            hipLaunchKernelGGL(k_seg_scan, sgrid, dim3(kThreads), 0, st, ws, P - 1, D, 0, (float *)nullptr,
                                (float *)nullptr, s0.S, s0.z, pk, pl.Hkv, (const float *)gs);
         if (record(ev, 2, st)) return LINATTN_ERR_HIP;
         const dim3 grid((pl.packed ? pl.Hkv : pl.nseq) * (pl.G / pl.gt) * P);
@@ -966,7 +966,7 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
                                 pl.Hkv, 0))
             return LINATTN_ERR_UNSUPPORTED;
         if (record(ev, 1, st)) return LINATTN_ERR_HIP;
-        hipLaunchKernelGGL(k_seg_scan, scan_grid, dim3(kThreads), 0, st, ws, P, D, 1, state_out, z_out, s0.S, s0.z, pk,
+        hipLaunchKernelGGL(k_seg_scan, sgrid, dim3(kThreads), 0, st, ws, P, D, 1, state_out, z_out, s0.S, s0.z, pk,
                            pl.Hkv);
         if (record(ev, 2, st)) return LINATTN_ERR_HIP;
         const int nblk = (pl.N + 127) / 128;

@@ -700,11 +700,15 @@ __global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, i
                                                        Packed pk = Packed{nullptr, 0, 0}, int Hkv = 1,
                                                        const float *__restrict__ gs = nullptr)
 {
+    // Four consecutive elements per thread (E is a multiple of 4), every
+    // access a 16-byte buffer access: slots past the sequence's last read
+    // zeros and take no stores, so no load or store sits behind a branch and
+    // a whole batch of slots is in flight at once.
     const int E = D * D + D;
     const int seq = blockIdx.y;
-    const int e = blockIdx.x * kThreads + threadIdx.x;
+    const int e = 4 * (int)(blockIdx.x * kThreads + threadIdx.x);
     if (e >= E) return;
-    float *base = ws + (size_t)seq * nslots * E + e;
+    size_t base = (size_t)seq * nslots * E;
     if (pk.tab) {
         const int b = seq / Hkv, gk = seq % Hkv, causal = mode != 1;
         SegLoc r;
@@ -712,30 +716,34 @@ __global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, i
         r.sb = pk.tab[b];
         r.np = pk.tab[b + 1] - r.sb;
         nslots = r.np - causal;
-        base = ws + packed_slot0(r, gk, Hkv, causal) * E + e;
+        base = packed_slot0(r, gk, Hkv, causal) * E;
     }
     // the sums start from the given ones (continuation), else from zero
-    float acc = 0.f;
+    f32x4 acc = f32x4{};
     if (e < D * D) {
-        if (s_in) acc = s_in[(size_t)seq * D * D + e];
+        if (s_in) acc = *reinterpret_cast<const f32x4 *>(s_in + (size_t)seq * D * D + e);
     } else if (z_in) {
-        acc = z_in[(size_t)seq * D + (e - D * D)];
+        acc = *reinterpret_cast<const f32x4 *>(z_in + (size_t)seq * D + (e - D * D));
     }
-    // Batches of independent loads, then the running sum over the batch.
+    const Rsrc rw = make_rsrc(ws + base, nslots > 0 ? nslots * E * 4 : 0);
+    // byte offset of the slot visited at step i: forwards for modes 0 and 1,
+    // backwards for mode 2 (steps past the last slot land out of range)
+    auto off = [&](int i) {
+        const int sl = mode == 2 ? nslots - 1 - i : i;
+        return sl >= 0 && sl < nslots ? (unsigned)(sl * E + e) * 4u : kOutOfRange;
+    };
     constexpr int BATCH = 32;
-    // slot visited at step i: forwards for modes 0 and 1, backwards for mode 2
-    auto slot = [&](int i) { return mode == 2 ? nslots - 1 - i : i; };
     for (int p0 = 0; p0 < nslots; p0 += BATCH) {
-        float x[BATCH];
+        f32x4 x[BATCH];
 #pragma unroll
-        for (int j = 0; j < BATCH; ++j) x[j] = p0 + j < nslots ? base[(size_t)slot(p0 + j) * E] : 0.f;
+        for (int j = 0; j < BATCH; ++j) x[j] = buf_load16<f32x4>(rw, off(p0 + j));
         if (gs) {
             const float *gq = gs + (size_t)seq * nslots;
 #pragma unroll
             for (int j = 0; j < BATCH; ++j) {
                 if (p0 + j < nslots) {
                     acc = __builtin_amdgcn_exp2f(gq[p0 + j] * kLog2e) * acc + x[j];
-                    base[(size_t)(p0 + j) * E] = acc;
+                    buf_store16<f32x4>(rw, off(p0 + j), acc);
                 }
             }
             continue;
@@ -743,17 +751,24 @@ __global__ __launch_bounds__(kThreads) void k_seg_scan(float *__restrict__ ws, i
 #pragma unroll
         for (int j = 0; j < BATCH; ++j) {
             acc += x[j];
-            if (mode != 1 && p0 + j < nslots) base[(size_t)slot(p0 + j) * E] = acc;
+            if (mode != 1) buf_store16<f32x4>(rw, off(p0 + j), acc);
         }
     }
     if (mode == 1) {
-        base[0] = acc;
+        buf_store16<f32x4>(rw, off(0), acc);
         if (e < D * D) {
-            if (state_out) state_out[(size_t)seq * D * D + e] = acc;
+            if (state_out) *reinterpret_cast<f32x4 *>(state_out + (size_t)seq * D * D + e) = acc;
         } else if (z_out) {
-            z_out[(size_t)seq * D + (e - D * D)] = acc;
+            *reinterpret_cast<f32x4 *>(z_out + (size_t)seq * D + (e - D * D)) = acc;
         }
     }
+}
+
+// Grid of k_seg_scan for head dimension d over nseq sequences.
+inline dim3 scan_grid(int d, int nseq)
+{
+    const int e4 = (d * d + d) / 4;
+    return dim3((e4 + kThreads - 1) / kThreads, nseq);
 }
 
 // ------------------------------------------------------ format dispatch
