@@ -83,9 +83,11 @@ struct Main {
     static constexpr int LK = (KVG + TH - 1) / TH;
     static constexpr int LQ = (QG + TH - 1) / TH;
     static constexpr int NU = GT * CT;               // units (query head, 32-row query tile) per chunk
-    // With fewer units than waves, a unit's output columns are split over
-    // PARTS waves (each recomputes the unit's scores and denominator).
-    static constexpr int PARTS = NU >= NW ? 1 : (NW / NU < DT ? NW / NU : DT);
+    // Waves that take phase-2 items: all, or the first half with staging waves.
+    static constexpr int NWC = SH.pipe ? NW / 2 : NW;
+    // With fewer units than those waves, a unit's output columns are split
+    // over PARTS waves (each recomputes the unit's scores and denominator).
+    static constexpr int PARTS = NU >= NWC ? 1 : (NWC / NU < DT ? NWC / NU : DT);
     static constexpr int NWI = NU * PARTS;           // phase-2 work items
     static constexpr int CTP = DT / PARTS;           // 32-column output tiles per item
     static constexpr int NSC = SH.nsc;
@@ -93,10 +95,10 @@ struct Main {
     static constexpr int RPC = SHIFT ? 1 : CT / NSC;
     static constexpr bool FITS = SH.fits;
     static constexpr int OCC = SH.occ;
-    static constexpr bool PIPE = SH.pipe;            // compute on waves 0 .. NW/2-1, staging on the rest
+    static constexpr bool PIPE = SH.pipe;            // phase-2 items on waves 0 .. NW/2-1, staging on the rest
     static_assert(SH.lk == LK && SH.lq == LQ, "staging shape");
     static_assert(!SHIFT || (sizeof(T) == 4 && NSC == CT - 1), "shifted copies");
-    static_assert(DT % PARTS == 0 && (PARTS == 1 || NWI <= NW), "phase-2 split");
+    static_assert(DT % PARTS == 0 && (PARTS == 1 || NWI <= NWC), "phase-2 split");
     static_assert(DT % MAXST == 0 || NST <= NW, "z owner: every column-0 state tile is some wave's first");
     __device__ static int tile_of(int w, int i) { return w * MAXST + i; }
 };
@@ -530,18 +532,24 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
             }
         }
     } else {
-        // Staging waves (fp32 shapes whose state tiles and phase-2 items all
-        // sit on the first half of the waves): waves 0 .. NC-1 only compute
-        // (phase 1, then phase 2 of chunk c, from buffer c & 1) while waves
-        // NC .. NW-1 stage chunk c+1 into the other buffer, store the outputs
-        // of chunk c-1 and keep chunk c+2 in flight.  Each role runs its own
-        // loop (one pair of barriers per chunk in both), so the staging
-        // registers are not live in the compute code.
-        constexpr int NC = NW / 2, PTH = TH - 64 * NC;
+        // Staging waves (MainShape::pipe): every wave runs phase 1 for its
+        // state tiles; waves 0 .. NC-1 then take the phase-2 items of chunk c
+        // (from buffer c & 1), while waves NC .. NW-1 stage chunk c+1 into
+        // the other buffer, store the outputs of chunk c-1 and keep chunk c+2
+        // in flight (16-bit rows: chunks c+2 and c+3, in two register sets;
+        // the fp32 shape measured slower with the second set).  Each role
+        // runs its own loop (one pair of barriers per chunk in both), so the
+        // staging registers are not live in the phase-2 code.
+        constexpr int NC = M::NWC, PTH = TH - 64 * NC;
         constexpr int LKP = (M::KVG + PTH - 1) / PTH, LQP = (M::QG + PTH - 1) / PTH;
         if (__builtin_amdgcn_readfirstlane(w) >= NC) {
             const int pt = tid - 64 * NC;
-            g16 pk[LKP], pv[LKP], pq[LQP];
+            struct PSet {
+                g16 k[LKP], v[LKP], q[LQP];
+            };
+            constexpr int NSET = sizeof(T) == 2 ? 2 : 1;  // register sets of chunks in flight
+            static_assert(NSET == 2 || M::NST <= NC * M::MAXST, "one set: the state tiles sit on the first half");
+            PSet sa, sb;  // two sets: sa holds the even chunks, sb the odd ones
             unsigned pqoff[LQP];
             int pqt[LQP];
 #pragma unroll
@@ -551,24 +559,24 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                 pqoff[l] = (unsigned)(((row / C) * N + row % C) * D + qq * U) * E;
                 pqt[l] = (M::QG % PTH == 0 || e < M::QG) ? row % C : C;
             }
-            auto p_load = [&](int t0) {
+            auto p_load = [&](PSet &r, int t0) {
                 const int rows = rows_at(t0);
                 const Rsrc rk = make_rsrc(kb + (size_t)t0 * D, rows * D * E);
                 const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, rows * D * E);
 #pragma unroll
                 for (int l = 0; l < LKP; ++l) {
                     const unsigned off = (unsigned)(pt + l * PTH) * 16u;
-                    pk[l] = buf_load16<g16>(rk, off);
-                    pv[l] = buf_load16<g16>(rv, off);
+                    r.k[l] = buf_load16<g16>(rk, off);
+                    r.v[l] = buf_load16<g16>(rv, off);
                 }
                 const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, rows ? (qspan - t0 * D) * E : 0);
 #pragma unroll
-                for (int l = 0; l < LQP; ++l) pq[l] = buf_load16<g16>(rq, pqt[l] < rows ? pqoff[l] : kOutOfRange);
+                for (int l = 0; l < LQP; ++l) r.q[l] = buf_load16<g16>(rq, pqt[l] < rows ? pqoff[l] : kOutOfRange);
             };
-            auto p_stage_kv = [&](int b, int rows) {
-                stage_rows<T, D, C, PTH, IO>(pk, pv, Tile<T, D>{smK[b]}, Tile<T, D>{smV[b]}, rows, pt);
+            auto p_stage_kv = [&](const PSet &r, int b, int rows) {
+                stage_rows<T, D, C, PTH, IO>(r.k, r.v, Tile<T, D>{smK[b]}, Tile<T, D>{smV[b]}, rows, pt);
             };
-            auto p_stage_q = [&](int b) {
+            auto p_stage_q = [&](const PSet &r, int b) {
                 const Tile<T, D> tq{smQ[b]};
 #pragma unroll
                 for (int l = 0; l < LQP; ++l) {
@@ -576,7 +584,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                     if (M::QG % PTH == 0 || e < M::QG) {
                         g16 fq;
 #pragma unroll
-                        for (int i = 0; i < U; ++i) fq[i] = (T)IO::phi::f(Io<T, IO>::f(pq[l][i]));
+                        for (int i = 0; i < U; ++i) fq[i] = (T)IO::phi::f(Io<T, IO>::f(r.q[l][i]));
                         tq.write16(e / GPR, (e % GPR) * U, fq);
                     }
                 }
@@ -596,25 +604,47 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
 #pragma unroll
                 for (int l = 0; l < LQP; ++l) buf_store16<g16>(ro, pqt[l] < rows ? pqoff[l] : kOutOfRange, o[l]);
             };
-            // ---- prologue: chunk 0 staged into buffer 0, chunk 1 requested
-            p_load(s0);
-            p_stage_kv(0, min(C, N - s0));
-            p_stage_q(0);
-            p_load(s0 + C);
-            lds_barrier();
-            for (int c = 0; c < nch; ++c) {
+            // One chunk step (two sets); r holds chunk c+1 and is refilled
+            // with chunk c+3.  The one-set loop below is the same step with
+            // chunk c+2 requested, and phase 1 only where these waves own
+            // state tiles (never for the fp32 shape).
+            auto step = [&](int c, PSet &r) {
                 const int t0 = s0 + c * C, nb = (c + 1) & 1;
-                // while the compute waves run phase 1 of chunk c: K, V of chunk c+1
-                if (c + 1 < nch) p_stage_kv(nb, min(C, N - t0 - C));
+                phase1(c, t0, Tile<T, D>{smK[c & 1]}, Tile<T, D>{smV[c & 1]});
+                // while the other waves finish phase 1 of chunk c: K, V of chunk c+1
+                if (c + 1 < nch) p_stage_kv(r, nb, min(C, N - t0 - C));
                 lds_barrier();
                 // while they run phase 2: the outputs of chunk c-1 (parked in
-                // buffer nb) out, phi(q) of chunk c+1 in, chunk c+2 requested
+                // buffer nb) out, phi(q) of chunk c+1 in, chunk c+3 requested
                 if (c >= 1) p_out(nb, t0 - C);
-                if (c + 1 < nch) {
-                    p_stage_q(nb);
-                    p_load(t0 + 2 * C);  // past the segment: no access
-                }
+                if (c + 1 < nch) p_stage_q(r, nb);
+                p_load(r, t0 + 3 * C);  // past the segment: no access
                 lds_barrier();
+            };
+            // ---- prologue: chunk 0 staged into buffer 0, chunks 1 .. NSET requested
+            p_load(sa, s0);
+            if constexpr (NSET == 2) p_load(sb, s0 + C);
+            p_stage_kv(sa, 0, min(C, N - s0));
+            p_stage_q(sa, 0);
+            p_load(sa, s0 + NSET * C);
+            lds_barrier();
+            if constexpr (NSET == 2) {
+                for (int c = 0; c < nch; c += 2) {
+                    step(c, sb);
+                    if (c + 1 < nch) step(c + 1, sa);
+                }
+            } else {
+                for (int c = 0; c < nch; ++c) {
+                    const int t0 = s0 + c * C, nb = (c + 1) & 1;
+                    if (c + 1 < nch) p_stage_kv(sa, nb, min(C, N - t0 - C));
+                    lds_barrier();
+                    if (c >= 1) p_out(nb, t0 - C);
+                    if (c + 1 < nch) {
+                        p_stage_q(sa, nb);
+                        p_load(sa, t0 + 2 * C);
+                    }
+                    lds_barrier();
+                }
             }
             if (nch > 0) p_out((nch - 1) & 1, s0 + (nch - 1) * C);
         } else {

@@ -65,14 +65,18 @@ constexpr MainShape main_shape(int e, int D, int C, int GT)
     const int th = 64 * nw;
     const int lk = (C * (D / u) + th - 1) / th;
     const int lq = (GT * C * (D / u) + th - 1) / th;
-    // Staging waves: every state tile and every phase-2 item (query tile,
-    // output-column part) on a wave of the first half of the workgroup, the
-    // second half staging; K, V and q double-buffered.
-    const int dt = D / 32, nu = GT * ct;
-    const int parts = nu >= nw ? 1 : (nw / nu < dt ? nw / nu : dt);
+    // Staging waves: every phase-2 item (query tile, output-column part) on
+    // a wave of the first half of the workgroup, the second half staging
+    // (state tiles stay spread over all waves); K, V and q double-buffered.
+    // fp32 at d = 64 (its state tiles all sit on the first half anyway) and
+    // 16-bit rows at d = 128, whose matrix work is small next to the bytes
+    // each chunk moves, so deeper prefetch pays for fewer computing waves.
+    const int dt = D / 32, nu = GT * ct, nwc = nw / 2;
+    const int parts = nu >= nwc ? 1 : (nwc / nu < dt ? nwc / nu : dt);
     const unsigned long lds_pipe = (unsigned long)e * (4ul * C * D + 2ul * GT * C * D +
                                                        (unsigned long)nsc * ((unsigned long)D * D + D));
-    const bool pipe = e == 4 && nw == 8 && !shift && dt * dt <= nw / 2 && nu * parts <= nw / 2 && lds_pipe <= full;
+    const bool pipe = nw == 8 && occ == 1 && !shift && nu * parts <= nwc && lds_pipe <= full &&
+                      ((e == 4 && D == 64 && dt * dt <= nwc) || (e == 2 && D == 128));
     const unsigned long lds_used = pipe ? lds_pipe : lds;
     MainShape m{nsc, occ, nw, lk, lq, shift, lds_used <= full && lq4 <= 8 && (shift || ct / nsc <= 2), lds_used, pipe};
     return m;
