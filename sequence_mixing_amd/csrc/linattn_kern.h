@@ -592,6 +592,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
     constexpr int E = (int)sizeof(T);
     g16 kA[G::LDV], vA[G::LDV], kB[G::LDV], vB[G::LDV];
     auto rows_at = [&](int t0) { return t0 < s1 ? min(C1, s1 - t0) : 0; };
+    // First token of the i-th chunk taken (i >= nch: past the segment, no
+    // rows).  Plain sums take the segment's chunks last to first: the pass
+    // that follows starts at the segment's first tokens, which are then the
+    // ones most recently read, still in the memory-side cache when K and V
+    // do not fit it whole.  Decayed sums need the forward order.
+    auto tpos = [&](int i) {
+        const int kx = DK ? i : nch - 1 - i;
+        return i < nch && kx >= 0 ? s0 + kx * C1 : s1;
+    };
     // log-decay of token t0 + tid (zero past the segment)
     const float *gb = DK ? gd + (size_t)seq * N : nullptr;
     float gA = 0.f, gB = 0.f, glog = 0.f;
@@ -609,11 +618,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
             vr[l] = buf_load16<g16>(rv, off);
         }
     };
-    load(kA, vA, s0);
-    load_g(gA, s0);
+    load(kA, vA, tpos(0));
+    load_g(gA, tpos(0));
     __builtin_amdgcn_sched_barrier(0);  // keep chunk 0's loads ahead of chunk 1's, as in the loop
-    load(kB, vB, s0 + C1);
-    load_g(gB, s0 + C1);
+    load(kB, vB, tpos(1));
+    load_g(gB, tpos(1));
     auto absorb = [&](int buf) {
         const Tile<T, D> sK{smK[buf]}, sV{smV[buf]};
 #pragma unroll
@@ -644,20 +653,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
     // Chunks in pairs; with an odd count the last pair's second chunk lies
     // past the segment and adds zeros (every step issues the same loads).
     for (int ci = 0; ci < nch; ci += 2) {
-        stage_rows<T, D, C1, kThreads, IO>(kA, vA, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, rows_at(s0 + ci * C1), tid);
+        stage_rows<T, D, C1, kThreads, IO>(kA, vA, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, rows_at(tpos(ci)), tid);
         if constexpr (DK) {
             decay_stage<C1>(smD[0], gA, tid);
-            load_g(gA, s0 + (ci + 2) * C1);
+            load_g(gA, tpos(ci + 2));
         }
-        load(kA, vA, s0 + (ci + 2) * C1);
+        load(kA, vA, tpos(ci + 2));
         lds_barrier();
         absorb(0);
-        stage_rows<T, D, C1, kThreads, IO>(kB, vB, Tile<T, D>{smK[1]}, Tile<T, D>{smV[1]}, rows_at(s0 + (ci + 1) * C1), tid);
+        stage_rows<T, D, C1, kThreads, IO>(kB, vB, Tile<T, D>{smK[1]}, Tile<T, D>{smV[1]}, rows_at(tpos(ci + 1)), tid);
         if constexpr (DK) {
             decay_stage<C1>(smD[1], gB, tid);
-            load_g(gB, s0 + (ci + 3) * C1);
+            load_g(gB, tpos(ci + 3));
         }
-        load(kB, vB, s0 + (ci + 3) * C1);
+        load(kB, vB, tpos(ci + 3));
         lds_barrier();
         absorb(1);
     }
