@@ -606,8 +606,9 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
             };
             // One chunk step (two sets); r holds chunk c+1 and is refilled
             // with chunk c+3.  The one-set loop below is the same step with
-            // chunk c+2 requested, and phase 1 only where these waves own
-            // state tiles (never for the fp32 shape).
+            // chunk c+2 requested, the outputs of chunk c-1 written beside
+            // phase 1 (balancing the two halves), and no phase 1 (its state
+            // tiles all sit on the first half: the fp32 shape).
             auto step = [&](int c, PSet &r) {
                 const int t0 = s0 + c * C, nb = (c + 1) & 1;
                 phase1(c, t0, Tile<T, D>{smK[c & 1]}, Tile<T, D>{smV[c & 1]});
@@ -636,9 +637,11 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
             } else {
                 for (int c = 0; c < nch; ++c) {
                     const int t0 = s0 + c * C, nb = (c + 1) & 1;
+                    // beside phase 1: the outputs of chunk c-1 out, K, V of chunk c+1 in
+                    if (c >= 1) p_out(nb, t0 - C);
                     if (c + 1 < nch) p_stage_kv(sa, nb, min(C, N - t0 - C));
                     lds_barrier();
-                    if (c >= 1) p_out(nb, t0 - C);
+                    // beside phase 2: phi(q) of chunk c+1 in, chunk c+2 requested
                     if (c + 1 < nch) {
                         p_stage_q(sa, nb);
                         p_load(sa, t0 + 2 * C);
