@@ -245,8 +245,11 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
             const int st = BG::tile_of(w, i);
             if (st < BG::NST) publish_tile<T, D>(S[i], sS, st / BG::DT, st % BG::DT, lane);
         }
-        for (int i = tid; i < D; i += BG::TH) sZp[i] = init[(size_t)D * D + i];
-        for (int e = tid; e < kBC * D; e += BG::TH) sZt[e] = init[(size_t)D * D + e % D];
+        // one load per thread: every e it fills has e % D == tid % D
+        static_assert(BG::TH % D == 0, "z element of a thread");
+        const float zt = init[(size_t)D * D + tid % D];
+        if (tid < D) sZp[tid] = zt;
+        for (int e = tid; e < kBC * D; e += BG::TH) sZt[e] = zt;
     }
 
     g16 kr[LDV], vr[LDV], qr[LDV], orr[LDV], dr[LDV];

@@ -741,12 +741,21 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restric
     }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
     const float *S = ws + slot0 * (size_t)D * (D + 1);
-    // S^T into LDS: element (row j, col i) = S[i][j].
-    for (int e = tid; e < D * D; e += kThreads) {
-        const int i = e / D, j = e % D;
-        smST[sST.at(j, i)] = (T)S[e];
+    // S^T into LDS: element (row j, col i) = S[i][j].  Every thread's 16-byte
+    // groups of S (and z) are requested at once, then written transposed.
+    constexpr int S4 = D * D / 4, SPT = S4 / kThreads;
+    static_assert(S4 % kThreads == 0 && D <= kThreads, "S in whole 16-byte groups per thread");
+    f32x4 sg[SPT];
+#pragma unroll
+    for (int l = 0; l < SPT; ++l) sg[l] = *reinterpret_cast<const f32x4 *>(S + 4 * (tid + l * kThreads));
+    const float zv = tid < D ? S[(size_t)D * D + tid] : 0.f;
+#pragma unroll
+    for (int l = 0; l < SPT; ++l) {
+        const int e = 4 * (tid + l * kThreads), i = e / D, j0 = e % D;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) smST[sST.at(j0 + x, i)] = (T)sg[l][x];
     }
-    for (int e = tid; e < D; e += kThreads) smZ[e] = S[(size_t)D * D + e];
+    if (tid < D) smZ[tid] = zv;
     __syncthreads();
 
     const T *qb = q + qbase;
