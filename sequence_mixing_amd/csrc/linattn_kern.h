@@ -489,10 +489,32 @@ __device__ __forceinline__ size_t packed_slot0(const SegLoc &r, int g, int Hkv, 
 }
 
 // One workgroup: builds the tables of a packed batch from cu[0..nb].
+// Exclusive scan of x over the workgroup's threads in thread order, starting
+// from init: thread t gets op(init, x_0, ..., x_{t-1}).  Shuffles within each
+// wave, then the wave totals through LDS (sw: one int per wave).
+template <class Op>
+__device__ __forceinline__ int block_exclusive_scan(int x, int init, int *sw, Op op)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int incl = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl = op(incl, y);
+    }
+    if (lane == 63) sw[w] = incl;
+    __syncthreads();
+    int pre = init;
+    for (int i = 0; i < w; ++i) pre = op(pre, sw[i]);
+    const int prev = __shfl_up(incl, 1);
+    __syncthreads();  // sw may be reused by the caller
+    return lane == 0 ? pre : op(pre, prev);
+}
+
 __global__ __launch_bounds__(kThreads) void k_pack_plan(const int *__restrict__ cu, int nb, int total, int seg_len,
                                                         int nsmax, int *__restrict__ tab)
 {
-    __shared__ int sred[kThreads];
+    __shared__ int sw[kThreads / 64];
     int *segpre = tab, *off = tab + nb + 1, *len = off + nb, *segb = len + nb;
     const int tid = threadIdx.x;
     const int per = (nb + kThreads - 1) / kThreads;
@@ -501,18 +523,10 @@ __global__ __launch_bounds__(kThreads) void k_pack_plan(const int *__restrict__ 
     // boundary j is the running maximum of cu[0..j], clamped to [0, total]
     int m = -2147483647 - 1;
     for (int j = b0 + 1; j <= b1; ++j) m = max(m, cu[j]);
-    sred[tid] = m;
-    __syncthreads();
-    if (tid == 0) {
-        int run = cu[0];
-        for (int t = 0; t < kThreads; ++t) {
-            const int x = sred[t];
-            sred[t] = run;  // maximum of cu[0 .. b0 of thread t]
-            run = max(run, x);
-        }
-    }
-    __syncthreads();
-    int run = sred[tid], nseg = 0;
+    auto imax = [](int a, int b) { return a > b ? a : b; };
+    auto iadd = [](int a, int b) { return a + b; };
+    // maximum of cu[0 .. b0] for this thread's first sequence
+    int run = block_exclusive_scan(m, cu[0], sw, imax), nseg = 0;
     for (int b = b0; b < b1; ++b) {
         const int lo = clampt(run);
         run = max(run, cu[b + 1]);
@@ -521,20 +535,8 @@ __global__ __launch_bounds__(kThreads) void k_pack_plan(const int *__restrict__ 
         len[b] = hi - lo;
         nseg += hi > lo ? (hi - lo + seg_len - 1) / seg_len : 1;
     }
-    __syncthreads();
-    sred[tid] = nseg;
-    __syncthreads();
-    if (tid == 0) {
-        int acc = 0;
-        for (int t = 0; t < kThreads; ++t) {
-            const int x = sred[t];
-            sred[t] = acc;
-            acc += x;
-        }
-        segpre[nb] = acc;
-    }
-    __syncthreads();
-    int sbase = sred[tid];
+    int sbase = block_exclusive_scan(nseg, 0, sw, iadd);  // segments of the sequences before b0
+    if (tid == kThreads - 1) segpre[nb] = sbase + nseg;
     for (int b = b0; b < b1; ++b) {
         segpre[b] = sbase;
         const int np = len[b] > 0 ? (len[b] + seg_len - 1) / seg_len : 1;
