@@ -10,7 +10,8 @@
 // phi(k_s) (README "Features": causal masking without a quadratic buffer;
 // Katharopoulos et al. 2020, cited in the README's "Reference" section).
 //
-// Kernel family (one workgroup = 4 wave64s = 256 threads everywhere):
+// Kernel family (workgroups of 4 wave64s = 256 threads; the chunk kernel's
+// shapes that run one workgroup per CU use 8):
 //   seg_totals    per (sequence, segment): T_p = phi(K_p)^T V_p and sum phi(K_p)
 //                 on MFMA, written as fp32 partials (causal: all segments but
 //                 the last; non-causal: all segments).
@@ -21,8 +22,8 @@
 //                   O^T = V^T (M . phi(K) phi(Q)^T) + S_prev^T phi(Q)^T
 //                 (intra-chunk masked term plus the carried-state term, both
 //                 on MFMA), then S += phi(K)^T V on MFMA.  The d x d fp32 state
-//                 lives in MFMA accumulators spread over the four waves; the
-//                 waves see it through an LDS copy refreshed once per chunk.
+//                 lives in MFMA accumulators spread over the waves; the waves
+//                 see it through LDS copies refreshed every key tile (or pair).
 //   noncausal_apply  O = phi(Q) S / phi(Q) . z with the summed S, z.
 //   decode_step   one token: S += phi(k) v^T, z += phi(k), then G query heads
 //                 read the updated state.  Bandwidth bound, plain fp32 VALU.
@@ -69,7 +70,8 @@ using linattn::Timing;
 //            and the denominator; it parks O in its own phi(Q) rows.
 // Global memory is touched only during staging: one wait there covers loads
 // and stores issued a whole chunk earlier, and the compute phases never wait
-// on memory.
+// on memory.  With staging waves (MainShape::pipe) half of the waves stage
+// chunk c+1 while the other half run phase 2 of chunk c (see below).
 template <typename T, int D, int C, int GT>
 struct Main {
     static constexpr linattn::MainShape SH = linattn::main_shape((int)sizeof(T), D, C, GT);
