@@ -901,8 +901,17 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
     for (int g0 = 0; g0 < G; g0 += GMAX) {
         const int gn = G - g0 < GMAX ? G - g0 : GMAX;
         if (g0 > 0) {
+            // the next GMAX query heads, requested at once as in the first pass
+            const Rsrc rq2 = make_rsrc(qb + (size_t)g0 * D, gn * D * E);
+#pragma unroll
+            for (int j = 0; j < QGR; ++j) qg[j] = buf_load16<g16>(rq2, off + (unsigned)j * kThreads * 16u);
             lds_barrier();
-            for (int e = tid; e < gn * D; e += kThreads) sqf[e] = IO::phi::f(Io<T, IO>::f(qb[(size_t)g0 * D + e]));
+#pragma unroll
+            for (int j = 0; j < QGR; ++j) {
+                const int e0 = (tid + j * kThreads) * U;
+#pragma unroll
+                for (int i = 0; i < U; ++i) sqf[e0 + i] = IO::phi::f(Io<T, IO>::f(qg[j][i]));
+            }
             __syncthreads();
         }
         // Denominators: wave wv reduces phi(q_g) . z for heads g = wv, wv + 4, ...
