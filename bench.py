@@ -716,6 +716,33 @@ def decode_oracle(seconds):
             "sample": f"{steps} decode steps at batch {dw.B} in {el:.1f} s (single thread)"}
 
 
+def gpu_clocks():
+    """Current shader (sclk) and memory (mclk) clocks of the GPU in MHz, read
+    after the timed work with rocm-smi in a child process; None if unavailable."""
+    import re
+    import subprocess
+
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        data = json.loads(r.stdout)
+    except Exception:  # no tool, no JSON: the figures are optional
+        return None
+    dev = os.environ.get("HIP_VISIBLE_DEVICES", "0").split(",")[0] or "0"
+    card = data.get(f"card{dev}") or next((v for k, v in data.items() if k.startswith("card")), None)
+    if not isinstance(card, dict):
+        return None
+    out = {}
+    for key, val in card.items():
+        m = re.search(r"(\d+)\s*Mhz", str(val), re.IGNORECASE)
+        for name in ("sclk", "mclk"):
+            if name in key.lower() and m and f"{name}_mhz" not in out:
+                out[f"{name}_mhz"] = int(m.group(1))
+    if not out:
+        return None
+    out["source"] = "rocm-smi --showclocks, after the timed work"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -815,6 +842,7 @@ def main():
         "stage_us": head["stage_us"],
         "cold": {"stage_us": head.get("cold_stage_us"), "roofline_path": head.get("cold_roofline_path")},
         "cpu_baseline": cpu,
+        "gpu_clocks": gpu_clocks(),
         "rows": rows,
     }
     print(json.dumps(res), flush=True)
