@@ -294,6 +294,21 @@ def test_chunk_invariance():
         assert rows_rel_err(o, outs[0]) <= 2e-2
 
 
+@pytest.mark.parametrize("causal", [1, 0])
+@pytest.mark.parametrize("d,G", [(64, 1), (128, 4)])
+def test_fp32_kernel_vs_bf16_kernel(causal, d, G):
+    # bf16-representable inputs: the fp32 path reads them exactly, so the two
+    # kernels differ only by the bf16 path's operand and output roundings
+    q, k, v = make_qkv(2, 2 * G, 2, 1500, d, "bf16", 12 + d)
+    o16 = host(ops.fwd(gpu(q), gpu(k), gpu(v), causal=causal))
+    o32 = host(ops.fwd(gpu(q.float()), gpu(k.float()), gpu(v.float()), causal=causal))
+    torch.cuda.synchronize()
+    ref = oracle.ref_fwd(q, k, v, causal=causal)
+    assert rows_rel_err(o32, ref) <= TOL["f32"]
+    assert rows_rel_err(o16, ref) <= TOL["bf16"]
+    assert rows_rel_err(o16, o32) <= TOL["bf16"]
+
+
 def test_last_causal_row_equals_noncausal():
     q, k, v = make_qkv(2, 4, 2, 999, 64, "f32", 10)
     c = ops.fwd(gpu(q), gpu(k), gpu(v), causal=True)
