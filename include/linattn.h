@@ -212,8 +212,10 @@ int linattn_fwd_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype,
  * after a prefill of N tokens equals row N of a prefill of N + 1 tokens.
  *
  *   state   device fp32 [B][Hkv][d][d], read and written in place.
- *   z       device fp32 [B][Hkv][d], read and written in place; may be NULL
- *           only when normalise == 0 (then it is neither read nor written).
+ *   z       device fp32 [B][Hkv][d], read and written in place.  May be NULL
+ *           only when normalise == 0; when given it is always advanced
+ *           (z += phi(k)), whatever normalise is, so a state carried through
+ *           unnormalised steps can later be read normalised.
  *   q, out  device, dtype, [B][H][d];  k, v  device, dtype, [B][Hkv][d].
  *   out must not alias state, z, q, k or v.
  * Returns LINATTN_OK or a LINATTN_ERR_* code.

@@ -858,7 +858,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
     const unsigned off = (unsigned)tid * 16u;
     const g16 kg = buf_load16<g16>(make_rsrc(k + (size_t)seq * D, D * E), off);
     const g16 vg = buf_load16<g16>(make_rsrc(v + (size_t)seq * D, D * E), off);
-    const f32x4 zg = buf_load16<f32x4>(make_rsrc(normalise ? z + (size_t)seq * D : nullptr, normalise ? D * 4 : 0), off);
+    // z is advanced whenever it is given, also when the output is not
+    // normalised, so a state carried through such steps stays whole.
+    const f32x4 zg = buf_load16<f32x4>(make_rsrc(z ? z + (size_t)seq * D : nullptr, z ? D * 4 : 0), off);
     g16 qg[QGR];
     const Rsrc rq = make_rsrc(qb, g_first * D * E);
 #pragma unroll
@@ -896,7 +898,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
         __builtin_amdgcn_sched_barrier(0);  // rows in load order: each store waits for its own row only
     }
     lds_barrier();
-    if (normalise && tid < D) z[(size_t)seq * D + tid] = sz[tid];
+    if (z && tid < D) z[(size_t)seq * D + tid] = sz[tid];
 
     for (int g0 = 0; g0 < G; g0 += GMAX) {
         const int gn = G - g0 < GMAX ? G - g0 : GMAX;

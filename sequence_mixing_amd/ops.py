@@ -7,6 +7,7 @@ from __future__ import annotations
 import torch
 
 from . import (LINATTN_BF16, LINATTN_F16, LINATTN_F32, LinattnError, linattn_bwd, linattn_bwd_workspace_bytes,
+               linattn_fwd_plan,
                linattn_decode_step, linattn_decode_step_decay, linattn_fwd, linattn_fwd_decay,
                linattn_fwd_decay_workspace_bytes, linattn_fwd_from_state, linattn_fwd_packed,
                linattn_fwd_packed_workspace_bytes, linattn_fwd_workspace_bytes)
@@ -30,8 +31,48 @@ def dtype_code(t: torch.dtype, phi: str = "elu1") -> int:
 def workspace(B, H, Hkv, N, d, causal, dtype: torch.dtype, chunk=0, device="cuda") -> torch.Tensor | None:
     n = linattn_fwd_workspace_bytes(B, H, Hkv, N, d, causal, dtype_code(dtype), chunk)
     if n < 0:
-        raise LinattnError(-2, "linattn_fwd_workspace_bytes")
+        # the plan call reports why the arguments were rejected
+        rc, _, _ = linattn_fwd_plan(B, H, Hkv, N, d, causal, dtype_code(dtype), chunk)
+        raise LinattnError(rc if rc != 0 else -2, "linattn_fwd_workspace_bytes")
     return torch.empty((n + 3) // 4, dtype=torch.float32, device=device) if n > 0 else None
+
+
+def _nbytes(ws) -> int:
+    """Bytes of a caller's workspace tensor (any dtype), 0 for None."""
+    return ws.numel() * ws.element_size() if ws is not None else 0
+
+
+def _check_decode(state, z, q, k, v, normalise):
+    """Shapes, dtypes, contiguity and device of a decode step's tensors: the kernel writes
+    B*Hkv*d*d fp32 state values in place, so a wrong buffer must be refused here."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [B, H, d] and k, v [B, Hkv, d]")
+    B, H, d = q.shape
+    Hkv = k.shape[1]
+    for t in (q, k, v):
+        if not (t.is_cuda and t.is_contiguous() and t.dtype == q.dtype and t.device == q.device):
+            raise ValueError("q, k, v must be contiguous device tensors of one dtype on one device")
+    if k.shape != (B, Hkv, d) or v.shape != (B, Hkv, d):
+        raise ValueError("k and v must be [B, Hkv, d]")
+    if not (state.is_cuda and state.is_contiguous() and state.dtype == torch.float32 and
+            state.shape == (B, Hkv, d, d) and state.device == q.device):
+        raise ValueError("state must be a contiguous fp32 device tensor [B, Hkv, d, d] on q's device")
+    if z is None:
+        if normalise:
+            raise ValueError("z is required when normalise is set")
+    elif not (z.is_cuda and z.is_contiguous() and z.dtype == torch.float32 and z.shape == (B, Hkv, d) and
+              z.device == q.device):
+        raise ValueError("z must be a contiguous fp32 device tensor [B, Hkv, d] on q's device")
+    return B, H, Hkv, d
+
+
+def _check_out(out, q):
+    if out is None:
+        return torch.empty_like(q)
+    if not (out.is_cuda and out.is_contiguous() and out.dtype == q.dtype and out.shape == q.shape and
+            out.device == q.device):
+        raise ValueError("out must be a contiguous device tensor of q's shape, dtype and device")
+    return out
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=True, normalise=True, chunk=0,
@@ -54,7 +95,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=True, normalis
         z = torch.empty(B, Hkv, d, dtype=torch.float32, device=q.device)
     if ws is None:
         ws = workspace(B, H, Hkv, N, d, causal, q.dtype, chunk, q.device)
-    nbytes = ws.numel() * 4 if ws is not None else 0
+    nbytes = _nbytes(ws)
     if state_in is not None:
         starts = ((state_in, (B, Hkv, d, d)),) + (((z_in, (B, Hkv, d)),) if z_in is not None else ())
         for t, shape in starts:
@@ -99,7 +140,7 @@ def fwd_decay(q, k, v, g, normalise=True, chunk=0, want_state=False, out=None, w
         if n < 0:
             raise LinattnError(-4, "linattn_fwd_decay_workspace_bytes")
         ws = torch.empty((n + 3) // 4, dtype=torch.float32, device=q.device) if n > 0 else None
-    nbytes = ws.numel() * 4 if ws is not None else 0
+    nbytes = _nbytes(ws)
     rc = linattn_fwd_decay(q, k, v, g, out, B, H, Hkv, N, d, normalise, code, state_in, z_in, S, z, chunk, ws, nbytes,
                            stream)
     if rc != 0:
@@ -150,7 +191,7 @@ def fwd_packed(q, k, v, cu_seqlens, H, Hkv, d, causal=True, normalise=True, chun
     if ws is None:
         ws = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=q.device)
     rc = linattn_fwd_packed(q, k, v, out, cu_seqlens, nseqs, total, H, Hkv, d, causal, normalise, code, S, z, chunk,
-                            ws, ws.numel() * 4, stream)
+                            ws, _nbytes(ws), stream)
     if rc != 0:
         raise LinattnError(rc, "linattn_fwd_packed")
     return (out, S, z) if want_state else out
@@ -173,7 +214,7 @@ def bwd(q, k, v, out, dout, causal=True, normalise=True, ws=None, stream=None, g
     if ws is None:
         ws = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=q.device)
     rc = linattn_bwd(q, k, v, out if normalise else None, dout, dq, dk, dv, B, H, Hkv, N, d, causal, normalise, code,
-                     ws, ws.numel() * 4, stream)
+                     ws, _nbytes(ws), stream)
     if rc != 0:
         raise LinattnError(rc, "linattn_bwd")
     return dq, dk, dv
@@ -182,10 +223,8 @@ def bwd(q, k, v, out, dout, causal=True, normalise=True, ws=None, stream=None, g
 def decode_step(state: torch.Tensor, z: torch.Tensor | None, q, k, v, normalise=True, out=None, stream=None,
                 phi="elu1"):
     """One recurrent step through ``linattn_decode_step``; state [B,Hkv,d,d] and z [B,Hkv,d] fp32, in place."""
-    B, H, d = q.shape
-    Hkv = k.shape[1]
-    if out is None:
-        out = torch.empty_like(q)
+    B, H, Hkv, d = _check_decode(state, z, q, k, v, normalise)
+    out = _check_out(out, q)
     rc = linattn_decode_step(state, z, q, k, v, out, B, H, Hkv, d, normalise, dtype_code(q.dtype, phi), stream)
     if rc != 0:
         raise LinattnError(rc, "linattn_decode_step")
@@ -196,12 +235,10 @@ def decode_step_decay(state: torch.Tensor, z: torch.Tensor | None, q, k, v, g, n
                       stream=None):
     """One step through ``linattn_decode_step_decay``: S and z fade by exp(g) [B,Hkv] (fp32,
     device), then absorb (k, v) and are read by q; state and z are updated in place."""
-    B, H, d = q.shape
-    Hkv = k.shape[1]
+    B, H, Hkv, d = _check_decode(state, z, q, k, v, normalise)
     if not (g.is_cuda and g.is_contiguous() and g.dtype == torch.float32 and g.shape == (B, Hkv)):
         raise ValueError("g must be a contiguous fp32 device tensor [B, Hkv]")
-    if out is None:
-        out = torch.empty_like(q)
+    out = _check_out(out, q)
     rc = linattn_decode_step_decay(state, z, q, k, v, g, out, B, H, Hkv, d, normalise, dtype_code(q.dtype), stream)
     if rc != 0:
         raise LinattnError(rc, "linattn_decode_step_decay")

@@ -22,8 +22,8 @@ pytestmark = pytest.mark.gpu
 # (a, b, v, g, the masked scores, the carried S and R copies) are each rounded
 # to bf16 (2^-9 relative), and dq, dk subtract the normaliser term from the
 # value term, which amplifies those roundings by a small factor; measured
-# worst rows stay under 2e-2, the bar is 3e-2.
-TOL = {"f32": 1e-4, "bf16": 3e-2, "f16": 3e-2}
+# worst rows stay under 2e-2, which is the bar (the forward's bf16 bar).
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2e-2}
 TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
@@ -166,9 +166,9 @@ def test_bwd_deterministic_and_gqa_sum():
     m = ops.bwd(q, kr, vr, out, dout)
     torch.cuda.synchronize()
     sc = term_scale(host(dout), host(v))
-    assert rows_rel_err(host(a[0]), host(m[0]), sc) <= 3e-2
-    assert rows_rel_err(host(a[1]), host(m[1].view(B, Hkv, G, N, d).float().sum(2)), sc) <= 3e-2
-    assert rows_rel_err(host(a[2]), host(m[2].view(B, Hkv, G, N, d).float().sum(2)), sc) <= 3e-2
+    assert rows_rel_err(host(a[0]), host(m[0]), sc) <= 2e-2
+    assert rows_rel_err(host(a[1]), host(m[1].view(B, Hkv, G, N, d).float().sum(2)), sc) <= 2e-2
+    assert rows_rel_err(host(a[2]), host(m[2].view(B, Hkv, G, N, d).float().sum(2)), sc) <= 2e-2
 
 
 def test_bwd_argument_errors():

@@ -140,38 +140,55 @@ def test_config3_full(normalise):
     run_case(w.B, w.H, w.Hkv, w.N, w.d, w.dtype, 1, normalise, seed=w.seed)
 
 
-def sampled_check(w, out, S, z, seqs, normalise, q, k, v):
-    """Oracle on the sampled (b, kv head) sequences only; all their query heads."""
+def full_check(w, out, S, z, ref, Sr, zr, label):
+    """Every output row, state and normaliser of a full-size workload against the oracle."""
     tol = TOL[w.dtype]
-    G = w.G
-    for (b, g) in seqs:
-        hs = slice(g * G, (g + 1) * G)
-        ref, Sr, zr = oracle.ref_fwd(q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
-                                     causal=True, normalise=normalise, want_state=True)
-        e = rows_rel_err(host(out[b:b + 1, hs]), ref)
-        es = mat_rel_err(host(S[b:b + 1, g:g + 1]), Sr)
-        ez = mat_rel_err(host(z[b:b + 1, g:g + 1]), zr)
-        print(f"  seq b={b} g={g}: out {e:.2e} state {es:.2e} z {ez:.2e}", flush=True)
-        assert e <= tol and es <= tol and ez <= tol
+    e = rows_rel_err(host(out), ref)
+    es, ez = mat_rel_err(host(S), Sr), mat_rel_err(host(z), zr)
+    print(f"  {label}: out {e:.2e} state {es:.2e} z {ez:.2e}", flush=True)
+    assert e <= tol and es <= tol and ez <= tol, f"{label}: out {e:.3e} state {es:.3e} z {ez:.3e}"
 
 
+_REF_CACHE = {}
+
+
+def workload_ref(name, normalise):
+    """The oracle's rows and final sums for a whole workload (every batch entry and kv head),
+    computed once per (workload, normaliser) and shared by the chunk sizes."""
+    key = (name, normalise)
+    if key not in _REF_CACHE:
+        for other in [k_ for k_ in _REF_CACHE if k_[0] != name]:
+            del _REF_CACHE[other]  # the references of one workload held at a time
+        q, k, v = workload_qkv(WORKLOADS[name])
+        _REF_CACHE[key] = oracle.ref_fwd(q, k, v, causal=True, normalise=normalise, want_state=True)
+    return _REF_CACHE[key]
+
+
+@pytest.mark.parametrize("normalise", [1, 0])
 @pytest.mark.parametrize("chunk", [64, 128, 256])
-def test_config4_full_sampled(chunk):
+def test_config4_full(chunk, normalise):
+    """bf16 B2 H8 N65536 d64 at every chunk size and both normaliser settings, all 16 sequences."""
     w = WORKLOADS["cfg4"]
     q, k, v = workload_qkv(w)
-    print(f"cfg4 chunk={chunk}", flush=True)
-    out, S, z = ops.fwd(gpu(q), gpu(k), gpu(v), causal=True, normalise=True, chunk=chunk, want_state=True)
+    print(f"cfg4 chunk={chunk} normalise={normalise}", flush=True)
+    out, S, z = ops.fwd(gpu(q), gpu(k), gpu(v), causal=True, normalise=normalise, chunk=chunk, want_state=True)
     torch.cuda.synchronize()
-    sampled_check(w, out, S, z, [(0, 0), (1, 7)], True, q, k, v)
+    del q, k, v
+    ref, Sr, zr = workload_ref("cfg4", normalise)
+    full_check(w, out, S, z, ref, Sr, zr, f"cfg4 chunk {chunk} normalise {normalise}")
 
 
-def test_config5_prefill_full_sampled():
+@pytest.mark.parametrize("normalise", [1, 0])
+def test_config5_prefill_full(normalise):
+    """GQA bf16 B1 H32 Hkv8 N32768 d128, both normaliser settings, all 8 kv heads and 32 query heads."""
     w = WORKLOADS["cfg5"]
     q, k, v = workload_qkv(w)
-    print("cfg5 prefill", flush=True)
-    out, S, z = ops.fwd(gpu(q), gpu(k), gpu(v), causal=True, normalise=True, want_state=True)
+    print(f"cfg5 prefill normalise={normalise}", flush=True)
+    out, S, z = ops.fwd(gpu(q), gpu(k), gpu(v), causal=True, normalise=normalise, want_state=True)
     torch.cuda.synchronize()
-    sampled_check(w, out, S, z, [(0, 0), (0, 5)], True, q, k, v)
+    del q, k, v
+    ref, Sr, zr = workload_ref("cfg5", normalise)
+    full_check(w, out, S, z, ref, Sr, zr, f"cfg5 prefill normalise {normalise}")
 
 
 # ------------------------------------------------------------------ decode
@@ -231,18 +248,18 @@ def test_decode_continues_prefill_on_gpu():
 def test_config5_decode_1024_steps_sampled():
     """GQA prefill, its state replicated into 64 slots, then 1024 decode steps at batch 64.
 
-    The GPU runs the whole batch; the oracle follows slots 0 and 63 end to end
-    (its own prefill state, its own decode steps) over all 1024 steps.
+    The GPU runs the whole batch; the oracle follows slots 0, 31 and 63 with all 8 kv
+    heads and all 32 query heads end to end (its own prefill state, its own decode
+    steps) over all 1024 steps, and compares their states and normalisers at the end.
     """
     w, dw = WORKLOADS["cfg5"], DECODE
     q, k, v = workload_qkv(w)
     _, S1, z1 = ops.fwd(gpu(q), gpu(k), gpu(v), want_state=True)
-    _, Sr1, zr1 = oracle.ref_fwd(q[:, :8], k[:, :2], v[:, :2], want_state=True)  # kv heads 0, 1 only
+    _, Sr1, zr1 = workload_ref("cfg5", 1)
     del q, k, v
     S = S1.expand(dw.B, -1, -1, -1).contiguous()
     z = z1.expand(dw.B, -1, -1).contiguous()
-    slots = [0, 63]
-    # Oracle state for the sampled slots: kv heads 0 and 1 only (heads are independent).
+    slots = [0, 31, 63]
     Sr = np.ascontiguousarray(np.repeat(Sr1, len(slots), axis=0))
     zr = np.ascontiguousarray(np.repeat(zr1, len(slots), axis=0))
     stream = DecodeStream(dw.B, dw.H, dw.Hkv, dw.d, dw.dtype, dw.seed)
@@ -250,11 +267,36 @@ def test_config5_decode_1024_steps_sampled():
     for step in range(1024):
         qs, ks, vs = stream.next()
         o = ops.decode_step(S, z, gpu(qs), gpu(ks), gpu(vs))
-        ref = oracle.ref_decode_step(Sr, zr, qs[slots, :8], ks[slots, :2], vs[slots, :2], normalise=True)
-        e = rows_rel_err(host(o[slots, :8]), ref)
+        ref = oracle.ref_decode_step(Sr, zr, qs[slots], ks[slots], vs[slots], normalise=True)
+        e = rows_rel_err(host(o[slots]), ref)
         worst = max(worst, e)
         assert e <= TOL["bf16"], f"step {step}: {e:.3e}"
-    print(f"decode worst rel err over 1024 steps: {worst:.3e}", flush=True)
+    torch.cuda.synchronize()
+    es, ez = mat_rel_err(host(S[slots]), Sr), mat_rel_err(host(z[slots]), zr)
+    print(f"decode worst rel err over 1024 steps: {worst:.3e}; final state {es:.2e}, z {ez:.2e}", flush=True)
+    # the start sums are the bf16 prefill's (phi(k) rounded to bf16 at the matrix core)
+    assert es <= TOL["bf16"] and ez <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_unnormalised_steps_advance_z(dtype):
+    """Steps with normalise = 0 and z given advance z, so a later normalised step (and a
+    continued prefill) read the whole sums: three unnormalised steps, then a normalised one."""
+    B, H, Hkv, d = 2, 8, 2, 64
+    q0, k0, v0 = make_qkv(B, Hkv, Hkv, 40, d, dtype, 123)
+    _, S, z = ops.fwd(gpu(q0), gpu(k0), gpu(v0), want_state=True)
+    Sr, zr = host(S).copy(), host(z).copy()
+    stream = DecodeStream(B, H, Hkv, d, dtype, 321)
+    tol = 1e-5 if dtype == "f32" else TOL[dtype]
+    for step, normalise in enumerate((0, 0, 0, 1)):
+        q, k, v = stream.next()
+        o = ops.decode_step(S, z, gpu(q), gpu(k), gpu(v), normalise=normalise)
+        ref = oracle.ref_decode_step(Sr, zr, q, k, v, normalise=normalise)
+        torch.cuda.synchronize()
+        e = rows_rel_err(host(o), ref)
+        assert e <= tol, f"step {step} normalise {normalise}: {e:.3e}"
+        assert mat_rel_err(host(S), Sr) <= 1e-5
+        assert mat_rel_err(host(z), zr) <= 1e-6, f"step {step}: z not advanced"
 
 
 # ---------------------------------------------------------- structure on GPU
