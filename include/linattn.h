@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 8
+#define LINATTN_ABI_VERSION 9
 
 enum { LINATTN_F32 = 0, LINATTN_BF16 = 1, LINATTN_F16 = 2 };
 /* Feature maps phi (README "Features": custom kernel plugins, phi
@@ -68,7 +68,9 @@ enum {
     LINATTN_ERR_UNSUPPORTED = -4, /* d or chunk not supported by the kernels          */
     LINATTN_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required       */
     LINATTN_ERR_HIP = -6,         /* a HIP launch or runtime call failed              */
-    LINATTN_ERR_ALIGN = -7        /* a pointer is not 16-byte aligned                 */
+    LINATTN_ERR_ALIGN = -7,       /* a pointer is not 16-byte aligned                 */
+    LINATTN_ERR_SCRATCH = -8      /* linattn_fwd_noalloc: the call needs more than the
+                                     library's static scratch                          */
 };
 
 /*
@@ -189,6 +191,27 @@ int linattn_fwd_timed(const void *q, const void *k, const void *v, void *out,
  */
 size_t linattn_fwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int causal, int dtype,
                                    int chunk);
+
+/*
+ * linattn_fwd_noalloc - linattn_fwd for callers that cannot allocate: code
+ * under HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as linattn_fwd, without the
+ * workspace: the call uses the library's static device scratch of
+ * LINATTN_NOALLOC_SCRATCH_BYTES (64 MiB; one copy per GPU the library runs
+ * on, held until the process ends) and calls no hipMalloc, hipFree or other
+ * allocating routine.  A call whose linattn_fwd_workspace_bytes(...) exceeds
+ * that size returns LINATTN_ERR_SCRATCH before anything is launched.  The
+ * caller still provides q, k, v, out and the optional state_out / z_out.
+ * Every call on one GPU shares that GPU's scratch, so calls that overlap in
+ * time on one GPU (two streams, or two host threads) race and must be
+ * ordered by the caller; calls ordered on one stream are safe.  The first
+ * call on a device looks up the scratch's address there (a host-side
+ * lookup, no allocation) under a lock.
+ */
+#define LINATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int linattn_fwd_noalloc(const void *q, const void *k, const void *v, void *out,
+                        int B, int H, int Hkv, int N, int d, int causal, int normalise, int dtype,
+                        float *state_out, float *z_out, int chunk, hipStream_t stream);
 
 /*
  * linattn_fwd_plan - the launch plan linattn_fwd would use (host only, no

@@ -18,7 +18,8 @@ __all__ = [
     "LINATTN_F32", "LINATTN_BF16", "LINATTN_F16", "LINATTN_OK", "LinattnError", "library_path", "load",
     "linattn_fwd", "linattn_fwd_from_state", "linattn_fwd_timed", "linattn_fwd_workspace_bytes", "linattn_fwd_plan", "linattn_decode_step",
     "linattn_status_string", "linattn_abi_version", "linattn_bwd", "linattn_bwd_workspace_bytes",
-    "linattn_fwd_packed", "linattn_fwd_packed_workspace_bytes",
+    "linattn_fwd_packed", "linattn_fwd_packed_workspace_bytes", "linattn_fwd_noalloc",
+    "LINATTN_NOALLOC_SCRATCH_BYTES",
 ]
 
 LINATTN_F32 = 0
@@ -28,8 +29,10 @@ LINATTN_OK = 0
 ERRORS = {
     -1: "LINATTN_ERR_NULL", -2: "LINATTN_ERR_SHAPE", -3: "LINATTN_ERR_DTYPE",
     -4: "LINATTN_ERR_UNSUPPORTED", -5: "LINATTN_ERR_WORKSPACE", -6: "LINATTN_ERR_HIP",
-    -7: "LINATTN_ERR_ALIGN",
+    -7: "LINATTN_ERR_ALIGN", -8: "LINATTN_ERR_SCRATCH",
 }
+# size of the library's static device scratch used by linattn_fwd_noalloc
+LINATTN_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liblinattn.so")
@@ -61,6 +64,8 @@ def load():
         lib.linattn_fwd_timed.restype = i
         lib.linattn_fwd_timed.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i, vp, sz, vp,
                                           ctypes.POINTER(vp), i, i]
+        lib.linattn_fwd_noalloc.restype = i
+        lib.linattn_fwd_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i, vp]
         lib.linattn_fwd_workspace_bytes.restype = sz
         lib.linattn_fwd_workspace_bytes.argtypes = [i] * 8
         lib.linattn_fwd_plan.restype = i
@@ -114,6 +119,13 @@ def linattn_fwd(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_o
     return load().linattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, N, d, int(causal),
                               int(normalise), dtype, _ptr(state_out), _ptr(z_out), chunk, _ptr(workspace),
                               workspace_bytes, _stream(stream))
+
+
+def linattn_fwd_noalloc(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_out=None, z_out=None,
+                        chunk=0, stream=None) -> int:
+    """C ``linattn_fwd_noalloc`` (the library's static scratch, no workspace); returns the status code."""
+    return load().linattn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, N, d, int(causal),
+                                      int(normalise), dtype, _ptr(state_out), _ptr(z_out), chunk, _stream(stream))
 
 
 def linattn_fwd_from_state(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_in, z_in,

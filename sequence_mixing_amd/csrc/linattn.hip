@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "linattn.h"
 #include "linattn_fwd.h"
 #include "linattn_kern.h"
@@ -83,6 +85,7 @@ const char *linattn_status_string(int status)
     case LINATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case LINATTN_ERR_HIP: return "HIP launch failed";
     case LINATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case LINATTN_ERR_SCRATCH: return "problem needs more than the library's static scratch (LINATTN_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }
@@ -224,6 +227,64 @@ int linattn_fwd_timed(const void *q, const void *k, const void *v, void *out, in
     for (int i = 0; i < 4; ++i)
         if (record(&t, i, stream)) return LINATTN_ERR_HIP;
     return LINATTN_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ forward without allocation
+//
+// linattn_fwd_noalloc runs linattn_fwd with the library's own device scratch
+// instead of a caller's workspace: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol); each device's address is taken once with hipGetSymbolAddress,
+// with that device current, and kept in scratch_ptr[device].  Nothing in the
+// scratch has to start at zero: every pass writes the slots it later reads.
+namespace {
+static __device__ __align__(256) float scratch[LINATTN_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];
+
+// Address of this library's scratch on the device that runs `stream`.
+int scratch_for(hipStream_t stream, void **out)
+{
+    int dev = -1, cur = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || hipGetDevice(&cur) != hipSuccess) return LINATTN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return LINATTN_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return LINATTN_ERR_HIP;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return LINATTN_ERR_HIP;
+        if (e != hipSuccess || !p) return LINATTN_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return LINATTN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int linattn_fwd_noalloc(const void *q, const void *k, const void *v, void *out, int B, int H, int Hkv, int N, int d,
+                        int causal, int normalise, int dtype, float *state_out, float *z_out, int chunk,
+                        hipStream_t stream)
+{
+    const size_t need = linattn_fwd_workspace_bytes(B, H, Hkv, N, d, causal, dtype, chunk);
+    if (need == (size_t)-1) {
+        linattn::Plan pl;
+        return linattn::make_plan(B, H, Hkv, N, d, causal, dtype, chunk, &pl);
+    }
+    if (need > LINATTN_NOALLOC_SCRATCH_BYTES) return LINATTN_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (need > 0) {
+        const int rc = scratch_for(stream, &ws);
+        if (rc != LINATTN_OK) return rc;
+    }
+    return fwd_impl(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_out, z_out, chunk, ws,
+                    LINATTN_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 }  // extern "C"
