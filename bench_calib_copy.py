@@ -1,6 +1,6 @@
 """A plain device copy of known size, for calibrating HBM byte counters.
 
-    python -m sequence_mixing_amd.calib_copy [MiB]
+    python bench_calib_copy.py [MiB]
 
 Copies a MiB-sized fp32 buffer into another three times with torch's copy
 kernel: each launch reads MiB and writes MiB.  Profiled with

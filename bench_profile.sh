@@ -2,7 +2,7 @@
 # Regenerates the rocprofv3 summaries kept under profiles/ (run from the
 # repository root on a machine with the GPU; raw output goes to $1).
 #
-#   bash sequence_mixing_amd/profile.sh <raw-output-dir> [summaries]
+#   bash bench_profile.sh <raw-output-dir> [summaries]
 #
 # With "summaries" only the text summaries are written again from the raw
 # output already in the directory (no GPU needed).
@@ -26,7 +26,7 @@ KR="k_causal_chunks|k_seg_totals|k_seg_scan|k_noncausal_apply"
 step() { echo "== $*"; }
 
 C1="rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace_all -o run -- python3 bench.py --cpu-seconds 2"
-C2="rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace_cfg2 -o run -- python3 bench.py --rows 0 --cpu-seconds 0"
+C2="rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace_cfg2 -o run -- python3 bench.py --cold-only --cpu-seconds 0"
 CTRS="MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT"
 C3="rocprofv3 --pmc $CTRS --kernel-include-regex '$KR|k_decode_step|k_bwd' -f csv -d $OUT/counters_all -o run -- python3 bench.py --rows 1 --steps 5 --warmup 2 --cpu-seconds 0"
 if [ "${2:-}" != "summaries" ]; then
@@ -37,16 +37,16 @@ timeout -k 10 300 $C2 > "$OUT/trace_cfg2.json" 2> "$OUT/trace_cfg2.err"
 for ctr in FETCH_SIZE WRITE_SIZE; do
     step "$ctr: headline workload"
     timeout -s KILL 200 rocprofv3 --pmc $ctr --kernel-include-regex "$KR" -f csv -d $OUT/${ctr}_cfg2 -o run -- \
-        python3 bench.py --rows 0 --steps 5 --warmup 2 --cpu-seconds 0 > "$OUT/${ctr}_cfg2.out" 2>&1
+        python3 bench.py --cold-only --steps 5 --warmup 2 --cpu-seconds 0 > "$OUT/${ctr}_cfg2.out" 2>&1
     step "$ctr: headline workload, non-causal"
     timeout -s KILL 200 rocprofv3 --pmc $ctr --kernel-include-regex "$KR" -f csv -d $OUT/${ctr}_nc -o run -- \
-        python3 bench.py --causal 0 --rows 0 --steps 5 --warmup 2 --cpu-seconds 0 > "$OUT/${ctr}_nc.out" 2>&1
+        python3 bench.py --causal 0 --cold-only --steps 5 --warmup 2 --cpu-seconds 0 > "$OUT/${ctr}_nc.out" 2>&1
     step "$ctr: decode"
     timeout -s KILL 300 rocprofv3 --pmc $ctr --kernel-include-regex "k_decode_step" -f csv -d $OUT/${ctr}_decode -o run -- \
         python3 bench.py --rows 1 --steps 5 --warmup 2 --cpu-seconds 0 > "$OUT/${ctr}_decode.out" 2>&1
     step "$ctr: copy calibration"
     timeout -s KILL 90 rocprofv3 --pmc $ctr -f csv -d $OUT/${ctr}_copy -o run -- \
-        python3 -m sequence_mixing_amd.calib_copy 256 > "$OUT/${ctr}_copy.out" 2>&1
+        python3 bench_calib_copy.py 256 > "$OUT/${ctr}_copy.out" 2>&1
 done
 
 step "counters: every workload"
@@ -54,21 +54,21 @@ timeout -s KILL 500 rocprofv3 --pmc $CTRS --kernel-include-regex "$KR|k_decode_s
     python3 bench.py --rows 1 --steps 5 --warmup 2 --cpu-seconds 0 > "$OUT/counters_all.out" 2>&1
 fi
 
-PMC="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --kernel-include-regex '<kernels>' -f csv -- python3 bench.py --steps 5 --warmup 2 --cpu-seconds 0 (--rows 0 headline, --causal 0 --rows 0 non-causal, --rows 1 decode); calibration: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 -m sequence_mixing_amd.calib_copy 256"
-python3 -m sequence_mixing_amd.profsum "$OUT/trace_all/run_kernel_stats.csv" "$C1" \
+PMC="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --kernel-include-regex '<kernels>' -f csv -- python3 bench.py --steps 5 --warmup 2 --cpu-seconds 0 (--cold-only headline, --causal 0 --cold-only non-causal, --rows 1 decode); calibration: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 bench_calib_copy.py 256"
+python3 bench_profsum.py "$OUT/trace_all/run_kernel_stats.csv" "$C1" \
     "all kernels of the default bench run (every workload row; bench JSON in the same run)" > "$OUT/kernels_all_workloads.txt"
-python3 -m sequence_mixing_amd.profsum "$OUT/trace_cfg2/run_kernel_stats.csv" "$C2" \
-    "headline workload: causal fp32 B2 H8 N4096 d64 (k_causal_chunks dominant)" > "$OUT/k_causal_chunks_f32_B2H8N4096d64.txt"
-python3 -m sequence_mixing_amd.profsum traffic cfg2 "$OUT/FETCH_SIZE_cfg2/run_counter_collection.csv" \
+python3 bench_profsum.py "$OUT/trace_cfg2/run_kernel_stats.csv" "$C2" \
+    "headline workload, cold launches only: causal fp32 B2 H8 N4096 d64 (k_causal_chunks dominant)" > "$OUT/k_causal_chunks_f32_B2H8N4096d64.txt"
+python3 bench_profsum.py traffic cfg2 "$OUT/FETCH_SIZE_cfg2/run_counter_collection.csv" \
     "$OUT/WRITE_SIZE_cfg2/run_counter_collection.csv" "$OUT/FETCH_SIZE_copy/run_counter_collection.csv" \
     "$OUT/WRITE_SIZE_copy/run_counter_collection.csv" 256 "$PMC" $SRC > "$OUT/traffic_cfg2_f32_B2H8N4096d64.txt"
-python3 -m sequence_mixing_amd.profsum traffic cfg2_noncausal "$OUT/FETCH_SIZE_nc/run_counter_collection.csv" \
+python3 bench_profsum.py traffic cfg2_noncausal "$OUT/FETCH_SIZE_nc/run_counter_collection.csv" \
     "$OUT/WRITE_SIZE_nc/run_counter_collection.csv" "$OUT/FETCH_SIZE_copy/run_counter_collection.csv" \
     "$OUT/WRITE_SIZE_copy/run_counter_collection.csv" 256 "$PMC" $SRC > "$OUT/traffic_cfg2_noncausal_f32_B2H8N4096d64.txt"
-python3 -m sequence_mixing_amd.profsum counters "$OUT/counters_all/run_counter_collection.csv" "$C3" \
+python3 bench_profsum.py counters "$OUT/counters_all/run_counter_collection.csv" "$C3" \
     "SQ counters per kernel over every workload of the default bench run (matrix-core use, waits, LDS)" \
     > "$OUT/counters_all_workloads.txt"
-python3 -m sequence_mixing_amd.profsum traffic decode "$OUT/FETCH_SIZE_decode/run_counter_collection.csv" \
+python3 bench_profsum.py traffic decode "$OUT/FETCH_SIZE_decode/run_counter_collection.csv" \
     "$OUT/WRITE_SIZE_decode/run_counter_collection.csv" "$OUT/FETCH_SIZE_copy/run_counter_collection.csv" \
     "$OUT/WRITE_SIZE_copy/run_counter_collection.csv" 256 "$PMC" $SRC > "$OUT/traffic_decode_bf16_B64H32Hkv8d128.txt"
 grep -h "^headline\|^cfg\|^decay\|^packed" "$OUT/trace_all.err" > "$OUT/bench_rows_under_trace.txt" || true

@@ -1,14 +1,14 @@
 """Short text summaries of rocprofv3 output.
 
-    python -m sequence_mixing_amd.profsum <kernel_stats.csv> "<command>" [title]
+    python bench_profsum.py <kernel_stats.csv> "<command>" [title]
         a ``--kernel-trace --stats`` kernel table.
-    python -m sequence_mixing_amd.profsum traffic <workload> <fetch.csv> <write.csv> <copy_fetch.csv> \
+    python bench_profsum.py traffic <workload> <fetch.csv> <write.csv> <copy_fetch.csv> \
             <copy_write.csv> <copy_MiB> "<commands>" <source files...>
         HBM bytes per launch of every kernel in a ``--pmc FETCH_SIZE`` and a
         ``--pmc WRITE_SIZE`` run, each counter scaled by what it reads for a
         plain copy of known size, plus a machine-readable line keyed by the
         SHA-256 of the kernel sources (a later source change voids it).
-    python -m sequence_mixing_amd.profsum counters <counters.csv> "<command>" [title]
+    python bench_profsum.py counters <counters.csv> "<command>" [title]
         per-kernel means of a ``--pmc`` run of SQ counters: matrix-core
         utilisation (MfmaUtil), matrix-core flops (MOPS x 512) over the
         dispatch time, and where the waves spend their cycles.

@@ -37,7 +37,13 @@
  *   - Errors: arguments are checked before anything is enqueued; a negative
  *     LINATTN_ERR_* code is returned and nothing is launched.  A failed
  *     kernel launch returns LINATTN_ERR_HIP.  The library never prints,
- *     aborts or throws.  NaN / Inf inputs are not checked and propagate.
+ *     aborts or throws.  NaN / Inf inputs are not checked and propagate: a
+ *     non-finite query spoils its own row; a non-finite key or value at
+ *     token s spoils the causal rows from s on (all rows when non-causal).
+ *     Rows before s stay finite, except that a non-finite VALUE may also
+ *     spoil the rows of its own 32-token tile (its pair of tiles, for chunk
+ *     kernels that keep one state copy per pair) that come before it: the
+ *     tile's values are multiplied by the masked (zero) scores.
  */
 #ifndef LINATTN_H
 #define LINATTN_H

@@ -77,7 +77,8 @@ int linattn_ref_set_feature_map(int kind)
 
 double linattn_ref_phi(double x)
 {
-    if (g_feature_map == 1) return x > 0.0 ? x : 0.0;
+    /* ReLU keeps a NaN input (non-finite inputs propagate through every map) */
+    if (g_feature_map == 1) return x > 0.0 || x != x ? x : 0.0;
     if (g_feature_map == 2) return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
     return x > 0.0 ? x + 1.0 : exp(x);
 }
@@ -325,7 +326,7 @@ int linattn_ref_decode_step_decay(double *state, double *z, const double *q, con
  * 0); ReLU: 1 for x > 0, else 0; softplus: the logistic function. */
 double linattn_ref_dphi(double x)
 {
-    if (g_feature_map == 1) return x > 0.0 ? 1.0 : 0.0;
+    if (g_feature_map == 1) return x > 0.0 ? 1.0 : (x != x ? x : 0.0);
     if (g_feature_map == 2) return 1.0 / (1.0 + exp(-x));
     return x > 0.0 ? 1.0 : exp(x);
 }

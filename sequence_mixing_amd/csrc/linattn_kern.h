@@ -65,20 +65,22 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // these two members plus a code in the dispatch.
 //
 // ELU(x) + 1 (alpha = 1), the README's phi: x + 1 for x > 0, exp(x) otherwise,
-// written without a branch as max(x, 0) + exp(min(x, 0)) (one v_exp_f32);
-// phi' = 1 for x > 0, exp(x) = phi otherwise, i.e. min(1, phi).
+// as a select between the two (one v_exp_f32, no branch); phi' = 1 for x > 0,
+// exp(x) = phi otherwise, i.e. min(1, phi).  Both are written so that NaN
+// propagates (a NaN input gives NaN: fmaxf / fminf would turn it into 0).
 struct PhiElu1 {
     static __device__ __forceinline__ float f(float x)
     {
-        return fmaxf(x, 0.f) + __builtin_amdgcn_exp2f(fminf(x, 0.f) * 1.44269504088896340736f);
+        const float e = __builtin_amdgcn_exp2f(x * 1.44269504088896340736f);
+        return x > 0.f ? x + 1.f : e;
     }
-    static __device__ __forceinline__ float df(float y) { return fminf(1.f, y); }
+    static __device__ __forceinline__ float df(float y) { return y >= 1.f ? 1.f : y; }
 };
 // ReLU: max(x, 0); phi' = 1 where phi > 0.  (A normalised row whose query or
-// keys are all <= 0 divides by zero.)
+// keys are all <= 0 divides by zero.)  NaN propagates through both.
 struct PhiRelu {
-    static __device__ __forceinline__ float f(float x) { return fmaxf(x, 0.f); }
-    static __device__ __forceinline__ float df(float y) { return y > 0.f ? 1.f : 0.f; }
+    static __device__ __forceinline__ float f(float x) { return x > 0.f || x != x ? x : 0.f; }
+    static __device__ __forceinline__ float df(float y) { return y > 0.f ? 1.f : (y == y ? 0.f : y); }
 };
 // softplus: log(1 + e^x) = max(x, 0) + log1p(e^-|x|); phi' = the logistic
 // function = 1 - e^-phi (written -expm1(-phi), exact for small phi).

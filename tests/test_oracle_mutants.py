@@ -125,8 +125,8 @@ MUTANTS = {
     "bwd_gradient_not_divided_by_denominator": lambda s: s.replace("gt[j] = dot[j] / den;", "gt[j] = dot[j];"),
     "softplus_positive_branch_sign": lambda s: s.replace("x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x))",
                                                          "x > 0.0 ? x + log1p(exp(x)) : log1p(exp(x))"),
-    "relu_keeps_negatives": lambda s: s.replace("if (g_feature_map == 1) return x > 0.0 ? x : 0.0;",
-                                                "if (g_feature_map == 1) return x > -0.5 ? x : 0.0;"),
+    "relu_keeps_negatives": lambda s: s.replace("if (g_feature_map == 1) return x > 0.0 || x != x ? x : 0.0;",
+                                                "if (g_feature_map == 1) return x > -0.5 || x != x ? x : 0.0;"),
     "softplus_derivative_sign": lambda s: s.replace("return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(x));"),
     "decay_applied_after_absorb": _decay_after_absorb,
     "decay_skips_z": lambda s: s.replace("S[(size_t)i * w + jj] *= a;\n                    z[i] *= a;",
