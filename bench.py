@@ -643,6 +643,57 @@ def decay_row(la, hip, torch, steps):
             "roofline_path": roofline(nbytes, 0.0, ms / 1e3, w.dtype, "whole decayed forward (graph replay, events)")}
 
 
+def window_row(la, hip, torch, steps, W=256):
+    """Sliding-window pass (band of W keys) on the bf16 B2 H8 N16384 d64 shape, replayed
+    from one HIP graph (warm), beside the plain causal pass of the same inputs."""
+    from linattn_inputs import WORKLOADS, workload_qkv
+
+    w = WORKLOADS["cfg3"]
+    q, k, v = (t.cuda() for t in workload_qkv(w))
+    out = torch.empty_like(q)
+    dt = la.LINATTN_BF16
+
+    def call(st):
+        rc = la.linattn_fwd_window(q, k, v, out, w.B, w.H, w.Hkv, w.N, w.d, W, 1, dt, st)
+        if rc != 0:
+            raise la.LinattnError(rc, "linattn_fwd_window")
+
+    ms, same = graph_ms(hip, torch, call, out, steps)
+    nb = fwd_bytes(w)
+    # the band's flops: per query-head token and key of its band, 2d for the score, 2d for the value
+    # product and 2 for the denominator (the masked half of the diagonal tile is not counted)
+    band = sum(min(t + 1, W) for t in range(w.N))
+    fl = float(w.B * w.H) * band * (4 * w.d + 2)
+    row = {"window": W, "workload": "bf16 B2 H8 N16384 d64", "ms_per_step": round(ms, 5),
+           "tokens_per_s": round(w.B * w.N / (ms / 1e3), 1), "graph_matches_eager": same,
+           "roofline_path": roofline(nb, fl, ms / 1e3, w.dtype, "k_window<bf16,64> (graph replay, warm)"),
+           "band_tflops": round(fl / (ms / 1e3) / 1e12, 2)}
+    del q, k, v, out
+    return row
+
+
+def window_oracle(seconds, W=256, max_tokens=2048):
+    """The oracle's band sum on the first tokens of every sequence of the window workload."""
+    import numpy as np
+
+    import oracle
+    from linattn_inputs import WORKLOADS, workload_qkv
+
+    w = WORKLOADS["cfg3"]
+    n = min(w.N, max_tokens)
+    q, k, v = (np.ascontiguousarray(t[:, :, :n].double().numpy()) for t in workload_qkv(w))
+    threads = oracle.default_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.ref_fwd_window(q, k, v, W, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    return {"value": round(w.B * n * reps / el, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {w.N} tokens of all {w.B * w.H} heads, W = {W}, {reps} reps in {el:.1f} s"}
+
+
 def decay_oracle(seconds, max_tokens=2048):
     """The fp64 oracle's decayed recurrence on the first tokens of every sequence of the
     decayed workload (the cost per token does not depend on the position)."""
@@ -941,6 +992,10 @@ def main():
         if args.cpu_seconds > 0:
             rows["decay"]["cpu_oracle"] = decay_oracle(min(2.0, args.cpu_seconds))
         log("decay", json.dumps(rows["decay"]))
+        rows["window"] = window_row(la, hip, torch, 20)
+        if args.cpu_seconds > 0:
+            rows["window"]["cpu_oracle"] = window_oracle(min(2.0, args.cpu_seconds))
+        log("window", json.dumps(rows["window"]))
         rows["packed"] = packed_row(la, hip, torch, 20)
         if args.cpu_seconds > 0:
             rows["packed"]["cpu_oracle"] = packed_oracle(min(2.0, args.cpu_seconds))

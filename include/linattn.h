@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 9
+#define LINATTN_ABI_VERSION 10
 
 enum { LINATTN_F32 = 0, LINATTN_BF16 = 1, LINATTN_F16 = 2 };
 /* Feature maps phi (README "Features": custom kernel plugins, phi
@@ -294,6 +294,25 @@ size_t linattn_fwd_decay_workspace_bytes(int B, int H, int Hkv, int N, int d, in
 int linattn_decode_step_decay(float *state, float *z, const void *q, const void *k, const void *v,
                               const float *gd, void *out, int B, int H, int Hkv, int d, int normalise,
                               int dtype, hipStream_t stream);
+
+/*
+ * linattn_fwd_window - causal forward pass over a sliding window of keys.
+ * The pages name a sliding window (LinearTile 1.0.0 README, "Features" list,
+ * sliding-window item: local context) without defining it; the reading taken
+ * is the causal band of `window` keys: query t sees keys t - window < s <= t,
+ *     o_t = sum_{band} (phi(q_t) . phi(k_s)) v_s / sum_{band} phi(q_t) . phi(k_s)
+ * (the numerator only when normalise == 0).  window >= N gives linattn_fwd's
+ * causal rows.  The band is formed directly (masked scores times values on the
+ * matrix cores), so the cost is O(N * min(window, N) * d) per query head and
+ * no running state is kept or returned.
+ *
+ *   q, out      device, dtype, [B][H][N][d];  k, v  device, dtype, [B][Hkv][N][d].
+ *   window      keys per band, >= 1.
+ * Other arguments, layouts and errors as for linattn_fwd; no workspace.
+ */
+int linattn_fwd_window(const void *q, const void *k, const void *v, void *out,
+                       int B, int H, int Hkv, int N, int d, int window, int normalise, int dtype,
+                       hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *linattn_status_string(int status);

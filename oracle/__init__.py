@@ -9,7 +9,9 @@ double precision), this module only converts arrays and calls it.
 Definition followed (LinearTile 1.0.0 README, "How It Works"; causal form
 from its "Features" list and Katharopoulos et al. 2020 cited under its
 "Reference" section): O = phi(Q) (phi(K)^T V), phi = ELU + 1, causal rows
-see keys s <= t, optional normaliser phi(q_t) . z_t.  The backward pass is the
+see keys s <= t, optional normaliser phi(q_t) . z_t.  The sliding window
+(a reading of the "Features" list's sliding-window item) restricts query t
+to the keys t - W < s <= t.  The backward pass is the
 chain rule on that definition, with the reverse-time walk of a running sum
 (Stream efficiency essay, section 4.2).  The decayed variant multiplies the
 running sums by exp(g_t) before token t is added, the essay's scan form
@@ -70,6 +72,8 @@ def _load():
         lib.linattn_ref_decode_step.argtypes = [dp] * 6 + [ctypes.c_int] * 5
         lib.linattn_ref_fwd_decay.restype = ctypes.c_int
         lib.linattn_ref_fwd_decay.argtypes = [dp] * 5 + [ctypes.c_int] * 6 + [dp] * 4 + [ctypes.c_int]
+        lib.linattn_ref_fwd_window.restype = ctypes.c_int
+        lib.linattn_ref_fwd_window.argtypes = [dp, dp, dp, dp] + [ctypes.c_int] * 8
         lib.linattn_ref_decode_step_decay.restype = ctypes.c_int
         lib.linattn_ref_decode_step_decay.argtypes = [dp] * 7 + [ctypes.c_int] * 5
         _lib = lib
@@ -154,6 +158,26 @@ def ref_fwd(q, k, v, causal: bool = True, normalise: bool = True,
     if rc != 0:
         raise ValueError(f"linattn_ref_fwd_from rejected its arguments (rc={rc})")
     return (out, S, z) if want_state else out
+
+
+def ref_fwd_window(q, k, v, window: int, normalise: bool = True, nthreads: int | None = None,
+                   phi_map: str = "elu1"):
+    """Sliding-window forward pass: query t sees keys t - window < s <= t.
+    q [B,H,N,d], k/v [B,Hkv,N,d] -> out [B,H,N,d] (fp64)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, d) and v.shape == (B, Hkv, N, d)
+    out = np.zeros((B, H, N, d), dtype=np.float64)
+    _use(phi_map)
+    try:
+        rc = _load().linattn_ref_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, N, d, int(window),
+                                            int(bool(normalise)), nthreads or default_threads())
+    finally:
+        _use("elu1")
+    if rc != 0:
+        raise ValueError(f"linattn_ref_fwd_window rejected its arguments (rc={rc})")
+    return out
 
 
 def ref_bwd(q, k, v, out, dout, causal: bool = True, normalise: bool = True, nthreads: int | None = None,

@@ -38,6 +38,12 @@
  *         S_t = a_t S_{t-1} + phi(k_t) v_t^T,   z_t = a_t z_{t-1} + phi(k_t),
  *     and o_t as above; causal only (linattn_ref_fwd_decay); decode likewise
  *     (linattn_ref_decode_step_decay).  g = 0 everywhere is the plain form.
+ *   - sliding window (a reading of the README's "Features" list, the
+ *     sliding-window item, which gives no definition): query t sees the keys
+ *     of the band t - W < s <= t only,
+ *         o_t = sum_{band} (phi(q_t) . phi(k_s)) v_s / sum_{band} phi(q_t) . phi(k_s)
+ *     (numerator only when normalise == 0), written out per query as that
+ *     sum (linattn_ref_fwd_window); W >= N is the causal form.
  *   - backward (the README's project layout names a backward module and its
  *     test without their content; the Stream efficiency essay, section 4.2,
  *     gives the pattern of a running-sum recurrence differentiated by a
@@ -493,6 +499,79 @@ int linattn_ref_bwd(const double *q, const double *k, const double *v, const dou
     }
     for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, bwd_worker, &jobs[t]);
     bwd_worker(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+    free(jobs);
+    free(th);
+    return 0;
+}
+
+/*
+ * Sliding-window forward pass (causal band of W keys): for every batch b,
+ * query head h and token t, with g = h / (H / Hkv),
+ *     num = sum_{s = max(0, t-W+1)}^{t} (phi(q_t) . phi(k_s)) v_s,
+ *     den = sum over the same s of phi(q_t) . phi(k_s),
+ *     out = num / den   (or num when normalise == 0).
+ * The band's sum is formed directly for each query (no running state), one
+ * key at a time.  Threads split the (batch, query head) pairs.  Returns 0, or
+ * -1 on invalid arguments (W < 1 included).
+ */
+typedef struct {
+    const double *q, *k, *v;
+    double *out;
+    int B, H, Hkv, N, d, W, normalise, nthreads, tid;
+} win_job;
+
+static void *win_worker(void *arg)
+{
+    const win_job *J = (const win_job *)arg;
+    const int d = J->d, N = J->N, G = J->H / J->Hkv;
+    double *pq = malloc((size_t)d * sizeof(double));
+    double *pk = malloc((size_t)d * sizeof(double));
+    double *num = malloc((size_t)d * sizeof(double));
+    for (int item = J->tid; item < J->B * J->H; item += J->nthreads) {
+        const int b = item / J->H, h = item % J->H, g = h / G;
+        for (int t = 0; t < N; ++t) {
+            const double *qt = J->q + (((size_t)b * J->H + h) * N + t) * d;
+            for (int i = 0; i < d; ++i) pq[i] = linattn_ref_phi(qt[i]);
+            for (int j = 0; j < d; ++j) num[j] = 0.0;
+            double den = 0.0;
+            const int s0 = t - J->W + 1 > 0 ? t - J->W + 1 : 0;
+            for (int s = s0; s <= t; ++s) {
+                const double *ks = J->k + (((size_t)b * J->Hkv + g) * N + s) * d;
+                const double *vs = J->v + (((size_t)b * J->Hkv + g) * N + s) * d;
+                for (int i = 0; i < d; ++i) pk[i] = linattn_ref_phi(ks[i]);
+                double a = 0.0;
+                for (int i = 0; i < d; ++i) a += pq[i] * pk[i];
+                for (int j = 0; j < d; ++j) num[j] += a * vs[j];
+                den += a;
+            }
+            double *ot = J->out + (((size_t)b * J->H + h) * N + t) * d;
+            for (int j = 0; j < d; ++j) ot[j] = J->normalise ? num[j] / den : num[j];
+        }
+    }
+    free(pq);
+    free(pk);
+    free(num);
+    return NULL;
+}
+
+int linattn_ref_fwd_window(const double *q, const double *k, const double *v, double *out,
+                           int B, int H, int Hkv, int N, int d, int W, int normalise, int nthreads)
+{
+    if (!q || !k || !v || !out) return -1;
+    if (B < 0 || H <= 0 || Hkv <= 0 || N < 0 || d <= 0 || H % Hkv != 0 || W < 1) return -1;
+    if (B == 0 || N == 0) return 0;
+    const int nitems = B * H;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > nitems) nthreads = nitems;
+    win_job *jobs = malloc((size_t)nthreads * sizeof(win_job));
+    pthread_t *th = malloc((size_t)nthreads * sizeof(pthread_t));
+    for (int t = 0; t < nthreads; ++t) {
+        win_job J = {q, k, v, out, B, H, Hkv, N, d, W, normalise, nthreads, t};
+        jobs[t] = J;
+    }
+    for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, win_worker, &jobs[t]);
+    win_worker(&jobs[0]);
     for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
     free(jobs);
     free(th);

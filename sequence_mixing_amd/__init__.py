@@ -18,7 +18,7 @@ __all__ = [
     "LINATTN_F32", "LINATTN_BF16", "LINATTN_F16", "LINATTN_OK", "LinattnError", "library_path", "load",
     "linattn_fwd", "linattn_fwd_from_state", "linattn_fwd_timed", "linattn_fwd_workspace_bytes", "linattn_fwd_plan", "linattn_decode_step",
     "linattn_status_string", "linattn_abi_version", "linattn_bwd", "linattn_bwd_workspace_bytes",
-    "linattn_fwd_packed", "linattn_fwd_packed_workspace_bytes", "linattn_fwd_noalloc",
+    "linattn_fwd_packed", "linattn_fwd_packed_workspace_bytes", "linattn_fwd_noalloc", "linattn_fwd_window",
     "LINATTN_NOALLOC_SCRATCH_BYTES",
 ]
 
@@ -70,6 +70,8 @@ def load():
         lib.linattn_fwd_workspace_bytes.argtypes = [i] * 8
         lib.linattn_fwd_plan.restype = i
         lib.linattn_fwd_plan.argtypes = [i] * 8 + [ctypes.POINTER(i), ctypes.POINTER(i)]
+        lib.linattn_fwd_window.restype = i
+        lib.linattn_fwd_window.argtypes = [vp] * 4 + [i] * 8 + [vp]
         lib.linattn_decode_step.restype = i
         lib.linattn_decode_step.argtypes = [vp] * 6 + [i] * 6 + [vp]
         lib.linattn_fwd_packed.restype = i
@@ -157,6 +159,12 @@ def linattn_fwd_plan(B, H, Hkv, N, d, causal, dtype, chunk=0):
     c, p = ctypes.c_int(0), ctypes.c_int(0)
     rc = load().linattn_fwd_plan(B, H, Hkv, N, d, int(causal), dtype, chunk, ctypes.byref(c), ctypes.byref(p))
     return rc, c.value, p.value
+
+
+def linattn_fwd_window(q, k, v, out, B, H, Hkv, N, d, window, normalise, dtype, stream=None) -> int:
+    """C ``linattn_fwd_window``; returns the status code (0 = ok)."""
+    return load().linattn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, N, d, int(window),
+                                     int(normalise), dtype, _stream(stream))
 
 
 def linattn_decode_step(state, z, q, k, v, out, B, H, Hkv, d, normalise, dtype, stream=None) -> int:

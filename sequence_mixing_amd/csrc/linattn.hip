@@ -66,6 +66,18 @@ int decode_dispatch(int dtype, const linattn::DecodeCall &c)
     return LINATTN_ERR_DTYPE;
 }
 
+int window_dispatch(int dtype, const linattn::WindowCall &c)
+{
+    if (!valid_dtype(dtype)) return LINATTN_ERR_DTYPE;
+    switch (dtype) {
+#define LINATTN_CASE(PHI, ELEM) \
+    case (PHI << 8) | ELEM: return linattn::window_format<PHI, ELEM>(c);
+        LINATTN_FORMATS(LINATTN_CASE)
+#undef LINATTN_CASE
+    }
+    return LINATTN_ERR_DTYPE;
+}
+
 }  // namespace
 
 // =================================================================== C ABI
@@ -312,6 +324,22 @@ int linattn_decode_step(float *state, float *z, const void *q, const void *k, co
                         int Hkv, int d, int normalise, int dtype, hipStream_t stream)
 {
     return decode_impl(state, z, q, k, v, nullptr, out, B, H, Hkv, d, normalise, dtype, stream);
+}
+
+int linattn_fwd_window(const void *q, const void *k, const void *v, void *out, int B, int H, int Hkv, int N, int d,
+                       int window, int normalise, int dtype, hipStream_t stream)
+{
+    if (!valid_dtype(dtype)) return LINATTN_ERR_DTYPE;
+    if (B < 0 || H <= 0 || Hkv <= 0 || N < 0 || H % Hkv != 0 || window < 1) return LINATTN_ERR_SHAPE;
+    if (d != 32 && d != 64 && d != 128) return LINATTN_ERR_UNSUPPORTED;
+    if ((int64_t)N * d > INT32_MAX / 4) return LINATTN_ERR_SHAPE;  // byte offsets of one head stay 32-bit
+    const int64_t blocks = (int64_t)B * H * ((N + 127) / 128);
+    if (blocks > INT32_MAX) return LINATTN_ERR_SHAPE;
+    if (B == 0 || N == 0) return LINATTN_OK;
+    if (!q || !k || !v || !out) return LINATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LINATTN_ERR_ALIGN;
+    const linattn::WindowCall c{q, k, v, out, B, H, Hkv, N, d, window, normalise ? 1 : 0, stream};
+    return window_dispatch(dtype, c);
 }
 
 int linattn_decode_step_decay(float *state, float *z, const void *q, const void *k, const void *v, const float *g,

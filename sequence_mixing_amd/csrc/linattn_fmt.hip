@@ -41,6 +41,7 @@
 #include "linattn_fwd.h"
 #include "linattn_kern.h"
 #include "linattn_plan.h"
+#include "linattn_window.h"
 
 #if !defined(LINATTN_FMT_PHI) || !defined(LINATTN_FMT_ELEM)
 #error "built once per format: -DLINATTN_FMT_PHI=<LINATTN_PHI_*> -DLINATTN_FMT_ELEM=<LINATTN_F32|BF16|F16>"
@@ -1133,6 +1134,13 @@ template <>
 int decode_format<LINATTN_FMT_PHI, LINATTN_FMT_ELEM>(const DecodeCall &c)
 {
     return run_decode<K::T, K::IO>(c.state, c.z, c.q, c.k, c.v, c.g, c.out, c.B, c.H, c.Hkv, c.d, c.normalise,
+                                   c.stream);
+}
+
+template <>
+int window_format<LINATTN_FMT_PHI, LINATTN_FMT_ELEM>(const WindowCall &c)
+{
+    return run_window<K::T, K::IO>(c.q, c.k, c.v, c.out, c.B, c.H, c.Hkv, c.N, c.d, c.window, c.normalise,
                                    c.stream);
 }
 

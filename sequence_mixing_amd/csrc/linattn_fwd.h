@@ -50,10 +50,19 @@ struct DecodeCall {
     hipStream_t stream;
 };
 
+// One sliding-window forward pass (arguments checked by the caller).
+struct WindowCall {
+    const void *q, *k, *v;
+    void *out;
+    int B, H, Hkv, N, d, window, normalise;
+    hipStream_t stream;
+};
+
 // PHI: LINATTN_PHI_*; ELEM: LINATTN_F32 / LINATTN_BF16 / LINATTN_F16.  Each
 // pair is defined in the object built from linattn_fmt.hip with
 // -DLINATTN_FMT_PHI=PHI -DLINATTN_FMT_ELEM=ELEM.
 template <int PHI, int ELEM> int fwd_format(const FwdCall &c);
 template <int PHI, int ELEM> int decode_format(const DecodeCall &c);
+template <int PHI, int ELEM> int window_format(const WindowCall &c);
 
 }  // namespace linattn

@@ -7,7 +7,7 @@ from __future__ import annotations
 import torch
 
 from . import (LINATTN_BF16, LINATTN_F16, LINATTN_F32, LinattnError, linattn_bwd, linattn_bwd_workspace_bytes,
-               linattn_fwd_plan,
+               linattn_fwd_plan, linattn_fwd_window,
                linattn_decode_step, linattn_decode_step_decay, linattn_fwd, linattn_fwd_decay,
                linattn_fwd_decay_workspace_bytes, linattn_fwd_from_state, linattn_fwd_packed,
                linattn_fwd_packed_workspace_bytes, linattn_fwd_workspace_bytes)
@@ -110,6 +110,23 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=True, normalis
     if rc != 0:
         raise LinattnError(rc, "linattn_fwd")
     return (out, S, z) if want_state else out
+
+
+def fwd_window(q, k, v, window, normalise=True, out=None, stream=None, phi="elu1"):
+    """Sliding-window causal pass through ``linattn_fwd_window``: query t sees keys
+    t - window < s <= t; q [B,H,N,d], k/v [B,Hkv,N,d] on the GPU."""
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    for t in (q, k, v):
+        if not (t.is_cuda and t.is_contiguous() and t.dtype == q.dtype and t.device == q.device):
+            raise ValueError("q, k, v must be contiguous device tensors of one dtype on one device")
+    if k.shape != (B, Hkv, N, d) or v.shape != (B, Hkv, N, d):
+        raise ValueError("k and v must be [B, Hkv, N, d]")
+    out = _check_out(out, q)
+    rc = linattn_fwd_window(q, k, v, out, B, H, Hkv, N, d, window, normalise, dtype_code(q.dtype, phi), stream)
+    if rc != 0:
+        raise LinattnError(rc, "linattn_fwd_window")
+    return out
 
 
 def fwd_decay(q, k, v, g, normalise=True, chunk=0, want_state=False, out=None, ws=None, stream=None, state_in=None,

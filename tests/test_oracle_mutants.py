@@ -128,6 +128,9 @@ MUTANTS = {
     "relu_keeps_negatives": lambda s: s.replace("if (g_feature_map == 1) return x > 0.0 || x != x ? x : 0.0;",
                                                 "if (g_feature_map == 1) return x > -0.5 || x != x ? x : 0.0;"),
     "softplus_derivative_sign": lambda s: s.replace("return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(x));"),
+    "window_one_key_too_many": lambda s: s.replace("const int s0 = t - J->W + 1 > 0 ? t - J->W + 1 : 0;",
+                                                   "const int s0 = t - J->W > 0 ? t - J->W : 0;"),
+    "window_without_diagonal": lambda s: s.replace("for (int s = s0; s <= t; ++s) {", "for (int s = s0; s < t; ++s) {"),
     "decay_applied_after_absorb": _decay_after_absorb,
     "decay_skips_z": lambda s: s.replace("S[(size_t)i * w + jj] *= a;\n                    z[i] *= a;",
                                          "S[(size_t)i * w + jj] *= a;\n"),
@@ -153,6 +156,7 @@ def test_pins_catch_mutant(name, tmp_path):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle.py"), os.path.join(ROOT, "tests", "test_oracle_bwd.py"),
                         os.path.join(ROOT, "tests", "test_oracle_phi.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_decay.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_decay.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_window.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the oracle pins:\n{r.stdout[-2000:]}"
