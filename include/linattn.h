@@ -26,12 +26,19 @@
  *     [B][Hkv][N][d]; a state S [B][Hkv][d][d] with S[i][j] = sum phi(k)_i v_j;
  *     a normaliser z [B][Hkv][d].
  *   - q, k, v and out share `dtype` (LINATTN_F32, LINATTN_BF16 or
- *     LINATTN_F16; README "Features": mixed precision).  Arithmetic
+ *     LINATTN_F16; README "Features": mixed precision), except that fp8 rows
+ *     (LINATTN_FP8_E4M3, LINATTN_FP8_E5M2: the OCP 8-bit formats, E4M3 with
+ *     no infinities and largest value 448, E5M2 IEEE-like) are inputs only:
+ *     with an fp8 dtype, q, k and v are fp8 and out is bf16.  fp8 rows are
+ *     taken by linattn_fwd, linattn_fwd_from_state, linattn_fwd_packed,
+ *     linattn_fwd_noalloc, linattn_fwd_window and linattn_decode_step (the
+ *     backward and the decayed sums return LINATTN_ERR_UNSUPPORTED).  Arithmetic
  *     accumulates in fp32 and the state is always fp32.  fp16 rows are read
  *     and written as fp16 and enter the matrix cores as bf16, like bf16 rows
  *     (bf16 keeps fp32's exponent range, so the operand copies of the running
- *     sums, which grow with the sequence, cannot overflow as fp16 would).  The
- *     output is rounded once, to nearest even, when stored.
+ *     sums, which grow with the sequence, cannot overflow as fp16 would); fp8
+ *     rows likewise, widened exactly to bf16 when staged.  The output is
+ *     rounded once, to nearest even, when stored.
  *   - Supported: d in {32, 64, 128}; H % Hkv == 0; every pointer 16-byte
  *     aligned; out must not alias q, k or v.
  *   - Errors: arguments are checked before anything is enqueued; a negative
@@ -55,9 +62,9 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 10
+#define LINATTN_ABI_VERSION 11
 
-enum { LINATTN_F32 = 0, LINATTN_BF16 = 1, LINATTN_F16 = 2 };
+enum { LINATTN_F32 = 0, LINATTN_BF16 = 1, LINATTN_F16 = 2, LINATTN_FP8_E4M3 = 3, LINATTN_FP8_E5M2 = 4 };
 /* Feature maps phi (README "Features": custom kernel plugins, phi
  * replaceable): ELU(x) + 1 (the README's, the default), ReLU(x) (a normalised
  * row whose query or keys are all <= 0 divides by zero), softplus(x) =

@@ -9,8 +9,9 @@ Recipe (no dataset is involved; the pages measure on none):
   * generator: ``torch.Generator('cpu').manual_seed(seed)``;
   * prefill: draw fp32 ``randn`` for Q [B,H,N,d], then K [B,Hkv,N,d], then
     V [B,Hkv,N,d]; bf16 (or fp16) workloads round each with
-    round-to-nearest-even (``.to(torch.bfloat16)``), and the oracle reads the
-    rounded values;
+    round-to-nearest-even (``.to(torch.bfloat16)``), fp8 workloads likewise
+    to the OCP E4M3 or E5M2 format (``torch.float8_e4m3fn`` / ``float8_e5m2``),
+    and the oracle reads the rounded values;
   * decode: one generator per run, step-major: for every step draw q [B,H,d],
     then k [B,Hkv,d], then v [B,Hkv,d];
   * packed batches: sequence lengths log-uniform in [lo, hi] from their own
@@ -26,7 +27,8 @@ from dataclasses import dataclass
 
 import torch
 
-DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
+          "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
 
 
 @dataclass(frozen=True)

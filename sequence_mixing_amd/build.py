@@ -25,7 +25,7 @@ FLAGS = [
 # (source, extra defines): the forward/decode kernels are built once per
 # (feature map, element type), so the objects compile in parallel.
 _PHIS = ["LINATTN_PHI_ELU1", "LINATTN_PHI_RELU", "LINATTN_PHI_SOFTPLUS"]
-_ELEMS = ["LINATTN_F32", "LINATTN_BF16", "LINATTN_F16"]
+_ELEMS = ["LINATTN_F32", "LINATTN_BF16", "LINATTN_F16", "LINATTN_FP8_E4M3", "LINATTN_FP8_E5M2"]
 SOURCES = [(os.path.join(CSRC, "linattn_fmt.hip"), [f"-DLINATTN_FMT_PHI={p}", f"-DLINATTN_FMT_ELEM={e}"])
            for p in _PHIS for e in _ELEMS] + [
     (os.path.join(CSRC, "linattn_bwd.hip"), []), (os.path.join(CSRC, "linattn.hip"), []),

@@ -34,12 +34,18 @@ __global__ void k_fill_copy(float *__restrict__ p, const float *__restrict__ src
     X(LINATTN_PHI_ELU1, LINATTN_F32)                                                                           \
     X(LINATTN_PHI_ELU1, LINATTN_BF16)                                                                          \
     X(LINATTN_PHI_ELU1, LINATTN_F16)                                                                           \
+    X(LINATTN_PHI_ELU1, LINATTN_FP8_E4M3)                                                                      \
+    X(LINATTN_PHI_ELU1, LINATTN_FP8_E5M2)                                                                      \
     X(LINATTN_PHI_RELU, LINATTN_F32)                                                                           \
     X(LINATTN_PHI_RELU, LINATTN_BF16)                                                                          \
     X(LINATTN_PHI_RELU, LINATTN_F16)                                                                           \
+    X(LINATTN_PHI_RELU, LINATTN_FP8_E4M3)                                                                      \
+    X(LINATTN_PHI_RELU, LINATTN_FP8_E5M2)                                                                      \
     X(LINATTN_PHI_SOFTPLUS, LINATTN_F32)                                                                       \
     X(LINATTN_PHI_SOFTPLUS, LINATTN_BF16)                                                                      \
-    X(LINATTN_PHI_SOFTPLUS, LINATTN_F16)
+    X(LINATTN_PHI_SOFTPLUS, LINATTN_F16)                                                                       \
+    X(LINATTN_PHI_SOFTPLUS, LINATTN_FP8_E4M3)                                                                  \
+    X(LINATTN_PHI_SOFTPLUS, LINATTN_FP8_E5M2)
 
 // dtype: element type in bits 0-7, feature map in bits 8-15
 int fwd_dispatch(int dtype, const linattn::FwdCall &c)

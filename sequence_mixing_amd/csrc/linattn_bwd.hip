@@ -268,14 +268,14 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
             if (BG::NGRP % BG::TH == 0 || e < BG::NGRP) {
                 float bk[U];
 #pragma unroll
-                for (int i = 0; i < U; ++i) bk[i] = t < rows ? IO::phi::f(Io<T, IO>::f(kr[l][i])) : 0.f;
+                for (int i = 0; i < U; ++i) bk[i] = t < rows ? IO::phi::f(Io<T, IO>::fi(kr[l], i)) : 0.f;
                 sB.write16(t, cq, to_g16<T>(bk));
                 if constexpr (SPLIT) sBl.write16(t, cq, to_g16_lo<T>(bk));
                 sV.write16(t, cq, op16<T, IO>(vr[l]));
                 if constexpr (SPLITV) {
                     float vf[U];
 #pragma unroll
-                    for (int ii = 0; ii < U; ++ii) vf[ii] = Io<T, IO>::f(vr[l][ii]);
+                    for (int ii = 0; ii < U; ++ii) vf[ii] = Io<T, IO>::fi(vr[l], ii);
                     sVl.write16(t, cq, to_g16_lo<T>(vf));
                 }
             }
@@ -314,8 +314,8 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
                     float a[U], den = 0.f, dov = 0.f;
 #pragma unroll
                     for (int i = 0; i < U; ++i) {
-                        a[i] = IO::phi::f(Io<T, IO>::f(qr[l][i]));
-                        dov += Io<T, IO>::f(dr[l][i]) * Io<T, IO>::f(orr[l][i]);
+                        a[i] = IO::phi::f(Io<T, IO>::fi(qr[l], i));
+                        dov += Io<T, IO>::fi(dr[l], i) * Io<T, IO>::fi(orr[l], i);
                     }
                     if (grp) {
 #pragma unroll
@@ -326,7 +326,7 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
                     const float inv = t < rows ? (normalise ? 1.f / den : 1.f) : 0.f;
                     float gg[U];
 #pragma unroll
-                    for (int i = 0; i < U; ++i) gg[i] = Io<T, IO>::f(dr[l][i]) * inv;
+                    for (int i = 0; i < U; ++i) gg[i] = Io<T, IO>::fi(dr[l], i) * inv;
                     if (grp) {
                         sA.write16(t, cq, to_g16<T>(a));
                         sG.write16(t, cq, to_g16<T>(gg));
@@ -508,7 +508,7 @@ __global__ __launch_bounds__((BGeo<T, D, DKV_WAVES(D, TOTALS)>::TH), (BGeo<T, D,
                 if (BG::NGRP % BG::TH == 0 || e < BG::NGRP) {
                     float bk[U];
 #pragma unroll
-                    for (int i = 0; i < U; ++i) bk[i] = t < rows ? IO::phi::f(Io<T, IO>::f(kr[l][i])) : 0.f;
+                    for (int i = 0; i < U; ++i) bk[i] = t < rows ? IO::phi::f(Io<T, IO>::fi(kr[l], i)) : 0.f;
                     sB.write16(t, cq, to_g16<T>(bk));
                     sV.write16(t, cq, op16<T, IO>(vr[l]));
                 }
@@ -536,9 +536,9 @@ __global__ __launch_bounds__((BGeo<T, D, DKV_WAVES(D, TOTALS)>::TH), (BGeo<T, D,
                 float a[U], gg[U], dov = 0.f;
 #pragma unroll
                 for (int i = 0; i < U; ++i) {
-                    a[i] = real ? IO::phi::f(Io<T, IO>::f(qr[l][i])) : 0.f;
-                    gg[i] = Io<T, IO>::f(dr[l][i]) * inv;
-                    dov += Io<T, IO>::f(dr[l][i]) * Io<T, IO>::f(orr[l][i]);
+                    a[i] = real ? IO::phi::f(Io<T, IO>::fi(qr[l], i)) : 0.f;
+                    gg[i] = Io<T, IO>::fi(dr[l], i) * inv;
+                    dov += Io<T, IO>::fi(dr[l], i) * Io<T, IO>::fi(orr[l], i);
                 }
                 dov = row_sum<GPR>(dov);
                 if (BG::NGRP % BG::TH == 0 || e < BG::NGRP) {
@@ -689,6 +689,8 @@ int bwd_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, BwdPlan
     if (B < 0 || H <= 0 || Hkv <= 0 || N < 0 || H % Hkv != 0) return LINATTN_ERR_SHAPE;
     if (!valid_dtype(dtype)) return LINATTN_ERR_DTYPE;
     if (d != 32 && d != 64 && d != 128) return LINATTN_ERR_UNSUPPORTED;
+    // fp8 rows are forward inputs only (their gradients would be written as fp8)
+    if ((dtype & 0xff) == LINATTN_FP8_E4M3 || (dtype & 0xff) == LINATTN_FP8_E5M2) return LINATTN_ERR_UNSUPPORTED;
     const int e = (dtype & 0xff) != LINATTN_F32 ? 2 : 4;
     if ((long long)N * d * e > 0x7fffffffLL) return LINATTN_ERR_SHAPE;
     BwdPlan p{};
@@ -727,14 +729,16 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
     const int c1 = totals_chunk<T, D>(pl.seg_len);
     // 1. forward sums at the segment starts (or their total)
     if (causal) {
-        if (P > 1 && launch_totals<T, D, IO>(c1, pl.nseq * (P - 1), st, kk, vv, wf, N, pl.seg_len, P - 1))
+        if (P > 1 && launch_totals<T, D, IO>(c1, pl.nseq * (P - 1), st, in_ptr<IO>(kk), in_ptr<IO>(vv), wf, N,
+                                              pl.seg_len, P - 1))
             return LINATTN_ERR_UNSUPPORTED;
         if (P > 2)
             hipLaunchKernelGGL(k_seg_scan, scan_grid(D, pl.nseq), dim3(kThreads), 0, st, wf,
                                P - 1, D, 0, (float *)nullptr, (float *)nullptr, (const float *)nullptr,
                                (const float *)nullptr);
     } else {
-        if (launch_totals<T, D, IO>(c1, pl.nseq * P, st, kk, vv, wf, N, pl.seg_len, P)) return LINATTN_ERR_UNSUPPORTED;
+        if (launch_totals<T, D, IO>(c1, pl.nseq * P, st, in_ptr<IO>(kk), in_ptr<IO>(vv), wf, N, pl.seg_len, P))
+            return LINATTN_ERR_UNSUPPORTED;
         hipLaunchKernelGGL(k_seg_scan, scan_grid(D, pl.nseq), dim3(kThreads), 0, st, wf, P, D,
                            1, (float *)nullptr, (float *)nullptr, (const float *)nullptr, (const float *)nullptr);
     }

@@ -111,7 +111,8 @@ struct Main {
 // scores within and next to the diagonal, and the state copy each query reads.
 template <typename T, int D, int C, int GT, typename IO, bool DK = false>
 __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) void k_causal_chunks(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ out,
+    const typename IO::elem *__restrict__ q, const typename IO::elem *__restrict__ k,
+    const typename IO::elem *__restrict__ v, T *__restrict__ out,
     const float *__restrict__ ws, float *__restrict__ state_out, float *__restrict__ z_out,
     int H, int Hkv, int N, int G, int P, int seg_len, int normalise, const float *__restrict__ s_in,
     const float *__restrict__ z_in, Packed pk, const float *__restrict__ gd = nullptr)
@@ -165,9 +166,10 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         slot0 = packed_slot0(r, gk, Hkv, 1);
     }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
-    const T *kb = k + kbase;
-    const T *vb = v + kbase;
-    const T *qb = q + qbase;
+    using In = typename IO::elem;
+    const In *kb = k + kbase;
+    const In *vb = v + kbase;
+    const In *qb = q + qbase;
     T *ob = out + qbase;
     const int s0 = p * seg_len, s1 = min(N, s0 + seg_len);
     const int nch = (s1 - s0 + C - 1) / C;
@@ -196,16 +198,18 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
     }
     // ---- staging: raw K, V, q of a chunk in registers, one chunk ahead
     // Raw K, V, q of the next chunk in registers: loaded one chunk ahead.
-    constexpr int E = (int)sizeof(T);
+    // E: bytes of an output element; IE, GB: of an input element and of a raw
+    // input group (they differ for fp8 rows, whose output is bf16).
+    constexpr int E = (int)sizeof(T), IE = Io<T, IO>::EB, GB = Io<T, IO>::GB;
     struct Regs {
         g16 k[M::LK], v[M::LK], q[M::LQ];
         float g;  // DK: log-decay of token t0 + tid
     };
     const float *gb = DK ? gd + (size_t)seq * N : nullptr;
     Regs ra;
-    // q / out group l of this thread: byte offset from (head block, token t0)
-    // and its token row within the chunk (qt = C marks a group past the block).
-    unsigned qoff[M::LQ];
+    // q / out group l of this thread: element offset from (head block, token
+    // t0) and its token row within the chunk (qt = C marks a group past the block).
+    unsigned qel[M::LQ];
     int qt[M::LQ];
 #pragma unroll
     for (int l = 0; l < M::LQ; ++l) {
@@ -213,7 +217,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         const int row = e / GPR, qq = e % GPR;
         const int g = row / C, t = row % C;
         const bool in = M::QG % TH == 0 || e < M::QG;
-        qoff[l] = (unsigned)((g * N + t) * D + qq * U) * E;
+        qel[l] = (unsigned)((g * N + t) * D + qq * U);
         qt[l] = in ? t : C;
     }
     const int qspan = GT * N * D;  // elements of the head block's q (and out)
@@ -222,20 +226,20 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
     auto rows_at = [&](int t0) { return t0 < s1 ? min(C, N - t0) : 0; };
     auto load_kv = [&](Regs &r, int t0) {
         const int rows = rows_at(t0);
-        const Rsrc rk = make_rsrc(kb + (size_t)t0 * D, rows * D * E);
-        const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, rows * D * E);
+        const Rsrc rk = make_rsrc(kb + (size_t)t0 * D, rows * D * IE);
+        const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, rows * D * IE);
 #pragma unroll
         for (int l = 0; l < M::LK; ++l) {
-            const unsigned off = (unsigned)(tid + l * TH) * 16u;
-            r.k[l] = buf_load16<g16>(rk, off);
-            r.v[l] = buf_load16<g16>(rv, off);
+            const unsigned off = (unsigned)(tid + l * TH) * GB;
+            r.k[l] = load_in<T, IO>(rk, off);
+            r.v[l] = load_in<T, IO>(rv, off);
         }
     };
     auto load_q = [&](Regs &r, int t0) {
         const int rows = rows_at(t0);
-        const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, rows ? (qspan - t0 * D) * E : 0);
+        const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, rows ? (qspan - t0 * D) * IE : 0);
 #pragma unroll
-        for (int l = 0; l < M::LQ; ++l) r.q[l] = buf_load16<g16>(rq, qt[l] < rows ? qoff[l] : kOutOfRange);
+        for (int l = 0; l < M::LQ; ++l) r.q[l] = load_in<T, IO>(rq, qt[l] < rows ? qel[l] * IE : kOutOfRange);
     };
     auto load_all = [&](Regs &r, int t0) {
         load_kv(r, t0);
@@ -257,7 +261,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         const int rows = min(C, N - t_prev);
         const Rsrc ro = make_rsrc(ob + (size_t)t_prev * D, (qspan - t_prev * D) * E);
 #pragma unroll
-        for (int l = 0; l < M::LQ; ++l) buf_store16<g16>(ro, qt[l] < rows ? qoff[l] : kOutOfRange, o[l]);
+        for (int l = 0; l < M::LQ; ++l) buf_store16<g16>(ro, qt[l] < rows ? qel[l] * E : kOutOfRange, o[l]);
     };
     // phi(q) of the staged chunk into the q rows.
     auto stage_q = [&](const Regs &r) {
@@ -268,7 +272,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                 const int row = e / GPR, qq = e % GPR;
                 g16 fq;
 #pragma unroll
-                for (int i = 0; i < U; ++i) fq[i] = (T)IO::phi::f(Io<T, IO>::f(r.q[l][i]));
+                for (int i = 0; i < U; ++i) fq[i] = (T)IO::phi::f(Io<T, IO>::fi(r.q[l], i));
                 sQ.write16(row, qq * U, fq);
             }
         }
@@ -553,28 +557,28 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
             constexpr int NSET = sizeof(T) == 2 ? 2 : 1;  // register sets of chunks in flight
             static_assert(NSET == 2 || M::NST <= NC * M::MAXST, "one set: the state tiles sit on the first half");
             PSet sa, sb;  // two sets: sa holds the even chunks, sb the odd ones
-            unsigned pqoff[LQP];
+            unsigned pqel[LQP];  // element offsets, as qel above
             int pqt[LQP];
 #pragma unroll
             for (int l = 0; l < LQP; ++l) {
                 const int e = pt + l * PTH;
                 const int row = e / GPR, qq = e % GPR;
-                pqoff[l] = (unsigned)(((row / C) * N + row % C) * D + qq * U) * E;
+                pqel[l] = (unsigned)(((row / C) * N + row % C) * D + qq * U);
                 pqt[l] = (M::QG % PTH == 0 || e < M::QG) ? row % C : C;
             }
             auto p_load = [&](PSet &r, int t0) {
                 const int rows = rows_at(t0);
-                const Rsrc rk = make_rsrc(kb + (size_t)t0 * D, rows * D * E);
-                const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, rows * D * E);
+                const Rsrc rk = make_rsrc(kb + (size_t)t0 * D, rows * D * IE);
+                const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, rows * D * IE);
 #pragma unroll
                 for (int l = 0; l < LKP; ++l) {
-                    const unsigned off = (unsigned)(pt + l * PTH) * 16u;
-                    r.k[l] = buf_load16<g16>(rk, off);
-                    r.v[l] = buf_load16<g16>(rv, off);
+                    const unsigned off = (unsigned)(pt + l * PTH) * GB;
+                    r.k[l] = load_in<T, IO>(rk, off);
+                    r.v[l] = load_in<T, IO>(rv, off);
                 }
-                const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, rows ? (qspan - t0 * D) * E : 0);
+                const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, rows ? (qspan - t0 * D) * IE : 0);
 #pragma unroll
-                for (int l = 0; l < LQP; ++l) r.q[l] = buf_load16<g16>(rq, pqt[l] < rows ? pqoff[l] : kOutOfRange);
+                for (int l = 0; l < LQP; ++l) r.q[l] = load_in<T, IO>(rq, pqt[l] < rows ? pqel[l] * IE : kOutOfRange);
             };
             auto p_stage_kv = [&](const PSet &r, int b, int rows) {
                 stage_rows<T, D, C, PTH, IO>(r.k, r.v, Tile<T, D>{smK[b]}, Tile<T, D>{smV[b]}, rows, pt);
@@ -587,7 +591,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                     if (M::QG % PTH == 0 || e < M::QG) {
                         g16 fq;
 #pragma unroll
-                        for (int i = 0; i < U; ++i) fq[i] = (T)IO::phi::f(Io<T, IO>::f(r.q[l][i]));
+                        for (int i = 0; i < U; ++i) fq[i] = (T)IO::phi::f(Io<T, IO>::fi(r.q[l], i));
                         tq.write16(e / GPR, (e % GPR) * U, fq);
                     }
                 }
@@ -605,7 +609,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                 const int rows = min(C, N - t_prev);
                 const Rsrc ro = make_rsrc(ob + (size_t)t_prev * D, (qspan - t_prev * D) * E);
 #pragma unroll
-                for (int l = 0; l < LQP; ++l) buf_store16<g16>(ro, pqt[l] < rows ? pqoff[l] : kOutOfRange, o[l]);
+                for (int l = 0; l < LQP; ++l) buf_store16<g16>(ro, pqt[l] < rows ? pqel[l] * E : kOutOfRange, o[l]);
             };
             // One chunk step (two sets); r holds chunk c+1 and is refilled
             // with chunk c+3.  The one-set loop below is the same step with
@@ -706,7 +710,8 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
 // One workgroup per (sequence, block of 128 tokens); every wave takes whole
 // query tiles (head, 32 rows).  S and z are the sums left in slot 0 of ws.
 template <typename T, int D, typename IO>
-__global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restrict__ q, T *__restrict__ out,
+__global__ __launch_bounds__(kThreads) void k_noncausal_apply(const typename IO::elem *__restrict__ q,
+                                                              T *__restrict__ out,
                                                               const float *__restrict__ ws, int nslots, int H,
                                                               int Hkv, int N, int G, int nblk, int normalise,
                                                               Packed pk, int seg_len)
@@ -761,14 +766,14 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restric
     if (tid < D) smZ[tid] = zv;
     __syncthreads();
 
-    const T *qb = q + qbase;
+    const typename IO::elem *qb = q + qbase;
     T *ob = out + qbase;
     const int NU = G * (TQ / 32);
     for (int u = w; u < NU; u += 4) {
         const int g = u / (TQ / 32), r = u % (TQ / 32);
         const int t = blk * TQ + r * 32 + n;
         if (blk * TQ + r * 32 >= N) continue;
-        const T *src = qb + (size_t)g * N * D + (size_t)t * D;
+        const typename IO::elem *src = qb + (size_t)g * N * D + (size_t)t * D;
         v8 qf[Gm::KBD];
         float dq = 0.f;
 #pragma unroll
@@ -777,9 +782,16 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restric
 #pragma unroll
             for (int j = 0; j < QV; ++j) {
                 g16 x = {};
-                if (t < N) x = *reinterpret_cast<const g16 *>(src + kb * 16 + h * 8 + j * U);
+                if (t < N) {
+                    if constexpr (Io<T, IO>::FP8) {
+                        const u32x2 y = *reinterpret_cast<const u32x2 *>(src + kb * 16 + h * 8 + j * U);
+                        x = __builtin_bit_cast(g16, u32x4{y[0], y[1], 0u, 0u});
+                    } else {
+                        x = *reinterpret_cast<const g16 *>(src + kb * 16 + h * 8 + j * U);
+                    }
+                }
 #pragma unroll
-                for (int s = 0; s < U; ++s) f[j * U + s] = IO::phi::f(Io<T, IO>::f(x[s]));
+                for (int s = 0; s < U; ++s) f[j * U + s] = IO::phi::f(Io<T, IO>::fi(x, s));
             }
             qf[kb] = cvt8<T>(f);
 #pragma unroll
@@ -820,8 +832,9 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const T *__restric
 // wave reduction.
 template <typename T, int D, typename IO>
 __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ state, float *__restrict__ z,
-                                                          const T *__restrict__ q, const T *__restrict__ k,
-                                                          const T *__restrict__ v, T *__restrict__ out, int H,
+                                                          const typename IO::elem *__restrict__ q,
+                                                          const typename IO::elem *__restrict__ k,
+                                                          const typename IO::elem *__restrict__ v, T *__restrict__ out, int H,
                                                           int Hkv, int G, int normalise,
                                                           const float *__restrict__ gd = nullptr)
 {
@@ -845,7 +858,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
     const int b = seq / Hkv, gk = seq % Hkv;
     const int tid = threadIdx.x, c4 = tid % C4, rg = tid / C4, lane = tid & 63, wv = tid >> 6;
     float *Sb = state + (size_t)seq * D * D;
-    const T *qb = q + ((size_t)b * H + (size_t)gk * G) * D;
+    const typename IO::elem *qb = q + ((size_t)b * H + (size_t)gk * G) * D;
 
     // The small operands first (k, v, z, the first query heads, as 16-byte
     // buffer loads that read zeros past their end), then the state rows:
@@ -854,18 +867,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
     // overlap the remaining loads.
     using g16 = typename Vt<T>::g16;
     constexpr int U = Vt<T>::U;                             // elements per 16 bytes
-    constexpr int E = (int)sizeof(T);
+    constexpr int E = Io<T, IO>::EB, GB = Io<T, IO>::GB;   // input element and raw group bytes
     const int g_first = G < GMAX ? G : GMAX;
-    const unsigned off = (unsigned)tid * 16u;
-    const g16 kg = buf_load16<g16>(make_rsrc(k + (size_t)seq * D, D * E), off);
-    const g16 vg = buf_load16<g16>(make_rsrc(v + (size_t)seq * D, D * E), off);
+    const unsigned off = (unsigned)tid * GB;
+    const g16 kg = load_in<T, IO>(make_rsrc(k + (size_t)seq * D, D * E), off);
+    const g16 vg = load_in<T, IO>(make_rsrc(v + (size_t)seq * D, D * E), off);
     // z is advanced whenever it is given, also when the output is not
     // normalised, so a state carried through such steps stays whole.
-    const f32x4 zg = buf_load16<f32x4>(make_rsrc(z ? z + (size_t)seq * D : nullptr, z ? D * 4 : 0), off);
+    const f32x4 zg = buf_load16<f32x4>(make_rsrc(z ? z + (size_t)seq * D : nullptr, z ? D * 4 : 0), (unsigned)tid * 16u);
     g16 qg[QGR];
     const Rsrc rq = make_rsrc(qb, g_first * D * E);
 #pragma unroll
-    for (int j = 0; j < QGR; ++j) qg[j] = buf_load16<g16>(rq, off + (unsigned)j * kThreads * 16u);
+    for (int j = 0; j < QGR; ++j) qg[j] = load_in<T, IO>(rq, off + (unsigned)j * kThreads * GB);
     __builtin_amdgcn_sched_barrier(0);  // small loads stay ahead of the state loads
     f32x4 Sr[NV];
 #pragma unroll
@@ -875,14 +888,14 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
     }
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-        sk[tid * U + i] = IO::phi::f(Io<T, IO>::f(kg[i]));
-        sv[tid * U + i] = Io<T, IO>::f(vg[i]);
+        sk[tid * U + i] = IO::phi::f(Io<T, IO>::fi(kg, i));
+        sv[tid * U + i] = Io<T, IO>::fi(vg, i);
     }
 #pragma unroll
     for (int j = 0; j < QGR; ++j) {
         const int e0 = (tid + j * kThreads) * U;
 #pragma unroll
-        for (int i = 0; i < U; ++i) sqf[e0 + i] = IO::phi::f(Io<T, IO>::f(qg[j][i]));
+        for (int i = 0; i < U; ++i) sqf[e0 + i] = IO::phi::f(Io<T, IO>::fi(qg[j], i));
     }
     lds_barrier();
     // decayed sums: S and z fade by exp(g) before the token is added
@@ -907,13 +920,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
             // the next GMAX query heads, requested at once as in the first pass
             const Rsrc rq2 = make_rsrc(qb + (size_t)g0 * D, gn * D * E);
 #pragma unroll
-            for (int j = 0; j < QGR; ++j) qg[j] = buf_load16<g16>(rq2, off + (unsigned)j * kThreads * 16u);
+            for (int j = 0; j < QGR; ++j) qg[j] = load_in<T, IO>(rq2, off + (unsigned)j * kThreads * GB);
             lds_barrier();
 #pragma unroll
             for (int j = 0; j < QGR; ++j) {
                 const int e0 = (tid + j * kThreads) * U;
 #pragma unroll
-                for (int i = 0; i < U; ++i) sqf[e0 + i] = IO::phi::f(Io<T, IO>::f(qg[j][i]));
+                for (int i = 0; i < U; ++i) sqf[e0 + i] = IO::phi::f(Io<T, IO>::fi(qg[j], i));
             }
             __syncthreads();
         }
@@ -966,9 +979,10 @@ int run_fwd(const linattn::Plan &pl, const void *q, const void *k, const void *v
     // Totals pass: its own chunk size, the largest that divides the segments
     // (up to 128 tokens), independent of the main pass's chunk.
     const int c1 = totals_chunk<T, D>(pl.seg_len);
-    const T *qq = static_cast<const T *>(q);
-    const T *kk = static_cast<const T *>(k);
-    const T *vv = static_cast<const T *>(v);
+    using In = typename IO::elem;
+    const In *qq = static_cast<const In *>(q);
+    const In *kk = static_cast<const In *>(k);
+    const In *vv = static_cast<const In *>(v);
     T *oo = static_cast<T *>(out);
     const int P = pl.segments;  // packed: the segments the launches are sized for
     const int E = D * D + D;
@@ -1083,9 +1097,10 @@ int run_decode(float *state, float *z, const void *q, const void *k, const void 
 {
     const int G = H / Hkv;
     const dim3 grid(B * Hkv), block(kThreads);
-    const T *qq = static_cast<const T *>(q);
-    const T *kk = static_cast<const T *>(k);
-    const T *vv = static_cast<const T *>(v);
+    using In = typename IO::elem;
+    const In *qq = static_cast<const In *>(q);
+    const In *kk = static_cast<const In *>(k);
+    const In *vv = static_cast<const In *>(v);
     T *oo = static_cast<T *>(out);
     switch (d) {
     case 32: hipLaunchKernelGGL((k_decode_step<T, 32, IO>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise, g); break;
@@ -1109,6 +1124,8 @@ template <int ELEM, typename P> struct ElemOf;
 template <typename P> struct ElemOf<LINATTN_F32, P> { using T = float; using IO = Fmt<float, P>; };
 template <typename P> struct ElemOf<LINATTN_BF16, P> { using T = bf16; using IO = Fmt<bf16, P>; };
 template <typename P> struct ElemOf<LINATTN_F16, P> { using T = bf16; using IO = Fmt<f16, P>; };
+template <typename P> struct ElemOf<LINATTN_FP8_E4M3, P> { using T = bf16; using IO = Fmt<fp8e4m3, P>; };
+template <typename P> struct ElemOf<LINATTN_FP8_E5M2, P> { using T = bf16; using IO = Fmt<fp8e5m2, P>; };
 using Phi = PhiOf<LINATTN_FMT_PHI>::type;
 using K = ElemOf<LINATTN_FMT_ELEM, Phi>;
 }  // namespace

@@ -134,31 +134,98 @@ __device__ __forceinline__ f32x8 cat(const f32x4 &a, const f32x4 &b)
 
 // ------------------------------------------------------------ input/output
 //
-// Rows in memory may be fp16 while the matrix-core operands of the 16-bit
-// kernels are bf16 (T = bf16, IO = fp16): bf16 keeps fp32's exponent range, so
-// the operand copies of the running sums (which grow with the sequence) stay
-// finite where fp16 would overflow.  Registers hold the raw 16-byte groups;
-// these convert them at the loads and stores.  IO is a Fmt (below); its
-// element type equal to T is the plain case.
+// Rows in memory may be fp16 or fp8 while the matrix-core operands of the
+// 16-bit kernels are bf16 (T = bf16, IO = fp16 or fp8): bf16 keeps fp32's
+// exponent range, so the operand copies of the running sums (which grow with
+// the sequence) stay finite where fp16 would overflow, and it holds every fp8
+// value exactly.  Registers hold the raw input groups (one load each: 16 bytes
+// of 2- or 4-byte elements, 8 bytes of fp8, U elements either way); these
+// convert them at the staging that writes them to LDS.  IO is a Fmt (below);
+// its element type equal to T is the plain case.
 typedef _Float16 f16;
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// fp8 rows (README "Features": mixed precision; the OCP 8-bit formats MI355X
+// uses): E4M3 (bias 7, no infinities, S.1111.111 is NaN, largest 448) and
+// E5M2 (bias 15, IEEE-like infinities and NaN).  One byte each.
+struct fp8e4m3 {
+    unsigned char b;
+};
+struct fp8e5m2 {
+    unsigned char b;
+};
+template <typename E> constexpr bool is_fp8 = std::is_same_v<E, fp8e4m3> || std::is_same_v<E, fp8e5m2>;
+
+// The value of an fp8 code, exactly, from the formats' definitions.
+__device__ __forceinline__ float fp8_value(unsigned b, fp8e4m3)
+{
+    const unsigned e = (b >> 3) & 15u, m = b & 7u;
+    // normal: (1 + m/8) 2^(e-7), i.e. fp32 exponent e + 120; subnormal (e = 0): m 2^-9
+    const float normal = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    const float sub = (float)m * 0x1p-9f;
+    float x = e ? normal : sub;
+    x = (e == 15u && m == 7u) ? __builtin_nanf("") : x;
+    return __uint_as_float(__float_as_uint(x) | ((b & 0x80u) << 24));
+}
+__device__ __forceinline__ float fp8_value(unsigned b, fp8e5m2)
+{
+    // E5M2 is the upper byte of an IEEE fp16 (same exponent width and bias)
+    return (float)__builtin_bit_cast(f16, (unsigned short)(b << 8));
+}
+
 template <typename T, typename IO> struct Io {
     using E = typename IO::elem;
-    static_assert(std::is_same_v<T, E> || (std::is_same_v<T, bf16> && std::is_same_v<E, f16>), "I/O type");
+    static_assert(std::is_same_v<T, E> || (std::is_same_v<T, bf16> && (std::is_same_v<E, f16> || is_fp8<E>)),
+                  "I/O type");
     static constexpr bool SAME = std::is_same_v<T, E>;
-    // element (raw bits in a T) -> float
-    static __device__ __forceinline__ float f(T x)
+    static constexpr bool FP8 = is_fp8<E>;
+    static constexpr int EB = (int)sizeof(E);       // bytes of one input element in memory
+    static constexpr int GB = Vt<T>::U * EB;         // bytes of one raw input group
+    // output elements: the input format, except bf16 for fp8 rows
+    using OutE = std::conditional_t<FP8, bf16, E>;
+    static constexpr int OB = (int)sizeof(OutE);
+    // element i of a raw input group -> float
+    static __device__ __forceinline__ float fi(const typename Vt<T>::g16 &g, int i)
     {
-        if constexpr (SAME) return (float)x;
-        else return (float)__builtin_bit_cast(E, x);
+        if constexpr (FP8) {
+            const u32x4 w = __builtin_bit_cast(u32x4, g);
+            return fp8_value((w[i >> 2] >> (8 * (i & 3))) & 0xffu, E{});
+        } else {
+            // the element is copied out first: a bit cast of the vector
+            // element expression itself reads element 0
+            const T x = g[i];
+            if constexpr (SAME) return (float)x;
+            else return (float)__builtin_bit_cast(E, x);
+        }
     }
-    // float -> the stored element (IO bits in a T)
+    // float -> the stored output element (its bits in a T)
     static __device__ __forceinline__ T out(float x)
     {
-        if constexpr (SAME) return (T)x;
+        if constexpr (SAME || FP8) return (T)x;
         else return __builtin_bit_cast(T, (E)x);
     }
 };
+
+// A row pointer held as the operand type, seen as the memory element type
+// (the same bytes; fp16 rows travel in bf16-typed storage).
+template <typename IO, typename T> __device__ __host__ __forceinline__ const typename IO::elem *in_ptr(const T *p)
+{
+    return reinterpret_cast<const typename IO::elem *>(p);
+}
+
+// One raw input group at a byte offset of a buffer (offsets out of range read
+// zeros, as for every buffer load here).
+template <typename T, typename IO>
+__device__ __forceinline__ typename Vt<T>::g16 load_in(Rsrc r, unsigned off)
+{
+    if constexpr (Io<T, IO>::FP8) {
+        const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+        return __builtin_bit_cast(typename Vt<T>::g16, u32x4{x[0], x[1], 0u, 0u});
+    } else {
+        return buf_load16<typename Vt<T>::g16>(r, off);
+    }
+}
 
 template <typename E> __device__ __forceinline__ typename Vt<E>::v8 cvt8(const float *x);
 template <> __device__ __forceinline__ bf16x8 cvt8<bf16>(const float *x)
@@ -174,13 +241,13 @@ template <typename E> __device__ __forceinline__ typename Vt<E>::v4 cvt4(f32x4 x
 template <> __device__ __forceinline__ bf16x4 cvt4<bf16>(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
 template <> __device__ __forceinline__ f32x4 cvt4<float>(f32x4 x) { return x; }
 
-// Four results -> four stored elements of I/O type IO (in T-typed storage).
+// Four results -> four stored output elements of I/O type IO (in T-typed storage).
 template <typename T, typename IO> __device__ __forceinline__ typename Vt<T>::v4 out4(f32x4 x)
 {
-    if constexpr (std::is_same_v<T, typename IO::elem>) return cvt4<T>(x);
+    if constexpr (std::is_same_v<T, typename IO::elem> || Io<T, IO>::FP8) return cvt4<T>(x);
     else return __builtin_bit_cast(bf16x4, __builtin_convertvector(x, f16x4));
 }
-// A raw 16-byte group of IO elements -> the same values as operands of type T.
+// A raw input group of IO elements -> the same values as operands of type T.
 template <typename T, typename IO> __device__ __forceinline__ typename Vt<T>::g16 op16(const typename Vt<T>::g16 &g)
 {
     if constexpr (std::is_same_v<T, typename IO::elem>) {
@@ -188,7 +255,7 @@ template <typename T, typename IO> __device__ __forceinline__ typename Vt<T>::g1
     } else {
         float x[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = Io<T, IO>::f(g[i]);
+        for (int i = 0; i < 8; ++i) x[i] = Io<T, IO>::fi(g, i);
         return cvt8<T>(x);
     }
 }
@@ -325,7 +392,7 @@ __device__ __forceinline__ void stage_rows(const typename Vt<T>::g16 (&kr)[L], c
             const int t = e / GPR, q = e % GPR;
             typename Vt<T>::g16 fk;
 #pragma unroll
-            for (int i = 0; i < U; ++i) fk[i] = (T)IO::phi::f(Io<T, IO>::f(kr[l][i]));
+            for (int i = 0; i < U; ++i) fk[i] = (T)IO::phi::f(Io<T, IO>::fi(kr[l], i));
             if (!full) {
                 if (t >= rows) fk = typename Vt<T>::g16{};
             }
@@ -556,7 +623,8 @@ __global__ __launch_bounds__(kThreads) void k_pack_plan(const int *__restrict__ 
 // total is the decayed sum at the segment's end, and the segment's summed g
 // goes to gs[slot] for the scan.
 template <typename T, int D, int C1, typename IO, bool DK = false>
-__global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict__ k, const T *__restrict__ v,
+__global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const typename IO::elem *__restrict__ k,
+                                                            const typename IO::elem *__restrict__ v,
                                                             float *__restrict__ ws, int N, int seg_len, int nslots,
                                                             Packed pk, int Hkv, int causal,
                                                             const float *__restrict__ gd = nullptr,
@@ -567,9 +635,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
     __shared__ __attribute__((aligned(16))) T smV[2][C1 * D];
     __shared__ __attribute__((aligned(16))) DecayTab<C1> smD[DK ? 2 : 1];
 
+    using In = typename IO::elem;
     int seq = blockIdx.x / nslots, p = blockIdx.x % nslots;
-    const T *kb = k + (size_t)seq * N * D;
-    const T *vb = v + (size_t)seq * N * D;
+    const In *kb = k + (size_t)seq * N * D;
+    const In *vb = v + (size_t)seq * N * D;
     size_t slot = (size_t)seq * nslots + p;
     if (pk.tab) {
         SegLoc r;
@@ -593,7 +662,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
     // requested as soon as chunk ci has been staged.  Buffer loads: chunks
     // past the segment read nothing, tokens past N read zeros.
     using g16 = typename Vt<T>::g16;
-    constexpr int E = (int)sizeof(T);
+    constexpr int E = Io<T, IO>::EB, GB = Io<T, IO>::GB;  // input element and raw group bytes
     g16 kA[G::LDV], vA[G::LDV], kB[G::LDV], vB[G::LDV];
     auto rows_at = [&](int t0) { return t0 < s1 ? min(C1, s1 - t0) : 0; };
     // First token of the i-th chunk taken (i >= nch: past the segment, no
@@ -617,9 +686,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const T *__restrict_
         const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, rows * D * E);
 #pragma unroll
         for (int l = 0; l < G::LDV; ++l) {
-            const unsigned off = (unsigned)(tid + l * kThreads) * 16u;
-            kr[l] = buf_load16<g16>(rk, off);
-            vr[l] = buf_load16<g16>(rv, off);
+            const unsigned off = (unsigned)(tid + l * kThreads) * GB;
+            kr[l] = load_in<T, IO>(rk, off);
+            vr[l] = load_in<T, IO>(rv, off);
         }
     };
     load(kA, vA, tpos(0));
@@ -797,7 +866,9 @@ template <typename T_, typename IO_> struct Kind {
 inline bool valid_dtype(int dtype)
 {
     const int e = dtype & 0xff, m = dtype >> 8;
-    return dtype >= 0 && (e == LINATTN_F32 || e == LINATTN_BF16 || e == LINATTN_F16) &&
+    return dtype >= 0 &&
+           (e == LINATTN_F32 || e == LINATTN_BF16 || e == LINATTN_F16 || e == LINATTN_FP8_E4M3 ||
+            e == LINATTN_FP8_E5M2) &&
            (m == LINATTN_PHI_ELU1 || m == LINATTN_PHI_RELU || m == LINATTN_PHI_SOFTPLUS);
 }
 template <class P, class Fn> int with_elem(int e, Fn &fn)
@@ -832,7 +903,8 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Totals pass with chunks of c1 tokens (32, 64 or 128; at most 16 KiB of K per
 // chunk, so that two chunks of K and V double-buffer in 64 KiB of LDS).
 template <typename T, int D, typename IO = Fmt<T, PhiElu1>, bool DK = false>
-int launch_totals(int c1, unsigned nblocks, hipStream_t st, const T *k, const T *v, float *ws, int N, int seg_len,
+int launch_totals(int c1, unsigned nblocks, hipStream_t st, const typename IO::elem *k, const typename IO::elem *v,
+                  float *ws, int N, int seg_len,
                   int nslots, Packed pk = Packed{nullptr, 0, 0}, int Hkv = 1, int causal = 1,
                   const float *gd = nullptr, float *gs = nullptr)
 {

@@ -45,9 +45,7 @@ int auto_chunk(int dtype, int d, int G, int causal)
 
 int make_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int chunk, Plan *p)
 {
-    if (dtype < 0 || ((dtype & 0xff) != LINATTN_F32 && (dtype & 0xff) != LINATTN_BF16 && (dtype & 0xff) != LINATTN_F16) ||
-        (dtype >> 8) > LINATTN_PHI_SOFTPLUS)
-        return LINATTN_ERR_DTYPE;
+    if (dtype < 0 || (dtype & 0xff) > LINATTN_FP8_E5M2 || (dtype >> 8) > LINATTN_PHI_SOFTPLUS) return LINATTN_ERR_DTYPE;
     if (B < 0 || H <= 0 || Hkv <= 0 || N < 0 || d <= 0 || H % Hkv != 0) return LINATTN_ERR_SHAPE;
     if ((int64_t)B * H > INT32_MAX / 2 || (int64_t)N * d > INT32_MAX / 2) return LINATTN_ERR_SHAPE;
     if (!valid_d(d)) return LINATTN_ERR_UNSUPPORTED;
@@ -142,7 +140,9 @@ int make_plan_packed(int nb, int H, int Hkv, int total, int d, int causal, int d
 bool decay_ok(const Plan &p)
 {
     const int e = (p.dtype & 0xff) != LINATTN_F32 ? 2 : 4;
-    return p.causal && !p.packed && (p.dtype >> 8) == LINATTN_PHI_ELU1 && !main_shape(e, p.d, p.chunk, p.gt).shift;
+    const bool fp8 = (p.dtype & 0xff) == LINATTN_FP8_E4M3 || (p.dtype & 0xff) == LINATTN_FP8_E5M2;
+    return p.causal && !p.packed && !fp8 && (p.dtype >> 8) == LINATTN_PHI_ELU1 &&
+           !main_shape(e, p.d, p.chunk, p.gt).shift;
 }
 
 size_t decay_ws_bytes(const Plan &p)

@@ -34,16 +34,17 @@ struct Win {
 // sums, and O^T += V^T Pt (MFMA).  The outputs are parked in the wave's own
 // q rows and stored as whole rows.
 template <typename T, int D, typename IO>
-__global__ __launch_bounds__(kThreads) void k_window(const T *__restrict__ q, const T *__restrict__ k,
-                                                     const T *__restrict__ v, T *__restrict__ out, int H, int Hkv,
-                                                     int N, int W, int normalise, int nqt)
+__global__ __launch_bounds__(kThreads) void k_window(const typename IO::elem *__restrict__ q,
+                                                     const typename IO::elem *__restrict__ k,
+                                                     const typename IO::elem *__restrict__ v, T *__restrict__ out,
+                                                     int H, int Hkv, int N, int W, int normalise, int nqt)
 {
     using Wn = Win<T, D>;
     using v8 = typename Vt<T>::v8;
     using g16 = typename Vt<T>::g16;
     constexpr bool BF = sizeof(T) == 2;
     constexpr int U = Wn::U, GPR = Wn::GPR, DT = Wn::DT, KBD = Wn::KBD, TQ = Wn::TQ;
-    constexpr int E = (int)sizeof(T);
+    constexpr int E = (int)sizeof(T), IE = Io<T, IO>::EB, GB = Io<T, IO>::GB;  // output, input bytes
     __shared__ __attribute__((aligned(16))) T smQ[TQ * D];
     __shared__ __attribute__((aligned(16))) T smK[2][32 * D];
     __shared__ __attribute__((aligned(16))) T smV[2][32 * D];
@@ -51,21 +52,22 @@ __global__ __launch_bounds__(kThreads) void k_window(const T *__restrict__ q, co
 
     const int bh = blockIdx.x / nqt, qt = blockIdx.x % nqt;
     const int b = bh / H, hq = bh % H, g = hq / (H / Hkv);
-    const T *qb = q + (size_t)bh * N * D;
+    using In = typename IO::elem;
+    const In *qb = q + (size_t)bh * N * D;
     T *ob = out + (size_t)bh * N * D;
     const size_t kvb = ((size_t)b * Hkv + g) * N * D;
-    const T *kb = k + kvb, *vb = v + kvb;
+    const In *kb = k + kvb, *vb = v + kvb;
     const int t0 = qt * TQ, qrows = min(TQ, N - t0);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
 
     // phi(q) of the query tile into LDS (rows past N read zeros)
     {
-        const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, qrows * D * E);
+        const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, qrows * D * IE);
         g16 r[Wn::LQ];
 #pragma unroll
         for (int l = 0; l < Wn::LQ; ++l) {
             const int e = tid + l * kThreads;
-            r[l] = buf_load16<g16>(rq, (Wn::QG % kThreads == 0 || e < Wn::QG) ? (unsigned)e * 16u : kOutOfRange);
+            r[l] = load_in<T, IO>(rq, (Wn::QG % kThreads == 0 || e < Wn::QG) ? (unsigned)e * GB : kOutOfRange);
         }
 #pragma unroll
         for (int l = 0; l < Wn::LQ; ++l) {
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void k_window(const T *__restrict__ q, co
             if (Wn::QG % kThreads == 0 || e < Wn::QG) {
                 g16 f;
 #pragma unroll
-                for (int i = 0; i < U; ++i) f[i] = (T)IO::phi::f(Io<T, IO>::f(r[l][i]));
+                for (int i = 0; i < U; ++i) f[i] = (T)IO::phi::f(Io<T, IO>::fi(r[l], i));
                 sQ.write16(e / GPR, (e % GPR) * U, f);
             }
         }
@@ -85,14 +87,14 @@ __global__ __launch_bounds__(kThreads) void k_window(const T *__restrict__ q, co
     g16 kr[Wn::LK], vr[Wn::LK];
     auto load_kv = [&](int kt) {  // past the band: nothing is read
         const int rows = rows_of(kt);
-        const Rsrc rk = make_rsrc(kb + (size_t)kt * 32 * D, rows * D * E);
-        const Rsrc rv = make_rsrc(vb + (size_t)kt * 32 * D, rows * D * E);
+        const Rsrc rk = make_rsrc(kb + (size_t)kt * 32 * D, rows * D * IE);
+        const Rsrc rv = make_rsrc(vb + (size_t)kt * 32 * D, rows * D * IE);
 #pragma unroll
         for (int l = 0; l < Wn::LK; ++l) {
             const int e = tid + l * kThreads;
-            const unsigned off = (Wn::KG % kThreads == 0 || e < Wn::KG) ? (unsigned)e * 16u : kOutOfRange;
-            kr[l] = buf_load16<g16>(rk, off);
-            vr[l] = buf_load16<g16>(rv, off);
+            const unsigned off = (Wn::KG % kThreads == 0 || e < Wn::KG) ? (unsigned)e * GB : kOutOfRange;
+            kr[l] = load_in<T, IO>(rk, off);
+            vr[l] = load_in<T, IO>(rv, off);
         }
     };
     load_kv(kt0);
@@ -177,7 +179,8 @@ int run_window(const void *q, const void *k, const void *v, void *out, int B, in
 {
     const int nqt = (N + Win<T, 64>::TQ - 1) / Win<T, 64>::TQ;
     const dim3 grid((unsigned)((size_t)B * H * nqt)), block(kThreads);
-    const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k), *vv = static_cast<const T *>(v);
+    using In = typename IO::elem;
+    const In *qq = static_cast<const In *>(q), *kk = static_cast<const In *>(k), *vv = static_cast<const In *>(v);
     T *oo = static_cast<T *>(out);
     switch (d) {
     case 32: hipLaunchKernelGGL((k_window<T, 32, IO>), grid, block, 0, st, qq, kk, vv, oo, H, Hkv, N, W, normalise, nqt); break;

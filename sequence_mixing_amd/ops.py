@@ -12,7 +12,18 @@ from . import (LINATTN_BF16, LINATTN_F16, LINATTN_F32, LinattnError, linattn_bwd
                linattn_fwd_decay_workspace_bytes, linattn_fwd_from_state, linattn_fwd_packed,
                linattn_fwd_packed_workspace_bytes, linattn_fwd_workspace_bytes)
 
-_DT = {torch.float32: LINATTN_F32, torch.bfloat16: LINATTN_BF16, torch.float16: LINATTN_F16}
+_DT = {torch.float32: LINATTN_F32, torch.bfloat16: LINATTN_BF16, torch.float16: LINATTN_F16,
+       torch.float8_e4m3fn: 3, torch.float8_e5m2: 4}
+_FP8 = (torch.float8_e4m3fn, torch.float8_e5m2)
+
+
+def out_dtype(t: torch.dtype) -> torch.dtype:
+    """Element type of the outputs for inputs of type t: the same, except bf16 for fp8 rows."""
+    return torch.bfloat16 if t in _FP8 else t
+
+
+def _empty_out(q):
+    return torch.empty(q.shape, dtype=out_dtype(q.dtype), device=q.device)
 
 
 # feature maps (the `dtype` code's bits 8-15)
@@ -68,10 +79,11 @@ def _check_decode(state, z, q, k, v, normalise):
 
 def _check_out(out, q):
     if out is None:
-        return torch.empty_like(q)
-    if not (out.is_cuda and out.is_contiguous() and out.dtype == q.dtype and out.shape == q.shape and
+        return _empty_out(q)
+    if not (out.is_cuda and out.is_contiguous() and out.dtype == out_dtype(q.dtype) and out.shape == q.shape and
             out.device == q.device):
-        raise ValueError("out must be a contiguous device tensor of q's shape, dtype and device")
+        raise ValueError("out must be a contiguous device tensor of q's shape and device, of q's dtype "
+                         "(bf16 for fp8 q)")
     return out
 
 
@@ -87,8 +99,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=True, normalis
     if k.shape != (B, Hkv, N, d) or v.shape != (B, Hkv, N, d):
         raise ValueError("k and v must be [B, Hkv, N, d]")
     code = dtype_code(q.dtype, phi)
-    if out is None:
-        out = torch.empty_like(q)
+    out = _check_out(out, q)
     S = z = None
     if want_state:
         S = torch.empty(B, Hkv, d, d, dtype=torch.float32, device=q.device)
@@ -146,8 +157,7 @@ def fwd_decay(q, k, v, g, normalise=True, chunk=0, want_state=False, out=None, w
         if t is not None and not (t.is_cuda and t.is_contiguous() and t.dtype == torch.float32 and t.shape == shape):
             raise ValueError("state_in / z_in must be contiguous fp32 device tensors [B,Hkv,d,d] / [B,Hkv,d]")
     code = dtype_code(q.dtype)
-    if out is None:
-        out = torch.empty_like(q)
+    out = _check_out(out, q)
     S = z = None
     if want_state:
         S = torch.empty(B, Hkv, d, d, dtype=torch.float32, device=q.device)
@@ -196,8 +206,7 @@ def fwd_packed(q, k, v, cu_seqlens, H, Hkv, d, causal=True, normalise=True, chun
     if not (cu_seqlens.is_cuda and cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()):
         raise ValueError("cu_seqlens must be a contiguous int32 device tensor")
     code = dtype_code(q.dtype, phi)
-    if out is None:
-        out = torch.empty_like(q)
+    out = _check_out(out, q)
     S = z = None
     if want_state:
         S = torch.empty(nseqs, Hkv, d, d, dtype=torch.float32, device=q.device)

@@ -92,7 +92,7 @@ def test_fwd_rejects_before_launch():
 def test_decode_rejects_before_launch():
     assert la.linattn_decode_step(16, 16, 16, 16, 16, 16, 1, 3, 2, 64, 1, F32, stream=0) == -2
     assert la.linattn_decode_step(16, 16, 16, 16, 16, 16, 1, 2, 2, 48, 1, F32, stream=0) == -4
-    assert la.linattn_decode_step(16, 16, 16, 16, 16, 16, 1, 2, 2, 64, 1, 4, stream=0) == -3
+    assert la.linattn_decode_step(16, 16, 16, 16, 16, 16, 1, 2, 2, 64, 1, 9, stream=0) == -3
     assert la.linattn_decode_step(16, None, 16, 16, 16, 16, 1, 2, 2, 64, 1, F32, stream=0) == -1
     assert la.linattn_decode_step(None, 16, 16, 16, 16, 16, 1, 2, 2, 64, 1, F32, stream=0) == -1
     assert la.linattn_decode_step(16, 16, 24, 16, 16, 16, 1, 2, 2, 64, 1, F32, stream=0) == -7
@@ -186,7 +186,7 @@ def test_fp16_plans_like_bf16():
         assert la.linattn_fwd_plan(*args, la.LINATTN_F16) == la.linattn_fwd_plan(*args, la.LINATTN_BF16)
         assert la.linattn_fwd_workspace_bytes(*args, la.LINATTN_F16) == la.linattn_fwd_workspace_bytes(*args, la.LINATTN_BF16)
         assert la.linattn_bwd_workspace_bytes(*args, la.LINATTN_F16) == la.linattn_bwd_workspace_bytes(*args, la.LINATTN_BF16)
-    assert la.linattn_fwd_plan(1, 2, 2, 16, 64, 1, 3)[0] == -3
+    assert la.linattn_fwd_plan(1, 2, 2, 16, 64, 1, 9)[0] == -3
 
 
 def test_decay_validation_without_gpu():
