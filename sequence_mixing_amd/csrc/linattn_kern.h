@@ -765,6 +765,164 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const typename IO::e
     }
 }
 
+// ------------------------------------------------------ fp32 totals pass
+//
+// For fp32 rows the 16x16x4 fp32 matrix instruction takes, per lane (j, kq)
+// (j = lane % 16, kq = lane / 16), A[j][kq] and B[kq][j]: four tokens per
+// instruction, one per quarter-wave.  Lane (j, kq) loads 16 bytes (4
+// features; 8 bytes, 2 features, at d = 32) of token 4g + kq of K and of V
+// straight from global memory, so one load instruction brings four whole
+// rows (d = 64) with no LDS staging.  Instruction (e, e') takes feature
+// VEC i + e of phi(K) as A and feature VEC j + e' of V as B: together the
+// VEC^2 instructions add the four tokens' phi(k) v^T to a state whose row
+// VEC i + e, column VEC j + e' sits in register r of lane (j, kq) of
+// accumulator (e, e') with i = 4 kq + r.  d <= 64: each of the four waves
+// keeps the whole state over every fourth group of tokens and the waves are
+// summed through LDS at the end; d = 128: each wave keeps one quadrant (the
+// 64-feature halves of K and V it reads) over every token.  Per-lane word
+// loads in the 32x32x2 layout measured slower than LDS staging (a load
+// instruction then carries 256 bytes, and the address unit, not memory,
+// set the pace); these carry 1 KiB.  Same workgroups, slots and outputs as
+// k_seg_totals (plain sums only); token groups last to first as there.
+template <int D> struct X4 {
+    static constexpr int NW = 4, TH = 64 * NW;
+    static constexpr int VEC = D == 32 ? 2 : 4;  // features per lane and load
+    static constexpr bool QUAD = D == 128;       // waves own quadrants of the state
+    static constexpr int TS = QUAD ? 1 : NW;     // waves splitting the token groups
+    static constexpr int PD = 4;                 // token groups in flight per wave
+    static constexpr int NR = TS > 1 ? NW * VEC * VEC * 64 : 1;  // LDS f32x4 for the wave sums
+};
+
+template <int D, typename IO>
+__global__ __launch_bounds__(X4<D>::TH) void k_seg_totals_f32(const float *__restrict__ k,
+                                                              const float *__restrict__ v,
+                                                              float *__restrict__ ws, int N, int seg_len,
+                                                              int nslots, Packed pk, int Hkv, int causal)
+{
+    using X = X4<D>;
+    constexpr int VEC = X::VEC, TS = X::TS, PD = X::PD, NW = X::NW;
+    using fv = std::conditional_t<VEC == 4, f32x4, float __attribute__((ext_vector_type(2)))>;
+    __shared__ f32x4 red[X::NR];
+    __shared__ f32x4 redz[TS > 1 ? NW * 64 : 1];
+
+    int seq = blockIdx.x / nslots, p = blockIdx.x % nslots;
+    const float *kb = k + (size_t)seq * N * D;
+    const float *vb = v + (size_t)seq * N * D;
+    size_t slot = (size_t)seq * nslots + p;
+    if (pk.tab) {
+        SegLoc r;
+        const int gk = blockIdx.x / pk.nsmax;
+        if (!packed_locate(pk, blockIdx.x % pk.nsmax, r) || (causal && r.p == r.np - 1)) return;
+        p = r.p;
+        N = r.n;
+        kb = k + ((size_t)r.off * Hkv + (size_t)gk * r.n) * D;
+        vb = v + ((size_t)r.off * Hkv + (size_t)gk * r.n) * D;
+        slot = packed_slot0(r, gk, Hkv, causal) + r.p;
+    }
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane & 15, kq = lane >> 4;
+    const int tsi = TS > 1 ? w : 0;                         // token share
+    const int cK = X::QUAD ? w >> 1 : 0, cV = X::QUAD ? w & 1 : 0;  // quadrant (d = 128)
+    const int s0 = p * seg_len, len = max(0, min(N, s0 + seg_len) - s0);
+    const int ng = (len + 3) / 4, nj = (ng + TS - 1) / TS;
+    const Rsrc rk = make_rsrc(kb + (size_t)s0 * D, len * D * 4);
+    const Rsrc rv = make_rsrc(vb + (size_t)s0 * D, len * D * 4);
+
+    // Step i of this wave: token group g = ng - 1 - (i TS + tsi).  Tokens past
+    // the segment's end read zeros; groups before it (g < 0) have negative
+    // offsets, which as unsigned lie beyond every range: no branch, no read.
+    auto row_of = [&](int i) { return 4 * (ng - 1 - (i * TS + tsi)) + kq; };
+    auto ld = [&](Rsrc r, int t, int c) {
+        const unsigned off = (unsigned)((t * D + 64 * c + VEC * j) * 4);
+        if constexpr (VEC == 4) return buf_load16<f32x4>(r, off);
+        else return __builtin_bit_cast(fv, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    };
+    fv kr[PD], vr[PD];
+    auto load = [&](int u, int i) {
+        const int t = row_of(i);
+        kr[u] = ld(rk, t, cK);
+        vr[u] = ld(rv, t, cV);
+    };
+    f32x4 acc[VEC][VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+#pragma unroll
+        for (int f = 0; f < VEC; ++f) acc[e][f] = f32x4{};
+    f32x4 zs = {};
+    auto absorb = [&](int u, int i) {
+        // Tokens outside the segment read k = v = 0: their products with v
+        // vanish, and only z needs them masked (phi(0) need not be 0).
+        const bool live = (unsigned)row_of(i) < (unsigned)len;
+        float a[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            a[e] = IO::phi::f(kr[u][e]);
+            zs[e] += live ? a[e] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+#pragma unroll
+            for (int f = 0; f < VEC; ++f)
+                acc[e][f] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], vr[u][f], acc[e][f], 0, 0, 0);
+    };
+#pragma unroll
+    for (int u = 0; u < PD; ++u) load(u, u);
+    for (int i0 = 0; i0 < nj; i0 += PD) {
+#pragma unroll
+        for (int u = 0; u < PD; ++u) {
+            if (i0 + u < nj) absorb(u, i0 + u);
+            load(u, i0 + u + PD);
+        }
+    }
+    // z: the four quarter-waves hold four token subsets of the same features
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        zs[e] += __shfl_xor(zs[e], 16);
+        zs[e] += __shfl_xor(zs[e], 32);
+    }
+    float *out = ws + slot * (size_t)D * (D + 1);
+    // acc[e][f][r] is state row VEC (4 kq + r) + e of the wave's rows, column VEC j + f of its columns
+    auto store_row = [&](const f32x4 (&s)[VEC], int e, int r) {
+        float *o = out + (size_t)(64 * cK + VEC * (4 * kq + r) + e) * D + 64 * cV + VEC * j;
+        if constexpr (VEC == 4) *reinterpret_cast<f32x4 *>(o) = f32x4{s[0][r], s[1][r], s[2][r], s[3][r]};
+        else *reinterpret_cast<fv *>(o) = fv{s[0][r], s[1][r]};
+    };
+    if constexpr (TS > 1) {
+        // the waves' sums through LDS; wave w then adds up and stores rows e = w
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+#pragma unroll
+            for (int f = 0; f < VEC; ++f) red[(w * VEC * VEC + e * VEC + f) * 64 + lane] = acc[e][f];
+        redz[w * 64 + lane] = zs;
+        __syncthreads();
+        if (w < VEC) {
+            const int e = w;
+            f32x4 s[VEC];
+#pragma unroll
+            for (int f = 0; f < VEC; ++f) {
+                s[f] = red[(e * VEC + f) * 64 + lane];
+#pragma unroll
+                for (int o = 1; o < NW; ++o) s[f] += red[(o * VEC * VEC + e * VEC + f) * 64 + lane];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) store_row(s, e, r);
+        }
+        if (w == NW - 1 && kq == 0) {
+            f32x4 z = redz[lane];
+#pragma unroll
+            for (int o = 1; o < NW; ++o) z += redz[o * 64 + lane];
+            float *oz = out + (size_t)D * D + VEC * j;
+            if constexpr (VEC == 4) *reinterpret_cast<f32x4 *>(oz) = z;
+            else *reinterpret_cast<fv *>(oz) = fv{z[0], z[1]};
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) store_row(acc[e], e, r);
+        if (cV == 0 && kq == 0) *reinterpret_cast<f32x4 *>(out + (size_t)D * D + 64 * cK + VEC * j) = zs;
+    }
+}
+
 // ---------------------------------------------------------------- seg_scan
 //
 // ws holds nslots partials of E = D*D + D floats per sequence.  mode 0:
@@ -901,13 +1059,19 @@ int launch_status()
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Totals pass with chunks of c1 tokens (32, 64 or 128; at most 16 KiB of K per
-// chunk, so that two chunks of K and V double-buffer in 64 KiB of LDS).
+// chunk, so that two chunks of K and V double-buffer in 64 KiB of LDS); plain
+// fp32 sums take the pass without staging (k_seg_totals_f32), whatever c1.
 template <typename T, int D, typename IO = Fmt<T, PhiElu1>, bool DK = false>
 int launch_totals(int c1, unsigned nblocks, hipStream_t st, const typename IO::elem *k, const typename IO::elem *v,
                   float *ws, int N, int seg_len,
                   int nslots, Packed pk = Packed{nullptr, 0, 0}, int Hkv = 1, int causal = 1,
                   const float *gd = nullptr, float *gs = nullptr)
 {
+    if constexpr (std::is_same_v<T, float> && !DK) {
+        hipLaunchKernelGGL((k_seg_totals_f32<D, IO>), dim3(nblocks), dim3(X4<D>::TH), 0, st, k, v, ws, N, seg_len,
+                           nslots, pk, Hkv, causal);
+        return LINATTN_OK;
+    }
     constexpr int cap = 65536 / (4 * D * (int)sizeof(T));
     switch (c1) {
     case 32:
