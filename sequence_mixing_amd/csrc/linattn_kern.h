@@ -623,12 +623,12 @@ __global__ __launch_bounds__(kThreads) void k_pack_plan(const int *__restrict__ 
 // total is the decayed sum at the segment's end, and the segment's summed g
 // goes to gs[slot] for the scan.
 template <typename T, int D, int C1, typename IO, bool DK = false>
-__global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const typename IO::elem *__restrict__ k,
-                                                            const typename IO::elem *__restrict__ v,
-                                                            float *__restrict__ ws, int N, int seg_len, int nslots,
-                                                            Packed pk, int Hkv, int causal,
-                                                            const float *__restrict__ gd = nullptr,
-                                                            float *__restrict__ gs = nullptr)
+__global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 4 : 2))) void k_seg_totals(const typename IO::elem *__restrict__ k,
+                                                             const typename IO::elem *__restrict__ v,
+                                                             float *__restrict__ ws, int N, int seg_len, int nslots,
+                                                             Packed pk, int Hkv, int causal,
+                                                             const float *__restrict__ gd = nullptr,
+                                                             float *__restrict__ gs = nullptr)
 {
     using G = Geo<T, D, C1>;
     __shared__ __attribute__((aligned(16))) T smK[2][C1 * D];
@@ -650,7 +650,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const typename IO::e
         vb = v + ((size_t)r.off * Hkv + (size_t)gk * r.n) * D;
         slot = packed_slot0(r, gk, Hkv, causal) + r.p;
     }
+    // Waves 0-3 absorb (they own the state tiles), waves 4-7 stage: while the
+    // first four add chunk c from one LDS buffer, the other four write phi(K),
+    // V of chunk c + 1 into the other buffer and request chunk c + 3, so the
+    // vector work of staging runs beside the matrix work instead of before it.
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
+    const bool stager = w >= 4;
+    const int sid = tid - kThreads;  // staging thread 0..255
     const int s0 = p * seg_len, s1 = min(N, s0 + seg_len);
     const int nch = (s1 - s0 + C1 - 1) / C1;
 
@@ -658,12 +664,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const typename IO::e
     float zacc = 0.f;
 #pragma unroll
     for (int i = 0; i < G::MAXST; ++i) acc[i] = f32x16{};
-    // Two chunks in flight: register sets A and B alternate, chunk ci + 2 is
-    // requested as soon as chunk ci has been staged.  Buffer loads: chunks
-    // past the segment read nothing, tokens past N read zeros.
+    // The staging waves keep NS chunks in flight in register sets (two for
+    // 16-bit rows at d = 128, where one workgroup fills a CU anyway; one
+    // otherwise, so that two workgroups fit on a CU).  Buffer loads:
+    // chunks past the segment read nothing, tokens past N read zeros.
+    constexpr int NS = D >= 128 && sizeof(T) == 2 ? 2 : 1;
     using g16 = typename Vt<T>::g16;
     constexpr int E = Io<T, IO>::EB, GB = Io<T, IO>::GB;  // input element and raw group bytes
-    g16 kA[G::LDV], vA[G::LDV], kB[G::LDV], vB[G::LDV];
+    g16 kR[NS][G::LDV], vR[NS][G::LDV];
+    float gR[NS];
     auto rows_at = [&](int t0) { return t0 < s1 ? min(C1, s1 - t0) : 0; };
     // First token of the i-th chunk taken (i >= nch: past the segment, no
     // rows).  Plain sums take the segment's chunks last to first: the pass
@@ -674,28 +683,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const typename IO::e
         const int kx = DK ? i : nch - 1 - i;
         return i < nch && kx >= 0 ? s0 + kx * C1 : s1;
     };
-    // log-decay of token t0 + tid (zero past the segment)
+    // log-decay of token t0 + sid (zero past the segment)
     const float *gb = DK ? gd + (size_t)seq * N : nullptr;
-    float gA = 0.f, gB = 0.f, glog = 0.f;
-    auto load_g = [&](float &gr, int t0) {
-        if constexpr (DK) gr = tid < rows_at(t0) ? gb[t0 + tid] : 0.f;
-    };
-    auto load = [&](g16 (&kr)[G::LDV], g16 (&vr)[G::LDV], int t0) {
-        const int rows = rows_at(t0);
+    float glog = 0.f;
+    // chunk i into register set u
+    auto load = [&](int u, int i) {
+        const int t0 = tpos(i), rows = rows_at(t0);
         const Rsrc rk = make_rsrc(kb + (size_t)t0 * D, rows * D * E);
         const Rsrc rv = make_rsrc(vb + (size_t)t0 * D, rows * D * E);
 #pragma unroll
         for (int l = 0; l < G::LDV; ++l) {
-            const unsigned off = (unsigned)(tid + l * kThreads) * GB;
-            kr[l] = load_in<T, IO>(rk, off);
-            vr[l] = load_in<T, IO>(rv, off);
+            const unsigned off = (unsigned)(sid + l * kThreads) * GB;
+            kR[u][l] = load_in<T, IO>(rk, off);
+            vR[u][l] = load_in<T, IO>(rv, off);
         }
+        if constexpr (DK) gR[u] = sid < rows ? gb[t0 + sid] : 0.f;
     };
-    load(kA, vA, tpos(0));
-    load_g(gA, tpos(0));
-    __builtin_amdgcn_sched_barrier(0);  // keep chunk 0's loads ahead of chunk 1's, as in the loop
-    load(kB, vB, tpos(1));
-    load_g(gB, tpos(1));
+    // chunk i from register set u into LDS buffer buf
+    auto stage = [&](int u, int buf, int i) {
+        stage_rows<T, D, C1, kThreads, IO>(kR[u], vR[u], Tile<T, D>{smK[buf]}, Tile<T, D>{smV[buf]},
+                                           rows_at(tpos(i)), sid);
+        if constexpr (DK) decay_stage<C1>(smD[buf], gR[u], sid);
+    };
     auto absorb = [&](int buf) {
         const Tile<T, D> sK{smK[buf]}, sV{smV[buf]};
 #pragma unroll
@@ -723,26 +732,43 @@ __global__ __launch_bounds__(kThreads, 2) void k_seg_totals(const typename IO::e
             for (int kt = 0; kt < G::CT; ++kt) glog += smD[buf].TL[kt];
         }
     };
-    // Chunks in pairs; with an odd count the last pair's second chunk lies
-    // past the segment and adds zeros (every step issues the same loads).
-    for (int ci = 0; ci < nch; ci += 2) {
-        stage_rows<T, D, C1, kThreads, IO>(kA, vA, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, rows_at(tpos(ci)), tid);
-        if constexpr (DK) {
-            decay_stage<C1>(smD[0], gA, tid);
-            load_g(gA, tpos(ci + 2));
+    if (stager) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            load(u, u);
+            __builtin_amdgcn_sched_barrier(0);  // keep each chunk's loads ahead of the next one's
         }
-        load(kA, vA, tpos(ci + 2));
-        lds_barrier();
-        absorb(0);
-        stage_rows<T, D, C1, kThreads, IO>(kB, vB, Tile<T, D>{smK[1]}, Tile<T, D>{smV[1]}, rows_at(tpos(ci + 1)), tid);
-        if constexpr (DK) {
-            decay_stage<C1>(smD[1], gB, tid);
-            load_g(gB, tpos(ci + 3));
-        }
-        load(kB, vB, tpos(ci + 3));
-        lds_barrier();
-        absorb(1);
+        stage(0, 0, 0);
+        load(0, NS);
     }
+    lds_barrier();
+    // Step ci: the absorbing waves add chunk ci (buffer ci & 1) while the
+    // staging waves write chunk ci + 1 (register set (ci + 1) % NS) into the
+    // other buffer and request chunk ci + 1 + NS into that set; one barrier
+    // per step.  Steps in pairs, so that every step's register set is fixed.
+    for (int ci = 0; ci < nch; ci += 2) {
+        if (stager) {
+            if (ci + 1 < nch) {
+                stage(1 % NS, 1, ci + 1);
+                load(1 % NS, ci + 1 + NS);
+            }
+        } else {
+            absorb(0);
+        }
+        lds_barrier();
+        if (ci + 1 < nch) {
+            if (stager) {
+                if (ci + 2 < nch) {
+                    stage(0, 0, ci + 2);
+                    load(0, ci + 2 + NS);
+                }
+            } else {
+                absorb(1);
+            }
+            lds_barrier();
+        }
+    }
+    if (stager) return;
     if constexpr (DK) {
         if (tid == 0) gs[slot] = glog;
     }
@@ -1075,19 +1101,19 @@ int launch_totals(int c1, unsigned nblocks, hipStream_t st, const typename IO::e
     constexpr int cap = 65536 / (4 * D * (int)sizeof(T));
     switch (c1) {
     case 32:
-        hipLaunchKernelGGL((k_seg_totals<T, D, 32, IO, DK>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N, seg_len,
+        hipLaunchKernelGGL((k_seg_totals<T, D, 32, IO, DK>), dim3(nblocks), dim3(2 * kThreads), 0, st, k, v, ws, N, seg_len,
                            nslots, pk, Hkv, causal, gd, gs);
         return LINATTN_OK;
     case 64:
         if constexpr (64 <= cap) {
-            hipLaunchKernelGGL((k_seg_totals<T, D, 64, IO, DK>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N,
+            hipLaunchKernelGGL((k_seg_totals<T, D, 64, IO, DK>), dim3(nblocks), dim3(2 * kThreads), 0, st, k, v, ws, N,
                                seg_len, nslots, pk, Hkv, causal, gd, gs);
             return LINATTN_OK;
         }
         break;
     case 128:
         if constexpr (128 <= cap) {
-            hipLaunchKernelGGL((k_seg_totals<T, D, 128, IO, DK>), dim3(nblocks), dim3(kThreads), 0, st, k, v, ws, N,
+            hipLaunchKernelGGL((k_seg_totals<T, D, 128, IO, DK>), dim3(nblocks), dim3(2 * kThreads), 0, st, k, v, ws, N,
                                seg_len, nslots, pk, Hkv, causal, gd, gs);
             return LINATTN_OK;
         }
@@ -1099,8 +1125,11 @@ int launch_totals(int c1, unsigned nblocks, hipStream_t st, const typename IO::e
 template <typename T, int D>
 int totals_chunk(int seg_len)
 {
+    // 16-bit rows: at most 64 tokens, whose staging registers leave room for
+    // two workgroups per CU at d <= 64 (128-token chunks spill there)
     constexpr int cap = 65536 / (4 * D * (int)sizeof(T));
-    int c1 = cap < 128 ? cap : 128;
+    constexpr int lim = sizeof(T) == 2 ? 64 : 128;
+    int c1 = cap < lim ? cap : lim;
     while (c1 > 32 && seg_len % c1 != 0) c1 /= 2;  // segments are whole chunks of the pass
     return c1;
 }
