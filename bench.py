@@ -375,10 +375,10 @@ def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, flush, tag=
         # pass 1, the reduction phi(K)^T V, sum phi(K) over every token: K and V
         # read once (the partial sums it writes are not counted)
         kv = 2 * w.B * w.Hkv * w.N * w.d * (2 if w.dtype == "bf16" else 4)
-        t = {"f32": "float", "bf16": "bf16"}[w.dtype]
+        # fp32 rows take the pass without staging, k_seg_totals_f32<d, ...>
+        kn = f"k_seg_totals_f32<{w.d}" if w.dtype == "f32" else f"k_seg_totals<bf16,{w.d}"
         row["roofline_reduction"] = roofline(kv, 0.0, cold["stage_ms"][0] / 1e3, w.dtype,
-                                             f"k_seg_totals<{t},{w.d}> (pass 1, cold)",
-                                             measured_traffic(tag, f"k_seg_totals<{t},{w.d},"))
+                                             f"{kn}> (pass 1, cold)", measured_traffic(tag, kn + ","))
     del q, k, v, out, ws
     return row
 
