@@ -205,7 +205,7 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
     constexpr bool SPLITV = SPLIT && !std::is_same_v<T, typename IO::elem>;
     __shared__ __attribute__((aligned(16))) T smVl[SPLITV ? kBC * D : 8];
     __shared__ __attribute__((aligned(16))) float sZt[kBC * D];  // z_t of every token of the chunk, [t][i]
-    __shared__ float sZp[D];                                      // z before the chunk
+    __shared__ __attribute__((aligned(16))) float sZp[D];        // z before the chunk
     __shared__ float sH[kBC];
     const Tile<T, D> sA{smA}, sB{smB}, sV{smV}, sG{smG}, sO{OWN_O ? smO : smG}, sS{smS}, sBl{smBl}, sGl{smGl};
     const Tile<T, D> sVl{smVl};
@@ -382,16 +382,23 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
                 dacc[ui] = acc;
             }
             if constexpr (!OWN_O) lds_barrier();  // every read of the g tile is done
+            // registers 4 q4 .. 4 q4 + 3 are four consecutive features of
+            // token n: written (and a, z read) four at a time
 #pragma unroll
             for (int ui = 0; ui < MAXI; ++ui) {
                 const int it = w + BG::NW * ui;
                 if (it >= BG::DT) break;
                 const float hn = sH[n];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = it * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                    const float da = dacc[ui][r] + hn * sZp[i];
-                    sO.p[sO.at(n, i)] = Io<T, IO>::out(da * IO::phi::df((float)sA.p[sA.at(n, i)]));
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int i0 = it * 32 + 8 * q4 + 4 * h;
+                    const auto av = sA.read4(n, i0);
+                    const f32x4 zp = *reinterpret_cast<const f32x4 *>(sZp + i0);
+                    f32x4 x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        x[e] = (dacc[ui][4 * q4 + e] + hn * zp[e]) * IO::phi::df((float)av[e]);
+                    sO.write4(n, i0, out4<T, IO>(x));
                 }
             }
             if (causal && hh == G - 1) {
@@ -442,6 +449,7 @@ __global__ __launch_bounds__((BGeo<T, D, DKV_WAVES(D, TOTALS)>::TH), (BGeo<T, D,
     __shared__ __attribute__((aligned(16))) T smV[TOTALS ? 16 / sizeof(T) : kBC * D];
     __shared__ __attribute__((aligned(16))) T smR[TOTALS ? 16 / sizeof(T) : D * D];
     __shared__ float sH[kBC], sRp[RS * D];
+    __shared__ __attribute__((aligned(16))) float sRf[D];  // the r partials summed, per feature
     const Tile<T, D> sA{smA}, sG{smG}, sB{smB}, sV{smV}, sR{smR};
     const Tile<T, D> sOK{smA}, sOV{smG};  // dk, dv rows, once the heads are done
 
@@ -525,6 +533,18 @@ __global__ __launch_bounds__((BGeo<T, D, DKV_WAVES(D, TOTALS)>::TH), (BGeo<T, D,
                 sRp[rsl * D + rcol] = rpart;
             }
             lds_barrier();
+            // r as it stands before this chunk, summed over the slices once
+            // (read by the outputs after the heads' barriers; without heads,
+            // non-causal, it is fixed and summed at the first chunk)
+            if (causal || j == 0) {
+                if (tid < D) {
+                    float rs = 0.f;
+#pragma unroll
+                    for (int sl = 0; sl < RS; ++sl) rs += sRp[sl * D + tid];
+                    sRf[tid] = rs;
+                }
+                if (nheads == 0) lds_barrier();
+            }
         }
         for (int hh = 0; hh < nheads; ++hh) {
             // ---- a, g, h of this head; the next head's (or chunk's) rows requested
@@ -623,20 +643,25 @@ __global__ __launch_bounds__((BGeo<T, D, DKV_WAVES(D, TOTALS)>::TH), (BGeo<T, D,
                     }
                 }
             }
+            // registers 4 q4 .. 4 q4 + 3 of a unit are four consecutive
+            // features of token n: written (and phi(k) read) four at a time
 #pragma unroll
             for (int u = 0; u < MAXU; ++u) {
                 const int unit = w + BG::NW * u;
                 if (unit < NU) {
+                    const int fb = (unit < BG::DT ? unit : unit - BG::DT) * 32;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int f = (unit < BG::DT ? unit : unit - BG::DT) * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int f0 = fb + 8 * q4 + 4 * h;
+                        f32x4 x{out[u][4 * q4], out[u][4 * q4 + 1], out[u][4 * q4 + 2], out[u][4 * q4 + 3]};
                         if (unit < BG::DT) {
-                            sOV.p[sOV.at(n, f)] = Io<T, IO>::out(out[u][r]);
+                            sOV.write4(n, f0, out4<T, IO>(x));
                         } else {
-                            float rf = 0.f;
+                            const auto bv = sB.read4(n, f0);
+                            const f32x4 rf = *reinterpret_cast<const f32x4 *>(sRf + f0);
 #pragma unroll
-                            for (int sl = 0; sl < RS; ++sl) rf += sRp[sl * D + f];
-                            sOK.p[sOK.at(n, f)] = Io<T, IO>::out((out[u][r] + rf) * IO::phi::df((float)sB.p[sB.at(n, f)]));
+                            for (int e = 0; e < 4; ++e) x[e] = (x[e] + rf[e]) * IO::phi::df((float)bv[e]);
+                            sOK.write4(n, f0, out4<T, IO>(x));
                         }
                     }
                 }

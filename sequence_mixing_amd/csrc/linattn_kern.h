@@ -287,6 +287,10 @@ struct Tile {
     {
         *reinterpret_cast<typename Vt<E>::v4 *>(p + at(r, c)) = x;
     }
+    __device__ __forceinline__ typename Vt<E>::v4 read4(int r, int c) const
+    {
+        return *reinterpret_cast<const typename Vt<E>::v4 *>(p + at(r, c));
+    }
     __device__ __forceinline__ void write16(int r, int c, typename Vt<E>::g16 x) const
     {
         *reinterpret_cast<typename Vt<E>::g16 *>(p + at(r, c)) = x;
