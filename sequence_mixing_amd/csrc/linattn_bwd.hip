@@ -206,6 +206,7 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
     __shared__ __attribute__((aligned(16))) T smVl[SPLITV ? kBC * D : 8];
     __shared__ __attribute__((aligned(16))) float sZt[kBC * D];  // z_t of every token of the chunk, [t][i]
     __shared__ __attribute__((aligned(16))) float sZp[D];        // z before the chunk
+    __shared__ float sZq[BGeo<T, D, DQ_WAVES(D)>::TH];            // z over each quarter of the chunk's tokens
     __shared__ float sH[kBC];
     const Tile<T, D> sA{smA}, sB{smB}, sV{smV}, sG{smG}, sO{OWN_O ? smO : smG}, sS{smS}, sBl{smBl}, sGl{smGl};
     const Tile<T, D> sVl{smVl};
@@ -290,16 +291,34 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
             }
         }
         lds_barrier();
-        // ---- z before the chunk and z_t after each of its tokens
-        if (causal && tid < D) {
-            float z = zrun;
-            sZp[tid] = z;
-            for (int t = 0; t < kBC; ++t) {
-                z += (float)sB.p[sB.at(t, tid)];
-                if constexpr (SPLIT) z += (float)sBl.p[sBl.at(t, tid)];
-                sZt[t * D + tid] = z;
+        // ---- z before the chunk and z_t after each of its tokens: thread
+        // (quarter zq, feature zf) sums its quarter of the chunk's tokens,
+        // then adds the quarters before it and z before the chunk
+        if (causal) {
+            constexpr int ZQ = BG::TH / D, ZT = kBC / ZQ;  // token quarters, tokens per quarter
+            const int zf = tid % D, zq = tid / D;
+            float loc[ZT];
+            float z = 0.f;
+#pragma unroll
+            for (int i = 0; i < ZT; ++i) {
+                const int t = zq * ZT + i;
+                z += (float)sB.p[sB.at(t, zf)];
+                if constexpr (SPLIT) z += (float)sBl.p[sBl.at(t, zf)];
+                loc[i] = z;
             }
-            zrun = z;
+            sZq[zq * D + zf] = z;
+            if (zq == 0) sZp[zf] = zrun;
+            lds_barrier();
+            float off = sZp[zf], all = 0.f;
+#pragma unroll
+            for (int q2 = 0; q2 < ZQ; ++q2) {
+                const float x = sZq[q2 * D + zf];
+                if (q2 < zq) off += x;
+                all += x;
+            }
+#pragma unroll
+            for (int i = 0; i < ZT; ++i) sZt[(zq * ZT + i) * D + zf] = off + loc[i];
+            if (zq == 0) zrun += all;
         }
         lds_barrier();
         for (int hh = 0; hh < G; ++hh) {
