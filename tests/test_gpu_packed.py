@@ -64,7 +64,8 @@ def run_packed(lens, H, Hkv, d, dtype, causal, normalise, chunk=0, seed=0):
 @pytest.mark.parametrize("causal", [1, 0])
 @pytest.mark.parametrize("normalise", [1, 0])
 @pytest.mark.parametrize("H,Hkv,d,dtype", [(4, 4, 64, "f32"), (8, 2, 128, "bf16"), (2, 1, 32, "bf16"),
-                                           (6, 3, 64, "bf16"), (4, 2, 64, "f16")])
+                                           (6, 3, 64, "bf16"), (4, 2, 64, "f16"), (2, 2, 32, "f32"),
+                                           (4, 2, 128, "f32")])
 def test_packed_mixed_lengths(H, Hkv, d, dtype, causal, normalise):
     lens = lengths_mix(9, 1, 1500, seed=d + H, extra=(0, 1, 33, 700))
     run_packed(lens, H, Hkv, d, dtype, causal, normalise, seed=H * d)
