@@ -619,13 +619,18 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
             auto step = [&](int c, PSet &r) {
                 const int t0 = s0 + c * C, nb = (c + 1) & 1;
                 phase1(c, t0, Tile<T, D>{smK[c & 1]}, Tile<T, D>{smV[c & 1]});
-                // while the other waves finish phase 1 of chunk c: K, V of chunk c+1
-                if (c + 1 < nch) p_stage_kv(r, nb, min(C, N - t0 - C));
                 lds_barrier();
-                // while they run phase 2: the outputs of chunk c-1 (parked in
-                // buffer nb) out, phi(q) of chunk c+1 in, chunk c+3 requested
+                // while the other waves run phase 2 (from buffer c & 1): the
+                // outputs of chunk c-1 (parked in buffer nb) out, K, V and
+                // phi(q) of chunk c+1 into buffer nb, chunk c+3 requested.
+                // K and V are staged here rather than beside phase 1, which
+                // these waves also run: per-wave clocks put the staging half
+                // on the critical path of the first half-step.
                 if (c >= 1) p_out(nb, t0 - C);
-                if (c + 1 < nch) p_stage_q(r, nb);
+                if (c + 1 < nch) {
+                    p_stage_kv(r, nb, min(C, N - t0 - C));
+                    p_stage_q(r, nb);
+                }
                 p_load(r, t0 + 3 * C);  // past the segment: no access
                 lds_barrier();
             };
