@@ -481,6 +481,76 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
             }
         }
     };
+    // Half-query items (HQ: the fp32 d = 64 staging-wave shapes whose units
+    // are split over two waves): item (u, qh) takes queries 16 qh .. 16 qh + 15
+    // of unit u and every output column, on the 16x16x4 fp32 instruction
+    // (lane (j, kq), j = lane % 16, kq = lane / 16, supplies A[j][kq] and
+    // B[kq][j]; register r of its result is row 4 kq + r, column j).  Split
+    // by queries, the two items of a unit share no scores: split by output
+    // columns, as unit_run does, each recomputed the unit's whole 32 x 32
+    // score tile.  Instruction (s, e) takes feature 16 s + 4 kq + e in slot
+    // kq, so phi(q), phi(k) and the state copy are read four features (16
+    // bytes) at a time; scores come out with key 16 kt + 4 kq + r in register
+    // r of lane (query j, kq), which is the B operand of O^T += V^T P as it
+    // stands.
+    constexpr bool HQ = sizeof(T) == 4 && D == 64 && PIPE && M::PARTS == 2 && RPC == 1 && !M::SHIFT && !DK;
+    auto unit_run_hq = [&](int u, int qh, Tile<T, D> sK, Tile<T, D> sV, Tile<T, D> sQ) {
+        const int g = u / CT, r = u % CT, j = r;
+        const int jq = lane & 15, kq = lane >> 4;
+        const int qrow = g * C + r * 32 + 16 * qh + jq;  // the query of this lane's column
+        constexpr int NS = D / 16;
+        f32x4 bq[NS];
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) bq[s2] = *reinterpret_cast<const f32x4 *>(sQ.p + sQ.at(qrow, 16 * s2 + 4 * kq));
+        // scores of the diagonal key tile, masked (key <= query), and their sum
+        float pm[2][4], ds = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            f32x4 P = f32x4{};
+#pragma unroll
+            for (int s2 = 0; s2 < NS; ++s2) {
+                const f32x4 ak = *reinterpret_cast<const f32x4 *>(sK.p + sK.at(r * 32 + 16 * kt + jq, 16 * s2 + 4 * kq));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) P = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[e], bq[s2][e], P, 0, 0, 0);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                pm[kt][rr] = 16 * kt + 4 * kq + rr <= 16 * qh + jq ? P[rr] : 0.f;
+                ds += pm[kt][rr];
+            }
+        }
+        // the state copy's part of the denominator: phi(q) . z_j
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) {
+            const f32x4 zz = *reinterpret_cast<const f32x4 *>(&smZ[j][16 * s2 + 4 * kq]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ds += bq[s2][e] * zz[e];
+        }
+        ds += __shfl_xor(ds, 16);
+        ds += __shfl_xor(ds, 32);
+        const float inv = normalise ? 1.f / ds : 1.f;
+        const Tile<T, D> sST{smST[j]};
+#pragma unroll
+        for (int ct = 0; ct < NS; ++ct) {
+            // O^T[column][query]: V^T P over the diagonal tile's keys, then S_j^T phi(q)^T
+            f32x4 O = f32x4{};
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const float av = sV.p[sV.at(r * 32 + 16 * kt + 4 * kq + rr, 16 * ct + jq)];
+                    O = __builtin_amdgcn_mfma_f32_16x16x4f32(av, pm[kt][rr], O, 0, 0, 0);
+                }
+#pragma unroll
+            for (int s2 = 0; s2 < NS; ++s2) {
+                const f32x4 as = *reinterpret_cast<const f32x4 *>(sST.p + sST.at(16 * ct + jq, 16 * s2 + 4 * kq));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) O = __builtin_amdgcn_mfma_f32_16x16x4f32(as[e], bq[s2][e], O, 0, 0, 0);
+            }
+            // register rr is column 16 ct + 4 kq + rr of query jq: park four columns at once
+            sQ.write4(qrow, 16 * ct + 4 * kq, out4<T, IO>(f32x4{O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv}));
+        }
+    };
 
     if constexpr (!PIPE) {
         const Tile<T, D> sK{smK[0]}, sV{smV[0]};
@@ -673,7 +743,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                 const int u_split = w / M::PARTS;
                 const bool has_split = M::PARTS > 1 && w < M::NWI && t0 + (u_split % CT) * 32 < N;
                 v8 qf_split[KBD];
-                if constexpr (M::PARTS > 1) {
+                if constexpr (M::PARTS > 1 && !HQ) {
                     if (has_split) unit_qf(u_split, qf_split, tq);
                 }
                 phase1(c, t0, tk, tv);
@@ -685,6 +755,9 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                         unit_qf(u, qf, tq);
                         unit_run(u, 0, qf, tk, tv, tq);
                     }
+                } else if constexpr (HQ) {
+                    // each item reads and parks only its own 16 query rows
+                    if (has_split) unit_run_hq(u_split, w % 2, tk, tv, tq);
                 } else {
                     if (has_split) unit_run(u_split, (w % M::PARTS) * M::CTP, qf_split, tk, tv, tq);
                 }
