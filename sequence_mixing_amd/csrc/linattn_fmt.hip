@@ -499,20 +499,43 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         const int jq = lane & 15, kq = lane >> 4;
         const int qrow = g * C + r * 32 + 16 * qh + jq;  // the query of this lane's column
         constexpr int NS = D / 16;
-        f32x4 bq[NS];
+        const Tile<T, D> sST{smST[j]};
+        // Every LDS operand is requested ahead of the matrix instructions that
+        // use it: phi(q) and the diagonal tile's keys first; the value words
+        // and state-copy rows of output tile ct + 1 while tile ct is computed
+        // (scheduling barriers keep the compiler from sinking those reads
+        // next to their first use, where each group of four instructions
+        // waited for its own read).
+        f32x4 bq[NS], ak[2][NS];
 #pragma unroll
         for (int s2 = 0; s2 < NS; ++s2) bq[s2] = *reinterpret_cast<const f32x4 *>(sQ.p + sQ.at(qrow, 16 * s2 + 4 * kq));
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int s2 = 0; s2 < NS; ++s2)
+                ak[kt][s2] = *reinterpret_cast<const f32x4 *>(sK.p + sK.at(r * 32 + 16 * kt + jq, 16 * s2 + 4 * kq));
+        float av[2][2][4];
+        f32x4 as[2][NS];
+        auto load_o = [&](int ct, int b) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) av[b][kt][rr] = sV.p[sV.at(r * 32 + 16 * kt + 4 * kq + rr, 16 * ct + jq)];
+#pragma unroll
+            for (int s2 = 0; s2 < NS; ++s2)
+                as[b][s2] = *reinterpret_cast<const f32x4 *>(sST.p + sST.at(16 * ct + jq, 16 * s2 + 4 * kq));
+        };
+        load_o(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         // scores of the diagonal key tile, masked (key <= query), and their sum
         float pm[2][4], ds = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             f32x4 P = f32x4{};
 #pragma unroll
-            for (int s2 = 0; s2 < NS; ++s2) {
-                const f32x4 ak = *reinterpret_cast<const f32x4 *>(sK.p + sK.at(r * 32 + 16 * kt + jq, 16 * s2 + 4 * kq));
+            for (int s2 = 0; s2 < NS; ++s2)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) P = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[e], bq[s2][e], P, 0, 0, 0);
-            }
+                for (int e = 0; e < 4; ++e) P = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[kt][s2][e], bq[s2][e], P, 0, 0, 0);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 pm[kt][rr] = 16 * kt + 4 * kq + rr <= 16 * qh + jq ? P[rr] : 0.f;
@@ -529,24 +552,21 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         ds += __shfl_xor(ds, 16);
         ds += __shfl_xor(ds, 32);
         const float inv = normalise ? 1.f / ds : 1.f;
-        const Tile<T, D> sST{smST[j]};
 #pragma unroll
         for (int ct = 0; ct < NS; ++ct) {
+            const int b = ct & 1;
+            if (ct + 1 < NS) load_o(ct + 1, b ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
             // O^T[column][query]: V^T P over the diagonal tile's keys, then S_j^T phi(q)^T
             f32x4 O = f32x4{};
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const float av = sV.p[sV.at(r * 32 + 16 * kt + 4 * kq + rr, 16 * ct + jq)];
-                    O = __builtin_amdgcn_mfma_f32_16x16x4f32(av, pm[kt][rr], O, 0, 0, 0);
-                }
+                for (int rr = 0; rr < 4; ++rr) O = __builtin_amdgcn_mfma_f32_16x16x4f32(av[b][kt][rr], pm[kt][rr], O, 0, 0, 0);
 #pragma unroll
-            for (int s2 = 0; s2 < NS; ++s2) {
-                const f32x4 as = *reinterpret_cast<const f32x4 *>(sST.p + sST.at(16 * ct + jq, 16 * s2 + 4 * kq));
+            for (int s2 = 0; s2 < NS; ++s2)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) O = __builtin_amdgcn_mfma_f32_16x16x4f32(as[e], bq[s2][e], O, 0, 0, 0);
-            }
+                for (int e = 0; e < 4; ++e) O = __builtin_amdgcn_mfma_f32_16x16x4f32(as[b][s2][e], bq[s2][e], O, 0, 0, 0);
             // register rr is column 16 ct + 4 kq + rr of query jq: park four columns at once
             sQ.write4(qrow, 16 * ct + 4 * kq, out4<T, IO>(f32x4{O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv}));
         }
