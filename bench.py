@@ -908,6 +908,11 @@ def gpu_clocks():
     import re
     import subprocess
 
+    # Under a profiler that preloads itself into child processes the tool's
+    # interpreter would start with the GPU already initialised and could not
+    # re-exec itself: the figures are left out there.
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
         data = json.loads(r.stdout)
