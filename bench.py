@@ -9,14 +9,19 @@ chunked main pass.  Inputs are seeded N(0, 1) tensors already resident in
 HBM.  ``value`` and ``ms_per_step`` are cold: the K timed steps each run on
 their own copy of the inputs (enough copies that more than twice the 256 MiB
 memory-side cache is moved between two uses of one copy), captured as one HIP
-graph and replayed after a cache sweep (a 512 MiB read, outside the timed
-region); the device time between two HIP events over K, median of 5 replays.
+graph that is replayed right behind another graph of K steps continuing the
+same rotation, after a cache sweep (a 512 MiB read); the device time between
+two HIP events around the second graph over K, median of 5 measurements (the
+first graph keeps the host's graph submission out of the timed region).
 ``roofline`` prices the dominant kernel (the chunked main pass) against HBM:
-algorithmic bytes (Q, K, V read once, O written once) per launch over its
-median duration in W warm-up and K steps that each follow a cache sweep and
-run through ``linattn_fwd_timed`` (events on the call's stream around each
-stage; created without the system-scope fence, which costs about 1 us per
-event here); ``roofline_path`` prices the whole cold step the same way.
+algorithmic bytes (Q, K, V read once, O written once) per launch over its cold
+duration per launch, taken as the difference between the rotated cold steps
+above and the same steps without their last stage (``linattn_fwd_timed`` with
+reps = 0, also one HIP graph after a sweep), so that no event pair sits around
+a launch.  ``stage_us`` holds each stage between HIP events (on the call's
+stream, created without the system-scope fence, which costs about 1 us per
+event here) in K steps that each follow a cache sweep; ``roofline_path``
+prices the whole cold step.
 ``warm`` holds the same step with the caches warm: replayed K times back to
 back from one HIP graph on the same inputs (checked bitwise against an eager
 call), the eager rate with host launches, and the main pass launched 10 times
@@ -241,11 +246,19 @@ def time_graph(la, hip, torch, args, out, steps):
 def time_rotated(la, hip, torch, w, causal, chunk, steps, flush, out_check=True):
     """K steps, each on its own copy of the inputs (enough copies that the
     steps between two uses of one copy move more than twice the 256 MiB
-    memory-side cache), captured as one HIP graph and replayed after a cache
-    sweep; device time between two events over K.  Every step reads its inputs
-    from HBM and there is no host or event work between steps.  Returns the
-    median over 5 replays (ms per step), the copies used, and whether copy 0's
-    output from the replay equals an eager call's bitwise."""
+    memory-side cache), so every step reads its inputs from HBM.  Two graphs
+    of K steps each are captured, the second continuing the rotation of the
+    first (its step i takes copy (K + i) mod copies, which the first graph
+    last used `copies` steps earlier); per measurement the cache is swept, the
+    first graph replayed, then the second, and the second is timed between two
+    HIP events: its launch was submitted while the first ran, so the host's
+    graph submission is not inside the timed region and no host or event work
+    sits between steps.  The same is done for the steps without their last
+    stage (linattn_fwd_timed with reps = 0): the difference prices the last
+    stage per launch, cold, without an event pair around each launch.
+    Returns the medians over 5 measurements (ms per step, with and without the
+    last stage), the copies used, and whether copy 0's output from a replay
+    equals an eager call's bitwise."""
     from linattn_inputs import workload_qkv
     from sequence_mixing_amd import ops
 
@@ -266,29 +279,38 @@ def time_rotated(la, hip, torch, w, causal, chunk, steps, flush, out_check=True)
     with torch.cuda.stream(side):
         la.linattn_fwd(*argv[0], side.cuda_stream)
     torch.cuda.current_stream().wait_stream(side)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        cap = torch.cuda.current_stream().cuda_stream
-        for i in range(steps):
-            rc = la.linattn_fwd(*argv[i % ncopy], cap)
-            if rc != 0:
-                raise la.LinattnError(rc, "linattn_fwd (graph capture)")
+    evs = [hip.event() for _ in range(4)]
+
+    def capture(step, first):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream().cuda_stream
+            for i in range(first, first + steps):
+                rc = step(argv[i % ncopy], cap)
+                if rc != 0:
+                    raise la.LinattnError(rc, "linattn_fwd (graph capture)")
+        return g
+
+    full = [capture(lambda a, cap: la.linattn_fwd(*a, cap), f) for f in (0, steps)]
+    pre = [capture(lambda a, cap: la.linattn_fwd_timed(*a, cap, events=evs, reps=0), f) for f in (0, steps)]
     copies[0][3].zero_()
-    g.replay()
+    full[0].replay()
     torch.cuda.synchronize()
     same = bool(torch.equal(copies[0][3], ref))
     stream = torch.cuda.current_stream().cuda_stream
     e0, e1 = hip.event(), hip.event()
-    per = []
+    per, per_pre = [], []
     for _ in range(5):
-        flush()
-        hip.record(e0, stream)
-        g.replay()
-        hip.record(e1, stream)
-        torch.cuda.synchronize()
-        per.append(hip.ms(e0, e1) / steps)
-    del g, copies, argv, ws, ref
-    return {"ms": median(per), "copies": ncopy, "matches_eager": same}
+        for (ga, gb), acc in ((full, per), (pre, per_pre)):
+            flush()
+            ga.replay()
+            hip.record(e0, stream)
+            gb.replay()
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            acc.append(hip.ms(e0, e1) / steps)
+    del full, pre, copies, argv, ws, ref
+    return {"ms": median(per), "pre_ms": median(per_pre), "copies": ncopy, "matches_eager": same}
 
 
 class Flush:
@@ -306,8 +328,9 @@ class Flush:
 
 
 def timing_note(steps, copies):
-    return (f"cold: {steps} steps each on its own copy of the inputs ({copies} copies), replayed from one HIP "
-            "graph after a cache sweep; device time by events / steps, median of 5 replays")
+    return (f"cold: {steps} steps each on its own copy of the inputs ({copies} copies, rotated), one HIP graph "
+            "replayed behind another of the same rotation after a cache sweep; device time by events / steps, "
+            "median of 5 replays")
 
 
 def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, flush, tag="", cold_only=False):
@@ -331,6 +354,10 @@ def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, flush, tag=
     kname = kernel_name(w, c, causal)
     cold = time_stages(la, hip, torch, args, steps, warmup, stream, flush=flush, reps=1)
     rot = time_rotated(la, hip, torch, w, causal, chunk, steps, flush)
+    # the last stage per launch, cold: whole steps minus steps without it (rotated graphs)
+    main_s = (rot["ms"] - rot["pre_ms"]) / 1e3
+    main_label = kname + " (cold, per launch: rotated steps with it minus steps without it)"
+    main_rot = {"us": round(main_s * 1e6, 2), "steps_without_it_ms": round(rot["pre_ms"], 5)}
     if cold_only:
         step_s = rot["ms"] / 1e3
         return {"causal": bool(causal), "chunk": c, "segments": P, "ms_per_step": round(rot["ms"], 5),
@@ -339,8 +366,8 @@ def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, flush, tag=
                 "stage_us": {"seg_totals": round(cold["stage_ms"][0] * 1e3, 2),
                              "seg_scan": round(cold["stage_ms"][1] * 1e3, 2),
                              "main": round(cold["stage_ms"][2] * 1e3, 2)},
-                "roofline_main": roofline(nb, fl, cold["stage_ms"][2] / 1e3, w.dtype, kname + " (cold, per launch)",
-                                          measured_traffic(tag, kname[:-1] + ",")),
+                "main_rotated": main_rot,
+                "roofline_main": roofline(nb, fl, main_s, w.dtype, main_label, measured_traffic(tag, kname[:-1] + ",")),
                 "roofline_path": roofline(nb, fl, step_s, w.dtype, "whole step (cold)")}
     eager_s = time_eager(la, torch, args, steps, warmup, stream)
     gr = time_graph(la, hip, torch, args, out, steps)
@@ -357,8 +384,8 @@ def fwd_row(la, hip, torch, w, causal, chunk, steps, warmup, stream, flush, tag=
         "stage_us": {"seg_totals": round(cold["stage_ms"][0] * 1e3, 2),
                      "seg_scan": round(cold["stage_ms"][1] * 1e3, 2),
                      "main": round(cold["stage_ms"][2] * 1e3, 2)},
-        "roofline_main": roofline(nb, fl, cold["stage_ms"][2] / 1e3, w.dtype, kname + " (cold, per launch)",
-                                  measured_traffic(tag, kname[:-1] + ",")),
+        "main_rotated": main_rot,
+        "roofline_main": roofline(nb, fl, main_s, w.dtype, main_label, measured_traffic(tag, kname[:-1] + ",")),
         "roofline_path": roofline(nb, fl, step_s, w.dtype, "whole step (cold)"),
         "warm": {
             "ms_per_step": round(gr["event_ms"], 5), "tokens_per_s": round(w.B * w.N / (gr["event_ms"] / 1e3), 1),

@@ -186,8 +186,11 @@ int linattn_fwd_packed(const void *q, const void *k, const void *v, void *out, c
  * `reps` (>= 1) times back to back between events[2] and events[3], with
  * the same result: (events[3] - events[2]) / reps is then its duration per
  * launch without the cost of recording an event around every launch.
+ * reps == 0 launches the first two stages only (out is not written; events[2]
+ * and events[3] coincide): a caller can then price the last stage as the
+ * difference between timings of calls with and without it.
  * `events` points to n_events == 4 events created by the caller
- * (hipEventCreate); otherwise LINATTN_ERR_NULL is returned.  reps < 1 is
+ * (hipEventCreate); otherwise LINATTN_ERR_NULL is returned.  reps < 0 is
  * LINATTN_ERR_SHAPE.
  */
 int linattn_fwd_timed(const void *q, const void *k, const void *v, void *out,

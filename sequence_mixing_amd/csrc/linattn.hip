@@ -233,7 +233,7 @@ int linattn_fwd_timed(const void *q, const void *k, const void *v, void *out, in
     if (!events || n_events != 4) return LINATTN_ERR_NULL;
     for (int i = 0; i < 4; ++i)
         if (!events[i]) return LINATTN_ERR_NULL;
-    if (reps < 1) return LINATTN_ERR_SHAPE;
+    if (reps < 0) return LINATTN_ERR_SHAPE;
     const Timing t{events, reps};
     if (B > 0 && N > 0)
         return fwd_impl(q, k, v, out, B, H, Hkv, N, d, causal, normalise, dtype, state_out, z_out, chunk,

@@ -361,7 +361,8 @@ def test_last_causal_row_equals_noncausal():
 
 @pytest.mark.parametrize("causal", [1, 0])
 def test_timed_entry_point_with_repeats_matches_plain_call(causal):
-    """linattn_fwd_timed (last stage launched 3 times) leaves exactly the output of linattn_fwd."""
+    """linattn_fwd_timed (last stage launched 3 times) leaves exactly the output of linattn_fwd; with 0
+    launches of the last stage it leaves the output untouched."""
     B, H, Hkv, N, d = 2, 8, 2, 900, 64
     q, k, v = (t.contiguous().cuda() for t in make_qkv(B, H, Hkv, N, d, "bf16", 333))
     ref, S_ref, z_ref = ops.fwd(q, k, v, causal=causal, want_state=True)
@@ -381,8 +382,14 @@ def test_timed_entry_point_with_repeats_matches_plain_call(causal):
     assert rc == 0
     torch.cuda.synchronize()
     assert torch.equal(out, ref) and torch.equal(S, S_ref) and torch.equal(z, z_ref)
+    # reps = 0: the first two stages only, the output is left as it was
+    out.fill_(7.0)
     assert la.linattn_fwd_timed(q, k, v, out, B, H, Hkv, N, d, causal, 1, la.LINATTN_BF16, S, z, 0, ws, nbytes,
-                                None, events=evs, reps=0) == -2
+                                None, events=evs, reps=0) == 0
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    assert la.linattn_fwd_timed(q, k, v, out, B, H, Hkv, N, d, causal, 1, la.LINATTN_BF16, S, z, 0, ws, nbytes,
+                                None, events=evs, reps=-1) == -2
 
 
 # ------------------------------------------- continuing from given start sums
