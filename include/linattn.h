@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 11
+#define LINATTN_ABI_VERSION 12
 
 enum { LINATTN_F32 = 0, LINATTN_BF16 = 1, LINATTN_F16 = 2, LINATTN_FP8_E4M3 = 3, LINATTN_FP8_E5M2 = 4 };
 /* Feature maps phi (README "Features": custom kernel plugins, phi
