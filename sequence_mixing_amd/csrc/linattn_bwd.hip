@@ -68,13 +68,11 @@ struct BGeo {
     static constexpr int NST = DT * DT;
     static constexpr int MAXST = (NST + NW - 1) / NW;
     static constexpr int E = (int)sizeof(T);
-    // Several workgroups per CU (their waves on one SIMD hide each other's
-    // waits) where the registers allow: three for 16-bit rows up to d = 64
-    // (measured: the bf16 d = 64 walks 69 -> 59 us and 65 -> 58 us against two;
-    // four spill), two for the fp32 dq walk up to d = 64 and the fp32 dk/dv
-    // walk (two sets of output accumulators) up to 128 bytes per row.
-    static constexpr int OCC_DQ = D <= 64 ? (E == 2 ? 3 : 2) : 1;
-    static constexpr int OCC_DKV = D * E <= 128 ? (E == 2 ? 3 : 2) : 1;
+    // Two workgroups per CU (two waves per SIMD hide each other's waits) where
+    // the registers allow it without spilling: the dq walk up to d = 64, the
+    // dk/dv walk (two sets of output accumulators) up to 128 bytes per row.
+    static constexpr int OCC_DQ = D <= 64 ? 2 : 1;
+    static constexpr int OCC_DKV = D * E <= 128 ? 2 : 1;
     __device__ static int tile_of(int w, int i) { return w * MAXST + i; }
 };
 
@@ -182,8 +180,8 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
                                                       const T *__restrict__ v, const T *__restrict__ o,
                                                       const T *__restrict__ dout, T *__restrict__ dq,
                                                       float *__restrict__ den_out, const float *__restrict__ ws,
-                                                      int H, int Hkv, int N, int G, int P, int seg_len, int causal,
-                                                      int normalise)
+                                                      float *__restrict__ ws_r, int H, int Hkv, int N, int G, int P,
+                                                      int seg_len, int causal, int normalise)
 {
     using BG = BGeo<T, D, DQ_WAVES(D)>;
     using g16 = typename Vt<T>::g16;
@@ -210,6 +208,14 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
     __shared__ __attribute__((aligned(16))) float sZp[D];        // z before the chunk
     __shared__ float sZq[BGeo<T, D, DQ_WAVES(D)>::TH];            // z over each quarter of the chunk's tokens
     __shared__ float sH[kBC];
+    // 16-bit rows at d <= 64: this walk also forms the segment's sums
+    // R = sum a g^T and r = sum h a over its tokens and the group's heads (the
+    // a, g and h tiles are in LDS here anyway), which the dk/dv walk needs
+    // from the segments after its own; otherwise (the registers are short) a
+    // pass of k_bwd_dkv<totals> forms them.
+    constexpr bool RT = sizeof(T) == 2 && D <= 64;
+    constexpr int RS = BG::TH / D;  // row slices of the r partial sums
+    __shared__ float sRp[RT ? RS * D : 1];
     const Tile<T, D> sA{smA}, sB{smB}, sV{smV}, sG{smG}, sO{OWN_O ? smO : smG}, sS{smS}, sBl{smBl}, sGl{smGl};
     const Tile<T, D> sVl{smVl};
 
@@ -254,6 +260,12 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
         if (tid < D) sZp[tid] = zt;
         for (int e = tid; e < kBC * D; e += BG::TH) sZt[e] = zt;
     }
+
+    f32x16 Rt[RT ? BG::MAXST : 1];
+#pragma unroll
+    for (int i = 0; i < (RT ? BG::MAXST : 1); ++i) Rt[i] = f32x16{};
+    const int rcol = tid % D, rsl = tid / D;
+    float rpart = 0.f;
 
     g16 kr[LDV], vr[LDV], qr[LDV], orr[LDV], dr[LDV];
     load_rows<T, D, BG::TH>(kr, kb, s0, rows_of(0), tid);
@@ -422,6 +434,17 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
                     sO.write4(n, i0, out4<T, IO>(x));
                 }
             }
+            if constexpr (RT) {
+                // R += A^T G, r += A^T h over this head's tokens of the chunk
+#pragma unroll
+                for (int i = 0; i < BG::MAXST; ++i) {
+                    const int st = BG::tile_of(w, i);
+                    if (st < BG::NST) tile_state_update<T, D>(Rt[i], false, st / BG::DT, st % BG::DT, 0, sA, sG, lane);
+                }
+#pragma unroll
+                for (int t = rsl * (kBC / RS); t < (rsl + 1) * (kBC / RS); ++t)
+                    rpart += sH[t] * (float)sA.p[sA.at(t, rcol)];
+            }
             if (causal && hh == G - 1) {
 #pragma unroll
                 for (int i = 0; i < BG::MAXST; ++i) {
@@ -439,6 +462,31 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
                     if (BG::NGRP % BG::TH == 0 || e < BG::NGRP)
                         buf_store16<g16>(rdq, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sO.p + sO.at(t, cq)));
                 }
+            }
+        }
+    }
+    if constexpr (RT) {
+        // the segment's R, r: slot p - 1 of the causal suffix sums (segment 0
+        // is no later segment's), slot p of the non-causal total
+        if (!causal || p > 0) {
+            const int nsl = causal ? P - 1 : P;
+            float *dst = ws_r + ((size_t)sq * nsl + (causal ? p - 1 : p)) * (size_t)D * (D + 1);
+#pragma unroll
+            for (int i = 0; i < BG::MAXST; ++i) {
+                const int st = BG::tile_of(w, i);
+                if (st < BG::NST) {
+                    const int it = st / BG::DT, jt = st % BG::DT;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dst[(size_t)(it * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * D + jt * 32 + n] = Rt[i][r];
+                }
+            }
+            sRp[rsl * D + rcol] = rpart;
+            lds_barrier();
+            if (tid < D) {
+                float rf = 0.f;
+                for (int sl = 0; sl < RS; ++sl) rf += sRp[sl * D + tid];
+                dst[(size_t)D * D + tid] = rf;
             }
         }
     }
@@ -742,12 +790,10 @@ int bwd_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, BwdPlan
     BwdPlan p{};
     p.nseq = B * Hkv;
     p.G = H / Hkv;
-    // Segments: one resident round of the walks' workgroups (one per sequence
-    // and segment) where they run three per CU (16-bit rows, d <= 64: 768),
-    // about 512 otherwise; segments are whole chunks of 32 tokens.
+    // Segments: about 512 workgroups for the walks (one per sequence and
+    // segment), segments whole chunks of 32 tokens.
     const int nchunks = (N + kBC - 1) / kBC;
-    const int tgt = (e == 2 && d <= 64) ? 768 : 512;
-    int P = p.nseq > 0 ? (tgt + p.nseq - 1) / p.nseq : 1;
+    int P = p.nseq > 0 ? (512 + p.nseq - 1) / p.nseq : 1;
     if (P > nchunks) P = nchunks;
     if (P < 1) P = 1;
     p.seg_len = ((nchunks + P - 1) / P) * kBC;
@@ -791,24 +837,29 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
                            1, (float *)nullptr, (float *)nullptr, (const float *)nullptr, (const float *)nullptr);
     }
     // 2. dq (and den)
+    // (16-bit rows, d <= 64: the dq walk also writes each segment's sums of a g^T and h a)
+    constexpr bool RT = sizeof(T) == 2 && D <= 64;
     hipLaunchKernelGGL((k_bwd_dq<T, D, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D, DQ_WAVES(D)>::TH), 0, st, qq, kk, vv, oo, dd,
-                       static_cast<T *>(dq), wden, (const float *)wf, H, Hkv, N, pl.G, P, pl.seg_len, causal,
-                       normalise);
-    // 3. sums of a g^T and h a per segment: causal segments 1..P-1, suffix scan
+                       static_cast<T *>(dq), wden, (const float *)wf, RT ? wr : (float *)nullptr, H, Hkv, N, pl.G, P,
+                       pl.seg_len, causal, normalise);
+    // 3. sums of a g^T and h a per segment (otherwise their own pass):
+    // causal segments 1..P-1 with a suffix scan, non-causal all and their sum
     if (causal) {
         if (P > 1) {
-            hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * (P - 1)), dim3(BGeo<T, D, DKV_WAVES(D, true)>::TH), 0, st, qq, kk, vv,
-                               oo, dd, (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P,
-                               pl.seg_len, causal, normalise, P - 1, 1);
+            if (!RT)
+                hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * (P - 1)), dim3(BGeo<T, D, DKV_WAVES(D, true)>::TH), 0, st, qq, kk, vv,
+                                   oo, dd, (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P,
+                                   pl.seg_len, causal, normalise, P - 1, 1);
             if (P > 2)
                 hipLaunchKernelGGL(k_seg_scan, scan_grid(D, pl.nseq), dim3(kThreads), 0, st,
                                    wr, P - 1, D, 2, (float *)nullptr, (float *)nullptr, (const float *)nullptr,
                                    (const float *)nullptr);
         }
     } else {
-        hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D, DKV_WAVES(D, true)>::TH), 0, st, qq, kk, vv, oo, dd,
-                           (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P, pl.seg_len,
-                           causal, normalise, P, 0);
+        if (!RT)
+            hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D, DKV_WAVES(D, true)>::TH), 0, st, qq, kk, vv, oo, dd,
+                               (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P, pl.seg_len,
+                               causal, normalise, P, 0);
         hipLaunchKernelGGL(k_seg_scan, scan_grid(D, pl.nseq), dim3(kThreads), 0, st, wr, P, D,
                            1, (float *)nullptr, (float *)nullptr, (const float *)nullptr, (const float *)nullptr);
     }
