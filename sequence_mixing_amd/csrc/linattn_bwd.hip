@@ -69,10 +69,10 @@ struct BGeo {
     static constexpr int MAXST = (NST + NW - 1) / NW;
     static constexpr int E = (int)sizeof(T);
     // Two workgroups per CU (two waves per SIMD hide each other's waits) where
-    // the registers allow it without spilling: the dq walk up to d = 64, the
-    // dk/dv walk (two sets of output accumulators) up to 128 bytes per row.
+    // the registers allow it without spilling vector registers: both walks up
+    // to d = 64 (the fp32 dk/dv walk then needs 239 of the 256 registers).
     static constexpr int OCC_DQ = D <= 64 ? 2 : 1;
-    static constexpr int OCC_DKV = D * E <= 128 ? 2 : 1;
+    static constexpr int OCC_DKV = D <= 64 ? 2 : 1;
     __device__ static int tile_of(int w, int i) { return w * MAXST + i; }
 };
 

@@ -1088,9 +1088,19 @@ int launch_status()
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Totals pass with chunks of c1 tokens (32, 64 or 128; at most 16 KiB of K per
-// chunk, so that two chunks of K and V double-buffer in 64 KiB of LDS); plain
-// fp32 sums take the pass without staging (k_seg_totals_f32), whatever c1.
+// Largest chunk of the staged totals pass: at most 16 KiB of K per chunk, so
+// that two chunks of K and V double-buffer in 64 KiB of LDS, and for 16-bit
+// rows at most 64 tokens, whose staging registers leave room for two
+// workgroups per CU at d <= 64 (128-token chunks spill there).
+template <typename T, int D> constexpr int totals_cap()
+{
+    constexpr int bytes = 65536 / (4 * D * (int)sizeof(T));
+    constexpr int lim = sizeof(T) == 2 ? 64 : 128;
+    return bytes < lim ? bytes : lim;
+}
+
+// Totals pass with chunks of c1 tokens (32, 64 or 128, at most totals_cap);
+// plain fp32 sums take the pass without staging (k_seg_totals_f32), whatever c1.
 template <typename T, int D, typename IO = Fmt<T, PhiElu1>, bool DK = false>
 int launch_totals(int c1, unsigned nblocks, hipStream_t st, const typename IO::elem *k, const typename IO::elem *v,
                   float *ws, int N, int seg_len,
@@ -1102,7 +1112,7 @@ int launch_totals(int c1, unsigned nblocks, hipStream_t st, const typename IO::e
                            nslots, pk, Hkv, causal);
         return LINATTN_OK;
     }
-    constexpr int cap = 65536 / (4 * D * (int)sizeof(T));
+    constexpr int cap = totals_cap<T, D>();
     switch (c1) {
     case 32:
         hipLaunchKernelGGL((k_seg_totals<T, D, 32, IO, DK>), dim3(nblocks), dim3(2 * kThreads), 0, st, k, v, ws, N, seg_len,
@@ -1129,11 +1139,7 @@ int launch_totals(int c1, unsigned nblocks, hipStream_t st, const typename IO::e
 template <typename T, int D>
 int totals_chunk(int seg_len)
 {
-    // 16-bit rows: at most 64 tokens, whose staging registers leave room for
-    // two workgroups per CU at d <= 64 (128-token chunks spill there)
-    constexpr int cap = 65536 / (4 * D * (int)sizeof(T));
-    constexpr int lim = sizeof(T) == 2 ? 64 : 128;
-    int c1 = cap < lim ? cap : lim;
+    int c1 = totals_cap<T, D>();
     while (c1 > 32 && seg_len % c1 != 0) c1 /= 2;  // segments are whole chunks of the pass
     return c1;
 }
