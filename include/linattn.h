@@ -283,7 +283,9 @@ int linattn_decode_step(float *state, float *z, const void *q, const void *k, co
  * The other arguments are those of linattn_fwd with causal = 1.  Supported:
  * the default feature map (ELU + 1) in any element type, and every chunk
  * except one that makes an fp32 kernel shift its state copies (fp32,
- * d = 64, chunk 128): LINATTN_ERR_UNSUPPORTED otherwise.  The workspace is
+ * d = 64, chunk 128): LINATTN_ERR_UNSUPPORTED otherwise.  chunk = 0 takes
+ * linattn_fwd's automatic chunk, at most 64 tokens for 16-bit rows at
+ * d <= 64.  The workspace is
  * linattn_fwd_decay_workspace_bytes(B, H, Hkv, N, d, dtype, chunk) bytes:
  * that of linattn_fwd plus one float per segment partial.  state_out /
  * z_out may alias neither state_in nor z_in.

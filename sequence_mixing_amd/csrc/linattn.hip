@@ -189,7 +189,9 @@ int linattn_fwd_from_state(const void *q, const void *k, const void *v, void *ou
 size_t linattn_fwd_decay_workspace_bytes(int B, int H, int Hkv, int N, int d, int dtype, int chunk)
 {
     linattn::Plan pl;
-    if (linattn::make_plan(B, H, Hkv, N, d, 1, dtype, chunk, &pl) != LINATTN_OK || !linattn::decay_ok(pl))
+    if (linattn::make_plan(B, H, Hkv, N, d, 1, dtype, linattn::decay_chunk(dtype, d, H, Hkv, chunk), &pl) !=
+            LINATTN_OK ||
+        !linattn::decay_ok(pl))
         return (size_t)-1;
     return linattn::decay_ws_bytes(pl);
 }
@@ -205,8 +207,9 @@ int linattn_fwd_decay(const void *q, const void *k, const void *v, const float *
         return LINATTN_ERR_SHAPE;  // the start sums are read while the final ones are written
     // a g pointer is what selects the decayed kernels: with N == 0 none is read
     static const float no_tokens = 0.f;
-    return fwd_impl(q, k, v, out, B, H, Hkv, N, d, 1, normalise, dtype, state_out, z_out, chunk, workspace,
-                    workspace_bytes, stream, nullptr, Start{state_in, z_in, g ? g : &no_tokens});
+    return fwd_impl(q, k, v, out, B, H, Hkv, N, d, 1, normalise, dtype, state_out, z_out,
+                    linattn::decay_chunk(dtype, d, H, Hkv, chunk), workspace, workspace_bytes, stream, nullptr,
+                    Start{state_in, z_in, g ? g : &no_tokens});
 }
 
 size_t linattn_fwd_packed_workspace_bytes(int nseqs, int H, int Hkv, int total, int d, int causal, int dtype,

@@ -43,6 +43,16 @@ int auto_chunk(int dtype, int d, int G, int causal)
     return 0;
 }
 
+int decay_chunk(int dtype, int d, int H, int Hkv, int chunk)
+{
+    if (chunk != 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0) return chunk;
+    // The decayed chunk kernel carries the tile decay sums and key weights
+    // beside the plain kernel's registers: for 16-bit rows at d = 64 its
+    // 128-token form spills, and the 64-token form measured faster.
+    const int c = auto_chunk(dtype, d, H / Hkv, 1);
+    return (dtype & 0xff) != LINATTN_F32 && d <= 64 && c > 64 ? 64 : c;
+}
+
 int make_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int chunk, Plan *p)
 {
     if (dtype < 0 || (dtype & 0xff) > LINATTN_FP8_E5M2 || (dtype >> 8) > LINATTN_PHI_SOFTPLUS) return LINATTN_ERR_DTYPE;

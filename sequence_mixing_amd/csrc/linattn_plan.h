@@ -114,6 +114,11 @@ int heads_per_block(int dtype, int d, int chunk, int G);
 // Chunk size used when the caller passes chunk = 0.
 int auto_chunk(int dtype, int d, int G, int causal);
 
+// Chunk size of a decayed pass of H query heads over Hkv kv heads: `chunk`
+// itself when given, else the automatic one, capped at 64 tokens for 16-bit
+// rows at d <= 64.
+int decay_chunk(int dtype, int d, int H, int Hkv, int chunk);
+
 // Fills `p` and returns LINATTN_OK or an error code (see linattn.h).
 int make_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, int chunk, Plan *p);
 

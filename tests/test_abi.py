@@ -198,10 +198,14 @@ def test_decay_validation_without_gpu():
     for args in [(2, 8, 8, 4096, 64), (1, 32, 8, 32768, 128), (2, 8, 8, 16384, 64), (3, 6, 2, 777, 32)]:
         for dt in (f32, bf):
             rc, c, P = la.linattn_fwd_plan(*args, 1, dt, 0)
-            plain = la.linattn_fwd_workspace_bytes(*args, 1, dt, 0)
+            # the automatic chunk, at most 64 tokens for 16-bit rows at d <= 64
+            ch = 64 if dt == bf and args[4] <= 64 and c > 64 else c
+            rc, c, P = la.linattn_fwd_plan(*args, 1, dt, ch)
+            plain = la.linattn_fwd_workspace_bytes(*args, 1, dt, ch)
             B, H, Hkv = args[:3]
             # one float more per segment partial (the segment's summed log-decay)
             assert la.linattn_fwd_decay_workspace_bytes(*args, dt, 0) == plain + B * Hkv * (P - 1) * 4
+            assert la.linattn_fwd_decay_workspace_bytes(*args, dt, 0) == la.linattn_fwd_decay_workspace_bytes(*args, dt, ch)
     assert la.linattn_fwd_decay(None, None, None, None, None, 0, 2, 2, 64, 64, 1, f32, stream=0) == 0
     assert la.linattn_fwd_decay(16, 16, 16, None, 16, 1, 2, 2, 64, 64, 1, f32, stream=0) == -1
     assert la.linattn_fwd_decay(16, 16, 16, 16, 16, 1, 2, 2, 64, 64, 1, relu, stream=0) == -4
