@@ -857,7 +857,45 @@ def decode_row(la, hip, torch, steps_total, stream, flush=None, cold_steps=20):
                                         "event pair around one launch)")
 
     del S, z, qs, ks, vs, out, g
+    res["state_beyond_cache"] = decode_hbm(la, hip, torch, S1, z1, dw)
     return res
+
+
+def decode_hbm(la, hip, torch, S1, z1, dw, batch=1024, steps=32):
+    """Decode steps of the cfg5 shape at a batch whose state (512 MiB fp32) is twice the
+    256 MiB memory-side cache: replayed back to back from one HIP graph, every step streams
+    the state from HBM, so the per-step time prices the kernel against HBM."""
+    from linattn_inputs import DecodeStream
+
+    S = S1.expand(batch, -1, -1, -1).contiguous()
+    z = z1.expand(batch, -1, -1).contiguous()
+    gen = DecodeStream(batch, dw.H, dw.Hkv, dw.d, dw.dtype, dw.seed + 1)
+    qs, ks, vs = (torch.stack(x).cuda() for x in zip(*(gen.next() for _ in range(steps))))
+    out = torch.empty(steps, batch, dw.H, dw.d, dtype=qs.dtype, device="cuda")
+    dt = la.LINATTN_BF16
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream().cuda_stream
+        for t in range(steps):
+            la.linattn_decode_step(S, z, qs[t], ks[t], vs[t], out[t], batch, dw.H, dw.Hkv, dw.d, 1, dt, cap)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    g.replay()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    us = hip.ms(e0, e1) / steps * 1e3
+    nb = decode_bytes(batch, dw.H, dw.Hkv, dw.d, dw.dtype)
+    fl = float(batch) * (dw.Hkv * (2 * dw.d ** 2 + 2 * dw.d) + dw.H * (2 * dw.d ** 2 + 4 * dw.d))
+    del S, z, qs, ks, vs, out, g
+    return {"batch": batch, "steps": steps, "graph_us_per_step": round(us, 2),
+            "tokens_per_s": round(batch / (us / 1e6), 1),
+            "roofline": roofline(nb, fl, us / 1e6, "bf16",
+                                 f"k_decode_step<bf16,128> (graph replay, per step; batch {batch}: the "
+                                 f"{batch * dw.Hkv * dw.d * dw.d * 4 >> 20} MiB state is twice the memory-side "
+                                 "cache, so it streams from HBM every step)")}
 
 
 def cpu_baseline(w, seconds):

@@ -927,8 +927,10 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const typename IO:
 // step costs one memory round trip: the state is updated with phi(k)_i v_j
 // in registers and written back, partial phi(q)^T S sums for 4 query heads
 // at a time are reduced through LDS, and each head's denominator is one
-// wave reduction.
-template <typename T, int D, typename IO>
+// wave reduction.  NT: the state rows are read and written with the
+// non-temporal hint (chosen when the whole state is larger than the
+// memory-side cache, so that it streams rather than thrashing the cache).
+template <typename T, int D, typename IO, bool NT = false>
 __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ state, float *__restrict__ z,
                                                           const typename IO::elem *__restrict__ q,
                                                           const typename IO::elem *__restrict__ k,
@@ -981,7 +983,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
     f32x4 Sr[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        Sr[i] = *reinterpret_cast<const f32x4 *>(Sb + (size_t)(rg + RG * i) * D + 4 * c4);
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(Sb + (size_t)(rg + RG * i) * D + 4 * c4);
+        if constexpr (NT) Sr[i] = __builtin_nontemporal_load(src);
+        else Sr[i] = *src;
         __builtin_amdgcn_sched_barrier(0);  // state rows issued in the order they are consumed
     }
 #pragma unroll
@@ -1006,7 +1010,9 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(float *__restrict__ st
     for (int i = 0; i < NV; ++i) {
         if (gd) Sr[i] *= fade;
         Sr[i] += sk[rg + RG * i] * vv;
-        *reinterpret_cast<f32x4 *>(Sb + (size_t)(rg + RG * i) * D + 4 * c4) = Sr[i];
+        f32x4 *dst = reinterpret_cast<f32x4 *>(Sb + (size_t)(rg + RG * i) * D + 4 * c4);
+        if constexpr (NT) __builtin_nontemporal_store(Sr[i], dst);
+        else *dst = Sr[i];
         __builtin_amdgcn_sched_barrier(0);  // rows in load order: each store waits for its own row only
     }
     lds_barrier();
@@ -1200,10 +1206,19 @@ int run_decode(float *state, float *z, const void *q, const void *k, const void 
     const In *kk = static_cast<const In *>(k);
     const In *vv = static_cast<const In *>(v);
     T *oo = static_cast<T *>(out);
+    // A state larger than the 256 MiB memory-side cache cannot stay there
+    // between steps: it is streamed with the non-temporal hint (batch 1024 of
+    // 8 kv heads at d = 128: 220 -> 190 us per step), a smaller one is read
+    // and written plainly so that it stays cached (the hint cost batch 64
+    // 10.7 -> 13.0 us per step).
+    const bool nt = (size_t)B * Hkv * d * d * 4 > ((size_t)256 << 20);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise, g);
+    };
     switch (d) {
-    case 32: hipLaunchKernelGGL((k_decode_step<T, 32, IO>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise, g); break;
-    case 64: hipLaunchKernelGGL((k_decode_step<T, 64, IO>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise, g); break;
-    case 128: hipLaunchKernelGGL((k_decode_step<T, 128, IO>), grid, block, 0, st, state, z, qq, kk, vv, oo, H, Hkv, G, normalise, g); break;
+    case 32: nt ? go(k_decode_step<T, 32, IO, true>) : go(k_decode_step<T, 32, IO>); break;
+    case 64: nt ? go(k_decode_step<T, 64, IO, true>) : go(k_decode_step<T, 64, IO>); break;
+    case 128: nt ? go(k_decode_step<T, 128, IO, true>) : go(k_decode_step<T, 128, IO>); break;
     default: return LINATTN_ERR_UNSUPPORTED;
     }
     return launch_status();

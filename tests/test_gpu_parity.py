@@ -234,6 +234,50 @@ def test_decode_step_head_groups(B, H, Hkv, d, dtype):
         assert mat_rel_err(host(z), zr) <= 1e-6
 
 
+@pytest.mark.parametrize("B,H,Hkv,d,dtype,decay", [(1024, 32, 8, 128, "bf16", False), (2050, 16, 8, 64, "f32", False),
+                                                    (1024, 8, 8, 128, "bf16", True)])
+def test_decode_step_state_beyond_cache(B, H, Hkv, d, dtype, decay):
+    """A state larger than the 256 MiB memory-side cache, which the decode kernel streams
+    with the non-temporal hint: two steps on the whole batch (plain or decayed sums),
+    checked against the oracle on sampled slots (every kv head) and bitwise against the
+    same steps taken in pieces of 256 slots (states small enough for the plain path)."""
+    assert B * Hkv * d * d * 4 > 256 << 20
+    print(f"decode beyond cache B{B} H{H} Hkv{Hkv} d{d} {dtype} decay={decay}", flush=True)
+    gen = torch.Generator("cuda").manual_seed(61 + d)
+    S = torch.randn(B, Hkv, d, d, device="cuda", generator=gen) * 0.05
+    z = torch.rand(B, Hkv, d, device="cuda", generator=gen) + 1.0
+    slots = [0, 1, B // 2 + 3, B - 1]
+    Sr, zr = host(S[slots]).copy(), host(z[slots]).copy()
+    S2, z2 = S.clone(), z.clone()
+    stream = DecodeStream(B, H, Hkv, d, dtype, 17 + d)
+    for step in range(2):
+        q, k, v = stream.next()
+        qg, kg, vg = gpu(q), gpu(k), gpu(v)
+        g = -torch.rand(B, Hkv, generator=torch.Generator("cpu").manual_seed(step)) if decay else None
+
+        def call(S_, z_, sl):
+            a = (S_, z_, qg[sl].contiguous(), kg[sl].contiguous(), vg[sl].contiguous())
+            return ops.decode_step_decay(*a, gpu(g[sl])) if decay else ops.decode_step(*a)
+
+        o = call(S, z, slice(0, B))
+        parts = []
+        for b0 in range(0, B, 256):
+            sl = slice(b0, min(B, b0 + 256))
+            Sp, zp = S2[sl].contiguous(), z2[sl].contiguous()
+            parts.append(call(Sp, zp, sl))
+            S2[sl], z2[sl] = Sp, zp
+        if decay:
+            ref = oracle.ref_decode_step_decay(Sr, zr, q[slots], k[slots], v[slots], g[slots].numpy())
+        else:
+            ref = oracle.ref_decode_step(Sr, zr, q[slots], k[slots], v[slots], normalise=True)
+        torch.cuda.synchronize()
+        assert rows_rel_err(host(o[slots]), ref) <= (1e-5 if dtype == "f32" else TOL[dtype])
+        assert torch.equal(o, torch.cat(parts)), f"step {step}: outputs differ from the pieces"
+    assert torch.equal(S, S2) and torch.equal(z, z2)
+    assert mat_rel_err(host(S[slots]), Sr) <= 1e-5
+    assert mat_rel_err(host(z[slots]), zr) <= 1e-6
+
+
 def test_decode_continues_prefill_on_gpu():
     """Prefill(N) then one decode step equals row N of prefill(N + 1)."""
     B, H, Hkv, N, d = 2, 8, 2, 777, 64
