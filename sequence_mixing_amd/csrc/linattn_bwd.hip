@@ -28,8 +28,9 @@
 //                          forwards, serving the G query heads of the group.
 //                          Per chunk: z_t of every token (LDS prefix); per
 //                          head: den = a . z_t, then on MFMA
-//                          dA^T = B^T (M .* (V G^T + h)) + S G^T; writes dq
-//                          and den (kept for the next passes);
+//                          dA^T = B^T (M .* (V G^T + h)) + S G^T; writes dq,
+//                          and den and h of every token (kept for the next
+//                          passes, which then need not read the outputs);
 //   bwd_dkv<totals>        per (sequence, segment): sum of a g^T and h a over
 //                          the segment and the group's heads;
 //   seg_scan (suffix)      gives each segment the sums of the later ones;
@@ -179,7 +180,8 @@ template <typename T, int D, typename IO>
 __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES(D)>::OCC_DQ)) void k_bwd_dq(const T *__restrict__ q, const T *__restrict__ k,
                                                       const T *__restrict__ v, const T *__restrict__ o,
                                                       const T *__restrict__ dout, T *__restrict__ dq,
-                                                      float *__restrict__ den_out, const float *__restrict__ ws,
+                                                      float *__restrict__ den_out, float *__restrict__ h_out,
+                                                      const float *__restrict__ ws,
                                                       float *__restrict__ ws_r, int H, int Hkv, int N, int G, int P,
                                                       int seg_len, int causal, int normalise)
 {
@@ -340,6 +342,7 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
             // ---- a, den, g, h of this head; the next head's rows requested
             {
                 const Rsrc rden = make_rsrc_u(den_out + (size_t)qh * N + t0, normalise ? rows * 4 : 0);
+                const Rsrc rh = make_rsrc_u(h_out + (size_t)qh * N + t0, normalise ? rows * 4 : 0);
 #pragma unroll
                 for (int l = 0; l < LDV; ++l) {
                     const int e = tid + l * BG::TH, t = e / GPR, cq = (e % GPR) * U;
@@ -360,15 +363,17 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
                     float gg[U];
 #pragma unroll
                     for (int i = 0; i < U; ++i) gg[i] = Io<T, IO>::fi(dr[l], i) * inv;
+                    const float hv = normalise ? -dov * inv : 0.f;
                     if (grp) {
                         sA.write16(t, cq, to_g16<T>(a));
                         sG.write16(t, cq, to_g16<T>(gg));
                         if constexpr (SPLIT) sGl.write16(t, cq, to_g16_lo<T>(gg));
-                        if (e % GPR == 0) sH[t] = normalise ? -dov * inv : 0.f;
+                        if (e % GPR == 0) sH[t] = hv;
                     }
-                    // den for the dk/dv pass (one lane per row; the others' offsets are out of range)
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, den), rden,
-                                                          (grp && e % GPR == 0) ? (unsigned)t * 4u : kOutOfRange, 0, 0);
+                    // den and h for the dk/dv passes (one lane per row; the others' offsets are out of range)
+                    const unsigned roff = (grp && e % GPR == 0) ? (unsigned)t * 4u : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, den), rden, roff, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, hv), rh, roff, 0, 0);
                 }
                 const int nh = hh + 1 < G ? hh + 1 : 0, nc = hh + 1 < G ? c : c + 1;
                 const size_t nq = (size_t)(qh0 + nh) * N * D;
@@ -502,7 +507,7 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
 // waves; r in per-thread partial sums (column tid % D, a slice of the rows).
 template <typename T, int D, bool TOTALS, typename IO>
 __global__ __launch_bounds__((BGeo<T, D, DKV_WAVES(D, TOTALS)>::TH), (BGeo<T, D, DKV_WAVES(D, TOTALS)>::OCC_DKV)) void k_bwd_dkv(const T *__restrict__ q, const T *__restrict__ k,
-                                                       const T *__restrict__ v, const T *__restrict__ o,
+                                                       const T *__restrict__ v, const float *__restrict__ hrow,
                                                        const T *__restrict__ dout, const float *__restrict__ den,
                                                        T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ ws_r,
                                                        int H, int Hkv, int N, int G, int P, int seg_len, int causal,
@@ -560,8 +565,10 @@ __global__ __launch_bounds__((BGeo<T, D, DKV_WAVES(D, TOTALS)>::TH), (BGeo<T, D,
     f32x16 out[MAXU];
     const int nheads = (!TOTALS && !causal) ? 0 : G;
 
-    g16 kr[LDV], vr[LDV], qr[LDV], orr[LDV], dr[LDV];
-    float dn[LDV];
+    // h of every token comes from the dq walk (it formed h from dO and the
+    // outputs already), so the outputs are not read again here
+    g16 kr[LDV], vr[LDV], qr[LDV], dr[LDV];
+    float dn[LDV], hn[LDV];
     if (!TOTALS) {
         load_rows<T, D, BG::TH>(kr, kb, t0_of(0), rows_of(0), tid);
         load_rows<T, D, BG::TH>(vr, vb, t0_of(0), rows_of(0), tid);
@@ -569,9 +576,9 @@ __global__ __launch_bounds__((BGeo<T, D, DKV_WAVES(D, TOTALS)>::TH), (BGeo<T, D,
     {
         const int r0 = nheads > 0 ? rows_of(0) : 0;
         load_rows<T, D, BG::TH>(qr, q + (size_t)qh0 * N * D, t0_of(0), r0, tid);
-        load_rows<T, D, BG::TH>(orr, o + (size_t)qh0 * N * D, t0_of(0), normalise ? r0 : 0, tid);
         load_rows<T, D, BG::TH>(dr, dout + (size_t)qh0 * N * D, t0_of(0), r0, tid);
         load_row_scalars<T, D, BG::TH>(dn, den + (size_t)qh0 * N, t0_of(0), normalise ? r0 : 0, tid);
+        load_row_scalars<T, D, BG::TH>(hn, hrow + (size_t)qh0 * N, t0_of(0), normalise ? r0 : 0, tid);
     }
 
     for (int j = 0; j < nch; ++j) {
@@ -622,18 +629,16 @@ __global__ __launch_bounds__((BGeo<T, D, DKV_WAVES(D, TOTALS)>::TH), (BGeo<T, D,
                 const int e = tid + l * BG::TH, t = e / GPR, cq = (e % GPR) * U;
                 const bool real = t < rows;
                 const float inv = real ? (normalise ? 1.f / dn[l] : 1.f) : 0.f;
-                float a[U], gg[U], dov = 0.f;
+                float a[U], gg[U];
 #pragma unroll
                 for (int i = 0; i < U; ++i) {
                     a[i] = real ? IO::phi::f(Io<T, IO>::fi(qr[l], i)) : 0.f;
                     gg[i] = Io<T, IO>::fi(dr[l], i) * inv;
-                    dov += Io<T, IO>::fi(dr[l], i) * Io<T, IO>::fi(orr[l], i);
                 }
-                dov = row_sum<GPR>(dov);
                 if (BG::NGRP % BG::TH == 0 || e < BG::NGRP) {
                     sA.write16(t, cq, to_g16<T>(a));
                     sG.write16(t, cq, to_g16<T>(gg));
-                    if (e % GPR == 0) sH[t] = normalise ? -dov * inv : 0.f;
+                    if (e % GPR == 0) sH[t] = real && normalise ? hn[l] : 0.f;
                 }
             }
             {
@@ -641,9 +646,9 @@ __global__ __launch_bounds__((BGeo<T, D, DKV_WAVES(D, TOTALS)>::TH), (BGeo<T, D,
                 const size_t nq = (size_t)(qh0 + nh);
                 const int nt0 = t0_of(nj), nrows = rows_of(nj);
                 load_rows<T, D, BG::TH>(qr, q + nq * N * D, nt0, nrows, tid);
-                load_rows<T, D, BG::TH>(orr, o + nq * N * D, nt0, normalise ? nrows : 0, tid);
                 load_rows<T, D, BG::TH>(dr, dout + nq * N * D, nt0, nrows, tid);
                 load_row_scalars<T, D, BG::TH>(dn, den + nq * N, nt0, normalise ? nrows : 0, tid);
+                load_row_scalars<T, D, BG::TH>(hn, hrow + nq * N, nt0, normalise ? nrows : 0, tid);
             }
             lds_barrier();
             // ---- intra-chunk terms (causal), then R += A^T G, r += A^T h
@@ -773,7 +778,7 @@ __global__ __launch_bounds__((BGeo<T, D, DKV_WAVES(D, TOTALS)>::TH), (BGeo<T, D,
 
 struct BwdPlan {
     int nseq, G, P, seg_len, fwd_slots, r_slots;
-    size_t off_den, off_r, bytes;
+    size_t off_den, off_h, off_r, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -803,7 +808,8 @@ int bwd_plan(int B, int H, int Hkv, int N, int d, int causal, int dtype, BwdPlan
     const size_t part = (size_t)d * (d + 1) * 4;
     const size_t fwd = align256((size_t)p.nseq * p.fwd_slots * part);
     p.off_den = fwd;
-    p.off_r = p.off_den + align256((size_t)B * H * N * 4);
+    p.off_h = p.off_den + align256((size_t)B * H * N * 4);
+    p.off_r = p.off_h + align256((size_t)B * H * N * 4);
     p.bytes = p.off_r + align256((size_t)p.nseq * p.r_slots * part);
     *pl = p;
     return LINATTN_OK;
@@ -818,6 +824,7 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
     const T *dd = static_cast<const T *>(dout);
     float *wf = reinterpret_cast<float *>(ws);
     float *wden = reinterpret_cast<float *>(ws + pl.off_den);
+    float *wh = reinterpret_cast<float *>(ws + pl.off_h);
     float *wr = reinterpret_cast<float *>(ws + pl.off_r);
     const int P = pl.P, E = D * D + D;
     const int c1 = totals_chunk<T, D>(pl.seg_len);
@@ -840,7 +847,7 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
     // (16-bit rows, d <= 64: the dq walk also writes each segment's sums of a g^T and h a)
     constexpr bool RT = sizeof(T) == 2 && D <= 64;
     hipLaunchKernelGGL((k_bwd_dq<T, D, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D, DQ_WAVES(D)>::TH), 0, st, qq, kk, vv, oo, dd,
-                       static_cast<T *>(dq), wden, (const float *)wf, RT ? wr : (float *)nullptr, H, Hkv, N, pl.G, P,
+                       static_cast<T *>(dq), wden, wh, (const float *)wf, RT ? wr : (float *)nullptr, H, Hkv, N, pl.G, P,
                        pl.seg_len, causal, normalise);
     // 3. sums of a g^T and h a per segment (otherwise their own pass):
     // causal segments 1..P-1 with a suffix scan, non-causal all and their sum
@@ -848,7 +855,7 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
         if (P > 1) {
             if (!RT)
                 hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * (P - 1)), dim3(BGeo<T, D, DKV_WAVES(D, true)>::TH), 0, st, qq, kk, vv,
-                                   oo, dd, (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P,
+                                   (const float *)wh, dd, (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P,
                                    pl.seg_len, causal, normalise, P - 1, 1);
             if (P > 2)
                 hipLaunchKernelGGL(k_seg_scan, scan_grid(D, pl.nseq), dim3(kThreads), 0, st,
@@ -857,14 +864,14 @@ int run_bwd(const BwdPlan &pl, int H, int Hkv, int N, const void *q, const void 
         }
     } else {
         if (!RT)
-            hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D, DKV_WAVES(D, true)>::TH), 0, st, qq, kk, vv, oo, dd,
+            hipLaunchKernelGGL((k_bwd_dkv<T, D, true, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D, DKV_WAVES(D, true)>::TH), 0, st, qq, kk, vv, (const float *)wh, dd,
                                (const float *)wden, (T *)nullptr, (T *)nullptr, wr, H, Hkv, N, pl.G, P, pl.seg_len,
                                causal, normalise, P, 0);
         hipLaunchKernelGGL(k_seg_scan, scan_grid(D, pl.nseq), dim3(kThreads), 0, st, wr, P, D,
                            1, (float *)nullptr, (float *)nullptr, (const float *)nullptr, (const float *)nullptr);
     }
     // 4. dk, dv
-    hipLaunchKernelGGL((k_bwd_dkv<T, D, false, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D, DKV_WAVES(D, false)>::TH), 0, st, qq, kk, vv, oo, dd,
+    hipLaunchKernelGGL((k_bwd_dkv<T, D, false, IO>), dim3(pl.nseq * P), dim3(BGeo<T, D, DKV_WAVES(D, false)>::TH), 0, st, qq, kk, vv, (const float *)wh, dd,
                        (const float *)wden, static_cast<T *>(dk), static_cast<T *>(dv), wr, H, Hkv, N, pl.G, P,
                        pl.seg_len, causal, normalise, P, 0);
     return launch_status();
