@@ -23,6 +23,12 @@ struct Win {
     static constexpr int LQ = (QG + kThreads - 1) / kThreads;
     static constexpr int KG = 32 * GPR;                // 16-byte groups of one 32-key tile
     static constexpr int LK = (KG + kThreads - 1) / kThreads;
+    // key tiles in flight in registers (16-bit rows: three at d <= 64, two
+    // at d = 128, with the registers of 4, 3 and 2 workgroups per CU at d = 32,
+    // 64 and 128; fp32 rows: two, occupancy left to the compiler)
+    static constexpr bool B16 = sizeof(T) == 2;
+    static constexpr int NS = B16 && D <= 64 ? 3 : 2;
+    static constexpr int OCC = !B16 ? 1 : D <= 32 ? 4 : D <= 64 ? 3 : 2;
 };
 
 // One workgroup per (batch, query head, 128-query tile).  Key tiles of 32
@@ -34,7 +40,7 @@ struct Win {
 // sums, and O^T += V^T Pt (MFMA).  The outputs are parked in the wave's own
 // q rows and stored as whole rows.
 template <typename T, int D, typename IO>
-__global__ __launch_bounds__(kThreads) void k_window(const typename IO::elem *__restrict__ q,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Win<T, D>::OCC))) void k_window(const typename IO::elem *__restrict__ q,
                                                      const typename IO::elem *__restrict__ k,
                                                      const typename IO::elem *__restrict__ v, T *__restrict__ out,
                                                      int H, int Hkv, int N, int W, int normalise, int nqt)
@@ -84,8 +90,11 @@ __global__ __launch_bounds__(kThreads) void k_window(const typename IO::elem *__
     // key tiles of the workgroup's band: keys max(0, t0 - W + 1) .. t0 + qrows - 1
     const int kt0 = max(0, t0 - W + 1) / 32, kt1 = (t0 + qrows - 1) / 32;
     auto rows_of = [&](int kt) { return kt <= kt1 ? min(32, N - kt * 32) : 0; };
-    g16 kr[Wn::LK], vr[Wn::LK];
-    auto load_kv = [&](int kt) {  // past the band: nothing is read
+    // NS register sets: key tile kt waits in set (kt - kt0) % NS from NS
+    // steps before its staging (one step left the loads' round trip exposed).
+    constexpr int NS = Wn::NS;
+    g16 kr[NS][Wn::LK], vr[NS][Wn::LK];
+    auto load_kv = [&](int u, int kt) {  // past the band: nothing is read
         const int rows = rows_of(kt);
         const Rsrc rk = make_rsrc(kb + (size_t)kt * 32 * D, rows * D * IE);
         const Rsrc rv = make_rsrc(vb + (size_t)kt * 32 * D, rows * D * IE);
@@ -93,13 +102,14 @@ __global__ __launch_bounds__(kThreads) void k_window(const typename IO::elem *__
         for (int l = 0; l < Wn::LK; ++l) {
             const int e = tid + l * kThreads;
             const unsigned off = (Wn::KG % kThreads == 0 || e < Wn::KG) ? (unsigned)e * GB : kOutOfRange;
-            kr[l] = load_in<T, IO>(rk, off);
-            vr[l] = load_in<T, IO>(rv, off);
+            kr[u][l] = load_in<T, IO>(rk, off);
+            vr[u][l] = load_in<T, IO>(rv, off);
         }
     };
-    load_kv(kt0);
-    stage_rows<T, D, 32, kThreads, IO>(kr, vr, Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, rows_of(kt0), tid);
-    load_kv(kt0 + 1);
+#pragma unroll
+    for (int u = 0; u < NS; ++u) load_kv(u, kt0 + u);
+    stage_rows<T, D, 32, kThreads, IO>(kr[0], vr[0], Tile<T, D>{smK[0]}, Tile<T, D>{smV[0]}, rows_of(kt0), tid);
+    load_kv(0, kt0 + NS);
     lds_barrier();
 
     const int q0 = t0 + 32 * w;
@@ -114,8 +124,10 @@ __global__ __launch_bounds__(kThreads) void k_window(const typename IO::elem *__
     float ds = 0.f;
     const int t = q0 + n;  // this lane's query
 
-    for (int kt = kt0; kt <= kt1; ++kt) {
-        const int buf = (kt - kt0) & 1;
+    // Step kt uses LDS buffer (kt - kt0) & 1 and stages tile kt + 1 from
+    // register set (kt + 1 - kt0) % NS into the other; steps in groups of
+    // lcm(NS, 2) so that both indices are fixed.
+    auto step = [&](int kt, const int buf, const int nset) {
         const Tile<T, D> tK{smK[buf]}, tV{smV[buf]};
         const int ks = kt * 32;
         if (live && ks <= q0 + 31 && ks + 31 > q0 - W) {
@@ -145,11 +157,17 @@ __global__ __launch_bounds__(kThreads) void k_window(const typename IO::elem *__
         }
         if (kt < kt1) {
             // the next tile into the other buffer (last read before the previous barrier)
-            stage_rows<T, D, 32, kThreads, IO>(kr, vr, Tile<T, D>{smK[buf ^ 1]}, Tile<T, D>{smV[buf ^ 1]},
-                                               rows_of(kt + 1), tid);
-            load_kv(kt + 2);
+            stage_rows<T, D, 32, kThreads, IO>(kr[nset], vr[nset], Tile<T, D>{smK[buf ^ 1]},
+                                               Tile<T, D>{smV[buf ^ 1]}, rows_of(kt + 1), tid);
+            load_kv(nset, kt + 1 + NS);
         }
         lds_barrier();
+    };
+    constexpr int GRP = NS % 2 ? 2 * NS : NS;
+    for (int kt = kt0; kt <= kt1; kt += GRP) {
+#pragma unroll
+        for (int j = 0; j < GRP; ++j)
+            if (kt + j <= kt1) step(kt + j, j & 1, (j + 1) % NS);
     }
 
     // outputs into this wave's own q rows, then whole rows out
