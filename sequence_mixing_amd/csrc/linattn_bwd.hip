@@ -465,7 +465,7 @@ __global__ __launch_bounds__((BGeo<T, D, DQ_WAVES(D)>::TH), (BGeo<T, D, DQ_WAVES
                 for (int l = 0; l < LDV; ++l) {
                     const int e = tid + l * BG::TH, t = e / GPR, cq = (e % GPR) * U;
                     if (BG::NGRP % BG::TH == 0 || e < BG::NGRP)
-                        buf_store16<g16>(rdq, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sO.p + sO.at(t, cq)));
+                        buf_store16_nt<g16>(rdq, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sO.p + sO.at(t, cq)));
                 }
             }
         }
@@ -747,8 +747,8 @@ __global__ __launch_bounds__((BGeo<T, D, DKV_WAVES(D, TOTALS)>::TH), (BGeo<T, D,
             for (int l = 0; l < LDV; ++l) {
                 const int e = tid + l * BG::TH, t = e / GPR, cq = (e % GPR) * U;
                 if (BG::NGRP % BG::TH == 0 || e < BG::NGRP) {
-                    buf_store16<g16>(rdk, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sOK.p + sOK.at(t, cq)));
-                    buf_store16<g16>(rdv, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sOV.p + sOV.at(t, cq)));
+                    buf_store16_nt<g16>(rdk, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sOK.p + sOK.at(t, cq)));
+                    buf_store16_nt<g16>(rdv, (unsigned)e * 16u, *reinterpret_cast<const g16 *>(sOV.p + sOV.at(t, cq)));
                 }
             }
         }

@@ -261,7 +261,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         const int rows = min(C, N - t_prev);
         const Rsrc ro = make_rsrc(ob + (size_t)t_prev * D, (qspan - t_prev * D) * E);
 #pragma unroll
-        for (int l = 0; l < M::LQ; ++l) buf_store16<g16>(ro, qt[l] < rows ? qel[l] * E : kOutOfRange, o[l]);
+        for (int l = 0; l < M::LQ; ++l) buf_store16_nt<g16>(ro, qt[l] < rows ? qel[l] * E : kOutOfRange, o[l]);
     };
     // phi(q) of the staged chunk into the q rows.
     auto stage_q = [&](const Regs &r) {
@@ -699,7 +699,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                 const int rows = min(C, N - t_prev);
                 const Rsrc ro = make_rsrc(ob + (size_t)t_prev * D, (qspan - t_prev * D) * E);
 #pragma unroll
-                for (int l = 0; l < LQP; ++l) buf_store16<g16>(ro, pqt[l] < rows ? pqel[l] * E : kOutOfRange, o[l]);
+                for (int l = 0; l < LQP; ++l) buf_store16_nt<g16>(ro, pqt[l] < rows ? pqel[l] * E : kOutOfRange, o[l]);
             };
             // One chunk step (two sets); r holds chunk c+1 and is refilled
             // with chunk c+3.  The one-set loop below is the same step with

@@ -51,6 +51,14 @@ template <typename G> __device__ __forceinline__ void buf_store16(Rsrc r, unsign
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
 }
 
+// The same with the non-temporal hint (cache policy bit nt): for rows that
+// are written once and not read again by the kernels that follow.
+template <typename G> __device__ __forceinline__ void buf_store16_nt(Rsrc r, unsigned off, G x)
+{
+    static_assert(sizeof(G) == 16, "16-byte group");
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 2);
+}
+
 // Workgroup barrier for LDS hand-offs only.  __syncthreads() also drains
 // every outstanding global load (vmcnt), which would stall the register
 // prefetch of the next chunk at each barrier; here only LDS traffic
