@@ -239,7 +239,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
         const int rows = rows_at(t0);
         const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, rows ? (qspan - t0 * D) * IE : 0);
 #pragma unroll
-        for (int l = 0; l < M::LQ; ++l) r.q[l] = load_in<T, IO>(rq, qt[l] < rows ? qel[l] * IE : kOutOfRange);
+        for (int l = 0; l < M::LQ; ++l) r.q[l] = load_in_nt<T, IO>(rq, qt[l] < rows ? qel[l] * IE : kOutOfRange);
     };
     auto load_all = [&](Regs &r, int t0) {
         load_kv(r, t0);
@@ -668,7 +668,7 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
                 }
                 const Rsrc rq = make_rsrc(qb + (size_t)t0 * D, rows ? (qspan - t0 * D) * IE : 0);
 #pragma unroll
-                for (int l = 0; l < LQP; ++l) r.q[l] = load_in<T, IO>(rq, pqt[l] < rows ? pqel[l] * IE : kOutOfRange);
+                for (int l = 0; l < LQP; ++l) r.q[l] = load_in_nt<T, IO>(rq, pqt[l] < rows ? pqel[l] * IE : kOutOfRange);
             };
             auto p_stage_kv = [&](const PSet &r, int b, int rows) {
                 stage_rows<T, D, C, PTH, IO>(r.k, r.v, Tile<T, D>{smK[b]}, Tile<T, D>{smV[b]}, rows, pt);

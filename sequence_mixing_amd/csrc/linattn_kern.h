@@ -235,6 +235,18 @@ __device__ __forceinline__ typename Vt<T>::g16 load_in(Rsrc r, unsigned off)
     }
 }
 
+// The same with the non-temporal hint: for rows read once.
+template <typename T, typename IO>
+__device__ __forceinline__ typename Vt<T>::g16 load_in_nt(Rsrc r, unsigned off)
+{
+    if constexpr (Io<T, IO>::FP8) {
+        const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2));
+        return __builtin_bit_cast(typename Vt<T>::g16, u32x4{x[0], x[1], 0u, 0u});
+    } else {
+        return __builtin_bit_cast(typename Vt<T>::g16, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+    }
+}
+
 template <typename E> __device__ __forceinline__ typename Vt<E>::v8 cvt8(const float *x);
 template <> __device__ __forceinline__ bf16x8 cvt8<bf16>(const float *x)
 {
