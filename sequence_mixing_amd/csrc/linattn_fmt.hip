@@ -805,8 +805,13 @@ __global__ __launch_bounds__((Main<T, D, C, GT>::TH), (Main<T, D, C, GT>::OCC)) 
 
 // --------------------------------------------------------- noncausal_apply
 //
-// One workgroup per (sequence, block of 128 tokens); every wave takes whole
-// query tiles (head, 32 rows).  S and z are the sums left in slot 0 of ws.
+// One workgroup per (sequence, block of 128 tokens).  S and z are the sums
+// left in slot 0 of ws; S^T goes to LDS once.  Per query head of the group,
+// the block's 128 q rows are loaded as whole 16-byte row groups (coalesced),
+// phi(q) is written to an LDS tile, wave w computes O^T = S^T phi(Q)^T on
+// MFMA for rows 32 w .. 32 w + 31 and parks the outputs in its own rows of
+// the tile, and the tile is stored as whole rows with the non-temporal hint.
+// The next head's q rows are requested while the current head is computed.
 template <typename T, int D, typename IO>
 __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const typename IO::elem *__restrict__ q,
                                                               T *__restrict__ out,
@@ -818,11 +823,14 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const typename IO:
     using Gm = Geo<T, D, 32>;
     using v8 = typename Vt<T>::v8;
     using g16 = typename Vt<T>::g16;
-    constexpr int U = Gm::U;
-    constexpr int QV = 8 / U;
+    constexpr int U = Gm::U, GPR = D / U;
+    constexpr int QG = TQ * GPR, LQ = QG / kThreads;  // 16-byte groups of a 128-row tile, per thread
+    static_assert(QG % kThreads == 0, "whole groups per thread");
+    constexpr int E = (int)sizeof(T), IE = Io<T, IO>::EB, GB = Io<T, IO>::GB;  // output, input bytes
     __shared__ __attribute__((aligned(16))) T smST[D * D];
+    __shared__ __attribute__((aligned(16))) T smQ[TQ * D];
     __shared__ float smZ[D];
-    const Tile<T, D> sST{smST};
+    const Tile<T, D> sST{smST}, sQ{smQ};
 
     // Dense batch: blocks run over (sequence, 128-token block).  Packed batch
     // (segments of seg_len tokens, a multiple of 128): over (kv head, segment
@@ -846,9 +854,22 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const typename IO:
         slot0 = packed_slot0(r, gk, Hkv, 0);
     }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, n = lane & 31;
-    const float *S = ws + slot0 * (size_t)D * (D + 1);
+    const int t0 = blk * TQ, rows = min(TQ, N - t0);
+    const typename IO::elem *qb = q + qbase + (size_t)t0 * D;
+    T *ob = out + qbase + (size_t)t0 * D;
+
+    // raw q groups of head g's tile (rows past N, and heads past G, read zeros)
+    g16 xr[LQ];
+    auto load_tile = [&](int g) {
+        const Rsrc rq = make_rsrc(qb + (size_t)g * N * D, g < G ? rows * D * IE : 0);
+#pragma unroll
+        for (int l = 0; l < LQ; ++l) xr[l] = load_in_nt<T, IO>(rq, (unsigned)(tid + l * kThreads) * GB);
+    };
+    load_tile(0);
+
     // S^T into LDS: element (row j, col i) = S[i][j].  Every thread's 16-byte
     // groups of S (and z) are requested at once, then written transposed.
+    const float *S = ws + slot0 * (size_t)D * (D + 1);
     constexpr int S4 = D * D / 4, SPT = S4 / kThreads;
     static_assert(S4 % kThreads == 0 && D <= kThreads, "S in whole 16-byte groups per thread");
     f32x4 sg[SPT];
@@ -862,36 +883,25 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const typename IO:
         for (int x = 0; x < 4; ++x) smST[sST.at(j0 + x, i)] = (T)sg[l][x];
     }
     if (tid < D) smZ[tid] = zv;
-    __syncthreads();
 
-    const typename IO::elem *qb = q + qbase;
-    T *ob = out + qbase;
-    const int NU = G * (TQ / 32);
-    for (int u = w; u < NU; u += 4) {
-        const int g = u / (TQ / 32), r = u % (TQ / 32);
-        const int t = blk * TQ + r * 32 + n;
-        if (blk * TQ + r * 32 >= N) continue;
-        const typename IO::elem *src = qb + (size_t)g * N * D + (size_t)t * D;
+    const Rsrc ro0 = make_rsrc(ob, rows * D * E);
+    for (int g = 0; g < G; ++g) {
+        // phi(q) of this head's tile into LDS, then the next head's rows requested
+#pragma unroll
+        for (int l = 0; l < LQ; ++l) {
+            const int e = tid + l * kThreads;
+            g16 f;
+#pragma unroll
+            for (int i = 0; i < U; ++i) f[i] = (T)IO::phi::f(Io<T, IO>::fi(xr[l], i));
+            sQ.write16(e / GPR, (e % GPR) * U, f);
+        }
+        load_tile(g + 1);
+        lds_barrier();  // (the first time also S^T and z)
         v8 qf[Gm::KBD];
         float dq = 0.f;
 #pragma unroll
         for (int kb = 0; kb < Gm::KBD; ++kb) {
-            float f[8];
-#pragma unroll
-            for (int j = 0; j < QV; ++j) {
-                g16 x = {};
-                if (t < N) {
-                    if constexpr (Io<T, IO>::FP8) {
-                        const u32x2 y = *reinterpret_cast<const u32x2 *>(src + kb * 16 + h * 8 + j * U);
-                        x = __builtin_bit_cast(g16, u32x4{y[0], y[1], 0u, 0u});
-                    } else {
-                        x = *reinterpret_cast<const g16 *>(src + kb * 16 + h * 8 + j * U);
-                    }
-                }
-#pragma unroll
-                for (int s = 0; s < U; ++s) f[j * U + s] = IO::phi::f(Io<T, IO>::fi(x, s));
-            }
-            qf[kb] = cvt8<T>(f);
+            qf[kb] = sQ.read8(32 * w + n, kb * 16 + h * 8);
 #pragma unroll
             for (int s = 0; s < 8; ++s) dq += (float)qf[kb][s] * smZ[kb * 16 + h * 8 + s];
         }
@@ -905,17 +915,25 @@ __global__ __launch_bounds__(kThreads) void k_noncausal_apply(const typename IO:
         }
         dq += __shfl_xor(dq, 32);
         const float inv = normalise ? 1.f / dq : 1.f;
-        if (t < N) {
-            T *dst = ob + (size_t)g * N * D + (size_t)t * D;
+        // outputs into this wave's own rows of the tile (its phi(q) is in registers)
 #pragma unroll
-            for (int ct = 0; ct < Gm::DT; ++ct)
+        for (int ct = 0; ct < Gm::DT; ++ct)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    f32x4 x{O[ct][4 * q4] * inv, O[ct][4 * q4 + 1] * inv, O[ct][4 * q4 + 2] * inv,
-                            O[ct][4 * q4 + 3] * inv};
-                    *reinterpret_cast<typename Vt<T>::v4 *>(dst + ct * 32 + 8 * q4 + 4 * h) = out4<T, IO>(x);
-                }
+            for (int q4 = 0; q4 < 4; ++q4) {
+                f32x4 x{O[ct][4 * q4] * inv, O[ct][4 * q4 + 1] * inv, O[ct][4 * q4 + 2] * inv,
+                        O[ct][4 * q4 + 3] * inv};
+                sQ.write4(32 * w + n, ct * 32 + 8 * q4 + 4 * h, out4<T, IO>(x));
+            }
+        lds_barrier();
+        // whole output rows (rows past N are out of range: not stored)
+        const Rsrc ro = g == 0 ? ro0 : make_rsrc(ob + (size_t)g * N * D, rows * D * E);
+#pragma unroll
+        for (int l = 0; l < LQ; ++l) {
+            const int e = tid + l * kThreads;
+            const g16 o = *reinterpret_cast<const g16 *>(sQ.p + sQ.at(e / GPR, (e % GPR) * U));
+            buf_store16_nt<g16>(ro, (unsigned)e * 16u, o);
         }
+        lds_barrier();  // the tile is written again for the next head
     }
 }
 
